@@ -1,0 +1,156 @@
+"""Diffuser CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Plain double-precision CPU implementation of the Diffuser attention-diffusion
+path (graph, edge scores, edge softmax, K-step personalized-PageRank
+diffusion), written in C (``oracle.c``) and reached through ctypes.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module. It shares no code with the HIP library.
+
+Sources: "Diffuser" reading notes sections 2.1 (eqs. S.1-S.5), 2.2, 2.4
+(eq. S.7), 2.5; "1.2.1 Static sparsity" sections 1, 1.1 (eq. 5), 1.2 (eq. 12);
+"038 BigBird" section 2 (union neighbourhood).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+_lib = None
+
+
+def build(out_path: str = LIB_PATH, src_path: str = SRC_PATH, extra_flags=()) -> str:
+    """Compiles the oracle with gcc (plain -O2, no fast-math: summation order
+    is part of the oracle's definition)."""
+    tmp = out_path + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra",
+           *extra_flags, src_path, "-o", tmp, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def _bind(lib):
+    i64, i32, u64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64
+    p = ctypes.c_void_p
+    lib.oracle_mix64.restype = u64
+    lib.oracle_mix64.argtypes = [u64]
+    lib.oracle_draw.restype = u64
+    lib.oracle_draw.argtypes = [u64, i64, i64, i64, i64]
+    graph_args = [i64, i32, i32, p, i32, i32, i32, u64]
+    lib.oracle_graph_nnz.restype = ctypes.c_int
+    lib.oracle_graph_nnz.argtypes = graph_args + [p]
+    lib.oracle_graph_build.restype = ctypes.c_int
+    lib.oracle_graph_build.argtypes = graph_args + [p, p]
+    for name in ("oracle_scores_softmax", "oracle_scores"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [p, p, i64, i32, p, p, p, i32]
+    lib.oracle_diffuse.restype = ctypes.c_int
+    lib.oracle_diffuse.argtypes = [p, p, i64, i32, p, p, i32, ctypes.c_double, p, i32]
+    return lib
+
+
+def load(path: str = LIB_PATH):
+    """Loads (building first if absent) the oracle library."""
+    global _lib
+    if path != LIB_PATH:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(path):
+            build()
+        _lib = _bind(ctypes.CDLL(path))
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise OracleError(f"{what} failed with status {st}")
+
+
+class Oracle:
+    """Thin numpy-facing wrapper around one loaded oracle library."""
+
+    def __init__(self, lib=None):
+        self.lib = lib if lib is not None else load()
+
+    # -- random draws -----------------------------------------------------
+    def mix64(self, z: int) -> int:
+        return int(self.lib.oracle_mix64(z))
+
+    def draw(self, seed: int, b: int, n: int, i: int, t: int) -> int:
+        return int(self.lib.oracle_draw(seed, b, n, i, t))
+
+    # -- graph --------------------------------------------------------------
+    def graph(self, n, radius, global_idx, num_random, num_graphs=1, causal=False, seed=0):
+        """Returns (row_ptr int64[num_graphs, n+1], list of col_idx int32 arrays)."""
+        g = np.ascontiguousarray(np.asarray(global_idx, dtype=np.int32))
+        gp = _ptr(g) if g.size else None
+        nnz = np.zeros(num_graphs, dtype=np.int64)
+        args = (n, radius, g.size, gp, num_random, num_graphs, int(bool(causal)), seed)
+        _check(self.lib.oracle_graph_nnz(*args, _ptr(nnz)), "oracle_graph_nnz")
+        row_ptr = np.zeros((num_graphs, n + 1), dtype=np.int64)
+        cols = np.zeros(max(int(nnz.sum()), 1), dtype=np.int32)
+        _check(self.lib.oracle_graph_build(*args, _ptr(row_ptr), _ptr(cols)),
+               "oracle_graph_build")
+        out, base = [], 0
+        for gr in range(num_graphs):
+            out.append(cols[base:base + int(nnz[gr])].copy())
+            base += int(nnz[gr])
+        return row_ptr, out
+
+    # -- per (batch, head) arithmetic ----------------------------------------
+    def scores_softmax(self, Q, K, row_ptr, col_idx, threads=1):
+        Q = np.ascontiguousarray(Q, dtype=np.float64)
+        K = np.ascontiguousarray(K, dtype=np.float64)
+        rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+        ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+        n, d = Q.shape
+        A = np.zeros(max(int(rp[-1]), 1), dtype=np.float64)
+        _check(self.lib.oracle_scores_softmax(_ptr(Q), _ptr(K), n, d, _ptr(rp), _ptr(ci),
+                                              _ptr(A), threads), "oracle_scores_softmax")
+        return A[: int(rp[-1])]
+
+    def scores(self, Q, K, row_ptr, col_idx, threads=1):
+        Q = np.ascontiguousarray(Q, dtype=np.float64)
+        K = np.ascontiguousarray(K, dtype=np.float64)
+        rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+        ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+        n, d = Q.shape
+        S = np.zeros(max(int(rp[-1]), 1), dtype=np.float64)
+        _check(self.lib.oracle_scores(_ptr(Q), _ptr(K), n, d, _ptr(rp), _ptr(ci), _ptr(S),
+                                      threads), "oracle_scores")
+        return S[: int(rp[-1])]
+
+    def diffuse(self, A, V, row_ptr, col_idx, K_steps, alpha, threads=1):
+        A = np.ascontiguousarray(A, dtype=np.float64)
+        V = np.ascontiguousarray(V, dtype=np.float64)
+        rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+        ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+        n, d = V.shape
+        if A.size == 0:
+            A = np.zeros(1)
+        Z = np.zeros_like(V)
+        _check(self.lib.oracle_diffuse(_ptr(A), _ptr(V), n, d, _ptr(rp), _ptr(ci), K_steps,
+                                       float(alpha), _ptr(Z), threads), "oracle_diffuse")
+        return Z
+
+    def attn(self, Q, K, V, row_ptr, col_idx, K_steps, alpha, threads=1):
+        """Whole path for one (batch, head): scores, softmax, K diffusion steps."""
+        A = self.scores_softmax(Q, K, row_ptr, col_idx, threads)
+        return self.diffuse(A, V, row_ptr, col_idx, K_steps, alpha, threads)

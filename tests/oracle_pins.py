@@ -1,0 +1,384 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Every check here compares the oracle with something it does not compute:
+values printed on the pages (``tests/golden``), closed forms, invariants the
+mathematics fixes, a textbook dense routine, or brute force on tiny inputs.
+Each function takes an ``oracle.Oracle`` and raises AssertionError on a
+mismatch, so the same checks run against the real oracle
+(``test_oracle_pins.py``) and against deliberately broken builds of it
+(``test_oracle_mutants.py``).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def golden_dict(name):
+    return {r[0]: r[1:] for r in read_golden(name)}
+
+
+# --------------------------------------------------------------------------
+# Set definitions written out directly (window eq. 5, globals eq. 12).
+# --------------------------------------------------------------------------
+
+def window_set(n, r, i):
+    return set(range(max(0, i - r), min(n - 1, i + r) + 1))
+
+
+def csr_rows(row_ptr, cols):
+    return [cols[row_ptr[i]:row_ptr[i + 1]] for i in range(len(row_ptr) - 1)]
+
+
+# --------------------------------------------------------------------------
+# Random draws
+# --------------------------------------------------------------------------
+
+def pin_splitmix64(o):
+    """Draw t of row 0, graph 0 is SplitMix64(seed=0)'s output t+1."""
+    want = [int(r[0], 16) for r in read_golden("splitmix64_seed0.txt")]
+    got = [o.draw(0, 0, 1, 0, t) for t in range(3)]
+    assert got == want, (got, want)
+
+
+# --------------------------------------------------------------------------
+# Graph pins
+# --------------------------------------------------------------------------
+
+def pin_edge_counts_8pos(o):
+    for n, r, gl, edges in read_golden("edge_counts_8pos.txt"):
+        g = [] if gl == "-" else [int(x) for x in gl.split(",")]
+        rp, _ = o.graph(int(n), int(r), g, 0)
+        assert int(rp[0, -1]) == int(edges), (n, r, gl, int(rp[0, -1]), edges)
+
+
+def pin_window_closed_form(o):
+    """|E_local| = n(2r+1) - r(r+1) for n >= 2r+1; r >= n-1 gives n^2."""
+    for n in (1, 2, 3, 5, 8, 13, 40, 97):
+        for r in (0, 1, 2, 3, 7, 20, 48):
+            rp, _ = o.graph(n, r, [], 0)
+            nnz = int(rp[0, -1])
+            if n >= 2 * r + 1:
+                assert nnz == n * (2 * r + 1) - r * (r + 1), (n, r, nnz)
+            if r >= n - 1:
+                assert nnz == n * n, (n, r, nnz)
+
+
+def _degree_formula(n, r, G, R, i):
+    """Degree of row i from set sizes: n for a global row, else
+    |W(i)| + |G minus W(i)| + min(R, n - |W(i) u G|)."""
+    if i in G:
+        return n
+    w = window_set(n, r, i)
+    gx = len(G - w)
+    pool = n - len(w) - gx
+    return len(w) + gx + min(R, pool)
+
+
+def pin_degrees(o, cases=None):
+    if cases is None:
+        cases = [
+            (64, 3, [0, 17, 63], 5, 2),
+            (100, 10, [5, 6, 7, 50], 30, 1),
+            (37, 4, [], 40, 1),          # pool smaller than the budget
+            (50, 0, [10], 49, 1),        # r = 0, budget above the pool
+            (300, 16, [0, 150], 8, 3),
+        ]
+    for n, r, G, R, ng in cases:
+        rp, _ = o.graph(n, r, G, R, ng, False, 7)
+        Gs = set(G)
+        for gr in range(ng):
+            deg = np.diff(rp[gr])
+            want = np.array([_degree_formula(n, r, Gs, R, i) for i in range(n)])
+            assert np.array_equal(deg, want), (n, r, G, R, gr)
+
+
+def pin_row_structure(o):
+    """Rows ascending without duplicates; self, window and globals present;
+    random extras outside window and globals; causal graph is the
+    bidirectional graph filtered to j <= i; seeds and graphs differ."""
+    n, r, G, R = 200, 5, [0, 3, 99, 150], 12
+    Gs = set(G)
+    rp, cols = o.graph(n, r, G, R, 2, False, 11)
+    rpc, colsc = o.graph(n, r, G, R, 2, True, 11)
+    for gr in range(2):
+        rows = csr_rows(rp[gr], cols[gr])
+        rowsc = csr_rows(rpc[gr], colsc[gr])
+        for i, row in enumerate(rows):
+            assert np.all(np.diff(row) > 0), i
+            s = set(row.tolist())
+            assert i in s
+            if i in Gs:
+                assert s == set(range(n))
+            else:
+                assert window_set(n, r, i) <= s and Gs <= s
+                extra = s - window_set(n, r, i) - Gs
+                assert i not in extra and len(extra) == R
+            want_c = sorted(j for j in s if j <= i)
+            assert rowsc[i].tolist() == want_c, i
+    # determinism and variation
+    rp2, cols2 = o.graph(n, r, G, R, 2, False, 11)
+    assert all(np.array_equal(a, b) for a, b in zip(cols, cols2))
+    assert not np.array_equal(cols[0], cols[1])           # per-graph draws differ
+    _, cols3 = o.graph(n, r, G, R, 1, False, 12)
+    assert not np.array_equal(cols[0], cols3[0])           # per-seed draws differ
+
+
+def pin_random_uniform(o):
+    """Random extras are uniform over the pool: chi-square over column
+    position for a window-free, global-free graph (pool = all j != i)."""
+    n, R = 64, 8
+    counts = np.zeros(n)
+    ng = 200
+    rp, cols = o.graph(n, 0, [], R, ng, False, 5)
+    for gr in range(ng):
+        for i, row in enumerate(csr_rows(rp[gr], cols[gr])):
+            for j in row:
+                if j != i:
+                    counts[j] += 1
+    expected = ng * R  # each column is in n-1 pools, chosen w.p. R/(n-1)
+    chi2 = float(((counts - expected) ** 2 / expected).sum())
+    # 63 degrees of freedom: the 1e-6 tail is far above 140
+    assert chi2 < 140.0, chi2
+
+
+# --------------------------------------------------------------------------
+# Softmax pins
+# --------------------------------------------------------------------------
+
+def pin_softmax_8pos(o):
+    g = golden_dict("softmax_8pos.txt")
+    rp, cols = o.graph(8, 1, [], 0)
+    rp, cols = rp[0], cols[0]
+    w = np.array([float(x) for x in g["weights"]])
+    for d in (1, 4):
+        # score ln2 on the self edge of position 4 (index 3), 0 on its neighbours
+        Q = np.zeros((8, d)); K = np.zeros((8, d))
+        Q[3, 0] = math.sqrt(d)
+        K[3, 0] = float(g["scores"][1])
+        A = o.scores_softmax(Q, K, rp, cols)
+        row = A[rp[3]:rp[4]]
+        assert cols[rp[3]:rp[4]].tolist() == [2, 3, 4]
+        assert np.allclose(row, w, rtol=0, atol=1e-15), (d, row)
+    V = np.zeros((8, 2))
+    V[2] = [float(x) for x in g["v3"]]
+    V[3] = [float(x) for x in g["v4"]]
+    V[4] = [float(x) for x in g["v5"]]
+    Z = o.diffuse(A, V, rp, cols, 1, 0.0)
+    assert np.allclose(Z[3], [float(x) for x in g["o4"]], rtol=0, atol=1e-15), Z[3]
+
+
+def pin_row_sums(o):
+    rng = np.random.default_rng(3)
+    n, d = 150, 8
+    rp, cols = o.graph(n, 4, [0, 75], 6, 1, False, 3)
+    Q = rng.normal(size=(n, d)) * 3
+    K = rng.normal(size=(n, d)) * 3
+    A = o.scores_softmax(Q, K, rp[0], cols[0])
+    sums = np.add.reduceat(A, rp[0][:-1])
+    assert np.all(A > 0) and np.allclose(sums, 1.0, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Diffusion pins
+# --------------------------------------------------------------------------
+
+def pin_three_token(o):
+    g = golden_dict("diffusion_3token.txt")
+    A_dense = np.array([[float(x) for x in g[f"A_row{i}"]] for i in range(3)])
+    rp = np.array([0, 2, 4, 5], dtype=np.int64)
+    cols = np.array([0, 1, 1, 2, 2], dtype=np.int32)
+    A = np.array([A_dense[i, j] for i in range(3) for j in cols[rp[i]:rp[i + 1]]])
+    Z = o.diffuse(A, np.eye(3), rp, cols, int(g["K"][0]), float(g["alpha"][0]))
+    want = [float(x) for x in g["Z2_row0_coeffs"]]
+    assert np.allclose(Z[0], want, rtol=0, atol=1e-15), Z[0]
+
+
+def pin_expansion_coefficients(o):
+    """With A a cyclic shift, A^k e_0 are distinct unit vectors, so row 0 of
+    Z_K for V = I lists the coefficient of each power A^k directly."""
+    g = golden_dict("ppr_coeffs_k5.txt")
+    K, alpha = int(g["K"][0]), float(g["alpha"][0])
+    n = K + 2
+    rp = np.arange(n + 1, dtype=np.int64)
+    cols = ((np.arange(n) + 1) % n).astype(np.int32)      # A[i, i+1] = 1
+    Z = o.diffuse(np.ones(n), np.eye(n), rp, cols, K, alpha)
+    want = [float(x) for x in g["coeffs"]] + [0.0] * (n - K - 1)
+    assert np.allclose(Z[0], want, rtol=0, atol=1e-15), Z[0]
+    assert abs(sum(want) - 1.0) < 1e-15
+
+
+def _dense_A(rp, cols, vals, n):
+    A = np.zeros((n, n))
+    for i in range(n):
+        A[i, cols[rp[i]:rp[i + 1]]] = vals[rp[i]:rp[i + 1]]
+    return A
+
+
+def pin_finite_expansion(o):
+    """Z_K = [(1-a)^K A^K + a sum_{i<K} (1-a)^i A^i] V by dense matrix powers."""
+    rng = np.random.default_rng(9)
+    n, d = 40, 5
+    rp, cols = o.graph(n, 2, [7], 3, 1, False, 9)
+    rp, cols = rp[0], cols[0]
+    Q, Kx, V = (rng.normal(size=(n, d)) for _ in range(3))
+    A = o.scores_softmax(Q, Kx, rp, cols)
+    Ad = _dense_A(rp, cols, A, n)
+    for K in (0, 1, 2, 5, 9):
+        for alpha in (0.0, 0.05, 0.1, 0.3, 1.0):
+            M = (1 - alpha) ** K * np.linalg.matrix_power(Ad, K)
+            for i in range(K):
+                M = M + alpha * (1 - alpha) ** i * np.linalg.matrix_power(Ad, i)
+            Z = o.diffuse(A, V, rp, cols, K, alpha)
+            assert np.allclose(Z, M @ V, rtol=0, atol=1e-12), (K, alpha)
+
+
+def pin_dense_brute_force(o):
+    """Dense masked softmax (mask 0 / -inf, eqs. 2-4) plus dense diffusion on
+    tiny n; the mask comes from the set definitions, the random columns
+    from the CSR's entries outside window and globals."""
+    rng = np.random.default_rng(21)
+    for n, r, G, R, causal in [(16, 1, [3], 2, False), (33, 3, [0, 32], 4, False),
+                               (24, 2, [5, 11], 3, True), (9, 0, [], 0, False),
+                               (12, 20, [], 0, True)]:
+        d = 6
+        rp, cols = o.graph(n, r, G, R, 1, causal, 4)
+        rp, cols = rp[0], cols[0]
+        allowed = np.zeros((n, n), dtype=bool)
+        for i in range(n):
+            if i in G:
+                allowed[i, :] = True
+            else:
+                allowed[i, list(window_set(n, r, i))] = True
+                allowed[i, G] = True
+                row = set(cols[rp[i]:rp[i + 1]].tolist())
+                rnd = row - window_set(n, r, i) - set(G)
+                allowed[i, sorted(rnd)] = True
+            if causal:
+                allowed[i, i + 1:] = False
+        # the oracle's structure must equal the mask (random part is its own)
+        got = np.zeros((n, n), dtype=bool)
+        for i in range(n):
+            got[i, cols[rp[i]:rp[i + 1]]] = True
+        assert np.array_equal(got, allowed), (n, r, G, R, causal)
+        Q, Kx, V = (rng.normal(size=(n, d)) for _ in range(3))
+        S = Q @ Kx.T / math.sqrt(d) + np.where(allowed, 0.0, -np.inf)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        A = o.scores_softmax(Q, Kx, rp, cols)
+        assert np.allclose(_dense_A(rp, cols, A, n), P, rtol=0, atol=1e-14)
+        K, alpha = 4, 0.2
+        Z = V.copy()
+        for _ in range(K):
+            Z = (1 - alpha) * P @ Z + alpha * V
+        assert np.allclose(o.diffuse(A, V, rp, cols, K, alpha), Z, rtol=0, atol=1e-12)
+
+
+def pin_softmax_attention_reduction(o):
+    """Complete graph, alpha = 0, K = 1 is ordinary softmax attention; alpha = 1
+    or K = 0 returns V exactly."""
+    rng = np.random.default_rng(5)
+    n, d = 30, 8
+    rp, cols = o.graph(n, n, [], 0)
+    Q, Kx, V = (rng.normal(size=(n, d)) for _ in range(3))
+    S = Q @ Kx.T / math.sqrt(d)
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    A = o.scores_softmax(Q, Kx, rp[0], cols[0])
+    assert np.allclose(o.diffuse(A, V, rp[0], cols[0], 1, 0.0), P @ V, rtol=0, atol=1e-13)
+    assert np.array_equal(o.diffuse(A, V, rp[0], cols[0], 0, 0.1), V)
+    assert np.array_equal(o.diffuse(A, V, rp[0], cols[0], 6, 1.0), V)
+
+
+def pin_infinite_limit(o):
+    """||Z_K - a (I - (1-a) A)^-1 V||_inf <= 2 (1-a)^K ||V||_inf, and Z_K reaches
+    the linear-solve limit for large K."""
+    rng = np.random.default_rng(13)
+    n, d = 25, 4
+    rp, cols = o.graph(n, 2, [12], 3, 1, False, 8)
+    rp, cols = rp[0], cols[0]
+    Q, Kx, V = (rng.normal(size=(n, d)) for _ in range(3))
+    A = o.scores_softmax(Q, Kx, rp, cols)
+    Ad = _dense_A(rp, cols, A, n)
+    for alpha in (0.05, 0.1, 0.3):
+        Zinf = alpha * np.linalg.solve(np.eye(n) - (1 - alpha) * Ad, V)
+        for K in (1, 3, 5, 10):
+            err = np.abs(o.diffuse(A, V, rp, cols, K, alpha) - Zinf).max()
+            assert err <= 2 * (1 - alpha) ** K * np.abs(V).max() + 1e-12, (alpha, K, err)
+        Z = o.diffuse(A, V, rp, cols, 600, alpha)
+        assert np.allclose(Z, Zinf, rtol=0, atol=1e-9), alpha
+
+
+def _perturbation_dependence(o, n, r, G, R, causal, K, alpha, p, seed=2):
+    rng = np.random.default_rng(seed)
+    d = 3
+    rp, cols = o.graph(n, r, G, R, 1, causal, 6)
+    rp, cols = rp[0], cols[0]
+    Q, Kx, V = (rng.normal(size=(n, d)) for _ in range(3))
+    A = o.scores_softmax(Q, Kx, rp, cols)
+    Z0 = o.diffuse(A, V, rp, cols, K, alpha)
+    V2 = V.copy()
+    V2[p] += 1.0
+    Z1 = o.diffuse(A, V2, rp, cols, K, alpha)
+    return np.any(Z0 != Z1, axis=1)
+
+
+def pin_causality(o):
+    """Causal graph: changing V[p] leaves Z[i < p] bitwise unchanged."""
+    for p in (0, 10, 31, 59):
+        changed = _perturbation_dependence(o, 60, 3, [0, 20, 40], 4, True, 5, 0.1, p)
+        assert not changed[:p].any(), p
+        assert changed[p]
+
+
+def pin_reach(o):
+    """Window-only graph: Z[i] depends on V[p] iff |i - p| <= K r."""
+    n, r, K, p = 80, 3, 4, 40
+    changed = _perturbation_dependence(o, n, r, [], 0, False, K, 0.1, p)
+    idx = np.arange(n)
+    assert np.array_equal(changed, np.abs(idx - p) <= K * r), np.nonzero(changed)
+
+
+def pin_two_hop_global(o):
+    """Non-causal graph with a global token and K >= 2: every output depends
+    on every input row; with K = 1 a far token does not."""
+    n = 50
+    for p in (3, 25, 49):
+        assert _perturbation_dependence(o, n, 1, [20], 0, False, 2, 0.1, p).all(), p
+    changed = _perturbation_dependence(o, n, 1, [20], 0, False, 1, 0.1, 45)
+    assert not changed[0]
+
+
+def pin_constant_fixed_point(o):
+    """Constant V (every row the same) is a fixed point: Z_k = V."""
+    rng = np.random.default_rng(17)
+    n, d = 70, 4
+    rp, cols = o.graph(n, 5, [0, 69], 7, 1, False, 1)
+    Q, Kx = rng.normal(size=(n, d)), rng.normal(size=(n, d))
+    A = o.scores_softmax(Q, Kx, rp[0], cols[0])
+    V = np.tile(rng.normal(size=(1, d)), (n, 1))
+    Z = o.diffuse(A, V, rp[0], cols[0], 7, 0.1)
+    assert np.allclose(Z, V, rtol=0, atol=1e-13)
+
+
+ALL_PINS = [
+    pin_splitmix64, pin_edge_counts_8pos, pin_window_closed_form, pin_degrees,
+    pin_row_structure, pin_random_uniform, pin_softmax_8pos, pin_row_sums,
+    pin_three_token, pin_expansion_coefficients, pin_finite_expansion,
+    pin_dense_brute_force, pin_softmax_attention_reduction, pin_infinite_limit,
+    pin_causality, pin_reach, pin_two_hop_global, pin_constant_fixed_point,
+]

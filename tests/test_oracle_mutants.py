@@ -1,0 +1,74 @@
+"""Plants plausible mistakes in copies of the oracle's C source (on the CPU,
+in a temporary directory) and checks that at least one pin catches each.
+
+This shows the pins are strong enough: a dropped term, a wrong sign or index,
+an off-by-one window, a missing de-duplication or a wrong scale all fail.
+"""
+import os
+import shutil
+
+import pytest
+
+import oracle
+import oracle_pins
+
+ORACLE_DIR = os.path.dirname(oracle.SRC_PATH)
+
+# (name, original text, planted text); each original must occur in oracle.c.
+MUTANTS = [
+    ("drop_restart", "out[ch] = (1.0 - c->alpha) * out[ch] + c->alpha * v[ch];",
+     "out[ch] = (1.0 - c->alpha) * out[ch];"),
+    ("restart_sign", "out[ch] = (1.0 - c->alpha) * out[ch] + c->alpha * v[ch];",
+     "out[ch] = (1.0 + c->alpha) * out[ch] - c->alpha * v[ch];"),
+    ("gather_own_row", "const double* z = c->Zk + (int64_t)c->col_idx[e] * c->d;",
+     "const double* z = c->Zk + i * c->d;"),
+    ("gather_from_v", "const double* z = c->Zk + (int64_t)c->col_idx[e] * c->d;",
+     "const double* z = c->V + (int64_t)c->col_idx[e] * c->d;"),
+    ("k_off_by_one", "for (int32_t k = 0; k < K_steps; ++k) {",
+     "for (int32_t k = 0; k <= K_steps; ++k) {"),
+    ("window_short_left", "int64_t lo = i - s->radius < 0 ? 0 : i - s->radius;",
+     "int64_t lo = i - s->radius + 1 < 0 ? 0 : i - s->radius + 1;"),
+    ("no_global_columns",
+     "for (int32_t k = 0; k < s->num_global; ++k) member[s->global_idx[k]] = 1;",
+     "(void)0;"),
+    ("global_rows_half", "memset(member, 1, (size_t)n);",
+     "memset(member, 1, (size_t)n / 2);"),
+    ("random_may_repeat_window", "if (member[j] == 0) {\n            member[j] = 2;",
+     "if (member[j] != 2) {\n            member[j] = 2;"),
+    ("causal_strict", "int64_t last = s->causal ? i : s->n - 1;",
+     "int64_t last = s->causal ? i - 1 : s->n - 1;"),
+    ("scale_by_d", "const double scale = 1.0 / sqrt((double)c->d);",
+     "const double scale = 1.0 / (double)c->d;"),
+    ("no_scale", "const double scale = 1.0 / sqrt((double)c->d);",
+     "const double scale = 1.0;"),
+    ("unnormalised", "for (int64_t e = e0; e < e1; ++e) c->out[e] /= sum;",
+     "for (int64_t e = e0; e < e1; ++e) c->out[e] /= sum + 1.0;"),
+    ("dot_q_q", "dot += q[ch] * k[ch];", "dot += q[ch] * q[ch];"),
+    ("draw_counter_no_plus_one", "0x9E3779B97F4A7C15ull * (ctr + 1ull)",
+     "0x9E3779B97F4A7C15ull * ctr"),
+    ("mix_shift", "z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;",
+     "z = (z ^ (z >> 26)) * 0x94D049BB133111EBull;"),
+]
+
+
+def _caught(o):
+    failures = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(o)
+        except Exception as exc:  # AssertionError, OracleError, numpy errors
+            failures.append((pin.__name__, type(exc).__name__))
+    return failures
+
+
+@pytest.mark.parametrize("name,orig,planted", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, orig, planted):
+    src = open(oracle.SRC_PATH).read()
+    assert src.count(orig) >= 1, f"mutation site for {name} not found"
+    shutil.copy(os.path.join(ORACLE_DIR, "oracle.h"), tmp_path / "oracle.h")
+    mut_src = tmp_path / "oracle.c"
+    mut_src.write_text(src.replace(orig, planted))
+    lib = tmp_path / f"lib_{name}.so"
+    oracle.build(out_path=str(lib), src_path=str(mut_src))
+    o = oracle.Oracle(oracle.load(str(lib)))
+    assert _caught(o), f"planted mistake {name} passed every pin"
