@@ -1,0 +1,174 @@
+/*
+ * diffuser.h -- C ABI of the MI355X (gfx950) Diffuser attention-diffusion
+ * library.
+ *
+ * The library computes, on one GPU, the Diffuser hot path:
+ *   1. a static sparse token graph: a local window of radius r, g global
+ *      positions with full rows and columns, and up to R random extra keys
+ *      per token ("Diffuser" reading notes, section 2.2 connection table;
+ *      "1.2.1 Static sparsity", section 1.1 eq. 5 and section 1.2 eq. 12;
+ *      "038 BigBird", section 2, union neighbourhood S_i = W_i u R_i u G);
+ *   2. edge scores s_ij = q_i . k_j / sqrt(d_h) on graph edges only and a
+ *      softmax over each row's neighbour set into A ("Diffuser" notes,
+ *      section 2.1, eqs. S.1-S.5; "1.2.1", section 1, eqs. 1-3);
+ *   3. K personalized-PageRank steps Z_0 = V,
+ *      Z_{k+1} = (1 - alpha) A Z_k + alpha V, 0 <= k < K, reusing the same
+ *      A in every step ("Diffuser" notes, section 2.4, eq. S.7).
+ *
+ * General conventions
+ *  - Every entry point returns a diffuser_status. Nothing is thrown, no
+ *    entry point aborts or exits. On a non-OK status,
+ *    diffuser_last_error() returns a thread-local message.
+ *  - Arguments are validated synchronously, before any GPU work is
+ *    enqueued; an invalid call has no side effects.
+ *  - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *    Compute entry points only enqueue work on it; kernel faults surface at
+ *    the caller's next synchronisation. Launch failures are reported as
+ *    DIFFUSER_ERR_HIP.
+ *  - Device pointers are plain device addresses owned by the caller unless
+ *    stated otherwise; tensors are dense and row-major.
+ *  - Floating-point storage is fp32 or bf16 (round-to-nearest-even); all
+ *    accumulation is fp32.
+ */
+#ifndef DIFFUSER_H
+#define DIFFUSER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define DIFFUSER_API __attribute__((visibility("default")))
+#else
+#define DIFFUSER_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DIFFUSER_OK = 0,
+    DIFFUSER_ERR_INVALID_ARG = 1,   /* bad size, pointer, alignment, range */
+    DIFFUSER_ERR_UNSUPPORTED = 2,   /* valid but not implemented (d, dtype) */
+    DIFFUSER_ERR_OUT_OF_MEMORY = 3, /* device allocation failed (build only) */
+    DIFFUSER_ERR_HIP = 4,           /* a HIP runtime call or launch failed */
+    DIFFUSER_ERR_INTERNAL = 5       /* e.g. random-draw budget exhausted */
+} diffuser_status;
+
+typedef enum { DIFFUSER_F32 = 0, DIFFUSER_BF16 = 1 } diffuser_dtype;
+
+/*
+ * Graph descriptor ("Diffuser" notes, section 2.2; "1.2.1", eqs. 5 and 12;
+ * "038 BigBird", section 2). For each graph b < num_graphs and row i < n:
+ *  - i global:   N(i) = {0, ..., n-1};
+ *  - otherwise:  N(i) = W(i) u G u Rnd(i), W(i) = [max(0, i-r), min(n-1, i+r)],
+ *    Rnd(i) = min(R, P) distinct positions drawn uniformly from the pool
+ *    {0..n-1} minus (W(i) u G) of size P (the whole pool when P <= R);
+ *  - causal:     afterwards keep only j <= i (the draws are made on the
+ *    bidirectional pool, so the causal graph is a subgraph of it).
+ * The draws: u_t = SplitMix64 output number (c + 1) of a generator seeded
+ * with `seed`, where c = ((b*n + i) << 20) | t; the candidate is
+ * j = ((u_t >> 32) * n) >> 32; a candidate is accepted when it is in the
+ * pool and not yet taken; t runs 0, 1, ... below 2^20 (else
+ * DIFFUSER_ERR_INTERNAL).
+ * Rows are stored in CSR with strictly ascending columns; every row holds
+ * its own index (self edge).
+ */
+typedef struct {
+    int64_t n;                 /* tokens, 1 <= n <= 2^24 */
+    int32_t window_radius;     /* r >= 0 */
+    int32_t num_global;        /* g, 0 <= g <= n */
+    const int32_t* global_idx; /* HOST pointer, g strictly increasing in [0, n) */
+    int32_t num_random;        /* R >= 0; R <= 1024 unless every pool <= R */
+    int32_t num_graphs;        /* >= 1; graph of batch element b is b when
+                                  num_graphs == B, else graph 0 */
+    int32_t causal;            /* 0 or 1 */
+    uint64_t seed;
+} diffuser_graph_desc;
+
+/* Opaque, library-owned, immutable after build. Holds device CSR
+ * (row_ptr int64[num_graphs][n+1], col_idx int32[sum of nnz]) and per-row
+ * metadata. */
+typedef struct diffuser_graph diffuser_graph;
+
+/* Builds the graphs on the current HIP device. The call synchronises
+ * `stream` before returning; the graph may then be used on any stream of
+ * that device. *out receives the handle (unchanged on error). */
+DIFFUSER_API diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stream,
+                                     diffuser_graph** out);
+
+/* Imports caller-given CSR graphs (HOST arrays): row_ptr int64
+ * [num_graphs][n+1] with each graph's row_ptr starting at 0, col_idx int32
+ * = the graphs' columns concatenated. Each row must be strictly ascending,
+ * in [0, n), and contain its own index. Used for arbitrary layouts (no
+ * window metadata); synchronous like diffuser_build_graph. */
+DIFFUSER_API diffuser_status diffuser_graph_from_csr(int64_t n, int32_t num_graphs, const int64_t* row_ptr_host,
+                                        const int32_t* col_idx_host, void* stream,
+                                        diffuser_graph** out);
+
+/* n, num_graphs and (if nnz != NULL) nnz[num_graphs] edges per graph. Any
+ * output pointer may be NULL. */
+DIFFUSER_API diffuser_status diffuser_graph_info(const diffuser_graph* g, int64_t* n, int32_t* num_graphs,
+                                    int64_t* nnz);
+
+/* Copies graph `graph` to HOST arrays row_ptr[n+1] and col_idx[nnz];
+ * synchronous on return. */
+DIFFUSER_API diffuser_status diffuser_graph_copy_csr(const diffuser_graph* g, int32_t graph,
+                                        int64_t* row_ptr_host, int32_t* col_idx_host,
+                                        void* stream);
+
+/* Frees the graph (waits for the device first). Accepts NULL. */
+DIFFUSER_API void diffuser_graph_destroy(diffuser_graph* g);
+
+/* Size in bytes of the workspace diffuser_attn needs (A plus one Z buffer,
+ * each 256-byte aligned). diffuser_diffuse needs only the Z buffer part and
+ * diffuser_scores_softmax none; the same size is accepted by all three. */
+DIFFUSER_API diffuser_status diffuser_attn_workspace_size(const diffuser_graph* g, int32_t B, int32_t H,
+                                             int32_t d_h, int32_t d_v, diffuser_dtype dtype,
+                                             size_t* bytes);
+
+/*
+ * Layouts shared by the compute entry points:
+ *  Q, K : [B][H][n][d_h];  V, Z : [B][H][n][d_v];  all of `dtype`.
+ *  A    : edge weights in CSR order, concatenated over (b, h) in row-major
+ *         (b, h) order; the block of (b, h) holds nnz(graph(b)) values and
+ *         starts at sum_{b' < b} H * nnz(graph(b')) + h * nnz(graph(b)).
+ * Supported: d_h, d_v in {16, 32, 64, 128}; pointers 16-byte aligned
+ * (A: element aligned); Z must not overlap Q, K, V, A or the workspace.
+ */
+
+/* Whole path: scores and edge softmax into A (in the workspace), then
+ * K_steps diffusion steps; writes Z = Z_K. K_steps >= 0 (0 copies V),
+ * 0 <= alpha <= 1. No allocation is made. */
+DIFFUSER_API diffuser_status diffuser_attn(const void* Q, const void* K, const void* V, diffuser_dtype dtype,
+                              int32_t B, int32_t H, int32_t d_h, int32_t d_v,
+                              const diffuser_graph* g, int32_t K_steps, float alpha, void* Z,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* Stage 1 alone ("Diffuser" notes, section 2.1, eqs. S.1-S.5): A_out gets
+ * the edge-softmax weights in the A layout above. */
+DIFFUSER_API diffuser_status diffuser_scores_softmax(const void* Q, const void* K, diffuser_dtype dtype,
+                                        int32_t B, int32_t H, int32_t d_h,
+                                        const diffuser_graph* g, void* A_out, void* workspace,
+                                        size_t ws_bytes, void* stream);
+
+/* Stage 2 alone ("Diffuser" notes, section 2.4, eq. S.7): K_steps
+ * diffusion steps with caller-given edge weights A (A layout above; rows
+ * need not sum to one). */
+DIFFUSER_API diffuser_status diffuser_diffuse(const void* A, const void* V, diffuser_dtype dtype, int32_t B,
+                                 int32_t H, int32_t d_v, const diffuser_graph* g,
+                                 int32_t K_steps, float alpha, void* Z, void* workspace,
+                                 size_t ws_bytes, void* stream);
+
+/* Static string for a status code. */
+DIFFUSER_API const char* diffuser_status_string(diffuser_status s);
+
+/* Thread-local message describing the last non-OK status returned on this
+ * thread ("" if none). */
+DIFFUSER_API const char* diffuser_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFUSER_H */

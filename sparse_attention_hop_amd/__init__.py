@@ -1,0 +1,286 @@
+"""MI355X (gfx950) Diffuser attention-diffusion path: Python binding.
+
+Argument marshalling only: every step of the path runs in the HIP library
+``libdiffuser.so`` (C ABI declared in ``include/diffuser.h``), reached through
+ctypes. PyTorch supplies device memory and the current stream. There is no
+fallback: if the library is missing, every call raises.
+
+Functions mirror the C ABI names:
+  build_graph     -> diffuser_build_graph
+  graph_from_csr  -> diffuser_graph_from_csr
+  workspace_size  -> diffuser_attn_workspace_size
+  attn            -> diffuser_attn
+  scores_softmax  -> diffuser_scores_softmax
+  diffuse         -> diffuser_diffuse
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdiffuser.so")
+
+F32, BF16 = 0, 1
+
+STATUS_NAMES = {
+    0: "DIFFUSER_OK", 1: "DIFFUSER_ERR_INVALID_ARG", 2: "DIFFUSER_ERR_UNSUPPORTED",
+    3: "DIFFUSER_ERR_OUT_OF_MEMORY", 4: "DIFFUSER_ERR_HIP", 5: "DIFFUSER_ERR_INTERNAL",
+}
+
+# Every symbol the header declares.
+ABI_SYMBOLS = (
+    "diffuser_build_graph", "diffuser_graph_from_csr", "diffuser_graph_info",
+    "diffuser_graph_copy_csr", "diffuser_graph_destroy", "diffuser_attn_workspace_size",
+    "diffuser_attn", "diffuser_scores_softmax", "diffuser_diffuse",
+    "diffuser_status_string", "diffuser_last_error",
+)
+
+
+class DiffuserError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+class _GraphDesc(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int64),
+        ("window_radius", ctypes.c_int32),
+        ("num_global", ctypes.c_int32),
+        ("global_idx", ctypes.c_void_p),
+        ("num_random", ctypes.c_int32),
+        ("num_graphs", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libdiffuser.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library {path} is missing: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    i32, i64, u64, p, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t
+    st = ctypes.c_int
+    lib.diffuser_build_graph.argtypes = [ctypes.POINTER(_GraphDesc), p, ctypes.POINTER(p)]
+    lib.diffuser_build_graph.restype = st
+    lib.diffuser_graph_from_csr.argtypes = [i64, i32, p, p, p, ctypes.POINTER(p)]
+    lib.diffuser_graph_from_csr.restype = st
+    lib.diffuser_graph_info.argtypes = [p, p, p, p]
+    lib.diffuser_graph_info.restype = st
+    lib.diffuser_graph_copy_csr.argtypes = [p, i32, p, p, p]
+    lib.diffuser_graph_copy_csr.restype = st
+    lib.diffuser_graph_destroy.argtypes = [p]
+    lib.diffuser_graph_destroy.restype = None
+    lib.diffuser_attn_workspace_size.argtypes = [p, i32, i32, i32, i32, st, ctypes.POINTER(sz)]
+    lib.diffuser_attn_workspace_size.restype = st
+    lib.diffuser_attn.argtypes = [p, p, p, st, i32, i32, i32, i32, p, i32, ctypes.c_float, p, p,
+                                  sz, p]
+    lib.diffuser_attn.restype = st
+    lib.diffuser_scores_softmax.argtypes = [p, p, st, i32, i32, i32, p, p, p, sz, p]
+    lib.diffuser_scores_softmax.restype = st
+    lib.diffuser_diffuse.argtypes = [p, p, st, i32, i32, i32, p, i32, ctypes.c_float, p, p, sz, p]
+    lib.diffuser_diffuse.restype = st
+    lib.diffuser_status_string.argtypes = [st]
+    lib.diffuser_status_string.restype = ctypes.c_char_p
+    lib.diffuser_last_error.argtypes = []
+    lib.diffuser_last_error.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().diffuser_last_error().decode(errors="replace")
+        raise DiffuserError(status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(device=None) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise DiffuserError(2, f"dtype {t} is not supported (float32 or bfloat16)")
+
+
+class Graph:
+    """Owns a diffuser_graph handle; freed with diffuser_graph_destroy."""
+
+    def __init__(self, handle: int, desc: Optional[dict] = None):
+        self._lib = load_library()
+        self.handle = ctypes.c_void_p(handle)
+        n = ctypes.c_int64()
+        ng = ctypes.c_int32()
+        _check(self._lib.diffuser_graph_info(self.handle, ctypes.byref(n), ctypes.byref(ng), None))
+        self.n, self.num_graphs = int(n.value), int(ng.value)
+        nnz = np.zeros(self.num_graphs, dtype=np.int64)
+        _check(self._lib.diffuser_graph_info(self.handle, None, None,
+                                             nnz.ctypes.data_as(ctypes.c_void_p)))
+        self.nnz = [int(x) for x in nnz]
+        self.desc = desc
+
+    def copy_csr(self, graph: int = 0):
+        """(row_ptr int64[n+1], col_idx int32[nnz]) of one graph, on the host."""
+        rp = np.zeros(self.n + 1, dtype=np.int64)
+        ci = np.zeros(max(self.nnz[graph], 1), dtype=np.int32)
+        _check(self._lib.diffuser_graph_copy_csr(self.handle, graph,
+                                                 rp.ctypes.data_as(ctypes.c_void_p),
+                                                 ci.ctypes.data_as(ctypes.c_void_p),
+                                                 ctypes.c_void_p(_stream_handle())))
+        return rp, ci[: self.nnz[graph]]
+
+    def a_numel(self, B: int, H: int) -> int:
+        if self.num_graphs == 1:
+            return B * H * self.nnz[0]
+        return H * sum(self.nnz)
+
+    def a_offset(self, b: int, h: int, H: int) -> int:
+        """Start of the (b, h) block inside the A layout."""
+        if self.num_graphs == 1:
+            return (b * H + h) * self.nnz[0]
+        return H * sum(self.nnz[:b]) + h * self.nnz[b]
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            self._lib.diffuser_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def build_graph(n: int, radius: int, global_idx: Sequence[int], num_random: int,
+                num_graphs: int = 1, causal: bool = False, seed: int = 0) -> Graph:
+    lib = load_library()
+    g = np.ascontiguousarray(np.asarray(list(global_idx), dtype=np.int32))
+    desc = _GraphDesc(n, radius, g.size, g.ctypes.data if g.size else None, num_random,
+                      num_graphs, int(bool(causal)), seed)
+    out = ctypes.c_void_p()
+    _check(lib.diffuser_build_graph(ctypes.byref(desc), ctypes.c_void_p(_stream_handle()),
+                                    ctypes.byref(out)))
+    return Graph(out.value, dict(n=n, radius=radius, global_idx=tuple(g.tolist()),
+                                 num_random=num_random, num_graphs=num_graphs,
+                                 causal=bool(causal), seed=seed))
+
+
+def graph_from_csr(n: int, row_ptr, col_idx) -> Graph:
+    """row_ptr: int64 [num_graphs, n+1] (each from 0); col_idx: the graphs'
+    columns concatenated (or a list of per-graph arrays)."""
+    lib = load_library()
+    rp = np.ascontiguousarray(np.atleast_2d(np.asarray(row_ptr, dtype=np.int64)))
+    if isinstance(col_idx, (list, tuple)):
+        col_idx = np.concatenate([np.asarray(c, dtype=np.int32) for c in col_idx]) \
+            if len(col_idx) else np.zeros(0, np.int32)
+    ci = np.ascontiguousarray(np.asarray(col_idx, dtype=np.int32))
+    out = ctypes.c_void_p()
+    _check(lib.diffuser_graph_from_csr(n, rp.shape[0], rp.ctypes.data_as(ctypes.c_void_p),
+                                       ci.ctypes.data_as(ctypes.c_void_p) if ci.size else None,
+                                       ctypes.c_void_p(_stream_handle()), ctypes.byref(out)))
+    return Graph(out.value)
+
+
+def workspace_size(graph: Graph, B: int, H: int, d_h: int, d_v: int, dtype) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t()
+    _check(lib.diffuser_attn_workspace_size(graph.handle, B, H, d_h, d_v, _dtype_code(dtype),
+                                            ctypes.byref(out)))
+    return int(out.value)
+
+
+def _check_bhnd(t, name, n):
+    if not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.shape[2] != n:
+        raise DiffuserError(1, f"{name} must be a contiguous CUDA tensor [B, H, n={n}, d]")
+
+
+def _workspace(graph, B, H, d_h, d_v, dtype, device, workspace):
+    torch = _torch()
+    need = workspace_size(graph, B, H, d_h, d_v, dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace, need
+
+
+def attn(q, k, v, graph: Graph, K: int, alpha: float, out=None, workspace=None):
+    """Z = K diffusion steps of the edge-softmax attention of (q, k) over v."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check_bhnd(t, nm, graph.n)
+    B, H, _, d_h = q.shape
+    d_v = v.shape[3]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or not (q.dtype == k.dtype == v.dtype):
+        raise DiffuserError(1, "q, k, v shapes/dtypes disagree")
+    if out is None:
+        out = torch.empty_like(v)
+    workspace, _ = _workspace(graph, B, H, d_h, d_v, q.dtype, q.device, workspace)
+    lib = load_library()
+    _check(lib.diffuser_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q.dtype), B, H,
+                             d_h, d_v, graph.handle, K, float(alpha), out.data_ptr(),
+                             workspace.data_ptr(), workspace.numel(),
+                             ctypes.c_void_p(_stream_handle(q.device))))
+    return out
+
+
+def scores_softmax(q, k, graph: Graph, out=None):
+    """Edge-softmax weights A (1-D, the (b, h)-blocked CSR layout)."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k")):
+        _check_bhnd(t, nm, graph.n)
+    B, H, _, d_h = q.shape
+    if k.shape != q.shape or q.dtype != k.dtype:
+        raise DiffuserError(1, "q, k shapes/dtypes disagree")
+    if out is None:
+        out = torch.empty(graph.a_numel(B, H), dtype=q.dtype, device=q.device)
+    lib = load_library()
+    _check(lib.diffuser_scores_softmax(q.data_ptr(), k.data_ptr(), _dtype_code(q.dtype), B, H, d_h,
+                                       graph.handle, out.data_ptr(), None, 0,
+                                       ctypes.c_void_p(_stream_handle(q.device))))
+    return out
+
+
+def diffuse(A, v, graph: Graph, K: int, alpha: float, out=None, workspace=None):
+    """K steps of Z <- (1 - alpha) A Z + alpha V from Z = V with given A."""
+    torch = _torch()
+    _check_bhnd(v, "v", graph.n)
+    B, H, _, d_v = v.shape
+    if not A.is_cuda or not A.is_contiguous() or A.dtype != v.dtype or \
+            A.numel() != graph.a_numel(B, H):
+        raise DiffuserError(1, "A must be a contiguous CUDA tensor in the A layout")
+    if out is None:
+        out = torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(max(v.numel() * v.element_size() + 256, 1), dtype=torch.uint8,
+                                device=v.device)
+    lib = load_library()
+    _check(lib.diffuser_diffuse(A.data_ptr(), v.data_ptr(), _dtype_code(v.dtype), B, H, d_v,
+                                graph.handle, K, float(alpha), out.data_ptr(),
+                                workspace.data_ptr(), workspace.numel(),
+                                ctypes.c_void_p(_stream_handle(v.device))))
+    return out

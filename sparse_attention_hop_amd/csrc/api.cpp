@@ -1,0 +1,509 @@
+// C ABI of the Diffuser library: argument validation, graph handles,
+// workspace layout and stage dispatch. Every entry point validates its
+// arguments before enqueuing anything and reports failures as a status code
+// plus a thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace diffuser {
+
+namespace {
+thread_local std::string g_last_error;
+
+constexpr int64_t kMaxN = 1ll << 24;
+constexpr int32_t kMaxSampledRandom = 1024;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+size_t elem_size(diffuser_dtype t) { return t == DIFFUSER_F32 ? 4 : 2; }
+
+bool supported_width(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+diffuser_status hip_fail(hipError_t e, const char* what) {
+    return fail(DIFFUSER_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <typename P>
+hipError_t dev_alloc(P** p, size_t count) {
+    *p = nullptr;
+    if (count == 0) count = 1;
+    return hipMalloc(reinterpret_cast<void**>(p), sizeof(P) * count);
+}
+
+void free_graph_memory(diffuser_graph* g) {
+    hipFree(g->d_row_ptr);
+    hipFree(g->d_col_idx);
+    hipFree(g->d_col_off);
+    hipFree(g->d_global);
+    hipFree(g->d_rnd);
+    hipFree(g->d_rnd_cnt);
+    hipFree(g->d_win_off);
+    g->d_row_ptr = nullptr;
+    g->d_col_idx = nullptr;
+    g->d_col_off = nullptr;
+    g->d_global = nullptr;
+    g->d_rnd = nullptr;
+    g->d_rnd_cnt = nullptr;
+    g->d_win_off = nullptr;
+}
+
+diffuser_status alloc_status(hipError_t e, const char* what) {
+    if (e == hipErrorOutOfMemory) return fail(DIFFUSER_ERR_OUT_OF_MEMORY, what);
+    return hip_fail(e, what);
+}
+
+// Largest random pool of a non-global row: n minus |window u globals|.
+int64_t max_pool(int64_t n, int32_t r, const int32_t* G, int32_t g) {
+    int64_t best = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (g > 0 && std::binary_search(G, G + g, (int32_t)i)) continue;
+        const int64_t lo = std::max<int64_t>(0, i - r), hi = std::min<int64_t>(n - 1, i + r);
+        const int64_t in_w = std::upper_bound(G, G + g, (int32_t)hi) - std::lower_bound(G, G + g, (int32_t)lo);
+        best = std::max(best, n - (hi - lo + 1) - (g - in_w));
+    }
+    return best;
+}
+
+struct graph_guard {
+    diffuser_graph* g;
+    ~graph_guard() {
+        if (g) {
+            free_graph_memory(g);
+            delete g;
+        }
+    }
+};
+
+diffuser_status check_graph(const diffuser_graph* g) {
+    if (!g) return fail(DIFFUSER_ERR_INVALID_ARG, "graph handle is NULL");
+    return DIFFUSER_OK;
+}
+
+// Shared validation of (B, H, width, dtype) against a graph.
+diffuser_status check_shape(const diffuser_graph* g, int32_t B, int32_t H, int32_t d,
+                            diffuser_dtype dtype, const char* dname) {
+    if (auto s = check_graph(g)) return s;
+    if (B < 1 || H < 1) return fail(DIFFUSER_ERR_INVALID_ARG, "B and H must be >= 1");
+    if (g->num_graphs != 1 && g->num_graphs != B)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "graph has num_graphs not in {1, B}");
+    if (dtype != DIFFUSER_F32 && dtype != DIFFUSER_BF16)
+        return fail(DIFFUSER_ERR_UNSUPPORTED, "dtype must be DIFFUSER_F32 or DIFFUSER_BF16");
+    if (d < 1) return fail(DIFFUSER_ERR_INVALID_ARG, std::string(dname) + " must be >= 1");
+    if (!supported_width(d))
+        return fail(DIFFUSER_ERR_UNSUPPORTED, std::string(dname) + " must be 16, 32, 64 or 128");
+    if ((int64_t)B * H > 65535)
+        return fail(DIFFUSER_ERR_UNSUPPORTED, "B * H above 65535");
+    return DIFFUSER_OK;
+}
+
+int64_t total_a_elems(const diffuser_graph* g, int32_t B, int32_t H) {
+    if (g->num_graphs == 1) return (int64_t)B * H * g->nnz[0];
+    return (int64_t)H * g->col_off[g->num_graphs];
+}
+
+struct ws_layout {
+    size_t a_bytes, z_bytes, total;
+};
+
+ws_layout layout(const diffuser_graph* g, int32_t B, int32_t H, int32_t d_v, diffuser_dtype t) {
+    ws_layout w;
+    w.a_bytes = align_up((size_t)total_a_elems(g, B, H) * elem_size(t));
+    w.z_bytes = align_up((size_t)B * H * (size_t)g->n * d_v * elem_size(t));
+    w.total = w.a_bytes + w.z_bytes;
+    return w;
+}
+
+diffuser_status check_alpha_k(int32_t K_steps, float alpha) {
+    if (K_steps < 0) return fail(DIFFUSER_ERR_INVALID_ARG, "K_steps must be >= 0");
+    if (!(alpha >= 0.0f && alpha <= 1.0f))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "alpha must lie in [0, 1]");
+    return DIFFUSER_OK;
+}
+
+diffuser_status check_ptr(const void* p, const char* name, bool need16 = true) {
+    if (!p) return fail(DIFFUSER_ERR_INVALID_ARG, std::string(name) + " is NULL");
+    if (need16 && !aligned16(p))
+        return fail(DIFFUSER_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned");
+    return DIFFUSER_OK;
+}
+
+// K diffusion steps from V into Z, ping-ponging with `tmp` so that the last
+// step writes Z.
+diffuser_status run_diffusion(const diffuser_graph* g, const attn_shape& s, const void* A,
+                              const void* V, void* Z, void* tmp, int32_t K_steps, float alpha,
+                              hipStream_t st) {
+    const size_t zbytes = (size_t)s.B * s.H * (size_t)g->n * s.d * elem_size(s.dtype);
+    if (K_steps == 0) {
+        hipError_t e = hipMemcpyAsync(Z, V, zbytes, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return hip_fail(e, "copy of V into Z");
+        return DIFFUSER_OK;
+    }
+    const void* cur = V;
+    for (int32_t k = 0; k < K_steps; ++k) {
+        // Steps K-1, K-3, ... write Z; the others write tmp.
+        void* dst = ((K_steps - 1 - k) % 2 == 0) ? Z : tmp;
+        hipError_t e = launch_diffuse_step(*g, s, A, cur, V, dst, alpha, st);
+        if (e != hipSuccess) return hip_fail(e, "diffusion step launch");
+        cur = dst;
+    }
+    return DIFFUSER_OK;
+}
+
+}  // namespace
+
+diffuser_status fail(diffuser_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+}  // namespace diffuser
+
+using namespace diffuser;
+
+extern "C" {
+
+const char* diffuser_status_string(diffuser_status s) {
+    switch (s) {
+        case DIFFUSER_OK: return "DIFFUSER_OK";
+        case DIFFUSER_ERR_INVALID_ARG: return "DIFFUSER_ERR_INVALID_ARG";
+        case DIFFUSER_ERR_UNSUPPORTED: return "DIFFUSER_ERR_UNSUPPORTED";
+        case DIFFUSER_ERR_OUT_OF_MEMORY: return "DIFFUSER_ERR_OUT_OF_MEMORY";
+        case DIFFUSER_ERR_HIP: return "DIFFUSER_ERR_HIP";
+        case DIFFUSER_ERR_INTERNAL: return "DIFFUSER_ERR_INTERNAL";
+    }
+    return "DIFFUSER_ERR_UNKNOWN";
+}
+
+const char* diffuser_last_error(void) { return g_last_error.c_str(); }
+
+diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stream,
+                                     diffuser_graph** out) {
+    g_last_error.clear();
+    if (!desc || !out) return fail(DIFFUSER_ERR_INVALID_ARG, "desc and out must be non-NULL");
+    const int64_t n = desc->n;
+    if (n < 1 || n > kMaxN) return fail(DIFFUSER_ERR_INVALID_ARG, "n must lie in [1, 2^24]");
+    if (desc->window_radius < 0) return fail(DIFFUSER_ERR_INVALID_ARG, "window_radius < 0");
+    if (desc->num_global < 0 || desc->num_global > n)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "num_global must lie in [0, n]");
+    if (desc->num_global > 0 && !desc->global_idx)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "global_idx is NULL");
+    for (int32_t k = 0; k < desc->num_global; ++k) {
+        const int32_t p = desc->global_idx[k];
+        if (p < 0 || p >= n) return fail(DIFFUSER_ERR_INVALID_ARG, "global index out of range");
+        if (k > 0 && p <= desc->global_idx[k - 1])
+            return fail(DIFFUSER_ERR_INVALID_ARG, "global_idx must be strictly increasing");
+    }
+    if (desc->num_random < 0) return fail(DIFFUSER_ERR_INVALID_ARG, "num_random < 0");
+    if (desc->num_graphs < 1 || desc->num_graphs > 65535)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "num_graphs must lie in [1, 65535]");
+    if (desc->causal != 0 && desc->causal != 1)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if ((int64_t)desc->num_graphs * n >= (1ll << 44))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "num_graphs * n too large for the draw counter");
+    if (desc->num_random > kMaxSampledRandom &&
+        max_pool(n, desc->window_radius, desc->global_idx, desc->num_global) > desc->num_random)
+        return fail(DIFFUSER_ERR_UNSUPPORTED,
+                    "num_random above 1024 with a pool larger than the budget");
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    diffuser_graph* g = new (std::nothrow) diffuser_graph();
+    if (!g) return fail(DIFFUSER_ERR_OUT_OF_MEMORY, "host allocation of the graph");
+    graph_guard guard{g};
+    g->n = n;
+    g->num_graphs = desc->num_graphs;
+    g->structured = true;
+    g->radius = desc->window_radius;
+    g->num_global = desc->num_global;
+    g->num_random = desc->num_random;
+    g->rnd_width = (int32_t)std::min<int64_t>(desc->num_random, n);
+    g->causal = desc->causal;
+    g->seed = desc->seed;
+    hipGetDevice(&g->device);
+
+    const int64_t rows = (int64_t)g->num_graphs * n;
+    int32_t* d_deg = nullptr;
+    int32_t* d_status = nullptr;
+    int64_t* d_maxdeg = nullptr;
+    hipError_t e;
+    if ((e = dev_alloc(&g->d_global, g->num_global)) != hipSuccess ||
+        (e = dev_alloc(&g->d_rnd, (size_t)rows * std::max(g->rnd_width, 1))) != hipSuccess ||
+        (e = dev_alloc(&g->d_rnd_cnt, rows)) != hipSuccess ||
+        (e = dev_alloc(&g->d_win_off, rows)) != hipSuccess ||
+        (e = dev_alloc(&g->d_row_ptr, (size_t)g->num_graphs * (n + 1))) != hipSuccess ||
+        (e = dev_alloc(&g->d_col_off, g->num_graphs + 1)) != hipSuccess ||
+        (e = dev_alloc(&d_deg, rows)) != hipSuccess ||
+        (e = dev_alloc(&d_status, 1)) != hipSuccess ||
+        (e = dev_alloc(&d_maxdeg, g->num_graphs)) != hipSuccess) {
+        hipFree(d_deg);
+        hipFree(d_status);
+        hipFree(d_maxdeg);
+        return alloc_status(e, "device allocation for the graph build");
+    }
+    struct tmp_guard {
+        void* p[3];
+        ~tmp_guard() {
+            for (void* q : p) hipFree(q);
+        }
+    } tmps{{d_deg, d_status, d_maxdeg}};
+
+    if (g->num_global > 0 &&
+        (e = hipMemcpyAsync(g->d_global, desc->global_idx, sizeof(int32_t) * g->num_global,
+                            hipMemcpyHostToDevice, st)) != hipSuccess)
+        return hip_fail(e, "copy of global_idx");
+    if ((e = hipMemsetAsync(d_status, 0, sizeof(int32_t), st)) != hipSuccess)
+        return hip_fail(e, "status clear");
+    if ((e = launch_draw(*g, d_deg, d_status, st)) != hipSuccess) return hip_fail(e, "draw launch");
+    if ((e = launch_scan(*g, d_deg, d_maxdeg, st)) != hipSuccess) return hip_fail(e, "scan launch");
+    int32_t status = 0;
+    std::vector<int64_t> maxdeg(g->num_graphs);
+    std::vector<int64_t> last(g->num_graphs);
+    if ((e = hipMemcpyAsync(&status, d_status, sizeof(int32_t), hipMemcpyDeviceToHost, st)) !=
+            hipSuccess ||
+        (e = hipMemcpyAsync(maxdeg.data(), d_maxdeg, sizeof(int64_t) * g->num_graphs,
+                            hipMemcpyDeviceToHost, st)) != hipSuccess)
+        return hip_fail(e, "copy of build status");
+    for (int32_t gr = 0; gr < g->num_graphs; ++gr) {
+        if ((e = hipMemcpyAsync(&last[gr], g->d_row_ptr + (int64_t)gr * (n + 1) + n,
+                                sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess)
+            return hip_fail(e, "copy of edge counts");
+    }
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "graph draw");
+    if (status != 0)
+        return fail(DIFFUSER_ERR_INTERNAL, "random draw budget (2^20 draws per row) exhausted");
+    g->nnz = last;
+    g->col_off.assign(g->num_graphs + 1, 0);
+    for (int32_t gr = 0; gr < g->num_graphs; ++gr) g->col_off[gr + 1] = g->col_off[gr] + last[gr];
+    g->max_row_len = *std::max_element(maxdeg.begin(), maxdeg.end());
+    if ((e = dev_alloc(&g->d_col_idx, g->col_off[g->num_graphs])) != hipSuccess)
+        return alloc_status(e, "device allocation of col_idx");
+    if ((e = hipMemcpyAsync(g->d_col_off, g->col_off.data(), sizeof(int64_t) * (g->num_graphs + 1),
+                            hipMemcpyHostToDevice, st)) != hipSuccess)
+        return hip_fail(e, "copy of col offsets");
+    if ((e = launch_fill(*g, st)) != hipSuccess) return hip_fail(e, "fill launch");
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "graph fill");
+    guard.g = nullptr;
+    *out = g;
+    return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_graph_from_csr(int64_t n, int32_t num_graphs, const int64_t* row_ptr_host,
+                                        const int32_t* col_idx_host, void* stream,
+                                        diffuser_graph** out) {
+    g_last_error.clear();
+    if (!out || !row_ptr_host) return fail(DIFFUSER_ERR_INVALID_ARG, "NULL argument");
+    if (n < 1 || n > kMaxN) return fail(DIFFUSER_ERR_INVALID_ARG, "n must lie in [1, 2^24]");
+    if (num_graphs < 1 || num_graphs > 65535)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "num_graphs must lie in [1, 65535]");
+    std::vector<int64_t> nnz(num_graphs), col_off(num_graphs + 1, 0);
+    int64_t max_len = 0;
+    for (int32_t gr = 0; gr < num_graphs; ++gr) {
+        const int64_t* rp = row_ptr_host + (int64_t)gr * (n + 1);
+        if (rp[0] != 0) return fail(DIFFUSER_ERR_INVALID_ARG, "row_ptr must start at 0");
+        for (int64_t i = 0; i < n; ++i) {
+            if (rp[i + 1] < rp[i]) return fail(DIFFUSER_ERR_INVALID_ARG, "row_ptr decreasing");
+            max_len = std::max(max_len, rp[i + 1] - rp[i]);
+        }
+        nnz[gr] = rp[n];
+        col_off[gr + 1] = col_off[gr] + rp[n];
+    }
+    if (col_off[num_graphs] > 0 && !col_idx_host)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "col_idx is NULL");
+    if (col_off[num_graphs] >= (1ll << 40))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "too many edges");
+    for (int32_t gr = 0; gr < num_graphs; ++gr) {
+        const int64_t* rp = row_ptr_host + (int64_t)gr * (n + 1);
+        const int32_t* c = col_idx_host + col_off[gr];
+        for (int64_t i = 0; i < n; ++i) {
+            bool self = false;
+            for (int64_t e = rp[i]; e < rp[i + 1]; ++e) {
+                if (c[e] < 0 || c[e] >= n)
+                    return fail(DIFFUSER_ERR_INVALID_ARG, "column index out of range");
+                if (e > rp[i] && c[e] <= c[e - 1])
+                    return fail(DIFFUSER_ERR_INVALID_ARG, "row columns must be strictly ascending");
+                self |= c[e] == i;
+            }
+            if (!self) return fail(DIFFUSER_ERR_INVALID_ARG, "every row needs its self edge");
+        }
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    diffuser_graph* g = new (std::nothrow) diffuser_graph();
+    if (!g) return fail(DIFFUSER_ERR_OUT_OF_MEMORY, "host allocation of the graph");
+    graph_guard guard{g};
+    g->n = n;
+    g->num_graphs = num_graphs;
+    g->structured = false;
+    g->nnz = nnz;
+    g->col_off = col_off;
+    g->max_row_len = max_len;
+    hipGetDevice(&g->device);
+    hipError_t e;
+    if ((e = dev_alloc(&g->d_row_ptr, (size_t)num_graphs * (n + 1))) != hipSuccess ||
+        (e = dev_alloc(&g->d_col_idx, col_off[num_graphs])) != hipSuccess ||
+        (e = dev_alloc(&g->d_col_off, num_graphs + 1)) != hipSuccess)
+        return alloc_status(e, "device allocation of the imported graph");
+    if ((e = hipMemcpyAsync(g->d_row_ptr, row_ptr_host, sizeof(int64_t) * num_graphs * (n + 1),
+                            hipMemcpyHostToDevice, st)) != hipSuccess ||
+        (col_off[num_graphs] > 0 &&
+         (e = hipMemcpyAsync(g->d_col_idx, col_idx_host, sizeof(int32_t) * col_off[num_graphs],
+                             hipMemcpyHostToDevice, st)) != hipSuccess) ||
+        (e = hipMemcpyAsync(g->d_col_off, col_off.data(), sizeof(int64_t) * (num_graphs + 1),
+                            hipMemcpyHostToDevice, st)) != hipSuccess)
+        return hip_fail(e, "copy of the imported graph");
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "graph import");
+    guard.g = nullptr;
+    *out = g;
+    return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_graph_info(const diffuser_graph* g, int64_t* n, int32_t* num_graphs,
+                                    int64_t* nnz) {
+    g_last_error.clear();
+    if (auto s = check_graph(g)) return s;
+    if (n) *n = g->n;
+    if (num_graphs) *num_graphs = g->num_graphs;
+    if (nnz) std::copy(g->nnz.begin(), g->nnz.end(), nnz);
+    return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_graph_copy_csr(const diffuser_graph* g, int32_t graph,
+                                        int64_t* row_ptr_host, int32_t* col_idx_host,
+                                        void* stream) {
+    g_last_error.clear();
+    if (auto s = check_graph(g)) return s;
+    if (graph < 0 || graph >= g->num_graphs)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "graph index out of range");
+    if (!row_ptr_host || (!col_idx_host && g->nnz[graph] > 0))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "NULL output array");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if ((e = hipMemcpyAsync(row_ptr_host, g->d_row_ptr + (int64_t)graph * (g->n + 1),
+                            sizeof(int64_t) * (g->n + 1), hipMemcpyDeviceToHost, st)) !=
+            hipSuccess ||
+        (g->nnz[graph] > 0 &&
+         (e = hipMemcpyAsync(col_idx_host, g->d_col_idx + g->col_off[graph],
+                             sizeof(int32_t) * g->nnz[graph], hipMemcpyDeviceToHost, st)) !=
+             hipSuccess))
+        return hip_fail(e, "copy of the CSR");
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "CSR copy");
+    return DIFFUSER_OK;
+}
+
+void diffuser_graph_destroy(diffuser_graph* g) {
+    if (!g) return;
+    hipDeviceSynchronize();
+    free_graph_memory(g);
+    delete g;
+}
+
+diffuser_status diffuser_attn_workspace_size(const diffuser_graph* g, int32_t B, int32_t H,
+                                             int32_t d_h, int32_t d_v, diffuser_dtype dtype,
+                                             size_t* bytes) {
+    g_last_error.clear();
+    if (!bytes) return fail(DIFFUSER_ERR_INVALID_ARG, "bytes is NULL");
+    if (auto s = check_shape(g, B, H, d_h, dtype, "d_h")) return s;
+    if (auto s = check_shape(g, B, H, d_v, dtype, "d_v")) return s;
+    *bytes = layout(g, B, H, d_v, dtype).total;
+    return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_attn(const void* Q, const void* K, const void* V, diffuser_dtype dtype,
+                              int32_t B, int32_t H, int32_t d_h, int32_t d_v,
+                              const diffuser_graph* g, int32_t K_steps, float alpha, void* Z,
+                              void* workspace, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (auto s = check_shape(g, B, H, d_h, dtype, "d_h")) return s;
+    if (auto s = check_shape(g, B, H, d_v, dtype, "d_v")) return s;
+    if (auto s = check_alpha_k(K_steps, alpha)) return s;
+    for (auto pr : {std::make_pair(Q, "Q"), std::make_pair(K, "K"), std::make_pair(V, "V"),
+                    std::make_pair((const void*)Z, "Z"), std::make_pair((const void*)workspace,
+                                                                          "workspace")})
+        if (auto s = check_ptr(pr.first, pr.second)) return s;
+    const ws_layout w = layout(g, B, H, d_v, dtype);
+    if (ws_bytes < w.total) return fail(DIFFUSER_ERR_INVALID_ARG, "workspace too small");
+    const size_t es = elem_size(dtype);
+    const size_t qk_bytes = (size_t)B * H * g->n * d_h * es;
+    const size_t vz_bytes = (size_t)B * H * g->n * d_v * es;
+    if (overlaps(Z, vz_bytes, Q, qk_bytes) || overlaps(Z, vz_bytes, K, qk_bytes) ||
+        overlaps(Z, vz_bytes, V, vz_bytes) || overlaps(Z, vz_bytes, workspace, ws_bytes))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "Z overlaps an input or the workspace");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    void* A = ws;
+    void* tmp = ws + w.a_bytes;
+    const float scale_log2 = (float)(1.0 / std::sqrt((double)d_h) * 1.4426950408889634);
+    hipError_t e = launch_scores_softmax(*g, attn_shape{B, H, d_h, dtype}, Q, K, A, scale_log2, st);
+    if (e != hipSuccess) return hip_fail(e, "score/softmax launch");
+    return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, V, Z, tmp, K_steps, alpha, st);
+}
+
+diffuser_status diffuser_scores_softmax(const void* Q, const void* K, diffuser_dtype dtype,
+                                        int32_t B, int32_t H, int32_t d_h,
+                                        const diffuser_graph* g, void* A_out, void* workspace,
+                                        size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    (void)workspace;
+    (void)ws_bytes;
+    if (auto s = check_shape(g, B, H, d_h, dtype, "d_h")) return s;
+    if (auto s = check_ptr(Q, "Q")) return s;
+    if (auto s = check_ptr(K, "K")) return s;
+    if (auto s = check_ptr(A_out, "A_out", false)) return s;
+    if (reinterpret_cast<uintptr_t>(A_out) % elem_size(dtype))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "A_out is not element aligned");
+    const size_t es = elem_size(dtype);
+    const size_t qk_bytes = (size_t)B * H * g->n * d_h * es;
+    const size_t a_bytes = (size_t)total_a_elems(g, B, H) * es;
+    if (overlaps(A_out, a_bytes, Q, qk_bytes) || overlaps(A_out, a_bytes, K, qk_bytes))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "A_out overlaps Q or K");
+    const float scale_log2 = (float)(1.0 / std::sqrt((double)d_h) * 1.4426950408889634);
+    hipError_t e = launch_scores_softmax(*g, attn_shape{B, H, d_h, dtype}, Q, K, A_out,
+                                         scale_log2, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "score/softmax launch");
+    return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_diffuse(const void* A, const void* V, diffuser_dtype dtype, int32_t B,
+                                 int32_t H, int32_t d_v, const diffuser_graph* g,
+                                 int32_t K_steps, float alpha, void* Z, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (auto s = check_shape(g, B, H, d_v, dtype, "d_v")) return s;
+    if (auto s = check_alpha_k(K_steps, alpha)) return s;
+    if (auto s = check_ptr(A, "A", false)) return s;
+    if (reinterpret_cast<uintptr_t>(A) % elem_size(dtype))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "A is not element aligned");
+    if (auto s = check_ptr(V, "V")) return s;
+    if (auto s = check_ptr(Z, "Z")) return s;
+    const size_t es = elem_size(dtype);
+    const size_t vz_bytes = (size_t)B * H * g->n * d_v * es;
+    const size_t a_bytes = (size_t)total_a_elems(g, B, H) * es;
+    const size_t z_need = align_up(vz_bytes);
+    if (K_steps >= 2) {
+        if (auto s = check_ptr(workspace, "workspace")) return s;
+        if (ws_bytes < z_need) return fail(DIFFUSER_ERR_INVALID_ARG, "workspace too small");
+    }
+    if (overlaps(Z, vz_bytes, A, a_bytes) || overlaps(Z, vz_bytes, V, vz_bytes) ||
+        (K_steps >= 2 && overlaps(Z, vz_bytes, workspace, z_need)))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "Z overlaps an input or the workspace");
+    // The Z ping-pong buffer sits at the start of the caller's workspace.
+    return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, V, Z, workspace, K_steps, alpha,
+                         static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// One personalized-PageRank diffusion step ("Diffuser" reading notes,
+// section 2.4, eq. S.7):
+//   Z_{k+1}[i] = (1 - alpha) * sum_{j in N(i)} A_ij Z_k[j] + alpha * V[i].
+// The edge weights A are the same in every step; only Z changes.
+//
+// One wavefront per row. A group of L lanes gathers one neighbour row of Z_k
+// with 16-byte loads (L = d * elem_size / 16), so a wave consumes 64 / L
+// edges per iteration; the groups' partial sums are reduced at the end and
+// the restart term is fused into the store.
+#include "internal.h"
+#include "vec.h"
+
+namespace diffuser {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWave * kWavesPerBlock)
+void k_diffuse_step(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ row_ptr,
+                    const int32_t* __restrict__ col_idx, const int64_t* __restrict__ col_off,
+                    const T* __restrict__ A, const T* __restrict__ Zk, const T* __restrict__ V,
+                    T* __restrict__ Zn, float alpha) {
+    constexpr int E = chunk<T>::kElems;
+    constexpr int L = D / E;
+    constexpr int EPI = kWave / L;
+    static_assert(L >= 1 && L <= kWave && (kWave % L) == 0, "unsupported head width");
+
+    const int wave = threadIdx.x / kWave;
+    const int lane = __lane_id();
+    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (i >= n) return;
+    const int32_t bh = blockIdx.y;
+    const int32_t b = bh / H, h = bh - b * H;
+    const int32_t gr = num_graphs == 1 ? 0 : b;
+    const int64_t* rp = row_ptr + (int64_t)gr * (n + 1);
+    const int32_t* cols = col_idx + col_off[gr];
+    const T* Ab = A + a_block_offset(col_off, num_graphs, H, b, h);
+    const int64_t e0 = rp[i], e1 = rp[i + 1];
+    const int sub = lane % L, grp = lane / L;
+    const T* Zb = Zk + (int64_t)bh * n * D + sub * E;
+
+    float acc[E];
+#pragma unroll
+    for (int c = 0; c < E; ++c) acc[c] = 0.0f;
+    for (int64_t base = e0; base < e1; base += EPI) {
+        const int64_t e = base + grp;
+        if (e < e1) {
+            const float a = chunk<T>::load1(Ab + e);
+            float z[E];
+            chunk<T>::load(Zb + (int64_t)cols[e] * D, z);
+#pragma unroll
+            for (int c = 0; c < E; ++c) acc[c] = fmaf(a, z[c], acc[c]);
+        }
+    }
+#pragma unroll
+    for (int off = L; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int c = 0; c < E; ++c) acc[c] += __shfl_xor(acc[c], off);
+    }
+    if (grp == 0) {
+        const int64_t o = ((int64_t)bh * n + i) * D + sub * E;
+        float v[E];
+        chunk<T>::load(V + o, v);
+        const float keep = 1.0f - alpha;
+#pragma unroll
+        for (int c = 0; c < E; ++c) v[c] = keep * acc[c] + alpha * v[c];
+        chunk<T>::store(Zn + o, v);
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
+                    const void* V, void* Zn, float alpha, hipStream_t st) {
+    dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
+    hipLaunchKernelGGL((k_diffuse_step<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st, g.n,
+                       s.H, g.num_graphs, g.d_row_ptr, g.d_col_idx, g.d_col_off,
+                       static_cast<const T*>(A), static_cast<const T*>(Zk),
+                       static_cast<const T*>(V), static_cast<T*>(Zn), alpha);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_d(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
+                    const void* V, void* Zn, float alpha, hipStream_t st) {
+    switch (s.d) {
+        case 16: return launch_t<T, 16>(g, s, A, Zk, V, Zn, alpha, st);
+        case 32: return launch_t<T, 32>(g, s, A, Zk, V, Zn, alpha, st);
+        case 64: return launch_t<T, 64>(g, s, A, Zk, V, Zn, alpha, st);
+        case 128: return launch_t<T, 128>(g, s, A, Zk, V, Zn, alpha, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_diffuse_step(const diffuser_graph& g, const attn_shape& s, const void* A,
+                               const void* Zk, const void* V, void* Zn, float alpha,
+                               hipStream_t st) {
+    if (s.dtype == DIFFUSER_F32) return launch_d<float>(g, s, A, Zk, V, Zn, alpha, st);
+    return launch_d<bf16_t>(g, s, A, Zk, V, Zn, alpha, st);
+}
+
+}  // namespace diffuser

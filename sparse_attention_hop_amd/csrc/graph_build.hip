@@ -1,0 +1,266 @@
+// Static token-graph builder: window u globals u random extras, one CSR per
+// graph, ascending columns ("Diffuser" reading notes, section 2.2 connection
+// table; "1.2.1 Static sparsity", section 1.1 eq. 5 and section 1.2 eq. 12;
+// "038 BigBird", section 2, union neighbourhood). Random edges are seeded
+// and input-independent ("1.2.1", section 2: static random edges are fixed
+// before execution and reproducible from the seed).
+//
+// Three kernels, one wavefront per row where rows are independent:
+//   draw : random extras of a row by rejection sampling on a counter-based
+//          SplitMix64 stream, sorted into an ELL table, plus the row degree;
+//   scan : exclusive scan of the degrees into row_ptr (one block per graph);
+//   fill : the sorted merge window u (G minus window) u random into col_idx,
+//          and the CSR offset of each row's window run.
+#include "internal.h"
+
+namespace diffuser {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kMaxSampled = 1024;        // random budget held in LDS per row
+constexpr int64_t kMaxDraws = 1ll << 20; // draws per row before giving up
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+// SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014).
+__device__ __forceinline__ uint64_t splitmix_mix(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Number of entries of the ascending array a[0..len) that are < x.
+__device__ __forceinline__ int32_t count_less(const int32_t* a, int32_t len, int64_t x) {
+    int32_t lo = 0, hi = len;
+    while (lo < hi) {
+        int32_t mid = (lo + hi) >> 1;
+        if ((int64_t)a[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ bool is_global(const int32_t* G, int32_t g, int64_t j) {
+    int32_t k = count_less(G, g, j);
+    return k < g && G[k] == j;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__global__ __launch_bounds__(kWave * kWavesPerBlock)
+void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int32_t R,
+            int32_t rnd_width, int32_t causal, uint64_t seed, int32_t* __restrict__ deg,
+            int32_t* __restrict__ rnd, int32_t* __restrict__ rnd_cnt,
+            int32_t* __restrict__ status) {
+    __shared__ int32_t taken[kWavesPerBlock][kMaxSampled];
+    const int wave = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    const int64_t gr = blockIdx.y;
+    if (i >= n) return;
+    const int64_t row = gr * n + i;
+    int32_t* out = rnd + row * (int64_t)rnd_width;
+
+    if (is_global(G, g, i)) {
+        if (lane == 0) {
+            deg[row] = (int32_t)(causal ? i + 1 : n);
+            rnd_cnt[row] = 0;
+        }
+        return;
+    }
+    const int64_t lo = i - r < 0 ? 0 : i - r;
+    const int64_t hi = i + r > n - 1 ? n - 1 : i + r;
+    const int64_t wlen = hi - lo + 1;
+    const int32_t g_before = count_less(G, g, lo);
+    const int32_t g_in = count_less(G, g, hi + 1) - g_before;
+    const int64_t pool = n - wlen - (g - g_in);
+
+    int32_t m = 0;  // accepted random extras (wave-uniform)
+    if (pool <= R) {
+        // The whole pool: every position outside the window and the globals.
+        for (int64_t base = 0; base < n; base += kWave) {
+            const int64_t j = base + lane;
+            const bool in_pool = j < n && (j < lo || j > hi) && !is_global(G, g, j);
+            const uint64_t mask = __ballot(in_pool);
+            const int32_t pos = m + __popcll(mask & ((1ull << lane) - 1));
+            if (in_pool && pos < rnd_width) out[pos] = (int32_t)j;
+            m += __popcll(mask);
+        }
+    } else {
+        int32_t* list = taken[wave];
+        const uint64_t ctr_row = ((uint64_t)(gr * n + i)) << 20;
+        for (int64_t t0 = 0; m < R && t0 < kMaxDraws; t0 += kWave) {
+            const int64_t t = t0 + lane;
+            const uint64_t u = splitmix_mix(seed + kGamma * ((ctr_row | (uint64_t)t) + 1ull));
+            const int64_t j = (int64_t)(((u >> 32) * (uint64_t)n) >> 32);
+            bool ok = (j < lo || j > hi) && !is_global(G, g, j);
+            for (int32_t q = 0; q < m; ++q) ok = ok && list[q] != (int32_t)j;
+            uint64_t mask = __ballot(ok);
+            // Accept in draw order; drop later repeats of an accepted value.
+            while (mask != 0 && m < R) {
+                const int l = __ffsll((unsigned long long)mask) - 1;
+                const int32_t c = __shfl((int32_t)j, l);
+                if (lane == 0) list[m] = c;
+                ++m;
+                mask &= ~__ballot((int32_t)j == c);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        if (m < R) {
+            if (lane == 0) status[0] = 1;
+            return;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // Rank sort of the distinct values into ascending order.
+        for (int32_t e = lane; e < m; e += kWave) {
+            const int32_t v = list[e];
+            int32_t rank = 0;
+            for (int32_t q = 0; q < m; ++q) rank += list[q] < v;
+            if (rank < rnd_width) out[rank] = v;
+        }
+    }
+    if (lane == 0) {
+        rnd_cnt[row] = m;
+        if (!causal) {
+            deg[row] = (int32_t)(wlen + (g - g_in) + m);
+        }
+    }
+    if (causal) {
+        // Keep j <= i: the window part [lo, i], globals below lo, and the
+        // random extras below lo (none lie inside the window).
+        int32_t below = 0;
+        if (pool <= R) {
+            below = (int32_t)(lo - g_before);
+        } else {
+            const int32_t* list = taken[wave];
+            int32_t c = 0;
+            for (int32_t e = lane; e < m; e += kWave) c += list[e] < lo;
+            for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+            below = c;
+        }
+        if (lane == 0) deg[row] = (int32_t)((i - lo + 1) + g_before + below);
+    }
+}
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads)
+void k_scan(int64_t n, const int32_t* __restrict__ deg, int64_t* __restrict__ row_ptr,
+            int64_t* __restrict__ max_deg) {
+    __shared__ int64_t part[kScanThreads];
+    __shared__ int64_t pmax[kScanThreads];
+    const int64_t gr = blockIdx.x;
+    const int32_t* d = deg + gr * n;
+    int64_t* rp = row_ptr + gr * (n + 1);
+    const int64_t chunk = (n + kScanThreads - 1) / kScanThreads;
+    const int64_t b0 = threadIdx.x * chunk;
+    const int64_t b1 = b0 + chunk < n ? b0 + chunk : n;
+    int64_t s = 0, mx = 0;
+    for (int64_t i = b0; i < b1; ++i) {
+        s += d[i];
+        mx = d[i] > mx ? d[i] : mx;
+    }
+    part[threadIdx.x] = s;
+    pmax[threadIdx.x] = mx;
+    __syncthreads();
+    // Inclusive Hillis-Steele scan of the per-thread sums.
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+        int64_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+        int64_t w = threadIdx.x >= off ? pmax[threadIdx.x - off] : 0;
+        __syncthreads();
+        part[threadIdx.x] += v;
+        pmax[threadIdx.x] = pmax[threadIdx.x] > w ? pmax[threadIdx.x] : w;
+        __syncthreads();
+    }
+    int64_t run = part[threadIdx.x] - s;
+    for (int64_t i = b0; i < b1; ++i) {
+        rp[i] = run;
+        run += d[i];
+    }
+    if (threadIdx.x == kScanThreads - 1) {
+        rp[n] = part[kScanThreads - 1];
+        max_deg[gr] = pmax[kScanThreads - 1];
+    }
+}
+
+__global__ __launch_bounds__(kWave * kWavesPerBlock)
+void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int32_t rnd_width,
+            int32_t causal, const int64_t* __restrict__ row_ptr,
+            const int64_t* __restrict__ col_off, const int32_t* __restrict__ rnd,
+            const int32_t* __restrict__ rnd_cnt, int32_t* __restrict__ col_idx,
+            int32_t* __restrict__ win_off) {
+    const int wave = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    const int64_t gr = blockIdx.y;
+    if (i >= n) return;
+    const int64_t row = gr * n + i;
+    const int64_t* rp = row_ptr + gr * (n + 1);
+    int32_t* out = col_idx + col_off[gr] + rp[i];
+    // Every store below is kept inside this row's slots.
+    const int64_t deg = rp[i + 1] - rp[i];
+    const int64_t last = causal ? i : n - 1;
+
+    if (is_global(G, g, i)) {
+        for (int64_t j = lane; j <= last && j < deg; j += kWave) out[j] = (int32_t)j;
+        if (lane == 0) win_off[row] = 0;
+        return;
+    }
+    const int64_t lo = i - r < 0 ? 0 : i - r;
+    const int64_t hi = i + r > n - 1 ? n - 1 : i + r;
+    const int64_t wlen = hi - lo + 1;
+    const int32_t g_before = count_less(G, g, lo);
+    const int32_t g_in = count_less(G, g, hi + 1) - g_before;
+    const int32_t m = rnd_cnt[row];
+    const int32_t* rr = rnd + row * (int64_t)rnd_width;
+    const int32_t r_before = count_less(rr, m, lo);
+    const int64_t woff = g_before + r_before;
+
+    for (int64_t k = lane; k < wlen; k += kWave) {
+        const int64_t j = lo + k;
+        if (j <= last && woff + k < deg) out[woff + k] = (int32_t)j;
+    }
+    for (int32_t q = lane; q < g; q += kWave) {
+        const int64_t p = G[q];
+        if (p >= lo && p <= hi) continue;
+        const bool right = p > hi;
+        const int64_t pos = (q - (right ? g_in : 0)) + count_less(rr, m, p) + (right ? wlen : 0);
+        if (p <= last && pos < deg) out[pos] = (int32_t)p;
+    }
+    for (int32_t q = lane; q < m; q += kWave) {
+        const int64_t v = rr[q];
+        const bool right = v > hi;
+        const int64_t gx_less = count_less(G, g, v) - (right ? g_in : 0);
+        const int64_t pos = q + gx_less + (right ? wlen : 0);
+        if (v <= last && pos < deg) out[pos] = (int32_t)v;
+    }
+    if (lane == 0) win_off[row] = (int32_t)woff;
+}
+
+}  // namespace
+
+hipError_t launch_draw(const diffuser_graph& g, int32_t* deg, int32_t* status, hipStream_t st) {
+    dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
+    hipLaunchKernelGGL(k_draw, grid, dim3(kWave * kWavesPerBlock), 0, st, g.n, g.radius,
+                       g.d_global, g.num_global, g.num_random, g.rnd_width, g.causal, g.seed,
+                       deg, g.d_rnd, g.d_rnd_cnt, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const diffuser_graph& g, const int32_t* deg, int64_t* max_deg,
+                            hipStream_t st) {
+    hipLaunchKernelGGL(k_scan, dim3((unsigned)g.num_graphs), dim3(kScanThreads), 0, st, g.n,
+                       deg, g.d_row_ptr, max_deg);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill(const diffuser_graph& g, hipStream_t st) {
+    dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
+    hipLaunchKernelGGL(k_fill, grid, dim3(kWave * kWavesPerBlock), 0, st, g.n, g.radius,
+                       g.d_global, g.num_global, g.rnd_width, g.causal, g.d_row_ptr,
+                       g.d_col_off, g.d_rnd, g.d_rnd_cnt, g.d_col_idx, g.d_win_off);
+    return hipGetLastError();
+}
+
+}  // namespace diffuser

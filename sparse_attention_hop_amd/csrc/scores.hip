@@ -1,0 +1,131 @@
+// Edge scores and edge softmax on CSR rows ("Diffuser" reading notes,
+// section 2.1, eqs. S.1-S.5; "1.2.1 Static sparsity", section 1, eqs. 1-3):
+//   s_ij = q_i . k_j / sqrt(d_h) for j in N(i),
+//   A_ij = exp(s_ij - m_i) / sum_{u in N(i)} exp(s_iu - m_i),  m_i = max_j s_ij.
+// The normalisation runs over exactly the row's neighbour set.
+//
+// One wavefront per row. A group of L lanes covers one key row with
+// 16-byte loads (L = d * elem_size / 16), so a wave scores 64 / L edges per
+// iteration. The scale folds log2(e) so the exponentials are exp2.
+// Pass 1 keeps an online (max, sum) per lane group; pass 2 recomputes the
+// scores and writes A in the storage type.
+#include "internal.h"
+#include "vec.h"
+
+namespace diffuser {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWave * kWavesPerBlock)
+void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ row_ptr,
+                      const int32_t* __restrict__ col_idx, const int64_t* __restrict__ col_off,
+                      const T* __restrict__ Q, const T* __restrict__ K, T* __restrict__ A,
+                      float scale_log2) {
+    constexpr int E = chunk<T>::kElems;
+    constexpr int L = D / E;          // lanes per edge
+    constexpr int EPI = kWave / L;    // edges per iteration
+    static_assert(L >= 1 && L <= kWave && (kWave % L) == 0, "unsupported head width");
+
+    const int wave = threadIdx.x / kWave;
+    const int lane = __lane_id();
+    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (i >= n) return;
+    const int32_t bh = blockIdx.y;
+    const int32_t b = bh / H, h = bh - b * H;
+    const int32_t gr = num_graphs == 1 ? 0 : b;
+    const int64_t* rp = row_ptr + (int64_t)gr * (n + 1);
+    const int32_t* cols = col_idx + col_off[gr];
+    T* Ab = A + a_block_offset(col_off, num_graphs, H, b, h);
+    const int64_t e0 = rp[i], e1 = rp[i + 1];
+    const int sub = lane % L, grp = lane / L;
+
+    float q[E];
+    chunk<T>::load(Q + ((int64_t)bh * n + i) * D + sub * E, q);
+    const T* Kb = K + (int64_t)bh * n * D + sub * E;
+
+    float m = -INFINITY, l = 0.0f;
+    for (int64_t base = e0; base < e1; base += EPI) {
+        const int64_t e = base + grp;
+        const bool valid = e < e1;
+        float dot = 0.0f;
+        if (valid) {
+            float k[E];
+            chunk<T>::load(Kb + (int64_t)cols[e] * D, k);
+#pragma unroll
+            for (int c = 0; c < E; ++c) dot = fmaf(q[c], k[c], dot);
+        }
+#pragma unroll
+        for (int off = 1; off < L; off <<= 1) dot += __shfl_xor(dot, off);
+        if (valid) {
+            const float t = dot * scale_log2;
+            const float mn = fmaxf(m, t);
+            l = l * fast_exp2(m - mn) + fast_exp2(t - mn);
+            m = mn;
+        }
+    }
+    // Merge the per-group (max, sum) pairs.
+#pragma unroll
+    for (int off = L; off < kWave; off <<= 1) {
+        const float m2 = __shfl_xor(m, off);
+        const float l2 = __shfl_xor(l, off);
+        const float mn = fmaxf(m, m2);
+        const float a = m == -INFINITY ? 0.0f : l * fast_exp2(m - mn);
+        const float c = m2 == -INFINITY ? 0.0f : l2 * fast_exp2(m2 - mn);
+        l = a + c;
+        m = mn;
+    }
+    const float inv = 1.0f / l;
+
+    for (int64_t base = e0; base < e1; base += EPI) {
+        const int64_t e = base + grp;
+        const bool valid = e < e1;
+        float dot = 0.0f;
+        if (valid) {
+            float k[E];
+            chunk<T>::load(Kb + (int64_t)cols[e] * D, k);
+#pragma unroll
+            for (int c = 0; c < E; ++c) dot = fmaf(q[c], k[c], dot);
+        }
+#pragma unroll
+        for (int off = 1; off < L; off <<= 1) dot += __shfl_xor(dot, off);
+        if (valid && sub == 0) chunk<T>::store1(Ab + e, fast_exp2(dot * scale_log2 - m) * inv);
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
+                    void* A, float scale_log2, hipStream_t st) {
+    dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
+    hipLaunchKernelGGL((k_scores_softmax<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st, g.n,
+                       s.H, g.num_graphs, g.d_row_ptr, g.d_col_idx, g.d_col_off,
+                       static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<T*>(A),
+                       scale_log2);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_d(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
+                    void* A, float scale_log2, hipStream_t st) {
+    switch (s.d) {
+        case 16: return launch_t<T, 16>(g, s, Q, K, A, scale_log2, st);
+        case 32: return launch_t<T, 32>(g, s, Q, K, A, scale_log2, st);
+        case 64: return launch_t<T, 64>(g, s, Q, K, A, scale_log2, st);
+        case 128: return launch_t<T, 128>(g, s, Q, K, A, scale_log2, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_scores_softmax(const diffuser_graph& g, const attn_shape& s, const void* Q,
+                                 const void* K, void* A, float scale_log2, hipStream_t st) {
+    if (s.dtype == DIFFUSER_F32) return launch_d<float>(g, s, Q, K, A, scale_log2, st);
+    return launch_d<bf16_t>(g, s, Q, K, A, scale_log2, st);
+}
+
+}  // namespace diffuser

@@ -1,0 +1,47 @@
+"""Comparison helpers shared by the GPU parity tests.
+
+Tolerances (on Z, against the double-precision oracle):
+  fp32 storage: |z - z_ref| <= 1e-4 * max(|z_ref|, 1e-2)  (max relative error
+                1e-4 with a 1e-2 floor on the denominator);
+  bf16 storage: |z - z_ref| <= 2e-2 absolute.
+Edge-softmax rows: |sum_j A_ij - 1| <= 1e-5 (fp32), <= 2^-8 + 1e-6 (bf16,
+whose round-to-nearest-even step is at most 2^-8 relative per weight).
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+F32_REL = 1e-4
+F32_FLOOR = 1e-2
+BF16_ABS = 2e-2
+ROWSUM_F32 = 1e-5
+ROWSUM_BF16 = 2.0 ** -8 + 1e-6
+
+
+def oracle_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def z_error(got: np.ndarray, ref: np.ndarray, dtype: str) -> float:
+    """Error in units of the tolerance (<= 1 passes)."""
+    d = np.abs(got.astype(np.float64) - ref)
+    if dtype == "f32":
+        return float((d / (F32_REL * np.maximum(np.abs(ref), F32_FLOOR))).max(initial=0.0))
+    return float(d.max(initial=0.0) / BF16_ABS)
+
+
+def assert_z_close(got, ref, dtype, what=""):
+    e = z_error(got, ref, dtype)
+    assert e <= 1.0, f"{what}: error {e:.3f} x tolerance ({dtype})"
+    return e
+
+
+def rowsum_bound(dtype: str) -> float:
+    return ROWSUM_F32 if dtype == "f32" else ROWSUM_BF16
+
+
+def dtype_name(t) -> str:
+    import torch
+    return "f32" if t == torch.float32 else "bf16"

@@ -1,0 +1,339 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+CSR graphs must match bit for bit; edge weights and outputs must agree
+within the tolerances of parity_util. Full-size workloads are compared on
+sampled (batch, head) pairs, every row of each; small randomized shapes are
+compared everywhere.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle_pins
+import parity_util as pu
+import sparse_attention_hop_amd as sah
+from workloads import WORKLOADS, make_qkv, make_tensor, sweep_variants
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _gpu_graph(n, r, G, R, ng, causal, seed):
+    return sah.build_graph(n, r, G, R, ng, causal, seed)
+
+
+def _check_csr(orc, g, n, r, G, R, ng, causal, seed):
+    rp, cols = orc.graph(n, r, G, R, ng, causal, seed)
+    for gr in range(ng):
+        grp, gcols = g.copy_csr(gr)
+        assert np.array_equal(grp, rp[gr]), f"row_ptr mismatch in graph {gr}"
+        assert np.array_equal(gcols, cols[gr]), f"col_idx mismatch in graph {gr}"
+    return rp, cols
+
+
+def _as64(t):
+    return t.double().cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# Graph builder: bit-exact CSR
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_csr_bitexact_workloads(orc, name):
+    w = WORKLOADS[name]
+    g = _gpu_graph(w.n, w.radius, w.global_idx, w.num_random, w.num_graphs, w.causal,
+                   w.graph_seed)
+    _check_csr(orc, g, w.n, w.radius, w.global_idx, w.num_random, w.num_graphs, w.causal,
+               w.graph_seed)
+
+
+@pytest.mark.parametrize("R", [0, 32, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_csr_bitexact_sweep(orc, R, causal):
+    w = WORKLOADS["sweep8192_f32"]
+    g = _gpu_graph(w.n, w.radius, w.global_idx, R, 1, causal, w.graph_seed)
+    _check_csr(orc, g, w.n, w.radius, w.global_idx, R, 1, causal, w.graph_seed)
+
+
+def _random_specs(count, seed):
+    rng = np.random.default_rng(seed)
+    specs = []
+    for _ in range(count):
+        n = int(rng.integers(1, 301))
+        r = int(rng.choice([0, 1, 2, 5, 17, n]))
+        g = int(rng.integers(0, min(n, 6) + 1))
+        G = sorted(rng.choice(n, size=g, replace=False).tolist()) if g else []
+        R = int(rng.choice([0, 1, 3, 8, 40, n]))
+        ng = int(rng.choice([1, 2, 3]))
+        causal = bool(rng.integers(0, 2))
+        specs.append((n, r, G, R, ng, causal, int(rng.integers(0, 2 ** 63))))
+    return specs
+
+
+@pytest.mark.parametrize("spec", _random_specs(40, 1), ids=lambda s: f"n{s[0]}r{s[1]}g{len(s[2])}R{s[3]}")
+def test_csr_bitexact_random(orc, spec):
+    g = _gpu_graph(*spec)
+    _check_csr(orc, g, *spec)
+
+
+def test_csr_edge_cases(orc):
+    for spec in [(1, 0, [], 0, 1, False, 0), (1, 3, [0], 5, 2, True, 1),
+                 (7, 0, [], 0, 1, False, 2), (9, 0, list(range(9)), 3, 1, False, 3),
+                 (64, 100, [], 0, 1, True, 4), (50, 2, [0, 49], 1000, 1, False, 5),
+                 (2000, 3, [1000], 1024, 1, False, 6)]:
+        g = _gpu_graph(*spec)
+        _check_csr(orc, g, *spec)
+
+
+# ---------------------------------------------------------------------------
+# Whole path at the workloads' full sizes, sampled (b, h) pairs
+# ---------------------------------------------------------------------------
+
+def _samples(B, H):
+    pairs = {(0, 0), (B - 1, H - 1), (B // 2, H // 3)}
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_attn_full_size(orc, name):
+    w = WORKLOADS[name]
+    print(f"\n[parity] {w.describe()}", flush=True)
+    g = _gpu_graph(w.n, w.radius, w.global_idx, w.num_random, w.num_graphs, w.causal,
+                   w.graph_seed)
+    rp, cols = _check_csr(orc, g, w.n, w.radius, w.global_idx, w.num_random, w.num_graphs,
+                          w.causal, w.graph_seed)
+    q, k, v = make_qkv(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    A = sah.scores_softmax(qd, kd, g)
+    z = sah.attn(qd, kd, vd, g, w.K, w.alpha)
+    torch.cuda.synchronize()
+    A_h = _as64(A)
+    threads = pu.oracle_threads()
+    pairs = _samples(w.B, w.H)
+    for b, h in pairs:
+        gr = 0 if w.num_graphs == 1 else b
+        A_ref = orc.scores_softmax(_as64(q[b, h]), _as64(k[b, h]), rp[gr], cols[gr], threads)
+        off = g.a_offset(b, h, w.H)
+        A_got = A_h[off:off + g.nnz[gr]]
+        bound = pu.rowsum_bound(w.dtype)
+        sums = np.add.reduceat(A_got, rp[gr][:-1])
+        assert np.abs(sums - 1).max() <= bound, (b, h, np.abs(sums - 1).max())
+        a_tol = 1e-5 if w.dtype == "f32" else 2.0 ** -8 + 1e-5
+        assert np.all(np.abs(A_got - A_ref) <= a_tol * np.maximum(A_ref, 1e-30) + 1e-12), (b, h)
+        z_ref = orc.diffuse(A_ref, _as64(v[b, h]), rp[gr], cols[gr], w.K, w.alpha, threads)
+        e = pu.assert_z_close(_as64(z[b, h]), z_ref, w.dtype, f"{name} b={b} h={h}")
+        print(f"[parity] {name} b={b} h={h} err={e:.3e} x tol", flush=True)
+
+
+@pytest.mark.parametrize("R", [0, 32, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_sweep_full_size(orc, R, causal):
+    base = WORKLOADS["sweep8192_f32"]
+    variants = [w for w in sweep_variants() if w.num_random == R and w.causal == causal]
+    g = _gpu_graph(base.n, base.radius, base.global_idx, R, 1, causal, base.graph_seed)
+    rp, cols = _check_csr(orc, g, base.n, base.radius, base.global_idx, R, 1, causal,
+                          base.graph_seed)
+    q, k, v = make_qkv(base)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    b, h = base.B - 1, base.H // 2
+    threads = pu.oracle_threads()
+    A_ref = orc.scores_softmax(_as64(q[b, h]), _as64(k[b, h]), rp[0], cols[0], threads)
+    v_bh = _as64(v[b, h])
+    worst = 0.0
+    for w in variants:
+        z = sah.attn(qd, kd, vd, g, w.K, w.alpha)
+        z_ref = orc.diffuse(A_ref, v_bh, rp[0], cols[0], w.K, w.alpha, threads)
+        worst = max(worst, pu.assert_z_close(_as64(z[b, h]), z_ref, "f32", w.name))
+    print(f"\n[parity] sweep R={R} causal={causal}: {len(variants)} variants, "
+          f"worst {worst:.3e} x tol", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Small randomized shapes, compared on every (b, h)
+# ---------------------------------------------------------------------------
+
+def _small_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(count):
+        n = int(rng.integers(1, 301))
+        r = int(rng.choice([0, 1, 4, 13, 40, n]))
+        g = int(rng.integers(0, min(n, 5) + 1))
+        G = sorted(rng.choice(n, size=g, replace=False).tolist()) if g else []
+        R = int(rng.choice([0, 2, 7, 33]))
+        B = int(rng.integers(1, 4))
+        H = int(rng.integers(1, 4))
+        ng = int(rng.choice([1, B]))
+        causal = bool(rng.integers(0, 2))
+        d = int(rng.choice([16, 32, 64, 128]))
+        dtype = "f32" if rng.integers(0, 2) else "bf16"
+        K = int(rng.choice([0, 1, 2, 5, 10]))
+        alpha = float(rng.choice([0.0, 0.05, 0.1, 0.3, 1.0]))
+        cases.append(dict(n=n, r=r, G=G, R=R, B=B, H=H, ng=ng, causal=causal, d=d,
+                          dtype=dtype, K=K, alpha=alpha, seed=100 + c))
+    return cases
+
+
+@pytest.mark.parametrize("case", _small_cases(48, 7),
+                         ids=lambda c: f"n{c['n']}d{c['d']}{c['dtype']}K{c['K']}")
+def test_attn_small_random(orc, case):
+    c = case
+    tdt = torch.float32 if c["dtype"] == "f32" else torch.bfloat16
+    g = _gpu_graph(c["n"], c["r"], c["G"], c["R"], c["ng"], c["causal"], c["seed"])
+    rp, cols = _check_csr(orc, g, c["n"], c["r"], c["G"], c["R"], c["ng"], c["causal"],
+                          c["seed"])
+    shape = (c["B"], c["H"], c["n"], c["d"])
+    q = make_tensor(shape, c["seed"], tdt)
+    k = make_tensor(shape, c["seed"] + 1, tdt)
+    v = make_tensor(shape, c["seed"] + 2, tdt)
+    z = sah.attn(q.to(DEV), k.to(DEV), v.to(DEV), g, c["K"], c["alpha"])
+    z_h = _as64(z)
+    for b in range(c["B"]):
+        gr = 0 if c["ng"] == 1 else b
+        for h in range(c["H"]):
+            ref = orc.attn(_as64(q[b, h]), _as64(k[b, h]), _as64(v[b, h]), rp[gr], cols[gr],
+                           c["K"], c["alpha"])
+            pu.assert_z_close(z_h[b, h], ref, c["dtype"], f"b={b} h={h}")
+
+
+# ---------------------------------------------------------------------------
+# The pages' worked examples through the C ABI
+# ---------------------------------------------------------------------------
+
+def test_softmax_8pos_gpu():
+    """n=8, radius 1, query position 4 (index 3): scores (0, ln 2, 0) give
+    weights (1/4, 1/2, 1/4) and, with alpha=0, K=1, output (1, 1.5)."""
+    gold = oracle_pins.golden_dict("softmax_8pos.txt")
+    g = sah.build_graph(8, 1, [], 0)
+    d = 32
+    q = torch.zeros(1, 1, 8, d)
+    k = torch.zeros(1, 1, 8, d)
+    q[0, 0, 3, 0] = math.sqrt(d)
+    k[0, 0, 3, 0] = float(gold["scores"][1])
+    v = torch.zeros(1, 1, 8, d)
+    v[0, 0, 2, :2] = torch.tensor([float(x) for x in gold["v3"]])
+    v[0, 0, 3, :2] = torch.tensor([float(x) for x in gold["v4"]])
+    v[0, 0, 4, :2] = torch.tensor([float(x) for x in gold["v5"]])
+    A = sah.scores_softmax(q.to(DEV), k.to(DEV), g).cpu().numpy()
+    rp, _ = g.copy_csr(0)
+    want = np.array([float(x) for x in gold["weights"]])
+    assert np.allclose(A[rp[3]:rp[4]], want, rtol=0, atol=1e-6)
+    z = sah.attn(q.to(DEV), k.to(DEV), v.to(DEV), g, 1, 0.0).cpu().numpy()
+    assert np.allclose(z[0, 0, 3, :2], [float(x) for x in gold["o4"]], rtol=0, atol=1e-6)
+    assert np.all(z[0, 0, 3, 2:] == 0)
+
+
+def test_three_token_gpu():
+    """Imported CSR {0:[0,1], 1:[1,2], 2:[2]}, alpha=0.1, K=2, V=[I|0]: the
+    first row of Z is (0.3475, 0.45, 0.2025)."""
+    gold = oracle_pins.golden_dict("diffusion_3token.txt")
+    rp = np.array([[0, 2, 4, 5]], dtype=np.int64)
+    cols = np.array([0, 1, 1, 2, 2], dtype=np.int32)
+    g = sah.graph_from_csr(3, rp, cols)
+    A = torch.tensor([0.5, 0.5, 0.5, 0.5, 1.0], dtype=torch.float32, device=DEV)
+    v = torch.zeros(1, 1, 3, 32)
+    v[0, 0, :, :3] = torch.eye(3)
+    z = sah.diffuse(A, v.to(DEV), g, int(gold["K"][0]), float(gold["alpha"][0])).cpu().numpy()
+    want = [float(x) for x in gold["Z2_row0_coeffs"]]
+    assert np.allclose(z[0, 0, 0, :3], want, rtol=0, atol=1e-6), z[0, 0, 0, :3]
+
+
+# ---------------------------------------------------------------------------
+# Properties on the GPU
+# ---------------------------------------------------------------------------
+
+def _setup(n=300, r=6, G=(0, 150), R=9, causal=False, dtype=torch.float32, B=2, H=3, d=64):
+    g = sah.build_graph(n, r, list(G), R, 1, causal, 77)
+    shape = (B, H, n, d)
+    q, k, v = (make_tensor(shape, 5 + i, dtype).to(DEV) for i in range(3))
+    return g, q, k, v
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_identity_cases_bitwise(dtype):
+    g, q, k, v = _setup(dtype=dtype)
+    assert torch.equal(sah.attn(q, k, v, g, 0, 0.1), v)
+    assert torch.equal(sah.attn(q, k, v, g, 5, 1.0), v)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_determinism(dtype):
+    g, q, k, v = _setup(dtype=dtype)
+    z1 = sah.attn(q, k, v, g, 5, 0.1)
+    z2 = sah.attn(q, k, v, g, 5, 0.1)
+    assert torch.equal(z1, z2)
+
+
+def test_causality_gpu():
+    g, q, k, v = _setup(causal=True)
+    z0 = sah.attn(q, k, v, g, 5, 0.1)
+    for p in (0, 77, 299):
+        v2 = v.clone()
+        v2[:, :, p] += 1.0
+        z1 = sah.attn(q, k, v2, g, 5, 0.1)
+        assert torch.equal(z0[:, :, :p], z1[:, :, :p]), p
+        assert not torch.equal(z0[:, :, p], z1[:, :, p])
+
+
+def test_reach_gpu():
+    n, r, K, p = 200, 4, 3, 100
+    g, q, k, v = _setup(n=n, r=r, G=(), R=0)
+    z0 = sah.attn(q, k, v, g, K, 0.1)
+    v2 = v.clone()
+    v2[:, :, p] += 1.0
+    z1 = sah.attn(q, k, v2, g, K, 0.1)
+    changed = (z0 != z1).any(dim=-1).any(dim=0).any(dim=0).cpu().numpy()
+    assert np.array_equal(changed, np.abs(np.arange(n) - p) <= K * r)
+
+
+def test_constant_v_fixed_point_gpu():
+    g, q, k, v = _setup()
+    row = make_tensor((1, 1, 1, 64), 9).to(DEV)
+    vc = row.expand_as(v).contiguous()
+    z = sah.attn(q, k, vc, g, 7, 0.1)
+    assert torch.allclose(z, vc, rtol=1e-5, atol=1e-6)
+
+
+def test_rowsums_bf16():
+    g, q, k, v = _setup(dtype=torch.bfloat16)
+    A = sah.scores_softmax(q, k, g).double().cpu().numpy()
+    rp, _ = g.copy_csr(0)
+    nnz = g.nnz[0]
+    for bh in range(6):
+        sums = np.add.reduceat(A[bh * nnz:(bh + 1) * nnz], rp[:-1])
+        assert np.abs(sums - 1).max() <= pu.ROWSUM_BF16
+
+
+# ---------------------------------------------------------------------------
+# Boundary behaviour
+# ---------------------------------------------------------------------------
+
+def test_invalid_arguments_gpu():
+    g, q, k, v = _setup()
+    with pytest.raises(sah.DiffuserError) as ei:
+        sah.attn(q, k, v, g, -1, 0.1)
+    assert ei.value.status == 1
+    with pytest.raises(sah.DiffuserError):
+        sah.attn(q, k, v, g, 5, 1.5)
+    with pytest.raises(sah.DiffuserError) as ei:
+        sah.attn(q[..., :48].contiguous(), k[..., :48].contiguous(), v[..., :48].contiguous(),
+                 g, 5, 0.1)
+    assert ei.value.status == 2
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(sah.DiffuserError):
+        sah.attn(q, k, v, g, 5, 0.1, workspace=ws)
+    with pytest.raises(sah.DiffuserError):
+        sah.attn(q, k, v, g, 5, 0.1, out=v)          # Z aliases V
+    with pytest.raises(sah.DiffuserError):
+        sah.build_graph(10, 1, [4, 2], 0)
+    with pytest.raises(sah.DiffuserError):
+        sah.graph_from_csr(3, np.array([[0, 1, 2, 3]]), np.array([1, 0, 2], dtype=np.int32))
+    gB = sah.build_graph(300, 6, [0], 9, 3, False, 1)
+    with pytest.raises(sah.DiffuserError):
+        sah.attn(q, k, v, gB, 5, 0.1)                # num_graphs not in {1, B}
