@@ -118,15 +118,17 @@ int64_t total_a_elems(const diffuser_graph* g, int32_t B, int32_t H) {
     return (int64_t)H * g->col_off[g->num_graphs];
 }
 
+// Workspace of diffuser_attn: [A][Z ping-pong buffer][row scales (fp32)].
 struct ws_layout {
-    size_t a_bytes, z_bytes, total;
+    size_t a_bytes, z_bytes, s_bytes, total;
 };
 
 ws_layout layout(const diffuser_graph* g, int32_t B, int32_t H, int32_t d_v, diffuser_dtype t) {
     ws_layout w;
     w.a_bytes = align_up((size_t)total_a_elems(g, B, H) * elem_size(t));
     w.z_bytes = align_up((size_t)B * H * (size_t)g->n * d_v * elem_size(t));
-    w.total = w.a_bytes + w.z_bytes;
+    w.s_bytes = align_up((size_t)B * H * (size_t)g->n * sizeof(float));
+    w.total = w.a_bytes + w.z_bytes + w.s_bytes;
     return w;
 }
 
@@ -147,8 +149,8 @@ diffuser_status check_ptr(const void* p, const char* name, bool need16 = true) {
 // K diffusion steps from V into Z, ping-ponging with `tmp` so that the last
 // step writes Z.
 diffuser_status run_diffusion(const diffuser_graph* g, const attn_shape& s, const void* A,
-                              const void* V, void* Z, void* tmp, int32_t K_steps, float alpha,
-                              hipStream_t st) {
+                              const float* row_scale, const void* V, void* Z, void* tmp,
+                              int32_t K_steps, float alpha, hipStream_t st) {
     const size_t zbytes = (size_t)s.B * s.H * (size_t)g->n * s.d * elem_size(s.dtype);
     if (K_steps == 0) {
         hipError_t e = hipMemcpyAsync(Z, V, zbytes, hipMemcpyDeviceToDevice, st);
@@ -159,7 +161,7 @@ diffuser_status run_diffusion(const diffuser_graph* g, const attn_shape& s, cons
     for (int32_t k = 0; k < K_steps; ++k) {
         // Steps K-1, K-3, ... write Z; the others write tmp.
         void* dst = ((K_steps - 1 - k) % 2 == 0) ? Z : tmp;
-        hipError_t e = launch_diffuse_step(*g, s, A, cur, V, dst, alpha, st);
+        hipError_t e = launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, alpha, st);
         if (e != hipSuccess) return hip_fail(e, "diffusion step launch");
         cur = dst;
     }
@@ -447,10 +449,13 @@ diffuser_status diffuser_attn(const void* Q, const void* K, const void* V, diffu
     char* ws = static_cast<char*>(workspace);
     void* A = ws;
     void* tmp = ws + w.a_bytes;
+    float* row_scale = reinterpret_cast<float*>(ws + w.a_bytes + w.z_bytes);
     const float scale_log2 = (float)(1.0 / std::sqrt((double)d_h) * 1.4426950408889634);
-    hipError_t e = launch_scores_softmax(*g, attn_shape{B, H, d_h, dtype}, Q, K, A, scale_log2, st);
+    hipError_t e = launch_scores_softmax(*g, attn_shape{B, H, d_h, dtype}, Q, K, A, row_scale,
+                                         scale_log2, st);
     if (e != hipSuccess) return hip_fail(e, "score/softmax launch");
-    return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, V, Z, tmp, K_steps, alpha, st);
+    return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, row_scale, V, Z, tmp, K_steps,
+                         alpha, st);
 }
 
 diffuser_status diffuser_scores_softmax(const void* Q, const void* K, diffuser_dtype dtype,
@@ -472,7 +477,7 @@ diffuser_status diffuser_scores_softmax(const void* Q, const void* K, diffuser_d
     if (overlaps(A_out, a_bytes, Q, qk_bytes) || overlaps(A_out, a_bytes, K, qk_bytes))
         return fail(DIFFUSER_ERR_INVALID_ARG, "A_out overlaps Q or K");
     const float scale_log2 = (float)(1.0 / std::sqrt((double)d_h) * 1.4426950408889634);
-    hipError_t e = launch_scores_softmax(*g, attn_shape{B, H, d_h, dtype}, Q, K, A_out,
+    hipError_t e = launch_scores_softmax(*g, attn_shape{B, H, d_h, dtype}, Q, K, A_out, nullptr,
                                          scale_log2, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "score/softmax launch");
     return DIFFUSER_OK;
@@ -502,8 +507,8 @@ diffuser_status diffuser_diffuse(const void* A, const void* V, diffuser_dtype dt
         (K_steps >= 2 && overlaps(Z, vz_bytes, workspace, z_need)))
         return fail(DIFFUSER_ERR_INVALID_ARG, "Z overlaps an input or the workspace");
     // The Z ping-pong buffer sits at the start of the caller's workspace.
-    return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, V, Z, workspace, K_steps, alpha,
-                         static_cast<hipStream_t>(stream));
+    return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, nullptr, V, Z, workspace, K_steps,
+                         alpha, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

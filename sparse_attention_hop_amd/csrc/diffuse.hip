@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_diffuse_step(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ row_ptr,
                     const int32_t* __restrict__ col_idx, const int64_t* __restrict__ col_off,
                     const T* __restrict__ A, const T* __restrict__ Zk, const T* __restrict__ V,
-                    T* __restrict__ Zn, float alpha) {
+                    T* __restrict__ Zn, const float* __restrict__ row_scale, float alpha) {
     constexpr int E = chunk<T>::kElems;
     constexpr int L = D / E;
     constexpr int EPI = kWave / L;
@@ -63,7 +63,8 @@ void k_diffuse_step(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __r
         const int64_t o = ((int64_t)bh * n + i) * D + sub * E;
         float v[E];
         chunk<T>::load(V + o, v);
-        const float keep = 1.0f - alpha;
+        const float keep =
+            row_scale == nullptr ? 1.0f - alpha : (1.0f - alpha) * row_scale[(int64_t)bh * n + i];
 #pragma unroll
         for (int c = 0; c < E; ++c) v[c] = keep * acc[c] + alpha * v[c];
         chunk<T>::store(Zn + o, v);
@@ -72,23 +73,25 @@ void k_diffuse_step(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __r
 
 template <typename T, int D>
 hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
-                    const void* V, void* Zn, float alpha, hipStream_t st) {
+                    const void* V, void* Zn, const float* row_scale, float alpha,
+                    hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
     hipLaunchKernelGGL((k_diffuse_step<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st, g.n,
                        s.H, g.num_graphs, g.d_row_ptr, g.d_col_idx, g.d_col_off,
                        static_cast<const T*>(A), static_cast<const T*>(Zk),
-                       static_cast<const T*>(V), static_cast<T*>(Zn), alpha);
+                       static_cast<const T*>(V), static_cast<T*>(Zn), row_scale, alpha);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_d(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
-                    const void* V, void* Zn, float alpha, hipStream_t st) {
+                    const void* V, void* Zn, const float* row_scale, float alpha,
+                    hipStream_t st) {
     switch (s.d) {
-        case 16: return launch_t<T, 16>(g, s, A, Zk, V, Zn, alpha, st);
-        case 32: return launch_t<T, 32>(g, s, A, Zk, V, Zn, alpha, st);
-        case 64: return launch_t<T, 64>(g, s, A, Zk, V, Zn, alpha, st);
-        case 128: return launch_t<T, 128>(g, s, A, Zk, V, Zn, alpha, st);
+        case 16: return launch_t<T, 16>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
+        case 32: return launch_t<T, 32>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
+        case 64: return launch_t<T, 64>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
+        case 128: return launch_t<T, 128>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -96,10 +99,11 @@ hipError_t launch_d(const diffuser_graph& g, const attn_shape& s, const void* A,
 }  // namespace
 
 hipError_t launch_diffuse_step(const diffuser_graph& g, const attn_shape& s, const void* A,
-                               const void* Zk, const void* V, void* Zn, float alpha,
-                               hipStream_t st) {
-    if (s.dtype == DIFFUSER_F32) return launch_d<float>(g, s, A, Zk, V, Zn, alpha, st);
-    return launch_d<bf16_t>(g, s, A, Zk, V, Zn, alpha, st);
+                               const void* Zk, const void* V, void* Zn, const float* row_scale,
+                               float alpha, hipStream_t st) {
+    if (s.dtype == DIFFUSER_F32)
+        return launch_d<float>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
+    return launch_d<bf16_t>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
 }
 
 }  // namespace diffuser

@@ -56,12 +56,16 @@ struct attn_shape {
     diffuser_dtype dtype;
 };
 
+// Writes A; when row_scale != nullptr also 1 / (sum of each row's stored
+// weights) per (b, h, row).
 hipError_t launch_scores_softmax(const diffuser_graph& g, const attn_shape& s, const void* Q,
-                                 const void* K, void* A, float scale_log2, hipStream_t st);
+                                 const void* K, void* A, float* row_scale, float scale_log2,
+                                 hipStream_t st);
 
-// One step: Zn = (1 - alpha) * A Zk + alpha * V.
+// One step: Zn = (1 - alpha) * c_i * (A Zk)_i + alpha * V_i with c_i =
+// row_scale[(b, h, i)] or 1 when row_scale == nullptr.
 hipError_t launch_diffuse_step(const diffuser_graph& g, const attn_shape& s, const void* A,
-                               const void* Zk, const void* V, void* Zn, float alpha,
-                               hipStream_t st);
+                               const void* Zk, const void* V, void* Zn, const float* row_scale,
+                               float alpha, hipStream_t st);
 
 }  // namespace diffuser

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ row_ptr,
                       const int32_t* __restrict__ col_idx, const int64_t* __restrict__ col_off,
                       const T* __restrict__ Q, const T* __restrict__ K, T* __restrict__ A,
-                      float scale_log2) {
+                      float* __restrict__ row_scale, float scale_log2) {
     constexpr int E = chunk<T>::kElems;
     constexpr int L = D / E;          // lanes per edge
     constexpr int EPI = kWave / L;    // edges per iteration
@@ -81,6 +81,7 @@ void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* _
     }
     const float inv = 1.0f / l;
 
+    float stored_sum = 0.0f;  // sum of the weights as stored (after rounding)
     for (int64_t base = e0; base < e1; base += EPI) {
         const int64_t e = base + grp;
         const bool valid = e < e1;
@@ -93,29 +94,41 @@ void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* _
         }
 #pragma unroll
         for (int off = 1; off < L; off <<= 1) dot += __shfl_xor(dot, off);
-        if (valid && sub == 0) chunk<T>::store1(Ab + e, fast_exp2(dot * scale_log2 - m) * inv);
+        if (valid && sub == 0) {
+            const float a = fast_exp2(dot * scale_log2 - m) * inv;
+            chunk<T>::store1(Ab + e, a);
+            stored_sum += chunk<T>::round(a);
+        }
+    }
+    if (row_scale != nullptr) {
+        // 1 / (row sum of the stored weights): applied by the diffusion step,
+        // it keeps the stored operator row-stochastic, so storage rounding
+        // of A does not compound over the K steps.
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) stored_sum += __shfl_xor(stored_sum, off);
+        if (lane == 0) row_scale[(int64_t)bh * n + i] = 1.0f / stored_sum;
     }
 }
 
 template <typename T, int D>
 hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
-                    void* A, float scale_log2, hipStream_t st) {
+                    void* A, float* row_scale, float scale_log2, hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
     hipLaunchKernelGGL((k_scores_softmax<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st, g.n,
                        s.H, g.num_graphs, g.d_row_ptr, g.d_col_idx, g.d_col_off,
                        static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<T*>(A),
-                       scale_log2);
+                       row_scale, scale_log2);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_d(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
-                    void* A, float scale_log2, hipStream_t st) {
+                    void* A, float* row_scale, float scale_log2, hipStream_t st) {
     switch (s.d) {
-        case 16: return launch_t<T, 16>(g, s, Q, K, A, scale_log2, st);
-        case 32: return launch_t<T, 32>(g, s, Q, K, A, scale_log2, st);
-        case 64: return launch_t<T, 64>(g, s, Q, K, A, scale_log2, st);
-        case 128: return launch_t<T, 128>(g, s, Q, K, A, scale_log2, st);
+        case 16: return launch_t<T, 16>(g, s, Q, K, A, row_scale, scale_log2, st);
+        case 32: return launch_t<T, 32>(g, s, Q, K, A, row_scale, scale_log2, st);
+        case 64: return launch_t<T, 64>(g, s, Q, K, A, row_scale, scale_log2, st);
+        case 128: return launch_t<T, 128>(g, s, Q, K, A, row_scale, scale_log2, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -123,9 +136,10 @@ hipError_t launch_d(const diffuser_graph& g, const attn_shape& s, const void* Q,
 }  // namespace
 
 hipError_t launch_scores_softmax(const diffuser_graph& g, const attn_shape& s, const void* Q,
-                                 const void* K, void* A, float scale_log2, hipStream_t st) {
-    if (s.dtype == DIFFUSER_F32) return launch_d<float>(g, s, Q, K, A, scale_log2, st);
-    return launch_d<bf16_t>(g, s, Q, K, A, scale_log2, st);
+                                 const void* K, void* A, float* row_scale, float scale_log2,
+                                 hipStream_t st) {
+    if (s.dtype == DIFFUSER_F32) return launch_d<float>(g, s, Q, K, A, row_scale, scale_log2, st);
+    return launch_d<bf16_t>(g, s, Q, K, A, row_scale, scale_log2, st);
 }
 
 }  // namespace diffuser

@@ -36,6 +36,7 @@ template <> struct chunk<float> {
         *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     }
     __device__ __forceinline__ static float load1(const float* p) { return *p; }
+    __device__ __forceinline__ static float round(float v) { return v; }
     __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
 };
 
@@ -63,6 +64,8 @@ template <> struct chunk<bf16_t> {
     __device__ __forceinline__ static void store1(bf16_t* p, float v) {
         p->bits = (uint16_t)f32_to_bf16(v);
     }
+    // The value as it reads back after a store.
+    __device__ __forceinline__ static float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 };
 
 // Offset (in elements) of the A block of (b, h): graphs are per batch element

@@ -3,7 +3,12 @@
 Tolerances (on Z, against the double-precision oracle):
   fp32 storage: |z - z_ref| <= 1e-4 * max(|z_ref|, 1e-2)  (max relative error
                 1e-4 with a 1e-2 floor on the denominator);
-  bf16 storage: |z - z_ref| <= 2e-2 absolute.
+  bf16 storage: |z - z_ref| <= 2e-2 absolute at K = 5, alpha = 0.1 (the
+                workloads' setting). A and every Z_k are stored in bf16, so
+                rounding errors of up to 2^-8 relative enter at each of the
+                steps and decay by (1 - alpha) per later step: the error grows
+                with min(K, 1/alpha). For other (K, alpha) the bound scales by
+                max(1, min(K, 1/alpha) / 5).
 Edge-softmax rows: |sum_j A_ij - 1| <= 1e-5 (fp32), <= 2^-8 + 1e-6 (bf16,
 whose round-to-nearest-even step is at most 2^-8 relative per weight).
 """
@@ -24,16 +29,21 @@ def oracle_threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def z_error(got: np.ndarray, ref: np.ndarray, dtype: str) -> float:
+def bf16_tolerance(K: int = 5, alpha: float = 0.1) -> float:
+    steps = min(K, 1.0 / alpha) if alpha > 0 else K
+    return BF16_ABS * max(1.0, steps / 5.0)
+
+
+def z_error(got: np.ndarray, ref: np.ndarray, dtype: str, K: int = 5, alpha: float = 0.1) -> float:
     """Error in units of the tolerance (<= 1 passes)."""
     d = np.abs(got.astype(np.float64) - ref)
     if dtype == "f32":
         return float((d / (F32_REL * np.maximum(np.abs(ref), F32_FLOOR))).max(initial=0.0))
-    return float(d.max(initial=0.0) / BF16_ABS)
+    return float(d.max(initial=0.0) / bf16_tolerance(K, alpha))
 
 
-def assert_z_close(got, ref, dtype, what=""):
-    e = z_error(got, ref, dtype)
+def assert_z_close(got, ref, dtype, what="", K: int = 5, alpha: float = 0.1):
+    e = z_error(got, ref, dtype, K, alpha)
     assert e <= 1.0, f"{what}: error {e:.3f} x tolerance ({dtype})"
     return e
 

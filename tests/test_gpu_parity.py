@@ -199,7 +199,7 @@ def test_attn_small_random(orc, case):
         for h in range(c["H"]):
             ref = orc.attn(_as64(q[b, h]), _as64(k[b, h]), _as64(v[b, h]), rp[gr], cols[gr],
                            c["K"], c["alpha"])
-            pu.assert_z_close(z_h[b, h], ref, c["dtype"], f"b={b} h={h}")
+            pu.assert_z_close(z_h[b, h], ref, c["dtype"], f"b={b} h={h}", c["K"], c["alpha"])
 
 
 # ---------------------------------------------------------------------------
