@@ -39,7 +39,7 @@ def algorithmic_bytes(w, g, K):
     """Byte model: A and Z at the storage size, graph arrays once per graph
     per pass, dense or masked work avoided by the method not counted."""
     s = 2 if w.dtype == "bf16" else 4
-    nnz_tot = g.a_numel(w.B, w.H)
+    nnz_tot = g.edges(w.B, w.H)
     bh_nd = w.B * w.H * w.n * w.d
     score = 2 * bh_nd * s + nnz_tot * s + graph_bytes(g, w.n)
     diffusion = K * (s * nnz_tot + graph_bytes(g, w.n)) + (3 * K - 1) * bh_nd * s
@@ -143,7 +143,7 @@ def main():
                          reps, torch)
     t_step = t_diff / max(w.K, 1)
 
-    nnz_pass = g.a_numel(w.B, w.H)
+    nnz_pass = g.edges(w.B, w.H)
     diffused = nnz_pass * w.K
     score_b, diff_b = algorithmic_bytes(w, g, w.K)
     per_launch = diff_b / max(w.K, 1)

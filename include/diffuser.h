@@ -106,16 +106,32 @@ DIFFUSER_API diffuser_status diffuser_graph_from_csr(int64_t n, int32_t num_grap
                                         const int32_t* col_idx_host, void* stream,
                                         diffuser_graph** out);
 
-/* n, num_graphs and (if nnz != NULL) nnz[num_graphs] edges per graph. Any
- * output pointer may be NULL. */
-DIFFUSER_API diffuser_status diffuser_graph_info(const diffuser_graph* g, int64_t* n, int32_t* num_graphs,
-                                    int64_t* nnz);
+/* n, num_graphs, nnz[num_graphs] edges per graph and slots[num_graphs]
+ * weight slots per graph (see diffuser_graph_copy_slots). Any output
+ * pointer may be NULL. */
+DIFFUSER_API diffuser_status diffuser_graph_info(const diffuser_graph* g, int64_t* n,
+                                                 int32_t* num_graphs, int64_t* nnz,
+                                                 int64_t* slots);
 
 /* Copies graph `graph` to HOST arrays row_ptr[n+1] and col_idx[nnz];
  * synchronous on return. */
 DIFFUSER_API diffuser_status diffuser_graph_copy_csr(const diffuser_graph* g, int32_t graph,
                                         int64_t* row_ptr_host, int32_t* col_idx_host,
                                         void* stream);
+
+/* Copies the weight-slot layout of graph `graph` to HOST arrays:
+ * slot_ptr[n+1] (row i owns slots slot_ptr[i] .. slot_ptr[i+1]-1) and
+ * slot_col[slots] (the key column of each slot, or -1 for a padding slot,
+ * whose weight is always 0). Every edge of the graph owns exactly one slot.
+ * For a built graph, a global row's slots are its columns in order, padded
+ * to a multiple of 8; any other row has three segments, each a multiple of
+ * 8 slots: the window as 8-column blocks from (lo & ~7), the g globals in
+ * order (padding where a global lies in the window or, when causal, above
+ * the row), and the random columns in ascending order. An imported graph's
+ * slots are its CSR entries. Synchronous on return. */
+DIFFUSER_API diffuser_status diffuser_graph_copy_slots(const diffuser_graph* g, int32_t graph,
+                                                       int64_t* slot_ptr_host,
+                                                       int32_t* slot_col_host, void* stream);
 
 /* Frees the graph (waits for the device first). Accepts NULL. */
 DIFFUSER_API void diffuser_graph_destroy(diffuser_graph* g);
@@ -130,9 +146,11 @@ DIFFUSER_API diffuser_status diffuser_attn_workspace_size(const diffuser_graph* 
 /*
  * Layouts shared by the compute entry points:
  *  Q, K : [B][H][n][d_h];  V, Z : [B][H][n][d_v];  all of `dtype`.
- *  A    : edge weights in CSR order, concatenated over (b, h) in row-major
- *         (b, h) order; the block of (b, h) holds nnz(graph(b)) values and
- *         starts at sum_{b' < b} H * nnz(graph(b')) + h * nnz(graph(b)).
+ *  A    : edge weights in the graph's weight-slot layout
+ *         (diffuser_graph_copy_slots), concatenated over (b, h) in row-major
+ *         (b, h) order; the block of (b, h) holds slots(graph(b)) values
+ *         and starts at sum_{b' < b} H * slots(graph(b')) +
+ *         h * slots(graph(b)). Padding slots hold 0.
  * Supported: d_h, d_v in {16, 32, 64, 128}; pointers 16-byte aligned
  * (A: element aligned); Z must not overlap Q, K, V, A or the workspace.
  */

@@ -34,7 +34,8 @@ STATUS_NAMES = {
 # Every symbol the header declares.
 ABI_SYMBOLS = (
     "diffuser_build_graph", "diffuser_graph_from_csr", "diffuser_graph_info",
-    "diffuser_graph_copy_csr", "diffuser_graph_destroy", "diffuser_attn_workspace_size",
+    "diffuser_graph_copy_csr", "diffuser_graph_copy_slots", "diffuser_graph_destroy",
+    "diffuser_attn_workspace_size",
     "diffuser_attn", "diffuser_scores_softmax", "diffuser_diffuse",
     "diffuser_status_string", "diffuser_last_error",
 )
@@ -79,10 +80,12 @@ def load_library(path: str = LIB_PATH):
     lib.diffuser_build_graph.restype = st
     lib.diffuser_graph_from_csr.argtypes = [i64, i32, p, p, p, ctypes.POINTER(p)]
     lib.diffuser_graph_from_csr.restype = st
-    lib.diffuser_graph_info.argtypes = [p, p, p, p]
+    lib.diffuser_graph_info.argtypes = [p, p, p, p, p]
     lib.diffuser_graph_info.restype = st
     lib.diffuser_graph_copy_csr.argtypes = [p, i32, p, p, p]
     lib.diffuser_graph_copy_csr.restype = st
+    lib.diffuser_graph_copy_slots.argtypes = [p, i32, p, p, p]
+    lib.diffuser_graph_copy_slots.restype = st
     lib.diffuser_graph_destroy.argtypes = [p]
     lib.diffuser_graph_destroy.restype = None
     lib.diffuser_attn_workspace_size.argtypes = [p, i32, i32, i32, i32, st, ctypes.POINTER(sz)]
@@ -136,12 +139,16 @@ class Graph:
         self.handle = ctypes.c_void_p(handle)
         n = ctypes.c_int64()
         ng = ctypes.c_int32()
-        _check(self._lib.diffuser_graph_info(self.handle, ctypes.byref(n), ctypes.byref(ng), None))
+        _check(self._lib.diffuser_graph_info(self.handle, ctypes.byref(n), ctypes.byref(ng), None,
+                                             None))
         self.n, self.num_graphs = int(n.value), int(ng.value)
         nnz = np.zeros(self.num_graphs, dtype=np.int64)
+        slots = np.zeros(self.num_graphs, dtype=np.int64)
         _check(self._lib.diffuser_graph_info(self.handle, None, None,
-                                             nnz.ctypes.data_as(ctypes.c_void_p)))
+                                             nnz.ctypes.data_as(ctypes.c_void_p),
+                                             slots.ctypes.data_as(ctypes.c_void_p)))
         self.nnz = [int(x) for x in nnz]
+        self.slots = [int(x) for x in slots]
         self.desc = desc
 
     def copy_csr(self, graph: int = 0):
@@ -154,16 +161,33 @@ class Graph:
                                                  ctypes.c_void_p(_stream_handle())))
         return rp, ci[: self.nnz[graph]]
 
-    def a_numel(self, B: int, H: int) -> int:
+    def copy_slots(self, graph: int = 0):
+        """(slot_ptr int64[n+1], slot_col int32[slots]) of one graph: where the
+        edge weights of each row live in A; column -1 marks padding."""
+        sp = np.zeros(self.n + 1, dtype=np.int64)
+        sc = np.zeros(max(self.slots[graph], 1), dtype=np.int32)
+        _check(self._lib.diffuser_graph_copy_slots(self.handle, graph,
+                                                   sp.ctypes.data_as(ctypes.c_void_p),
+                                                   sc.ctypes.data_as(ctypes.c_void_p),
+                                                   ctypes.c_void_p(_stream_handle())))
+        return sp, sc[: self.slots[graph]]
+
+    def edges(self, B: int, H: int) -> int:
+        """Edges summed over every (b, h) pair (padding slots excluded)."""
         if self.num_graphs == 1:
             return B * H * self.nnz[0]
         return H * sum(self.nnz)
 
+    def a_numel(self, B: int, H: int) -> int:
+        if self.num_graphs == 1:
+            return B * H * self.slots[0]
+        return H * sum(self.slots)
+
     def a_offset(self, b: int, h: int, H: int) -> int:
         """Start of the (b, h) block inside the A layout."""
         if self.num_graphs == 1:
-            return (b * H + h) * self.nnz[0]
-        return H * sum(self.nnz[:b]) + h * self.nnz[b]
+            return (b * H + h) * self.slots[0]
+        return H * sum(self.slots[:b]) + h * self.slots[b]
 
     def close(self):
         if self.handle is not None and self.handle.value:

@@ -20,6 +20,7 @@ thread_local std::string g_last_error;
 
 constexpr int64_t kMaxN = 1ll << 24;
 constexpr int32_t kMaxSampledRandom = 1024;
+constexpr int64_t kMaxBoundEntries = 1ll << 26;   // 256 MB of chunk bounds
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -54,14 +55,20 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_global);
     hipFree(g->d_rnd);
     hipFree(g->d_rnd_cnt);
-    hipFree(g->d_win_off);
+    hipFree(g->d_slot_ptr);
+    hipFree(g->d_slot_col);
+    hipFree(g->d_slot_off);
+    hipFree(g->d_bnd);
     g->d_row_ptr = nullptr;
     g->d_col_idx = nullptr;
     g->d_col_off = nullptr;
     g->d_global = nullptr;
     g->d_rnd = nullptr;
     g->d_rnd_cnt = nullptr;
-    g->d_win_off = nullptr;
+    g->d_slot_ptr = nullptr;
+    g->d_slot_col = nullptr;
+    g->d_slot_off = nullptr;
+    g->d_bnd = nullptr;
 }
 
 diffuser_status alloc_status(hipError_t e, const char* what) {
@@ -113,9 +120,10 @@ diffuser_status check_shape(const diffuser_graph* g, int32_t B, int32_t H, int32
     return DIFFUSER_OK;
 }
 
+// Elements of A: every (b, h) holds the weight slots of its graph.
 int64_t total_a_elems(const diffuser_graph* g, int32_t B, int32_t H) {
-    if (g->num_graphs == 1) return (int64_t)B * H * g->nnz[0];
-    return (int64_t)H * g->col_off[g->num_graphs];
+    if (g->num_graphs == 1) return (int64_t)B * H * g->slots[0];
+    return (int64_t)H * g->slot_off[g->num_graphs];
 }
 
 // Workspace of diffuser_attn: [A][Z ping-pong buffer][row scales (fp32)].
@@ -157,11 +165,13 @@ diffuser_status run_diffusion(const diffuser_graph* g, const attn_shape& s, cons
         if (e != hipSuccess) return hip_fail(e, "copy of V into Z");
         return DIFFUSER_OK;
     }
+    const bool fast = fast_diffuse_supported(*g, s) && aligned16(A);
     const void* cur = V;
     for (int32_t k = 0; k < K_steps; ++k) {
         // Steps K-1, K-3, ... write Z; the others write tmp.
         void* dst = ((K_steps - 1 - k) % 2 == 0) ? Z : tmp;
-        hipError_t e = launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, alpha, st);
+        hipError_t e = fast ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, alpha, st)
+                            : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, alpha, st);
         if (e != hipSuccess) return hip_fail(e, "diffusion step launch");
         cur = dst;
     }
@@ -241,29 +251,33 @@ diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stre
 
     const int64_t rows = (int64_t)g->num_graphs * n;
     int32_t* d_deg = nullptr;
+    int32_t* d_slots = nullptr;
     int32_t* d_status = nullptr;
-    int64_t* d_maxdeg = nullptr;
+    int64_t* d_max = nullptr;
     hipError_t e;
     if ((e = dev_alloc(&g->d_global, g->num_global)) != hipSuccess ||
         (e = dev_alloc(&g->d_rnd, (size_t)rows * std::max(g->rnd_width, 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_rnd_cnt, rows)) != hipSuccess ||
-        (e = dev_alloc(&g->d_win_off, rows)) != hipSuccess ||
         (e = dev_alloc(&g->d_row_ptr, (size_t)g->num_graphs * (n + 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_col_off, g->num_graphs + 1)) != hipSuccess ||
+        (e = dev_alloc(&g->d_slot_ptr, (size_t)g->num_graphs * (n + 1))) != hipSuccess ||
+        (e = dev_alloc(&g->d_slot_off, g->num_graphs + 1)) != hipSuccess ||
         (e = dev_alloc(&d_deg, rows)) != hipSuccess ||
+        (e = dev_alloc(&d_slots, rows)) != hipSuccess ||
         (e = dev_alloc(&d_status, 1)) != hipSuccess ||
-        (e = dev_alloc(&d_maxdeg, g->num_graphs)) != hipSuccess) {
+        (e = dev_alloc(&d_max, 2 * (size_t)g->num_graphs)) != hipSuccess) {
         hipFree(d_deg);
+        hipFree(d_slots);
         hipFree(d_status);
-        hipFree(d_maxdeg);
+        hipFree(d_max);
         return alloc_status(e, "device allocation for the graph build");
     }
     struct tmp_guard {
-        void* p[3];
+        void* p[4];
         ~tmp_guard() {
             for (void* q : p) hipFree(q);
         }
-    } tmps{{d_deg, d_status, d_maxdeg}};
+    } tmps{{d_deg, d_slots, d_status, d_max}};
 
     if (g->num_global > 0 &&
         (e = hipMemcpyAsync(g->d_global, desc->global_idx, sizeof(int32_t) * g->num_global,
@@ -271,34 +285,58 @@ diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stre
         return hip_fail(e, "copy of global_idx");
     if ((e = hipMemsetAsync(d_status, 0, sizeof(int32_t), st)) != hipSuccess)
         return hip_fail(e, "status clear");
-    if ((e = launch_draw(*g, d_deg, d_status, st)) != hipSuccess) return hip_fail(e, "draw launch");
-    if ((e = launch_scan(*g, d_deg, d_maxdeg, st)) != hipSuccess) return hip_fail(e, "scan launch");
+    if ((e = launch_draw(*g, d_deg, d_slots, d_status, st)) != hipSuccess)
+        return hip_fail(e, "draw launch");
+    if ((e = launch_scan(n, g->num_graphs, d_deg, g->d_row_ptr, d_max, st)) != hipSuccess ||
+        (e = launch_scan(n, g->num_graphs, d_slots, g->d_slot_ptr, d_max + g->num_graphs, st)) !=
+            hipSuccess)
+        return hip_fail(e, "scan launch");
     int32_t status = 0;
-    std::vector<int64_t> maxdeg(g->num_graphs);
-    std::vector<int64_t> last(g->num_graphs);
+    std::vector<int64_t> maxes(2 * (size_t)g->num_graphs);
+    std::vector<int64_t> last_e(g->num_graphs), last_s(g->num_graphs);
     if ((e = hipMemcpyAsync(&status, d_status, sizeof(int32_t), hipMemcpyDeviceToHost, st)) !=
             hipSuccess ||
-        (e = hipMemcpyAsync(maxdeg.data(), d_maxdeg, sizeof(int64_t) * g->num_graphs,
+        (e = hipMemcpyAsync(maxes.data(), d_max, sizeof(int64_t) * 2 * g->num_graphs,
                             hipMemcpyDeviceToHost, st)) != hipSuccess)
         return hip_fail(e, "copy of build status");
     for (int32_t gr = 0; gr < g->num_graphs; ++gr) {
-        if ((e = hipMemcpyAsync(&last[gr], g->d_row_ptr + (int64_t)gr * (n + 1) + n,
+        if ((e = hipMemcpyAsync(&last_e[gr], g->d_row_ptr + (int64_t)gr * (n + 1) + n,
+                                sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess ||
+            (e = hipMemcpyAsync(&last_s[gr], g->d_slot_ptr + (int64_t)gr * (n + 1) + n,
                                 sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess)
             return hip_fail(e, "copy of edge counts");
     }
     if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "graph draw");
     if (status != 0)
         return fail(DIFFUSER_ERR_INTERNAL, "random draw budget (2^20 draws per row) exhausted");
-    g->nnz = last;
+    g->nnz = last_e;
+    g->slots = last_s;
     g->col_off.assign(g->num_graphs + 1, 0);
-    for (int32_t gr = 0; gr < g->num_graphs; ++gr) g->col_off[gr + 1] = g->col_off[gr] + last[gr];
-    g->max_row_len = *std::max_element(maxdeg.begin(), maxdeg.end());
-    if ((e = dev_alloc(&g->d_col_idx, g->col_off[g->num_graphs])) != hipSuccess)
-        return alloc_status(e, "device allocation of col_idx");
+    g->slot_off.assign(g->num_graphs + 1, 0);
+    for (int32_t gr = 0; gr < g->num_graphs; ++gr) {
+        g->col_off[gr + 1] = g->col_off[gr] + last_e[gr];
+        g->slot_off[gr + 1] = g->slot_off[gr] + last_s[gr];
+    }
+    g->max_row_len = *std::max_element(maxes.begin(), maxes.begin() + g->num_graphs);
+    g->max_row_slots = *std::max_element(maxes.begin() + g->num_graphs, maxes.end());
+    if ((e = dev_alloc(&g->d_col_idx, g->col_off[g->num_graphs])) != hipSuccess ||
+        (e = dev_alloc(&g->d_slot_col, g->slot_off[g->num_graphs])) != hipSuccess)
+        return alloc_status(e, "device allocation of the columns");
     if ((e = hipMemcpyAsync(g->d_col_off, g->col_off.data(), sizeof(int64_t) * (g->num_graphs + 1),
-                            hipMemcpyHostToDevice, st)) != hipSuccess)
-        return hip_fail(e, "copy of col offsets");
+                            hipMemcpyHostToDevice, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(g->d_slot_off, g->slot_off.data(),
+                            sizeof(int64_t) * (g->num_graphs + 1), hipMemcpyHostToDevice, st)) !=
+            hipSuccess)
+        return hip_fail(e, "copy of offsets");
     if ((e = launch_fill(*g, st)) != hipSuccess) return hip_fail(e, "fill launch");
+    // Chunk bounds for the LDS-streamed kernels (skipped when the table
+    // would be large; those graphs use the generic kernels).
+    const int64_t nchunks = (n + g->chunk - 1) / g->chunk;
+    if (rows * (nchunks + 1) <= kMaxBoundEntries) {
+        if ((e = dev_alloc(&g->d_bnd, (size_t)(rows * (nchunks + 1)))) != hipSuccess)
+            return alloc_status(e, "device allocation of the chunk bounds");
+        if ((e = launch_bounds(*g, st)) != hipSuccess) return hip_fail(e, "bounds launch");
+    }
     if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "graph fill");
     guard.g = nullptr;
     *out = g;
@@ -354,19 +392,35 @@ diffuser_status diffuser_graph_from_csr(int64_t n, int32_t num_graphs, const int
     g->nnz = nnz;
     g->col_off = col_off;
     g->max_row_len = max_len;
+    // The weight slots of an imported graph are its CSR entries.
+    g->slots = nnz;
+    g->slot_off = col_off;
+    g->max_row_slots = max_len;
     hipGetDevice(&g->device);
     hipError_t e;
+    const size_t rp_bytes = sizeof(int64_t) * num_graphs * (n + 1);
+    const size_t ci_bytes = sizeof(int32_t) * col_off[num_graphs];
+    const size_t off_bytes = sizeof(int64_t) * (num_graphs + 1);
     if ((e = dev_alloc(&g->d_row_ptr, (size_t)num_graphs * (n + 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_col_idx, col_off[num_graphs])) != hipSuccess ||
-        (e = dev_alloc(&g->d_col_off, num_graphs + 1)) != hipSuccess)
+        (e = dev_alloc(&g->d_col_off, num_graphs + 1)) != hipSuccess ||
+        (e = dev_alloc(&g->d_slot_ptr, (size_t)num_graphs * (n + 1))) != hipSuccess ||
+        (e = dev_alloc(&g->d_slot_col, col_off[num_graphs])) != hipSuccess ||
+        (e = dev_alloc(&g->d_slot_off, num_graphs + 1)) != hipSuccess)
         return alloc_status(e, "device allocation of the imported graph");
-    if ((e = hipMemcpyAsync(g->d_row_ptr, row_ptr_host, sizeof(int64_t) * num_graphs * (n + 1),
-                            hipMemcpyHostToDevice, st)) != hipSuccess ||
-        (col_off[num_graphs] > 0 &&
-         (e = hipMemcpyAsync(g->d_col_idx, col_idx_host, sizeof(int32_t) * col_off[num_graphs],
-                             hipMemcpyHostToDevice, st)) != hipSuccess) ||
-        (e = hipMemcpyAsync(g->d_col_off, col_off.data(), sizeof(int64_t) * (num_graphs + 1),
-                            hipMemcpyHostToDevice, st)) != hipSuccess)
+    if ((e = hipMemcpyAsync(g->d_row_ptr, row_ptr_host, rp_bytes, hipMemcpyHostToDevice, st)) !=
+            hipSuccess ||
+        (e = hipMemcpyAsync(g->d_slot_ptr, row_ptr_host, rp_bytes, hipMemcpyHostToDevice, st)) !=
+            hipSuccess ||
+        (ci_bytes > 0 &&
+         ((e = hipMemcpyAsync(g->d_col_idx, col_idx_host, ci_bytes, hipMemcpyHostToDevice, st)) !=
+              hipSuccess ||
+          (e = hipMemcpyAsync(g->d_slot_col, col_idx_host, ci_bytes, hipMemcpyHostToDevice, st)) !=
+              hipSuccess)) ||
+        (e = hipMemcpyAsync(g->d_col_off, col_off.data(), off_bytes, hipMemcpyHostToDevice, st)) !=
+            hipSuccess ||
+        (e = hipMemcpyAsync(g->d_slot_off, col_off.data(), off_bytes, hipMemcpyHostToDevice,
+                            st)) != hipSuccess)
         return hip_fail(e, "copy of the imported graph");
     if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "graph import");
     guard.g = nullptr;
@@ -375,12 +429,36 @@ diffuser_status diffuser_graph_from_csr(int64_t n, int32_t num_graphs, const int
 }
 
 diffuser_status diffuser_graph_info(const diffuser_graph* g, int64_t* n, int32_t* num_graphs,
-                                    int64_t* nnz) {
+                                    int64_t* nnz, int64_t* slots) {
     g_last_error.clear();
     if (auto s = check_graph(g)) return s;
     if (n) *n = g->n;
     if (num_graphs) *num_graphs = g->num_graphs;
     if (nnz) std::copy(g->nnz.begin(), g->nnz.end(), nnz);
+    if (slots) std::copy(g->slots.begin(), g->slots.end(), slots);
+    return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_graph_copy_slots(const diffuser_graph* g, int32_t graph,
+                                          int64_t* slot_ptr_host, int32_t* slot_col_host,
+                                          void* stream) {
+    g_last_error.clear();
+    if (auto s = check_graph(g)) return s;
+    if (graph < 0 || graph >= g->num_graphs)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "graph index out of range");
+    if (!slot_ptr_host || (!slot_col_host && g->slots[graph] > 0))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "NULL output array");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if ((e = hipMemcpyAsync(slot_ptr_host, g->d_slot_ptr + (int64_t)graph * (g->n + 1),
+                            sizeof(int64_t) * (g->n + 1), hipMemcpyDeviceToHost, st)) !=
+            hipSuccess ||
+        (g->slots[graph] > 0 &&
+         (e = hipMemcpyAsync(slot_col_host, g->d_slot_col + g->slot_off[graph],
+                             sizeof(int32_t) * g->slots[graph], hipMemcpyDeviceToHost, st)) !=
+             hipSuccess))
+        return hip_fail(e, "copy of the slot layout");
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "slot layout copy");
     return DIFFUSER_OK;
 }
 

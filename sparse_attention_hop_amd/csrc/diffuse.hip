@@ -3,7 +3,8 @@
 //   Z_{k+1}[i] = (1 - alpha) * sum_{j in N(i)} A_ij Z_k[j] + alpha * V[i].
 // The edge weights A are the same in every step; only Z changes.
 //
-// One wavefront per row. A group of L lanes gathers one neighbour row of Z_k
+// Generic path (any slot layout; padding slots are skipped). One wavefront
+// per row. A group of L lanes gathers one neighbour row of Z_k
 // with 16-byte loads (L = d * elem_size / 16), so a wave consumes 64 / L
 // edges per iteration; the groups' partial sums are reduced at the end and
 // the restart term is fused into the store.
@@ -18,8 +19,8 @@ constexpr int kWavesPerBlock = 4;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
-void k_diffuse_step(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ row_ptr,
-                    const int32_t* __restrict__ col_idx, const int64_t* __restrict__ col_off,
+void k_diffuse_step(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ slot_ptr,
+                    const int32_t* __restrict__ slot_col, const int64_t* __restrict__ slot_off,
                     const T* __restrict__ A, const T* __restrict__ Zk, const T* __restrict__ V,
                     T* __restrict__ Zn, const float* __restrict__ row_scale, float alpha) {
     constexpr int E = chunk<T>::kElems;
@@ -34,9 +35,9 @@ void k_diffuse_step(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __r
     const int32_t bh = blockIdx.y;
     const int32_t b = bh / H, h = bh - b * H;
     const int32_t gr = num_graphs == 1 ? 0 : b;
-    const int64_t* rp = row_ptr + (int64_t)gr * (n + 1);
-    const int32_t* cols = col_idx + col_off[gr];
-    const T* Ab = A + a_block_offset(col_off, num_graphs, H, b, h);
+    const int64_t* rp = slot_ptr + (int64_t)gr * (n + 1);
+    const int32_t* cols = slot_col + slot_off[gr];
+    const T* Ab = A + a_block_offset(slot_off, num_graphs, H, b, h);
     const int64_t e0 = rp[i], e1 = rp[i + 1];
     const int sub = lane % L, grp = lane / L;
     const T* Zb = Zk + (int64_t)bh * n * D + sub * E;
@@ -46,10 +47,11 @@ void k_diffuse_step(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __r
     for (int c = 0; c < E; ++c) acc[c] = 0.0f;
     for (int64_t base = e0; base < e1; base += EPI) {
         const int64_t e = base + grp;
-        if (e < e1) {
+        const int32_t j = e < e1 ? cols[e] : -1;
+        if (j >= 0) {
             const float a = chunk<T>::load1(Ab + e);
             float z[E];
-            chunk<T>::load(Zb + (int64_t)cols[e] * D, z);
+            chunk<T>::load(Zb + (int64_t)j * D, z);
 #pragma unroll
             for (int c = 0; c < E; ++c) acc[c] = fmaf(a, z[c], acc[c]);
         }
@@ -77,7 +79,7 @@ hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A,
                     hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
     hipLaunchKernelGGL((k_diffuse_step<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st, g.n,
-                       s.H, g.num_graphs, g.d_row_ptr, g.d_col_idx, g.d_col_off,
+                       s.H, g.num_graphs, g.d_slot_ptr, g.d_slot_col, g.d_slot_off,
                        static_cast<const T*>(A), static_cast<const T*>(Zk),
                        static_cast<const T*>(V), static_cast<T*>(Zn), row_scale, alpha);
     return hipGetLastError();

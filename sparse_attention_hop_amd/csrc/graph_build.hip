@@ -7,10 +7,24 @@
 //
 // Three kernels, one wavefront per row where rows are independent:
 //   draw : random extras of a row by rejection sampling on a counter-based
-//          SplitMix64 stream, sorted into an ELL table, plus the row degree;
-//   scan : exclusive scan of the degrees into row_ptr (one block per graph);
-//   fill : the sorted merge window u (G minus window) u random into col_idx,
-//          and the CSR offset of each row's window run.
+//          SplitMix64 stream, sorted into an ELL table, plus the row's edge
+//          count and its weight-slot count;
+//   scan : exclusive scan of per-row counts into int64 offsets (one block
+//          per graph);
+//   fill : the sorted merge window u (G minus window) u random into the
+//          ascending CSR, and the column of every weight slot.
+//
+// Weight-slot layout (where a row's edge weights live in A). A global row
+// holds its columns 0, 1, ... in order. Any other row holds three segments,
+// each a multiple of 8 slots so every segment starts 16-byte aligned in bf16:
+//   window : 8-column blocks from (lo & ~7) through the last window column
+//            (hi, or i when causal); slot t is column (lo & ~7) + t when that
+//            column lies in the window, else padding;
+//   global : slot t < g is global G[t] unless G[t] lies in the window (or,
+//            when causal, above i); padding to a multiple of 8;
+//   random : the row's random columns in ascending order (when causal, only
+//            those below the window); padding to a multiple of 8.
+// Padding slots carry column -1 and weight 0.
 #include "internal.h"
 
 namespace diffuser {
@@ -46,11 +60,13 @@ __device__ __forceinline__ bool is_global(const int32_t* G, int32_t g, int64_t j
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+__host__ __device__ __forceinline__ int64_t round8(int64_t x) { return (x + 7) & ~7ll; }
+
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int32_t R,
             int32_t rnd_width, int32_t causal, uint64_t seed, int32_t* __restrict__ deg,
-            int32_t* __restrict__ rnd, int32_t* __restrict__ rnd_cnt,
-            int32_t* __restrict__ status) {
+            int32_t* __restrict__ slots, int32_t* __restrict__ rnd,
+            int32_t* __restrict__ rnd_cnt, int32_t* __restrict__ status) {
     __shared__ int32_t taken[kWavesPerBlock][kMaxSampled];
     const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
@@ -63,6 +79,7 @@ void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
     if (is_global(G, g, i)) {
         if (lane == 0) {
             deg[row] = (int32_t)(causal ? i + 1 : n);
+            slots[row] = (int32_t)round8(causal ? i + 1 : n);
             rnd_cnt[row] = 0;
         }
         return;
@@ -120,26 +137,31 @@ void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
             if (rank < rnd_width) out[rank] = v;
         }
     }
-    if (lane == 0) {
-        rnd_cnt[row] = m;
-        if (!causal) {
+    const int64_t wb0 = lo & ~7ll;
+    if (!causal) {
+        if (lane == 0) {
+            rnd_cnt[row] = m;
             deg[row] = (int32_t)(wlen + (g - g_in) + m);
+            slots[row] = (int32_t)((hi - wb0) / 8 * 8 + 8 + round8(g) + round8(m));
         }
+        return;
     }
-    if (causal) {
-        // Keep j <= i: the window part [lo, i], globals below lo, and the
-        // random extras below lo (none lie inside the window).
-        int32_t below = 0;
-        if (pool <= R) {
-            below = (int32_t)(lo - g_before);
-        } else {
-            const int32_t* list = taken[wave];
-            int32_t c = 0;
-            for (int32_t e = lane; e < m; e += kWave) c += list[e] < lo;
-            for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-            below = c;
-        }
-        if (lane == 0) deg[row] = (int32_t)((i - lo + 1) + g_before + below);
+    // Causal: keep j <= i: the window part [lo, i], globals below lo, and
+    // the random extras below lo (none lie inside the window).
+    int32_t below = 0;
+    if (pool <= R) {
+        below = (int32_t)(lo - g_before);
+    } else {
+        const int32_t* list = taken[wave];
+        int32_t c = 0;
+        for (int32_t e = lane; e < m; e += kWave) c += list[e] < lo;
+        for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+        below = c;
+    }
+    if (lane == 0) {
+        rnd_cnt[row] = below;
+        deg[row] = (int32_t)((i - lo + 1) + g_before + below);
+        slots[row] = (int32_t)((i - wb0) / 8 * 8 + 8 + round8(g_before) + round8(below));
     }
 }
 
@@ -148,6 +170,7 @@ constexpr int kScanThreads = 1024;
 __global__ __launch_bounds__(kScanThreads)
 void k_scan(int64_t n, const int32_t* __restrict__ deg, int64_t* __restrict__ row_ptr,
             int64_t* __restrict__ max_deg) {
+    // deg: [graphs][n] counts; row_ptr: [graphs][n + 1] exclusive offsets.
     __shared__ int64_t part[kScanThreads];
     __shared__ int64_t pmax[kScanThreads];
     const int64_t gr = blockIdx.x;
@@ -187,9 +210,10 @@ void k_scan(int64_t n, const int32_t* __restrict__ deg, int64_t* __restrict__ ro
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int32_t rnd_width,
             int32_t causal, const int64_t* __restrict__ row_ptr,
-            const int64_t* __restrict__ col_off, const int32_t* __restrict__ rnd,
+            const int64_t* __restrict__ col_off, const int64_t* __restrict__ slot_ptr,
+            const int64_t* __restrict__ slot_off, const int32_t* __restrict__ rnd,
             const int32_t* __restrict__ rnd_cnt, int32_t* __restrict__ col_idx,
-            int32_t* __restrict__ win_off) {
+            int32_t* __restrict__ slot_col) {
     const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
     const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -197,26 +221,36 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
     if (i >= n) return;
     const int64_t row = gr * n + i;
     const int64_t* rp = row_ptr + gr * (n + 1);
+    const int64_t* sp = slot_ptr + gr * (n + 1);
     int32_t* out = col_idx + col_off[gr] + rp[i];
-    // Every store below is kept inside this row's slots.
+    int32_t* sout = slot_col + slot_off[gr] + sp[i];
+    // Every store below is kept inside this row's entries.
     const int64_t deg = rp[i + 1] - rp[i];
+    const int64_t nslot = sp[i + 1] - sp[i];
     const int64_t last = causal ? i : n - 1;
 
     if (is_global(G, g, i)) {
-        for (int64_t j = lane; j <= last && j < deg; j += kWave) out[j] = (int32_t)j;
-        if (lane == 0) win_off[row] = 0;
+        for (int64_t j = lane; j < nslot; j += kWave) {
+            if (j < deg) out[j] = (int32_t)j;
+            sout[j] = j <= last ? (int32_t)j : -1;
+        }
         return;
     }
     const int64_t lo = i - r < 0 ? 0 : i - r;
     const int64_t hi = i + r > n - 1 ? n - 1 : i + r;
     const int64_t wlen = hi - lo + 1;
+    const int64_t wend = causal ? i : hi;
+    const int64_t wb0 = lo & ~7ll;
+    const int64_t wseg = (wend - wb0) / 8 * 8 + 8;
     const int32_t g_before = count_less(G, g, lo);
     const int32_t g_in = count_less(G, g, hi + 1) - g_before;
-    const int32_t m = rnd_cnt[row];
+    const int64_t gseg = round8(causal ? g_before : g);
+    const int32_t m = rnd_cnt[row];  // random columns kept in this row
     const int32_t* rr = rnd + row * (int64_t)rnd_width;
     const int32_t r_before = count_less(rr, m, lo);
     const int64_t woff = g_before + r_before;
 
+    // Ascending CSR: (left extras) window (right extras).
     for (int64_t k = lane; k < wlen; k += kWave) {
         const int64_t j = lo + k;
         if (j <= last && woff + k < deg) out[woff + k] = (int32_t)j;
@@ -235,23 +269,65 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
         const int64_t pos = q + gx_less + (right ? wlen : 0);
         if (v <= last && pos < deg) out[pos] = (int32_t)v;
     }
-    if (lane == 0) win_off[row] = (int32_t)woff;
+    // Weight slots: window blocks, globals, randoms.
+    for (int64_t t = lane; t < wseg && t < nslot; t += kWave) {
+        const int64_t j = wb0 + t;
+        sout[t] = (j >= lo && j <= wend) ? (int32_t)j : -1;
+    }
+    for (int64_t t = lane; t < gseg && wseg + t < nslot; t += kWave) {
+        int32_t c = -1;
+        if (t < g) {
+            const int64_t p = G[t];
+            if ((p < lo || p > hi) && p <= last) c = (int32_t)p;
+        }
+        sout[wseg + t] = c;
+    }
+    for (int64_t t = lane; wseg + gseg + t < nslot; t += kWave) {
+        sout[wseg + gseg + t] = t < m ? rr[t] : -1;
+    }
+}
+
+// bnd[row][c] = number of the row's kept random columns below c * chunk.
+__global__ __launch_bounds__(256)
+void k_bounds(int64_t rows, int32_t rnd_width, int32_t chunk, int32_t nchunks,
+              const int32_t* __restrict__ rnd, const int32_t* __restrict__ rnd_cnt,
+              int32_t* __restrict__ bnd) {
+    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= rows) return;
+    const int32_t m = rnd_cnt[row];
+    const int32_t* rr = rnd + row * (int64_t)rnd_width;
+    int32_t* out = bnd + row * (int64_t)(nchunks + 1);
+    int32_t k = 0;
+    for (int32_t c = 0; c <= nchunks; ++c) {
+        const int64_t lim = (int64_t)c * chunk;
+        while (k < m && rr[k] < lim) ++k;
+        out[c] = k;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_draw(const diffuser_graph& g, int32_t* deg, int32_t* status, hipStream_t st) {
-    dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
-    hipLaunchKernelGGL(k_draw, grid, dim3(kWave * kWavesPerBlock), 0, st, g.n, g.radius,
-                       g.d_global, g.num_global, g.num_random, g.rnd_width, g.causal, g.seed,
-                       deg, g.d_rnd, g.d_rnd_cnt, status);
+hipError_t launch_bounds(const diffuser_graph& g, hipStream_t st) {
+    const int64_t rows = (int64_t)g.num_graphs * g.n;
+    const int32_t nchunks = (int32_t)((g.n + g.chunk - 1) / g.chunk);
+    hipLaunchKernelGGL(k_bounds, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, rows,
+                       g.rnd_width, g.chunk, nchunks, g.d_rnd, g.d_rnd_cnt, g.d_bnd);
     return hipGetLastError();
 }
 
-hipError_t launch_scan(const diffuser_graph& g, const int32_t* deg, int64_t* max_deg,
-                            hipStream_t st) {
-    hipLaunchKernelGGL(k_scan, dim3((unsigned)g.num_graphs), dim3(kScanThreads), 0, st, g.n,
-                       deg, g.d_row_ptr, max_deg);
+hipError_t launch_draw(const diffuser_graph& g, int32_t* deg, int32_t* slots, int32_t* status,
+                       hipStream_t st) {
+    dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
+    hipLaunchKernelGGL(k_draw, grid, dim3(kWave * kWavesPerBlock), 0, st, g.n, g.radius,
+                       g.d_global, g.num_global, g.num_random, g.rnd_width, g.causal, g.seed,
+                       deg, slots, g.d_rnd, g.d_rnd_cnt, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(int64_t n, int32_t num_graphs, const int32_t* counts, int64_t* offsets,
+                       int64_t* max_count, hipStream_t st) {
+    hipLaunchKernelGGL(k_scan, dim3((unsigned)num_graphs), dim3(kScanThreads), 0, st, n, counts,
+                       offsets, max_count);
     return hipGetLastError();
 }
 
@@ -259,7 +335,8 @@ hipError_t launch_fill(const diffuser_graph& g, hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
     hipLaunchKernelGGL(k_fill, grid, dim3(kWave * kWavesPerBlock), 0, st, g.n, g.radius,
                        g.d_global, g.num_global, g.rnd_width, g.causal, g.d_row_ptr,
-                       g.d_col_off, g.d_rnd, g.d_rnd_cnt, g.d_col_idx, g.d_win_off);
+                       g.d_col_off, g.d_slot_ptr, g.d_slot_off, g.d_rnd, g.d_rnd_cnt,
+                       g.d_col_idx, g.d_slot_col);
     return hipGetLastError();
 }
 

@@ -1,10 +1,11 @@
-// Edge scores and edge softmax on CSR rows ("Diffuser" reading notes,
+// Edge scores and edge softmax on weight-slot rows ("Diffuser" reading notes,
 // section 2.1, eqs. S.1-S.5; "1.2.1 Static sparsity", section 1, eqs. 1-3):
 //   s_ij = q_i . k_j / sqrt(d_h) for j in N(i),
 //   A_ij = exp(s_ij - m_i) / sum_{u in N(i)} exp(s_iu - m_i),  m_i = max_j s_ij.
 // The normalisation runs over exactly the row's neighbour set.
 //
-// One wavefront per row. A group of L lanes covers one key row with
+// Generic path (any slot layout). One wavefront per row; padding slots
+// (column -1) get weight 0. A group of L lanes covers one key row with
 // 16-byte loads (L = d * elem_size / 16), so a wave scores 64 / L edges per
 // iteration. The scale folds log2(e) so the exponentials are exp2.
 // Pass 1 keeps an online (max, sum) per lane group; pass 2 recomputes the
@@ -22,8 +23,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 template <typename T, int D>
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
-void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ row_ptr,
-                      const int32_t* __restrict__ col_idx, const int64_t* __restrict__ col_off,
+void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ slot_ptr,
+                      const int32_t* __restrict__ slot_col, const int64_t* __restrict__ slot_off,
                       const T* __restrict__ Q, const T* __restrict__ K, T* __restrict__ A,
                       float* __restrict__ row_scale, float scale_log2) {
     constexpr int E = chunk<T>::kElems;
@@ -38,9 +39,9 @@ void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* _
     const int32_t bh = blockIdx.y;
     const int32_t b = bh / H, h = bh - b * H;
     const int32_t gr = num_graphs == 1 ? 0 : b;
-    const int64_t* rp = row_ptr + (int64_t)gr * (n + 1);
-    const int32_t* cols = col_idx + col_off[gr];
-    T* Ab = A + a_block_offset(col_off, num_graphs, H, b, h);
+    const int64_t* rp = slot_ptr + (int64_t)gr * (n + 1);
+    const int32_t* cols = slot_col + slot_off[gr];
+    T* Ab = A + a_block_offset(slot_off, num_graphs, H, b, h);
     const int64_t e0 = rp[i], e1 = rp[i + 1];
     const int sub = lane % L, grp = lane / L;
 
@@ -51,11 +52,12 @@ void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* _
     float m = -INFINITY, l = 0.0f;
     for (int64_t base = e0; base < e1; base += EPI) {
         const int64_t e = base + grp;
-        const bool valid = e < e1;
+        const int32_t j = e < e1 ? cols[e] : -1;
+        const bool valid = j >= 0;
         float dot = 0.0f;
         if (valid) {
             float k[E];
-            chunk<T>::load(Kb + (int64_t)cols[e] * D, k);
+            chunk<T>::load(Kb + (int64_t)j * D, k);
 #pragma unroll
             for (int c = 0; c < E; ++c) dot = fmaf(q[c], k[c], dot);
         }
@@ -84,18 +86,19 @@ void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* _
     float stored_sum = 0.0f;  // sum of the weights as stored (after rounding)
     for (int64_t base = e0; base < e1; base += EPI) {
         const int64_t e = base + grp;
-        const bool valid = e < e1;
+        const int32_t j = e < e1 ? cols[e] : -1;
+        const bool valid = j >= 0;
         float dot = 0.0f;
         if (valid) {
             float k[E];
-            chunk<T>::load(Kb + (int64_t)cols[e] * D, k);
+            chunk<T>::load(Kb + (int64_t)j * D, k);
 #pragma unroll
             for (int c = 0; c < E; ++c) dot = fmaf(q[c], k[c], dot);
         }
 #pragma unroll
         for (int off = 1; off < L; off <<= 1) dot += __shfl_xor(dot, off);
-        if (valid && sub == 0) {
-            const float a = fast_exp2(dot * scale_log2 - m) * inv;
+        if (e < e1 && sub == 0) {
+            const float a = valid ? fast_exp2(dot * scale_log2 - m) * inv : 0.0f;
             chunk<T>::store1(Ab + e, a);
             stored_sum += chunk<T>::round(a);
         }
@@ -115,7 +118,7 @@ hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* Q,
                     void* A, float* row_scale, float scale_log2, hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
     hipLaunchKernelGGL((k_scores_softmax<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st, g.n,
-                       s.H, g.num_graphs, g.d_row_ptr, g.d_col_idx, g.d_col_off,
+                       s.H, g.num_graphs, g.d_slot_ptr, g.d_slot_col, g.d_slot_off,
                        static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<T*>(A),
                        row_scale, scale_log2);
     return hipGetLastError();

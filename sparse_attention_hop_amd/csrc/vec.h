@@ -68,13 +68,14 @@ template <> struct chunk<bf16_t> {
     __device__ __forceinline__ static float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 };
 
-// Offset (in elements) of the A block of (b, h): graphs are per batch element
-// when num_graphs == B, else one graph serves every (b, h).
-__device__ __forceinline__ int64_t a_block_offset(const int64_t* col_off, int32_t num_graphs,
+// Offset (in elements) of the A block of (b, h) given the per-graph slot
+// offsets: graphs are per batch element when num_graphs == B, else one
+// graph serves every (b, h).
+__device__ __forceinline__ int64_t a_block_offset(const int64_t* slot_off, int32_t num_graphs,
                                                   int32_t H, int32_t b, int32_t h) {
-    if (num_graphs == 1) return ((int64_t)b * H + h) * col_off[1];
-    const int64_t nnz_b = col_off[b + 1] - col_off[b];
-    return (int64_t)H * col_off[b] + (int64_t)h * nnz_b;
+    if (num_graphs == 1) return ((int64_t)b * H + h) * slot_off[1];
+    const int64_t slots_b = slot_off[b + 1] - slot_off[b];
+    return (int64_t)H * slot_off[b] + (int64_t)h * slots_b;
 }
 
 }  // namespace diffuser

@@ -33,7 +33,21 @@ def _check_csr(orc, g, n, r, G, R, ng, causal, seed):
         grp, gcols = g.copy_csr(gr)
         assert np.array_equal(grp, rp[gr]), f"row_ptr mismatch in graph {gr}"
         assert np.array_equal(gcols, cols[gr]), f"col_idx mismatch in graph {gr}"
+        sp, sc = g.copy_slots(gr)
+        pu.slot_permutation(sp, sc, rp[gr], cols[gr])
+        assert np.all(np.diff(sp) % 8 == 0), "segments are multiples of 8 slots"
     return rp, cols
+
+
+def _a_csr(g, A_h, b, h, H, gr, rp, cols):
+    """The (b, h) block of A (slot layout) in ascending-CSR order; padding
+    slots must hold exactly 0."""
+    sp, sc = g.copy_slots(gr)
+    perm, pad = pu.slot_permutation(sp, sc, rp[gr], cols[gr])
+    off = g.a_offset(b, h, H)
+    blk = A_h[off:off + g.slots[gr]]
+    assert np.all(blk[pad] == 0), "padding slots must hold 0"
+    return blk[perm]
 
 
 def _as64(t):
@@ -119,8 +133,7 @@ def test_attn_full_size(orc, name):
     for b, h in pairs:
         gr = 0 if w.num_graphs == 1 else b
         A_ref = orc.scores_softmax(_as64(q[b, h]), _as64(k[b, h]), rp[gr], cols[gr], threads)
-        off = g.a_offset(b, h, w.H)
-        A_got = A_h[off:off + g.nnz[gr]]
+        A_got = _a_csr(g, A_h, b, h, w.H, gr, rp, cols)
         bound = pu.rowsum_bound(w.dtype)
         sums = np.add.reduceat(A_got, rp[gr][:-1])
         assert np.abs(sums - 1).max() <= bound, (b, h, np.abs(sums - 1).max())
@@ -221,9 +234,10 @@ def test_softmax_8pos_gpu():
     v[0, 0, 3, :2] = torch.tensor([float(x) for x in gold["v4"]])
     v[0, 0, 4, :2] = torch.tensor([float(x) for x in gold["v5"]])
     A = sah.scores_softmax(q.to(DEV), k.to(DEV), g).cpu().numpy()
-    rp, _ = g.copy_csr(0)
+    rp, cols = g.copy_csr(0)
+    A_csr = _a_csr(g, A, 0, 0, 1, 0, [rp], [cols])
     want = np.array([float(x) for x in gold["weights"]])
-    assert np.allclose(A[rp[3]:rp[4]], want, rtol=0, atol=1e-6)
+    assert np.allclose(A_csr[rp[3]:rp[4]], want, rtol=0, atol=1e-6)
     z = sah.attn(q.to(DEV), k.to(DEV), v.to(DEV), g, 1, 0.0).cpu().numpy()
     assert np.allclose(z[0, 0, 3, :2], [float(x) for x in gold["o4"]], rtol=0, atol=1e-6)
     assert np.all(z[0, 0, 3, 2:] == 0)
@@ -303,10 +317,10 @@ def test_constant_v_fixed_point_gpu():
 def test_rowsums_bf16():
     g, q, k, v = _setup(dtype=torch.bfloat16)
     A = sah.scores_softmax(q, k, g).double().cpu().numpy()
-    rp, _ = g.copy_csr(0)
-    nnz = g.nnz[0]
+    sp, _ = g.copy_slots(0)
+    ns = g.slots[0]
     for bh in range(6):
-        sums = np.add.reduceat(A[bh * nnz:(bh + 1) * nnz], rp[:-1])
+        sums = np.add.reduceat(A[bh * ns:(bh + 1) * ns], sp[:-1])
         assert np.abs(sums - 1).max() <= pu.ROWSUM_BF16
 
 
@@ -337,3 +351,98 @@ def test_invalid_arguments_gpu():
     gB = sah.build_graph(300, 6, [0], 9, 3, False, 1)
     with pytest.raises(sah.DiffuserError):
         sah.attn(q, k, v, gB, 5, 0.1)                # num_graphs not in {1, B}
+
+
+# ---------------------------------------------------------------------------
+# LDS-streamed MFMA diffusion (built graphs, bf16, d = 64): shapes that cross
+# chunk and tile boundaries, several global-row workgroups, causal rows,
+# empty random sets, windows wider than the sequence.
+# ---------------------------------------------------------------------------
+
+FAST_CASES = [
+    # n, r, G, R, num_graphs(B), causal, B, H
+    (300, 6, [0, 150], 9, 1, False, 2, 3),
+    (700, 20, list(range(0, 700, 7))[:70], 12, 2, False, 2, 2),
+    (513, 64, list(range(64)), 64, 1, False, 1, 2),
+    (1000, 3, [5, 999], 0, 1, True, 1, 3),
+    (257, 300, [], 5, 1, False, 1, 1),
+    (64, 1, [], 3, 1, True, 2, 1),
+    (1100, 50, [0, 1, 2, 700, 1099], 40, 3, True, 3, 1),
+    (33, 2, [32], 40, 1, False, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", FAST_CASES, ids=lambda c: f"n{c[0]}r{c[1]}g{len(c[2])}R{c[3]}c{int(c[5])}")
+@pytest.mark.parametrize("K,alpha", [(5, 0.1), (2, 0.0), (1, 0.3)])
+def test_fast_diffusion_shapes(orc, case, K, alpha):
+    n, r, G, R, ngr, causal, B, H = case
+    ng = ngr if ngr in (1, B) else B
+    g = _gpu_graph(n, r, G, R, ng, causal, 31)
+    rp, cols = _check_csr(orc, g, n, r, G, R, ng, causal, 31)
+    shape = (B, H, n, 64)
+    q = make_tensor(shape, 71, torch.bfloat16)
+    k = make_tensor(shape, 72, torch.bfloat16)
+    v = make_tensor(shape, 73, torch.bfloat16)
+    z = sah.attn(q.to(DEV), k.to(DEV), v.to(DEV), g, K, alpha)
+    # the stage entry (no row rescale) must match the oracle on the given A
+    A = sah.scores_softmax(q.to(DEV), k.to(DEV), g)
+    zs = sah.diffuse(A, v.to(DEV), g, K, alpha)
+    z_h, zs_h, A_h = _as64(z), _as64(zs), _as64(A)
+    for b in range(B):
+        gr = 0 if ng == 1 else b
+        for h in range(H):
+            ref = orc.attn(_as64(q[b, h]), _as64(k[b, h]), _as64(v[b, h]), rp[gr], cols[gr], K,
+                           alpha)
+            pu.assert_z_close(z_h[b, h], ref, "bf16", f"attn b={b} h={h}", K, alpha)
+            A_csr = _a_csr(g, A_h, b, h, H, gr, rp, cols)
+            ref_s = orc.diffuse(A_csr, _as64(v[b, h]), rp[gr], cols[gr], K, alpha)
+            # same stored A on both sides: only the Z_k roundings differ
+            pu.assert_z_close(zs_h[b, h], ref_s, "bf16", f"diffuse b={b} h={h}", K, alpha)
+
+
+def _slot_classes(g, gr, n, r, G, causal):
+    """Class of every weight slot of graph gr: 0 window, 1 global column,
+    2 random, 3 global row, -1 padding."""
+    sp, sc = g.copy_slots(gr)
+    rows = np.repeat(np.arange(n), np.diff(sp))
+    Gs = np.zeros(n, dtype=bool)
+    Gs[list(G)] = True
+    lo = np.maximum(rows - r, 0)
+    hi = np.minimum(rows + r, n - 1)
+    cls = np.full(len(sc), 2, dtype=np.int64)
+    cls[(sc >= lo) & (sc <= hi)] = 0
+    cls[(sc >= 0) & Gs[np.maximum(sc, 0)] & ~((sc >= lo) & (sc <= hi))] = 1
+    cls[Gs[rows]] = 3
+    cls[sc < 0] = -1
+    return cls
+
+
+@pytest.mark.parametrize("name", ["mlm4096_bf16", "long16k_bf16"])
+def test_fast_diffusion_by_segment(orc, name):
+    """One step, alpha = 0, with A restricted to one class of slots: isolates
+    the window, global-column, random and global-row parts of the kernel."""
+    w = WORKLOADS[name]
+    B, H = 1, 2
+    g = _gpu_graph(w.n, w.radius, w.global_idx, w.num_random, 1, w.causal, w.graph_seed)
+    rp, cols = _check_csr(orc, g, w.n, w.radius, w.global_idx, w.num_random, 1, w.causal,
+                          w.graph_seed)
+    cls = _slot_classes(g, 0, w.n, w.radius, w.global_idx, w.causal)
+    q = make_tensor((B, H, w.n, 64), 5, torch.bfloat16).to(DEV)
+    k = make_tensor((B, H, w.n, 64), 6, torch.bfloat16).to(DEV)
+    v = make_tensor((B, H, w.n, 64), 7, torch.bfloat16).to(DEV)
+    A = sah.scores_softmax(q, k, g)
+    ns = g.slots[0]
+    sp, sc = g.copy_slots(0)
+    perm, _ = pu.slot_permutation(sp, sc, rp[0], cols[0])
+    for c, cname in enumerate(["window", "global-col", "random", "global-row"]):
+        mask = torch.tensor(np.tile(cls == c, B * H), device=DEV)
+        Ac = torch.where(mask, A, torch.zeros_like(A))
+        z = _as64(sah.diffuse(Ac, v, g, 1, 0.0))
+        Ac_h = _as64(Ac)
+        for h in range(H):
+            ref = orc.diffuse(Ac_h[h * ns:(h + 1) * ns][perm], _as64(v[0, h]), rp[0], cols[0], 1,
+                              0.0)
+            err = np.abs(z[0, h] - ref)
+            bad = np.argwhere(err > 1e-2 * np.maximum(np.abs(ref), 1) + 1e-3)
+            assert bad.size == 0, (f"{cname} h={h}: {len(bad)} bad, first rows/ch "
+                                   f"{bad[:6].tolist()} max err {err.max():.3e}")
