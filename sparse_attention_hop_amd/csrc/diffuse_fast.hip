@@ -32,14 +32,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kWaves = 8;
+constexpr int kWaves = 16;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kD = 64;            // head width
 constexpr int kNB = kD / 16;      // 16-channel MFMA blocks
 constexpr int kZS = 72;           // LDS row stride in bf16 (144 B: 16-B aligned, bank-spread)
 constexpr int kGrowRows = 32;     // global rows per global-row workgroup
 constexpr int kStage = 16;        // random edges per row staged per pass
-constexpr int kChunk = 256;       // key rows per LDS chunk
+constexpr int kChunk = 512;       // key rows per LDS chunk
 
 struct FastArgs {
     int64_t n;
@@ -108,11 +108,11 @@ __device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)f32_to_b
 // was dropped when both results stayed live, so the swaps are written out.)
 // a <-> b: lanes 32-63 of a trade places with lanes 0-31 of b.
 __device__ __forceinline__ void swap32(float& a, float& b) {
-    asm volatile("s_nop 4\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 // a <-> b: the odd 16-lane rows of a trade places with the even rows of b.
 __device__ __forceinline__ void swap16(float& a, float& b) {
-    asm volatile("s_nop 4\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
 // Restart and store of one 16x16 accumulator block (rows row0 + 4*(l/16) + e,
@@ -134,7 +134,7 @@ __device__ __forceinline__ void store_block(const FastArgs& a, int32_t bh, int64
 }
 
 template <int RPW>  // rows per wave (multiple of 16, at most 32)
-__global__ __launch_bounds__(kThreads, 2)
+__global__ __launch_bounds__(kThreads)
 void k_diffuse_fast(FastArgs a) {
     extern __shared__ __align__(16) uint16_t lds[];
     constexpr int MB = RPW / 16;
@@ -207,8 +207,8 @@ void k_diffuse_fast(FastArgs a) {
         }
         // Fixed-order tree reduction of the 8 waves' partial sums in LDS.
         __syncthreads();
-        float* red = reinterpret_cast<float*>(lds);   // 4 waves x 2 x 4 x 64 x 4 floats
-        for (int half = 4; half >= 1; half >>= 1) {
+        float* red = reinterpret_cast<float*>(lds);   // kWaves/2 waves x 2 x kNB x 4 x 64 floats
+        for (int half = kWaves / 2; half >= 1; half >>= 1) {
             if (wave >= half && wave < 2 * half) {
                 float* dst = red + (wave - half) * (2 * kNB * 4 * kWave);
 #pragma unroll
@@ -525,19 +525,20 @@ bool fast_diffuse_supported(const diffuser_graph& g, const attn_shape& s) {
            g.chunk == kChunk;
 }
 
+constexpr int kRPW = 16;   // rows per wave
+
 size_t fast_diffuse_lds_bytes(const diffuser_graph& g) {
-    constexpr int RPW = 32;
     const int gpad = (g.num_global + 31) & ~31;
     const size_t chunk = (size_t)g.chunk * kZS * 2 + (size_t)gpad * kZS * 2 +
-                         (size_t)kWaves * RPW * kStage * 6;
-    const size_t red = (size_t)4 * 2 * kNB * 4 * kWave * 4;   // global-row reduction
+                         (size_t)kWaves * kRPW * kStage * 6;
+    const size_t red = (size_t)(kWaves / 2) * 2 * kNB * 4 * kWave * 4;   // global-row reduction
     return chunk > red ? chunk : red;
 }
 
 hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
                                float alpha, hipStream_t st) {
-    constexpr int RPW = 32;
+    constexpr int RPW = kRPW;
     FastArgs a;
     a.n = g.n;
     a.H = s.H;
@@ -566,6 +567,14 @@ hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, con
     a.total_items = a.BH * (a.tiles_per_bh + a.grow_per_bh);
     a.per_xcd = (a.total_items + 7) / 8;
     const size_t lds = fast_diffuse_lds_bytes(g);
+    static bool attr_set = false;   // dynamic LDS above 64 KB must be enabled once
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_diffuse_fast<RPW>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
     hipLaunchKernelGGL(k_diffuse_fast<RPW>, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), lds,
                        st, a);
     return hipGetLastError();

@@ -46,7 +46,7 @@ struct diffuser_graph {
     int32_t* d_rnd_cnt = nullptr;   // [num_graphs][n] random columns kept per row
     // Key-row chunking of the LDS-streamed kernels: bnd[gr][i][c] = number of
     // row i's kept random columns below c * chunk, c = 0 .. ceil(n / chunk).
-    int32_t chunk = 256;
+    int32_t chunk = 512;
     int32_t* d_bnd = nullptr;
 };
 
