@@ -119,18 +119,22 @@ DIFFUSER_API diffuser_status diffuser_graph_copy_csr(const diffuser_graph* g, in
                                         int64_t* row_ptr_host, int32_t* col_idx_host,
                                         void* stream);
 
-/* Copies the weight-slot layout of graph `graph` to HOST arrays:
- * slot_ptr[n+1] (row i owns slots slot_ptr[i] .. slot_ptr[i+1]-1) and
- * slot_col[slots] (the key column of each slot, or -1 for a padding slot,
- * whose weight is always 0). Every edge of the graph owns exactly one slot.
- * For a built graph, a global row's slots are its columns in order, padded
- * to a multiple of 8; any other row has three segments, each a multiple of
- * 8 slots: the window as 8-column blocks from (lo & ~7), the g globals in
- * order (padding where a global lies in the window or, when causal, above
- * the row), and the random columns in ascending order. An imported graph's
- * slots are its CSR entries. Synchronous on return. */
+/* Copies the weight-slot layout of graph `graph` (where A holds its edge
+ * weights) to HOST arrays slot_row[slots] and slot_col[slots]: slot s holds
+ * the weight of edge (slot_row[s], slot_col[s]); both are -1 for a padding
+ * slot, whose weight is always 0. Every edge of the graph owns exactly one
+ * slot. An imported graph's slots are its CSR entries. A built graph's
+ * slots are, first, one segment per row, each a multiple of 8 slots: a
+ * global row's columns in order; for any other row the window as 8-column
+ * blocks from (lo & ~7), then the g globals in order (padding where a
+ * global lies in the window or, when causal, above the row), then, for
+ * n > 65536 only, its random columns in ascending order. For n <= 65536 the
+ * random edges follow all row segments in schedule order: for each block of
+ * 16 rows and each 512-key chunk, the block's random edges into the chunk,
+ * by row and then column, two of one row per pair, 16 pairs per 32-slot
+ * group. Synchronous on return. */
 DIFFUSER_API diffuser_status diffuser_graph_copy_slots(const diffuser_graph* g, int32_t graph,
-                                                       int64_t* slot_ptr_host,
+                                                       int32_t* slot_row_host,
                                                        int32_t* slot_col_host, void* stream);
 
 /* Frees the graph (waits for the device first). Accepts NULL. */

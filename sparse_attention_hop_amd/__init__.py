@@ -162,15 +162,16 @@ class Graph:
         return rp, ci[: self.nnz[graph]]
 
     def copy_slots(self, graph: int = 0):
-        """(slot_ptr int64[n+1], slot_col int32[slots]) of one graph: where the
-        edge weights of each row live in A; column -1 marks padding."""
-        sp = np.zeros(self.n + 1, dtype=np.int64)
+        """(slot_row int32[slots], slot_col int32[slots]) of one graph: slot s
+        of A's (b, h) block holds the weight of edge (slot_row[s],
+        slot_col[s]); -1 marks padding."""
+        sr = np.zeros(max(self.slots[graph], 1), dtype=np.int32)
         sc = np.zeros(max(self.slots[graph], 1), dtype=np.int32)
         _check(self._lib.diffuser_graph_copy_slots(self.handle, graph,
-                                                   sp.ctypes.data_as(ctypes.c_void_p),
+                                                   sr.ctypes.data_as(ctypes.c_void_p),
                                                    sc.ctypes.data_as(ctypes.c_void_p),
                                                    ctypes.c_void_p(_stream_handle())))
-        return sp, sc[: self.slots[graph]]
+        return sr[: self.slots[graph]], sc[: self.slots[graph]]
 
     def edges(self, B: int, H: int) -> int:
         """Edges summed over every (b, h) pair (padding slots excluded)."""

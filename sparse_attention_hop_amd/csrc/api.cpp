@@ -20,7 +20,6 @@ thread_local std::string g_last_error;
 
 constexpr int64_t kMaxN = 1ll << 24;
 constexpr int32_t kMaxSampledRandom = 1024;
-constexpr int64_t kMaxBoundEntries = 1ll << 26;   // 256 MB of chunk bounds
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -55,20 +54,32 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_global);
     hipFree(g->d_rnd);
     hipFree(g->d_rnd_cnt);
-    hipFree(g->d_slot_ptr);
+    hipFree(g->d_seg_ptr);
     hipFree(g->d_slot_col);
+    hipFree(g->d_slot_row);
     hipFree(g->d_slot_off);
-    hipFree(g->d_bnd);
+    hipFree(g->d_rslot);
+    hipFree(g->d_grp_off);
+    hipFree(g->d_grp_ptr);
+    hipFree(g->d_grp_chunk);
+    hipFree(g->d_sched_row);
+    hipFree(g->d_sched_j);
     g->d_row_ptr = nullptr;
     g->d_col_idx = nullptr;
     g->d_col_off = nullptr;
     g->d_global = nullptr;
     g->d_rnd = nullptr;
     g->d_rnd_cnt = nullptr;
-    g->d_slot_ptr = nullptr;
+    g->d_seg_ptr = nullptr;
     g->d_slot_col = nullptr;
+    g->d_slot_row = nullptr;
     g->d_slot_off = nullptr;
-    g->d_bnd = nullptr;
+    g->d_rslot = nullptr;
+    g->d_grp_off = nullptr;
+    g->d_grp_ptr = nullptr;
+    g->d_grp_chunk = nullptr;
+    g->d_sched_row = nullptr;
+    g->d_sched_j = nullptr;
 }
 
 diffuser_status alloc_status(hipError_t e, const char* what) {
@@ -247,37 +258,45 @@ diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stre
     g->rnd_width = (int32_t)std::min<int64_t>(desc->num_random, n);
     g->causal = desc->causal;
     g->seed = desc->seed;
+    g->scheduled = n <= kMaxScheduledN;
     hipGetDevice(&g->device);
 
     const int64_t rows = (int64_t)g->num_graphs * n;
+    const int64_t nrb = (n + kRowBlock - 1) / kRowBlock;
     int32_t* d_deg = nullptr;
     int32_t* d_slots = nullptr;
     int32_t* d_status = nullptr;
     int64_t* d_max = nullptr;
+    int32_t* d_gcount = nullptr;
     hipError_t e;
     if ((e = dev_alloc(&g->d_global, g->num_global)) != hipSuccess ||
         (e = dev_alloc(&g->d_rnd, (size_t)rows * std::max(g->rnd_width, 1))) != hipSuccess ||
+        (e = dev_alloc(&g->d_rslot, (size_t)rows * std::max(g->rnd_width, 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_rnd_cnt, rows)) != hipSuccess ||
         (e = dev_alloc(&g->d_row_ptr, (size_t)g->num_graphs * (n + 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_col_off, g->num_graphs + 1)) != hipSuccess ||
-        (e = dev_alloc(&g->d_slot_ptr, (size_t)g->num_graphs * (n + 1))) != hipSuccess ||
+        (e = dev_alloc(&g->d_seg_ptr, (size_t)g->num_graphs * (n + 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_slot_off, g->num_graphs + 1)) != hipSuccess ||
+        (e = dev_alloc(&g->d_grp_ptr, (size_t)g->num_graphs * (nrb + 1))) != hipSuccess ||
+        (e = dev_alloc(&g->d_grp_off, g->num_graphs + 1)) != hipSuccess ||
         (e = dev_alloc(&d_deg, rows)) != hipSuccess ||
         (e = dev_alloc(&d_slots, rows)) != hipSuccess ||
         (e = dev_alloc(&d_status, 1)) != hipSuccess ||
-        (e = dev_alloc(&d_max, 2 * (size_t)g->num_graphs)) != hipSuccess) {
+        (e = dev_alloc(&d_max, 3 * (size_t)g->num_graphs)) != hipSuccess ||
+        (e = dev_alloc(&d_gcount, (size_t)g->num_graphs * nrb)) != hipSuccess) {
         hipFree(d_deg);
         hipFree(d_slots);
         hipFree(d_status);
         hipFree(d_max);
+        hipFree(d_gcount);
         return alloc_status(e, "device allocation for the graph build");
     }
     struct tmp_guard {
-        void* p[4];
+        void* p[5];
         ~tmp_guard() {
             for (void* q : p) hipFree(q);
         }
-    } tmps{{d_deg, d_slots, d_status, d_max}};
+    } tmps{{d_deg, d_slots, d_status, d_max, d_gcount}};
 
     if (g->num_global > 0 &&
         (e = hipMemcpyAsync(g->d_global, desc->global_idx, sizeof(int32_t) * g->num_global,
@@ -288,12 +307,17 @@ diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stre
     if ((e = launch_draw(*g, d_deg, d_slots, d_status, st)) != hipSuccess)
         return hip_fail(e, "draw launch");
     if ((e = launch_scan(n, g->num_graphs, d_deg, g->d_row_ptr, d_max, st)) != hipSuccess ||
-        (e = launch_scan(n, g->num_graphs, d_slots, g->d_slot_ptr, d_max + g->num_graphs, st)) !=
+        (e = launch_scan(n, g->num_graphs, d_slots, g->d_seg_ptr, d_max + g->num_graphs, st)) !=
             hipSuccess)
         return hip_fail(e, "scan launch");
+    if (g->scheduled &&
+        ((e = launch_sched_count(*g, d_gcount, st)) != hipSuccess ||
+         (e = launch_scan(nrb, g->num_graphs, d_gcount, g->d_grp_ptr, d_max + 2 * g->num_graphs,
+                          st)) != hipSuccess))
+        return hip_fail(e, "schedule count launch");
     int32_t status = 0;
-    std::vector<int64_t> maxes(2 * (size_t)g->num_graphs);
-    std::vector<int64_t> last_e(g->num_graphs), last_s(g->num_graphs);
+    std::vector<int64_t> maxes(3 * (size_t)g->num_graphs);
+    std::vector<int64_t> last_e(g->num_graphs), last_s(g->num_graphs), last_g(g->num_graphs, 0);
     if ((e = hipMemcpyAsync(&status, d_status, sizeof(int32_t), hipMemcpyDeviceToHost, st)) !=
             hipSuccess ||
         (e = hipMemcpyAsync(maxes.data(), d_max, sizeof(int64_t) * 2 * g->num_graphs,
@@ -302,41 +326,51 @@ diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stre
     for (int32_t gr = 0; gr < g->num_graphs; ++gr) {
         if ((e = hipMemcpyAsync(&last_e[gr], g->d_row_ptr + (int64_t)gr * (n + 1) + n,
                                 sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess ||
-            (e = hipMemcpyAsync(&last_s[gr], g->d_slot_ptr + (int64_t)gr * (n + 1) + n,
-                                sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess)
+            (e = hipMemcpyAsync(&last_s[gr], g->d_seg_ptr + (int64_t)gr * (n + 1) + n,
+                                sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess ||
+            (g->scheduled &&
+             (e = hipMemcpyAsync(&last_g[gr], g->d_grp_ptr + (int64_t)gr * (nrb + 1) + nrb,
+                                 sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess))
             return hip_fail(e, "copy of edge counts");
     }
     if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "graph draw");
     if (status != 0)
         return fail(DIFFUSER_ERR_INTERNAL, "random draw budget (2^20 draws per row) exhausted");
     g->nnz = last_e;
-    g->slots = last_s;
+    g->groups = last_g;
+    g->slots.assign(g->num_graphs, 0);
     g->col_off.assign(g->num_graphs + 1, 0);
     g->slot_off.assign(g->num_graphs + 1, 0);
+    g->grp_off.assign(g->num_graphs + 1, 0);
     for (int32_t gr = 0; gr < g->num_graphs; ++gr) {
+        g->slots[gr] = last_s[gr] + (int64_t)kGroupSlots * last_g[gr];
         g->col_off[gr + 1] = g->col_off[gr] + last_e[gr];
-        g->slot_off[gr + 1] = g->slot_off[gr] + last_s[gr];
+        g->slot_off[gr + 1] = g->slot_off[gr] + g->slots[gr];
+        g->grp_off[gr + 1] = g->grp_off[gr] + last_g[gr];
     }
     g->max_row_len = *std::max_element(maxes.begin(), maxes.begin() + g->num_graphs);
-    g->max_row_slots = *std::max_element(maxes.begin() + g->num_graphs, maxes.end());
+    g->max_row_slots =
+        *std::max_element(maxes.begin() + g->num_graphs, maxes.begin() + 2 * g->num_graphs);
+    const int64_t ngroups = g->grp_off[g->num_graphs];
     if ((e = dev_alloc(&g->d_col_idx, g->col_off[g->num_graphs])) != hipSuccess ||
-        (e = dev_alloc(&g->d_slot_col, g->slot_off[g->num_graphs])) != hipSuccess)
+        (e = dev_alloc(&g->d_slot_col, g->slot_off[g->num_graphs])) != hipSuccess ||
+        (e = dev_alloc(&g->d_slot_row, g->slot_off[g->num_graphs])) != hipSuccess ||
+        (e = dev_alloc(&g->d_grp_chunk, ngroups)) != hipSuccess ||
+        (e = dev_alloc(&g->d_sched_row, (size_t)ngroups * 4)) != hipSuccess ||
+        (e = dev_alloc(&g->d_sched_j, (size_t)ngroups * 16)) != hipSuccess)
         return alloc_status(e, "device allocation of the columns");
     if ((e = hipMemcpyAsync(g->d_col_off, g->col_off.data(), sizeof(int64_t) * (g->num_graphs + 1),
                             hipMemcpyHostToDevice, st)) != hipSuccess ||
         (e = hipMemcpyAsync(g->d_slot_off, g->slot_off.data(),
                             sizeof(int64_t) * (g->num_graphs + 1), hipMemcpyHostToDevice, st)) !=
+            hipSuccess ||
+        (e = hipMemcpyAsync(g->d_grp_off, g->grp_off.data(),
+                            sizeof(int64_t) * (g->num_graphs + 1), hipMemcpyHostToDevice, st)) !=
             hipSuccess)
         return hip_fail(e, "copy of offsets");
     if ((e = launch_fill(*g, st)) != hipSuccess) return hip_fail(e, "fill launch");
-    // Chunk bounds for the LDS-streamed kernels (skipped when the table
-    // would be large; those graphs use the generic kernels).
-    const int64_t nchunks = (n + g->chunk - 1) / g->chunk;
-    if (rows * (nchunks + 1) <= kMaxBoundEntries) {
-        if ((e = dev_alloc(&g->d_bnd, (size_t)(rows * (nchunks + 1)))) != hipSuccess)
-            return alloc_status(e, "device allocation of the chunk bounds");
-        if ((e = launch_bounds(*g, st)) != hipSuccess) return hip_fail(e, "bounds launch");
-    }
+    if (g->scheduled && (e = launch_sched_fill(*g, st)) != hipSuccess)
+        return hip_fail(e, "schedule fill launch");
     if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "graph fill");
     guard.g = nullptr;
     *out = g;
@@ -401,22 +435,32 @@ diffuser_status diffuser_graph_from_csr(int64_t n, int32_t num_graphs, const int
     const size_t rp_bytes = sizeof(int64_t) * num_graphs * (n + 1);
     const size_t ci_bytes = sizeof(int32_t) * col_off[num_graphs];
     const size_t off_bytes = sizeof(int64_t) * (num_graphs + 1);
+    // Row of every edge (the slot_row of an imported graph).
+    std::vector<int32_t> edge_row((size_t)col_off[num_graphs]);
+    for (int32_t gr = 0; gr < num_graphs; ++gr) {
+        const int64_t* rp = row_ptr_host + (int64_t)gr * (n + 1);
+        for (int64_t i = 0; i < n; ++i)
+            for (int64_t q = rp[i]; q < rp[i + 1]; ++q) edge_row[col_off[gr] + q] = (int32_t)i;
+    }
     if ((e = dev_alloc(&g->d_row_ptr, (size_t)num_graphs * (n + 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_col_idx, col_off[num_graphs])) != hipSuccess ||
         (e = dev_alloc(&g->d_col_off, num_graphs + 1)) != hipSuccess ||
-        (e = dev_alloc(&g->d_slot_ptr, (size_t)num_graphs * (n + 1))) != hipSuccess ||
+        (e = dev_alloc(&g->d_seg_ptr, (size_t)num_graphs * (n + 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_slot_col, col_off[num_graphs])) != hipSuccess ||
+        (e = dev_alloc(&g->d_slot_row, col_off[num_graphs])) != hipSuccess ||
         (e = dev_alloc(&g->d_slot_off, num_graphs + 1)) != hipSuccess)
         return alloc_status(e, "device allocation of the imported graph");
     if ((e = hipMemcpyAsync(g->d_row_ptr, row_ptr_host, rp_bytes, hipMemcpyHostToDevice, st)) !=
             hipSuccess ||
-        (e = hipMemcpyAsync(g->d_slot_ptr, row_ptr_host, rp_bytes, hipMemcpyHostToDevice, st)) !=
+        (e = hipMemcpyAsync(g->d_seg_ptr, row_ptr_host, rp_bytes, hipMemcpyHostToDevice, st)) !=
             hipSuccess ||
         (ci_bytes > 0 &&
          ((e = hipMemcpyAsync(g->d_col_idx, col_idx_host, ci_bytes, hipMemcpyHostToDevice, st)) !=
               hipSuccess ||
           (e = hipMemcpyAsync(g->d_slot_col, col_idx_host, ci_bytes, hipMemcpyHostToDevice, st)) !=
-              hipSuccess)) ||
+              hipSuccess ||
+          (e = hipMemcpyAsync(g->d_slot_row, edge_row.data(), ci_bytes, hipMemcpyHostToDevice,
+                              st)) != hipSuccess)) ||
         (e = hipMemcpyAsync(g->d_col_off, col_off.data(), off_bytes, hipMemcpyHostToDevice, st)) !=
             hipSuccess ||
         (e = hipMemcpyAsync(g->d_slot_off, col_off.data(), off_bytes, hipMemcpyHostToDevice,
@@ -440,23 +484,22 @@ diffuser_status diffuser_graph_info(const diffuser_graph* g, int64_t* n, int32_t
 }
 
 diffuser_status diffuser_graph_copy_slots(const diffuser_graph* g, int32_t graph,
-                                          int64_t* slot_ptr_host, int32_t* slot_col_host,
+                                          int32_t* slot_row_host, int32_t* slot_col_host,
                                           void* stream) {
     g_last_error.clear();
     if (auto s = check_graph(g)) return s;
     if (graph < 0 || graph >= g->num_graphs)
         return fail(DIFFUSER_ERR_INVALID_ARG, "graph index out of range");
-    if (!slot_ptr_host || (!slot_col_host && g->slots[graph] > 0))
+    if (g->slots[graph] > 0 && (!slot_row_host || !slot_col_host))
         return fail(DIFFUSER_ERR_INVALID_ARG, "NULL output array");
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if ((e = hipMemcpyAsync(slot_ptr_host, g->d_slot_ptr + (int64_t)graph * (g->n + 1),
-                            sizeof(int64_t) * (g->n + 1), hipMemcpyDeviceToHost, st)) !=
-            hipSuccess ||
-        (g->slots[graph] > 0 &&
-         (e = hipMemcpyAsync(slot_col_host, g->d_slot_col + g->slot_off[graph],
-                             sizeof(int32_t) * g->slots[graph], hipMemcpyDeviceToHost, st)) !=
-             hipSuccess))
+    const size_t bytes = sizeof(int32_t) * g->slots[graph];
+    if (g->slots[graph] > 0 &&
+        ((e = hipMemcpyAsync(slot_row_host, g->d_slot_row + g->slot_off[graph], bytes,
+                             hipMemcpyDeviceToHost, st)) != hipSuccess ||
+         (e = hipMemcpyAsync(slot_col_host, g->d_slot_col + g->slot_off[graph], bytes,
+                             hipMemcpyDeviceToHost, st)) != hipSuccess))
         return hip_fail(e, "copy of the slot layout");
     if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "slot layout copy");
     return DIFFUSER_OK;

@@ -3,7 +3,8 @@
 //   Z_{k+1}[i] = (1 - alpha) * sum_{j in N(i)} A_ij Z_k[j] + alpha * V[i].
 // The edge weights A are the same in every step; only Z changes.
 //
-// Generic path (any slot layout; padding slots are skipped). One wavefront
+// Generic path (any slot layout: the row segment, then any scheduled random
+// slots; padding slots are skipped). One wavefront
 // per row. A group of L lanes gathers one neighbour row of Z_k
 // with 16-byte loads (L = d * elem_size / 16), so a wave consumes 64 / L
 // edges per iteration; the groups' partial sums are reduced at the end and
@@ -19,10 +20,9 @@ constexpr int kWavesPerBlock = 4;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
-void k_diffuse_step(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ slot_ptr,
-                    const int32_t* __restrict__ slot_col, const int64_t* __restrict__ slot_off,
-                    const T* __restrict__ A, const T* __restrict__ Zk, const T* __restrict__ V,
-                    T* __restrict__ Zn, const float* __restrict__ row_scale, float alpha) {
+void k_diffuse_step(GenericGraph gg, int32_t H, const T* __restrict__ A, const T* __restrict__ Zk,
+                    const T* __restrict__ V, T* __restrict__ Zn,
+                    const float* __restrict__ row_scale, float alpha) {
     constexpr int E = chunk<T>::kElems;
     constexpr int L = D / E;
     constexpr int EPI = kWave / L;
@@ -30,26 +30,27 @@ void k_diffuse_step(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __r
 
     const int wave = threadIdx.x / kWave;
     const int lane = __lane_id();
+    const int64_t n = gg.n;
     const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     if (i >= n) return;
     const int32_t bh = blockIdx.y;
     const int32_t b = bh / H, h = bh - b * H;
-    const int32_t gr = num_graphs == 1 ? 0 : b;
-    const int64_t* rp = slot_ptr + (int64_t)gr * (n + 1);
-    const int32_t* cols = slot_col + slot_off[gr];
-    const T* Ab = A + a_block_offset(slot_off, num_graphs, H, b, h);
-    const int64_t e0 = rp[i], e1 = rp[i + 1];
+    const int32_t gr = gg.num_graphs == 1 ? 0 : b;
+    const RowSlots rs = gg.row(gr, i);
+    const T* Ab = A + a_block_offset(gg.slot_off, gg.num_graphs, H, b, h);
+    const int64_t e1 = rs.count();
     const int sub = lane % L, grp = lane / L;
     const T* Zb = Zk + (int64_t)bh * n * D + sub * E;
 
     float acc[E];
 #pragma unroll
     for (int c = 0; c < E; ++c) acc[c] = 0.0f;
-    for (int64_t base = e0; base < e1; base += EPI) {
+    for (int64_t base = 0; base < e1; base += EPI) {
         const int64_t e = base + grp;
-        const int32_t j = e < e1 ? cols[e] : -1;
+        int32_t j = -1;
+        const int64_t slot = e < e1 ? rs.slot(e, j) : 0;
         if (j >= 0) {
-            const float a = chunk<T>::load1(Ab + e);
+            const float a = chunk<T>::load1(Ab + slot);
             float z[E];
             chunk<T>::load(Zb + (int64_t)j * D, z);
 #pragma unroll
@@ -78,10 +79,10 @@ hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A,
                     const void* V, void* Zn, const float* row_scale, float alpha,
                     hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
-    hipLaunchKernelGGL((k_diffuse_step<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st, g.n,
-                       s.H, g.num_graphs, g.d_slot_ptr, g.d_slot_col, g.d_slot_off,
-                       static_cast<const T*>(A), static_cast<const T*>(Zk),
-                       static_cast<const T*>(V), static_cast<T*>(Zn), row_scale, alpha);
+    hipLaunchKernelGGL((k_diffuse_step<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
+                       generic_graph(g), s.H, static_cast<const T*>(A),
+                       static_cast<const T*>(Zk), static_cast<const T*>(V),
+                       static_cast<T*>(Zn), row_scale, alpha);
     return hipGetLastError();
 }
 
@@ -99,6 +100,20 @@ hipError_t launch_d(const diffuser_graph& g, const attn_shape& s, const void* A,
 }
 
 }  // namespace
+
+GenericGraph generic_graph(const diffuser_graph& g) {
+    GenericGraph gg;
+    gg.n = g.n;
+    gg.num_graphs = g.num_graphs;
+    gg.rnd_width = g.rnd_width;
+    gg.seg_ptr = g.d_seg_ptr;
+    gg.slot_col = g.d_slot_col;
+    gg.slot_off = g.d_slot_off;
+    gg.rnd = g.scheduled ? g.d_rnd : nullptr;
+    gg.rnd_cnt = g.scheduled ? g.d_rnd_cnt : nullptr;
+    gg.rslot = g.scheduled ? g.d_rslot : nullptr;
+    return gg;
+}
 
 hipError_t launch_diffuse_step(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,

@@ -5,26 +5,33 @@
 // and input-independent ("1.2.1", section 2: static random edges are fixed
 // before execution and reproducible from the seed).
 //
-// Three kernels, one wavefront per row where rows are independent:
-//   draw : random extras of a row by rejection sampling on a counter-based
-//          SplitMix64 stream, sorted into an ELL table, plus the row's edge
-//          count and its weight-slot count;
-//   scan : exclusive scan of per-row counts into int64 offsets (one block
-//          per graph);
-//   fill : the sorted merge window u (G minus window) u random into the
-//          ascending CSR, and the column of every weight slot.
+// Kernels, one wavefront per row (or row block) where those are independent:
+//   draw  : random extras of a row by rejection sampling on a counter-based
+//           SplitMix64 stream, sorted into an ELL table, plus the row's edge
+//           count and its row-segment slot count;
+//   scan  : exclusive scan of per-row counts into int64 offsets (one block
+//           per graph);
+//   fill  : the sorted merge window u (G minus window) u random into the
+//           ascending CSR, and the edge of every row-segment slot;
+//   sched : the random schedule of each row block (count, then fill).
 //
-// Weight-slot layout (where a row's edge weights live in A). A global row
-// holds its columns 0, 1, ... in order. Any other row holds three segments,
-// each a multiple of 8 slots so every segment starts 16-byte aligned in bf16:
+// Weight-slot layout (where the edge weights live in A). Every segment is a
+// multiple of 8 slots, so it starts 16-byte aligned in bf16. A global row's
+// segment holds its columns 0, 1, ... in order. Any other row's segment:
 //   window : 8-column blocks from (lo & ~7) through the last window column
 //            (hi, or i when causal); slot t is column (lo & ~7) + t when that
 //            column lies in the window, else padding;
 //   global : slot t < g is global G[t] unless G[t] lies in the window (or,
 //            when causal, above i); padding to a multiple of 8;
-//   random : the row's random columns in ascending order (when causal, only
-//            those below the window); padding to a multiple of 8.
-// Padding slots carry column -1 and weight 0.
+//   random : (unscheduled graphs only) the row's random columns, ascending
+//            (when causal, only those below the window), padded.
+// Scheduled graphs hold the random edges after all row segments, in
+// schedule order: for each row block (kRowBlock rows) and key chunk
+// (kChunkRows keys) with random edges, the block's edges into that chunk by
+// row, then column, two edges of one row per pair (an odd one out paired
+// with a dummy), 16 pairs = kGroupSlots slots per group, the last group of
+// a (block, chunk) padded with dummy pairs. Padding and dummy slots carry
+// row and column -1 and weight 0.
 #include "internal.h"
 
 namespace diffuser {
@@ -64,7 +71,8 @@ __host__ __device__ __forceinline__ int64_t round8(int64_t x) { return (x + 7) &
 
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int32_t R,
-            int32_t rnd_width, int32_t causal, uint64_t seed, int32_t* __restrict__ deg,
+            int32_t rnd_width, int32_t causal, int32_t scheduled, uint64_t seed,
+            int32_t* __restrict__ deg,
             int32_t* __restrict__ slots, int32_t* __restrict__ rnd,
             int32_t* __restrict__ rnd_cnt, int32_t* __restrict__ status) {
     __shared__ int32_t taken[kWavesPerBlock][kMaxSampled];
@@ -142,7 +150,7 @@ void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
         if (lane == 0) {
             rnd_cnt[row] = m;
             deg[row] = (int32_t)(wlen + (g - g_in) + m);
-            slots[row] = (int32_t)((hi - wb0) / 8 * 8 + 8 + round8(g) + round8(m));
+            slots[row] = (int32_t)((hi - wb0) / 8 * 8 + 8 + round8(g) + (scheduled ? 0 : round8(m)));
         }
         return;
     }
@@ -161,7 +169,8 @@ void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
     if (lane == 0) {
         rnd_cnt[row] = below;
         deg[row] = (int32_t)((i - lo + 1) + g_before + below);
-        slots[row] = (int32_t)((i - wb0) / 8 * 8 + 8 + round8(g_before) + round8(below));
+        slots[row] = (int32_t)((i - wb0) / 8 * 8 + 8 + round8(g_before) +
+                               (scheduled ? 0 : round8(below)));
     }
 }
 
@@ -209,11 +218,12 @@ void k_scan(int64_t n, const int32_t* __restrict__ deg, int64_t* __restrict__ ro
 
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int32_t rnd_width,
-            int32_t causal, const int64_t* __restrict__ row_ptr,
-            const int64_t* __restrict__ col_off, const int64_t* __restrict__ slot_ptr,
+            int32_t causal, int32_t scheduled, const int64_t* __restrict__ row_ptr,
+            const int64_t* __restrict__ col_off, const int64_t* __restrict__ seg_ptr,
             const int64_t* __restrict__ slot_off, const int32_t* __restrict__ rnd,
             const int32_t* __restrict__ rnd_cnt, int32_t* __restrict__ col_idx,
-            int32_t* __restrict__ slot_col) {
+            int32_t* __restrict__ slot_col, int32_t* __restrict__ slot_row,
+            int32_t* __restrict__ rslot) {
     const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
     const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -221,9 +231,10 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
     if (i >= n) return;
     const int64_t row = gr * n + i;
     const int64_t* rp = row_ptr + gr * (n + 1);
-    const int64_t* sp = slot_ptr + gr * (n + 1);
+    const int64_t* sp = seg_ptr + gr * (n + 1);
     int32_t* out = col_idx + col_off[gr] + rp[i];
     int32_t* sout = slot_col + slot_off[gr] + sp[i];
+    int32_t* rout = slot_row + slot_off[gr] + sp[i];
     // Every store below is kept inside this row's entries.
     const int64_t deg = rp[i + 1] - rp[i];
     const int64_t nslot = sp[i + 1] - sp[i];
@@ -233,6 +244,7 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
         for (int64_t j = lane; j < nslot; j += kWave) {
             if (j < deg) out[j] = (int32_t)j;
             sout[j] = j <= last ? (int32_t)j : -1;
+            rout[j] = j <= last ? (int32_t)i : -1;
         }
         return;
     }
@@ -269,10 +281,12 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
         const int64_t pos = q + gx_less + (right ? wlen : 0);
         if (v <= last && pos < deg) out[pos] = (int32_t)v;
     }
-    // Weight slots: window blocks, globals, randoms.
+    // Row segment: window blocks, globals, then (unscheduled) randoms.
     for (int64_t t = lane; t < wseg && t < nslot; t += kWave) {
         const int64_t j = wb0 + t;
-        sout[t] = (j >= lo && j <= wend) ? (int32_t)j : -1;
+        const bool in = j >= lo && j <= wend;
+        sout[t] = in ? (int32_t)j : -1;
+        rout[t] = in ? (int32_t)i : -1;
     }
     for (int64_t t = lane; t < gseg && wseg + t < nslot; t += kWave) {
         int32_t c = -1;
@@ -281,46 +295,145 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
             if ((p < lo || p > hi) && p <= last) c = (int32_t)p;
         }
         sout[wseg + t] = c;
+        rout[wseg + t] = c >= 0 ? (int32_t)i : -1;
     }
+    if (scheduled) return;
+    int32_t* rs = rslot + row * (int64_t)rnd_width;
     for (int64_t t = lane; wseg + gseg + t < nslot; t += kWave) {
         sout[wseg + gseg + t] = t < m ? rr[t] : -1;
+        rout[wseg + gseg + t] = t < m ? (int32_t)i : -1;
+        if (t < m) rs[t] = (int32_t)(sp[i] + wseg + gseg + t);
     }
 }
 
-// bnd[row][c] = number of the row's kept random columns below c * chunk.
-__global__ __launch_bounds__(256)
-void k_bounds(int64_t rows, int32_t rnd_width, int32_t chunk, int32_t nchunks,
-              const int32_t* __restrict__ rnd, const int32_t* __restrict__ rnd_cnt,
-              int32_t* __restrict__ bnd) {
-    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= rows) return;
-    const int32_t m = rnd_cnt[row];
-    const int32_t* rr = rnd + row * (int64_t)rnd_width;
-    int32_t* out = bnd + row * (int64_t)(nchunks + 1);
-    int32_t k = 0;
-    for (int32_t c = 0; c <= nchunks; ++c) {
-        const int64_t lim = (int64_t)c * chunk;
-        while (k < m && rr[k] < lim) ++k;
-        out[c] = k;
+// Random schedule of one row block per wavefront (lanes 0..kRowBlock-1 own
+// its rows). The block's rows are merged chunk by chunk in ascending key
+// order; for each chunk with random edges every row contributes
+// ceil(count / 2) pairs, the block ceil(pairs / 16) groups. kFill = false
+// counts the groups; kFill = true writes them (group numbering from
+// grp_ptr) plus the slots' edges and each random edge's slot.
+struct SchedArgs {
+    int64_t n;
+    int32_t rnd_width, nrb;
+    const int32_t* rnd;
+    const int32_t* rnd_cnt;
+    int32_t* counts;               // [graphs][nrb] (count pass)
+    const int64_t* grp_ptr;        // [graphs][nrb + 1]
+    const int64_t* grp_off;        // [graphs + 1]
+    const int64_t* seg_ptr;        // [graphs][n + 1]
+    const int64_t* slot_off;       // [graphs + 1]
+    int32_t* grp_chunk;
+    uint8_t* sched_row;            // [groups][16] pair rows
+    uint16_t* sched_j;             // [groups][32] slot key rows
+    int32_t* slot_col;
+    int32_t* slot_row;
+    int32_t* rslot;
+};
+
+__device__ __forceinline__ int32_t wave_min(int32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const int32_t o = __shfl_xor(v, off);
+        v = o < v ? o : v;
     }
+    return v;
+}
+
+// Position of slot s (0..31) of a group in the [32] key-row array: slot
+// 8k + a is the low half of word 4k + a, slot 8k + 4 + a its high half.
+__device__ __forceinline__ int32_t sched_j_index(int32_t s) {
+    const int32_t k = s >> 3, a = s & 7;
+    return 2 * (4 * k + (a & 3)) + (a >> 2);
+}
+
+template <bool kFill>
+__global__ __launch_bounds__(kWave * kWavesPerBlock)
+void k_sched(SchedArgs a) {
+    const int wave = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const int32_t rb = (int32_t)blockIdx.x * kWavesPerBlock + wave;
+    const int64_t gr = blockIdx.y;
+    if (rb >= a.nrb) return;
+    const int64_t n = a.n;
+    const int64_t i = (int64_t)rb * kRowBlock + lane;
+    const bool own = lane < kRowBlock && i < n;
+    const int64_t row = gr * n + (own ? i : 0);
+    const int32_t cnt = own ? a.rnd_cnt[row] : 0;
+    const int32_t* rr = a.rnd + row * (int64_t)a.rnd_width;
+    int64_t grp = 0, gbase = 0, rand_base = 0, soff = 0;
+    if (kFill) {
+        gbase = a.grp_off[gr];
+        grp = a.grp_ptr[gr * (a.nrb + 1) + rb];
+        rand_base = a.seg_ptr[gr * (n + 1) + n];
+        soff = a.slot_off[gr];
+    }
+    int64_t groups = 0;
+    int32_t p = 0;
+    while (true) {
+        const int32_t cur = p < cnt ? rr[p] / kChunkRows : INT32_MAX;
+        const int32_t c = wave_min(cur);
+        if (c == INT32_MAX) break;
+        int32_t k = p;
+        while (k < cnt && rr[k] / kChunkRows == c) ++k;
+        const int32_t pairs = (k - p + 1) >> 1;
+        // Exclusive prefix of the pair counts over the lanes.
+        int32_t incl = pairs;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int32_t o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        const int32_t total = __shfl(incl, kWave - 1);
+        const int32_t ng = (total + 15) / 16;
+        if (kFill) {
+            const int32_t pre = incl - pairs;
+            const int64_t g0 = grp + groups;   // first group of this chunk (in graph)
+            for (int32_t t = 0; t < pairs; ++t) {
+                const int32_t pidx = pre + t;
+                const int64_t gg = gbase + g0 + pidx / 16;
+                const int32_t pig = pidx % 16;
+                a.sched_row[gg * 16 + pig] = (uint8_t)lane;
+                for (int h = 0; h < 2; ++h) {
+                    const int32_t kk = p + 2 * t + h;
+                    const bool real = kk < k;
+                    const int32_t s = 2 * pig + h;
+                    const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
+                    a.sched_j[gg * kGroupSlots + sched_j_index(s)] =
+                        real ? (uint16_t)(rr[kk] - c * kChunkRows) : (uint16_t)kZeroRow;
+                    a.slot_col[soff + slot] = real ? rr[kk] : -1;
+                    a.slot_row[soff + slot] = real ? (int32_t)i : -1;
+                    if (real) a.rslot[row * (int64_t)a.rnd_width + kk] = (int32_t)slot;
+                }
+            }
+            // Dummy pairs that pad the chunk's last group.
+            for (int32_t pidx = total + lane; pidx < 16 * ng; pidx += kWave) {
+                const int64_t gg = gbase + g0 + pidx / 16;
+                const int32_t pig = pidx % 16;
+                a.sched_row[gg * 16 + pig] = (uint8_t)0xFF;
+                for (int h = 0; h < 2; ++h) {
+                    const int32_t s = 2 * pig + h;
+                    const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
+                    a.sched_j[gg * kGroupSlots + sched_j_index(s)] = (uint16_t)kZeroRow;
+                    a.slot_col[soff + slot] = -1;
+                    a.slot_row[soff + slot] = -1;
+                }
+            }
+            for (int32_t q = lane; q < ng; q += kWave) a.grp_chunk[gbase + g0 + q] = c;
+        }
+        groups += ng;
+        p = k;
+    }
+    if (!kFill && lane == 0) a.counts[gr * a.nrb + rb] = (int32_t)groups;
 }
 
 }  // namespace
-
-hipError_t launch_bounds(const diffuser_graph& g, hipStream_t st) {
-    const int64_t rows = (int64_t)g.num_graphs * g.n;
-    const int32_t nchunks = (int32_t)((g.n + g.chunk - 1) / g.chunk);
-    hipLaunchKernelGGL(k_bounds, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, rows,
-                       g.rnd_width, g.chunk, nchunks, g.d_rnd, g.d_rnd_cnt, g.d_bnd);
-    return hipGetLastError();
-}
 
 hipError_t launch_draw(const diffuser_graph& g, int32_t* deg, int32_t* slots, int32_t* status,
                        hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
     hipLaunchKernelGGL(k_draw, grid, dim3(kWave * kWavesPerBlock), 0, st, g.n, g.radius,
-                       g.d_global, g.num_global, g.num_random, g.rnd_width, g.causal, g.seed,
-                       deg, slots, g.d_rnd, g.d_rnd_cnt, status);
+                       g.d_global, g.num_global, g.num_random, g.rnd_width, g.causal,
+                       (int32_t)g.scheduled, g.seed, deg, slots, g.d_rnd, g.d_rnd_cnt, status);
     return hipGetLastError();
 }
 
@@ -334,9 +447,44 @@ hipError_t launch_scan(int64_t n, int32_t num_graphs, const int32_t* counts, int
 hipError_t launch_fill(const diffuser_graph& g, hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
     hipLaunchKernelGGL(k_fill, grid, dim3(kWave * kWavesPerBlock), 0, st, g.n, g.radius,
-                       g.d_global, g.num_global, g.rnd_width, g.causal, g.d_row_ptr,
-                       g.d_col_off, g.d_slot_ptr, g.d_slot_off, g.d_rnd, g.d_rnd_cnt,
-                       g.d_col_idx, g.d_slot_col);
+                       g.d_global, g.num_global, g.rnd_width, g.causal, (int32_t)g.scheduled,
+                       g.d_row_ptr, g.d_col_off, g.d_seg_ptr, g.d_slot_off, g.d_rnd,
+                       g.d_rnd_cnt, g.d_col_idx, g.d_slot_col, g.d_slot_row, g.d_rslot);
+    return hipGetLastError();
+}
+
+static SchedArgs sched_args(const diffuser_graph& g) {
+    SchedArgs a{};
+    a.n = g.n;
+    a.rnd_width = g.rnd_width;
+    a.nrb = (int32_t)((g.n + kRowBlock - 1) / kRowBlock);
+    a.rnd = g.d_rnd;
+    a.rnd_cnt = g.d_rnd_cnt;
+    a.grp_ptr = g.d_grp_ptr;
+    a.grp_off = g.d_grp_off;
+    a.seg_ptr = g.d_seg_ptr;
+    a.slot_off = g.d_slot_off;
+    a.grp_chunk = g.d_grp_chunk;
+    a.sched_row = reinterpret_cast<uint8_t*>(g.d_sched_row);
+    a.sched_j = reinterpret_cast<uint16_t*>(g.d_sched_j);
+    a.slot_col = g.d_slot_col;
+    a.slot_row = g.d_slot_row;
+    a.rslot = g.d_rslot;
+    return a;
+}
+
+hipError_t launch_sched_count(const diffuser_graph& g, int32_t* counts, hipStream_t st) {
+    SchedArgs a = sched_args(g);
+    a.counts = counts;
+    dim3 grid((unsigned)((a.nrb + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
+    hipLaunchKernelGGL(k_sched<false>, grid, dim3(kWave * kWavesPerBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sched_fill(const diffuser_graph& g, hipStream_t st) {
+    SchedArgs a = sched_args(g);
+    dim3 grid((unsigned)((a.nrb + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
+    hipLaunchKernelGGL(k_sched<true>, grid, dim3(kWave * kWavesPerBlock), 0, st, a);
     return hipGetLastError();
 }
 

@@ -9,6 +9,14 @@
 
 #include "../../include/diffuser.h"
 
+namespace diffuser {
+constexpr int32_t kRowBlock = 16;     // rows per block of the random schedule
+constexpr int32_t kChunkRows = 512;   // key rows per chunk of the random schedule
+constexpr int32_t kGroupSlots = 32;   // weight slots per schedule group
+constexpr uint32_t kZeroRow = kChunkRows;  // key row index of a dummy slot
+constexpr int64_t kMaxScheduledN = 1 << 16;
+}  // namespace diffuser
+
 struct diffuser_graph {
     int64_t n = 0;
     int32_t num_graphs = 0;
@@ -30,24 +38,45 @@ struct diffuser_graph {
     int32_t* d_col_idx = nullptr;   // [col_off[num_graphs]]
     int64_t* d_col_off = nullptr;   // [num_graphs + 1]
 
-    // Weight-slot layout (where the edge weights live in A): per graph,
-    // slot_ptr [n + 1] row offsets and slot_col [slots] the column of each
-    // slot (-1 = padding, weight 0). Imported graphs use their CSR as is.
+    // Weight-slot layout (where the edge weights live in A), per graph:
+    //  * row segments: seg_ptr [n + 1] row offsets (a global row: its
+    //    columns; any other row: window blocks then global columns);
+    //  * random area (built graphs): from seg_ptr[n], groups of kGroupSlots
+    //    slots in random-schedule order (below).
+    // slot_col / slot_row [slots] give each slot's edge, or -1 for padding
+    // (weight 0). Imported graphs use their CSR as is (no random area).
     std::vector<int64_t> slots;     // [num_graphs]
     std::vector<int64_t> slot_off;  // [num_graphs + 1] prefix sums of slots
-    int64_t max_row_slots = 0;
-    int64_t* d_slot_ptr = nullptr;  // [num_graphs][n + 1]
+    int64_t max_row_slots = 0;      // longest row segment
+    int64_t* d_seg_ptr = nullptr;   // [num_graphs][n + 1]
     int32_t* d_slot_col = nullptr;  // [slot_off[num_graphs]]
+    int32_t* d_slot_row = nullptr;  // [slot_off[num_graphs]]
     int64_t* d_slot_off = nullptr;  // [num_graphs + 1]
 
     // Generator metadata (structured graphs).
     int32_t* d_global = nullptr;    // [num_global]
     int32_t* d_rnd = nullptr;       // [num_graphs][n][rnd_width] ascending
     int32_t* d_rnd_cnt = nullptr;   // [num_graphs][n] random columns kept per row
-    // Key-row chunking of the LDS-streamed kernels: bnd[gr][i][c] = number of
-    // row i's kept random columns below c * chunk, c = 0 .. ceil(n / chunk).
-    int32_t chunk = 512;
-    int32_t* d_bnd = nullptr;
+    int32_t* d_rslot = nullptr;     // [num_graphs][n][rnd_width] slot of each kept random edge
+
+    // Random schedule (built graphs with n <= kMaxScheduledN; larger graphs
+    // keep each row's random columns as a third row segment, ascending,
+    // padded to a multiple of 8). Rows form blocks of kRowBlock, key rows
+    // chunks of kChunkRows. For each (row block, chunk) the block's random
+    // edges with keys in the chunk are listed by row, two edges of one row
+    // per pair (a lone edge is paired with a dummy), 16 pairs per group; a
+    // group's 32 weights occupy 32 consecutive slots of the random area.
+    bool scheduled = false;
+    std::vector<int64_t> groups;    // [num_graphs]
+    std::vector<int64_t> grp_off;   // [num_graphs + 1] prefix sums of groups
+    int64_t* d_grp_off = nullptr;   // [num_graphs + 1]
+    int64_t* d_grp_ptr = nullptr;   // [num_graphs][nrb + 1] groups of each row block
+    int32_t* d_grp_chunk = nullptr; // [grp_off[num_graphs]] key chunk of each group
+    uint32_t* d_sched_row = nullptr;// [groups][4]: byte p of word k = row (within the
+                                    //   block) of pair 4k + p, 0xFF for a dummy pair
+    uint32_t* d_sched_j = nullptr;  // [groups][16]: word 4k + a = key row (within the
+                                    //   chunk) of slot 8k + a (low half) and of slot
+                                    //   8k + 4 + a (high half); kZeroRow for a dummy
 };
 
 namespace diffuser {
@@ -64,12 +93,19 @@ hipError_t launch_draw(const diffuser_graph& g, int32_t* deg, int32_t* slots, in
 // (each graph from 0); max_count[gr] receives each graph's largest count.
 hipError_t launch_scan(int64_t n, int32_t num_graphs, const int32_t* counts, int64_t* offsets,
                        int64_t* max_count, hipStream_t st);
-// Fills d_col_idx and d_slot_col from the draws.
+// Fills d_col_idx and the row segments' d_slot_col / d_slot_row.
 hipError_t launch_fill(const diffuser_graph& g, hipStream_t st);
-// Fills d_bnd from the draws.
-hipError_t launch_bounds(const diffuser_graph& g, hipStream_t st);
+// Counts the schedule groups of every row block into counts [graphs][nrb].
+hipError_t launch_sched_count(const diffuser_graph& g, int32_t* counts, hipStream_t st);
+// Writes the random schedule, the random area's slot_col / slot_row and
+// d_rslot (needs d_grp_ptr, d_grp_off and the allocated schedule arrays).
+hipError_t launch_sched_fill(const diffuser_graph& g, hipStream_t st);
 
 // --- compute (scores.hip, diffuse.hip) --------------------------------------
+// Graph arrays of the generic kernels (defined in vec.h).
+struct GenericGraph;
+GenericGraph generic_graph(const diffuser_graph& g);
+
 struct attn_shape {
     int32_t B, H, d;          // d = d_h for scores, d_v for diffusion
     diffuser_dtype dtype;

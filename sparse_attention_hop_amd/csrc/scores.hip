@@ -4,8 +4,8 @@
 //   A_ij = exp(s_ij - m_i) / sum_{u in N(i)} exp(s_iu - m_i),  m_i = max_j s_ij.
 // The normalisation runs over exactly the row's neighbour set.
 //
-// Generic path (any slot layout). One wavefront per row; padding slots
-// (column -1) get weight 0. A group of L lanes covers one key row with
+// Generic path (any slot layout: the row segment, then any scheduled random
+// slots). One wavefront per row; padding slots (column -1) get weight 0. A group of L lanes covers one key row with
 // 16-byte loads (L = d * elem_size / 16), so a wave scores 64 / L edges per
 // iteration. The scale folds log2(e) so the exponentials are exp2.
 // Pass 1 keeps an online (max, sum) per lane group; pass 2 recomputes the
@@ -23,10 +23,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 template <typename T, int D>
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
-void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ slot_ptr,
-                      const int32_t* __restrict__ slot_col, const int64_t* __restrict__ slot_off,
-                      const T* __restrict__ Q, const T* __restrict__ K, T* __restrict__ A,
-                      float* __restrict__ row_scale, float scale_log2) {
+void k_scores_softmax(GenericGraph gg, int32_t H, const T* __restrict__ Q,
+                      const T* __restrict__ K, T* __restrict__ A, float* __restrict__ row_scale,
+                      float scale_log2) {
     constexpr int E = chunk<T>::kElems;
     constexpr int L = D / E;          // lanes per edge
     constexpr int EPI = kWave / L;    // edges per iteration
@@ -34,15 +33,15 @@ void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* _
 
     const int wave = threadIdx.x / kWave;
     const int lane = __lane_id();
+    const int64_t n = gg.n;
     const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     if (i >= n) return;
     const int32_t bh = blockIdx.y;
     const int32_t b = bh / H, h = bh - b * H;
-    const int32_t gr = num_graphs == 1 ? 0 : b;
-    const int64_t* rp = slot_ptr + (int64_t)gr * (n + 1);
-    const int32_t* cols = slot_col + slot_off[gr];
-    T* Ab = A + a_block_offset(slot_off, num_graphs, H, b, h);
-    const int64_t e0 = rp[i], e1 = rp[i + 1];
+    const int32_t gr = gg.num_graphs == 1 ? 0 : b;
+    const RowSlots rs = gg.row(gr, i);
+    T* Ab = A + a_block_offset(gg.slot_off, gg.num_graphs, H, b, h);
+    const int64_t e1 = rs.count();
     const int sub = lane % L, grp = lane / L;
 
     float q[E];
@@ -50,9 +49,10 @@ void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* _
     const T* Kb = K + (int64_t)bh * n * D + sub * E;
 
     float m = -INFINITY, l = 0.0f;
-    for (int64_t base = e0; base < e1; base += EPI) {
+    for (int64_t base = 0; base < e1; base += EPI) {
         const int64_t e = base + grp;
-        const int32_t j = e < e1 ? cols[e] : -1;
+        int32_t j = -1;
+        if (e < e1) rs.slot(e, j);
         const bool valid = j >= 0;
         float dot = 0.0f;
         if (valid) {
@@ -84,9 +84,10 @@ void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* _
     const float inv = 1.0f / l;
 
     float stored_sum = 0.0f;  // sum of the weights as stored (after rounding)
-    for (int64_t base = e0; base < e1; base += EPI) {
+    for (int64_t base = 0; base < e1; base += EPI) {
         const int64_t e = base + grp;
-        const int32_t j = e < e1 ? cols[e] : -1;
+        int32_t j = -1;
+        const int64_t slot = e < e1 ? rs.slot(e, j) : 0;
         const bool valid = j >= 0;
         float dot = 0.0f;
         if (valid) {
@@ -99,7 +100,7 @@ void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* _
         for (int off = 1; off < L; off <<= 1) dot += __shfl_xor(dot, off);
         if (e < e1 && sub == 0) {
             const float a = valid ? fast_exp2(dot * scale_log2 - m) * inv : 0.0f;
-            chunk<T>::store1(Ab + e, a);
+            chunk<T>::store1(Ab + slot, a);
             stored_sum += chunk<T>::round(a);
         }
     }
@@ -113,14 +114,36 @@ void k_scores_softmax(int64_t n, int32_t H, int32_t num_graphs, const int64_t* _
     }
 }
 
+// Zeroes the dummy slots of the random area (no row owns them) in every
+// (b, h) block of A.
+template <typename T>
+__global__ __launch_bounds__(256)
+void k_zero_dummies(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ slot_off,
+                    const int32_t* __restrict__ slot_col, const int64_t* __restrict__ seg_ptr,
+                    const int64_t* __restrict__ grp_off, T* __restrict__ A) {
+    const int32_t bh = blockIdx.y;
+    const int32_t b = bh / H, h = bh - b * H;
+    const int32_t gr = num_graphs == 1 ? 0 : b;
+    const int64_t base = seg_ptr[(int64_t)gr * (n + 1) + n];           // random area start
+    const int64_t len = kGroupSlots * (grp_off[gr + 1] - grp_off[gr]);  // its length
+    const int32_t* cols = slot_col + slot_off[gr] + base;
+    T* Ab = A + a_block_offset(slot_off, num_graphs, H, b, h) + base;
+    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < len;
+         s += (int64_t)gridDim.x * blockDim.x)
+        if (cols[s] < 0) chunk<T>::store1(Ab + s, 0.0f);
+}
+
 template <typename T, int D>
 hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
                     void* A, float* row_scale, float scale_log2, hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
-    hipLaunchKernelGGL((k_scores_softmax<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st, g.n,
-                       s.H, g.num_graphs, g.d_slot_ptr, g.d_slot_col, g.d_slot_off,
-                       static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<T*>(A),
-                       row_scale, scale_log2);
+    hipLaunchKernelGGL((k_scores_softmax<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
+                       generic_graph(g), s.H, static_cast<const T*>(Q),
+                       static_cast<const T*>(K), static_cast<T*>(A), row_scale, scale_log2);
+    if (g.scheduled)
+        hipLaunchKernelGGL((k_zero_dummies<T>), dim3(64, (unsigned)(s.B * s.H)), dim3(256), 0, st,
+                           g.n, s.H, g.num_graphs, g.d_slot_off, g.d_slot_col, g.d_seg_ptr,
+                           g.d_grp_off, static_cast<T*>(A));
     return hipGetLastError();
 }
 

@@ -78,4 +78,56 @@ __device__ __forceinline__ int64_t a_block_offset(const int64_t* slot_off, int32
     return (int64_t)H * slot_off[b] + (int64_t)h * slots_b;
 }
 
+// The weight slots of one row for the generic kernels: its row segment
+// [seg_begin, seg_end) (columns from slot_col) followed by its scheduled
+// random edges (slots from rslot, columns from rnd), if any.
+struct RowSlots {
+    int64_t seg_begin, seg_len;
+    const int32_t* slot_col;   // the graph's slot columns
+    const int32_t* rslot;      // this row's random slots (or null)
+    const int32_t* rcol;       // this row's random columns
+    int32_t rcnt;
+
+    __device__ __forceinline__ int64_t count() const { return seg_len + rcnt; }
+    // Slot and column of the row's k-th slot; column -1 marks padding.
+    __device__ __forceinline__ int64_t slot(int64_t k, int32_t& col) const {
+        if (k < seg_len) {
+            col = slot_col[seg_begin + k];
+            return seg_begin + k;
+        }
+        col = rcol[k - seg_len];
+        return rslot[k - seg_len];
+    }
+};
+
+// Graph arrays the generic kernels read.
+struct GenericGraph {
+    int64_t n;
+    int32_t num_graphs, rnd_width;
+    const int64_t* seg_ptr;    // [graphs][n + 1]
+    const int32_t* slot_col;   // [slots of all graphs]
+    const int64_t* slot_off;   // [graphs + 1]
+    const int32_t* rnd;        // [graphs][n][rnd_width] (scheduled graphs, else null)
+    const int32_t* rnd_cnt;    // [graphs][n]
+    const int32_t* rslot;      // [graphs][n][rnd_width]
+
+    __device__ __forceinline__ RowSlots row(int32_t gr, int64_t i) const {
+        RowSlots r;
+        const int64_t* sp = seg_ptr + (int64_t)gr * (n + 1);
+        r.seg_begin = sp[i];
+        r.seg_len = sp[i + 1] - sp[i];
+        r.slot_col = slot_col + slot_off[gr];
+        r.rcnt = 0;
+        r.rslot = nullptr;
+        r.rcol = nullptr;
+        if (rslot != nullptr) {
+            const int64_t row = (int64_t)gr * n + i;
+            r.rcnt = rnd_cnt[row];
+            r.rslot = rslot + row * rnd_width;
+            r.rcol = rnd + row * rnd_width;
+        }
+        return r;
+    }
+};
+
 }  // namespace diffuser

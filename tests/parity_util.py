@@ -57,19 +57,20 @@ def dtype_name(t) -> str:
     return "f32" if t == torch.float32 else "bf16"
 
 
-def slot_permutation(slot_ptr, slot_col, row_ptr, col_idx):
+def slot_permutation(slot_row, slot_col, row_ptr, col_idx):
     """Indices of the non-padding weight slots in ascending-CSR order.
 
-    Checks that every row's non-padding slots hold exactly that row's CSR
-    columns (each once), so A in slot layout maps one-to-one onto edges."""
-    slot_ptr = np.asarray(slot_ptr)
+    Checks that padding slots carry row and column -1 and that the other
+    slots hold exactly the graph's edges, each once, so A in slot layout maps
+    one-to-one onto the edges."""
+    slot_row = np.asarray(slot_row)
     slot_col = np.asarray(slot_col)
-    n = len(slot_ptr) - 1
-    rows = np.repeat(np.arange(n), np.diff(slot_ptr))
+    n = len(row_ptr) - 1
     valid = slot_col >= 0
+    assert np.array_equal(valid, slot_row >= 0), "padding slots carry row and column -1"
     idx = np.nonzero(valid)[0]
-    order = np.lexsort((slot_col[idx], rows[idx]))
+    order = np.lexsort((slot_col[idx], slot_row[idx]))
     perm = idx[order]
-    assert np.array_equal(rows[perm], np.repeat(np.arange(n), np.diff(row_ptr))), "slot rows"
+    assert np.array_equal(slot_row[perm], np.repeat(np.arange(n), np.diff(row_ptr))), "slot rows"
     assert np.array_equal(slot_col[perm], col_idx), "slot columns"
     return perm, ~valid

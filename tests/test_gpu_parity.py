@@ -33,17 +33,17 @@ def _check_csr(orc, g, n, r, G, R, ng, causal, seed):
         grp, gcols = g.copy_csr(gr)
         assert np.array_equal(grp, rp[gr]), f"row_ptr mismatch in graph {gr}"
         assert np.array_equal(gcols, cols[gr]), f"col_idx mismatch in graph {gr}"
-        sp, sc = g.copy_slots(gr)
-        pu.slot_permutation(sp, sc, rp[gr], cols[gr])
-        assert np.all(np.diff(sp) % 8 == 0), "segments are multiples of 8 slots"
+        sr, sc = g.copy_slots(gr)
+        pu.slot_permutation(sr, sc, rp[gr], cols[gr])
+        assert len(sc) % 8 == 0, "segments and groups are multiples of 8 slots"
     return rp, cols
 
 
 def _a_csr(g, A_h, b, h, H, gr, rp, cols):
     """The (b, h) block of A (slot layout) in ascending-CSR order; padding
     slots must hold exactly 0."""
-    sp, sc = g.copy_slots(gr)
-    perm, pad = pu.slot_permutation(sp, sc, rp[gr], cols[gr])
+    sr, sc = g.copy_slots(gr)
+    perm, pad = pu.slot_permutation(sr, sc, rp[gr], cols[gr])
     off = g.a_offset(b, h, H)
     blk = A_h[off:off + g.slots[gr]]
     assert np.all(blk[pad] == 0), "padding slots must hold 0"
@@ -317,10 +317,11 @@ def test_constant_v_fixed_point_gpu():
 def test_rowsums_bf16():
     g, q, k, v = _setup(dtype=torch.bfloat16)
     A = sah.scores_softmax(q, k, g).double().cpu().numpy()
-    sp, _ = g.copy_slots(0)
+    sr, _ = g.copy_slots(0)
     ns = g.slots[0]
+    valid = sr >= 0
     for bh in range(6):
-        sums = np.add.reduceat(A[bh * ns:(bh + 1) * ns], sp[:-1])
+        sums = np.bincount(sr[valid], weights=A[bh * ns:(bh + 1) * ns][valid], minlength=g.n)
         assert np.abs(sums - 1).max() <= pu.ROWSUM_BF16
 
 
@@ -403,8 +404,8 @@ def test_fast_diffusion_shapes(orc, case, K, alpha):
 def _slot_classes(g, gr, n, r, G, causal):
     """Class of every weight slot of graph gr: 0 window, 1 global column,
     2 random, 3 global row, -1 padding."""
-    sp, sc = g.copy_slots(gr)
-    rows = np.repeat(np.arange(n), np.diff(sp))
+    rows, sc = g.copy_slots(gr)
+    rows = np.maximum(rows, 0)
     Gs = np.zeros(n, dtype=bool)
     Gs[list(G)] = True
     lo = np.maximum(rows - r, 0)
@@ -432,8 +433,8 @@ def test_fast_diffusion_by_segment(orc, name):
     v = make_tensor((B, H, w.n, 64), 7, torch.bfloat16).to(DEV)
     A = sah.scores_softmax(q, k, g)
     ns = g.slots[0]
-    sp, sc = g.copy_slots(0)
-    perm, _ = pu.slot_permutation(sp, sc, rp[0], cols[0])
+    sr, sc = g.copy_slots(0)
+    perm, _ = pu.slot_permutation(sr, sc, rp[0], cols[0])
     for c, cname in enumerate(["window", "global-col", "random", "global-row"]):
         mask = torch.tensor(np.tile(cls == c, B * H), device=DEV)
         Ac = torch.where(mask, A, torch.zeros_like(A))
