@@ -59,6 +59,7 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_slot_row);
     hipFree(g->d_slot_off);
     hipFree(g->d_rslot);
+    hipFree(g->d_row_info);
     hipFree(g->d_grp_off);
     hipFree(g->d_grp_ptr);
     hipFree(g->d_grp_chunk);
@@ -75,6 +76,7 @@ void free_graph_memory(diffuser_graph* g) {
     g->d_slot_row = nullptr;
     g->d_slot_off = nullptr;
     g->d_rslot = nullptr;
+    g->d_row_info = nullptr;
     g->d_grp_off = nullptr;
     g->d_grp_ptr = nullptr;
     g->d_grp_chunk = nullptr;
@@ -272,6 +274,7 @@ diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stre
     if ((e = dev_alloc(&g->d_global, g->num_global)) != hipSuccess ||
         (e = dev_alloc(&g->d_rnd, (size_t)rows * std::max(g->rnd_width, 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_rslot, (size_t)rows * std::max(g->rnd_width, 1))) != hipSuccess ||
+        (e = dev_alloc(&g->d_row_info, (size_t)rows * 4)) != hipSuccess ||
         (e = dev_alloc(&g->d_rnd_cnt, rows)) != hipSuccess ||
         (e = dev_alloc(&g->d_row_ptr, (size_t)g->num_graphs * (n + 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_col_off, g->num_graphs + 1)) != hipSuccess ||

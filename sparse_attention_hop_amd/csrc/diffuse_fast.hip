@@ -1,14 +1,440 @@
-// Diffusion step on scheduled graphs (bf16, head width 64): being rebuilt
-// on the random schedule; the generic kernel runs meanwhile.
+// Diffusion step on scheduled graphs, bf16 storage, head width 64:
+//   Z_{k+1}[i] = (1 - alpha) * c_i * sum_j A_ij Z_k[j] + alpha * V[i]
+// ("Diffuser" reading notes, section 2.4, eq. S.7; c_i rescales the stored
+// weights of row i to sum to one, or is 1).
+//
+// Every part of the sum is a v_mfma_f32_16x16x32_bf16 product
+//   D[channel][row] += Z^T[channel][key] * W^T[key][row]
+// over 16 rows, 16 channels and 32 keys. The Z^T operand comes from LDS
+// with ds_read_b64_tr_b16 (each lane reads 4 channels of one key row; the
+// read hands every lane one channel of 4 key rows); the W^T operand is 8
+// consecutive weight slots of one row, one 16-byte load.
+//  * window edges: the 32 keys are consecutive columns of the band;
+//  * global columns: the g global rows of Z_k, staged once per workgroup;
+//  * random edges: the 32 keys are the slots of one schedule group, whose
+//    key rows lie in the current chunk; the weight operand keeps a pair's
+//    two weights in the lanes of the pair's row and zeroes them elsewhere.
+// A workgroup (16 waves, 16 rows each) streams Z_k of its (batch, head)
+// through LDS in chunks of kChunkRows rows, double-buffered: the next
+// chunk is fetched into registers while the current one is used. Rows of
+// Z_k sit in LDS at 128 bytes; the 32-byte quarter of channel block nb is
+// stored at quarter nb ^ sw(row), which spreads the 16 rows of one
+// transposed read over the banks.
+// Global rows get workgroups of their own (32 rows; the 16 waves split each
+// chunk's keys and add their partial sums in a fixed order at the end).
+// Workgroups are numbered so that each XCD (workgroup id mod 8) works
+// through a contiguous range of (batch, head) pairs.
 #include "internal.h"
+#include "vec.h"
 
 namespace diffuser {
+namespace {
 
-bool fast_diffuse_supported(const diffuser_graph&, const attn_shape&) { return false; }
+#define LDS_AS __attribute__((address_space(3)))
 
-hipError_t launch_diffuse_fast(const diffuser_graph&, const attn_shape&, const void*, const void*,
-                               const void*, void*, const float*, float, hipStream_t) {
-    return hipErrorNotSupported;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kWaves = 16;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kD = 64;                                // head width
+constexpr int kNB = 4;                                // 16-channel blocks
+constexpr int kRowBytes = kD * 2;                     // a Z row in LDS
+constexpr int kBufBytes = (kChunkRows + 1) * kRowBytes;  // chunk + zero row
+constexpr int kTileRows = kWaves * kRowBlock;         // rows per row-tile workgroup
+constexpr int kGrowRows = 32;                         // global rows per workgroup
+constexpr int kMaxGlobal = 224;                       // staged global rows (LDS room)
+constexpr int kLdsBytes = 2 * kBufBytes + kMaxGlobal * kRowBytes;
+
+static_assert(kWaves * 2 * kNB * 4 * kWave * 4 <= 2 * kBufBytes, "grow partial sums fit");
+
+struct FastArgs {
+    int64_t n;
+    int32_t H, num_graphs, radius, g, causal, nchunks, nrb;
+    const int64_t* slot_off;    // [graphs + 1]
+    const int64_t* seg_ptr;     // [graphs][n + 1]
+    const int4* row_info;       // [graphs][n]
+    const int32_t* G;           // [g]
+    const int64_t* grp_ptr;     // [graphs][nrb + 1]
+    const int64_t* grp_off;     // [graphs + 1]
+    const int32_t* grp_chunk;   // [groups]
+    const uint32_t* sched_row;  // [groups][4]
+    const uint32_t* sched_j;    // [groups][16]
+    const uint16_t* A;
+    const uint16_t* Z;
+    const uint16_t* V;
+    uint16_t* Zn;
+    const float* row_scale;     // [B*H][n] or null
+    float alpha;
+    int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items;
+};
+
+// Quarter swizzle of a row in LDS (two bits, so the 16 rows 8k + q of one
+// transposed read land in distinct bank groups), as a byte XOR.
+__device__ __forceinline__ uint32_t swz(uint32_t row) {
+    return (((row >> 1) & 1u) | (((row >> 3) & 1u) << 1)) << 5;
+}
+
+// Byte address, for channel block 0, of the 8 bytes lane `a4` reads from
+// `row` (quarter swizzle applied; XOR with nb << 5 selects block nb).
+__device__ __forceinline__ uint32_t row_addr(uint32_t buf, uint32_t row, uint32_t a4) {
+    return (buf + row * kRowBytes + 8u * a4) ^ swz(row);
+}
+
+__device__ __forceinline__ i16x4 tr_read(const char LDS_AS* lds, uint32_t addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + addr));
+}
+
+// Z^T operand of channel block nb: key rows of b1 (k = 8 kg + 0..3) and of
+// b2 (k = 8 kg + 4..7).
+__device__ __forceinline__ bf16x8 z_operand(const char LDS_AS* lds, uint32_t b1, uint32_t b2,
+                                            int nb) {
+    const i16x4 lo = tr_read(lds, b1 ^ ((uint32_t)nb << 5));
+    const i16x4 hi = tr_read(lds, b2 ^ ((uint32_t)nb << 5));
+    const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], h[0], h[1]});
+}
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Chunk rows [c0, c0 + kChunkRows) of Z_k, 16 bytes per thread and piece:
+// piece t of thread x is quarter-half (x + kThreads t) % 8 of row
+// (x + kThreads t) / 8. Rows at or beyond n repeat row n - 1 (their
+// weights are zero).
+constexpr int kPieces = kChunkRows * 8 / kThreads;
+
+__device__ __forceinline__ void fetch_chunk(u32x4 (&zr)[kPieces], const uint16_t* Zbh, int64_t n,
+                                            int64_t c0) {
+#pragma unroll
+    for (int t = 0; t < kPieces; ++t) {
+        const int idx = threadIdx.x + kThreads * t;
+        int64_t src = c0 + (idx >> 3);
+        src = src < n ? src : n - 1;
+        zr[t] = load16(Zbh + src * kD + (idx & 7) * 8);
+    }
+}
+
+__device__ __forceinline__ void store_chunk(char LDS_AS* lds, uint32_t buf,
+                                            const u32x4 (&zr)[kPieces]) {
+#pragma unroll
+    for (int t = 0; t < kPieces; ++t) {
+        const uint32_t idx = threadIdx.x + kThreads * t;
+        const uint32_t row = idx >> 3;
+        *reinterpret_cast<u32x4 LDS_AS*>(lds + buf + row * kRowBytes +
+                                        (((idx & 7) * 16) ^ swz(row))) = zr[t];
+    }
+}
+
+__device__ __forceinline__ uint32_t to_bf16_pair(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Restart and store of one lane's accumulators: row `i`, channels
+// 16 nb + 4 kg .. + 3 for nb = 0..3.
+__device__ __forceinline__ void store_row(const FastArgs& a, int32_t bh, int64_t i, int kg,
+                                          const f32x4 (&acc)[kNB]) {
+    const float keep = a.row_scale ? (1.0f - a.alpha) * a.row_scale[(int64_t)bh * a.n + i]
+                                   : 1.0f - a.alpha;
+    const int64_t base = ((int64_t)bh * a.n + i) * kD + 4 * kg;
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(a.V + base + 16 * nb);
+        u32x2 o;
+        o[0] = to_bf16_pair(keep * acc[nb][0] + a.alpha * bf16_to_f32(v[0] & 0xffffu),
+                            keep * acc[nb][1] + a.alpha * bf16_to_f32(v[0] >> 16));
+        o[1] = to_bf16_pair(keep * acc[nb][2] + a.alpha * bf16_to_f32(v[1] & 0xffffu),
+                            keep * acc[nb][3] + a.alpha * bf16_to_f32(v[1] >> 16));
+        *reinterpret_cast<u32x2*>(a.Zn + base + 16 * nb) = o;
+    }
+}
+
+// Weight operand of a schedule group for the lanes of row `row` (0..15):
+// pair p of words w keeps its two weights where the pair's row matches.
+__device__ __forceinline__ u32x4 group_weights(const u32x4& w, uint32_t rows, uint32_t row) {
+    u32x4 b;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) b[p] = ((rows >> (8 * p)) & 0xffu) == row ? w[p] : 0u;
+    return b;
+}
+
+__global__ __launch_bounds__(kThreads)
+void k_diffuse_sched(FastArgs a) {
+    extern __shared__ __align__(16) char lds_raw[];
+    char LDS_AS* lds = (char LDS_AS*)lds_raw;
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int kg = lane >> 4;          // k-group of the MFMA operands
+    const int s16 = lane & 15;         // row (W^T) / channel (Z^T) index
+    const uint32_t a4 = lane & 3, q4 = (lane >> 2) & 3;   // transposed-read source
+
+    const int32_t item = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
+    if (item >= a.total_items) return;
+    const int32_t per_bh = a.grow_per_bh + a.tiles_per_bh;
+    const int32_t bh = item / per_bh;
+    const int32_t sub = item - bh * per_bh;
+    const int32_t b = bh / a.H, h = bh - b * a.H;
+    const int32_t gr = a.num_graphs == 1 ? 0 : b;
+    const int64_t n = a.n;
+    const uint16_t* Abh = a.A + a_block_offset(a.slot_off, a.num_graphs, a.H, b, h);
+    const uint16_t* Zbh = a.Z + (int64_t)bh * n * kD;
+    const int4* info = a.row_info + (int64_t)gr * n;
+    const uint32_t buf_off[2] = {0u, (uint32_t)kBufBytes};
+
+    // Zero row kChunkRows of both buffers (the key row of dummy slots).
+    if (threadIdx.x < 16) {
+        *reinterpret_cast<u32x4 LDS_AS*>(lds + buf_off[threadIdx.x >> 3] +
+                                        kChunkRows * kRowBytes + (threadIdx.x & 7) * 16) =
+            u32x4{0u, 0u, 0u, 0u};
+    }
+
+    if (sub < a.grow_per_bh) {
+        // ---------------- global rows -------------------------------------
+        const int q0 = sub * kGrowRows;
+        int64_t wbase[2];
+        int64_t wlen[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int q = q0 + 16 * mb + s16;
+            wbase[mb] = 0;
+            wlen[mb] = 0;
+            if (q < a.g) {
+                const int64_t i = a.G[q];
+                const int64_t* sp = a.seg_ptr + (int64_t)gr * (n + 1);
+                wbase[mb] = info[i].x;
+                wlen[mb] = sp[i + 1] - sp[i];
+            }
+        }
+        f32x4 acc[2][kNB];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 zr[kPieces];
+        fetch_chunk(zr, Zbh, n, 0);
+        store_chunk(lds, buf_off[0], zr);
+        for (int c = 0; c < a.nchunks; ++c) {
+            const int64_t c0 = (int64_t)c * kChunkRows;
+            const int64_t kc = c0 + 32 * wave;
+            u32x4 bop[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                bop[mb] = u32x4{0u, 0u, 0u, 0u};
+                if (kc + 8 * kg < wlen[mb]) bop[mb] = load16(Abh + wbase[mb] + kc + 8 * kg);
+            }
+            __syncthreads();   // chunk c stored by every wave
+            if (c + 1 < a.nchunks) fetch_chunk(zr, Zbh, n, c0 + kChunkRows);
+            if (kc < n) {
+                const uint32_t r1 = 32u * wave + 8u * kg + q4;
+                const uint32_t b1 = row_addr(buf_off[c & 1], r1, a4);
+                const uint32_t b2 = row_addr(buf_off[c & 1], r1 + 4, a4);
+#pragma unroll
+                for (int nb = 0; nb < kNB; ++nb) {
+                    const bf16x8 zop = z_operand(lds, b1, b2, nb);
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma(zop, bop[mb], acc[mb][nb]);
+                }
+            }
+            if (c + 1 < a.nchunks) store_chunk(lds, buf_off[(c + 1) & 1], zr);
+        }
+        // Fixed-order sum of the 16 waves' partial sums.
+        __syncthreads();
+        float LDS_AS* part = (float LDS_AS*)lds;   // [wave][mb][nb][e][lane]
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    part[(((wave * 2 + mb) * kNB + nb) * 4 + e) * kWave + lane] = acc[mb][nb][e];
+        __syncthreads();
+        constexpr int kPer = 2 * kNB * 4 * kWave;   // partial sums per wave
+        for (int idx = threadIdx.x; idx < kPer; idx += kThreads) {
+            float sum = 0.0f;
+            for (int w = 0; w < kWaves; ++w) sum += part[w * kPer + idx];
+            const int l = idx & 63, e = (idx >> 6) & 3, nb = (idx >> 8) & 3, mb = idx >> 10;
+            const int q = q0 + 16 * mb + (l & 15);
+            if (q >= a.g) continue;
+            const int64_t i = a.G[q];
+            const int ch = 16 * nb + 4 * (l >> 4) + e;
+            const int64_t o = ((int64_t)bh * n + i) * kD + ch;
+            const float keep = a.row_scale ? (1.0f - a.alpha) * a.row_scale[(int64_t)bh * n + i]
+                                           : 1.0f - a.alpha;
+            a.Zn[o] = (uint16_t)f32_to_bf16(keep * sum + a.alpha * bf16_to_f32(a.V[o]));
+        }
+        return;
+    }
+
+    // ---------------- row tile --------------------------------------------
+    const int64_t r0w = (int64_t)(sub - a.grow_per_bh) * kTileRows + (int64_t)kRowBlock * wave;
+    const bool active = r0w < n;
+    const int64_t my_row = r0w + s16;            // W^T column / output row of this lane
+    int4 ri = make_int4(0, 0, -1, 0);
+    if (my_row < n) ri = info[my_row];
+    const bool rok = my_row < n && ri.z >= 0;    // a non-global row
+
+    // Staged global rows (quarter swizzle by position q).
+    const uint32_t zg = 2u * kBufBytes;
+    const int gpad = (a.g + 31) & ~31;
+    for (int idx = threadIdx.x; idx < gpad * 8; idx += kThreads) {
+        const int q = idx >> 3, lu = idx & 7;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (q < a.g) v = load16(Zbh + (int64_t)a.G[q] * kD + lu * 8);
+        *reinterpret_cast<u32x4 LDS_AS*>(lds + zg + q * kRowBytes +
+                                        ((lu * 16) ^ swz((uint32_t)q))) = v;
+    }
+    u32x4 zr[kPieces];
+    fetch_chunk(zr, Zbh, n, 0);
+    store_chunk(lds, buf_off[0], zr);
+
+    // Schedule groups of this row block.
+    int64_t gp = 0, gend = 0, rbase = 0;
+    if (active) {
+        const int64_t rb = r0w / kRowBlock;
+        const int64_t* gpt = a.grp_ptr + (int64_t)gr * (a.nrb + 1);
+        gp = gpt[rb];
+        gend = gpt[rb + 1];
+        rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];   // random area of the graph
+    }
+    const int64_t goff = a.grp_off[gr];
+
+    // Band of this wave: key columns [band_lo, band_hi].
+    const int64_t wr_last = min(r0w + kRowBlock - 1, n - 1);
+    const int64_t band_lo = (r0w - a.radius < 0 ? 0 : r0w - a.radius) & ~31ll;
+    const int64_t band_hi = a.causal ? wr_last : min(n - 1, wr_last + a.radius);
+
+    f32x4 acc[kNB];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();   // globals staged, chunk 0 stored
+
+    // Global columns.
+    if (active) {
+        for (int q = 0; q < gpad; q += 32) {
+            u32x4 bop = {0u, 0u, 0u, 0u};
+            if (rok && q + 8 * kg < ri.w) bop = load16(Abh + ri.x + ri.z + q + 8 * kg);
+            const uint32_t r1 = (uint32_t)q + 8u * kg + q4;
+            const uint32_t b1 = row_addr(zg, r1, a4), b2 = row_addr(zg, r1 + 4, a4);
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(lds, b1, b2, nb), bop, acc[nb]);
+        }
+    }
+
+    // Random-group data, one group ahead.
+    uint32_t nx_j = 0, nx_rows = 0xffffffffu;
+    u32x4 nx_w = {0u, 0u, 0u, 0u};
+    auto fetch_group = [&](int64_t gi) {
+        nx_j = a.sched_j[(goff + gi) * 16 + 4 * kg + q4];
+        nx_rows = a.sched_row[(goff + gi) * 4 + kg];
+        nx_w = load16(Abh + rbase + (int64_t)kGroupSlots * gi + 8 * kg);
+    };
+    if (active && gp < gend) fetch_group(gp);
+
+    for (int c = 0; c < a.nchunks; ++c) {
+        const int64_t c0 = (int64_t)c * kChunkRows;
+        const uint32_t cur = buf_off[c & 1];
+        if (c > 0) __syncthreads();   // chunk c stored by every wave
+        const bool more = c + 1 < a.nchunks;
+        if (more) fetch_chunk(zr, Zbh, n, c0 + kChunkRows);
+        if (!active) {
+            if (more) store_chunk(lds, buf_off[(c + 1) & 1], zr);
+            continue;
+        }
+
+        // Window band.
+        const int64_t k_lo = max(band_lo, c0);
+        const int64_t k_hi = min(band_hi, c0 + kChunkRows - 1);
+        for (int64_t kc = k_lo; kc <= k_hi; kc += 32) {
+            const int32_t off = (int32_t)(kc + 8 * kg) - ri.y;
+            u32x4 bop = {0u, 0u, 0u, 0u};
+            if (rok && off >= 0 && off < ri.z) bop = load16(Abh + ri.x + off);
+            const uint32_t r1 = (uint32_t)(kc - c0) + 8u * kg + q4;
+            const uint32_t b1 = row_addr(cur, r1, a4), b2 = row_addr(cur, r1 + 4, a4);
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(lds, b1, b2, nb), bop, acc[nb]);
+        }
+
+        // Random groups of this chunk.
+        while (gp < gend && a.grp_chunk[goff + gp] == c) {
+            const uint32_t cj = nx_j, crows = nx_rows;
+            const u32x4 cw = nx_w;
+            if (gp + 1 < gend) fetch_group(gp + 1);
+            const u32x4 bop = group_weights(cw, crows, (uint32_t)s16);
+            const uint32_t b1 = row_addr(cur, cj & 0xffffu, a4);
+            const uint32_t b2 = row_addr(cur, cj >> 16, a4);
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(lds, b1, b2, nb), bop, acc[nb]);
+            ++gp;
+        }
+        if (more) store_chunk(lds, buf_off[(c + 1) & 1], zr);
+    }
+
+    if (rok) store_row(a, bh, my_row, kg, acc);
+}
+
+}  // namespace
+
+bool fast_diffuse_supported(const diffuser_graph& g, const attn_shape& s) {
+    if (!g.structured || !g.scheduled || s.dtype != DIFFUSER_BF16 || s.d != kD) return false;
+    if (g.num_global > kMaxGlobal) return false;
+    for (int64_t x : g.slots)
+        if (x >= (1ll << 31)) return false;
+    return true;
+}
+
+hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, const void* A,
+                               const void* Zk, const void* V, void* Zn, const float* row_scale,
+                               float alpha, hipStream_t st) {
+    FastArgs a;
+    a.n = g.n;
+    a.H = s.H;
+    a.num_graphs = g.num_graphs;
+    a.radius = g.radius;
+    a.g = g.num_global;
+    a.causal = g.causal;
+    a.nchunks = (int32_t)((g.n + kChunkRows - 1) / kChunkRows);
+    a.nrb = (int32_t)((g.n + kRowBlock - 1) / kRowBlock);
+    a.slot_off = g.d_slot_off;
+    a.seg_ptr = g.d_seg_ptr;
+    a.row_info = reinterpret_cast<const int4*>(g.d_row_info);
+    a.G = g.d_global;
+    a.grp_ptr = g.d_grp_ptr;
+    a.grp_off = g.d_grp_off;
+    a.grp_chunk = g.d_grp_chunk;
+    a.sched_row = g.d_sched_row;
+    a.sched_j = g.d_sched_j;
+    a.A = static_cast<const uint16_t*>(A);
+    a.Z = static_cast<const uint16_t*>(Zk);
+    a.V = static_cast<const uint16_t*>(V);
+    a.Zn = static_cast<uint16_t*>(Zn);
+    a.row_scale = row_scale;
+    a.alpha = alpha;
+    const int32_t BH = s.B * s.H;
+    a.tiles_per_bh = (int32_t)((g.n + kTileRows - 1) / kTileRows);
+    a.grow_per_bh = (g.num_global + kGrowRows - 1) / kGrowRows;
+    a.total_items = BH * (a.tiles_per_bh + a.grow_per_bh);
+    a.per_xcd = (a.total_items + 7) / 8;
+    static int attr_device = -1;   // dynamic LDS above 64 KB is enabled per device
+    if (attr_device != g.device) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_diffuse_sched),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e != hipSuccess) return e;
+        attr_device = g.device;
+    }
+    const size_t lds = (size_t)2 * kBufBytes + (size_t)((g.num_global + 31) & ~31) * kRowBytes;
+    hipLaunchKernelGGL(k_diffuse_sched, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), lds, st,
+                       a);
+    return hipGetLastError();
 }
 
 }  // namespace diffuser

@@ -223,7 +223,7 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
             const int64_t* __restrict__ slot_off, const int32_t* __restrict__ rnd,
             const int32_t* __restrict__ rnd_cnt, int32_t* __restrict__ col_idx,
             int32_t* __restrict__ slot_col, int32_t* __restrict__ slot_row,
-            int32_t* __restrict__ rslot) {
+            int32_t* __restrict__ rslot, int4* __restrict__ row_info) {
     const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
     const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -246,6 +246,7 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
             sout[j] = j <= last ? (int32_t)j : -1;
             rout[j] = j <= last ? (int32_t)i : -1;
         }
+        if (lane == 0) row_info[row] = make_int4((int32_t)sp[i], 0, -1, 0);
         return;
     }
     const int64_t lo = i - r < 0 ? 0 : i - r;
@@ -261,6 +262,7 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
     const int32_t* rr = rnd + row * (int64_t)rnd_width;
     const int32_t r_before = count_less(rr, m, lo);
     const int64_t woff = g_before + r_before;
+    if (lane == 0) row_info[row] = make_int4((int32_t)sp[i], (int32_t)wb0, (int32_t)wseg, (int32_t)gseg);
 
     // Ascending CSR: (left extras) window (right extras).
     for (int64_t k = lane; k < wlen; k += kWave) {
@@ -449,7 +451,8 @@ hipError_t launch_fill(const diffuser_graph& g, hipStream_t st) {
     hipLaunchKernelGGL(k_fill, grid, dim3(kWave * kWavesPerBlock), 0, st, g.n, g.radius,
                        g.d_global, g.num_global, g.rnd_width, g.causal, (int32_t)g.scheduled,
                        g.d_row_ptr, g.d_col_off, g.d_seg_ptr, g.d_slot_off, g.d_rnd,
-                       g.d_rnd_cnt, g.d_col_idx, g.d_slot_col, g.d_slot_row, g.d_rslot);
+                       g.d_rnd_cnt, g.d_col_idx, g.d_slot_col, g.d_slot_row, g.d_rslot,
+                       reinterpret_cast<int4*>(g.d_row_info));
     return hipGetLastError();
 }
 

@@ -58,6 +58,9 @@ struct diffuser_graph {
     int32_t* d_rnd = nullptr;       // [num_graphs][n][rnd_width] ascending
     int32_t* d_rnd_cnt = nullptr;   // [num_graphs][n] random columns kept per row
     int32_t* d_rslot = nullptr;     // [num_graphs][n][rnd_width] slot of each kept random edge
+    // Per-row segment geometry, int4 {segment start, window block start
+    // column (lo & ~7), window slots (-1 for a global row), global slots}.
+    int32_t* d_row_info = nullptr;  // [num_graphs][n][4]
 
     // Random schedule (built graphs with n <= kMaxScheduledN; larger graphs
     // keep each row's random columns as a third row segment, ascending,
