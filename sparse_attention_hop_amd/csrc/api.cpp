@@ -62,7 +62,7 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_row_info);
     hipFree(g->d_grp_off);
     hipFree(g->d_grp_ptr);
-    hipFree(g->d_grp_chunk);
+    hipFree(g->d_grp_cptr);
     hipFree(g->d_sched_row);
     hipFree(g->d_sched_j);
     g->d_row_ptr = nullptr;
@@ -79,7 +79,7 @@ void free_graph_memory(diffuser_graph* g) {
     g->d_row_info = nullptr;
     g->d_grp_off = nullptr;
     g->d_grp_ptr = nullptr;
-    g->d_grp_chunk = nullptr;
+    g->d_grp_cptr = nullptr;
     g->d_sched_row = nullptr;
     g->d_sched_j = nullptr;
 }
@@ -358,7 +358,9 @@ diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stre
     if ((e = dev_alloc(&g->d_col_idx, g->col_off[g->num_graphs])) != hipSuccess ||
         (e = dev_alloc(&g->d_slot_col, g->slot_off[g->num_graphs])) != hipSuccess ||
         (e = dev_alloc(&g->d_slot_row, g->slot_off[g->num_graphs])) != hipSuccess ||
-        (e = dev_alloc(&g->d_grp_chunk, ngroups)) != hipSuccess ||
+        (e = dev_alloc(&g->d_grp_cptr, g->scheduled ? (size_t)g->num_graphs * nrb *
+                                                          ((n + kChunkRows - 1) / kChunkRows + 1)
+                                                    : 1)) != hipSuccess ||
         (e = dev_alloc(&g->d_sched_row, (size_t)ngroups * 4)) != hipSuccess ||
         (e = dev_alloc(&g->d_sched_j, (size_t)ngroups * 16)) != hipSuccess)
         return alloc_status(e, "device allocation of the columns");

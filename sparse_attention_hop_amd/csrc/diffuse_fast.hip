@@ -47,8 +47,12 @@ constexpr int kRowBytes = kD * 2;                     // a Z row in LDS
 constexpr int kBufBytes = (kChunkRows + 1) * kRowBytes;  // chunk + zero row
 constexpr int kTileRows = kWaves * kRowBlock;         // rows per row-tile workgroup
 constexpr int kGrowRows = 32;                         // global rows per workgroup
-constexpr int kMaxGlobal = 224;                       // staged global rows (LDS room)
-constexpr int kLdsBytes = 2 * kBufBytes + kMaxGlobal * kRowBytes;
+constexpr int kMaxGlobal = 128;                       // staged global rows (LDS room)
+constexpr int kGroupBytes = 144;                      // staged group: weights, key rows, pair rows
+constexpr int kStageGroups = 6;                       // groups per wave and chunk staged in LDS
+constexpr int kStageBytes = kStageGroups * kGroupBytes;
+constexpr int kLdsBytes = 2 * kBufBytes + kMaxGlobal * kRowBytes + kWaves * kStageBytes;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 static_assert(kWaves * 2 * kNB * 4 * kWave * 4 <= 2 * kBufBytes, "grow partial sums fit");
 
@@ -61,7 +65,7 @@ struct FastArgs {
     const int32_t* G;           // [g]
     const int64_t* grp_ptr;     // [graphs][nrb + 1]
     const int64_t* grp_off;     // [graphs + 1]
-    const int32_t* grp_chunk;   // [groups]
+    const int32_t* grp_cptr;    // [graphs][nrb][nchunks + 1]
     const uint32_t* sched_row;  // [groups][4]
     const uint32_t* sched_j;    // [groups][16]
     const uint16_t* A;
@@ -167,6 +171,11 @@ __device__ __forceinline__ u32x4 group_weights(const u32x4& w, uint32_t rows, ui
     return b;
 }
 
+// Barrier for LDS traffic only: global loads in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __global__ __launch_bounds__(kThreads)
 void k_diffuse_sched(FastArgs a) {
     extern __shared__ __align__(16) char lds_raw[];
@@ -214,6 +223,13 @@ void k_diffuse_sched(FastArgs a) {
                 wlen[mb] = sp[i + 1] - sp[i];
             }
         }
+        auto fetch_w = [&](u32x4 (&bop)[2], int64_t kc) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                bop[mb] = u32x4{0u, 0u, 0u, 0u};
+                if (kc + 8 * kg < wlen[mb]) bop[mb] = load16(Abh + wbase[mb] + kc + 8 * kg);
+            }
+        };
         f32x4 acc[2][kNB];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -221,18 +237,19 @@ void k_diffuse_sched(FastArgs a) {
             for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         u32x4 zr[kPieces];
         fetch_chunk(zr, Zbh, n, 0);
+        u32x4 bop[2];
+        fetch_w(bop, 32 * wave);
         store_chunk(lds, buf_off[0], zr);
         for (int c = 0; c < a.nchunks; ++c) {
             const int64_t c0 = (int64_t)c * kChunkRows;
             const int64_t kc = c0 + 32 * wave;
-            u32x4 bop[2];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                bop[mb] = u32x4{0u, 0u, 0u, 0u};
-                if (kc + 8 * kg < wlen[mb]) bop[mb] = load16(Abh + wbase[mb] + kc + 8 * kg);
+            lds_barrier();   // chunk c stored by every wave
+            const bool more = c + 1 < a.nchunks;
+            u32x4 nbop[2];
+            if (more) {
+                fetch_chunk(zr, Zbh, n, c0 + kChunkRows);
+                fetch_w(nbop, kc + kChunkRows);
             }
-            __syncthreads();   // chunk c stored by every wave
-            if (c + 1 < a.nchunks) fetch_chunk(zr, Zbh, n, c0 + kChunkRows);
             if (kc < n) {
                 const uint32_t r1 = 32u * wave + 8u * kg + q4;
                 const uint32_t b1 = row_addr(buf_off[c & 1], r1, a4);
@@ -244,10 +261,14 @@ void k_diffuse_sched(FastArgs a) {
                     for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma(zop, bop[mb], acc[mb][nb]);
                 }
             }
-            if (c + 1 < a.nchunks) store_chunk(lds, buf_off[(c + 1) & 1], zr);
+            if (more) {
+                store_chunk(lds, buf_off[(c + 1) & 1], zr);
+                bop[0] = nbop[0];
+                bop[1] = nbop[1];
+            }
         }
         // Fixed-order sum of the 16 waves' partial sums.
-        __syncthreads();
+        lds_barrier();
         float LDS_AS* part = (float LDS_AS*)lds;   // [wave][mb][nb][e][lane]
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -256,7 +277,7 @@ void k_diffuse_sched(FastArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     part[(((wave * 2 + mb) * kNB + nb) * 4 + e) * kWave + lane] = acc[mb][nb][e];
-        __syncthreads();
+        lds_barrier();
         constexpr int kPer = 2 * kNB * 4 * kWave;   // partial sums per wave
         for (int idx = threadIdx.x; idx < kPer; idx += kThreads) {
             float sum = 0.0f;
@@ -294,29 +315,60 @@ void k_diffuse_sched(FastArgs a) {
     }
     u32x4 zr[kPieces];
     fetch_chunk(zr, Zbh, n, 0);
-    store_chunk(lds, buf_off[0], zr);
 
-    // Schedule groups of this row block.
-    int64_t gp = 0, gend = 0, rbase = 0;
-    if (active) {
-        const int64_t rb = r0w / kRowBlock;
-        const int64_t* gpt = a.grp_ptr + (int64_t)gr * (a.nrb + 1);
-        gp = gpt[rb];
-        gend = gpt[rb + 1];
-        rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];   // random area of the graph
-    }
+    // Schedule groups of this row block, chunk by chunk. The groups of the
+    // next chunk (up to kStageGroups) are fetched into registers, compactly,
+    // and moved to this wave's LDS staging area once the current chunk's
+    // groups are done with it.
+    const uint32_t stg = zg + (uint32_t)gpad * kRowBytes + (uint32_t)wave * kStageBytes;
+    const int64_t rb = active ? r0w / kRowBlock : 0;
+    const int32_t* cptr = a.grp_cptr + ((int64_t)gr * a.nrb + rb) * (a.nchunks + 1);
     const int64_t goff = a.grp_off[gr];
+    const int64_t rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];   // random area of the graph
+    u32x4 pw = {0u, 0u, 0u, 0u}, pj = {0u, 0u, 0u, 0u}, pr = {0u, 0u, 0u, 0u};
+    auto fetch_groups = [&](int c) {
+        const int32_t g0 = cptr[c];
+        const int32_t cnt = min(cptr[c + 1] - g0, kStageGroups);
+        if (lane < 4 * cnt) {
+            pw = load16(Abh + rbase + (int64_t)kGroupSlots * g0 + 8 * lane);
+            pj = *reinterpret_cast<const u32x4*>(a.sched_j + (goff + g0) * 16 + 4 * lane);
+        }
+        if (lane < cnt) pr = *reinterpret_cast<const u32x4*>(a.sched_row + (goff + g0 + lane) * 4);
+    };
+    auto store_groups = [&](int cnt) {
+        if (lane < 4 * cnt) {
+            const uint32_t o = stg + (uint32_t)(lane >> 2) * kGroupBytes + (lane & 3) * 16;
+            *reinterpret_cast<u32x4 LDS_AS*>(lds + o) = pw;
+            *reinterpret_cast<u32x4 LDS_AS*>(lds + o + 64) = pj;
+        }
+        if (lane < cnt)
+            *reinterpret_cast<u32x4 LDS_AS*>(lds + stg + (uint32_t)lane * kGroupBytes + 128) = pr;
+    };
+    if (active) {
+        fetch_groups(0);
+        store_groups(min(cptr[1] - cptr[0], kStageGroups));
+    }
 
-    // Band of this wave: key columns [band_lo, band_hi].
+    // Band of this wave: key columns [band_lo, band_hi], 32 at a time; the
+    // weights of the next step are always in flight.
     const int64_t wr_last = min(r0w + kRowBlock - 1, n - 1);
     const int64_t band_lo = (r0w - a.radius < 0 ? 0 : r0w - a.radius) & ~31ll;
     const int64_t band_hi = a.causal ? wr_last : min(n - 1, wr_last + a.radius);
+    auto band_w = [&](int64_t kc) {
+        const int32_t off = (int32_t)(kc + 8 * kg) - ri.y;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (rok && kc <= band_hi && off >= 0 && off < ri.z) w = load16(Abh + ri.x + off);
+        return w;
+    };
+    int64_t kc_next = band_lo;
+    u32x4 band_next = band_w(band_lo);
 
     f32x4 acc[kNB];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();   // globals staged, chunk 0 stored
+    store_chunk(lds, buf_off[0], zr);
+    lds_barrier();   // globals staged, chunk 0 stored
 
     // Global columns.
     if (active) {
@@ -330,53 +382,58 @@ void k_diffuse_sched(FastArgs a) {
         }
     }
 
-    // Random-group data, one group ahead.
-    uint32_t nx_j = 0, nx_rows = 0xffffffffu;
-    u32x4 nx_w = {0u, 0u, 0u, 0u};
-    auto fetch_group = [&](int64_t gi) {
-        nx_j = a.sched_j[(goff + gi) * 16 + 4 * kg + q4];
-        nx_rows = a.sched_row[(goff + gi) * 4 + kg];
-        nx_w = load16(Abh + rbase + (int64_t)kGroupSlots * gi + 8 * kg);
-    };
-    if (active && gp < gend) fetch_group(gp);
-
     for (int c = 0; c < a.nchunks; ++c) {
         const int64_t c0 = (int64_t)c * kChunkRows;
         const uint32_t cur = buf_off[c & 1];
-        if (c > 0) __syncthreads();   // chunk c stored by every wave
+        if (c > 0) lds_barrier();   // chunk c stored by every wave
         const bool more = c + 1 < a.nchunks;
         if (more) fetch_chunk(zr, Zbh, n, c0 + kChunkRows);
         if (!active) {
             if (more) store_chunk(lds, buf_off[(c + 1) & 1], zr);
             continue;
         }
+        const int32_t g0 = cptr[c], gcnt = cptr[c + 1] - g0;
+        if (more) fetch_groups(c + 1);
 
         // Window band.
-        const int64_t k_lo = max(band_lo, c0);
         const int64_t k_hi = min(band_hi, c0 + kChunkRows - 1);
-        for (int64_t kc = k_lo; kc <= k_hi; kc += 32) {
-            const int32_t off = (int32_t)(kc + 8 * kg) - ri.y;
-            u32x4 bop = {0u, 0u, 0u, 0u};
-            if (rok && off >= 0 && off < ri.z) bop = load16(Abh + ri.x + off);
+        while (kc_next <= k_hi) {
+            const int64_t kc = kc_next;
+            const u32x4 bop = band_next;
+            kc_next += 32;
+            band_next = band_w(kc_next);
             const uint32_t r1 = (uint32_t)(kc - c0) + 8u * kg + q4;
             const uint32_t b1 = row_addr(cur, r1, a4), b2 = row_addr(cur, r1 + 4, a4);
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(lds, b1, b2, nb), bop, acc[nb]);
         }
 
-        // Random groups of this chunk.
-        while (gp < gend && a.grp_chunk[goff + gp] == c) {
-            const uint32_t cj = nx_j, crows = nx_rows;
-            const u32x4 cw = nx_w;
-            if (gp + 1 < gend) fetch_group(gp + 1);
+        // Random groups of this chunk (staged ones from LDS, any others
+        // straight from memory).
+        for (int32_t k = 0; k < gcnt; ++k) {
+            uint32_t cj, crows;
+            u32x4 cw;
+            if (k < kStageGroups) {
+                const uint32_t o = stg + (uint32_t)k * kGroupBytes;
+                cw = *reinterpret_cast<const u32x4 LDS_AS*>(lds + o + 16 * kg);
+                cj = *reinterpret_cast<const uint32_t LDS_AS*>(lds + o + 64 + 4 * (4 * kg + q4));
+                crows = *reinterpret_cast<const uint32_t LDS_AS*>(lds + o + 128 + 4 * kg);
+            } else {
+                const int64_t gi = g0 + k;
+                cw = load16(Abh + rbase + (int64_t)kGroupSlots * gi + 8 * kg);
+                cj = a.sched_j[(goff + gi) * 16 + 4 * kg + q4];
+                crows = a.sched_row[(goff + gi) * 4 + kg];
+            }
             const u32x4 bop = group_weights(cw, crows, (uint32_t)s16);
             const uint32_t b1 = row_addr(cur, cj & 0xffffu, a4);
             const uint32_t b2 = row_addr(cur, cj >> 16, a4);
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(lds, b1, b2, nb), bop, acc[nb]);
-            ++gp;
         }
-        if (more) store_chunk(lds, buf_off[(c + 1) & 1], zr);
+        if (more) {
+            store_groups(min(cptr[c + 2] - cptr[c + 1], kStageGroups));
+            store_chunk(lds, buf_off[(c + 1) & 1], zr);
+        }
     }
 
     if (rok) store_row(a, bh, my_row, kg, acc);
@@ -410,7 +467,7 @@ hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, con
     a.G = g.d_global;
     a.grp_ptr = g.d_grp_ptr;
     a.grp_off = g.d_grp_off;
-    a.grp_chunk = g.d_grp_chunk;
+    a.grp_cptr = g.d_grp_cptr;
     a.sched_row = g.d_sched_row;
     a.sched_j = g.d_sched_j;
     a.A = static_cast<const uint16_t*>(A);
@@ -431,7 +488,8 @@ hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, con
         if (e != hipSuccess) return e;
         attr_device = g.device;
     }
-    const size_t lds = (size_t)2 * kBufBytes + (size_t)((g.num_global + 31) & ~31) * kRowBytes;
+    const size_t lds = (size_t)2 * kBufBytes + (size_t)((g.num_global + 31) & ~31) * kRowBytes +
+                       (size_t)kWaves * kStageBytes;
     hipLaunchKernelGGL(k_diffuse_sched, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), lds, st,
                        a);
     return hipGetLastError();

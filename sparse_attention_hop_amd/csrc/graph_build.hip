@@ -324,7 +324,8 @@ struct SchedArgs {
     const int64_t* grp_off;        // [graphs + 1]
     const int64_t* seg_ptr;        // [graphs][n + 1]
     const int64_t* slot_off;       // [graphs + 1]
-    int32_t* grp_chunk;
+    int32_t nchunks;
+    int32_t* grp_cptr;             // [graphs][nrb][nchunks + 1]
     uint8_t* sched_row;            // [groups][16] pair rows
     uint16_t* sched_j;             // [groups][32] slot key rows
     int32_t* slot_col;
@@ -371,6 +372,8 @@ void k_sched(SchedArgs a) {
     }
     int64_t groups = 0;
     int32_t p = 0;
+    int32_t filled = -1;   // chunk table entries 0..filled are written
+    int32_t* cptr = kFill ? a.grp_cptr + (gr * a.nrb + rb) * (int64_t)(a.nchunks + 1) : nullptr;
     while (true) {
         const int32_t cur = p < cnt ? rr[p] / kChunkRows : INT32_MAX;
         const int32_t c = wave_min(cur);
@@ -420,11 +423,16 @@ void k_sched(SchedArgs a) {
                     a.slot_row[soff + slot] = -1;
                 }
             }
-            for (int32_t q = lane; q < ng; q += kWave) a.grp_chunk[gbase + g0 + q] = c;
+            // Chunks filled + 1 .. c start at this chunk's first group.
+            for (int32_t cc = filled + 1 + lane; cc <= c; cc += kWave) cptr[cc] = (int32_t)g0;
+            filled = c;
         }
         groups += ng;
         p = k;
     }
+    if (kFill)
+        for (int32_t cc = filled + 1 + lane; cc <= a.nchunks; cc += kWave)
+            cptr[cc] = (int32_t)(grp + groups);
     if (!kFill && lane == 0) a.counts[gr * a.nrb + rb] = (int32_t)groups;
 }
 
@@ -467,7 +475,8 @@ static SchedArgs sched_args(const diffuser_graph& g) {
     a.grp_off = g.d_grp_off;
     a.seg_ptr = g.d_seg_ptr;
     a.slot_off = g.d_slot_off;
-    a.grp_chunk = g.d_grp_chunk;
+    a.nchunks = (int32_t)((g.n + kChunkRows - 1) / kChunkRows);
+    a.grp_cptr = g.d_grp_cptr;
     a.sched_row = reinterpret_cast<uint8_t*>(g.d_sched_row);
     a.sched_j = reinterpret_cast<uint16_t*>(g.d_sched_j);
     a.slot_col = g.d_slot_col;

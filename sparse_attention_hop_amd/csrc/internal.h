@@ -74,7 +74,8 @@ struct diffuser_graph {
     std::vector<int64_t> grp_off;   // [num_graphs + 1] prefix sums of groups
     int64_t* d_grp_off = nullptr;   // [num_graphs + 1]
     int64_t* d_grp_ptr = nullptr;   // [num_graphs][nrb + 1] groups of each row block
-    int32_t* d_grp_chunk = nullptr; // [grp_off[num_graphs]] key chunk of each group
+    int32_t* d_grp_cptr = nullptr;  // [num_graphs][nrb][nchunks + 1] first group (in the
+                                    //   graph) of each key chunk of each row block
     uint32_t* d_sched_row = nullptr;// [groups][4]: byte p of word k = row (within the
                                     //   block) of pair 4k + p, 0xFF for a dummy pair
     uint32_t* d_sched_j = nullptr;  // [groups][16]: word 4k + a = key row (within the
