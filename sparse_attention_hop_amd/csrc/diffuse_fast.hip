@@ -15,11 +15,10 @@
 //    key rows lie in the current chunk; the weight operand keeps a pair's
 //    two weights in the lanes of the pair's row and zeroes them elsewhere.
 // A workgroup (16 waves, 16 rows each) streams Z_k of its (batch, head)
-// through LDS in chunks of kChunkRows rows, double-buffered: the next
-// chunk is fetched into registers while the current one is used. Rows of
-// Z_k sit in LDS at 128 bytes; the 32-byte quarter of channel block nb is
-// stored at quarter nb ^ sw(row), which spreads the 16 rows of one
-// transposed read over the banks.
+// through LDS in chunks of kChunkRows rows, double-buffered with direct
+// global-to-LDS loads of the next chunk while the current one is used. Rows
+// of Z_k sit in LDS at 128 bytes, quarters permuted by key_row_code, which
+// spreads the 16 rows of one transposed read over the banks.
 // Global rows get workgroups of their own (32 rows; the 16 waves split each
 // chunk's keys and add their partial sums in a fixed order at the end).
 // Workgroups are numbered so that each XCD (workgroup id mod 8) works
@@ -77,28 +76,23 @@ struct FastArgs {
     int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items;
 };
 
-// Quarter swizzle of a row in LDS (two bits, so the 16 rows 8k + q of one
-// transposed read land in distinct bank groups), as a byte XOR.
-__device__ __forceinline__ uint32_t swz(uint32_t row) {
-    return (((row >> 1) & 1u) | (((row >> 3) & 1u) << 1)) << 5;
+// Byte address, within a buffer, of the 8 bytes lane `a4` reads from key
+// row `code` (a key_row_code) for channel block 0; XOR with nb << 5 selects
+// channel block nb.
+__device__ __forceinline__ uint32_t code_addr(uint32_t code, uint32_t a4) {
+    return code * 32u + 8u * a4;
 }
 
-// Byte address, for channel block 0, of the 8 bytes lane `a4` reads from
-// `row` (quarter swizzle applied; XOR with nb << 5 selects block nb).
-__device__ __forceinline__ uint32_t row_addr(uint32_t buf, uint32_t row, uint32_t a4) {
-    return (buf + row * kRowBytes + 8u * a4) ^ swz(row);
+__device__ __forceinline__ i16x4 tr_read(const char LDS_AS* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)p);
 }
 
-__device__ __forceinline__ i16x4 tr_read(const char LDS_AS* lds, uint32_t addr) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + addr));
-}
-
-// Z^T operand of channel block nb: key rows of b1 (k = 8 kg + 0..3) and of
-// b2 (k = 8 kg + 4..7).
-__device__ __forceinline__ bf16x8 z_operand(const char LDS_AS* lds, uint32_t b1, uint32_t b2,
+// Z^T operand of channel block nb: key rows at b1 (k = 8 kg + 0..3) and b2
+// (k = 8 kg + 4..7) of buffer `buf`.
+__device__ __forceinline__ bf16x8 z_operand(const char LDS_AS* buf, uint32_t b1, uint32_t b2,
                                             int nb) {
-    const i16x4 lo = tr_read(lds, b1 ^ ((uint32_t)nb << 5));
-    const i16x4 hi = tr_read(lds, b2 ^ ((uint32_t)nb << 5));
+    const i16x4 lo = tr_read(buf + (b1 ^ ((uint32_t)nb << 5)));
+    const i16x4 hi = tr_read(buf + (b2 ^ ((uint32_t)nb << 5)));
     const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
     return __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], h[0], h[1]});
 }
@@ -107,36 +101,53 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const u32x4& b, const f32
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// acc[nb] += Z^T(b1, b2) W^T for the four channel blocks.
+__device__ __forceinline__ void mfma4(f32x4 (&acc)[kNB], const char LDS_AS* buf, uint32_t b1,
+                                      uint32_t b2, const u32x4& w) {
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(buf, b1, b2, nb), w, acc[nb]);
+}
+
+// Load of a wave-uniform int32 of read-only graph data through the scalar
+// cache (the constant address space).
+__device__ __forceinline__ int32_t uniform_load(const int32_t* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+        ((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Chunk rows [c0, c0 + kChunkRows) of Z_k, 16 bytes per thread and piece:
-// piece t of thread x is quarter-half (x + kThreads t) % 8 of row
-// (x + kThreads t) / 8. Rows at or beyond n repeat row n - 1 (their
-// weights are zero).
-constexpr int kPieces = kChunkRows * 8 / kThreads;
-
-__device__ __forceinline__ void fetch_chunk(u32x4 (&zr)[kPieces], const uint16_t* Zbh, int64_t n,
-                                            int64_t c0) {
+// Direct loads of chunk rows [c0, c0 + kChunkRows) of Z_k into `buf`: wave w
+// fills 1 KB blocks 4w .. 4w+3 (8 rows each); lane l of a block writes 16
+// bytes at block + 16 l, which is 16-byte unit l % 8 of row l / 8, holding
+// the row's logical unit (l % 8) ^ (2 sw). Rows at or beyond n repeat row
+// n - 1 (their weights are zero).
+__device__ __forceinline__ void dma_chunk(char LDS_AS* buf, const uint16_t* Zbh, int64_t n,
+                                          int64_t c0, int wave, int lane) {
 #pragma unroll
-    for (int t = 0; t < kPieces; ++t) {
-        const int idx = threadIdx.x + kThreads * t;
-        int64_t src = c0 + (idx >> 3);
+    for (int t = 0; t < 4; ++t) {
+        const int blk = 4 * wave + t;
+        const uint32_t pr = (uint32_t)(blk * 8 + (lane >> 3));
+        const uint32_t lu = (uint32_t)(lane & 7) ^ ((key_row_code(pr) & 3u) << 1);
+        int64_t src = c0 + pr;
         src = src < n ? src : n - 1;
-        zr[t] = load16(Zbh + src * kD + (idx & 7) * 8);
+        __builtin_amdgcn_global_load_lds(Zbh + src * kD + lu * 8, (void LDS_AS*)(buf + blk * 1024),
+                                         16, 0, 0);
     }
 }
 
-__device__ __forceinline__ void store_chunk(char LDS_AS* lds, uint32_t buf,
-                                            const u32x4 (&zr)[kPieces]) {
-#pragma unroll
-    for (int t = 0; t < kPieces; ++t) {
-        const uint32_t idx = threadIdx.x + kThreads * t;
-        const uint32_t row = idx >> 3;
-        *reinterpret_cast<u32x4 LDS_AS*>(lds + buf + row * kRowBytes +
-                                        (((idx & 7) * 16) ^ swz(row))) = zr[t];
-    }
+// Waits for this wave's outstanding loads (direct-to-LDS ones included)
+// and LDS traffic, then for the whole workgroup.
+__device__ __forceinline__ void full_barrier() { __syncthreads(); }
+
+// Barrier for LDS traffic only: global loads in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ uint32_t to_bf16_pair(float lo, float hi) {
@@ -171,9 +182,121 @@ __device__ __forceinline__ u32x4 group_weights(const u32x4& w, uint32_t rows, ui
     return b;
 }
 
-// Barrier for LDS traffic only: global loads in flight stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Per-lane state of a row-tile wave.
+struct TileLane {
+    int kg, s16;
+    uint32_t a4, q4;
+    int4 ri;                 // row info of row r0w + s16
+    bool rok;
+    int64_t r0w, band_hi, kc_next;
+    u32x4 band_next;         // weights of band step kc_next
+    const int32_t* cptr;     // chunk -> first group of this row block
+    int64_t goff, rbase;
+    u32x4 pw, pj, pr;        // next chunk's groups, compact
+};
+
+__device__ __forceinline__ u32x4 band_weights(const TileLane& t, const uint16_t* Abh, int64_t kc) {
+    const int32_t off = (int32_t)(kc + 8 * t.kg) - t.ri.y;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (t.rok && kc <= t.band_hi && off >= 0 && off < t.ri.z) w = load16(Abh + t.ri.x + off);
+    return w;
+}
+
+// Compact loads of the first kStageGroups groups of chunk c: lanes 4 k .. 4 k
+// + 3 hold group k's weights and key-row codes, lane k its pair rows.
+__device__ __forceinline__ void fetch_groups(TileLane& t, const FastArgs& a, const uint16_t* Abh,
+                                             int c, int lane) {
+    const int32_t g0 = uniform_load(t.cptr + c);
+    const int32_t cnt = min(uniform_load(t.cptr + c + 1) - g0, kStageGroups);
+    if (lane < 4 * cnt) {
+        t.pw = load16(Abh + t.rbase + (int64_t)kGroupSlots * g0 + 8 * lane);
+        t.pj = *reinterpret_cast<const u32x4*>(a.sched_j + (t.goff + g0) * 16 + 4 * lane);
+    }
+    if (lane < cnt) t.pr = *reinterpret_cast<const u32x4*>(a.sched_row + (t.goff + g0 + lane) * 4);
+}
+
+__device__ __forceinline__ void store_groups(const TileLane& t, char LDS_AS* __restrict__ stg,
+                                             int cnt, int lane) {
+    if (lane < 4 * cnt) {
+        char LDS_AS* o = stg + (lane >> 2) * kGroupBytes + (lane & 3) * 16;
+        *reinterpret_cast<u32x4 LDS_AS*>(o) = t.pw;
+        *reinterpret_cast<u32x4 LDS_AS*>(o + 64) = t.pj;
+    }
+    if (lane < cnt) *reinterpret_cast<u32x4 LDS_AS*>(stg + lane * kGroupBytes + 128) = t.pr;
+}
+
+// One key chunk of a row-tile wave: multiplies the band of chunk c (rows in
+// `cur`), starts the direct loads of chunk c + 1 into `nxt`, then multiplies
+// the random groups of chunk c (staged in `stg`) and stages those of chunk
+// c + 1. The three LDS regions are disjoint, which lets the reads of `cur`
+// and `stg` run while the loads into `nxt` are in flight; every global load
+// the band needs is issued before them.
+__device__ __forceinline__ void tile_chunk(TileLane& t, f32x4 (&acc)[kNB], const FastArgs& a,
+                                           const uint16_t* Abh, const uint16_t* Zbh,
+                                           char LDS_AS* __restrict__ nxt,
+                                           const char LDS_AS* __restrict__ cur,
+                                           char LDS_AS* __restrict__ stg, int c, int wave,
+                                           int lane) {
+    const int64_t c0 = (int64_t)c * kChunkRows;
+    const bool more = c + 1 < a.nchunks;
+    const int32_t g0 = uniform_load(t.cptr + c);
+    const int32_t gcnt = uniform_load(t.cptr + c + 1) - g0;
+    const int32_t ncnt = more ? min(uniform_load(t.cptr + c + 2) - (g0 + gcnt), kStageGroups) : 0;
+    if (more) fetch_groups(t, a, Abh, c + 1, lane);
+
+    // Window band: steps of 32 key columns inside this chunk.
+    const int64_t k_hi = min(t.band_hi, c0 + kChunkRows - 1);
+    const uint32_t bb1 = code_addr(key_row_code(8u * t.kg + t.q4), t.a4);
+    const uint32_t bb2 = code_addr(key_row_code(8u * t.kg + 4u + t.q4), t.a4);
+    while (t.kc_next <= k_hi) {
+        const int64_t kc = t.kc_next;
+        const u32x4 w = t.band_next;
+        t.kc_next += 32;
+        t.band_next = band_weights(t, Abh, t.kc_next);
+        const uint32_t off = (uint32_t)(kc - c0) * kRowBytes;   // multiple of 32 rows
+        mfma4(acc, cur, bb1 + off, bb2 + off, w);
+    }
+
+    if (more) dma_chunk(nxt, Zbh, a.n, c0 + kChunkRows, wave, lane);
+
+    // Random groups (staged ones from LDS, any others from memory).
+    for (int32_t k = 0; k < gcnt; ++k) {
+        uint32_t cj, crows;
+        u32x4 cw;
+        if (k < kStageGroups) {
+            const char LDS_AS* o = stg + k * kGroupBytes;
+            cw = *reinterpret_cast<const u32x4 LDS_AS*>(o + 16 * t.kg);
+            cj = *reinterpret_cast<const uint32_t LDS_AS*>(o + 64 + 4 * (4 * t.kg + t.q4));
+            crows = *reinterpret_cast<const uint32_t LDS_AS*>(o + 128 + 4 * t.kg);
+        } else {
+            const int64_t gi = g0 + k;
+            cw = load16(Abh + t.rbase + (int64_t)kGroupSlots * gi + 8 * t.kg);
+            cj = a.sched_j[(t.goff + gi) * 16 + 4 * t.kg + t.q4];
+            crows = a.sched_row[(t.goff + gi) * 4 + t.kg];
+        }
+        const u32x4 w = group_weights(cw, crows, (uint32_t)t.s16);
+        mfma4(acc, cur, code_addr(cj & 0xffffu, t.a4), code_addr(cj >> 16, t.a4), w);
+    }
+    if (more) store_groups(t, stg, ncnt, lane);
+}
+
+// One key chunk of a global-row wave: starts the direct loads of chunk
+// c + 1 into `nxt` and multiplies keys c0 + 32 w .. + 31 of `cur`.
+__device__ __forceinline__ void grow_chunk(f32x4 (&acc)[2][kNB], const u32x4 (&w)[2],
+                                           const uint16_t* Zbh, int64_t n, int nchunks,
+                                           char LDS_AS* __restrict__ nxt,
+                                           const char LDS_AS* __restrict__ cur, int c, int wave,
+                                           int lane, uint32_t b1, uint32_t b2) {
+    const int64_t c0 = (int64_t)c * kChunkRows;
+    if (c + 1 < nchunks) dma_chunk(nxt, Zbh, n, c0 + kChunkRows, wave, lane);
+    if (c0 + 32 * wave < n) {
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+            const bf16x8 zop = z_operand(cur, b1, b2, nb);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma(zop, w[mb], acc[mb][nb]);
+        }
+    }
 }
 
 __global__ __launch_bounds__(kThreads)
@@ -197,13 +320,12 @@ void k_diffuse_sched(FastArgs a) {
     const uint16_t* Abh = a.A + a_block_offset(a.slot_off, a.num_graphs, a.H, b, h);
     const uint16_t* Zbh = a.Z + (int64_t)bh * n * kD;
     const int4* info = a.row_info + (int64_t)gr * n;
-    const uint32_t buf_off[2] = {0u, (uint32_t)kBufBytes};
+    char LDS_AS* buf[2] = {lds, lds + kBufBytes};
 
     // Zero row kChunkRows of both buffers (the key row of dummy slots).
     if (threadIdx.x < 16) {
-        *reinterpret_cast<u32x4 LDS_AS*>(lds + buf_off[threadIdx.x >> 3] +
-                                        kChunkRows * kRowBytes + (threadIdx.x & 7) * 16) =
-            u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 LDS_AS*>(buf[threadIdx.x >> 3] + kChunkRows * kRowBytes +
+                                        (threadIdx.x & 7) * 16) = u32x4{0u, 0u, 0u, 0u};
     }
 
     if (sub < a.grow_per_bh) {
@@ -223,11 +345,11 @@ void k_diffuse_sched(FastArgs a) {
                 wlen[mb] = sp[i + 1] - sp[i];
             }
         }
-        auto fetch_w = [&](u32x4 (&bop)[2], int64_t kc) {
+        auto fetch_w = [&](u32x4 (&w)[2], int64_t kc) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
-                bop[mb] = u32x4{0u, 0u, 0u, 0u};
-                if (kc + 8 * kg < wlen[mb]) bop[mb] = load16(Abh + wbase[mb] + kc + 8 * kg);
+                w[mb] = u32x4{0u, 0u, 0u, 0u};
+                if (kc + 8 * kg < wlen[mb]) w[mb] = load16(Abh + wbase[mb] + kc + 8 * kg);
             }
         };
         f32x4 acc[2][kNB];
@@ -235,40 +357,22 @@ void k_diffuse_sched(FastArgs a) {
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        u32x4 zr[kPieces];
-        fetch_chunk(zr, Zbh, n, 0);
-        u32x4 bop[2];
-        fetch_w(bop, 32 * wave);
-        store_chunk(lds, buf_off[0], zr);
+        u32x4 w[2], wn[2];
+        fetch_w(w, 32 * wave);
+        dma_chunk(buf[0], Zbh, n, 0, wave, lane);
+        const uint32_t b1 = code_addr(key_row_code(32u * wave + 8u * kg + q4), a4);
+        const uint32_t b2 = code_addr(key_row_code(32u * wave + 8u * kg + 4u + q4), a4);
         for (int c = 0; c < a.nchunks; ++c) {
             const int64_t c0 = (int64_t)c * kChunkRows;
-            const int64_t kc = c0 + 32 * wave;
-            lds_barrier();   // chunk c stored by every wave
-            const bool more = c + 1 < a.nchunks;
-            u32x4 nbop[2];
-            if (more) {
-                fetch_chunk(zr, Zbh, n, c0 + kChunkRows);
-                fetch_w(nbop, kc + kChunkRows);
-            }
-            if (kc < n) {
-                const uint32_t r1 = 32u * wave + 8u * kg + q4;
-                const uint32_t b1 = row_addr(buf_off[c & 1], r1, a4);
-                const uint32_t b2 = row_addr(buf_off[c & 1], r1 + 4, a4);
-#pragma unroll
-                for (int nb = 0; nb < kNB; ++nb) {
-                    const bf16x8 zop = z_operand(lds, b1, b2, nb);
-#pragma unroll
-                    for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma(zop, bop[mb], acc[mb][nb]);
-                }
-            }
-            if (more) {
-                store_chunk(lds, buf_off[(c + 1) & 1], zr);
-                bop[0] = nbop[0];
-                bop[1] = nbop[1];
-            }
+            full_barrier();   // chunk c in LDS
+            if (c + 1 < a.nchunks) fetch_w(wn, c0 + kChunkRows + 32 * wave);
+            grow_chunk(acc, w, Zbh, n, a.nchunks, buf[(c + 1) & 1], buf[c & 1], c, wave, lane, b1,
+                       b2);
+            w[0] = wn[0];
+            w[1] = wn[1];
         }
         // Fixed-order sum of the 16 waves' partial sums.
-        lds_barrier();
+        full_barrier();
         float LDS_AS* part = (float LDS_AS*)lds;   // [wave][mb][nb][e][lane]
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -281,7 +385,7 @@ void k_diffuse_sched(FastArgs a) {
         constexpr int kPer = 2 * kNB * 4 * kWave;   // partial sums per wave
         for (int idx = threadIdx.x; idx < kPer; idx += kThreads) {
             float sum = 0.0f;
-            for (int w = 0; w < kWaves; ++w) sum += part[w * kPer + idx];
+            for (int w2 = 0; w2 < kWaves; ++w2) sum += part[w2 * kPer + idx];
             const int l = idx & 63, e = (idx >> 6) & 3, nb = (idx >> 8) & 3, mb = idx >> 10;
             const int q = q0 + 16 * mb + (l & 15);
             if (q >= a.g) continue;
@@ -296,147 +400,79 @@ void k_diffuse_sched(FastArgs a) {
     }
 
     // ---------------- row tile --------------------------------------------
-    const int64_t r0w = (int64_t)(sub - a.grow_per_bh) * kTileRows + (int64_t)kRowBlock * wave;
-    const bool active = r0w < n;
-    const int64_t my_row = r0w + s16;            // W^T column / output row of this lane
-    int4 ri = make_int4(0, 0, -1, 0);
-    if (my_row < n) ri = info[my_row];
-    const bool rok = my_row < n && ri.z >= 0;    // a non-global row
+    TileLane t;
+    t.kg = kg;
+    t.s16 = s16;
+    t.a4 = a4;
+    t.q4 = q4;
+    t.r0w = (int64_t)(sub - a.grow_per_bh) * kTileRows + (int64_t)kRowBlock * wave;
+    const bool active = t.r0w < n;
+    const int64_t my_row = t.r0w + s16;          // W^T column / output row of this lane
+    t.ri = make_int4(0, 0, -1, 0);
+    if (my_row < n) t.ri = info[my_row];
+    t.rok = my_row < n && t.ri.z >= 0;           // a non-global row
 
-    // Staged global rows (quarter swizzle by position q).
-    const uint32_t zg = 2u * kBufBytes;
+    // Staged global rows (key-row code placement by position q).
+    char LDS_AS* zg = lds + 2 * kBufBytes;
     const int gpad = (a.g + 31) & ~31;
     for (int idx = threadIdx.x; idx < gpad * 8; idx += kThreads) {
         const int q = idx >> 3, lu = idx & 7;
         u32x4 v = {0u, 0u, 0u, 0u};
         if (q < a.g) v = load16(Zbh + (int64_t)a.G[q] * kD + lu * 8);
-        *reinterpret_cast<u32x4 LDS_AS*>(lds + zg + q * kRowBytes +
-                                        ((lu * 16) ^ swz((uint32_t)q))) = v;
+        *reinterpret_cast<u32x4 LDS_AS*>(zg + q * kRowBytes +
+                                        ((lu * 16) ^ ((key_row_code(q) & 3u) << 5))) = v;
     }
-    u32x4 zr[kPieces];
-    fetch_chunk(zr, Zbh, n, 0);
 
-    // Schedule groups of this row block, chunk by chunk. The groups of the
-    // next chunk (up to kStageGroups) are fetched into registers, compactly,
-    // and moved to this wave's LDS staging area once the current chunk's
-    // groups are done with it.
-    const uint32_t stg = zg + (uint32_t)gpad * kRowBytes + (uint32_t)wave * kStageBytes;
-    const int64_t rb = active ? r0w / kRowBlock : 0;
-    const int32_t* cptr = a.grp_cptr + ((int64_t)gr * a.nrb + rb) * (a.nchunks + 1);
-    const int64_t goff = a.grp_off[gr];
-    const int64_t rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];   // random area of the graph
-    u32x4 pw = {0u, 0u, 0u, 0u}, pj = {0u, 0u, 0u, 0u}, pr = {0u, 0u, 0u, 0u};
-    auto fetch_groups = [&](int c) {
-        const int32_t g0 = cptr[c];
-        const int32_t cnt = min(cptr[c + 1] - g0, kStageGroups);
-        if (lane < 4 * cnt) {
-            pw = load16(Abh + rbase + (int64_t)kGroupSlots * g0 + 8 * lane);
-            pj = *reinterpret_cast<const u32x4*>(a.sched_j + (goff + g0) * 16 + 4 * lane);
-        }
-        if (lane < cnt) pr = *reinterpret_cast<const u32x4*>(a.sched_row + (goff + g0 + lane) * 4);
-    };
-    auto store_groups = [&](int cnt) {
-        if (lane < 4 * cnt) {
-            const uint32_t o = stg + (uint32_t)(lane >> 2) * kGroupBytes + (lane & 3) * 16;
-            *reinterpret_cast<u32x4 LDS_AS*>(lds + o) = pw;
-            *reinterpret_cast<u32x4 LDS_AS*>(lds + o + 64) = pj;
-        }
-        if (lane < cnt)
-            *reinterpret_cast<u32x4 LDS_AS*>(lds + stg + (uint32_t)lane * kGroupBytes + 128) = pr;
-    };
+    // Schedule groups of this row block, chunk by chunk; the next chunk's
+    // groups (up to kStageGroups) travel through registers into this wave's
+    // LDS staging area.
+    char LDS_AS* stg = zg + gpad * kRowBytes + wave * kStageBytes;
+    const int64_t rb = active ? t.r0w / kRowBlock : 0;
+    t.cptr = a.grp_cptr + ((int64_t)gr * a.nrb + rb) * (a.nchunks + 1);
+    t.goff = a.grp_off[gr];
+    t.rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];   // random area of the graph
+    t.pw = t.pj = t.pr = u32x4{0u, 0u, 0u, 0u};
     if (active) {
-        fetch_groups(0);
-        store_groups(min(cptr[1] - cptr[0], kStageGroups));
+        fetch_groups(t, a, Abh, 0, lane);
+        store_groups(t, stg, min(uniform_load(t.cptr + 1) - uniform_load(t.cptr), kStageGroups),
+                     lane);
     }
 
     // Band of this wave: key columns [band_lo, band_hi], 32 at a time; the
     // weights of the next step are always in flight.
-    const int64_t wr_last = min(r0w + kRowBlock - 1, n - 1);
-    const int64_t band_lo = (r0w - a.radius < 0 ? 0 : r0w - a.radius) & ~31ll;
-    const int64_t band_hi = a.causal ? wr_last : min(n - 1, wr_last + a.radius);
-    auto band_w = [&](int64_t kc) {
-        const int32_t off = (int32_t)(kc + 8 * kg) - ri.y;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (rok && kc <= band_hi && off >= 0 && off < ri.z) w = load16(Abh + ri.x + off);
-        return w;
-    };
-    int64_t kc_next = band_lo;
-    u32x4 band_next = band_w(band_lo);
+    const int64_t wr_last = min(t.r0w + kRowBlock - 1, n - 1);
+    const int64_t band_lo = (t.r0w - a.radius < 0 ? 0 : t.r0w - a.radius) & ~31ll;
+    t.band_hi = a.causal ? wr_last : min(n - 1, wr_last + a.radius);
+    t.kc_next = band_lo;
+    t.band_next = band_weights(t, Abh, band_lo);
 
+    dma_chunk(buf[0], Zbh, n, 0, wave, lane);
     f32x4 acc[kNB];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    store_chunk(lds, buf_off[0], zr);
-    lds_barrier();   // globals staged, chunk 0 stored
+    full_barrier();   // globals staged, chunk 0 in LDS
 
     // Global columns.
     if (active) {
+        const uint32_t gb1 = code_addr(key_row_code(8u * kg + q4), a4);
+        const uint32_t gb2 = code_addr(key_row_code(8u * kg + 4u + q4), a4);
         for (int q = 0; q < gpad; q += 32) {
-            u32x4 bop = {0u, 0u, 0u, 0u};
-            if (rok && q + 8 * kg < ri.w) bop = load16(Abh + ri.x + ri.z + q + 8 * kg);
-            const uint32_t r1 = (uint32_t)q + 8u * kg + q4;
-            const uint32_t b1 = row_addr(zg, r1, a4), b2 = row_addr(zg, r1 + 4, a4);
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(lds, b1, b2, nb), bop, acc[nb]);
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (t.rok && q + 8 * kg < t.ri.w) w = load16(Abh + t.ri.x + t.ri.z + q + 8 * kg);
+            mfma4(acc, zg, gb1 + q * kRowBytes, gb2 + q * kRowBytes, w);
         }
     }
 
     for (int c = 0; c < a.nchunks; ++c) {
-        const int64_t c0 = (int64_t)c * kChunkRows;
-        const uint32_t cur = buf_off[c & 1];
-        if (c > 0) lds_barrier();   // chunk c stored by every wave
-        const bool more = c + 1 < a.nchunks;
-        if (more) fetch_chunk(zr, Zbh, n, c0 + kChunkRows);
-        if (!active) {
-            if (more) store_chunk(lds, buf_off[(c + 1) & 1], zr);
-            continue;
-        }
-        const int32_t g0 = cptr[c], gcnt = cptr[c + 1] - g0;
-        if (more) fetch_groups(c + 1);
-
-        // Window band.
-        const int64_t k_hi = min(band_hi, c0 + kChunkRows - 1);
-        while (kc_next <= k_hi) {
-            const int64_t kc = kc_next;
-            const u32x4 bop = band_next;
-            kc_next += 32;
-            band_next = band_w(kc_next);
-            const uint32_t r1 = (uint32_t)(kc - c0) + 8u * kg + q4;
-            const uint32_t b1 = row_addr(cur, r1, a4), b2 = row_addr(cur, r1 + 4, a4);
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(lds, b1, b2, nb), bop, acc[nb]);
-        }
-
-        // Random groups of this chunk (staged ones from LDS, any others
-        // straight from memory).
-        for (int32_t k = 0; k < gcnt; ++k) {
-            uint32_t cj, crows;
-            u32x4 cw;
-            if (k < kStageGroups) {
-                const uint32_t o = stg + (uint32_t)k * kGroupBytes;
-                cw = *reinterpret_cast<const u32x4 LDS_AS*>(lds + o + 16 * kg);
-                cj = *reinterpret_cast<const uint32_t LDS_AS*>(lds + o + 64 + 4 * (4 * kg + q4));
-                crows = *reinterpret_cast<const uint32_t LDS_AS*>(lds + o + 128 + 4 * kg);
-            } else {
-                const int64_t gi = g0 + k;
-                cw = load16(Abh + rbase + (int64_t)kGroupSlots * gi + 8 * kg);
-                cj = a.sched_j[(goff + gi) * 16 + 4 * kg + q4];
-                crows = a.sched_row[(goff + gi) * 4 + kg];
-            }
-            const u32x4 bop = group_weights(cw, crows, (uint32_t)s16);
-            const uint32_t b1 = row_addr(cur, cj & 0xffffu, a4);
-            const uint32_t b2 = row_addr(cur, cj >> 16, a4);
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(lds, b1, b2, nb), bop, acc[nb]);
-        }
-        if (more) {
-            store_groups(min(cptr[c + 2] - cptr[c + 1], kStageGroups));
-            store_chunk(lds, buf_off[(c + 1) & 1], zr);
+        if (c > 0) full_barrier();   // chunk c in LDS, chunk c - 1 done by every wave
+        if (active) {
+            tile_chunk(t, acc, a, Abh, Zbh, buf[(c + 1) & 1], buf[c & 1], stg, c, wave, lane);
+        } else if (c + 1 < a.nchunks) {
+            dma_chunk(buf[(c + 1) & 1], Zbh, n, (int64_t)(c + 1) * kChunkRows, wave, lane);
         }
     }
 
-    if (rok) store_row(a, bh, my_row, kg, acc);
+    if (t.rok) store_row(a, bh, my_row, kg, acc);
 }
 
 }  // namespace

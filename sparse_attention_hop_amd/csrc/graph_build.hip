@@ -404,7 +404,8 @@ void k_sched(SchedArgs a) {
                     const int32_t s = 2 * pig + h;
                     const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
                     a.sched_j[gg * kGroupSlots + sched_j_index(s)] =
-                        real ? (uint16_t)(rr[kk] - c * kChunkRows) : (uint16_t)kZeroRow;
+                        (uint16_t)key_row_code(real ? (uint32_t)(rr[kk] - c * kChunkRows)
+                                                    : kZeroRow);
                     a.slot_col[soff + slot] = real ? rr[kk] : -1;
                     a.slot_row[soff + slot] = real ? (int32_t)i : -1;
                     if (real) a.rslot[row * (int64_t)a.rnd_width + kk] = (int32_t)slot;
@@ -418,7 +419,7 @@ void k_sched(SchedArgs a) {
                 for (int h = 0; h < 2; ++h) {
                     const int32_t s = 2 * pig + h;
                     const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
-                    a.sched_j[gg * kGroupSlots + sched_j_index(s)] = (uint16_t)kZeroRow;
+                    a.sched_j[gg * kGroupSlots + sched_j_index(s)] = (uint16_t)key_row_code(kZeroRow);
                     a.slot_col[soff + slot] = -1;
                     a.slot_row[soff + slot] = -1;
                 }

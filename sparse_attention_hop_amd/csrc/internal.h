@@ -15,6 +15,15 @@ constexpr int32_t kChunkRows = 512;   // key rows per chunk of the random schedu
 constexpr int32_t kGroupSlots = 32;   // weight slots per schedule group
 constexpr uint32_t kZeroRow = kChunkRows;  // key row index of a dummy slot
 constexpr int64_t kMaxScheduledN = 1 << 16;
+
+// LDS placement of key row `row` (0..kChunkRows) of a chunk, in 32-byte
+// units: the row's 128 bytes start at unit 4 * row, and the 32-byte quarter
+// of channel block nb sits at quarter nb ^ sw(row), sw taken from row bits 1
+// and 3, so the 16 rows 8k + q (k, q < 4) of one transposed read fall in
+// distinct LDS bank groups. The schedule stores this code for every slot.
+__host__ __device__ constexpr uint32_t key_row_code(uint32_t row) {
+    return (row << 2) | ((row >> 1) & 1u) | (((row >> 3) & 1u) << 1);
+}
 }  // namespace diffuser
 
 struct diffuser_graph {
@@ -78,9 +87,10 @@ struct diffuser_graph {
                                     //   graph) of each key chunk of each row block
     uint32_t* d_sched_row = nullptr;// [groups][4]: byte p of word k = row (within the
                                     //   block) of pair 4k + p, 0xFF for a dummy pair
-    uint32_t* d_sched_j = nullptr;  // [groups][16]: word 4k + a = key row (within the
-                                    //   chunk) of slot 8k + a (low half) and of slot
-                                    //   8k + 4 + a (high half); kZeroRow for a dummy
+    uint32_t* d_sched_j = nullptr;  // [groups][16]: word 4k + a = key_row_code of the
+                                    //   key row (within the chunk) of slot 8k + a (low
+                                    //   half) and of slot 8k + 4 + a (high half);
+                                    //   kZeroRow's code for a dummy
 };
 
 namespace diffuser {
