@@ -24,18 +24,10 @@
 // Workgroups are numbered so that each XCD (workgroup id mod 8) works
 // through a contiguous range of (batch, head) pairs.
 #include "internal.h"
-#include "vec.h"
+#include "mfma_util.h"
 
 namespace diffuser {
 namespace {
-
-#define LDS_AS __attribute__((address_space(3)))
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kWaves = 16;
@@ -98,7 +90,7 @@ __device__ __forceinline__ bf16x8 z_operand(const char LDS_AS* buf, uint32_t b1,
 }
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const u32x4& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    return mfma_bf16(__builtin_bit_cast(u32x4, a), b, c);
 }
 
 // acc[nb] += Z^T(b1, b2) W^T for the four channel blocks.
@@ -106,20 +98,6 @@ __device__ __forceinline__ void mfma4(f32x4 (&acc)[kNB], const char LDS_AS* buf,
                                       uint32_t b2, const u32x4& w) {
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(buf, b1, b2, nb), w, acc[nb]);
-}
-
-// Load of a wave-uniform int32 of read-only graph data through the scalar
-// cache (the constant address space).
-__device__ __forceinline__ int32_t uniform_load(const int32_t* p) {
-    const uint64_t u = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-    return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
-        ((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
-    return *reinterpret_cast<const u32x4*>(p);
 }
 
 // Direct loads of chunk rows [c0, c0 + kChunkRows) of Z_k into `buf`: wave w
@@ -139,19 +117,6 @@ __device__ __forceinline__ void dma_chunk(char LDS_AS* buf, const uint16_t* Zbh,
         __builtin_amdgcn_global_load_lds(Zbh + src * kD + lu * 8, (void LDS_AS*)(buf + blk * 1024),
                                          16, 0, 0);
     }
-}
-
-// Waits for this wave's outstanding loads (direct-to-LDS ones included)
-// and LDS traffic, then for the whole workgroup.
-__device__ __forceinline__ void full_barrier() { __syncthreads(); }
-
-// Barrier for LDS traffic only: global loads in flight stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t to_bf16_pair(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
 // Restart and store of one lane's accumulators: row `i`, channels

@@ -131,6 +131,15 @@ hipError_t launch_scores_softmax(const diffuser_graph& g, const attn_shape& s, c
                                  const void* K, void* A, float* row_scale, float scale_log2,
                                  hipStream_t st);
 
+// The same on scheduled graphs (bf16, d_h = 64), LDS-streamed with MFMA.
+// normalized: A holds the softmax weights; otherwise A holds exp(s - m)
+// unnormalised and row_scale (required) 1 / (sum of each row's stored
+// weights), the form the diffusion step applies.
+bool fast_scores_supported(const diffuser_graph& g, const attn_shape& s);
+hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, const void* Q,
+                              const void* K, void* A, float* row_scale, float scale_log2,
+                              bool normalized, hipStream_t st);
+
 // One step: Zn = (1 - alpha) * c_i * (A Zk)_i + alpha * V_i with c_i =
 // row_scale[(b, h, i)] or 1 when row_scale == nullptr. Generic kernel.
 hipError_t launch_diffuse_step(const diffuser_graph& g, const attn_shape& s, const void* A,

@@ -1,0 +1,61 @@
+// Device helpers shared by the LDS-streamed MFMA kernels (bf16 storage,
+// v_mfma_f32_16x16x32_bf16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "vec.h"
+
+#define LDS_AS __attribute__((address_space(3)))
+
+namespace diffuser {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// D += A B for a 16 x 32 A (lane l: row l % 16, k = 8 (l / 16) .. + 7) and a
+// 32 x 16 B (lane l: column l % 16, the same k); D lane l holds rows
+// 4 (l / 16) .. + 3 of column l % 16.
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Load of a wave-uniform int32 of read-only graph data through the scalar
+// cache (the constant address space).
+__device__ __forceinline__ int32_t uniform_load(const int32_t* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+        ((uint64_t)hi << 32) | lo);
+}
+
+// Waits for this wave's outstanding loads (direct-to-LDS ones included)
+// and LDS traffic, then for the whole workgroup. The explicit vmcnt(0)
+// matters: a workgroup barrier by itself does not wait for loads, and a
+// direct-to-LDS load has only written LDS once it is counted complete.
+__device__ __forceinline__ void full_barrier() {
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0); expcnt not waited
+    __syncthreads();
+}
+
+// Barrier for LDS traffic only: global loads in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t to_bf16_pair(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+}  // namespace diffuser

@@ -1,0 +1,616 @@
+// Edge scores and edge softmax on scheduled graphs, bf16 storage, d_h = 64
+// ("Diffuser" reading notes, section 2.1, eqs. S.1-S.5; "1.2.1 Static
+// sparsity", section 1, eqs. 1-3):
+//   s_ij = q_i . k_j / sqrt(d_h) on the edges of row i,
+//   A_ij = exp(s_ij - m_i) / sum_u exp(s_iu - m_i),  m_i = max_j s_ij.
+//
+// Scores come from v_mfma_f32_16x16x32_bf16 products
+//   D[key][row] = sum_c K[key][c] Q[row][c]   (two products for c < 64)
+// over 16 keys and 16 rows: the K operand is 8 consecutive channels of one
+// key row, read from LDS with ds_read_b128; the Q^T operand 8 channels of
+// one query row, held in registers. Lane l of D holds keys 4 (l / 16) .. + 3
+// of row l % 16, so each lane owns one row and writes 4 consecutive slots.
+//  * window edges: keys are consecutive columns of the band;
+//  * global columns: the g global rows of K, staged once per workgroup;
+//  * random edges: keys are the 16 slots of half a schedule group; a slot's
+//    score is kept by the lanes of its pair's row.
+// A workgroup (16 waves, 16 rows each) streams K of its (batch, head)
+// through LDS in chunks of kChunkRows rows with direct global-to-LDS loads,
+// double-buffered, once per pass:
+//   pass 1: the row maxima;
+//   fused mode: pass 2 writes w_ij = exp(s_ij - m_i) unnormalised and c_i =
+//     1 / (sum of the stored w_ij), which the diffusion step applies;
+//   normalised mode: pass 2 sums w_ij, pass 3 writes w_ij / sum.
+// Global rows (full rows of length n) get workgroups of their own: 32 rows,
+// the 16 waves split each chunk's keys and merge their partial maxima and
+// sums in a fixed order. K rows sit in LDS at 128 bytes; 16-byte unit u of
+// row r is stored at unit u ^ ((r >> 1) & 7), which spreads the 16 rows of
+// one operand read over the banks.
+#include "internal.h"
+#include "mfma_util.h"
+
+namespace diffuser {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 16;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kD = 64;
+constexpr int kRowBytes = kD * 2;
+constexpr int kBufBytes = (kChunkRows + 1) * kRowBytes;   // chunk + zero row
+constexpr int kTileRows = kWaves * kRowBlock;
+constexpr int kGrowRows = 32;
+constexpr int kMaxGlobal = 128;
+constexpr int kSGroupBytes = 80;                          // staged group: codes, pair rows
+constexpr int kStageGroups = 8;
+constexpr int kStageBytes = kStageGroups * kSGroupBytes;
+constexpr int kLdsBytes = 2 * kBufBytes + kMaxGlobal * (kRowBytes + 4) + kWaves * kStageBytes;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(2 * kWaves * kGrowRows * 4 <= 2 * kBufBytes, "grow merge fits");
+
+constexpr uint32_t kZeroCode = key_row_code(kZeroRow);
+
+enum Pass { kPassMax = 0, kPassWriteFused = 1, kPassSum = 2, kPassWriteNorm = 3 };
+
+struct ScoreArgs {
+    int64_t n;
+    int32_t H, num_graphs, radius, g, causal, nchunks, nrb;
+    const int64_t* slot_off;    // [graphs + 1]
+    const int64_t* seg_ptr;     // [graphs][n + 1]
+    const int4* row_info;       // [graphs][n]
+    const int32_t* G;           // [g]
+    const int64_t* grp_off;     // [graphs + 1]
+    const int32_t* grp_cptr;    // [graphs][nrb][nchunks + 1]
+    const uint32_t* sched_row;  // [groups][4]
+    const uint32_t* sched_j;    // [groups][16]
+    const uint16_t* Q;
+    const uint16_t* K;
+    uint16_t* A;
+    float* row_scale;           // [B*H][n] (fused mode)
+    float scale_log2;           // log2(e) / sqrt(d_h)
+    int32_t normalized;
+    int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items;
+};
+
+// Byte offset of 16-byte unit u of key row r inside a buffer.
+__device__ __forceinline__ uint32_t unit_addr(uint32_t r, uint32_t u) {
+    return r * kRowBytes + ((u ^ ((r >> 1) & 7u)) << 4);
+}
+
+// The K operands (channels 8 kg .. + 7 and 32 + 8 kg .. + 7) of key row r.
+__device__ __forceinline__ void k_operands(const char LDS_AS* buf, uint32_t r, uint32_t kg,
+                                           u32x4& k0, u32x4& k1) {
+    const uint32_t o = unit_addr(r, kg);
+    k0 = *reinterpret_cast<const u32x4 LDS_AS*>(buf + o);
+    k1 = *reinterpret_cast<const u32x4 LDS_AS*>(buf + (o ^ 64u));   // unit kg + 4
+}
+
+// D[key][row] of one 16 x 16 tile, scaled to log2 units.
+__device__ __forceinline__ f32x4 score_tile(const u32x4& k0, const u32x4& k1, const u32x4& q0,
+                                            const u32x4& q1, float scale_log2) {
+    f32x4 d = mfma_bf16(k0, q0, f32x4{0.f, 0.f, 0.f, 0.f});
+    d = mfma_bf16(k1, q1, d);
+    return d * scale_log2;
+}
+
+// Direct loads of chunk rows [c0, c0 + kChunkRows) of K into `buf` (wave w
+// fills 1 KB blocks 4w .. 4w+3); rows at or beyond n repeat row n - 1.
+__device__ __forceinline__ void dma_chunk(char LDS_AS* buf, const uint16_t* Kbh, int64_t n,
+                                          int64_t c0, int wave, int lane) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int blk = 4 * wave + t;
+        const uint32_t pr = (uint32_t)(blk * 8 + (lane >> 3));
+        const uint32_t lu = (uint32_t)(lane & 7) ^ ((pr >> 1) & 7u);
+        int64_t src = c0 + pr;
+        src = src < n ? src : n - 1;
+        __builtin_amdgcn_global_load_lds(Kbh + src * kD + lu * 8, (void LDS_AS*)(buf + blk * 1024),
+                                         16, 0, 0);
+    }
+}
+
+// Per-lane state of a row-tile wave (the lane's row is r0w + l % 16).
+struct SLane {
+    int kg, s16;
+    int64_t i;                 // the lane's row
+    int4 ri;                   // {segment start, window block start, window slots, global slots}
+    bool rok;                  // a non-global row below n
+    int64_t lo, whi;           // window columns [lo, whi] (whi = i when causal)
+    u32x4 q0, q1;              // Q^T operands
+    float m, sum, inv;         // row maximum (log2 units), stored sum, 1 / sum
+    int64_t band_lo, band_hi;
+    const int32_t* cptr;
+    int64_t goff, rbase;
+    u32x4 pj;                  // next chunk's key-row codes, compact
+    uint32_t pr;               // next chunk's pair rows, compact
+};
+
+__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Pass-specific treatment of 4 scores of consecutive slots of the lane's
+// row: pass 1 folds them into the maximum, pass 2 (sum) into the sum; the
+// write passes store them at `dst` (when non-null) and, when fused, add the
+// stored values to the sum.
+template <int P>
+__device__ __forceinline__ void consume4(SLane& t, const f32x4& s, const bool (&valid)[4],
+                                         uint16_t* dst) {
+    if (P == kPassMax) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t.m = valid[e] ? fmaxf(t.m, s[e]) : t.m;
+        return;
+    }
+    float w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = valid[e] ? exp2f_fast(s[e] - t.m) : 0.0f;
+    if (P == kPassSum) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t.sum += w[e];
+        return;
+    }
+    if (P == kPassWriteNorm) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] *= t.inv;
+    }
+    const uint32_t lo = to_bf16_pair(w[0], w[1]), hi = to_bf16_pair(w[2], w[3]);
+    if (dst != nullptr) *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
+    if (P == kPassWriteFused && dst != nullptr)
+        t.sum += bf16_to_f32(lo & 0xffffu) + bf16_to_f32(lo >> 16) + bf16_to_f32(hi & 0xffffu) +
+                 bf16_to_f32(hi >> 16);
+}
+
+// One key chunk of a row-tile wave in pass P: band tiles of chunk c, then
+// (with the direct loads of chunk c + 1 into `nxt` in flight) the random
+// groups of chunk c, whose codes are staged in `stg`.
+template <int P>
+__device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const uint16_t* Kbh,
+                                           uint16_t* Abh, char LDS_AS* __restrict__ nxt,
+                                           const char LDS_AS* __restrict__ cur,
+                                           char LDS_AS* __restrict__ stg, int c, int wave,
+                                           int lane) {
+    const int64_t c0 = (int64_t)c * kChunkRows;
+    const bool more = c + 1 < a.nchunks;
+    const int32_t g0 = uniform_load(t.cptr + c);
+    const int32_t gcnt = uniform_load(t.cptr + c + 1) - g0;
+    int32_t ncnt = 0;
+    if (more) {
+        const int32_t n0 = g0 + gcnt;
+        ncnt = min(uniform_load(t.cptr + c + 2) - n0, kStageGroups);
+        if (lane < 4 * ncnt) {
+            t.pj = *reinterpret_cast<const u32x4*>(a.sched_j + (t.goff + n0) * 16 + 4 * lane);
+            t.pr = a.sched_row[(t.goff + n0) * 4 + lane];
+        }
+    }
+
+    // Window band, 16 keys per tile.
+    const int64_t k_lo = max(t.band_lo, c0);
+    const int64_t k_hi = min(t.band_hi, c0 + kChunkRows - 1);
+    for (int64_t kb = k_lo; kb <= k_hi; kb += 16) {
+        u32x4 k0, k1;
+        k_operands(cur, (uint32_t)(kb - c0) + (uint32_t)t.s16, (uint32_t)t.kg, k0, k1);
+        const f32x4 s = score_tile(k0, k1, t.q0, t.q1, a.scale_log2);
+        const int64_t key0 = kb + 4 * t.kg;
+        bool valid[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) valid[e] = t.rok && key0 + e >= t.lo && key0 + e <= t.whi;
+        uint16_t* dst = nullptr;
+        const int64_t off = key0 - t.ri.y;
+        if (P != kPassMax && P != kPassSum && t.rok && off >= 0 && off < t.ri.z)
+            dst = Abh + t.ri.x + off;
+        consume4<P>(t, s, valid, dst);
+    }
+
+    if (more) dma_chunk(nxt, Kbh, a.n, c0 + kChunkRows, wave, lane);
+
+    // Random groups: two tiles of 16 slots each.
+    for (int32_t k = 0; k < gcnt; ++k) {
+        const char LDS_AS* o = stg + (k < kStageGroups ? k : 0) * kSGroupBytes;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // Key row of slot 16 h + l % 16 (this lane's K operand row).
+            const int sl = 16 * h + t.s16;
+            const int ji = 2 * (4 * (sl >> 3) + (sl & 3)) + ((sl >> 2) & 1);
+            uint32_t code_mine, words0, words1, words2, words3, rows2;
+            const int wq = 4 * (2 * h + (t.kg >> 1));   // first code word of this lane's 4 slots
+            if (k < kStageGroups) {
+                code_mine = *reinterpret_cast<const uint16_t LDS_AS*>(o + 2 * ji);
+                const u32x4 wv = *reinterpret_cast<const u32x4 LDS_AS*>(o + 4 * wq);
+                words0 = wv[0]; words1 = wv[1]; words2 = wv[2]; words3 = wv[3];
+                rows2 = *reinterpret_cast<const uint16_t LDS_AS*>(o + 64 + 8 * h + 2 * t.kg);
+            } else {
+                const int64_t gi = t.goff + g0 + k;
+                const uint16_t* codes = reinterpret_cast<const uint16_t*>(a.sched_j + gi * 16);
+                code_mine = codes[ji];
+                words0 = a.sched_j[gi * 16 + wq];
+                words1 = a.sched_j[gi * 16 + wq + 1];
+                words2 = a.sched_j[gi * 16 + wq + 2];
+                words3 = a.sched_j[gi * 16 + wq + 3];
+                rows2 = reinterpret_cast<const uint16_t*>(a.sched_row + gi * 4)[4 * h + t.kg];
+            }
+            u32x4 k0, k1;
+            k_operands(cur, code_mine >> 2, (uint32_t)t.kg, k0, k1);
+            const f32x4 s = score_tile(k0, k1, t.q0, t.q1, a.scale_log2);
+            // This lane's slots 16 h + 4 kg + e: codes from the low (kg even)
+            // or high (kg odd) halves of words wq .. wq + 3.
+            const uint32_t sh = (t.kg & 1) ? 16u : 0u;
+            const uint32_t cd[4] = {(words0 >> sh) & 0xffffu, (words1 >> sh) & 0xffffu,
+                                    (words2 >> sh) & 0xffffu, (words3 >> sh) & 0xffffu};
+            const uint32_t row_a = rows2 & 0xffu, row_b = (rows2 >> 8) & 0xffu;
+            const bool ma = t.rok && row_a == (uint32_t)t.s16;
+            const bool mb = t.rok && row_b == (uint32_t)t.s16;
+            bool valid[4] = {ma && cd[0] != kZeroCode, ma && cd[1] != kZeroCode,
+                             mb && cd[2] != kZeroCode, mb && cd[3] != kZeroCode};
+            if (P == kPassMax || P == kPassSum) {
+                consume4<P>(t, s, valid, nullptr);
+            } else {
+                float w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    w[e] = valid[e] ? exp2f_fast(s[e] - t.m) : 0.0f;
+                    if (P == kPassWriteNorm) w[e] *= t.inv;
+                }
+                const uint32_t pa = to_bf16_pair(w[0], w[1]), pb = to_bf16_pair(w[2], w[3]);
+                uint16_t* gdst = Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 16 * h +
+                                 4 * t.kg;
+                // A pair is written by the lanes of its row; a dummy pair by
+                // the lane of row 0.
+                if (ma || (row_a == 0xffu && t.s16 == 0))
+                    *reinterpret_cast<uint32_t*>(gdst) = pa;
+                if (mb || (row_b == 0xffu && t.s16 == 0))
+                    *reinterpret_cast<uint32_t*>(gdst + 2) = pb;
+                if (P == kPassWriteFused) {
+                    if (ma) t.sum += bf16_to_f32(pa & 0xffffu) + bf16_to_f32(pa >> 16);
+                    if (mb) t.sum += bf16_to_f32(pb & 0xffffu) + bf16_to_f32(pb >> 16);
+                }
+            }
+        }
+    }
+    if (more && lane < 4 * ncnt) {
+        char LDS_AS* d = stg + (lane >> 2) * kSGroupBytes;
+        *reinterpret_cast<u32x4 LDS_AS*>(d + (lane & 3) * 16) = t.pj;
+        *reinterpret_cast<uint32_t LDS_AS*>(d + 64 + (lane & 3) * 4) = t.pr;
+    }
+}
+
+// Global columns of a row-tile wave in pass P (keys = staged global rows).
+template <int P>
+__device__ __forceinline__ void tile_globals(SLane& t, const ScoreArgs& a, uint16_t* Abh,
+                                             const char LDS_AS* zg, const int32_t LDS_AS* gidx,
+                                             int gpad) {
+    for (int qb = 0; qb < gpad; qb += 16) {
+        u32x4 k0, k1;
+        k_operands(zg, (uint32_t)(qb + t.s16), (uint32_t)t.kg, k0, k1);
+        const f32x4 s = score_tile(k0, k1, t.q0, t.q1, a.scale_log2);
+        const int q0 = qb + 4 * t.kg;
+        bool valid[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int q = q0 + e;
+            const int64_t p = q < a.g ? gidx[q] : 0;
+            valid[e] = t.rok && q < a.g && (a.causal ? p < t.lo : (p < t.lo || p > t.whi));
+        }
+        uint16_t* dst = nullptr;
+        if (P != kPassMax && P != kPassSum && t.rok && q0 < t.ri.w)
+            dst = Abh + t.ri.x + t.ri.z + q0;
+        consume4<P>(t, s, valid, dst);
+    }
+}
+
+template <int P>
+__device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uint16_t* Abh,
+                          char LDS_AS* lds, int gpad, bool active, int wave, int lane) {
+    char LDS_AS* buf0 = lds;
+    char LDS_AS* buf1 = lds + kBufBytes;
+    char LDS_AS* zg = lds + 2 * kBufBytes;
+    const int32_t LDS_AS* gidx = (const int32_t LDS_AS*)(zg + gpad * kRowBytes);
+    char LDS_AS* stg = zg + gpad * (kRowBytes + 4) + wave * kStageBytes;
+
+    // Stage chunk 0 and its groups.
+    dma_chunk(buf0, Kbh, a.n, 0, wave, lane);
+    if (active) {
+        const int32_t g0 = uniform_load(t.cptr);
+        const int32_t cnt = min(uniform_load(t.cptr + 1) - g0, kStageGroups);
+        if (lane < 4 * cnt) {
+            char LDS_AS* d = stg + (lane >> 2) * kSGroupBytes;
+            *reinterpret_cast<u32x4 LDS_AS*>(d + (lane & 3) * 16) =
+                *reinterpret_cast<const u32x4*>(a.sched_j + (t.goff + g0) * 16 + 4 * lane);
+            *reinterpret_cast<uint32_t LDS_AS*>(d + 64 + (lane & 3) * 4) =
+                a.sched_row[(t.goff + g0) * 4 + lane];
+        }
+    }
+    full_barrier();
+    if (active) tile_globals<P>(t, a, Abh, zg, gidx, gpad);
+    for (int c = 0; c < a.nchunks; ++c) {
+        if (c > 0) full_barrier();
+        if (active) {
+            tile_chunk<P>(t, a, Kbh, Abh, (c & 1) ? buf0 : buf1, (c & 1) ? buf1 : buf0, stg, c,
+                          wave, lane);
+        } else if (c + 1 < a.nchunks) {
+            dma_chunk((c & 1) ? buf0 : buf1, Kbh, a.n, (int64_t)(c + 1) * kChunkRows, wave, lane);
+        }
+    }
+    full_barrier();   // every wave is done with the buffers
+}
+
+// Max over the 4 lanes of one row (lanes l, l ^ 16, l ^ 32, l ^ 48).
+__device__ __forceinline__ float row_max(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+// Sum over the 4 lanes of one row, in a fixed order.
+__device__ __forceinline__ float row_sum(float x) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+
+// ---------------------------------------------------------------------------
+// Global rows: 32 per workgroup (two 16-row blocks); wave w scores keys
+// c0 + 32 w .. + 31 of every chunk.
+struct GLane {
+    int kg, s16;
+    int64_t i[2];              // the lane's global rows (or -1)
+    int64_t sbase[2], slen[2];
+    u32x4 q0[2], q1[2];
+    float m[2], sum[2], inv[2];
+};
+
+template <int P>
+__device__ __forceinline__ void grow_chunk(GLane& t, const ScoreArgs& a, const uint16_t* Kbh,
+                                           uint16_t* Abh, char LDS_AS* __restrict__ nxt,
+                                           const char LDS_AS* __restrict__ cur, int c, int wave,
+                                           int lane) {
+    const int64_t c0 = (int64_t)c * kChunkRows;
+    if (c + 1 < a.nchunks) dma_chunk(nxt, Kbh, a.n, c0 + kChunkRows, wave, lane);
+    if (c0 + 32 * wave >= a.n) return;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        u32x4 k0, k1;
+        k_operands(cur, (uint32_t)(32 * wave + 16 * h + t.s16), (uint32_t)t.kg, k0, k1);
+        const int64_t key0 = c0 + 32 * wave + 16 * h + 4 * t.kg;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const f32x4 s = score_tile(k0, k1, t.q0[mb], t.q1[mb], a.scale_log2);
+            const int64_t last = a.causal ? t.i[mb] : a.n - 1;
+            bool valid[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) valid[e] = t.i[mb] >= 0 && key0 + e <= last;
+            if (P == kPassMax) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t.m[mb] = valid[e] ? fmaxf(t.m[mb], s[e]) : t.m[mb];
+                continue;
+            }
+            float w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = valid[e] ? exp2f_fast(s[e] - t.m[mb]) : 0.0f;
+            if (P == kPassSum) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t.sum[mb] += w[e];
+                continue;
+            }
+            if (P == kPassWriteNorm) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] *= t.inv[mb];
+            }
+            const uint32_t lo = to_bf16_pair(w[0], w[1]), hi = to_bf16_pair(w[2], w[3]);
+            if (t.i[mb] >= 0 && key0 < t.slen[mb])
+                *reinterpret_cast<u32x2*>(Abh + t.sbase[mb] + key0) = u32x2{lo, hi};
+            if (P == kPassWriteFused)
+                t.sum[mb] += bf16_to_f32(lo & 0xffffu) + bf16_to_f32(lo >> 16) +
+                             bf16_to_f32(hi & 0xffffu) + bf16_to_f32(hi >> 16);
+        }
+    }
+}
+
+template <int P>
+__device__ void grow_pass(GLane& t, const ScoreArgs& a, const uint16_t* Kbh, uint16_t* Abh,
+                          char LDS_AS* lds, int wave, int lane) {
+    char LDS_AS* buf0 = lds;
+    char LDS_AS* buf1 = lds + kBufBytes;
+    dma_chunk(buf0, Kbh, a.n, 0, wave, lane);
+    for (int c = 0; c < a.nchunks; ++c) {
+        full_barrier();
+        grow_chunk<P>(t, a, Kbh, Abh, (c & 1) ? buf0 : buf1, (c & 1) ? buf1 : buf0, c, wave, lane);
+    }
+    full_barrier();
+}
+
+// Merges the waves' per-row values (max or sum, fixed order) through LDS;
+// every lane gets the workgroup value of its rows.
+template <bool kMax>
+__device__ __forceinline__ void grow_merge(float (&v)[2], char LDS_AS* lds, int wave, int lane) {
+    float LDS_AS* part = (float LDS_AS*)lds;   // [wave][32 rows]
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const float x = kMax ? row_max(v[mb]) : row_sum(v[mb]);
+        if (lane < 16) part[wave * kGrowRows + 16 * mb + lane] = x;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int r = 16 * mb + (lane & 15);
+        float x = part[r];
+        for (int w = 1; w < kWaves; ++w) {
+            const float y = part[w * kGrowRows + r];
+            x = kMax ? fmaxf(x, y) : x + y;
+        }
+        v[mb] = x;
+    }
+    lds_barrier();
+}
+
+__global__ __launch_bounds__(kThreads)
+void k_scores_sched(ScoreArgs a) {
+    extern __shared__ __align__(16) char lds_raw[];
+    char LDS_AS* lds = (char LDS_AS*)lds_raw;
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int kg = lane >> 4, s16 = lane & 15;
+
+    const int32_t item = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
+    if (item >= a.total_items) return;
+    const int32_t per_bh = a.grow_per_bh + a.tiles_per_bh;
+    const int32_t bh = item / per_bh;
+    const int32_t sub = item - bh * per_bh;
+    const int32_t b = bh / a.H, h = bh - b * a.H;
+    const int32_t gr = a.num_graphs == 1 ? 0 : b;
+    const int64_t n = a.n;
+    uint16_t* Abh = a.A + a_block_offset(a.slot_off, a.num_graphs, a.H, b, h);
+    const uint16_t* Kbh = a.K + (int64_t)bh * n * kD;
+    const uint16_t* Qbh = a.Q + (int64_t)bh * n * kD;
+    const int4* info = a.row_info + (int64_t)gr * n;
+
+    // Zero row kChunkRows of both buffers (the key row of dummy slots).
+    if (threadIdx.x < 16)
+        *reinterpret_cast<u32x4 LDS_AS*>(lds + (threadIdx.x >> 3) * kBufBytes +
+                                        kChunkRows * kRowBytes + (threadIdx.x & 7) * 16) =
+            u32x4{0u, 0u, 0u, 0u};
+
+    if (sub < a.grow_per_bh) {
+        GLane t;
+        t.kg = kg;
+        t.s16 = s16;
+        const int64_t* sp = a.seg_ptr + (int64_t)gr * (n + 1);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int q = sub * kGrowRows + 16 * mb + s16;
+            t.i[mb] = q < a.g ? a.G[q] : -1;
+            t.sbase[mb] = t.i[mb] >= 0 ? sp[t.i[mb]] : 0;
+            t.slen[mb] = t.i[mb] >= 0 ? sp[t.i[mb] + 1] - sp[t.i[mb]] : 0;
+            const int64_t qi = t.i[mb] >= 0 ? t.i[mb] : 0;
+            t.q0[mb] = load16(Qbh + qi * kD + 8 * kg);
+            t.q1[mb] = load16(Qbh + qi * kD + 32 + 8 * kg);
+            t.m[mb] = -INFINITY;
+            t.sum[mb] = 0.0f;
+            t.inv[mb] = 0.0f;
+        }
+        grow_pass<kPassMax>(t, a, Kbh, Abh, lds, wave, lane);
+        grow_merge<true>(t.m, lds, wave, lane);
+        if (a.normalized) {
+            grow_pass<kPassSum>(t, a, Kbh, Abh, lds, wave, lane);
+            grow_merge<false>(t.sum, lds, wave, lane);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) t.inv[mb] = t.i[mb] >= 0 ? 1.0f / t.sum[mb] : 0.0f;
+            grow_pass<kPassWriteNorm>(t, a, Kbh, Abh, lds, wave, lane);
+        } else {
+            grow_pass<kPassWriteFused>(t, a, Kbh, Abh, lds, wave, lane);
+            grow_merge<false>(t.sum, lds, wave, lane);
+            if (a.row_scale != nullptr && wave == 0 && kg == 0) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+                    if (t.i[mb] >= 0) a.row_scale[(int64_t)bh * n + t.i[mb]] = 1.0f / t.sum[mb];
+            }
+        }
+        return;
+    }
+
+    // ---------------- row tile --------------------------------------------
+    SLane t;
+    t.kg = kg;
+    t.s16 = s16;
+    const int64_t r0w = (int64_t)(sub - a.grow_per_bh) * kTileRows + (int64_t)kRowBlock * wave;
+    const bool active = r0w < n;
+    t.i = r0w + s16;
+    t.ri = make_int4(0, 0, -1, 0);
+    if (t.i < n) t.ri = info[t.i];
+    t.rok = t.i < n && t.ri.z >= 0;
+    t.lo = t.i - a.radius < 0 ? 0 : t.i - a.radius;
+    const int64_t hi = t.i + a.radius > n - 1 ? n - 1 : t.i + a.radius;
+    t.whi = a.causal ? t.i : hi;
+    const int64_t qi = t.i < n ? t.i : n - 1;
+    t.q0 = load16(Qbh + qi * kD + 8 * kg);
+    t.q1 = load16(Qbh + qi * kD + 32 + 8 * kg);
+    t.m = -INFINITY;
+    t.sum = 0.0f;
+    t.inv = 0.0f;
+    const int64_t wr_last = min(r0w + kRowBlock - 1, n - 1);
+    t.band_lo = (r0w - a.radius < 0 ? 0 : r0w - a.radius) & ~15ll;
+    t.band_hi = a.causal ? wr_last : min(n - 1, wr_last + a.radius);
+    const int64_t rb = active ? r0w / kRowBlock : 0;
+    t.cptr = a.grp_cptr + ((int64_t)gr * a.nrb + rb) * (a.nchunks + 1);
+    t.goff = a.grp_off[gr];
+    t.rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];
+    t.pj = u32x4{0u, 0u, 0u, 0u};
+    t.pr = 0u;
+
+    // Staged global rows of K and their positions.
+    const int gpad = (a.g + 31) & ~31;
+    char LDS_AS* zg = lds + 2 * kBufBytes;
+    int32_t LDS_AS* gidx = (int32_t LDS_AS*)(zg + gpad * kRowBytes);
+    for (int idx = threadIdx.x; idx < gpad * 8; idx += kThreads) {
+        const int q = idx >> 3, lu = idx & 7;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (q < a.g) v = load16(Kbh + (int64_t)a.G[q] * kD + lu * 8);
+        *reinterpret_cast<u32x4 LDS_AS*>(zg + unit_addr((uint32_t)q, (uint32_t)lu)) = v;
+    }
+    for (int q = threadIdx.x; q < gpad; q += kThreads) gidx[q] = q < a.g ? a.G[q] : 0;
+
+    tile_pass<kPassMax>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
+    t.m = row_max(t.m);
+    if (a.normalized) {
+        tile_pass<kPassSum>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
+        t.sum = row_sum(t.sum);
+        t.inv = t.rok ? 1.0f / t.sum : 0.0f;   // rows without edges here write zeros only
+        tile_pass<kPassWriteNorm>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
+    } else {
+        tile_pass<kPassWriteFused>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
+        t.sum = row_sum(t.sum);
+        if (a.row_scale != nullptr && t.rok && kg == 0)
+            a.row_scale[(int64_t)bh * n + t.i] = 1.0f / t.sum;
+    }
+}
+
+}  // namespace
+
+bool fast_scores_supported(const diffuser_graph& g, const attn_shape& s) {
+    if (!g.structured || !g.scheduled || s.dtype != DIFFUSER_BF16 || s.d != kD) return false;
+    if (g.num_global > kMaxGlobal) return false;
+    for (int64_t x : g.slots)
+        if (x >= (1ll << 31)) return false;
+    return true;
+}
+
+hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, const void* Q,
+                              const void* K, void* A, float* row_scale, float scale_log2,
+                              bool normalized, hipStream_t st) {
+    ScoreArgs a;
+    a.n = g.n;
+    a.H = s.H;
+    a.num_graphs = g.num_graphs;
+    a.radius = g.radius;
+    a.g = g.num_global;
+    a.causal = g.causal;
+    a.nchunks = (int32_t)((g.n + kChunkRows - 1) / kChunkRows);
+    a.nrb = (int32_t)((g.n + kRowBlock - 1) / kRowBlock);
+    a.slot_off = g.d_slot_off;
+    a.seg_ptr = g.d_seg_ptr;
+    a.row_info = reinterpret_cast<const int4*>(g.d_row_info);
+    a.G = g.d_global;
+    a.grp_off = g.d_grp_off;
+    a.grp_cptr = g.d_grp_cptr;
+    a.sched_row = g.d_sched_row;
+    a.sched_j = g.d_sched_j;
+    a.Q = static_cast<const uint16_t*>(Q);
+    a.K = static_cast<const uint16_t*>(K);
+    a.A = static_cast<uint16_t*>(A);
+    a.row_scale = row_scale;
+    a.scale_log2 = scale_log2;
+    a.normalized = normalized ? 1 : 0;
+    const int32_t BH = s.B * s.H;
+    a.tiles_per_bh = (int32_t)((g.n + kTileRows - 1) / kTileRows);
+    a.grow_per_bh = (g.num_global + kGrowRows - 1) / kGrowRows;
+    a.total_items = BH * (a.tiles_per_bh + a.grow_per_bh);
+    a.per_xcd = (a.total_items + 7) / 8;
+    static int attr_device = -1;   // dynamic LDS above 64 KB is enabled per device
+    if (attr_device != g.device) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_scores_sched),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e != hipSuccess) return e;
+        attr_device = g.device;
+    }
+    const int gpad = (g.num_global + 31) & ~31;
+    const size_t lds = (size_t)2 * kBufBytes + (size_t)gpad * (kRowBytes + 4) +
+                       (size_t)kWaves * kStageBytes;
+    hipLaunchKernelGGL(k_scores_sched, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), lds, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace diffuser
