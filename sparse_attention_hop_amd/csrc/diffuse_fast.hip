@@ -139,11 +139,12 @@ __device__ __forceinline__ void store_row(const FastArgs& a, int32_t bh, int64_t
 }
 
 // Weight operand of a schedule group for the lanes of row `row` (0..15):
-// pair p of words w keeps its two weights where the pair's row matches.
+// pair p of words w keeps its two weights where the pair's row (low 7 bits
+// of its byte) matches.
 __device__ __forceinline__ u32x4 group_weights(const u32x4& w, uint32_t rows, uint32_t row) {
     u32x4 b;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) b[p] = ((rows >> (8 * p)) & 0xffu) == row ? w[p] : 0u;
+    for (int p = 0; p < 4; ++p) b[p] = ((rows >> (8 * p)) & 0x7fu) == row ? w[p] : 0u;
     return b;
 }
 

@@ -397,7 +397,8 @@ void k_sched(SchedArgs a) {
                 const int32_t pidx = pre + t;
                 const int64_t gg = gbase + g0 + pidx / 16;
                 const int32_t pig = pidx % 16;
-                a.sched_row[gg * 16 + pig] = (uint8_t)lane;
+                const bool lone = p + 2 * t + 1 >= k;   // second slot is a dummy
+                a.sched_row[gg * 16 + pig] = (uint8_t)(lane | (lone ? 0x80 : 0));
                 for (int h = 0; h < 2; ++h) {
                     const int32_t kk = p + 2 * t + h;
                     const bool real = kk < k;

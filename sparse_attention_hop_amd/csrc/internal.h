@@ -86,7 +86,9 @@ struct diffuser_graph {
     int32_t* d_grp_cptr = nullptr;  // [num_graphs][nrb][nchunks + 1] first group (in the
                                     //   graph) of each key chunk of each row block
     uint32_t* d_sched_row = nullptr;// [groups][4]: byte p of word k = row (within the
-                                    //   block) of pair 4k + p, 0xFF for a dummy pair
+                                    //   block) of pair 4k + p, plus 0x80 when the
+                                    //   pair's second slot is a dummy; 0xFF for a
+                                    //   dummy pair
     uint32_t* d_sched_j = nullptr;  // [groups][16]: word 4k + a = key_row_code of the
                                     //   key row (within the chunk) of slot 8k + a (low
                                     //   half) and of slot 8k + 4 + a (high half);

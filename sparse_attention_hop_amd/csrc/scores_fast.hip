@@ -48,8 +48,6 @@ constexpr int kLdsBytes = 2 * kBufBytes + kMaxGlobal * (kRowBytes + 4) + kWaves 
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(2 * kWaves * kGrowRows * 4 <= 2 * kBufBytes, "grow merge fits");
 
-constexpr uint32_t kZeroCode = key_row_code(kZeroRow);
-
 enum Pass { kPassMax = 0, kPassWriteFused = 1, kPassSum = 2, kPassWriteNorm = 3 };
 
 struct ScoreArgs {
@@ -154,8 +152,7 @@ __device__ __forceinline__ void consume4(SLane& t, const f32x4& s, const bool (&
     const uint32_t lo = to_bf16_pair(w[0], w[1]), hi = to_bf16_pair(w[2], w[3]);
     if (dst != nullptr) *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
     if (P == kPassWriteFused && dst != nullptr)
-        t.sum += bf16_to_f32(lo & 0xffffu) + bf16_to_f32(lo >> 16) + bf16_to_f32(hi & 0xffffu) +
-                 bf16_to_f32(hi >> 16);
+        t.sum += bf16_lo(lo) + bf16_hi(lo) + bf16_lo(hi) + bf16_hi(hi);
 }
 
 // One key chunk of a row-tile wave in pass P: band tiles of chunk c, then
@@ -201,7 +198,8 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
 
     if (more) dma_chunk(nxt, Kbh, a.n, c0 + kChunkRows, wave, lane);
 
-    // Random groups: two tiles of 16 slots each.
+    // Random groups: two tiles of 16 slots each. A pair's byte is its row
+    // (+ 0x80 when its second slot is a dummy, 0xFF for a dummy pair).
     for (int32_t k = 0; k < gcnt; ++k) {
         const char LDS_AS* o = stg + (k < kStageGroups ? k : 0) * kSGroupBytes;
 #pragma unroll
@@ -209,36 +207,24 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
             // Key row of slot 16 h + l % 16 (this lane's K operand row).
             const int sl = 16 * h + t.s16;
             const int ji = 2 * (4 * (sl >> 3) + (sl & 3)) + ((sl >> 2) & 1);
-            uint32_t code_mine, words0, words1, words2, words3, rows2;
-            const int wq = 4 * (2 * h + (t.kg >> 1));   // first code word of this lane's 4 slots
+            uint32_t code_mine, rows2;
             if (k < kStageGroups) {
                 code_mine = *reinterpret_cast<const uint16_t LDS_AS*>(o + 2 * ji);
-                const u32x4 wv = *reinterpret_cast<const u32x4 LDS_AS*>(o + 4 * wq);
-                words0 = wv[0]; words1 = wv[1]; words2 = wv[2]; words3 = wv[3];
                 rows2 = *reinterpret_cast<const uint16_t LDS_AS*>(o + 64 + 8 * h + 2 * t.kg);
             } else {
                 const int64_t gi = t.goff + g0 + k;
-                const uint16_t* codes = reinterpret_cast<const uint16_t*>(a.sched_j + gi * 16);
-                code_mine = codes[ji];
-                words0 = a.sched_j[gi * 16 + wq];
-                words1 = a.sched_j[gi * 16 + wq + 1];
-                words2 = a.sched_j[gi * 16 + wq + 2];
-                words3 = a.sched_j[gi * 16 + wq + 3];
+                code_mine = reinterpret_cast<const uint16_t*>(a.sched_j + gi * 16)[ji];
                 rows2 = reinterpret_cast<const uint16_t*>(a.sched_row + gi * 4)[4 * h + t.kg];
             }
             u32x4 k0, k1;
             k_operands(cur, code_mine >> 2, (uint32_t)t.kg, k0, k1);
             const f32x4 s = score_tile(k0, k1, t.q0, t.q1, a.scale_log2);
-            // This lane's slots 16 h + 4 kg + e: codes from the low (kg even)
-            // or high (kg odd) halves of words wq .. wq + 3.
-            const uint32_t sh = (t.kg & 1) ? 16u : 0u;
-            const uint32_t cd[4] = {(words0 >> sh) & 0xffffu, (words1 >> sh) & 0xffffu,
-                                    (words2 >> sh) & 0xffffu, (words3 >> sh) & 0xffffu};
+            // This lane's slots 16 h + 4 kg + e are pairs 8 h + 2 kg + e / 2.
             const uint32_t row_a = rows2 & 0xffu, row_b = (rows2 >> 8) & 0xffu;
-            const bool ma = t.rok && row_a == (uint32_t)t.s16;
-            const bool mb = t.rok && row_b == (uint32_t)t.s16;
-            bool valid[4] = {ma && cd[0] != kZeroCode, ma && cd[1] != kZeroCode,
-                             mb && cd[2] != kZeroCode, mb && cd[3] != kZeroCode};
+            const uint32_t me = (uint32_t)t.s16;
+            const bool ma = t.rok && (row_a & 0x7fu) == me;
+            const bool mb = t.rok && (row_b & 0x7fu) == me;
+            bool valid[4] = {ma, ma && row_a == me, mb, mb && row_b == me};
             if (P == kPassMax || P == kPassSum) {
                 consume4<P>(t, s, valid, nullptr);
             } else {
@@ -258,8 +244,8 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
                 if (mb || (row_b == 0xffu && t.s16 == 0))
                     *reinterpret_cast<uint32_t*>(gdst + 2) = pb;
                 if (P == kPassWriteFused) {
-                    if (ma) t.sum += bf16_to_f32(pa & 0xffffu) + bf16_to_f32(pa >> 16);
-                    if (mb) t.sum += bf16_to_f32(pb & 0xffffu) + bf16_to_f32(pb >> 16);
+                    if (ma) t.sum += bf16_lo(pa) + bf16_hi(pa);
+                    if (mb) t.sum += bf16_lo(pb) + bf16_hi(pb);
                 }
             }
         }
@@ -394,8 +380,7 @@ __device__ __forceinline__ void grow_chunk(GLane& t, const ScoreArgs& a, const u
             if (t.i[mb] >= 0 && key0 < t.slen[mb])
                 *reinterpret_cast<u32x2*>(Abh + t.sbase[mb] + key0) = u32x2{lo, hi};
             if (P == kPassWriteFused)
-                t.sum[mb] += bf16_to_f32(lo & 0xffffu) + bf16_to_f32(lo >> 16) +
-                             bf16_to_f32(hi & 0xffffu) + bf16_to_f32(hi >> 16);
+                t.sum[mb] += bf16_lo(lo) + bf16_hi(lo) + bf16_lo(hi) + bf16_hi(hi);
         }
     }
 }
