@@ -65,6 +65,7 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_grp_cptr);
     hipFree(g->d_sched_row);
     hipFree(g->d_sched_j);
+    hipFree(g->d_sched_k);
     g->d_row_ptr = nullptr;
     g->d_col_idx = nullptr;
     g->d_col_off = nullptr;
@@ -82,6 +83,7 @@ void free_graph_memory(diffuser_graph* g) {
     g->d_grp_cptr = nullptr;
     g->d_sched_row = nullptr;
     g->d_sched_j = nullptr;
+    g->d_sched_k = nullptr;
 }
 
 diffuser_status alloc_status(hipError_t e, const char* what) {
@@ -362,7 +364,8 @@ diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stre
                                                           ((n + kChunkRows - 1) / kChunkRows + 1)
                                                     : 1)) != hipSuccess ||
         (e = dev_alloc(&g->d_sched_row, (size_t)ngroups * 4)) != hipSuccess ||
-        (e = dev_alloc(&g->d_sched_j, (size_t)ngroups * 16)) != hipSuccess)
+        (e = dev_alloc(&g->d_sched_j, (size_t)ngroups * 16)) != hipSuccess ||
+        (e = dev_alloc(&g->d_sched_k, (size_t)ngroups * kGroupSlots)) != hipSuccess)
         return alloc_status(e, "device allocation of the columns");
     if ((e = hipMemcpyAsync(g->d_col_off, g->col_off.data(), sizeof(int64_t) * (g->num_graphs + 1),
                             hipMemcpyHostToDevice, st)) != hipSuccess ||

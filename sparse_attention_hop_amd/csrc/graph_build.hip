@@ -327,7 +327,8 @@ struct SchedArgs {
     int32_t nchunks;
     int32_t* grp_cptr;             // [graphs][nrb][nchunks + 1]
     uint8_t* sched_row;            // [groups][16] pair rows
-    uint16_t* sched_j;             // [groups][32] slot key rows
+    uint16_t* sched_j;             // [groups][32] slot key rows (diffusion layout)
+    uint16_t* sched_k;             // [groups][32] slot key rows (score layout)
     int32_t* slot_col;
     int32_t* slot_row;
     int32_t* rslot;
@@ -404,9 +405,9 @@ void k_sched(SchedArgs a) {
                     const bool real = kk < k;
                     const int32_t s = 2 * pig + h;
                     const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
-                    a.sched_j[gg * kGroupSlots + sched_j_index(s)] =
-                        (uint16_t)key_row_code(real ? (uint32_t)(rr[kk] - c * kChunkRows)
-                                                    : kZeroRow);
+                    const uint32_t jr = real ? (uint32_t)(rr[kk] - c * kChunkRows) : kZeroRow;
+                    a.sched_j[gg * kGroupSlots + sched_j_index(s)] = (uint16_t)key_row_code(jr);
+                    a.sched_k[gg * kGroupSlots + s] = (uint16_t)score_row_code(jr);
                     a.slot_col[soff + slot] = real ? rr[kk] : -1;
                     a.slot_row[soff + slot] = real ? (int32_t)i : -1;
                     if (real) a.rslot[row * (int64_t)a.rnd_width + kk] = (int32_t)slot;
@@ -421,6 +422,7 @@ void k_sched(SchedArgs a) {
                     const int32_t s = 2 * pig + h;
                     const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
                     a.sched_j[gg * kGroupSlots + sched_j_index(s)] = (uint16_t)key_row_code(kZeroRow);
+                    a.sched_k[gg * kGroupSlots + s] = (uint16_t)score_row_code(kZeroRow);
                     a.slot_col[soff + slot] = -1;
                     a.slot_row[soff + slot] = -1;
                 }
@@ -481,6 +483,7 @@ static SchedArgs sched_args(const diffuser_graph& g) {
     a.grp_cptr = g.d_grp_cptr;
     a.sched_row = reinterpret_cast<uint8_t*>(g.d_sched_row);
     a.sched_j = reinterpret_cast<uint16_t*>(g.d_sched_j);
+    a.sched_k = g.d_sched_k;
     a.slot_col = g.d_slot_col;
     a.slot_row = g.d_slot_row;
     a.rslot = g.d_rslot;

@@ -16,6 +16,14 @@ constexpr int32_t kGroupSlots = 32;   // weight slots per schedule group
 constexpr uint32_t kZeroRow = kChunkRows;  // key row index of a dummy slot
 constexpr int64_t kMaxScheduledN = 1 << 16;
 
+// LDS placement of key row `row` (0..kChunkRows) in the score kernel's
+// layout, in 16-byte units: unit u of the row sits at unit (code ^ u) with
+// code = 8 row + ((row >> 1) & 7), so the 16 rows of one 16-byte-per-lane
+// operand read fall in distinct LDS bank groups.
+__host__ __device__ constexpr uint32_t score_row_code(uint32_t row) {
+    return (row << 3) | ((row >> 1) & 7u);
+}
+
 // LDS placement of key row `row` (0..kChunkRows) of a chunk, in 32-byte
 // units: the row's 128 bytes start at unit 4 * row, and the 32-byte quarter
 // of channel block nb sits at quarter nb ^ sw(row), sw taken from row bits 1
@@ -93,6 +101,8 @@ struct diffuser_graph {
                                     //   key row (within the chunk) of slot 8k + a (low
                                     //   half) and of slot 8k + 4 + a (high half);
                                     //   kZeroRow's code for a dummy
+    uint16_t* d_sched_k = nullptr;  // [groups][32]: score_row_code of the key row of
+                                    //   each slot, in slot order
 };
 
 namespace diffuser {

@@ -10,22 +10,24 @@
 // key row, read from LDS with ds_read_b128; the Q^T operand 8 channels of
 // one query row, held in registers. Lane l of D holds keys 4 (l / 16) .. + 3
 // of row l % 16, so each lane owns one row and writes 4 consecutive slots.
-//  * window edges: keys are consecutive columns of the band;
+//  * window edges: keys are consecutive columns of the band (tiles that lie
+//    inside every row's window skip the masking);
 //  * global columns: the g global rows of K, staged once per workgroup;
 //  * random edges: keys are the 16 slots of half a schedule group; a slot's
-//    score is kept by the lanes of its pair's row.
+//    score is kept by the lane of its pair's row.
 // A workgroup (16 waves, 16 rows each) streams K of its (batch, head)
 // through LDS in chunks of kChunkRows rows with direct global-to-LDS loads,
 // double-buffered, once per pass:
-//   pass 1: the row maxima;
+//   pass 1: the row maxima (of the unscaled dot products);
 //   fused mode: pass 2 writes w_ij = exp(s_ij - m_i) unnormalised and c_i =
 //     1 / (sum of the stored w_ij), which the diffusion step applies;
 //   normalised mode: pass 2 sums w_ij, pass 3 writes w_ij / sum.
-// Global rows (full rows of length n) get workgroups of their own: 32 rows,
-// the 16 waves split each chunk's keys and merge their partial maxima and
-// sums in a fixed order. K rows sit in LDS at 128 bytes; 16-byte unit u of
-// row r is stored at unit u ^ ((r >> 1) & 7), which spreads the 16 rows of
-// one operand read over the banks.
+// exp(s - m) is evaluated as exp2(x * log2(e) / sqrt(d_h) - m'), x the dot
+// product and m' the scaled maximum. Global rows (full rows of length n)
+// get workgroups of their own: 32 rows, the 16 waves split each chunk's
+// keys and merge their partial maxima and sums in a fixed order. K rows sit
+// in LDS at 128 bytes, 16-byte units permuted by score_row_code, which
+// spreads the 16 rows of one operand read over the banks.
 #include "internal.h"
 #include "mfma_util.h"
 
@@ -51,8 +53,7 @@ static_assert(2 * kWaves * kGrowRows * 4 <= 2 * kBufBytes, "grow merge fits");
 enum Pass { kPassMax = 0, kPassWriteFused = 1, kPassSum = 2, kPassWriteNorm = 3 };
 
 struct ScoreArgs {
-    int64_t n;
-    int32_t H, num_graphs, radius, g, causal, nchunks, nrb;
+    int32_t n, H, num_graphs, radius, g, causal, nchunks, nrb;
     const int64_t* slot_off;    // [graphs + 1]
     const int64_t* seg_ptr;     // [graphs][n + 1]
     const int4* row_info;       // [graphs][n]
@@ -60,7 +61,7 @@ struct ScoreArgs {
     const int64_t* grp_off;     // [graphs + 1]
     const int32_t* grp_cptr;    // [graphs][nrb][nchunks + 1]
     const uint32_t* sched_row;  // [groups][4]
-    const uint32_t* sched_j;    // [groups][16]
+    const uint16_t* sched_k;    // [groups][32]
     const uint16_t* Q;
     const uint16_t* K;
     uint16_t* A;
@@ -70,79 +71,86 @@ struct ScoreArgs {
     int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items;
 };
 
-// Byte offset of 16-byte unit u of key row r inside a buffer.
-__device__ __forceinline__ uint32_t unit_addr(uint32_t r, uint32_t u) {
-    return r * kRowBytes + ((u ^ ((r >> 1) & 7u)) << 4);
-}
-
-// The K operands (channels 8 kg .. + 7 and 32 + 8 kg .. + 7) of key row r.
-__device__ __forceinline__ void k_operands(const char LDS_AS* buf, uint32_t r, uint32_t kg,
+// The K operands (channels 8 kg .. + 7 and 32 + 8 kg .. + 7) of the key row
+// with score_row_code `code`.
+__device__ __forceinline__ void k_operands(const char LDS_AS* buf, uint32_t code, uint32_t kg,
                                            u32x4& k0, u32x4& k1) {
-    const uint32_t o = unit_addr(r, kg);
+    const uint32_t o = (code ^ kg) << 4;
     k0 = *reinterpret_cast<const u32x4 LDS_AS*>(buf + o);
     k1 = *reinterpret_cast<const u32x4 LDS_AS*>(buf + (o ^ 64u));   // unit kg + 4
 }
 
-// D[key][row] of one 16 x 16 tile, scaled to log2 units.
-__device__ __forceinline__ f32x4 score_tile(const u32x4& k0, const u32x4& k1, const u32x4& q0,
-                                            const u32x4& q1, float scale_log2) {
-    f32x4 d = mfma_bf16(k0, q0, f32x4{0.f, 0.f, 0.f, 0.f});
-    d = mfma_bf16(k1, q1, d);
-    return d * scale_log2;
+// Unscaled dot products D[key][row] of one 16 x 16 tile.
+__device__ __forceinline__ f32x4 dots(const u32x4& k0, const u32x4& k1, const u32x4& q0,
+                                      const u32x4& q1) {
+    return mfma_bf16(k1, q1, mfma_bf16(k0, q0, f32x4{0.f, 0.f, 0.f, 0.f}));
 }
 
 // Direct loads of chunk rows [c0, c0 + kChunkRows) of K into `buf` (wave w
 // fills 1 KB blocks 4w .. 4w+3); rows at or beyond n repeat row n - 1.
-__device__ __forceinline__ void dma_chunk(char LDS_AS* buf, const uint16_t* Kbh, int64_t n,
-                                          int64_t c0, int wave, int lane) {
+__device__ __forceinline__ void dma_chunk(char LDS_AS* buf, const uint16_t* Kbh, int32_t n,
+                                          int32_t c0, int wave, int lane) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int blk = 4 * wave + t;
         const uint32_t pr = (uint32_t)(blk * 8 + (lane >> 3));
-        const uint32_t lu = (uint32_t)(lane & 7) ^ ((pr >> 1) & 7u);
-        int64_t src = c0 + pr;
-        src = src < n ? src : n - 1;
-        __builtin_amdgcn_global_load_lds(Kbh + src * kD + lu * 8, (void LDS_AS*)(buf + blk * 1024),
-                                         16, 0, 0);
+        const uint32_t lu = (uint32_t)(lane & 7) ^ (score_row_code(pr) & 7u);
+        const int32_t src = min(c0 + (int32_t)pr, n - 1);
+        __builtin_amdgcn_global_load_lds(Kbh + (int64_t)src * kD + lu * 8,
+                                         (void LDS_AS*)(buf + blk * 1024), 16, 0, 0);
     }
+}
+
+__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum of the two bf16 halves of `w` added to acc (one v_dot2_f32_bf16).
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
 }
 
 // Per-lane state of a row-tile wave (the lane's row is r0w + l % 16).
 struct SLane {
-    int kg, s16;
-    int64_t i;                 // the lane's row
+    int32_t kg, s16, i, r0w;
     int4 ri;                   // {segment start, window block start, window slots, global slots}
     bool rok;                  // a non-global row below n
-    int64_t lo, whi;           // window columns [lo, whi] (whi = i when causal)
+    bool block_ok;             // every row of the wave's block is such a row
+    int32_t lo;                // window columns [lo, lo + span]
+    uint32_t span;
     u32x4 q0, q1;              // Q^T operands
-    float m, sum, inv;         // row maximum (log2 units), stored sum, 1 / sum
-    int64_t band_lo, band_hi;
+    float m;                   // row maximum of the dot products
+    float ms;                  // m * scale_log2
+    float sum, inv;            // sum of the weights, its inverse (normalised mode)
+    int32_t band_lo, band_hi;
     const int32_t* cptr;
     int64_t goff, rbase;
-    u32x4 pj;                  // next chunk's key-row codes, compact
+    u32x4 pk;                  // next chunk's score codes, compact
     uint32_t pr;               // next chunk's pair rows, compact
 };
 
-__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Pass-specific treatment of 4 scores of consecutive slots of the lane's
-// row: pass 1 folds them into the maximum, pass 2 (sum) into the sum; the
-// write passes store them at `dst` (when non-null) and, when fused, add the
-// stored values to the sum.
-template <int P>
-__device__ __forceinline__ void consume4(SLane& t, const f32x4& s, const bool (&valid)[4],
-                                         uint16_t* dst) {
+// Pass-specific treatment of 4 dot products of consecutive slots of the
+// lane's row. kMask: valid[] applies (otherwise all four are edges).
+template <int P, bool kMask>
+__device__ __forceinline__ void consume4(SLane& t, const f32x4& x, const bool (&valid)[4],
+                                         float scale_log2, uint16_t* dst) {
     if (P == kPassMax) {
+        if (kMask) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t.m = valid[e] ? fmaxf(t.m, s[e]) : t.m;
+            for (int e = 0; e < 4; ++e) t.m = valid[e] ? fmaxf(t.m, x[e]) : t.m;
+        } else {
+            t.m = fmaxf(fmaxf(t.m, x[0]), fmaxf(x[1], fmaxf(x[2], x[3])));
+        }
         return;
     }
     float w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = valid[e] ? exp2f_fast(s[e] - t.m) : 0.0f;
+    for (int e = 0; e < 4; ++e) {
+        w[e] = exp2f_fast(__builtin_fmaf(x[e], scale_log2, -t.ms));
+        if (kMask) w[e] = valid[e] ? w[e] : 0.0f;
+    }
     if (P == kPassSum) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t.sum += w[e];
+        t.sum += (w[0] + w[1]) + (w[2] + w[3]);
         return;
     }
     if (P == kPassWriteNorm) {
@@ -150,9 +158,76 @@ __device__ __forceinline__ void consume4(SLane& t, const f32x4& s, const bool (&
         for (int e = 0; e < 4; ++e) w[e] *= t.inv;
     }
     const uint32_t lo = to_bf16_pair(w[0], w[1]), hi = to_bf16_pair(w[2], w[3]);
-    if (dst != nullptr) *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
-    if (P == kPassWriteFused && dst != nullptr)
-        t.sum += bf16_lo(lo) + bf16_hi(lo) + bf16_lo(hi) + bf16_hi(hi);
+    if (dst != nullptr) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
+        if (P == kPassWriteFused) t.sum = add_pair(hi, add_pair(lo, t.sum));
+    }
+}
+
+// One band tile: keys kb .. kb + 15 (rows of `cur` from kb - c0).
+template <int P>
+__device__ __forceinline__ void band_tile(SLane& t, const ScoreArgs& a, uint16_t* Abh,
+                                          const char LDS_AS* cur, int32_t kb, int32_t c0) {
+    u32x4 k0, k1;
+    k_operands(cur, score_row_code((uint32_t)(kb - c0 + t.s16)), (uint32_t)t.kg, k0, k1);
+    const f32x4 x = dots(k0, k1, t.q0, t.q1);
+    const int32_t key0 = kb + 4 * t.kg;
+    // The whole tile lies in every row's window (a wave-uniform test).
+    const bool interior = t.block_ok && kb >= t.r0w + 15 - a.radius &&
+                          kb + 15 <= (a.causal ? t.r0w : t.r0w + a.radius) &&
+                          kb + 15 <= a.n - 1;
+    const bool write = P == kPassWriteFused || P == kPassWriteNorm;
+    if (interior) {
+        const bool valid[4] = {true, true, true, true};
+        consume4<P, false>(t, x, valid, a.scale_log2,
+                           write ? Abh + t.ri.x + (key0 - t.ri.y) : nullptr);
+        return;
+    }
+    const uint32_t d = (uint32_t)(key0 - t.lo);
+    bool valid[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) valid[e] = t.rok && d + (uint32_t)e <= t.span;
+    const int32_t off = key0 - t.ri.y;
+    uint16_t* dst = (write && t.rok && off >= 0 && off < t.ri.z) ? Abh + t.ri.x + off : nullptr;
+    consume4<P, true>(t, x, valid, a.scale_log2, dst);
+}
+
+// One random tile: slots 16 h .. 16 h + 15 of a group. The lane's slots
+// 16 h + 4 kg + e are pairs 8 h + 2 kg + e / 2, whose bytes (row, + 0x80
+// when the second slot is a dummy, 0xFF for a dummy pair) are `rows2`;
+// gdst is the weight slot of the lane's first slot.
+template <int P>
+__device__ __forceinline__ void random_tile(SLane& t, const f32x4& x, uint32_t rows2,
+                                            float scale_log2, uint16_t* gdst) {
+    const uint32_t ra = rows2 & 0xffu, rb = (rows2 >> 8) & 0xffu;
+    const uint32_t me = (uint32_t)t.s16;
+    const bool ma = (ra & 0x7fu) == me, mb = (rb & 0x7fu) == me;
+    const bool sa = (ra & 0x80u) != 0, sb = (rb & 0x80u) != 0;   // lone slots
+    if (P == kPassMax) {
+        if (ma) t.m = fmaxf(t.m, fmaxf(x[0], sa ? x[0] : x[1]));
+        if (mb) t.m = fmaxf(t.m, fmaxf(x[2], sb ? x[2] : x[3]));
+        return;
+    }
+    float w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = exp2f_fast(__builtin_fmaf(x[e], scale_log2, -t.ms));
+    w[0] = ma ? w[0] : 0.0f;
+    w[1] = ma && !sa ? w[1] : 0.0f;
+    w[2] = mb ? w[2] : 0.0f;
+    w[3] = mb && !sb ? w[3] : 0.0f;
+    if (P == kPassSum) {
+        t.sum += (w[0] + w[1]) + (w[2] + w[3]);
+        return;
+    }
+    if (P == kPassWriteNorm) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] *= t.inv;
+    }
+    const uint32_t pa = to_bf16_pair(w[0], w[1]), pb = to_bf16_pair(w[2], w[3]);
+    // A pair is written by the lane of its row; a dummy pair by row 0's lane.
+    if (ma || (ra == 0xffu && me == 0)) *reinterpret_cast<uint32_t*>(gdst) = pa;
+    if (mb || (rb == 0xffu && me == 0)) *reinterpret_cast<uint32_t*>(gdst + 2) = pb;
+    if (P == kPassWriteFused) t.sum = add_pair(pb, add_pair(pa, t.sum));
 }
 
 // One key chunk of a row-tile wave in pass P: band tiles of chunk c, then
@@ -164,7 +239,7 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
                                            const char LDS_AS* __restrict__ cur,
                                            char LDS_AS* __restrict__ stg, int c, int wave,
                                            int lane) {
-    const int64_t c0 = (int64_t)c * kChunkRows;
+    const int32_t c0 = c * kChunkRows;
     const bool more = c + 1 < a.nchunks;
     const int32_t g0 = uniform_load(t.cptr + c);
     const int32_t gcnt = uniform_load(t.cptr + c + 1) - g0;
@@ -173,86 +248,42 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
         const int32_t n0 = g0 + gcnt;
         ncnt = min(uniform_load(t.cptr + c + 2) - n0, kStageGroups);
         if (lane < 4 * ncnt) {
-            t.pj = *reinterpret_cast<const u32x4*>(a.sched_j + (t.goff + n0) * 16 + 4 * lane);
+            t.pk = *reinterpret_cast<const u32x4*>(a.sched_k + (t.goff + n0) * kGroupSlots +
+                                                   8 * lane);
             t.pr = a.sched_row[(t.goff + n0) * 4 + lane];
         }
     }
 
     // Window band, 16 keys per tile.
-    const int64_t k_lo = max(t.band_lo, c0);
-    const int64_t k_hi = min(t.band_hi, c0 + kChunkRows - 1);
-    for (int64_t kb = k_lo; kb <= k_hi; kb += 16) {
-        u32x4 k0, k1;
-        k_operands(cur, (uint32_t)(kb - c0) + (uint32_t)t.s16, (uint32_t)t.kg, k0, k1);
-        const f32x4 s = score_tile(k0, k1, t.q0, t.q1, a.scale_log2);
-        const int64_t key0 = kb + 4 * t.kg;
-        bool valid[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) valid[e] = t.rok && key0 + e >= t.lo && key0 + e <= t.whi;
-        uint16_t* dst = nullptr;
-        const int64_t off = key0 - t.ri.y;
-        if (P != kPassMax && P != kPassSum && t.rok && off >= 0 && off < t.ri.z)
-            dst = Abh + t.ri.x + off;
-        consume4<P>(t, s, valid, dst);
-    }
+    const int32_t k_lo = max(t.band_lo, c0);
+    const int32_t k_hi = min(t.band_hi, c0 + kChunkRows - 1);
+    for (int32_t kb = k_lo; kb <= k_hi; kb += 16) band_tile<P>(t, a, Abh, cur, kb, c0);
 
     if (more) dma_chunk(nxt, Kbh, a.n, c0 + kChunkRows, wave, lane);
 
-    // Random groups: two tiles of 16 slots each. A pair's byte is its row
-    // (+ 0x80 when its second slot is a dummy, 0xFF for a dummy pair).
+    // Random groups: two tiles of 16 slots each (staged ones from LDS, any
+    // others straight from memory).
     for (int32_t k = 0; k < gcnt; ++k) {
-        const char LDS_AS* o = stg + (k < kStageGroups ? k : 0) * kSGroupBytes;
+        const bool staged = k < kStageGroups;
+        const char LDS_AS* o = stg + (staged ? k : 0) * kSGroupBytes;
+        const int64_t gi = t.goff + g0 + k;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            // Key row of slot 16 h + l % 16 (this lane's K operand row).
-            const int sl = 16 * h + t.s16;
-            const int ji = 2 * (4 * (sl >> 3) + (sl & 3)) + ((sl >> 2) & 1);
-            uint32_t code_mine, rows2;
-            if (k < kStageGroups) {
-                code_mine = *reinterpret_cast<const uint16_t LDS_AS*>(o + 2 * ji);
-                rows2 = *reinterpret_cast<const uint16_t LDS_AS*>(o + 64 + 8 * h + 2 * t.kg);
-            } else {
-                const int64_t gi = t.goff + g0 + k;
-                code_mine = reinterpret_cast<const uint16_t*>(a.sched_j + gi * 16)[ji];
-                rows2 = reinterpret_cast<const uint16_t*>(a.sched_row + gi * 4)[4 * h + t.kg];
-            }
+            const uint32_t code =
+                staged ? *reinterpret_cast<const uint16_t LDS_AS*>(o + 2 * (16 * h + t.s16))
+                       : a.sched_k[gi * kGroupSlots + 16 * h + t.s16];
+            const uint32_t rows2 =
+                staged ? *reinterpret_cast<const uint16_t LDS_AS*>(o + 64 + 8 * h + 2 * t.kg)
+                       : reinterpret_cast<const uint16_t*>(a.sched_row + gi * 4)[4 * h + t.kg];
             u32x4 k0, k1;
-            k_operands(cur, code_mine >> 2, (uint32_t)t.kg, k0, k1);
-            const f32x4 s = score_tile(k0, k1, t.q0, t.q1, a.scale_log2);
-            // This lane's slots 16 h + 4 kg + e are pairs 8 h + 2 kg + e / 2.
-            const uint32_t row_a = rows2 & 0xffu, row_b = (rows2 >> 8) & 0xffu;
-            const uint32_t me = (uint32_t)t.s16;
-            const bool ma = t.rok && (row_a & 0x7fu) == me;
-            const bool mb = t.rok && (row_b & 0x7fu) == me;
-            bool valid[4] = {ma, ma && row_a == me, mb, mb && row_b == me};
-            if (P == kPassMax || P == kPassSum) {
-                consume4<P>(t, s, valid, nullptr);
-            } else {
-                float w[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    w[e] = valid[e] ? exp2f_fast(s[e] - t.m) : 0.0f;
-                    if (P == kPassWriteNorm) w[e] *= t.inv;
-                }
-                const uint32_t pa = to_bf16_pair(w[0], w[1]), pb = to_bf16_pair(w[2], w[3]);
-                uint16_t* gdst = Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 16 * h +
-                                 4 * t.kg;
-                // A pair is written by the lanes of its row; a dummy pair by
-                // the lane of row 0.
-                if (ma || (row_a == 0xffu && t.s16 == 0))
-                    *reinterpret_cast<uint32_t*>(gdst) = pa;
-                if (mb || (row_b == 0xffu && t.s16 == 0))
-                    *reinterpret_cast<uint32_t*>(gdst + 2) = pb;
-                if (P == kPassWriteFused) {
-                    if (ma) t.sum += bf16_lo(pa) + bf16_hi(pa);
-                    if (mb) t.sum += bf16_lo(pb) + bf16_hi(pb);
-                }
-            }
+            k_operands(cur, code, (uint32_t)t.kg, k0, k1);
+            random_tile<P>(t, dots(k0, k1, t.q0, t.q1), rows2, a.scale_log2,
+                           Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 16 * h + 4 * t.kg);
         }
     }
     if (more && lane < 4 * ncnt) {
         char LDS_AS* d = stg + (lane >> 2) * kSGroupBytes;
-        *reinterpret_cast<u32x4 LDS_AS*>(d + (lane & 3) * 16) = t.pj;
+        *reinterpret_cast<u32x4 LDS_AS*>(d + (lane & 3) * 16) = t.pk;
         *reinterpret_cast<uint32_t LDS_AS*>(d + 64 + (lane & 3) * 4) = t.pr;
     }
 }
@@ -262,22 +293,22 @@ template <int P>
 __device__ __forceinline__ void tile_globals(SLane& t, const ScoreArgs& a, uint16_t* Abh,
                                              const char LDS_AS* zg, const int32_t LDS_AS* gidx,
                                              int gpad) {
+    const bool write = P == kPassWriteFused || P == kPassWriteNorm;
+    const int32_t hi = (int32_t)t.span + t.lo;   // window end
     for (int qb = 0; qb < gpad; qb += 16) {
         u32x4 k0, k1;
-        k_operands(zg, (uint32_t)(qb + t.s16), (uint32_t)t.kg, k0, k1);
-        const f32x4 s = score_tile(k0, k1, t.q0, t.q1, a.scale_log2);
+        k_operands(zg, score_row_code((uint32_t)(qb + t.s16)), (uint32_t)t.kg, k0, k1);
+        const f32x4 x = dots(k0, k1, t.q0, t.q1);
         const int q0 = qb + 4 * t.kg;
         bool valid[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int q = q0 + e;
-            const int64_t p = q < a.g ? gidx[q] : 0;
-            valid[e] = t.rok && q < a.g && (a.causal ? p < t.lo : (p < t.lo || p > t.whi));
+            const int32_t p = gidx[q];
+            valid[e] = t.rok && q < a.g && (p < t.lo || (!a.causal && p > hi));
         }
-        uint16_t* dst = nullptr;
-        if (P != kPassMax && P != kPassSum && t.rok && q0 < t.ri.w)
-            dst = Abh + t.ri.x + t.ri.z + q0;
-        consume4<P>(t, s, valid, dst);
+        uint16_t* dst = (write && t.rok && q0 < t.ri.w) ? Abh + t.ri.x + t.ri.z + q0 : nullptr;
+        consume4<P, true>(t, x, valid, a.scale_log2, dst);
     }
 }
 
@@ -298,7 +329,8 @@ __device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uin
         if (lane < 4 * cnt) {
             char LDS_AS* d = stg + (lane >> 2) * kSGroupBytes;
             *reinterpret_cast<u32x4 LDS_AS*>(d + (lane & 3) * 16) =
-                *reinterpret_cast<const u32x4*>(a.sched_j + (t.goff + g0) * 16 + 4 * lane);
+                *reinterpret_cast<const u32x4*>(a.sched_k + (t.goff + g0) * kGroupSlots +
+                                                8 * lane);
             *reinterpret_cast<uint32_t LDS_AS*>(d + 64 + (lane & 3) * 4) =
                 a.sched_row[(t.goff + g0) * 4 + lane];
         }
@@ -311,7 +343,7 @@ __device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uin
             tile_chunk<P>(t, a, Kbh, Abh, (c & 1) ? buf0 : buf1, (c & 1) ? buf1 : buf0, stg, c,
                           wave, lane);
         } else if (c + 1 < a.nchunks) {
-            dma_chunk((c & 1) ? buf0 : buf1, Kbh, a.n, (int64_t)(c + 1) * kChunkRows, wave, lane);
+            dma_chunk((c & 1) ? buf0 : buf1, Kbh, a.n, (c + 1) * kChunkRows, wave, lane);
         }
     }
     full_barrier();   // every wave is done with the buffers
@@ -332,11 +364,13 @@ __device__ __forceinline__ float row_sum(float x) {
 // Global rows: 32 per workgroup (two 16-row blocks); wave w scores keys
 // c0 + 32 w .. + 31 of every chunk.
 struct GLane {
-    int kg, s16;
-    int64_t i[2];              // the lane's global rows (or -1)
-    int64_t sbase[2], slen[2];
+    int32_t kg, s16;
+    int32_t i[2];              // the lane's global rows (or -1)
+    int32_t last[2];           // their last key (n - 1, or the row when causal)
+    int64_t sbase[2];
+    int32_t slen[2];
     u32x4 q0[2], q1[2];
-    float m[2], sum[2], inv[2];
+    float m[2], ms[2], sum[2], inv[2];
 };
 
 template <int P>
@@ -344,32 +378,34 @@ __device__ __forceinline__ void grow_chunk(GLane& t, const ScoreArgs& a, const u
                                            uint16_t* Abh, char LDS_AS* __restrict__ nxt,
                                            const char LDS_AS* __restrict__ cur, int c, int wave,
                                            int lane) {
-    const int64_t c0 = (int64_t)c * kChunkRows;
+    const int32_t c0 = c * kChunkRows;
     if (c + 1 < a.nchunks) dma_chunk(nxt, Kbh, a.n, c0 + kChunkRows, wave, lane);
     if (c0 + 32 * wave >= a.n) return;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         u32x4 k0, k1;
-        k_operands(cur, (uint32_t)(32 * wave + 16 * h + t.s16), (uint32_t)t.kg, k0, k1);
-        const int64_t key0 = c0 + 32 * wave + 16 * h + 4 * t.kg;
+        k_operands(cur, score_row_code((uint32_t)(32 * wave + 16 * h + t.s16)), (uint32_t)t.kg,
+                   k0, k1);
+        const int32_t key0 = c0 + 32 * wave + 16 * h + 4 * t.kg;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            const f32x4 s = score_tile(k0, k1, t.q0[mb], t.q1[mb], a.scale_log2);
-            const int64_t last = a.causal ? t.i[mb] : a.n - 1;
+            const f32x4 x = dots(k0, k1, t.q0[mb], t.q1[mb]);
             bool valid[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) valid[e] = t.i[mb] >= 0 && key0 + e <= last;
+            for (int e = 0; e < 4; ++e) valid[e] = key0 + e <= t.last[mb];
             if (P == kPassMax) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t.m[mb] = valid[e] ? fmaxf(t.m[mb], s[e]) : t.m[mb];
+                for (int e = 0; e < 4; ++e) t.m[mb] = valid[e] ? fmaxf(t.m[mb], x[e]) : t.m[mb];
                 continue;
             }
             float w[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = valid[e] ? exp2f_fast(s[e] - t.m[mb]) : 0.0f;
+            for (int e = 0; e < 4; ++e) {
+                w[e] = exp2f_fast(__builtin_fmaf(x[e], a.scale_log2, -t.ms[mb]));
+                w[e] = valid[e] ? w[e] : 0.0f;
+            }
             if (P == kPassSum) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) t.sum[mb] += w[e];
+                t.sum[mb] += (w[0] + w[1]) + (w[2] + w[3]);
                 continue;
             }
             if (P == kPassWriteNorm) {
@@ -377,10 +413,10 @@ __device__ __forceinline__ void grow_chunk(GLane& t, const ScoreArgs& a, const u
                 for (int e = 0; e < 4; ++e) w[e] *= t.inv[mb];
             }
             const uint32_t lo = to_bf16_pair(w[0], w[1]), hi = to_bf16_pair(w[2], w[3]);
-            if (t.i[mb] >= 0 && key0 < t.slen[mb])
+            if (key0 < t.slen[mb]) {
                 *reinterpret_cast<u32x2*>(Abh + t.sbase[mb] + key0) = u32x2{lo, hi};
-            if (P == kPassWriteFused)
-                t.sum[mb] += bf16_lo(lo) + bf16_hi(lo) + bf16_lo(hi) + bf16_hi(hi);
+                if (P == kPassWriteFused) t.sum[mb] = add_pair(hi, add_pair(lo, t.sum[mb]));
+            }
         }
     }
 }
@@ -437,7 +473,7 @@ void k_scores_sched(ScoreArgs a) {
     const int32_t sub = item - bh * per_bh;
     const int32_t b = bh / a.H, h = bh - b * a.H;
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
-    const int64_t n = a.n;
+    const int32_t n = a.n;
     uint16_t* Abh = a.A + a_block_offset(a.slot_off, a.num_graphs, a.H, b, h);
     const uint16_t* Kbh = a.K + (int64_t)bh * n * kD;
     const uint16_t* Qbh = a.Q + (int64_t)bh * n * kD;
@@ -458,17 +494,20 @@ void k_scores_sched(ScoreArgs a) {
         for (int mb = 0; mb < 2; ++mb) {
             const int q = sub * kGrowRows + 16 * mb + s16;
             t.i[mb] = q < a.g ? a.G[q] : -1;
+            t.last[mb] = t.i[mb] < 0 ? -1 : (a.causal ? t.i[mb] : n - 1);
             t.sbase[mb] = t.i[mb] >= 0 ? sp[t.i[mb]] : 0;
-            t.slen[mb] = t.i[mb] >= 0 ? sp[t.i[mb] + 1] - sp[t.i[mb]] : 0;
-            const int64_t qi = t.i[mb] >= 0 ? t.i[mb] : 0;
-            t.q0[mb] = load16(Qbh + qi * kD + 8 * kg);
-            t.q1[mb] = load16(Qbh + qi * kD + 32 + 8 * kg);
+            t.slen[mb] = t.i[mb] >= 0 ? (int32_t)(sp[t.i[mb] + 1] - sp[t.i[mb]]) : 0;
+            const int32_t qi = t.i[mb] >= 0 ? t.i[mb] : 0;
+            t.q0[mb] = load16(Qbh + (int64_t)qi * kD + 8 * kg);
+            t.q1[mb] = load16(Qbh + (int64_t)qi * kD + 32 + 8 * kg);
             t.m[mb] = -INFINITY;
             t.sum[mb] = 0.0f;
             t.inv[mb] = 0.0f;
         }
         grow_pass<kPassMax>(t, a, Kbh, Abh, lds, wave, lane);
         grow_merge<true>(t.m, lds, wave, lane);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) t.ms[mb] = t.m[mb] * a.scale_log2;
         if (a.normalized) {
             grow_pass<kPassSum>(t, a, Kbh, Abh, lds, wave, lane);
             grow_merge<false>(t.sum, lds, wave, lane);
@@ -491,29 +530,31 @@ void k_scores_sched(ScoreArgs a) {
     SLane t;
     t.kg = kg;
     t.s16 = s16;
-    const int64_t r0w = (int64_t)(sub - a.grow_per_bh) * kTileRows + (int64_t)kRowBlock * wave;
-    const bool active = r0w < n;
-    t.i = r0w + s16;
+    t.r0w = (sub - a.grow_per_bh) * kTileRows + kRowBlock * wave;
+    const bool active = t.r0w < n;
+    t.i = t.r0w + s16;
     t.ri = make_int4(0, 0, -1, 0);
     if (t.i < n) t.ri = info[t.i];
     t.rok = t.i < n && t.ri.z >= 0;
-    t.lo = t.i - a.radius < 0 ? 0 : t.i - a.radius;
-    const int64_t hi = t.i + a.radius > n - 1 ? n - 1 : t.i + a.radius;
-    t.whi = a.causal ? t.i : hi;
-    const int64_t qi = t.i < n ? t.i : n - 1;
-    t.q0 = load16(Qbh + qi * kD + 8 * kg);
-    t.q1 = load16(Qbh + qi * kD + 32 + 8 * kg);
+    t.block_ok = __all(t.rok);   // wave-uniform
+    t.lo = max(t.i - a.radius, 0);
+    const int32_t whi = a.causal ? t.i : min(t.i + a.radius, n - 1);
+    t.span = (uint32_t)(whi - t.lo);
+    const int32_t qi = min(t.i, n - 1);
+    t.q0 = load16(Qbh + (int64_t)qi * kD + 8 * kg);
+    t.q1 = load16(Qbh + (int64_t)qi * kD + 32 + 8 * kg);
     t.m = -INFINITY;
+    t.ms = 0.0f;
     t.sum = 0.0f;
     t.inv = 0.0f;
-    const int64_t wr_last = min(r0w + kRowBlock - 1, n - 1);
-    t.band_lo = (r0w - a.radius < 0 ? 0 : r0w - a.radius) & ~15ll;
+    const int32_t wr_last = min(t.r0w + kRowBlock - 1, n - 1);
+    t.band_lo = max(t.r0w - a.radius, 0) & ~15;
     t.band_hi = a.causal ? wr_last : min(n - 1, wr_last + a.radius);
-    const int64_t rb = active ? r0w / kRowBlock : 0;
+    const int64_t rb = active ? t.r0w / kRowBlock : 0;
     t.cptr = a.grp_cptr + ((int64_t)gr * a.nrb + rb) * (a.nchunks + 1);
     t.goff = a.grp_off[gr];
     t.rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];
-    t.pj = u32x4{0u, 0u, 0u, 0u};
+    t.pk = u32x4{0u, 0u, 0u, 0u};
     t.pr = 0u;
 
     // Staged global rows of K and their positions.
@@ -524,12 +565,14 @@ void k_scores_sched(ScoreArgs a) {
         const int q = idx >> 3, lu = idx & 7;
         u32x4 v = {0u, 0u, 0u, 0u};
         if (q < a.g) v = load16(Kbh + (int64_t)a.G[q] * kD + lu * 8);
-        *reinterpret_cast<u32x4 LDS_AS*>(zg + unit_addr((uint32_t)q, (uint32_t)lu)) = v;
+        *reinterpret_cast<u32x4 LDS_AS*>(zg + ((score_row_code((uint32_t)q) ^ (uint32_t)lu) << 4)) =
+            v;
     }
     for (int q = threadIdx.x; q < gpad; q += kThreads) gidx[q] = q < a.g ? a.G[q] : 0;
 
     tile_pass<kPassMax>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
     t.m = row_max(t.m);
+    t.ms = t.m * a.scale_log2;
     if (a.normalized) {
         tile_pass<kPassSum>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
         t.sum = row_sum(t.sum);
@@ -557,10 +600,10 @@ hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, cons
                               const void* K, void* A, float* row_scale, float scale_log2,
                               bool normalized, hipStream_t st) {
     ScoreArgs a;
-    a.n = g.n;
+    a.n = (int32_t)g.n;
     a.H = s.H;
     a.num_graphs = g.num_graphs;
-    a.radius = g.radius;
+    a.radius = (int32_t)std::min<int64_t>(g.radius, g.n);
     a.g = g.num_global;
     a.causal = g.causal;
     a.nchunks = (int32_t)((g.n + kChunkRows - 1) / kChunkRows);
@@ -572,7 +615,7 @@ hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, cons
     a.grp_off = g.d_grp_off;
     a.grp_cptr = g.d_grp_cptr;
     a.sched_row = g.d_sched_row;
-    a.sched_j = g.d_sched_j;
+    a.sched_k = g.d_sched_k;
     a.Q = static_cast<const uint16_t*>(Q);
     a.K = static_cast<const uint16_t*>(K);
     a.A = static_cast<uint16_t*>(A);
