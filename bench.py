@@ -11,15 +11,26 @@ once, outside the timed region.
 Prints one JSON line. `value` is diffused edges per second
 (B * H * nnz * K / t). `roofline` describes the diffusion-step kernel (the
 dominant one): algorithmic bytes per launch over its mean launch time,
-measured with HIP events on the launch stream, against 8 TB/s.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same work.
+measured with HIP events on the launch stream, against 8 TB/s, and beside it
+a measured device-to-device copy rate. `traffic` is the kernel's HBM bytes
+per launch from the FETCH_SIZE / WRITE_SIZE counter summary under
+profiles/, scaled by what the same counters read for the copy of known size
+that this script also runs; it is null when the kernel sources no longer
+match the ones the counters were taken on. `cpu_baseline` times the CPU
+oracle on a bounded sample of the same work.
+
+`--write-traffic FETCH_DIR WRITE_DIR` turns two `rocprofv3 --pmc` runs of
+this script (one counter each, csv output) into that summary.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
-import statistics
+import re
 import sys
 import time
 
@@ -28,6 +39,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+# Device-to-device copy used both as the measured-bandwidth reference and as
+# the calibration dispatch of the FETCH_SIZE / WRITE_SIZE counters.
+COPY_BYTES = 1 << 29
+COPY_REPS = 10
+
+# Sources whose change invalidates the diffusion kernel's counter figures.
+DIFFUSION_SOURCES = ("diffuse_fast.hip", "mfma_util.h", "internal.h", "graph_build.hip")
+DIFFUSION_KERNEL = "k_diffuse_sched"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+TRAFFIC_FILE = "traffic_diffuse_step_{workload}.txt"
 
 
 def graph_bytes(g, n):
@@ -57,6 +79,107 @@ def time_events(fn, reps, torch):
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / reps
+
+
+def copy_bandwidth(torch):
+    """GB/s (read + write) of a plain device-to-device copy of COPY_BYTES."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    ms = time_events(lambda: dst.copy_(src), COPY_REPS, torch)
+    del src, dst
+    return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
+
+
+def sources_digest(names):
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "sparse_attention_hop_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_rows(folder, counter):
+    """(kernel name, grid size, counter value) per dispatch of a csv pmc run."""
+    paths = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    out = []
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return out
+
+
+def write_traffic(fetch_dir, write_dir, workload):
+    """Summarise FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the diffusion
+    kernel, calibrated against the COPY_BYTES copies of the same runs."""
+    lines = []
+    per = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(folder, counter)
+        copies = [r for r in rows if r[0].startswith(COPY_KERNEL)]
+        big = max(r[1] for r in copies)
+        cal = [r[2] for r in copies if r[1] == big]
+        kern = [r[2] for r in rows if DIFFUSION_KERNEL in r[0]]
+        if not cal or not kern:
+            raise SystemExit(f"{counter}: calibration copies or {DIFFUSION_KERNEL} missing")
+        cal_kib = sum(cal) / len(cal)
+        factor = (COPY_BYTES / 1024) / cal_kib
+        kib = sum(kern) / len(kern)
+        per[counter] = kib * factor * 1024
+        lines += [
+            f"{counter.lower()}_copy_dispatches: {len(cal)}",
+            f"{counter.lower()}_copy_kib_per_dispatch: {cal_kib:.1f}",
+            f"{counter.lower()}_copy_expected_kib: {COPY_BYTES / 1024:.1f}",
+            f"{counter.lower()}_factor: {factor:.4f}",
+            f"{counter.lower()}_kernel_dispatches: {len(kern)}",
+            f"{counter.lower()}_kernel_kib_per_dispatch: {kib:.1f}",
+            f"{counter.lower()}_kernel_bytes_per_launch: {per[counter]:.0f}",
+        ]
+    total = per["FETCH_SIZE"] + per["WRITE_SIZE"]
+    head = [
+        f"# HBM traffic of {DIFFUSION_KERNEL} (one diffusion step), workload {workload}",
+        "#",
+        "# Made by (repository root, one MI355X, TMPDIR=/tmp):",
+        "#   timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch "
+        f"-o p -- python -u bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline",
+        "#   timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write "
+        f"-o p -- python -u bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline",
+        "#   python bench.py --workload "
+        f"{workload} --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "#",
+        f"# Each counter is the mean over the kernel's dispatches, in KiB, scaled by factor =",
+        f"# {COPY_BYTES} B / (what the same counter reads for a {COPY_BYTES} B device copy,",
+        f"# {COPY_KERNEL}, in the same run).",
+        f"sources: {' '.join(DIFFUSION_SOURCES)}",
+        f"sources_sha256: {sources_digest(DIFFUSION_SOURCES)}",
+    ]
+    text = "\n".join(head + lines + [f"traffic_bytes_per_launch: {total:.0f}"]) + "\n"
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILE.format(workload=workload))
+    with open(path, "w") as f:
+        f.write(text)
+    print(text, end="")
+
+
+def read_traffic(workload):
+    """HBM bytes per diffusion launch from the committed counter summary, or
+    None if there is none or the kernel sources changed since it was made."""
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILE.format(workload=workload))
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^([a-z_0-9]+): (.*)$", line.strip())
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("sources_sha256") != sources_digest(DIFFUSION_SOURCES):
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, q, k, v, budget_s=15.0, max_pairs=None):
@@ -98,7 +221,13 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+
+    if args.write_traffic:
+        from workloads import HEADLINE
+        write_traffic(*args.write_traffic, args.workload or HEADLINE)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
@@ -128,13 +257,23 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The timed region: exactly `steps` whole-path calls. Each call is also
+    # bracketed by HIP events on the launch stream for the median.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for a, b in evs:
+        a.record()
         step()
+        b.record()
     torch.cuda.synchronize()
     t = (time.perf_counter() - t0) / args.steps
+    per_call = sorted(a.elapsed_time(b) for a, b in evs)
+    t_median = per_call[len(per_call) // 2]
 
-    # Stage timing on the same stream (HIP events).
+    # Stage timing on the same stream (HIP events): the diffusion stage alone
+    # (K launches of the step kernel) and the normalised score + softmax
+    # entry point. The fused score stage inside attn is the difference.
     A = sah.scores_softmax(q, k, g)
     zs = torch.empty_like(v)
     reps = max(5, args.steps)
@@ -142,12 +281,14 @@ def main():
     t_diff = time_events(lambda: sah.diffuse(A, v, g, w.K, w.alpha, out=zs, workspace=ws),
                          reps, torch)
     t_step = t_diff / max(w.K, 1)
+    copy_gbs = copy_bandwidth(torch)
 
     nnz_pass = g.edges(w.B, w.H)
     diffused = nnz_pass * w.K
     score_b, diff_b = algorithmic_bytes(w, g, w.K)
     per_launch = diff_b / max(w.K, 1)
     achieved = per_launch / (t_step * 1e-3) / 1e9
+    traffic = read_traffic(w.name)
 
     line = {
         "metric": "diffused edges/s (nnz*K/s) + % HBM roofline at n=4096, K=5, alpha=0.1",
@@ -157,6 +298,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": t * 1e3,
+        "median_ms_per_step": t_median,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -169,19 +311,22 @@ def main():
             "alpha": w.alpha, "nnz_per_graph": g.nnz[0], "edges_per_pass": nnz_pass,
         },
         "roofline": {
-            "kernel": "diffusion step",
+            "kernel": "diffusion step (" + DIFFUSION_KERNEL + ")",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": traffic,
             "algorithmic_bytes_per_launch": per_launch,
             "mean_launch_ms": t_step,
+            "copy_GBs": copy_gbs,
+            "frac_of_copy": achieved / copy_gbs,
         },
         "stages": {
-            "score_softmax_ms": t_score,
-            "score_softmax_GBs": score_b / (t_score * 1e-3) / 1e9,
+            "score_softmax_fused_ms": t_median - t_diff,
+            "score_softmax_fused_GBs": score_b / ((t_median - t_diff) * 1e-3) / 1e9,
+            "score_softmax_normalised_ms": t_score,
             "diffusion_ms": t_diff,
             "diffusion_GBs": diff_b / (t_diff * 1e-3) / 1e9,
         },
