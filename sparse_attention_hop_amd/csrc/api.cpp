@@ -52,6 +52,7 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_col_idx);
     hipFree(g->d_col_off);
     hipFree(g->d_global);
+    hipFree(g->d_gchunk);
     hipFree(g->d_rnd);
     hipFree(g->d_rnd_cnt);
     hipFree(g->d_seg_ptr);
@@ -70,6 +71,7 @@ void free_graph_memory(diffuser_graph* g) {
     g->d_col_idx = nullptr;
     g->d_col_off = nullptr;
     g->d_global = nullptr;
+    g->d_gchunk = nullptr;
     g->d_rnd = nullptr;
     g->d_rnd_cnt = nullptr;
     g->d_seg_ptr = nullptr;
@@ -273,7 +275,14 @@ diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stre
     int64_t* d_max = nullptr;
     int32_t* d_gcount = nullptr;
     hipError_t e;
+    // Globals below the start of every key chunk (G is ascending).
+    const int64_t nchunks = (n + kChunkRows - 1) / kChunkRows;
+    std::vector<int32_t> gchunk((size_t)nchunks + 1);
+    for (int64_t c = 0; c <= nchunks; ++c)
+        gchunk[c] = (int32_t)(std::lower_bound(desc->global_idx, desc->global_idx + g->num_global,
+                                               (int64_t)c * kChunkRows) - desc->global_idx);
     if ((e = dev_alloc(&g->d_global, g->num_global)) != hipSuccess ||
+        (e = dev_alloc(&g->d_gchunk, (size_t)nchunks + 1)) != hipSuccess ||
         (e = dev_alloc(&g->d_rnd, (size_t)rows * std::max(g->rnd_width, 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_rslot, (size_t)rows * std::max(g->rnd_width, 1))) != hipSuccess ||
         (e = dev_alloc(&g->d_row_info, (size_t)rows * 4)) != hipSuccess ||
@@ -307,6 +316,9 @@ diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stre
         (e = hipMemcpyAsync(g->d_global, desc->global_idx, sizeof(int32_t) * g->num_global,
                             hipMemcpyHostToDevice, st)) != hipSuccess)
         return hip_fail(e, "copy of global_idx");
+    if ((e = hipMemcpyAsync(g->d_gchunk, gchunk.data(), sizeof(int32_t) * gchunk.size(),
+                            hipMemcpyHostToDevice, st)) != hipSuccess)
+        return hip_fail(e, "copy of the global chunk table");
     if ((e = hipMemsetAsync(d_status, 0, sizeof(int32_t), st)) != hipSuccess)
         return hip_fail(e, "status clear");
     if ((e = launch_draw(*g, d_deg, d_slots, d_status, st)) != hipSuccess)

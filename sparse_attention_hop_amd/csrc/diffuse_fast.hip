@@ -10,13 +10,19 @@
 // read hands every lane one channel of 4 key rows); the W^T operand is 8
 // consecutive weight slots of one row, one 16-byte load.
 //  * window edges: the 32 keys are consecutive columns of the band;
-//  * global columns: the g global rows of Z_k, staged once per workgroup;
+//  * global columns: 32 global slots at a time, in the chunk that holds the
+//    globals' key rows (a slot whose global lies in another chunk reads the
+//    zero row instead);
 //  * random edges: the 32 keys are the slots of one schedule group, whose
 //    key rows lie in the current chunk; the weight operand keeps a pair's
 //    two weights in the lanes of the pair's row and zeroes them elsewhere.
 // A workgroup (16 waves, 16 rows each) streams Z_k of its (batch, head)
 // through LDS in chunks of kChunkRows rows, double-buffered with direct
-// global-to-LDS loads of the next chunk while the current one is used. Rows
+// global-to-LDS loads of the next chunk while the current one is used; each
+// wave's schedule groups of the next chunk travel the same way into a
+// double-buffered staging area of its own. The weights of a chunk's dense
+// steps (band and global columns) are loaded when the chunk starts and used
+// after its random groups. Rows
 // of Z_k sit in LDS at 128 bytes, quarters permuted by key_row_code, which
 // spreads the 16 rows of one transposed read over the banks.
 // Global rows get workgroups of their own (32 rows; the 16 waves split each
@@ -38,11 +44,15 @@ constexpr int kRowBytes = kD * 2;                     // a Z row in LDS
 constexpr int kBufBytes = (kChunkRows + 1) * kRowBytes;  // chunk + zero row
 constexpr int kTileRows = kWaves * kRowBlock;         // rows per row-tile workgroup
 constexpr int kGrowRows = 32;                         // global rows per workgroup
-constexpr int kMaxGlobal = 128;                       // staged global rows (LDS room)
-constexpr int kGroupBytes = 144;                      // staged group: weights, key rows, pair rows
-constexpr int kStageGroups = 6;                       // groups per wave and chunk staged in LDS
-constexpr int kStageBytes = kStageGroups * kGroupBytes;
-constexpr int kLdsBytes = 2 * kBufBytes + kMaxGlobal * kRowBytes + kWaves * kStageBytes;
+// Per-wave staging of one chunk's first kStageGroups schedule groups:
+// weights [group][64 B], key-row codes [group][64 B], pair rows [group][16 B].
+constexpr int kStageGroups = 6;
+constexpr int kStageJ = kStageGroups * 64;
+constexpr int kStageR = 2 * kStageGroups * 64;
+constexpr int kStageBytes = kStageR + kStageGroups * 16;
+constexpr int kMaxBand = 5;                           // band steps per chunk held in registers
+constexpr int kMaxGlob = 2;                           // global steps per chunk held in registers
+constexpr int kLdsBytes = 2 * kBufBytes + kWaves * 2 * kStageBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 static_assert(kWaves * 2 * kNB * 4 * kWave * 4 <= 2 * kBufBytes, "grow partial sums fit");
@@ -54,6 +64,7 @@ struct FastArgs {
     const int64_t* seg_ptr;     // [graphs][n + 1]
     const int4* row_info;       // [graphs][n]
     const int32_t* G;           // [g]
+    const int32_t* gchunk;      // [nchunks + 1] globals below each chunk start
     const int64_t* grp_ptr;     // [graphs][nrb + 1]
     const int64_t* grp_off;     // [graphs + 1]
     const int32_t* grp_cptr;    // [graphs][nrb][nchunks + 1]
@@ -154,86 +165,101 @@ struct TileLane {
     uint32_t a4, q4;
     int4 ri;                 // row info of row r0w + s16
     bool rok;
-    int64_t r0w, band_hi, kc_next;
-    u32x4 band_next;         // weights of band step kc_next
+    int64_t r0w, band_lo, band_hi;
     const int32_t* cptr;     // chunk -> first group of this row block
     int64_t goff, rbase;
-    u32x4 pw, pj, pr;        // next chunk's groups, compact
 };
 
+// Weights of the band step at key column kc (8 slots of this lane's row).
 __device__ __forceinline__ u32x4 band_weights(const TileLane& t, const uint16_t* Abh, int64_t kc) {
     const int32_t off = (int32_t)(kc + 8 * t.kg) - t.ri.y;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (t.rok && kc <= t.band_hi && off >= 0 && off < t.ri.z) w = load16(Abh + t.ri.x + off);
+    if (t.rok && off >= 0 && off < t.ri.z) w = load16(Abh + t.ri.x + off);
     return w;
 }
 
-// Compact loads of the first kStageGroups groups of chunk c: lanes 4 k .. 4 k
-// + 3 hold group k's weights and key-row codes, lane k its pair rows.
-__device__ __forceinline__ void fetch_groups(TileLane& t, const FastArgs& a, const uint16_t* Abh,
-                                             int c, int lane) {
+// Weights of global step s (global slots 32 s + 8 kg .. + 7 of this lane's row).
+__device__ __forceinline__ u32x4 glob_weights(const TileLane& t, const uint16_t* Abh, int s) {
+    const int32_t off = 32 * s + 8 * t.kg;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (t.rok && off < t.ri.w) w = load16(Abh + t.ri.x + t.ri.z + off);
+    return w;
+}
+
+// Key row, within chunk c0, of global slot q when that global lies in
+// [q0, q1) (the chunk's globals), else the zero row.
+__device__ __forceinline__ uint32_t glob_row(const FastArgs& a, int q, int q0, int q1,
+                                             int64_t c0) {
+    return (q >= q0 && q < q1) ? (uint32_t)(a.G[q] - c0) : kZeroRow;
+}
+
+// Direct loads of chunk c's first kStageGroups schedule groups (weights,
+// key-row codes, pair rows) into the staging area `stg`.
+__device__ __forceinline__ void dma_groups(const TileLane& t, const FastArgs& a,
+                                           const uint16_t* Abh, char LDS_AS* stg, int c, int lane) {
     const int32_t g0 = uniform_load(t.cptr + c);
     const int32_t cnt = min(uniform_load(t.cptr + c + 1) - g0, kStageGroups);
     if (lane < 4 * cnt) {
-        t.pw = load16(Abh + t.rbase + (int64_t)kGroupSlots * g0 + 8 * lane);
-        t.pj = *reinterpret_cast<const u32x4*>(a.sched_j + (t.goff + g0) * 16 + 4 * lane);
+        dma16(Abh + t.rbase + (int64_t)kGroupSlots * g0 + 8 * lane, stg);
+        dma16(a.sched_j + (t.goff + g0) * 16 + 4 * lane, stg + kStageJ);
     }
-    if (lane < cnt) t.pr = *reinterpret_cast<const u32x4*>(a.sched_row + (t.goff + g0 + lane) * 4);
+    if (lane < cnt) dma16(a.sched_row + (t.goff + g0 + lane) * 4, stg + kStageR);
 }
 
-__device__ __forceinline__ void store_groups(const TileLane& t, char LDS_AS* __restrict__ stg,
-                                             int cnt, int lane) {
-    if (lane < 4 * cnt) {
-        char LDS_AS* o = stg + (lane >> 2) * kGroupBytes + (lane & 3) * 16;
-        *reinterpret_cast<u32x4 LDS_AS*>(o) = t.pw;
-        *reinterpret_cast<u32x4 LDS_AS*>(o + 64) = t.pj;
-    }
-    if (lane < cnt) *reinterpret_cast<u32x4 LDS_AS*>(stg + lane * kGroupBytes + 128) = t.pr;
-}
-
-// One key chunk of a row-tile wave: multiplies the band of chunk c (rows in
-// `cur`), starts the direct loads of chunk c + 1 into `nxt`, then multiplies
-// the random groups of chunk c (staged in `stg`) and stages those of chunk
-// c + 1. The three LDS regions are disjoint, which lets the reads of `cur`
-// and `stg` run while the loads into `nxt` are in flight; every global load
-// the band needs is issued before them.
-__device__ __forceinline__ void tile_chunk(TileLane& t, f32x4 (&acc)[kNB], const FastArgs& a,
+// One key chunk of a row-tile wave, with chunk c's Z_k rows in `cur` and its
+// staged groups in `stg`: loads the weights of the chunk's dense steps,
+// starts the direct loads of chunk c + 1 (rows into `nxt`, groups into
+// `nstg`), multiplies the random groups, then the dense steps. The LDS
+// regions are disjoint, which lets the reads of `cur` and `stg` run while
+// the loads into `nxt` and `nstg` are in flight.
+__device__ __forceinline__ void tile_chunk(const TileLane& t, f32x4 (&acc)[kNB], const FastArgs& a,
                                            const uint16_t* Abh, const uint16_t* Zbh,
                                            char LDS_AS* __restrict__ nxt,
                                            const char LDS_AS* __restrict__ cur,
-                                           char LDS_AS* __restrict__ stg, int c, int wave,
+                                           char LDS_AS* __restrict__ nstg,
+                                           const char LDS_AS* __restrict__ stg, int c, int wave,
                                            int lane) {
     const int64_t c0 = (int64_t)c * kChunkRows;
     const bool more = c + 1 < a.nchunks;
-    const int32_t g0 = uniform_load(t.cptr + c);
-    const int32_t gcnt = uniform_load(t.cptr + c + 1) - g0;
-    const int32_t ncnt = more ? min(uniform_load(t.cptr + c + 2) - (g0 + gcnt), kStageGroups) : 0;
-    if (more) fetch_groups(t, a, Abh, c + 1, lane);
 
-    // Window band: steps of 32 key columns inside this chunk.
-    const int64_t k_hi = min(t.band_hi, c0 + kChunkRows - 1);
-    const uint32_t bb1 = code_addr(key_row_code(8u * t.kg + t.q4), t.a4);
-    const uint32_t bb2 = code_addr(key_row_code(8u * t.kg + 4u + t.q4), t.a4);
-    while (t.kc_next <= k_hi) {
-        const int64_t kc = t.kc_next;
-        const u32x4 w = t.band_next;
-        t.kc_next += 32;
-        t.band_next = band_weights(t, Abh, t.kc_next);
-        const uint32_t off = (uint32_t)(kc - c0) * kRowBytes;   // multiple of 32 rows
-        mfma4(acc, cur, bb1 + off, bb2 + off, w);
+    // Dense steps of this chunk: global steps [gs0, gs1), band steps from kb0
+    // to kb1 (32-column steps inside the chunk).
+    const int q0 = uniform_load(a.gchunk + c), q1 = uniform_load(a.gchunk + c + 1);
+    const int gs0 = q0 >> 5, gs1 = q1 > q0 ? ((q1 - 1) >> 5) + 1 : gs0;
+    const int64_t kb0 = max(t.band_lo, c0);
+    const int64_t kb1 = min(t.band_hi, c0 + kChunkRows - 1);
+    const int nbs = kb0 <= kb1 ? (int)((kb1 - kb0) >> 5) + 1 : 0;
+    u32x4 gw[kMaxGlob], bw[kMaxBand];
+    uint32_t gr1[kMaxGlob], gr2[kMaxGlob];
+#pragma unroll
+    for (int i = 0; i < kMaxGlob; ++i) {
+        if (gs0 + i < gs1) {
+            const int qa = 32 * (gs0 + i) + 8 * t.kg + t.q4;
+            gw[i] = glob_weights(t, Abh, gs0 + i);
+            gr1[i] = glob_row(a, qa, q0, q1, c0);
+            gr2[i] = glob_row(a, qa + 4, q0, q1, c0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxBand; ++i)
+        if (i < nbs) bw[i] = band_weights(t, Abh, kb0 + 32 * i);
+
+    if (more) {
+        dma_chunk(nxt, Zbh, a.n, c0 + kChunkRows, wave, lane);
+        dma_groups(t, a, Abh, nstg, c + 1, lane);
     }
 
-    if (more) dma_chunk(nxt, Zbh, a.n, c0 + kChunkRows, wave, lane);
-
     // Random groups (staged ones from LDS, any others from memory).
+    const int32_t g0 = uniform_load(t.cptr + c);
+    const int32_t gcnt = uniform_load(t.cptr + c + 1) - g0;
     for (int32_t k = 0; k < gcnt; ++k) {
         uint32_t cj, crows;
         u32x4 cw;
         if (k < kStageGroups) {
-            const char LDS_AS* o = stg + k * kGroupBytes;
-            cw = *reinterpret_cast<const u32x4 LDS_AS*>(o + 16 * t.kg);
-            cj = *reinterpret_cast<const uint32_t LDS_AS*>(o + 64 + 4 * (4 * t.kg + t.q4));
-            crows = *reinterpret_cast<const uint32_t LDS_AS*>(o + 128 + 4 * t.kg);
+            cw = *reinterpret_cast<const u32x4 LDS_AS*>(stg + 64 * k + 16 * t.kg);
+            cj = *reinterpret_cast<const uint32_t LDS_AS*>(stg + kStageJ + 64 * k +
+                                                           4 * (4 * t.kg + t.q4));
+            crows = *reinterpret_cast<const uint32_t LDS_AS*>(stg + kStageR + 16 * k + 4 * t.kg);
         } else {
             const int64_t gi = g0 + k;
             cw = load16(Abh + t.rbase + (int64_t)kGroupSlots * gi + 8 * t.kg);
@@ -243,7 +269,36 @@ __device__ __forceinline__ void tile_chunk(TileLane& t, f32x4 (&acc)[kNB], const
         const u32x4 w = group_weights(cw, crows, (uint32_t)t.s16);
         mfma4(acc, cur, code_addr(cj & 0xffffu, t.a4), code_addr(cj >> 16, t.a4), w);
     }
-    if (more) store_groups(t, stg, ncnt, lane);
+
+    // Global steps.
+#pragma unroll
+    for (int i = 0; i < kMaxGlob; ++i) {
+        if (gs0 + i < gs1)
+            mfma4(acc, cur, code_addr(key_row_code(gr1[i]), t.a4),
+                  code_addr(key_row_code(gr2[i]), t.a4), gw[i]);
+    }
+    for (int s = gs0 + kMaxGlob; s < gs1; ++s) {
+        const int qa = 32 * s + 8 * t.kg + t.q4;
+        mfma4(acc, cur, code_addr(key_row_code(glob_row(a, qa, q0, q1, c0)), t.a4),
+              code_addr(key_row_code(glob_row(a, qa + 4, q0, q1, c0)), t.a4),
+              glob_weights(t, Abh, s));
+    }
+
+    // Window band.
+    const uint32_t bb1 = code_addr(key_row_code(8u * t.kg + t.q4), t.a4);
+    const uint32_t bb2 = code_addr(key_row_code(8u * t.kg + 4u + t.q4), t.a4);
+#pragma unroll
+    for (int i = 0; i < kMaxBand; ++i) {
+        if (i < nbs) {
+            const uint32_t off = (uint32_t)(kb0 + 32 * i - c0) * kRowBytes;  // 32-row multiple
+            mfma4(acc, cur, bb1 + off, bb2 + off, bw[i]);
+        }
+    }
+    for (int i = kMaxBand; i < nbs; ++i) {
+        const int64_t kc = kb0 + 32 * i;
+        const uint32_t off = (uint32_t)(kc - c0) * kRowBytes;
+        mfma4(acc, cur, bb1 + off, bb2 + off, band_weights(t, Abh, kc));
+    }
 }
 
 // One key chunk of a global-row wave: starts the direct loads of chunk
@@ -378,61 +433,30 @@ void k_diffuse_sched(FastArgs a) {
     if (my_row < n) t.ri = info[my_row];
     t.rok = my_row < n && t.ri.z >= 0;           // a non-global row
 
-    // Staged global rows (key-row code placement by position q).
-    char LDS_AS* zg = lds + 2 * kBufBytes;
-    const int gpad = (a.g + 31) & ~31;
-    for (int idx = threadIdx.x; idx < gpad * 8; idx += kThreads) {
-        const int q = idx >> 3, lu = idx & 7;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (q < a.g) v = load16(Zbh + (int64_t)a.G[q] * kD + lu * 8);
-        *reinterpret_cast<u32x4 LDS_AS*>(zg + q * kRowBytes +
-                                        ((lu * 16) ^ ((key_row_code(q) & 3u) << 5))) = v;
-    }
+    // Band of this wave: key columns [band_lo, band_hi], 32-aligned steps.
+    const int64_t wr_last = min(t.r0w + kRowBlock - 1, n - 1);
+    t.band_lo = (t.r0w - a.radius < 0 ? 0 : t.r0w - a.radius) & ~31ll;
+    t.band_hi = a.causal ? wr_last : min(n - 1, wr_last + a.radius);
 
-    // Schedule groups of this row block, chunk by chunk; the next chunk's
-    // groups (up to kStageGroups) travel through registers into this wave's
-    // LDS staging area.
-    char LDS_AS* stg = zg + gpad * kRowBytes + wave * kStageBytes;
+    // Schedule groups of this row block, staged chunk by chunk.
+    char LDS_AS* stg[2] = {lds + 2 * kBufBytes + (2 * wave) * kStageBytes,
+                           lds + 2 * kBufBytes + (2 * wave + 1) * kStageBytes};
     const int64_t rb = active ? t.r0w / kRowBlock : 0;
     t.cptr = a.grp_cptr + ((int64_t)gr * a.nrb + rb) * (a.nchunks + 1);
     t.goff = a.grp_off[gr];
     t.rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];   // random area of the graph
-    t.pw = t.pj = t.pr = u32x4{0u, 0u, 0u, 0u};
-    if (active) {
-        fetch_groups(t, a, Abh, 0, lane);
-        store_groups(t, stg, min(uniform_load(t.cptr + 1) - uniform_load(t.cptr), kStageGroups),
-                     lane);
-    }
-
-    // Band of this wave: key columns [band_lo, band_hi], 32 at a time; the
-    // weights of the next step are always in flight.
-    const int64_t wr_last = min(t.r0w + kRowBlock - 1, n - 1);
-    const int64_t band_lo = (t.r0w - a.radius < 0 ? 0 : t.r0w - a.radius) & ~31ll;
-    t.band_hi = a.causal ? wr_last : min(n - 1, wr_last + a.radius);
-    t.kc_next = band_lo;
-    t.band_next = band_weights(t, Abh, band_lo);
 
     dma_chunk(buf[0], Zbh, n, 0, wave, lane);
+    if (active) dma_groups(t, a, Abh, stg[0], 0, lane);
     f32x4 acc[kNB];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    full_barrier();   // globals staged, chunk 0 in LDS
-
-    // Global columns.
-    if (active) {
-        const uint32_t gb1 = code_addr(key_row_code(8u * kg + q4), a4);
-        const uint32_t gb2 = code_addr(key_row_code(8u * kg + 4u + q4), a4);
-        for (int q = 0; q < gpad; q += 32) {
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (t.rok && q + 8 * kg < t.ri.w) w = load16(Abh + t.ri.x + t.ri.z + q + 8 * kg);
-            mfma4(acc, zg, gb1 + q * kRowBytes, gb2 + q * kRowBytes, w);
-        }
-    }
 
     for (int c = 0; c < a.nchunks; ++c) {
-        if (c > 0) full_barrier();   // chunk c in LDS, chunk c - 1 done by every wave
+        full_barrier();   // chunk c in LDS, chunk c - 1 done by every wave
         if (active) {
-            tile_chunk(t, acc, a, Abh, Zbh, buf[(c + 1) & 1], buf[c & 1], stg, c, wave, lane);
+            tile_chunk(t, acc, a, Abh, Zbh, buf[(c + 1) & 1], buf[c & 1], stg[(c + 1) & 1],
+                       stg[c & 1], c, wave, lane);
         } else if (c + 1 < a.nchunks) {
             dma_chunk(buf[(c + 1) & 1], Zbh, n, (int64_t)(c + 1) * kChunkRows, wave, lane);
         }
@@ -445,7 +469,6 @@ void k_diffuse_sched(FastArgs a) {
 
 bool fast_diffuse_supported(const diffuser_graph& g, const attn_shape& s) {
     if (!g.structured || !g.scheduled || s.dtype != DIFFUSER_BF16 || s.d != kD) return false;
-    if (g.num_global > kMaxGlobal) return false;
     for (int64_t x : g.slots)
         if (x >= (1ll << 31)) return false;
     return true;
@@ -467,6 +490,7 @@ hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, con
     a.seg_ptr = g.d_seg_ptr;
     a.row_info = reinterpret_cast<const int4*>(g.d_row_info);
     a.G = g.d_global;
+    a.gchunk = g.d_gchunk;
     a.grp_ptr = g.d_grp_ptr;
     a.grp_off = g.d_grp_off;
     a.grp_cptr = g.d_grp_cptr;
@@ -490,8 +514,7 @@ hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, con
         if (e != hipSuccess) return e;
         attr_device = g.device;
     }
-    const size_t lds = (size_t)2 * kBufBytes + (size_t)((g.num_global + 31) & ~31) * kRowBytes +
-                       (size_t)kWaves * kStageBytes;
+    const size_t lds = kLdsBytes;
     hipLaunchKernelGGL(k_diffuse_sched, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), lds, st,
                        a);
     return hipGetLastError();

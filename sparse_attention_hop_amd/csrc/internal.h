@@ -72,6 +72,7 @@ struct diffuser_graph {
 
     // Generator metadata (structured graphs).
     int32_t* d_global = nullptr;    // [num_global]
+    int32_t* d_gchunk = nullptr;    // [nchunks + 1] globals below key row kChunkRows * c
     int32_t* d_rnd = nullptr;       // [num_graphs][n][rnd_width] ascending
     int32_t* d_rnd_cnt = nullptr;   // [num_graphs][n] random columns kept per row
     int32_t* d_rslot = nullptr;     // [num_graphs][n][rnd_width] slot of each kept random edge

@@ -30,6 +30,12 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Direct global-to-LDS load of 16 bytes per active lane: lane l writes its
+// 16 bytes at lds + 16 l (lds wave-uniform, src 16-byte aligned).
+__device__ __forceinline__ void dma16(const void* src, void LDS_AS* lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
 // Load of a wave-uniform int32 of read-only graph data through the scalar
 // cache (the constant address space).
 __device__ __forceinline__ int32_t uniform_load(const int32_t* p) {
