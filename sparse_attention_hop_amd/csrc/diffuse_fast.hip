@@ -79,23 +79,27 @@ struct FastArgs {
     int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items;
 };
 
-// Byte address, within a buffer, of the 8 bytes lane `a4` reads from key
-// row `code` (a key_row_code) for channel block 0; XOR with nb << 5 selects
-// channel block nb.
-__device__ __forceinline__ uint32_t code_addr(uint32_t code, uint32_t a4) {
-    return code * 32u + 8u * a4;
+__device__ __forceinline__ uint32_t lds_addr(const char LDS_AS* p) {
+    return (uint32_t)(uintptr_t)p;
 }
 
-__device__ __forceinline__ i16x4 tr_read(const char LDS_AS* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)p);
+__device__ __forceinline__ i16x4 tr_read(uint32_t addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(uintptr_t)addr);
 }
 
-// Z^T operand of channel block nb: key rows at b1 (k = 8 kg + 0..3) and b2
-// (k = 8 kg + 4..7) of buffer `buf`.
-__device__ __forceinline__ bf16x8 z_operand(const char LDS_AS* buf, uint32_t b1, uint32_t b2,
-                                            int nb) {
-    const i16x4 lo = tr_read(buf + (b1 ^ ((uint32_t)nb << 5)));
-    const i16x4 hi = tr_read(buf + (b2 ^ ((uint32_t)nb << 5)));
+// LDS address of the 8 bytes lane `a4` reads from the key row with
+// key_row_code `code` of the buffer at `base` (128-byte aligned), for
+// channel block 0; XOR with nb << 5 selects channel block nb (the XOR only
+// touches address bits 5 and 6, which neither the base nor 8 a4 sets).
+__device__ __forceinline__ uint32_t code_addr(uint32_t base_a4, uint32_t code) {
+    return base_a4 + (code << 5);
+}
+
+// Z^T operand of channel block nb: key rows at addresses r1 (k = 8 kg +
+// 0..3) and r2 (k = 8 kg + 4..7).
+__device__ __forceinline__ bf16x8 z_operand(uint32_t r1, uint32_t r2, int nb) {
+    const i16x4 lo = tr_read(r1 ^ ((uint32_t)nb << 5));
+    const i16x4 hi = tr_read(r2 ^ ((uint32_t)nb << 5));
     const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
     return __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], h[0], h[1]});
 }
@@ -104,29 +108,47 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const u32x4& b, const f32
     return mfma_bf16(__builtin_bit_cast(u32x4, a), b, c);
 }
 
-// acc[nb] += Z^T(b1, b2) W^T for the four channel blocks.
-__device__ __forceinline__ void mfma4(f32x4 (&acc)[kNB], const char LDS_AS* buf, uint32_t b1,
-                                      uint32_t b2, const u32x4& w) {
+// acc[nb] += Z^T(r1, r2) W^T for the four channel blocks.
+__device__ __forceinline__ void mfma4(f32x4 (&acc)[kNB], uint32_t r1, uint32_t r2,
+                                      const u32x4& w) {
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(buf, b1, b2, nb), w, acc[nb]);
+    for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(r1, r2, nb), w, acc[nb]);
 }
 
-// Direct loads of chunk rows [c0, c0 + kChunkRows) of Z_k into `buf`: wave w
-// fills 1 KB blocks 4w .. 4w+3 (8 rows each); lane l of a block writes 16
-// bytes at block + 16 l, which is 16-byte unit l % 8 of row l / 8, holding
-// the row's logical unit (l % 8) ^ (2 sw). Rows at or beyond n repeat row
-// n - 1 (their weights are zero).
-__device__ __forceinline__ void dma_chunk(char LDS_AS* buf, const uint16_t* Zbh, int64_t n,
-                                          int64_t c0, int wave, int lane) {
+// Per-lane byte offsets, within a chunk of Z_k rows, of the 16 bytes each of
+// this lane's four direct loads fetches: in LDS block 4 w + j (8 rows, 1 KB)
+// lane l writes 16-byte unit l % 8 of row l / 8, which holds the row's
+// logical unit (l % 8) ^ (2 sw), sw the row's quarter swizzle.
+struct ChunkLanes {
+    uint32_t off[4];
+};
+
+__device__ __forceinline__ ChunkLanes chunk_lanes(int wave, int lane) {
+    ChunkLanes cl;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int blk = 4 * wave + t;
-        const uint32_t pr = (uint32_t)(blk * 8 + (lane >> 3));
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t pr = (uint32_t)((4 * wave + j) * 8 + (lane >> 3));
         const uint32_t lu = (uint32_t)(lane & 7) ^ ((key_row_code(pr) & 3u) << 1);
-        int64_t src = c0 + pr;
-        src = src < n ? src : n - 1;
-        __builtin_amdgcn_global_load_lds(Zbh + src * kD + lu * 8, (void LDS_AS*)(buf + blk * 1024),
-                                         16, 0, 0);
+        cl.off[j] = pr * kRowBytes + lu * 16;
+    }
+    return cl;
+}
+
+// Direct loads of chunk rows [c0, c0 + kChunkRows) of Z_k into `buf`. Rows
+// at or beyond n repeat row n - 1 (their weights are zero).
+__device__ __forceinline__ void dma_chunk(char LDS_AS* buf, const uint16_t* Zbh, int64_t n,
+                                          int64_t c0, const ChunkLanes& cl, int wave) {
+    const char* src = reinterpret_cast<const char*>(Zbh + c0 * kD);
+    if (c0 + kChunkRows <= n) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(src + cl.off[j], buf + (4 * wave + j) * 1024);
+    } else {
+        const uint32_t last = (uint32_t)(n - 1 - c0) * kRowBytes;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t o = cl.off[j] < last + kRowBytes ? cl.off[j] : last | (cl.off[j] & 127u);
+            dma16(src + o, buf + (4 * wave + j) * 1024);
+        }
     }
 }
 
@@ -149,20 +171,10 @@ __device__ __forceinline__ void store_row(const FastArgs& a, int32_t bh, int64_t
     }
 }
 
-// Weight operand of a schedule group for the lanes of row `row` (0..15):
-// pair p of words w keeps its two weights where the pair's row (low 7 bits
-// of its byte) matches.
-__device__ __forceinline__ u32x4 group_weights(const u32x4& w, uint32_t rows, uint32_t row) {
-    u32x4 b;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) b[p] = ((rows >> (8 * p)) & 0x7fu) == row ? w[p] : 0u;
-    return b;
-}
-
 // Per-lane state of a row-tile wave.
 struct TileLane {
     int kg, s16;
-    uint32_t a4, q4;
+    uint32_t a8, q4;         // 8 (lane % 4) and the transposed-read source row
     int4 ri;                 // row info of row r0w + s16
     bool rok;
     int64_t r0w, band_lo, band_hi;
@@ -199,11 +211,38 @@ __device__ __forceinline__ void dma_groups(const TileLane& t, const FastArgs& a,
                                            const uint16_t* Abh, char LDS_AS* stg, int c, int lane) {
     const int32_t g0 = uniform_load(t.cptr + c);
     const int32_t cnt = min(uniform_load(t.cptr + c + 1) - g0, kStageGroups);
+    const uint32_t l16 = 16u * (uint32_t)lane;
     if (lane < 4 * cnt) {
-        dma16(Abh + t.rbase + (int64_t)kGroupSlots * g0 + 8 * lane, stg);
-        dma16(a.sched_j + (t.goff + g0) * 16 + 4 * lane, stg + kStageJ);
+        dma16(reinterpret_cast<const char*>(Abh + t.rbase + (int64_t)kGroupSlots * g0) + l16, stg);
+        dma16(reinterpret_cast<const char*>(a.sched_j + (t.goff + g0) * 16) + l16, stg + kStageJ);
     }
-    if (lane < cnt) dma16(a.sched_row + (t.goff + g0 + lane) * 4, stg + kStageR);
+    if (lane < cnt)
+        dma16(reinterpret_cast<const char*>(a.sched_row + (t.goff + g0) * 4) + l16, stg + kStageR);
+}
+
+// One schedule group as this lane uses it: the 8 weights of its k-group,
+// the key-row codes of its two transposed reads, the rows of its 4 pairs.
+struct GroupLane {
+    u32x4 w;
+    uint32_t j, r;
+};
+
+__device__ __forceinline__ GroupLane group_lane(const TileLane& t, const FastArgs& a,
+                                                const uint16_t* Abh, const char LDS_AS* stg,
+                                                int32_t g0, int k) {
+    GroupLane gl;
+    if (k < kStageGroups) {
+        gl.w = *reinterpret_cast<const u32x4 LDS_AS*>(stg + 64 * k + 16 * t.kg);
+        gl.j = *reinterpret_cast<const uint32_t LDS_AS*>(stg + kStageJ + 64 * k +
+                                                         4 * (4 * t.kg + t.q4));
+        gl.r = *reinterpret_cast<const uint32_t LDS_AS*>(stg + kStageR + 16 * k + 4 * t.kg);
+    } else {
+        const int64_t gi = g0 + k;
+        gl.w = load16(Abh + t.rbase + (int64_t)kGroupSlots * gi + 8 * t.kg);
+        gl.j = a.sched_j[(t.goff + gi) * 16 + 4 * t.kg + t.q4];
+        gl.r = a.sched_row[(t.goff + gi) * 4 + t.kg];
+    }
+    return gl;
 }
 
 // One key chunk of a row-tile wave, with chunk c's Z_k rows in `cur` and its
@@ -214,13 +253,14 @@ __device__ __forceinline__ void dma_groups(const TileLane& t, const FastArgs& a,
 // the loads into `nxt` and `nstg` are in flight.
 __device__ __forceinline__ void tile_chunk(const TileLane& t, f32x4 (&acc)[kNB], const FastArgs& a,
                                            const uint16_t* Abh, const uint16_t* Zbh,
-                                           char LDS_AS* __restrict__ nxt,
+                                           const ChunkLanes& cl, char LDS_AS* __restrict__ nxt,
                                            const char LDS_AS* __restrict__ cur,
                                            char LDS_AS* __restrict__ nstg,
                                            const char LDS_AS* __restrict__ stg, int c, int wave,
                                            int lane) {
     const int64_t c0 = (int64_t)c * kChunkRows;
     const bool more = c + 1 < a.nchunks;
+    const uint32_t base = lds_addr(cur) + t.a8;
 
     // Dense steps of this chunk: global steps [gs0, gs1), band steps from kb0
     // to kb1 (32-column steps inside the chunk).
@@ -245,59 +285,55 @@ __device__ __forceinline__ void tile_chunk(const TileLane& t, f32x4 (&acc)[kNB],
         if (i < nbs) bw[i] = band_weights(t, Abh, kb0 + 32 * i);
 
     if (more) {
-        dma_chunk(nxt, Zbh, a.n, c0 + kChunkRows, wave, lane);
+        dma_chunk(nxt, Zbh, a.n, c0 + kChunkRows, cl, wave);
         dma_groups(t, a, Abh, nstg, c + 1, lane);
     }
 
-    // Random groups (staged ones from LDS, any others from memory).
+    // Random groups; each group's staged words are read one group ahead.
     const int32_t g0 = uniform_load(t.cptr + c);
     const int32_t gcnt = uniform_load(t.cptr + c + 1) - g0;
+    GroupLane nx;
+    if (gcnt > 0) nx = group_lane(t, a, Abh, stg, g0, 0);
     for (int32_t k = 0; k < gcnt; ++k) {
-        uint32_t cj, crows;
-        u32x4 cw;
-        if (k < kStageGroups) {
-            cw = *reinterpret_cast<const u32x4 LDS_AS*>(stg + 64 * k + 16 * t.kg);
-            cj = *reinterpret_cast<const uint32_t LDS_AS*>(stg + kStageJ + 64 * k +
-                                                           4 * (4 * t.kg + t.q4));
-            crows = *reinterpret_cast<const uint32_t LDS_AS*>(stg + kStageR + 16 * k + 4 * t.kg);
-        } else {
-            const int64_t gi = g0 + k;
-            cw = load16(Abh + t.rbase + (int64_t)kGroupSlots * gi + 8 * t.kg);
-            cj = a.sched_j[(t.goff + gi) * 16 + 4 * t.kg + t.q4];
-            crows = a.sched_row[(t.goff + gi) * 4 + t.kg];
-        }
-        const u32x4 w = group_weights(cw, crows, (uint32_t)t.s16);
-        mfma4(acc, cur, code_addr(cj & 0xffffu, t.a4), code_addr(cj >> 16, t.a4), w);
+        const GroupLane gl = nx;
+        if (k + 1 < gcnt) nx = group_lane(t, a, Abh, stg, g0, k + 1);
+        // Pair p of the lane's k-group keeps its two weights when its row
+        // (the low 7 bits of byte p) is the lane's row.
+        const uint32_t rm = gl.r & 0x7f7f7f7fu;
+        u32x4 w;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) w[p] = ((rm >> (8 * p)) & 0xffu) == (uint32_t)t.s16 ? gl.w[p] : 0u;
+        mfma4(acc, code_addr(base, gl.j & 0xffffu), code_addr(base, gl.j >> 16), w);
     }
 
     // Global steps.
 #pragma unroll
     for (int i = 0; i < kMaxGlob; ++i) {
         if (gs0 + i < gs1)
-            mfma4(acc, cur, code_addr(key_row_code(gr1[i]), t.a4),
-                  code_addr(key_row_code(gr2[i]), t.a4), gw[i]);
+            mfma4(acc, code_addr(base, key_row_code(gr1[i])), code_addr(base, key_row_code(gr2[i])),
+                  gw[i]);
     }
     for (int s = gs0 + kMaxGlob; s < gs1; ++s) {
         const int qa = 32 * s + 8 * t.kg + t.q4;
-        mfma4(acc, cur, code_addr(key_row_code(glob_row(a, qa, q0, q1, c0)), t.a4),
-              code_addr(key_row_code(glob_row(a, qa + 4, q0, q1, c0)), t.a4),
+        mfma4(acc, code_addr(base, key_row_code(glob_row(a, qa, q0, q1, c0))),
+              code_addr(base, key_row_code(glob_row(a, qa + 4, q0, q1, c0))),
               glob_weights(t, Abh, s));
     }
 
     // Window band.
-    const uint32_t bb1 = code_addr(key_row_code(8u * t.kg + t.q4), t.a4);
-    const uint32_t bb2 = code_addr(key_row_code(8u * t.kg + 4u + t.q4), t.a4);
+    const uint32_t bb1 = code_addr(base, key_row_code(8u * t.kg + t.q4));
+    const uint32_t bb2 = code_addr(base, key_row_code(8u * t.kg + 4u + t.q4));
 #pragma unroll
     for (int i = 0; i < kMaxBand; ++i) {
         if (i < nbs) {
             const uint32_t off = (uint32_t)(kb0 + 32 * i - c0) * kRowBytes;  // 32-row multiple
-            mfma4(acc, cur, bb1 + off, bb2 + off, bw[i]);
+            mfma4(acc, bb1 + off, bb2 + off, bw[i]);
         }
     }
     for (int i = kMaxBand; i < nbs; ++i) {
         const int64_t kc = kb0 + 32 * i;
         const uint32_t off = (uint32_t)(kc - c0) * kRowBytes;
-        mfma4(acc, cur, bb1 + off, bb2 + off, band_weights(t, Abh, kc));
+        mfma4(acc, bb1 + off, bb2 + off, band_weights(t, Abh, kc));
     }
 }
 
@@ -305,15 +341,16 @@ __device__ __forceinline__ void tile_chunk(const TileLane& t, f32x4 (&acc)[kNB],
 // c + 1 into `nxt` and multiplies keys c0 + 32 w .. + 31 of `cur`.
 __device__ __forceinline__ void grow_chunk(f32x4 (&acc)[2][kNB], const u32x4 (&w)[2],
                                            const uint16_t* Zbh, int64_t n, int nchunks,
-                                           char LDS_AS* __restrict__ nxt,
+                                           const ChunkLanes& cl, char LDS_AS* __restrict__ nxt,
                                            const char LDS_AS* __restrict__ cur, int c, int wave,
-                                           int lane, uint32_t b1, uint32_t b2) {
+                                           uint32_t b1, uint32_t b2) {
     const int64_t c0 = (int64_t)c * kChunkRows;
-    if (c + 1 < nchunks) dma_chunk(nxt, Zbh, n, c0 + kChunkRows, wave, lane);
+    if (c + 1 < nchunks) dma_chunk(nxt, Zbh, n, c0 + kChunkRows, cl, wave);
     if (c0 + 32 * wave < n) {
+        const uint32_t base = lds_addr(cur);
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
-            const bf16x8 zop = z_operand(cur, b1, b2, nb);
+            const bf16x8 zop = z_operand(base + b1, base + b2, nb);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma(zop, w[mb], acc[mb][nb]);
         }
@@ -322,13 +359,13 @@ __device__ __forceinline__ void grow_chunk(f32x4 (&acc)[2][kNB], const u32x4 (&w
 
 __global__ __launch_bounds__(kThreads)
 void k_diffuse_sched(FastArgs a) {
-    extern __shared__ __align__(16) char lds_raw[];
+    extern __shared__ __align__(128) char lds_raw[];
     char LDS_AS* lds = (char LDS_AS*)lds_raw;
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int kg = lane >> 4;          // k-group of the MFMA operands
     const int s16 = lane & 15;         // row (W^T) / channel (Z^T) index
-    const uint32_t a4 = lane & 3, q4 = (lane >> 2) & 3;   // transposed-read source
+    const uint32_t a8 = 8u * (lane & 3), q4 = (lane >> 2) & 3;   // transposed-read source
 
     const int32_t item = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
     if (item >= a.total_items) return;
@@ -342,6 +379,7 @@ void k_diffuse_sched(FastArgs a) {
     const uint16_t* Zbh = a.Z + (int64_t)bh * n * kD;
     const int4* info = a.row_info + (int64_t)gr * n;
     char LDS_AS* buf[2] = {lds, lds + kBufBytes};
+    const ChunkLanes cl = chunk_lanes(wave, lane);
 
     // Zero row kChunkRows of both buffers (the key row of dummy slots).
     if (threadIdx.x < 16) {
@@ -380,15 +418,14 @@ void k_diffuse_sched(FastArgs a) {
             for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         u32x4 w[2], wn[2];
         fetch_w(w, 32 * wave);
-        dma_chunk(buf[0], Zbh, n, 0, wave, lane);
-        const uint32_t b1 = code_addr(key_row_code(32u * wave + 8u * kg + q4), a4);
-        const uint32_t b2 = code_addr(key_row_code(32u * wave + 8u * kg + 4u + q4), a4);
+        dma_chunk(buf[0], Zbh, n, 0, cl, wave);
+        const uint32_t b1 = code_addr(a8, key_row_code(32u * wave + 8u * kg + q4));
+        const uint32_t b2 = code_addr(a8, key_row_code(32u * wave + 8u * kg + 4u + q4));
         for (int c = 0; c < a.nchunks; ++c) {
             const int64_t c0 = (int64_t)c * kChunkRows;
             full_barrier();   // chunk c in LDS
             if (c + 1 < a.nchunks) fetch_w(wn, c0 + kChunkRows + 32 * wave);
-            grow_chunk(acc, w, Zbh, n, a.nchunks, buf[(c + 1) & 1], buf[c & 1], c, wave, lane, b1,
-                       b2);
+            grow_chunk(acc, w, Zbh, n, a.nchunks, cl, buf[(c + 1) & 1], buf[c & 1], c, wave, b1, b2);
             w[0] = wn[0];
             w[1] = wn[1];
         }
@@ -424,7 +461,7 @@ void k_diffuse_sched(FastArgs a) {
     TileLane t;
     t.kg = kg;
     t.s16 = s16;
-    t.a4 = a4;
+    t.a8 = a8;
     t.q4 = q4;
     t.r0w = (int64_t)(sub - a.grow_per_bh) * kTileRows + (int64_t)kRowBlock * wave;
     const bool active = t.r0w < n;
@@ -446,7 +483,7 @@ void k_diffuse_sched(FastArgs a) {
     t.goff = a.grp_off[gr];
     t.rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];   // random area of the graph
 
-    dma_chunk(buf[0], Zbh, n, 0, wave, lane);
+    dma_chunk(buf[0], Zbh, n, 0, cl, wave);
     if (active) dma_groups(t, a, Abh, stg[0], 0, lane);
     f32x4 acc[kNB];
 #pragma unroll
@@ -455,10 +492,10 @@ void k_diffuse_sched(FastArgs a) {
     for (int c = 0; c < a.nchunks; ++c) {
         full_barrier();   // chunk c in LDS, chunk c - 1 done by every wave
         if (active) {
-            tile_chunk(t, acc, a, Abh, Zbh, buf[(c + 1) & 1], buf[c & 1], stg[(c + 1) & 1],
+            tile_chunk(t, acc, a, Abh, Zbh, cl, buf[(c + 1) & 1], buf[c & 1], stg[(c + 1) & 1],
                        stg[c & 1], c, wave, lane);
         } else if (c + 1 < a.nchunks) {
-            dma_chunk(buf[(c + 1) & 1], Zbh, n, (int64_t)(c + 1) * kChunkRows, wave, lane);
+            dma_chunk(buf[(c + 1) & 1], Zbh, n, (int64_t)(c + 1) * kChunkRows, cl, wave);
         }
     }
 
