@@ -17,15 +17,25 @@
 //    score is kept by the lane of its pair's row.
 // A workgroup (16 waves, 16 rows each) streams K of its (batch, head)
 // through LDS in chunks of kChunkRows rows with direct global-to-LDS loads,
-// double-buffered, once per pass:
-//   pass 1: the row maxima (of the unscaled dot products);
-//   fused mode: pass 2 writes w_ij = exp(s_ij - m_i) unnormalised and c_i =
-//     1 / (sum of the stored w_ij), which the diffusion step applies;
-//   normalised mode: pass 2 sums w_ij, pass 3 writes w_ij / sum.
+// double-buffered, once per pass. The shift m_i of the exponentials can be
+// any value: exp(s - m) / sum exp(s - m) does not depend on it, and any m_i
+// at most the row maximum keeps every weight at least as large as with the
+// maximum itself (no extra underflow). The kernel takes m_i = the maximum
+// over the row's window and global columns, scored in a prologue from a
+// band window of K staged next to the first chunk; a random score above it
+// only makes a weight exceed one. A row whose stored weights sum to 2^64 or
+// more (a random score far above the window) is redone with the exact
+// maximum from a full pass, so the weights never overflow.
+//   fused mode: one pass writes w_ij = exp(s_ij - m_i) unnormalised and c_i
+//     = 1 / (sum of the stored w_ij), which the diffusion step applies;
+//   normalised mode: one pass sums w_ij, a second writes w_ij / sum.
+// Without room for the band window (a large radius), m_i is the exact row
+// maximum from a first full pass.
 // exp(s - m) is evaluated as exp2(x * log2(e) / sqrt(d_h) - m'), x the dot
 // product and m' the scaled maximum. Global rows (full rows of length n)
 // get workgroups of their own: 32 rows, the 16 waves split each chunk's
-// keys and merge their partial maxima and sums in a fixed order. K rows sit
+// keys and merge their partial maxima and sums in a fixed order; their
+// shift is the maximum over the first chunk's keys. K rows sit
 // in LDS at 128 bytes, 16-byte units permuted by score_row_code, which
 // spreads the 16 rows of one operand read over the banks.
 #include "internal.h"
@@ -51,6 +61,10 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(2 * kWaves * kGrowRows * 4 <= 2 * kBufBytes, "grow merge fits");
 
 enum Pass { kPassMax = 0, kPassWriteFused = 1, kPassSum = 2, kPassWriteNorm = 3 };
+// A row whose weights (shifted by less than its maximum) sum to this or
+// more is redone with its exact maximum: every weight then stays far from
+// the float and bf16 overflow threshold (2^128), and so does the sum.
+constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
 
 struct ScoreArgs {
     int32_t n, H, num_graphs, radius, g, causal, nchunks, nrb;
@@ -68,6 +82,7 @@ struct ScoreArgs {
     float* row_scale;           // [B*H][n] (fused mode)
     float scale_log2;           // log2(e) / sqrt(d_h)
     int32_t normalized;
+    int32_t band_prepass;       // the band window of a row tile fits one buffer
     int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items;
 };
 
@@ -312,17 +327,12 @@ __device__ __forceinline__ void tile_globals(SLane& t, const ScoreArgs& a, uint1
     }
 }
 
-template <int P>
-__device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uint16_t* Abh,
-                          char LDS_AS* lds, int gpad, bool active, int wave, int lane) {
-    char LDS_AS* buf0 = lds;
-    char LDS_AS* buf1 = lds + kBufBytes;
-    char LDS_AS* zg = lds + 2 * kBufBytes;
-    const int32_t LDS_AS* gidx = (const int32_t LDS_AS*)(zg + gpad * kRowBytes);
-    char LDS_AS* stg = zg + gpad * (kRowBytes + 4) + wave * kStageBytes;
-
-    // Stage chunk 0 and its groups.
-    dma_chunk(buf0, Kbh, a.n, 0, wave, lane);
+// Direct loads of chunk 0 into buffer 0 and of the wave's first staged
+// groups.
+__device__ __forceinline__ void stage_first(const SLane& t, const ScoreArgs& a,
+                                            const uint16_t* Kbh, char LDS_AS* lds,
+                                            char LDS_AS* stg, bool active, int wave, int lane) {
+    dma_chunk(lds, Kbh, a.n, 0, wave, lane);
     if (active) {
         const int32_t g0 = uniform_load(t.cptr);
         const int32_t cnt = min(uniform_load(t.cptr + 1) - g0, kStageGroups);
@@ -335,7 +345,24 @@ __device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uin
                 a.sched_row[(t.goff + g0) * 4 + lane];
         }
     }
-    full_barrier();
+}
+
+// One pass of a row-tile wave; `prestaged`: chunk 0 and its groups are
+// already in LDS (and the barrier after their loads has passed).
+template <int P>
+__device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uint16_t* Abh,
+                          char LDS_AS* lds, int gpad, bool active, int wave, int lane,
+                          bool prestaged) {
+    char LDS_AS* buf0 = lds;
+    char LDS_AS* buf1 = lds + kBufBytes;
+    char LDS_AS* zg = lds + 2 * kBufBytes;
+    const int32_t LDS_AS* gidx = (const int32_t LDS_AS*)(zg + gpad * kRowBytes);
+    char LDS_AS* stg = zg + gpad * (kRowBytes + 4) + wave * kStageBytes;
+
+    if (!prestaged) {
+        stage_first(t, a, Kbh, lds, stg, active, wave, lane);
+        full_barrier();
+    }
     if (active) tile_globals<P>(t, a, Abh, zg, gidx, gpad);
     for (int c = 0; c < a.nchunks; ++c) {
         if (c > 0) full_barrier();
@@ -377,9 +404,9 @@ template <int P>
 __device__ __forceinline__ void grow_chunk(GLane& t, const ScoreArgs& a, const uint16_t* Kbh,
                                            uint16_t* Abh, char LDS_AS* __restrict__ nxt,
                                            const char LDS_AS* __restrict__ cur, int c, int wave,
-                                           int lane) {
+                                           int lane, bool prefetch = true) {
     const int32_t c0 = c * kChunkRows;
-    if (c + 1 < a.nchunks) dma_chunk(nxt, Kbh, a.n, c0 + kChunkRows, wave, lane);
+    if (prefetch && c + 1 < a.nchunks) dma_chunk(nxt, Kbh, a.n, c0 + kChunkRows, wave, lane);
     if (c0 + 32 * wave >= a.n) return;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -504,24 +531,45 @@ void k_scores_sched(ScoreArgs a) {
             t.sum[mb] = 0.0f;
             t.inv[mb] = 0.0f;
         }
-        grow_pass<kPassMax>(t, a, Kbh, Abh, lds, wave, lane);
+        // Shift: the maximum over the keys of chunk 0.
+        dma_chunk(lds, Kbh, a.n, 0, wave, lane);
+        full_barrier();
+        grow_chunk<kPassMax>(t, a, Kbh, Abh, lds + kBufBytes, lds, 0, wave, lane, false);
+        full_barrier();
         grow_merge<true>(t.m, lds, wave, lane);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) t.ms[mb] = t.m[mb] * a.scale_log2;
-        if (a.normalized) {
-            grow_pass<kPassSum>(t, a, Kbh, Abh, lds, wave, lane);
+        for (int attempt = 0; attempt < 2; ++attempt) {
+            if (attempt == 1) {
+                // Some row's weights reached 2^64: the exact maxima instead.
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    t.m[mb] = -INFINITY;
+                    t.sum[mb] = 0.0f;
+                }
+                grow_pass<kPassMax>(t, a, Kbh, Abh, lds, wave, lane);
+                grow_merge<true>(t.m, lds, wave, lane);
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) t.ms[mb] = t.m[mb] * a.scale_log2;
+            }
+            if (a.normalized) {
+                grow_pass<kPassSum>(t, a, Kbh, Abh, lds, wave, lane);
+            } else {
+                grow_pass<kPassWriteFused>(t, a, Kbh, Abh, lds, wave, lane);
+            }
             grow_merge<false>(t.sum, lds, wave, lane);
+            const bool big = (t.i[0] >= 0 && !(t.sum[0] < kSumLimit)) ||
+                             (t.i[1] >= 0 && !(t.sum[1] < kSumLimit));
+            if (attempt == 1 || !__syncthreads_or(big)) break;
+        }
+        if (a.normalized) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) t.inv[mb] = t.i[mb] >= 0 ? 1.0f / t.sum[mb] : 0.0f;
             grow_pass<kPassWriteNorm>(t, a, Kbh, Abh, lds, wave, lane);
-        } else {
-            grow_pass<kPassWriteFused>(t, a, Kbh, Abh, lds, wave, lane);
-            grow_merge<false>(t.sum, lds, wave, lane);
-            if (a.row_scale != nullptr && wave == 0 && kg == 0) {
+        } else if (a.row_scale != nullptr && wave == 0 && kg == 0) {
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-                    if (t.i[mb] >= 0) a.row_scale[(int64_t)bh * n + t.i[mb]] = 1.0f / t.sum[mb];
-            }
+            for (int mb = 0; mb < 2; ++mb)
+                if (t.i[mb] >= 0) a.row_scale[(int64_t)bh * n + t.i[mb]] = 1.0f / t.sum[mb];
         }
         return;
     }
@@ -560,7 +608,7 @@ void k_scores_sched(ScoreArgs a) {
     // Staged global rows of K and their positions.
     const int gpad = (a.g + 31) & ~31;
     char LDS_AS* zg = lds + 2 * kBufBytes;
-    int32_t LDS_AS* gidx = (int32_t LDS_AS*)(zg + gpad * kRowBytes);
+    const int32_t LDS_AS* gidx = (const int32_t LDS_AS*)(zg + gpad * kRowBytes);
     for (int idx = threadIdx.x; idx < gpad * 8; idx += kThreads) {
         const int q = idx >> 3, lu = idx & 7;
         u32x4 v = {0u, 0u, 0u, 0u};
@@ -568,21 +616,55 @@ void k_scores_sched(ScoreArgs a) {
         *reinterpret_cast<u32x4 LDS_AS*>(zg + ((score_row_code((uint32_t)q) ^ (uint32_t)lu) << 4)) =
             v;
     }
-    for (int q = threadIdx.x; q < gpad; q += kThreads) gidx[q] = q < a.g ? a.G[q] : 0;
+    for (int q = threadIdx.x; q < gpad; q += kThreads)
+        ((int32_t LDS_AS*)gidx)[q] = q < a.g ? a.G[q] : 0;
 
-    tile_pass<kPassMax>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
+    char LDS_AS* stg = zg + gpad * (kRowBytes + 4) + wave * kStageBytes;
+    bool prestaged = false;
+    if (a.band_prepass) {
+        // Shift: the maximum over the window and global columns, from the
+        // band window of the tile's rows staged in buffer 1.
+        const int32_t tile_r0 = (sub - a.grow_per_bh) * kTileRows;
+        const int32_t bw0 = max(tile_r0 - a.radius, 0) & ~15;
+        stage_first(t, a, Kbh, lds, stg, active, wave, lane);
+        dma_chunk(lds + kBufBytes, Kbh, n, bw0, wave, lane);
+        full_barrier();
+        if (active) {
+            for (int32_t kb = t.band_lo; kb <= t.band_hi; kb += 16)
+                band_tile<kPassMax>(t, a, Abh, lds + kBufBytes, kb, bw0);
+            tile_globals<kPassMax>(t, a, Abh, zg, gidx, gpad);
+        }
+        lds_barrier();   // buffer 1 is free again
+        prestaged = true;
+    } else {
+        tile_pass<kPassMax>(t, a, Kbh, Abh, lds, gpad, active, wave, lane, false);
+    }
     t.m = row_max(t.m);
     t.ms = t.m * a.scale_log2;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        if (attempt == 1) {
+            // Some row's weights reached 2^64: the exact maxima instead.
+            t.m = -INFINITY;
+            tile_pass<kPassMax>(t, a, Kbh, Abh, lds, gpad, active, wave, lane, false);
+            t.m = row_max(t.m);
+            t.ms = t.m * a.scale_log2;
+            t.sum = 0.0f;
+        }
+        if (a.normalized) {
+            tile_pass<kPassSum>(t, a, Kbh, Abh, lds, gpad, active, wave, lane, prestaged);
+        } else {
+            tile_pass<kPassWriteFused>(t, a, Kbh, Abh, lds, gpad, active, wave, lane, prestaged);
+        }
+        prestaged = false;
+        t.sum = row_sum(t.sum);
+        if (attempt == 1 || !a.band_prepass || !__syncthreads_or(t.rok && !(t.sum < kSumLimit)))
+            break;
+    }
     if (a.normalized) {
-        tile_pass<kPassSum>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
-        t.sum = row_sum(t.sum);
         t.inv = t.rok ? 1.0f / t.sum : 0.0f;   // rows without edges here write zeros only
-        tile_pass<kPassWriteNorm>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
-    } else {
-        tile_pass<kPassWriteFused>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
-        t.sum = row_sum(t.sum);
-        if (a.row_scale != nullptr && t.rok && kg == 0)
-            a.row_scale[(int64_t)bh * n + t.i] = 1.0f / t.sum;
+        tile_pass<kPassWriteNorm>(t, a, Kbh, Abh, lds, gpad, active, wave, lane, false);
+    } else if (a.row_scale != nullptr && t.rok && kg == 0) {
+        a.row_scale[(int64_t)bh * n + t.i] = 1.0f / t.sum;
     }
 }
 
@@ -622,6 +704,10 @@ hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, cons
     a.row_scale = row_scale;
     a.scale_log2 = scale_log2;
     a.normalized = normalized ? 1 : 0;
+    // The band window of a tile's rows (keys from (r0 - r) rounded down to 16
+    // through r0 + kTileRows - 1 + r) must fit one buffer.
+    const int64_t span = kTileRows - 1 + 2 * (int64_t)a.radius + (a.radius % 16 ? 15 : 0);
+    a.band_prepass = span < kChunkRows ? 1 : 0;
     const int32_t BH = s.B * s.H;
     a.tiles_per_bh = (int32_t)((g.n + kTileRows - 1) / kTileRows);
     a.grow_per_bh = (g.num_global + kGrowRows - 1) / kGrowRows;

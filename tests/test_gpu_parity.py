@@ -420,6 +420,38 @@ def test_fast_paths_deterministic(case):
         assert torch.equal(sah.attn(q, k, v, g, 5, 0.1), z0)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fast_scores_far_random_maximum(orc, causal):
+    """Rows whose maximum score is a random (or, for a global row, a
+    late-chunk) edge far above the window: the shifted weights would pass
+    2^64, so the kernel redoes those rows with their exact maximum. Head 0
+    has that structure, head 1 ordinary inputs."""
+    n, r, G, R = 1100, 20, [0, 1, 700], 40
+    g = _gpu_graph(n, r, G, R, 1, causal, 41)
+    rp, cols = _check_csr(orc, g, n, r, G, R, 1, causal, 41)
+    shape = (1, 2, n, 64)
+    q = make_tensor(shape, 91, torch.bfloat16)
+    k = make_tensor(shape, 92, torch.bfloat16)
+    v = make_tensor(shape, 93, torch.bfloat16)
+    q[0, 0] = 0
+    q[0, 0, :, 0] = 16.0
+    k[0, 0] = 0
+    k[0, 0, 900, 0] = 32.0            # score 64 for key 900, 0 for every other key
+    z = sah.attn(q.to(DEV), k.to(DEV), v.to(DEV), g, 5, 0.1)
+    A = sah.scores_softmax(q.to(DEV), k.to(DEV), g)
+    z_h, A_h = _as64(z), _as64(A)
+    rpa, ca = np.asarray(rp[0]), np.asarray(cols[0])
+    rows900 = np.repeat(np.arange(n), np.diff(rpa))[ca == 900]
+    far = [i for i in rows900 if abs(i - 900) > r and i not in G]
+    assert far, "key 900 must be a random neighbour of some row"
+    for h in range(2):
+        A_ref = orc.scores_softmax(_as64(q[0, h]), _as64(k[0, h]), rp[0], cols[0])
+        A_csr = _a_csr(g, A_h, 0, h, 2, 0, rp, cols)
+        assert np.all(np.abs(A_csr - A_ref) <= 2.0 ** -8 * A_ref + 1e-6), h
+        ref = orc.attn(_as64(q[0, h]), _as64(k[0, h]), _as64(v[0, h]), rp[0], cols[0], 5, 0.1)
+        pu.assert_z_close(z_h[0, h], ref, "bf16", f"attn h={h}", 5, 0.1)
+
+
 def _slot_classes(g, gr, n, r, G, causal):
     """Class of every weight slot of graph gr: 0 window, 1 global column,
     2 random, 3 global row, -1 padding."""
