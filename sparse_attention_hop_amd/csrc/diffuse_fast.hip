@@ -20,9 +20,11 @@
 // through LDS in chunks of kChunkRows rows, double-buffered with direct
 // global-to-LDS loads of the next chunk while the current one is used; each
 // wave's schedule groups of the next chunk travel the same way into a
-// double-buffered staging area of its own. The weights of a chunk's dense
-// steps (band and global columns) are loaded when the chunk starts and used
-// after its random groups. Rows
+// double-buffered staging area of its own. The weights of the wave's dense
+// steps (band and global columns) are loaded once, with the first chunk, and
+// used in the chunk that holds their key rows; during the last chunk the
+// tile's rows of V (and c_i) travel into the idle buffer for the restart
+// term. Rows
 // of Z_k sit in LDS at 128 bytes, quarters permuted by key_row_code, which
 // spreads the 16 rows of one transposed read over the banks.
 // Global rows get workgroups of their own (32 rows; the 16 waves split each
@@ -152,21 +154,33 @@ __device__ __forceinline__ void dma_chunk(char LDS_AS* buf, const uint16_t* Zbh,
     }
 }
 
-// Restart and store of one lane's accumulators: row `i`, channels
-// 16 nb + 4 kg .. + 3 for nb = 0..3.
-__device__ __forceinline__ void store_row(const FastArgs& a, int32_t bh, int64_t i, int kg,
-                                          const f32x4 (&acc)[kNB]) {
-    const float keep = a.row_scale ? (1.0f - a.alpha) * a.row_scale[(int64_t)bh * a.n + i]
-                                   : 1.0f - a.alpha;
+// Direct loads of the rows r0 .. r0 + 15 of V (a wave's restart inputs)
+// into `vbuf`, row j at vbuf + 128 j in order; rows at or beyond n repeat
+// row n - 1.
+__device__ __forceinline__ void dma_restart(const FastArgs& a, int32_t bh, int64_t r0,
+                                            char LDS_AS* vbuf, int lane) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t row = min(r0 + 8 * u + (lane >> 3), a.n - 1);
+        dma16(a.V + ((int64_t)bh * a.n + row) * kD + 8 * (lane & 7), vbuf + 1024 * u);
+    }
+}
+
+// Restart and store of one lane's accumulators: row `i` (row j of the
+// wave's staged restart inputs), channels 16 nb + 4 kg .. + 3 for nb = 0..3.
+__device__ __forceinline__ void store_row(const FastArgs& a, int32_t bh, int64_t i, int j, int kg,
+                                          const f32x4 (&acc)[kNB], const char LDS_AS* vbuf,
+                                          float scale) {
+    const float keep = (1.0f - a.alpha) * scale;
     const int64_t base = ((int64_t)bh * a.n + i) * kD + 4 * kg;
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(a.V + base + 16 * nb);
+        const u32x2 v = *reinterpret_cast<const u32x2 LDS_AS*>(vbuf + 128 * j + 2 * (16 * nb + 4 * kg));
         u32x2 o;
-        o[0] = to_bf16_pair(keep * acc[nb][0] + a.alpha * bf16_to_f32(v[0] & 0xffffu),
-                            keep * acc[nb][1] + a.alpha * bf16_to_f32(v[0] >> 16));
-        o[1] = to_bf16_pair(keep * acc[nb][2] + a.alpha * bf16_to_f32(v[1] & 0xffffu),
-                            keep * acc[nb][3] + a.alpha * bf16_to_f32(v[1] >> 16));
+        o[0] = to_bf16_pair(keep * acc[nb][0] + a.alpha * bf16_lo(v[0]),
+                            keep * acc[nb][1] + a.alpha * bf16_hi(v[0]));
+        o[1] = to_bf16_pair(keep * acc[nb][2] + a.alpha * bf16_lo(v[1]),
+                            keep * acc[nb][3] + a.alpha * bf16_hi(v[1]));
         *reinterpret_cast<u32x2*>(a.Zn + base + 16 * nb) = o;
     }
 }
@@ -180,6 +194,11 @@ struct TileLane {
     int64_t r0w, band_lo, band_hi;
     const int32_t* cptr;     // chunk -> first group of this row block
     int64_t goff, rbase;
+    int nbs;                 // band steps (32 columns each from band_lo)
+    u32x4 bw[kMaxBand];      // weights of the first kMaxBand band steps
+    int ngs;                 // global steps (32 global slots each)
+    u32x4 gw[kMaxGlob];      // weights of the first kMaxGlob global steps
+    int32_t gv1[kMaxGlob], gv2[kMaxGlob];   // their globals read by this lane (-1: none)
 };
 
 // Weights of the band step at key column kc (8 slots of this lane's row).
@@ -262,41 +281,25 @@ __device__ __forceinline__ void tile_chunk(const TileLane& t, f32x4 (&acc)[kNB],
     const bool more = c + 1 < a.nchunks;
     const uint32_t base = lds_addr(cur) + t.a8;
 
-    // Dense steps of this chunk: global steps [gs0, gs1), band steps from kb0
-    // to kb1 (32-column steps inside the chunk).
+    // Dense steps of this chunk: global steps [gs0, gs1), band steps
+    // [ib0, ib1] (32-column steps from band_lo inside the chunk).
     const int q0 = uniform_load(a.gchunk + c), q1 = uniform_load(a.gchunk + c + 1);
     const int gs0 = q0 >> 5, gs1 = q1 > q0 ? ((q1 - 1) >> 5) + 1 : gs0;
     const int64_t kb0 = max(t.band_lo, c0);
     const int64_t kb1 = min(t.band_hi, c0 + kChunkRows - 1);
-    const int nbs = kb0 <= kb1 ? (int)((kb1 - kb0) >> 5) + 1 : 0;
-    u32x4 gw[kMaxGlob], bw[kMaxBand];
-    uint32_t gr1[kMaxGlob], gr2[kMaxGlob];
-#pragma unroll
-    for (int i = 0; i < kMaxGlob; ++i) {
-        if (gs0 + i < gs1) {
-            const int qa = 32 * (gs0 + i) + 8 * t.kg + t.q4;
-            gw[i] = glob_weights(t, Abh, gs0 + i);
-            gr1[i] = glob_row(a, qa, q0, q1, c0);
-            gr2[i] = glob_row(a, qa + 4, q0, q1, c0);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kMaxBand; ++i)
-        if (i < nbs) bw[i] = band_weights(t, Abh, kb0 + 32 * i);
+    const int ib0 = (int)((kb0 - t.band_lo) >> 5);
+    const int ib1 = kb0 <= kb1 ? (int)((kb1 - t.band_lo) >> 5) : ib0 - 1;
 
     if (more) {
         dma_chunk(nxt, Zbh, a.n, c0 + kChunkRows, cl, wave);
         dma_groups(t, a, Abh, nstg, c + 1, lane);
     }
 
-    // Random groups; each group's staged words are read one group ahead.
+    // Random groups.
     const int32_t g0 = uniform_load(t.cptr + c);
     const int32_t gcnt = uniform_load(t.cptr + c + 1) - g0;
-    GroupLane nx;
-    if (gcnt > 0) nx = group_lane(t, a, Abh, stg, g0, 0);
     for (int32_t k = 0; k < gcnt; ++k) {
-        const GroupLane gl = nx;
-        if (k + 1 < gcnt) nx = group_lane(t, a, Abh, stg, g0, k + 1);
+        const GroupLane gl = group_lane(t, a, Abh, stg, g0, k);
         // Pair p of the lane's k-group keeps its two weights when its row
         // (the low 7 bits of byte p) is the lane's row.
         const uint32_t rm = gl.r & 0x7f7f7f7fu;
@@ -309,11 +312,14 @@ __device__ __forceinline__ void tile_chunk(const TileLane& t, f32x4 (&acc)[kNB],
     // Global steps.
 #pragma unroll
     for (int i = 0; i < kMaxGlob; ++i) {
-        if (gs0 + i < gs1)
-            mfma4(acc, code_addr(base, key_row_code(gr1[i])), code_addr(base, key_row_code(gr2[i])),
-                  gw[i]);
+        if (i >= gs0 && i < gs1) {
+            const uint32_t r1 = t.gv1[i] >= c0 && t.gv1[i] < c0 + kChunkRows ? (uint32_t)(t.gv1[i] - c0) : kZeroRow;
+            const uint32_t r2 = t.gv2[i] >= c0 && t.gv2[i] < c0 + kChunkRows ? (uint32_t)(t.gv2[i] - c0) : kZeroRow;
+            mfma4(acc, code_addr(base, key_row_code(r1)), code_addr(base, key_row_code(r2)),
+                  t.gw[i]);
+        }
     }
-    for (int s = gs0 + kMaxGlob; s < gs1; ++s) {
+    for (int s = max(gs0, kMaxGlob); s < gs1; ++s) {
         const int qa = 32 * s + 8 * t.kg + t.q4;
         mfma4(acc, code_addr(base, key_row_code(glob_row(a, qa, q0, q1, c0))),
               code_addr(base, key_row_code(glob_row(a, qa + 4, q0, q1, c0))),
@@ -325,13 +331,13 @@ __device__ __forceinline__ void tile_chunk(const TileLane& t, f32x4 (&acc)[kNB],
     const uint32_t bb2 = code_addr(base, key_row_code(8u * t.kg + 4u + t.q4));
 #pragma unroll
     for (int i = 0; i < kMaxBand; ++i) {
-        if (i < nbs) {
-            const uint32_t off = (uint32_t)(kb0 + 32 * i - c0) * kRowBytes;  // 32-row multiple
-            mfma4(acc, bb1 + off, bb2 + off, bw[i]);
+        if (i >= ib0 && i <= ib1) {
+            const uint32_t off = (uint32_t)(t.band_lo + 32 * i - c0) * kRowBytes;  // 32-row multiple
+            mfma4(acc, bb1 + off, bb2 + off, t.bw[i]);
         }
     }
-    for (int i = kMaxBand; i < nbs; ++i) {
-        const int64_t kc = kb0 + 32 * i;
+    for (int i = max(ib0, kMaxBand); i <= ib1; ++i) {
+        const int64_t kc = t.band_lo + 32 * i;
         const uint32_t off = (uint32_t)(kc - c0) * kRowBytes;
         mfma4(acc, bb1 + off, bb2 + off, band_weights(t, Abh, kc));
     }
@@ -484,13 +490,35 @@ void k_diffuse_sched(FastArgs a) {
     t.rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];   // random area of the graph
 
     dma_chunk(buf[0], Zbh, n, 0, cl, wave);
+    t.nbs = active ? (int)((t.band_hi - t.band_lo) >> 5) + 1 : 0;
+    t.ngs = (a.g + 31) >> 5;
+#pragma unroll
+    for (int i = 0; i < kMaxBand; ++i)
+        t.bw[i] = i < t.nbs ? band_weights(t, Abh, t.band_lo + 32 * i) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kMaxGlob; ++i) {
+        t.gw[i] = u32x4{0u, 0u, 0u, 0u};
+        t.gv1[i] = t.gv2[i] = -1;
+        if (i < t.ngs) {
+            const int qa = 32 * i + 8 * kg + (int)q4;
+            t.gw[i] = glob_weights(t, Abh, i);
+            if (qa < a.g) t.gv1[i] = a.G[qa];
+            if (qa + 4 < a.g) t.gv2[i] = a.G[qa + 4];
+        }
+    }
     if (active) dma_groups(t, a, Abh, stg[0], 0, lane);
     f32x4 acc[kNB];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    float scale = 1.0f;   // c_i of this lane's row
     for (int c = 0; c < a.nchunks; ++c) {
         full_barrier();   // chunk c in LDS, chunk c - 1 done by every wave
+        if (c + 1 == a.nchunks && active) {
+            // The idle buffer takes the restart inputs of the wave's rows.
+            dma_restart(a, bh, t.r0w, buf[(c + 1) & 1] + wave * 2048, lane);
+            if (a.row_scale != nullptr && t.rok) scale = a.row_scale[(int64_t)bh * n + my_row];
+        }
         if (active) {
             tile_chunk(t, acc, a, Abh, Zbh, cl, buf[(c + 1) & 1], buf[c & 1], stg[(c + 1) & 1],
                        stg[c & 1], c, wave, lane);
@@ -499,7 +527,11 @@ void k_diffuse_sched(FastArgs a) {
         }
     }
 
-    if (t.rok) store_row(a, bh, my_row, kg, acc);
+    if (active) {
+        __builtin_amdgcn_s_waitcnt(0x0070);   // this wave's restart inputs have landed
+        if (t.rok)
+            store_row(a, bh, my_row, s16, kg, acc, buf[a.nchunks & 1] + wave * 2048, scale);
+    }
 }
 
 }  // namespace
