@@ -55,6 +55,8 @@ def _bind(lib):
         f.argtypes = [p, p, i64, i32, p, p, p, i32]
     lib.oracle_diffuse.restype = ctypes.c_int
     lib.oracle_diffuse.argtypes = [p, p, i64, i32, p, p, i32, ctypes.c_double, p, i32]
+    lib.oracle_diffuse_theta.restype = ctypes.c_int
+    lib.oracle_diffuse_theta.argtypes = [p, p, i64, i32, p, p, i32, p, p, i32]
     return lib
 
 
@@ -149,6 +151,27 @@ class Oracle:
         _check(self.lib.oracle_diffuse(_ptr(A), _ptr(V), n, d, _ptr(rp), _ptr(ci), K_steps,
                                        float(alpha), _ptr(Z), threads), "oracle_diffuse")
         return Z
+
+    def diffuse_theta(self, A, V, row_ptr, col_idx, theta, threads=1):
+        """Z = sum_k theta[k] A^k V, k = 0 .. len(theta) - 1."""
+        A = np.ascontiguousarray(A, dtype=np.float64)
+        V = np.ascontiguousarray(V, dtype=np.float64)
+        th = np.ascontiguousarray(theta, dtype=np.float64)
+        rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+        ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+        n, d = V.shape
+        if A.size == 0:
+            A = np.zeros(1)
+        Z = np.zeros_like(V)
+        _check(self.lib.oracle_diffuse_theta(_ptr(A), _ptr(V), n, d, _ptr(rp), _ptr(ci),
+                                             len(th) - 1, _ptr(th), _ptr(Z), threads),
+               "oracle_diffuse_theta")
+        return Z
+
+    def attn_theta(self, Q, K, V, row_ptr, col_idx, theta, threads=1):
+        """Whole path with general diffusion coefficients for one (batch, head)."""
+        A = self.scores_softmax(Q, K, row_ptr, col_idx, threads)
+        return self.diffuse_theta(A, V, row_ptr, col_idx, theta, threads)
 
     def attn(self, Q, K, V, row_ptr, col_idx, K_steps, alpha, threads=1):
         """Whole path for one (batch, head): scores, softmax, K diffusion steps."""

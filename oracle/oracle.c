@@ -388,3 +388,37 @@ int oracle_diffuse(const double* A, const double* V, int64_t n, int32_t d,
     free(tmp);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* General diffusion coefficients: Z = sum_{k=0..K} theta_k A^k V           */
+/* (Diffuser notes section 2.3, eq. S.6, the series taken through A^K).     */
+/* The powers are applied one at a time: Y_0 = V, Y_{k+1} = A Y_k.          */
+/* ------------------------------------------------------------------------ */
+
+int oracle_diffuse_theta(const double* A, const double* V, int64_t n, int32_t d,
+                         const int64_t* row_ptr, const int32_t* col_idx, int32_t K_steps,
+                         const double* theta, double* Z_out, int32_t threads) {
+    if (check_csr(n, d, row_ptr, col_idx) || !A || !V || !Z_out || !theta || K_steps < 0)
+        return -1;
+    const size_t count = (size_t)n * (size_t)d;
+    const size_t bytes = sizeof(double) * count;
+    double* y = (double*)malloc(bytes);
+    double* next = (double*)malloc(bytes);
+    if (!y || !next) {
+        free(y);
+        free(next);
+        return -1;
+    }
+    memcpy(y, V, bytes);
+    for (size_t e = 0; e < count; ++e) Z_out[e] = theta[0] * V[e];
+    for (int32_t k = 1; k <= K_steps; ++k) {
+        /* next = A y: the step of eq. S.7 with no restart term */
+        diffuse_ctx c = {A, V, y, next, d, 0.0, row_ptr, col_idx};
+        parallel_rows(diffuse_row, &c, n, threads);
+        memcpy(y, next, bytes);
+        for (size_t e = 0; e < count; ++e) Z_out[e] += theta[k] * y[e];
+    }
+    free(y);
+    free(next);
+    return 0;
+}

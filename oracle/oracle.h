@@ -10,6 +10,7 @@
  *  - "Diffuser: modelling long sequences with multi-hop attention diffusion"
  *    reading notes, section 2.1 (edge-restricted softmax, eqs. S.1-S.5),
  *    section 2.2 (local window / global / random connection table),
+ *    section 2.3 (diffusion operator with general coefficients, eq. S.6),
  *    section 2.4 (PPR recurrence, eq. S.7), section 2.5 (finite-K expansion).
  *  - "1.2.1 Static sparsity: Longformer, BigBird and sliding windows",
  *    section 1 (score eq. 1, mask eq. 2, normalisation eqs. 3-4),
@@ -70,6 +71,12 @@ int oracle_scores(const double* Q, const double* K, int64_t n, int32_t d,
 int oracle_diffuse(const double* A, const double* V, int64_t n, int32_t d,
                    const int64_t* row_ptr, const int32_t* col_idx,
                    int32_t K_steps, double alpha, double* Z_out, int32_t threads);
+
+/* Z = sum_{k=0..K} theta[k] A^k V (theta has K_steps + 1 entries). */
+int oracle_diffuse_theta(const double* A, const double* V, int64_t n, int32_t d,
+                         const int64_t* row_ptr, const int32_t* col_idx,
+                         int32_t K_steps, const double* theta, double* Z_out,
+                         int32_t threads);
 
 #ifdef __cplusplus
 }

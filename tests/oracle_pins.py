@@ -375,10 +375,69 @@ def pin_constant_fixed_point(o):
     assert np.allclose(Z, V, rtol=0, atol=1e-13)
 
 
+def pin_theta_printed_coefficients(o):
+    """General coefficients (eq. S.6): with A a cyclic shift and V = I, row 0
+    of sum_k theta_k A^k V lists theta itself; with the printed K = 5,
+    alpha = 0.1 coefficients the operator equals the PPR recurrence."""
+    g = golden_dict("ppr_coeffs_k5.txt")
+    K, alpha = int(g["K"][0]), float(g["alpha"][0])
+    theta = [float(x) for x in g["coeffs"]]
+    n = K + 2
+    rp = np.arange(n + 1, dtype=np.int64)
+    cols = ((np.arange(n) + 1) % n).astype(np.int32)
+    Z = o.diffuse_theta(np.ones(n), np.eye(n), rp, cols, theta)
+    assert np.allclose(Z[0], theta + [0.0] * (n - K - 1), rtol=0, atol=1e-15), Z[0]
+    rng = np.random.default_rng(11)
+    m = 40
+    rp, cols = o.graph(m, 2, [5, 30], 4, 1, False, 17)
+    A = o.scores_softmax(rng.standard_normal((m, 8)), rng.standard_normal((m, 8)), rp[0],
+                         cols[0])
+    V = rng.standard_normal((m, 3))
+    Zt = o.diffuse_theta(A, V, rp[0], cols[0], theta)
+    Zp = o.diffuse(A, V, rp[0], cols[0], K, alpha)
+    assert np.max(np.abs(Zt - Zp)) < 1e-12
+
+
+def pin_theta_three_token(o):
+    """The three-token example through the general form: theta = (alpha,
+    alpha (1 - alpha), (1 - alpha)^2) for K = 2 gives the printed row."""
+    g = golden_dict("diffusion_3token.txt")
+    alpha = float(g["alpha"][0])
+    A_dense = np.array([[float(x) for x in g[f"A_row{i}"]] for i in range(3)])
+    rp = np.array([0, 2, 4, 5], dtype=np.int64)
+    cols = np.array([0, 1, 1, 2, 2], dtype=np.int32)
+    A = np.array([A_dense[i, j] for i in range(3) for j in cols[rp[i]:rp[i + 1]]])
+    theta = [alpha, alpha * (1 - alpha), (1 - alpha) ** 2]
+    Z = o.diffuse_theta(A, np.eye(3), rp, cols, theta)
+    want = [float(x) for x in g["Z2_row0_coeffs"]]
+    assert np.allclose(Z[0], want, rtol=0, atol=1e-15), Z[0]
+
+
+def pin_theta_powers(o):
+    """theta = e_k gives A^k V (dense matrix powers); theta = e_0 gives V
+    exactly; mixtures are the same mixture of powers."""
+    rng = np.random.default_rng(12)
+    n = 24
+    rp, cols = o.graph(n, 1, [7], 3, 1, False, 23)
+    A = o.scores_softmax(rng.standard_normal((n, 4)), rng.standard_normal((n, 4)), rp[0],
+                         cols[0])
+    Ad = _dense_A(rp[0], cols[0], A, n)
+    V = rng.standard_normal((n, 5))
+    assert np.array_equal(o.diffuse_theta(A, V, rp[0], cols[0], [1.0]), V)
+    for k in range(1, 5):
+        th = [0.0] * k + [1.0]
+        want = np.linalg.matrix_power(Ad, k) @ V
+        assert np.max(np.abs(o.diffuse_theta(A, V, rp[0], cols[0], th) - want)) < 1e-12, k
+    th = [0.2, 0.0, 0.5, 0.3]
+    want = 0.2 * V + 0.5 * Ad @ Ad @ V + 0.3 * np.linalg.matrix_power(Ad, 3) @ V
+    assert np.max(np.abs(o.diffuse_theta(A, V, rp[0], cols[0], th) - want)) < 1e-12
+
+
 ALL_PINS = [
     pin_splitmix64, pin_edge_counts_8pos, pin_window_closed_form, pin_degrees,
     pin_row_structure, pin_random_uniform, pin_softmax_8pos, pin_row_sums,
     pin_three_token, pin_expansion_coefficients, pin_finite_expansion,
     pin_dense_brute_force, pin_softmax_attention_reduction, pin_infinite_limit,
     pin_causality, pin_reach, pin_two_hop_global, pin_constant_fixed_point,
+    pin_theta_printed_coefficients, pin_theta_three_token, pin_theta_powers,
 ]

@@ -46,6 +46,12 @@ MUTANTS = [
     ("dot_q_q", "dot += q[ch] * k[ch];", "dot += q[ch] * q[ch];"),
     ("draw_counter_no_plus_one", "0x9E3779B97F4A7C15ull * (ctr + 1ull)",
      "0x9E3779B97F4A7C15ull * ctr"),
+    ("theta_index_shift", "for (size_t e = 0; e < count; ++e) Z_out[e] += theta[k] * y[e];",
+     "for (size_t e = 0; e < count; ++e) Z_out[e] += theta[k - 1] * y[e];"),
+    ("theta_no_identity_term", "for (size_t e = 0; e < count; ++e) Z_out[e] = theta[0] * V[e];",
+     "for (size_t e = 0; e < count; ++e) Z_out[e] = 0.0;"),
+    ("theta_powers_of_v", "diffuse_ctx c = {A, V, y, next, d, 0.0, row_ptr, col_idx};",
+     "diffuse_ctx c = {A, V, V, next, d, 0.0, row_ptr, col_idx};"),
     ("mix_shift", "z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;",
      "z = (z ^ (z >> 26)) * 0x94D049BB133111EBull;"),
 ]
