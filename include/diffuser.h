@@ -182,6 +182,29 @@ DIFFUSER_API diffuser_status diffuser_diffuse(const void* A, const void* V, diff
                                  int32_t K_steps, float alpha, void* Z, void* workspace,
                                  size_t ws_bytes, void* stream);
 
+/*
+ * General diffusion coefficients ("Diffuser" notes, section 2.3, eq. S.6,
+ * the series taken through A^K): Z = sum_{k=0..K_steps} theta[k] A^k V.
+ * theta: host array of K_steps + 1 floats, each finite and >= 0, summing to
+ * 1 within 1e-5 (otherwise DIFFUSER_ERR_INVALID_ARG); it is read before the
+ * call returns. PPR is the case theta[k] = alpha (1 - alpha)^k for k < K,
+ * theta[K] = (1 - alpha)^K. Evaluated in nested form, U_K = theta[K] V,
+ * U_k = theta[k] V + A U_{k+1}, Z = U_0: K_steps launches of the diffusion
+ * step (one for K_steps = 0), rounding U_k to `dtype` after each.
+ * Arguments, layouts, workspace, ownership and errors as for diffuser_attn
+ * and diffuser_diffuse.
+ */
+DIFFUSER_API diffuser_status diffuser_attn_theta(const void* Q, const void* K, const void* V,
+                                    diffuser_dtype dtype, int32_t B, int32_t H, int32_t d_h,
+                                    int32_t d_v, const diffuser_graph* g, int32_t K_steps,
+                                    const float* theta, void* Z, void* workspace,
+                                    size_t ws_bytes, void* stream);
+DIFFUSER_API diffuser_status diffuser_diffuse_theta(const void* A, const void* V, diffuser_dtype dtype,
+                                       int32_t B, int32_t H, int32_t d_v,
+                                       const diffuser_graph* g, int32_t K_steps,
+                                       const float* theta, void* Z, void* workspace,
+                                       size_t ws_bytes, void* stream);
+
 /* Static string for a status code. */
 DIFFUSER_API const char* diffuser_status_string(diffuser_status s);
 

@@ -37,6 +37,7 @@ ABI_SYMBOLS = (
     "diffuser_graph_copy_csr", "diffuser_graph_copy_slots", "diffuser_graph_destroy",
     "diffuser_attn_workspace_size",
     "diffuser_attn", "diffuser_scores_softmax", "diffuser_diffuse",
+    "diffuser_attn_theta", "diffuser_diffuse_theta",
     "diffuser_status_string", "diffuser_last_error",
 )
 
@@ -97,6 +98,10 @@ def load_library(path: str = LIB_PATH):
     lib.diffuser_scores_softmax.restype = st
     lib.diffuser_diffuse.argtypes = [p, p, st, i32, i32, i32, p, i32, ctypes.c_float, p, p, sz, p]
     lib.diffuser_diffuse.restype = st
+    lib.diffuser_attn_theta.argtypes = [p, p, p, st, i32, i32, i32, i32, p, i32, p, p, p, sz, p]
+    lib.diffuser_attn_theta.restype = st
+    lib.diffuser_diffuse_theta.argtypes = [p, p, st, i32, i32, i32, p, i32, p, p, p, sz, p]
+    lib.diffuser_diffuse_theta.restype = st
     lib.diffuser_status_string.argtypes = [st]
     lib.diffuser_status_string.restype = ctypes.c_char_p
     lib.diffuser_last_error.argtypes = []
@@ -308,4 +313,53 @@ def diffuse(A, v, graph: Graph, K: int, alpha: float, out=None, workspace=None):
                                 graph.handle, K, float(alpha), out.data_ptr(),
                                 workspace.data_ptr(), workspace.numel(),
                                 ctypes.c_void_p(_stream_handle(v.device))))
+    return out
+
+
+def _theta_array(theta):
+    th = [float(x) for x in theta]
+    if len(th) < 1:
+        raise DiffuserError(1, "theta needs at least one coefficient")
+    return (ctypes.c_float * len(th))(*th), len(th) - 1
+
+
+def attn_theta(q, k, v, graph: Graph, theta, out=None, workspace=None):
+    """Z = sum_k theta[k] A^k V with A the edge-softmax weights of (q, k)."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check_bhnd(t, nm, graph.n)
+    B, H, _, d_h = q.shape
+    d_v = v.shape[3]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or not (q.dtype == k.dtype == v.dtype):
+        raise DiffuserError(1, "q, k, v shapes/dtypes disagree")
+    if out is None:
+        out = torch.empty_like(v)
+    workspace, _ = _workspace(graph, B, H, d_h, d_v, q.dtype, q.device, workspace)
+    th, K = _theta_array(theta)
+    lib = load_library()
+    _check(lib.diffuser_attn_theta(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q.dtype),
+                                   B, H, d_h, d_v, graph.handle, K, th, out.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel(),
+                                   ctypes.c_void_p(_stream_handle(q.device))))
+    return out
+
+
+def diffuse_theta(A, v, graph: Graph, theta, out=None, workspace=None):
+    """Z = sum_k theta[k] A^k V with given A."""
+    torch = _torch()
+    _check_bhnd(v, "v", graph.n)
+    B, H, _, d_v = v.shape
+    if not A.is_cuda or not A.is_contiguous() or A.dtype != v.dtype or \
+            A.numel() != graph.a_numel(B, H):
+        raise DiffuserError(1, "A must be a contiguous CUDA tensor in the A layout")
+    if out is None:
+        out = torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(max(v.numel() * v.element_size() + 256, 1), dtype=torch.uint8,
+                                device=v.device)
+    th, K = _theta_array(theta)
+    lib = load_library()
+    _check(lib.diffuser_diffuse_theta(A.data_ptr(), v.data_ptr(), _dtype_code(v.dtype), B, H, d_v,
+                                      graph.handle, K, th, out.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel(), ctypes.c_void_p(_stream_handle(v.device))))
     return out

@@ -187,11 +187,52 @@ diffuser_status run_diffusion(const diffuser_graph* g, const attn_shape& s, cons
     for (int32_t k = 0; k < K_steps; ++k) {
         // Steps K-1, K-3, ... write Z; the others write tmp.
         void* dst = ((K_steps - 1 - k) % 2 == 0) ? Z : tmp;
-        hipError_t e = fast ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, alpha, st)
-                            : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, alpha, st);
+        const step_coefs kc{1.0f - alpha, alpha};
+        hipError_t e = fast ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st)
+                            : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
         if (e != hipSuccess) return hip_fail(e, "diffusion step launch");
         cur = dst;
     }
+    return DIFFUSER_OK;
+}
+
+// Z = sum_{k=0..K} theta_k A^k V (eq. S.6 through A^K) in nested form:
+// U_K = theta_K V, U_k = theta_k V + A U_{k+1}, Z = U_0. The first launch
+// computes U_{K-1} = theta_K (A V) + theta_{K-1} V straight from V, the
+// others U_k = (A U_{k+1}) + theta_k V; each is one diffusion step with
+// coefficients (keep, restart). K = 0 is one launch with keep = 0.
+diffuser_status run_diffusion_theta(const diffuser_graph* g, const attn_shape& s, const void* A,
+                                    const float* row_scale, const void* V, void* Z, void* tmp,
+                                    int32_t K_steps, const float* theta, hipStream_t st) {
+    const bool fast = fast_diffuse_supported(*g, s) && aligned16(A);
+    const int32_t launches = K_steps == 0 ? 1 : K_steps;
+    const void* cur = V;
+    for (int32_t j = 0; j < launches; ++j) {
+        void* dst = ((launches - 1 - j) % 2 == 0) ? Z : tmp;
+        const int32_t k = K_steps - 1 - j;   // U_k is written
+        const step_coefs kc = K_steps == 0 ? step_coefs{0.0f, theta[0]}
+                              : j == 0     ? step_coefs{theta[K_steps], theta[k]}
+                                           : step_coefs{1.0f, theta[k]};
+        hipError_t e = fast ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st)
+                            : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
+        if (e != hipSuccess) return hip_fail(e, "diffusion step launch");
+        cur = dst;
+    }
+    return DIFFUSER_OK;
+}
+
+// theta: K + 1 finite, non-negative host floats summing to 1 (eq. S.6).
+diffuser_status check_theta(int32_t K_steps, const float* theta) {
+    if (K_steps < 0) return fail(DIFFUSER_ERR_INVALID_ARG, "K_steps must be >= 0");
+    if (!theta) return fail(DIFFUSER_ERR_INVALID_ARG, "theta is NULL");
+    double sum = 0.0;
+    for (int32_t k = 0; k <= K_steps; ++k) {
+        if (!(theta[k] >= 0.0f) || !std::isfinite(theta[k]))
+            return fail(DIFFUSER_ERR_INVALID_ARG, "theta must be finite and non-negative");
+        sum += theta[k];
+    }
+    if (std::fabs(sum - 1.0) > 1e-5)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "theta must sum to 1");
     return DIFFUSER_OK;
 }
 
@@ -566,14 +607,18 @@ diffuser_status diffuser_attn_workspace_size(const diffuser_graph* g, int32_t B,
     return DIFFUSER_OK;
 }
 
-diffuser_status diffuser_attn(const void* Q, const void* K, const void* V, diffuser_dtype dtype,
-                              int32_t B, int32_t H, int32_t d_h, int32_t d_v,
-                              const diffuser_graph* g, int32_t K_steps, float alpha, void* Z,
-                              void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+
+// The whole path; theta == nullptr: the PPR recurrence with alpha, else
+// the general coefficients theta[0..K_steps].
+diffuser_status attn_impl(const void* Q, const void* K, const void* V, diffuser_dtype dtype,
+                          int32_t B, int32_t H, int32_t d_h, int32_t d_v, const diffuser_graph* g,
+                          int32_t K_steps, float alpha, const float* theta, void* Z,
+                          void* workspace, size_t ws_bytes, void* stream) {
     g_last_error.clear();
     if (auto s = check_shape(g, B, H, d_h, dtype, "d_h")) return s;
     if (auto s = check_shape(g, B, H, d_v, dtype, "d_v")) return s;
-    if (auto s = check_alpha_k(K_steps, alpha)) return s;
+    if (auto s = theta ? check_theta(K_steps, theta) : check_alpha_k(K_steps, alpha)) return s;
     for (auto pr : {std::make_pair(Q, "Q"), std::make_pair(K, "K"), std::make_pair(V, "V"),
                     std::make_pair((const void*)Z, "Z"), std::make_pair((const void*)workspace,
                                                                           "workspace")})
@@ -595,8 +640,30 @@ diffuser_status diffuser_attn(const void* Q, const void* K, const void* V, diffu
     hipError_t e = launch_scores_softmax(*g, attn_shape{B, H, d_h, dtype}, Q, K, A, row_scale,
                                          scale_log2, st);
     if (e != hipSuccess) return hip_fail(e, "score/softmax launch");
+    if (theta)
+        return run_diffusion_theta(g, attn_shape{B, H, d_v, dtype}, A, row_scale, V, Z, tmp,
+                                   K_steps, theta, st);
     return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, row_scale, V, Z, tmp, K_steps,
                          alpha, st);
+}
+
+}  // namespace
+
+diffuser_status diffuser_attn(const void* Q, const void* K, const void* V, diffuser_dtype dtype,
+                              int32_t B, int32_t H, int32_t d_h, int32_t d_v,
+                              const diffuser_graph* g, int32_t K_steps, float alpha, void* Z,
+                              void* workspace, size_t ws_bytes, void* stream) {
+    return attn_impl(Q, K, V, dtype, B, H, d_h, d_v, g, K_steps, alpha, nullptr, Z, workspace,
+                     ws_bytes, stream);
+}
+
+diffuser_status diffuser_attn_theta(const void* Q, const void* K, const void* V,
+                                    diffuser_dtype dtype, int32_t B, int32_t H, int32_t d_h,
+                                    int32_t d_v, const diffuser_graph* g, int32_t K_steps,
+                                    const float* theta, void* Z, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+    return attn_impl(Q, K, V, dtype, B, H, d_h, d_v, g, K_steps, 0.0f, theta, Z, workspace,
+                     ws_bytes, stream);
 }
 
 diffuser_status diffuser_scores_softmax(const void* Q, const void* K, diffuser_dtype dtype,
@@ -624,13 +691,15 @@ diffuser_status diffuser_scores_softmax(const void* Q, const void* K, diffuser_d
     return DIFFUSER_OK;
 }
 
-diffuser_status diffuser_diffuse(const void* A, const void* V, diffuser_dtype dtype, int32_t B,
-                                 int32_t H, int32_t d_v, const diffuser_graph* g,
-                                 int32_t K_steps, float alpha, void* Z, void* workspace,
-                                 size_t ws_bytes, void* stream) {
+namespace {
+
+diffuser_status diffuse_impl(const void* A, const void* V, diffuser_dtype dtype, int32_t B,
+                             int32_t H, int32_t d_v, const diffuser_graph* g, int32_t K_steps,
+                             float alpha, const float* theta, void* Z, void* workspace,
+                             size_t ws_bytes, void* stream) {
     g_last_error.clear();
     if (auto s = check_shape(g, B, H, d_v, dtype, "d_v")) return s;
-    if (auto s = check_alpha_k(K_steps, alpha)) return s;
+    if (auto s = theta ? check_theta(K_steps, theta) : check_alpha_k(K_steps, alpha)) return s;
     if (auto s = check_ptr(A, "A", false)) return s;
     if (reinterpret_cast<uintptr_t>(A) % elem_size(dtype))
         return fail(DIFFUSER_ERR_INVALID_ARG, "A is not element aligned");
@@ -648,8 +717,31 @@ diffuser_status diffuser_diffuse(const void* A, const void* V, diffuser_dtype dt
         (K_steps >= 2 && overlaps(Z, vz_bytes, workspace, z_need)))
         return fail(DIFFUSER_ERR_INVALID_ARG, "Z overlaps an input or the workspace");
     // The Z ping-pong buffer sits at the start of the caller's workspace.
+    if (theta)
+        return run_diffusion_theta(g, attn_shape{B, H, d_v, dtype}, A, nullptr, V, Z, workspace,
+                                   K_steps, theta, static_cast<hipStream_t>(stream));
     return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, nullptr, V, Z, workspace, K_steps,
                          alpha, static_cast<hipStream_t>(stream));
 }
+
+}  // namespace
+
+diffuser_status diffuser_diffuse(const void* A, const void* V, diffuser_dtype dtype, int32_t B,
+                                 int32_t H, int32_t d_v, const diffuser_graph* g,
+                                 int32_t K_steps, float alpha, void* Z, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+    return diffuse_impl(A, V, dtype, B, H, d_v, g, K_steps, alpha, nullptr, Z, workspace,
+                        ws_bytes, stream);
+}
+
+diffuser_status diffuser_diffuse_theta(const void* A, const void* V, diffuser_dtype dtype,
+                                       int32_t B, int32_t H, int32_t d_v,
+                                       const diffuser_graph* g, int32_t K_steps,
+                                       const float* theta, void* Z, void* workspace,
+                                       size_t ws_bytes, void* stream) {
+    return diffuse_impl(A, V, dtype, B, H, d_v, g, K_steps, 0.0f, theta, Z, workspace, ws_bytes,
+                        stream);
+}
+
 
 }  // extern "C"

@@ -1,7 +1,8 @@
-// One personalized-PageRank diffusion step ("Diffuser" reading notes,
-// section 2.4, eq. S.7):
-//   Z_{k+1}[i] = (1 - alpha) * sum_{j in N(i)} A_ij Z_k[j] + alpha * V[i].
-// The edge weights A are the same in every step; only Z changes.
+// One diffusion step ("Diffuser" reading notes, section 2.4, eq. S.7):
+//   Z_{k+1}[i] = (1 - alpha) * sum_{j in N(i)} A_ij Z_k[j] + alpha * V[i],
+// written as keep * c_i * sum_j A_ij Z_k[j] + restart * V[i] so that the
+// same step also evaluates general coefficients (section 2.3, eq. S.6) in
+// nested form. The edge weights A are the same in every step; only Z changes.
 //
 // Generic path (any slot layout: the row segment, then any scheduled random
 // slots; padding slots are skipped). One wavefront
@@ -22,7 +23,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_diffuse_step(GenericGraph gg, int32_t H, const T* __restrict__ A, const T* __restrict__ Zk,
                     const T* __restrict__ V, T* __restrict__ Zn,
-                    const float* __restrict__ row_scale, float alpha) {
+                    const float* __restrict__ row_scale, step_coefs kc) {
     constexpr int E = chunk<T>::kElems;
     constexpr int L = D / E;
     constexpr int EPI = kWave / L;
@@ -67,34 +68,34 @@ void k_diffuse_step(GenericGraph gg, int32_t H, const T* __restrict__ A, const T
         float v[E];
         chunk<T>::load(V + o, v);
         const float keep =
-            row_scale == nullptr ? 1.0f - alpha : (1.0f - alpha) * row_scale[(int64_t)bh * n + i];
+            row_scale == nullptr ? kc.keep : kc.keep * row_scale[(int64_t)bh * n + i];
 #pragma unroll
-        for (int c = 0; c < E; ++c) v[c] = keep * acc[c] + alpha * v[c];
+        for (int c = 0; c < E; ++c) v[c] = keep * acc[c] + kc.restart * v[c];
         chunk<T>::store(Zn + o, v);
     }
 }
 
 template <typename T, int D>
 hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
-                    const void* V, void* Zn, const float* row_scale, float alpha,
+                    const void* V, void* Zn, const float* row_scale, step_coefs kc,
                     hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
     hipLaunchKernelGGL((k_diffuse_step<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
                        generic_graph(g), s.H, static_cast<const T*>(A),
                        static_cast<const T*>(Zk), static_cast<const T*>(V),
-                       static_cast<T*>(Zn), row_scale, alpha);
+                       static_cast<T*>(Zn), row_scale, kc);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_d(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
-                    const void* V, void* Zn, const float* row_scale, float alpha,
+                    const void* V, void* Zn, const float* row_scale, step_coefs kc,
                     hipStream_t st) {
     switch (s.d) {
-        case 16: return launch_t<T, 16>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
-        case 32: return launch_t<T, 32>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
-        case 64: return launch_t<T, 64>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
-        case 128: return launch_t<T, 128>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
+        case 16: return launch_t<T, 16>(g, s, A, Zk, V, Zn, row_scale, kc, st);
+        case 32: return launch_t<T, 32>(g, s, A, Zk, V, Zn, row_scale, kc, st);
+        case 64: return launch_t<T, 64>(g, s, A, Zk, V, Zn, row_scale, kc, st);
+        case 128: return launch_t<T, 128>(g, s, A, Zk, V, Zn, row_scale, kc, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -117,10 +118,10 @@ GenericGraph generic_graph(const diffuser_graph& g) {
 
 hipError_t launch_diffuse_step(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
-                               float alpha, hipStream_t st) {
+                               step_coefs kc, hipStream_t st) {
     if (s.dtype == DIFFUSER_F32)
-        return launch_d<float>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
-    return launch_d<bf16_t>(g, s, A, Zk, V, Zn, row_scale, alpha, st);
+        return launch_d<float>(g, s, A, Zk, V, Zn, row_scale, kc, st);
+    return launch_d<bf16_t>(g, s, A, Zk, V, Zn, row_scale, kc, st);
 }
 
 }  // namespace diffuser

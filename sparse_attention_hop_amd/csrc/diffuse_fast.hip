@@ -1,7 +1,9 @@
 // Diffusion step on scheduled graphs, bf16 storage, head width 64:
-//   Z_{k+1}[i] = (1 - alpha) * c_i * sum_j A_ij Z_k[j] + alpha * V[i]
-// ("Diffuser" reading notes, section 2.4, eq. S.7; c_i rescales the stored
-// weights of row i to sum to one, or is 1).
+//   Z_{k+1}[i] = keep * c_i * sum_j A_ij Z_k[j] + restart * V[i]
+// ("Diffuser" reading notes, section 2.4, eq. S.7, with keep = 1 - alpha and
+// restart = alpha; other coefficients evaluate section 2.3's eq. S.6 in
+// nested form; c_i rescales the stored weights of row i to sum to one, or
+// is 1).
 //
 // Every part of the sum is a v_mfma_f32_16x16x32_bf16 product
 //   D[channel][row] += Z^T[channel][key] * W^T[key][row]
@@ -77,7 +79,7 @@ struct FastArgs {
     const uint16_t* V;
     uint16_t* Zn;
     const float* row_scale;     // [B*H][n] or null
-    float alpha;
+    float keep, restart;
     int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items;
 };
 
@@ -171,16 +173,16 @@ __device__ __forceinline__ void dma_restart(const FastArgs& a, int32_t bh, int64
 __device__ __forceinline__ void store_row(const FastArgs& a, int32_t bh, int64_t i, int j, int kg,
                                           const f32x4 (&acc)[kNB], const char LDS_AS* vbuf,
                                           float scale) {
-    const float keep = (1.0f - a.alpha) * scale;
+    const float keep = a.keep * scale;
     const int64_t base = ((int64_t)bh * a.n + i) * kD + 4 * kg;
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
         const u32x2 v = *reinterpret_cast<const u32x2 LDS_AS*>(vbuf + 128 * j + 2 * (16 * nb + 4 * kg));
         u32x2 o;
-        o[0] = to_bf16_pair(keep * acc[nb][0] + a.alpha * bf16_lo(v[0]),
-                            keep * acc[nb][1] + a.alpha * bf16_hi(v[0]));
-        o[1] = to_bf16_pair(keep * acc[nb][2] + a.alpha * bf16_lo(v[1]),
-                            keep * acc[nb][3] + a.alpha * bf16_hi(v[1]));
+        o[0] = to_bf16_pair(keep * acc[nb][0] + a.restart * bf16_lo(v[0]),
+                            keep * acc[nb][1] + a.restart * bf16_hi(v[0]));
+        o[1] = to_bf16_pair(keep * acc[nb][2] + a.restart * bf16_lo(v[1]),
+                            keep * acc[nb][3] + a.restart * bf16_hi(v[1]));
         *reinterpret_cast<u32x2*>(a.Zn + base + 16 * nb) = o;
     }
 }
@@ -456,9 +458,8 @@ void k_diffuse_sched(FastArgs a) {
             const int64_t i = a.G[q];
             const int ch = 16 * nb + 4 * (l >> 4) + e;
             const int64_t o = ((int64_t)bh * n + i) * kD + ch;
-            const float keep = a.row_scale ? (1.0f - a.alpha) * a.row_scale[(int64_t)bh * n + i]
-                                           : 1.0f - a.alpha;
-            a.Zn[o] = (uint16_t)f32_to_bf16(keep * sum + a.alpha * bf16_to_f32(a.V[o]));
+            const float keep = a.row_scale ? a.keep * a.row_scale[(int64_t)bh * n + i] : a.keep;
+            a.Zn[o] = (uint16_t)f32_to_bf16(keep * sum + a.restart * bf16_to_f32(a.V[o]));
         }
         return;
     }
@@ -545,7 +546,7 @@ bool fast_diffuse_supported(const diffuser_graph& g, const attn_shape& s) {
 
 hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
-                               float alpha, hipStream_t st) {
+                               step_coefs kc, hipStream_t st) {
     FastArgs a;
     a.n = g.n;
     a.H = s.H;
@@ -570,7 +571,8 @@ hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, con
     a.V = static_cast<const uint16_t*>(V);
     a.Zn = static_cast<uint16_t*>(Zn);
     a.row_scale = row_scale;
-    a.alpha = alpha;
+    a.keep = kc.keep;
+    a.restart = kc.restart;
     const int32_t BH = s.B * s.H;
     a.tiles_per_bh = (int32_t)((g.n + kTileRows - 1) / kTileRows);
     a.grow_per_bh = (g.num_global + kGrowRows - 1) / kGrowRows;

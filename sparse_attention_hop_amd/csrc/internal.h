@@ -153,15 +153,22 @@ hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, cons
                               const void* K, void* A, float* row_scale, float scale_log2,
                               bool normalized, hipStream_t st);
 
-// One step: Zn = (1 - alpha) * c_i * (A Zk)_i + alpha * V_i with c_i =
-// row_scale[(b, h, i)] or 1 when row_scale == nullptr. Generic kernel.
+// Coefficients of one diffusion step Zn = keep * c_i * (A Zk)_i + restart * V_i:
+// (1 - alpha, alpha) for the PPR recurrence, (theta_{k+1} or 1, theta_k)
+// for the nested evaluation of general coefficients.
+struct step_coefs {
+    float keep, restart;
+};
+
+// One step with c_i = row_scale[(b, h, i)], or 1 when row_scale == nullptr.
+// Generic kernel.
 hipError_t launch_diffuse_step(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
-                               float alpha, hipStream_t st);
+                               step_coefs k, hipStream_t st);
 // The same step on built graphs (bf16, d = 64), LDS-streamed with MFMA.
 bool fast_diffuse_supported(const diffuser_graph& g, const attn_shape& s);
 hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
-                               float alpha, hipStream_t st);
+                               step_coefs k, hipStream_t st);
 
 }  // namespace diffuser

@@ -498,3 +498,95 @@ def test_fast_diffusion_by_segment(orc, name):
             bad = np.argwhere(err > 1e-2 * np.maximum(np.abs(ref), 1) + 1e-3)
             assert bad.size == 0, (f"{cname} h={h}: {len(bad)} bad, first rows/ch "
                                    f"{bad[:6].tolist()} max err {err.max():.3e}")
+
+
+# ---------------------------------------------------------------------------
+# General diffusion coefficients (eq. S.6 through A^K)
+# ---------------------------------------------------------------------------
+
+def _thetas(K):
+    """PPR's coefficients at alpha 0.1, uniform ones, and A^K alone."""
+    ppr = [0.1 * 0.9 ** k for k in range(K)] + [0.9 ** K]
+    return {"ppr": ppr, "uniform": [1.0 / (K + 1)] * (K + 1), "last": [0.0] * K + [1.0]}
+
+
+THETA_CASES = [
+    # n, r, G, R, ng, causal, B, H, d, dtype
+    (700, 20, list(range(0, 700, 7))[:70], 12, 2, False, 2, 2, 64, "bf16"),   # fast path
+    (1100, 50, [0, 1, 2, 700, 1099], 40, 3, True, 3, 1, 64, "bf16"),          # fast, causal
+    (300, 6, [0, 150], 9, 1, False, 2, 3, 64, "f32"),                          # generic
+    (513, 16, [3, 200], 20, 1, False, 1, 2, 32, "bf16"),                       # generic, d 32
+]
+
+
+@pytest.mark.parametrize("case", THETA_CASES, ids=lambda c: f"n{c[0]}d{c[8]}{c[9]}c{int(c[5])}")
+@pytest.mark.parametrize("K", [0, 1, 4])
+def test_theta_small(orc, case, K):
+    n, r, G, R, ngr, causal, B, H, d, dt = case
+    ng = ngr if ngr in (1, B) else B
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    g = _gpu_graph(n, r, G, R, ng, causal, 37)
+    rp, cols = _check_csr(orc, g, n, r, G, R, ng, causal, 37)
+    shape = (B, H, n, d)
+    q, k, v = (make_tensor(shape, 61 + i, tdt) for i in range(3))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    A = sah.scores_softmax(qd, kd, g)
+    A_h = _as64(A)
+    for tname, theta in _thetas(K).items():
+        z = _as64(sah.attn_theta(qd, kd, vd, g, theta))
+        zs = _as64(sah.diffuse_theta(A, vd, g, theta))
+        for b in range(B):
+            gr = 0 if ng == 1 else b
+            for h in range(H):
+                ref = orc.attn_theta(_as64(q[b, h]), _as64(k[b, h]), _as64(v[b, h]), rp[gr],
+                                     cols[gr], theta)
+                pu.assert_z_close(z[b, h], ref, dt, f"attn_theta {tname} b={b} h={h}", K, 0.0)
+                A_csr = _a_csr(g, A_h, b, h, H, gr, rp, cols)
+                ref_s = orc.diffuse_theta(A_csr, _as64(v[b, h]), rp[gr], cols[gr], theta)
+                pu.assert_z_close(zs[b, h], ref_s, dt, f"diffuse_theta {tname} b={b} h={h}", K,
+                                  0.0)
+    if K == 0:   # theta = (1): Z = V exactly
+        assert torch.equal(sah.attn_theta(qd, kd, vd, g, [1.0]), vd)
+
+
+def test_theta_ppr_matches_recurrence():
+    """PPR's coefficients through the nested form agree with the recurrence
+    (the same operator, evaluated in another order)."""
+    n, r, G, R = 700, 20, list(range(0, 700, 7))[:70], 12
+    g = _gpu_graph(n, r, G, R, 2, False, 37)
+    shape = (2, 2, n, 64)
+    q, k, v = (make_tensor(shape, 71 + i, torch.bfloat16).to(DEV) for i in range(3))
+    z1 = _as64(sah.attn(q, k, v, g, 5, 0.1))
+    z2 = _as64(sah.attn_theta(q, k, v, g, _thetas(5)["ppr"]))
+    for b in range(2):
+        for h in range(2):
+            pu.assert_z_close(z2[b, h], z1[b, h], "bf16", f"b={b} h={h}", 5, 0.1)
+
+
+def test_theta_full_size(orc):
+    """Headline workload, uniform coefficients over A^0 .. A^5, sampled pairs."""
+    w = WORKLOADS["mlm4096_bf16"]
+    print(f"\n[parity] theta {w.describe()}", flush=True)
+    g = _gpu_graph(w.n, w.radius, w.global_idx, w.num_random, w.num_graphs, w.causal,
+                   w.graph_seed)
+    rp, cols = orc.graph(w.n, w.radius, w.global_idx, w.num_random, w.num_graphs, w.causal,
+                         w.graph_seed)
+    q, k, v = make_qkv(w)
+    theta = _thetas(w.K)["uniform"]
+    z = _as64(sah.attn_theta(q.to(DEV), k.to(DEV), v.to(DEV), g, theta))
+    threads = pu.oracle_threads()
+    for b, h in _samples(w.B, w.H)[:3]:
+        gr = 0 if w.num_graphs == 1 else b
+        ref = orc.attn_theta(_as64(q[b, h]), _as64(k[b, h]), _as64(v[b, h]), rp[gr], cols[gr],
+                             theta, threads)
+        e = pu.assert_z_close(z[b, h], ref, w.dtype, f"theta b={b} h={h}", w.K, 0.0)
+        print(f"[parity] theta b={b} h={h} err={e:.3e} x tol", flush=True)
+
+
+def test_theta_invalid():
+    g = _gpu_graph(64, 2, [0], 3, 1, False, 5)
+    x = make_tensor((1, 1, 64, 64), 1, torch.bfloat16).to(DEV)
+    for bad in ([0.5, 0.4], [1.2, -0.2], [float("nan"), 1.0], [0.5, 0.5 + 1e-3]):
+        with pytest.raises(sah.DiffuserError) as ei:
+            sah.attn_theta(x, x, x, g, bad)
+        assert ei.value.status_name == "DIFFUSER_ERR_INVALID_ARG", bad
