@@ -49,6 +49,10 @@ def _bind(lib):
     lib.oracle_graph_nnz.argtypes = graph_args + [p]
     lib.oracle_graph_build.restype = ctypes.c_int
     lib.oracle_graph_build.argtypes = graph_args + [p, p]
+    lib.oracle_graph_nnz_layout.restype = ctypes.c_int
+    lib.oracle_graph_nnz_layout.argtypes = graph_args + [i32, p]
+    lib.oracle_graph_build_layout.restype = ctypes.c_int
+    lib.oracle_graph_build_layout.argtypes = graph_args + [i32, p, p]
     for name in ("oracle_scores_softmax", "oracle_scores"):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
@@ -99,16 +103,19 @@ class Oracle:
         return int(self.lib.oracle_draw(seed, b, n, i, t))
 
     # -- graph --------------------------------------------------------------
-    def graph(self, n, radius, global_idx, num_random, num_graphs=1, causal=False, seed=0):
-        """Returns (row_ptr int64[num_graphs, n+1], list of col_idx int32 arrays)."""
+    def graph(self, n, radius, global_idx, num_random, num_graphs=1, causal=False, seed=0,
+              layout=0):
+        """Returns (row_ptr int64[num_graphs, n+1], list of col_idx int32 arrays).
+        layout 0: seeded random extras; 1: evenly spaced extras."""
         g = np.ascontiguousarray(np.asarray(global_idx, dtype=np.int32))
         gp = _ptr(g) if g.size else None
         nnz = np.zeros(num_graphs, dtype=np.int64)
-        args = (n, radius, g.size, gp, num_random, num_graphs, int(bool(causal)), seed)
-        _check(self.lib.oracle_graph_nnz(*args, _ptr(nnz)), "oracle_graph_nnz")
+        args = (n, radius, g.size, gp, num_random, num_graphs, int(bool(causal)), seed,
+                int(layout))
+        _check(self.lib.oracle_graph_nnz_layout(*args, _ptr(nnz)), "oracle_graph_nnz")
         row_ptr = np.zeros((num_graphs, n + 1), dtype=np.int64)
         cols = np.zeros(max(int(nnz.sum()), 1), dtype=np.int32)
-        _check(self.lib.oracle_graph_build(*args, _ptr(row_ptr), _ptr(cols)),
+        _check(self.lib.oracle_graph_build_layout(*args, _ptr(row_ptr), _ptr(cols)),
                "oracle_graph_build")
         out, base = [], 0
         for gr in range(num_graphs):

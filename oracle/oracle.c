@@ -46,6 +46,7 @@ typedef struct {
     int32_t num_random;
     int32_t causal;
     uint64_t seed;
+    int32_t layout;   /* 0: seeded random extras; 1: evenly spaced extras */
 } graph_spec;
 
 /* Marks N(i) of graph gr in member[0..n) (1 = window or global, 2 = random)
@@ -70,6 +71,20 @@ static int mark_row(const graph_spec* s, int64_t gr, int64_t i, unsigned char* m
     if (pool <= s->num_random) {
         for (int64_t j = 0; j < n; ++j)
             if (member[j] == 0) member[j] = 2;
+        return 0;
+    }
+    if (s->layout == 1) {
+        /* Evenly spaced extras ("w uni."): pool members number q * pool / R
+         * (q = 0 .. R - 1) in ascending order of the pool. */
+        int64_t q = 0, rank = 0;
+        for (int64_t j = 0; j < n && q < s->num_random; ++j) {
+            if (member[j] != 0) continue;
+            if (rank == q * pool / s->num_random) {
+                member[j] = 2;
+                ++q;
+            }
+            ++rank;
+        }
         return 0;
     }
     int32_t taken = 0;
@@ -164,9 +179,10 @@ static int run_graph_pass(const graph_spec* s, int64_t gr, int64_t* counts,
 
 static int make_spec(graph_spec* s, unsigned char** is_global, int64_t n, int32_t radius,
                      int32_t num_global, const int32_t* global_idx, int32_t num_random,
-                     int32_t num_graphs, int32_t causal, uint64_t seed) {
+                     int32_t num_graphs, int32_t causal, uint64_t seed, int32_t layout) {
     if (n < 1 || n > (1ll << 31) - 1 || radius < 0 || num_global < 0 || num_global > n ||
-        num_random < 0 || num_graphs < 1 || (num_global > 0 && global_idx == NULL))
+        num_random < 0 || num_graphs < 1 || (num_global > 0 && global_idx == NULL) ||
+        layout < 0 || layout > 1)
         return -1;
     for (int32_t k = 0; k < num_global; ++k) {
         if (global_idx[k] < 0 || global_idx[k] >= n) return -1;
@@ -183,17 +199,18 @@ static int make_spec(graph_spec* s, unsigned char** is_global, int64_t n, int32_
     s->num_random = num_random;
     s->causal = causal != 0;
     s->seed = seed;
+    s->layout = layout;
     *is_global = ig;
     return 0;
 }
 
-int oracle_graph_nnz(int64_t n, int32_t radius, int32_t num_global, const int32_t* global_idx,
-                     int32_t num_random, int32_t num_graphs, int32_t causal, uint64_t seed,
-                     int64_t* nnz_out) {
+int oracle_graph_nnz_layout(int64_t n, int32_t radius, int32_t num_global,
+                            const int32_t* global_idx, int32_t num_random, int32_t num_graphs,
+                            int32_t causal, uint64_t seed, int32_t layout, int64_t* nnz_out) {
     graph_spec s;
     unsigned char* ig = NULL;
     int st = make_spec(&s, &ig, n, radius, num_global, global_idx, num_random, num_graphs,
-                       causal, seed);
+                       causal, seed, layout);
     if (st) return st;
     int64_t* counts = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
     if (!counts) {
@@ -211,13 +228,14 @@ int oracle_graph_nnz(int64_t n, int32_t radius, int32_t num_global, const int32_
     return st;
 }
 
-int oracle_graph_build(int64_t n, int32_t radius, int32_t num_global, const int32_t* global_idx,
-                       int32_t num_random, int32_t num_graphs, int32_t causal, uint64_t seed,
-                       int64_t* row_ptr, int32_t* col_idx) {
+int oracle_graph_build_layout(int64_t n, int32_t radius, int32_t num_global,
+                              const int32_t* global_idx, int32_t num_random, int32_t num_graphs,
+                              int32_t causal, uint64_t seed, int32_t layout, int64_t* row_ptr,
+                              int32_t* col_idx) {
     graph_spec s;
     unsigned char* ig = NULL;
     int st = make_spec(&s, &ig, n, radius, num_global, global_idx, num_random, num_graphs,
-                       causal, seed);
+                       causal, seed, layout);
     if (st) return st;
     int64_t* counts = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
     if (!counts) {
@@ -237,6 +255,20 @@ int oracle_graph_build(int64_t n, int32_t radius, int32_t num_global, const int3
     free(counts);
     free(ig);
     return st;
+}
+
+int oracle_graph_nnz(int64_t n, int32_t radius, int32_t num_global, const int32_t* global_idx,
+                     int32_t num_random, int32_t num_graphs, int32_t causal, uint64_t seed,
+                     int64_t* nnz_out) {
+    return oracle_graph_nnz_layout(n, radius, num_global, global_idx, num_random, num_graphs,
+                                   causal, seed, 0, nnz_out);
+}
+
+int oracle_graph_build(int64_t n, int32_t radius, int32_t num_global, const int32_t* global_idx,
+                       int32_t num_random, int32_t num_graphs, int32_t causal, uint64_t seed,
+                       int64_t* row_ptr, int32_t* col_idx) {
+    return oracle_graph_build_layout(n, radius, num_global, global_idx, num_random, num_graphs,
+                                     causal, seed, 0, row_ptr, col_idx);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -11,7 +11,8 @@
  *    reading notes, section 2.1 (edge-restricted softmax, eqs. S.1-S.5),
  *    section 2.2 (local window / global / random connection table),
  *    section 2.3 (diffusion operator with general coefficients, eq. S.6),
- *    section 2.4 (PPR recurrence, eq. S.7), section 2.5 (finite-K expansion).
+ *    section 2.4 (PPR recurrence, eq. S.7), section 2.5 (finite-K expansion),
+ *    section 4.5 / table S.7 (the "w uni." evenly spaced extras).
  *  - "1.2.1 Static sparsity: Longformer, BigBird and sliding windows",
  *    section 1 (score eq. 1, mask eq. 2, normalisation eqs. 3-4),
  *    section 1.1 (window eq. 5), section 1.2 (global neighbourhood eq. 12).
@@ -55,6 +56,18 @@ int oracle_graph_build(int64_t n, int32_t radius, int32_t num_global,
                        const int32_t* global_idx, int32_t num_random,
                        int32_t num_graphs, int32_t causal, uint64_t seed,
                        int64_t* row_ptr, int32_t* col_idx);
+
+/* The same two with the extras' layout: 0 = seeded random draws (above),
+ * 1 = evenly spaced ("w uni.", "Diffuser" notes section 4.5, table S.7):
+ * row i takes the pool members of rank floor(q * P / R), q = 0 .. R - 1,
+ * P = |pool(i)| (all of the pool when P <= R); the seed is not used. */
+int oracle_graph_nnz_layout(int64_t n, int32_t radius, int32_t num_global,
+                            const int32_t* global_idx, int32_t num_random, int32_t num_graphs,
+                            int32_t causal, uint64_t seed, int32_t layout, int64_t* nnz_out);
+int oracle_graph_build_layout(int64_t n, int32_t radius, int32_t num_global,
+                              const int32_t* global_idx, int32_t num_random, int32_t num_graphs,
+                              int32_t causal, uint64_t seed, int32_t layout, int64_t* row_ptr,
+                              int32_t* col_idx);
 
 /* Edge scores and edge softmax for one (batch, head):
  * A[e] = exp(s_e - m_i) / sum_u exp(s_u - m_i), s_e = q_i . k_j / sqrt(d). */

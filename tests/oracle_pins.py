@@ -433,6 +433,48 @@ def pin_theta_powers(o):
     assert np.max(np.abs(o.diffuse_theta(A, V, rp[0], cols[0], th) - want)) < 1e-12
 
 
+def _pool_ranks(n, r, G, rp, cols, i):
+    """Pool of row i (positions outside its window and the globals) and the
+    ranks in it of the row's extras."""
+    lo, hi = max(0, i - r), min(n - 1, i + r)
+    Gs = set(G)
+    pool = [j for j in range(n) if (j < lo or j > hi) and j not in Gs]
+    row = set(int(c) for c in cols[rp[i]:rp[i + 1]])
+    extras = sorted(row - set(range(lo, hi + 1)) - Gs)
+    where = {j: t for t, j in enumerate(pool)}
+    return pool, [where[j] for j in extras]
+
+
+def pin_even_extras(o):
+    """Evenly spaced extras ("w uni."): min(R, P) of them; among the first m
+    members of the pool there are exactly ceil(m R / P) (even spacing with
+    the first member taken); the same for every seed and graph; the causal
+    graph is the bidirectional one filtered to j <= i; degrees as for random
+    extras."""
+    for n, r, G, R in [(40, 2, [5, 30], 4), (33, 1, [], 7), (64, 3, [0, 9, 50, 63], 13),
+                       (17, 4, [8], 20)]:
+        rp2, cols2 = o.graph(n, r, G, R, 2, False, 3, layout=1)
+        rp_b, cols_b = o.graph(n, r, G, R, 1, False, 99, layout=1)
+        assert np.array_equal(rp2[0], rp2[1]) and np.array_equal(cols2[0], cols2[1])
+        assert np.array_equal(rp2[0], rp_b[0]) and np.array_equal(cols2[0], cols_b[0])
+        rp, cols = rp2[0], cols2[0]
+        rpr, _ = o.graph(n, r, G, R, 1, False, 3, layout=0)
+        assert np.array_equal(rp, rpr[0]), "degrees differ from the random layout"
+        for i in range(n):
+            if i in G:
+                continue
+            pool, ranks = _pool_ranks(n, r, G, rp, cols, i)
+            P = len(pool)
+            assert len(ranks) == min(R, P), (n, i)
+            if P > R:
+                for m in range(P + 1):
+                    assert sum(t < m for t in ranks) == -(-m * R // P), (n, i, m)
+        rpc, colsc = o.graph(n, r, G, R, 1, True, 3, layout=1)
+        for i in range(n):
+            want = [int(c) for c in cols[rp[i]:rp[i + 1]] if c <= i]
+            assert [int(c) for c in colsc[0][rpc[0][i]:rpc[0][i + 1]]] == want, (n, i)
+
+
 ALL_PINS = [
     pin_splitmix64, pin_edge_counts_8pos, pin_window_closed_form, pin_degrees,
     pin_row_structure, pin_random_uniform, pin_softmax_8pos, pin_row_sums,
@@ -440,4 +482,5 @@ ALL_PINS = [
     pin_dense_brute_force, pin_softmax_attention_reduction, pin_infinite_limit,
     pin_causality, pin_reach, pin_two_hop_global, pin_constant_fixed_point,
     pin_theta_printed_coefficients, pin_theta_three_token, pin_theta_powers,
+    pin_even_extras,
 ]

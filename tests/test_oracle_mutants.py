@@ -52,6 +52,10 @@ MUTANTS = [
      "for (size_t e = 0; e < count; ++e) Z_out[e] = 0.0;"),
     ("theta_powers_of_v", "diffuse_ctx c = {A, V, y, next, d, 0.0, row_ptr, col_idx};",
      "diffuse_ctx c = {A, V, V, next, d, 0.0, row_ptr, col_idx};"),
+    ("even_rank_off_by_one", "if (rank == q * pool / s->num_random) {",
+     "if (rank == (q * pool + s->num_random - 1) / s->num_random) {"),
+    ("even_skip_first", "if (rank == q * pool / s->num_random) {",
+     "if (rank == (q + 1) * pool / s->num_random - 1) {"),
     ("mix_shift", "z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;",
      "z = (z ^ (z >> 26)) * 0x94D049BB133111EBull;"),
 ]
