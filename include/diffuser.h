@@ -97,6 +97,22 @@ typedef struct diffuser_graph diffuser_graph;
 DIFFUSER_API diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stream,
                                      diffuser_graph** out);
 
+/* Layouts of the extras Rnd(i). */
+enum {
+    DIFFUSER_EXTRAS_RANDOM = 0,   /* the seeded uniform draws above */
+    DIFFUSER_EXTRAS_EVEN = 1      /* evenly spaced ("w uni.", "Diffuser" notes section 4.5,
+                                     table S.7): the pool members of rank
+                                     floor(q * P / R), q = 0 .. R - 1, in ascending order;
+                                     the whole pool when P <= R; seed unused */
+};
+
+/* As diffuser_build_graph, with the extras in `layout`
+ * (DIFFUSER_EXTRAS_RANDOM or DIFFUSER_EXTRAS_EVEN; anything else gives
+ * DIFFUSER_ERR_INVALID_ARG). diffuser_build_graph is layout RANDOM. */
+DIFFUSER_API diffuser_status diffuser_build_graph_layout(const diffuser_graph_desc* desc,
+                                            int32_t layout, void* stream,
+                                            diffuser_graph** out);
+
 /* Imports caller-given CSR graphs (HOST arrays): row_ptr int64
  * [num_graphs][n+1] with each graph's row_ptr starting at 0, col_idx int32
  * = the graphs' columns concatenated. Each row must be strictly ascending,

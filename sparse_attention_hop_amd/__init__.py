@@ -6,12 +6,14 @@ ctypes. PyTorch supplies device memory and the current stream. There is no
 fallback: if the library is missing, every call raises.
 
 Functions mirror the C ABI names:
-  build_graph     -> diffuser_build_graph
+  build_graph     -> diffuser_build_graph (diffuser_build_graph_layout with layout=)
   graph_from_csr  -> diffuser_graph_from_csr
   workspace_size  -> diffuser_attn_workspace_size
   attn            -> diffuser_attn
   scores_softmax  -> diffuser_scores_softmax
   diffuse         -> diffuser_diffuse
+  attn_theta      -> diffuser_attn_theta
+  diffuse_theta   -> diffuser_diffuse_theta
 """
 from __future__ import annotations
 
@@ -33,7 +35,8 @@ STATUS_NAMES = {
 
 # Every symbol the header declares.
 ABI_SYMBOLS = (
-    "diffuser_build_graph", "diffuser_graph_from_csr", "diffuser_graph_info",
+    "diffuser_build_graph", "diffuser_build_graph_layout", "diffuser_graph_from_csr",
+    "diffuser_graph_info",
     "diffuser_graph_copy_csr", "diffuser_graph_copy_slots", "diffuser_graph_destroy",
     "diffuser_attn_workspace_size",
     "diffuser_attn", "diffuser_scores_softmax", "diffuser_diffuse",
@@ -79,6 +82,9 @@ def load_library(path: str = LIB_PATH):
     st = ctypes.c_int
     lib.diffuser_build_graph.argtypes = [ctypes.POINTER(_GraphDesc), p, ctypes.POINTER(p)]
     lib.diffuser_build_graph.restype = st
+    lib.diffuser_build_graph_layout.argtypes = [ctypes.POINTER(_GraphDesc), i32, p,
+                                                ctypes.POINTER(p)]
+    lib.diffuser_build_graph_layout.restype = st
     lib.diffuser_graph_from_csr.argtypes = [i64, i32, p, p, p, ctypes.POINTER(p)]
     lib.diffuser_graph_from_csr.restype = st
     lib.diffuser_graph_info.argtypes = [p, p, p, p, p]
@@ -207,18 +213,30 @@ class Graph:
             pass
 
 
+EXTRAS_RANDOM = 0   # seeded uniform draws
+EXTRAS_EVEN = 1     # evenly spaced over each row's pool
+
+
 def build_graph(n: int, radius: int, global_idx: Sequence[int], num_random: int,
-                num_graphs: int = 1, causal: bool = False, seed: int = 0) -> Graph:
+                num_graphs: int = 1, causal: bool = False, seed: int = 0,
+                layout: int = EXTRAS_RANDOM) -> Graph:
+    """diffuser_build_graph (layout EXTRAS_RANDOM) or
+    diffuser_build_graph_layout."""
     lib = load_library()
     g = np.ascontiguousarray(np.asarray(list(global_idx), dtype=np.int32))
     desc = _GraphDesc(n, radius, g.size, g.ctypes.data if g.size else None, num_random,
                       num_graphs, int(bool(causal)), seed)
     out = ctypes.c_void_p()
-    _check(lib.diffuser_build_graph(ctypes.byref(desc), ctypes.c_void_p(_stream_handle()),
-                                    ctypes.byref(out)))
+    if layout == EXTRAS_RANDOM:
+        _check(lib.diffuser_build_graph(ctypes.byref(desc), ctypes.c_void_p(_stream_handle()),
+                                        ctypes.byref(out)))
+    else:
+        _check(lib.diffuser_build_graph_layout(ctypes.byref(desc), int(layout),
+                                               ctypes.c_void_p(_stream_handle()),
+                                               ctypes.byref(out)))
     return Graph(out.value, dict(n=n, radius=radius, global_idx=tuple(g.tolist()),
                                  num_random=num_random, num_graphs=num_graphs,
-                                 causal=bool(causal), seed=seed))
+                                 causal=bool(causal), seed=seed, layout=int(layout)))
 
 
 def graph_from_csr(n: int, row_ptr, col_idx) -> Graph:

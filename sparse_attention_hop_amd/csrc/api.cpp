@@ -265,8 +265,15 @@ const char* diffuser_last_error(void) { return g_last_error.c_str(); }
 
 diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stream,
                                      diffuser_graph** out) {
+    return diffuser_build_graph_layout(desc, DIFFUSER_EXTRAS_RANDOM, stream, out);
+}
+
+diffuser_status diffuser_build_graph_layout(const diffuser_graph_desc* desc, int32_t layout,
+                                            void* stream, diffuser_graph** out) {
     g_last_error.clear();
     if (!desc || !out) return fail(DIFFUSER_ERR_INVALID_ARG, "desc and out must be non-NULL");
+    if (layout != DIFFUSER_EXTRAS_RANDOM && layout != DIFFUSER_EXTRAS_EVEN)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "layout must be DIFFUSER_EXTRAS_RANDOM or _EVEN");
     const int64_t n = desc->n;
     if (n < 1 || n > kMaxN) return fail(DIFFUSER_ERR_INVALID_ARG, "n must lie in [1, 2^24]");
     if (desc->window_radius < 0) return fail(DIFFUSER_ERR_INVALID_ARG, "window_radius < 0");
@@ -305,6 +312,7 @@ diffuser_status diffuser_build_graph(const diffuser_graph_desc* desc, void* stre
     g->rnd_width = (int32_t)std::min<int64_t>(desc->num_random, n);
     g->causal = desc->causal;
     g->seed = desc->seed;
+    g->random_layout = layout;
     g->scheduled = n <= kMaxScheduledN;
     hipGetDevice(&g->device);
 

@@ -67,11 +67,26 @@ __device__ __forceinline__ bool is_global(const int32_t* G, int32_t g, int64_t j
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// The member of rank t (0-based, ascending) of [a, b] minus the globals;
+// the caller guarantees it exists.
+__device__ __forceinline__ int64_t nth_outside_globals(const int32_t* G, int32_t g, int64_t a,
+                                                       int64_t b, int64_t t) {
+    const int32_t ga = count_less(G, g, a);
+    int64_t lo = a + t, hi = b;   // the answer lies in [a + t, min(b, a + t + g)]
+    if (hi > a + t + g) hi = a + t + g;
+    while (lo < hi) {             // smallest j with |[a, j] \ G| >= t + 1
+        const int64_t mid = (lo + hi) >> 1;
+        const int64_t have = (mid - a + 1) - (count_less(G, g, mid + 1) - ga);
+        if (have >= t + 1) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+}
+
 __host__ __device__ __forceinline__ int64_t round8(int64_t x) { return (x + 7) & ~7ll; }
 
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int32_t R,
-            int32_t rnd_width, int32_t causal, int32_t scheduled, uint64_t seed,
+            int32_t rnd_width, int32_t causal, int32_t scheduled, uint64_t seed, int32_t even,
             int32_t* __restrict__ deg,
             int32_t* __restrict__ slots, int32_t* __restrict__ rnd,
             int32_t* __restrict__ rnd_cnt, int32_t* __restrict__ status) {
@@ -110,6 +125,22 @@ void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
             if (in_pool && pos < rnd_width) out[pos] = (int32_t)j;
             m += __popcll(mask);
         }
+    } else if (even) {
+        // Evenly spaced extras: pool members of rank q * pool / R, ascending.
+        int32_t* list = taken[wave];
+        const int64_t below_lo = lo - g_before;   // pool members left of the window
+        for (int32_t q = lane; q < R; q += kWave) {
+            const int64_t t = (int64_t)q * pool / R;
+            const int64_t j = t < below_lo ? nth_outside_globals(G, g, 0, lo - 1, t)
+                                           : nth_outside_globals(G, g, hi + 1, n - 1,
+                                                                 t - below_lo);
+            list[q] = (int32_t)j;
+            if (q < rnd_width) out[q] = (int32_t)j;
+        }
+        m = R;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     } else {
         int32_t* list = taken[wave];
         const uint64_t ctr_row = ((uint64_t)(gr * n + i)) << 20;
@@ -447,7 +478,8 @@ hipError_t launch_draw(const diffuser_graph& g, int32_t* deg, int32_t* slots, in
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
     hipLaunchKernelGGL(k_draw, grid, dim3(kWave * kWavesPerBlock), 0, st, g.n, g.radius,
                        g.d_global, g.num_global, g.num_random, g.rnd_width, g.causal,
-                       (int32_t)g.scheduled, g.seed, deg, slots, g.d_rnd, g.d_rnd_cnt, status);
+                       (int32_t)g.scheduled, g.seed, g.random_layout, deg, slots, g.d_rnd,
+                       g.d_rnd_cnt, status);
     return hipGetLastError();
 }
 

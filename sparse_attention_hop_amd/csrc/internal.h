@@ -45,6 +45,7 @@ struct diffuser_graph {
     int32_t rnd_width = 0;    // ELL width of the random-column table
     int32_t causal = 0;
     uint64_t seed = 0;
+    int32_t random_layout = 0;   // DIFFUSER_EXTRAS_RANDOM or DIFFUSER_EXTRAS_EVEN
     int device = 0;
 
     // Ascending CSR (what the graph is).

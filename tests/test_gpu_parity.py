@@ -590,3 +590,50 @@ def test_theta_invalid():
         with pytest.raises(sah.DiffuserError) as ei:
             sah.attn_theta(x, x, x, g, bad)
         assert ei.value.status_name == "DIFFUSER_ERR_INVALID_ARG", bad
+
+
+# ---------------------------------------------------------------------------
+# Evenly spaced extras ("w uni.")
+# ---------------------------------------------------------------------------
+
+EVEN_SPECS = [
+    # n, r, G, R, num_graphs, causal
+    (40, 2, [5, 30], 4, 1, False),
+    (513, 16, [3, 200], 20, 2, False),
+    (1100, 50, [0, 1, 2, 700, 1099], 40, 1, True),
+    (64, 3, [0, 9, 50, 63], 100, 1, False),          # pool smaller than R
+    (4096, 64, list(range(64)), 64, 8, False),       # headline shape
+    (16384, 128, [k * 128 for k in range(128)], 128, 1, False),
+]
+
+
+@pytest.mark.parametrize("spec", EVEN_SPECS, ids=lambda s: f"n{s[0]}r{s[1]}R{s[3]}c{int(s[5])}")
+def test_even_extras_csr_bitexact(orc, spec):
+    n, r, G, R, ng, causal = spec
+    g = sah.build_graph(n, r, G, R, ng, causal, 5, layout=sah.EXTRAS_EVEN)
+    rp, cols = orc.graph(n, r, G, R, ng, causal, 5, layout=1)
+    for gr in range(ng):
+        grp, gcols = g.copy_csr(gr)
+        assert np.array_equal(grp, rp[gr]), f"row_ptr mismatch in graph {gr}"
+        assert np.array_equal(gcols, cols[gr]), f"col_idx mismatch in graph {gr}"
+        sr, sc = g.copy_slots(gr)
+        pu.slot_permutation(sr, sc, rp[gr], cols[gr])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_even_extras_attn(orc, causal):
+    n, r, G, R = 1100, 20, [0, 1, 700], 40
+    g = sah.build_graph(n, r, G, R, 1, causal, 5, layout=sah.EXTRAS_EVEN)
+    rp, cols = orc.graph(n, r, G, R, 1, causal, 5, layout=1)
+    shape = (1, 2, n, 64)
+    q, k, v = (make_tensor(shape, 51 + i, torch.bfloat16) for i in range(3))
+    z = _as64(sah.attn(q.to(DEV), k.to(DEV), v.to(DEV), g, 5, 0.1))
+    for h in range(2):
+        ref = orc.attn(_as64(q[0, h]), _as64(k[0, h]), _as64(v[0, h]), rp[0], cols[0], 5, 0.1)
+        pu.assert_z_close(z[0, h], ref, "bf16", f"even h={h}")
+
+
+def test_build_layout_invalid():
+    with pytest.raises(sah.DiffuserError) as ei:
+        sah.build_graph(64, 2, [0], 3, 1, False, 5, layout=2)
+    assert ei.value.status_name == "DIFFUSER_ERR_INVALID_ARG"
