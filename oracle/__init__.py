@@ -59,6 +59,9 @@ def _bind(lib):
         f.argtypes = [p, p, i64, i32, p, p, p, i32]
     lib.oracle_diffuse.restype = ctypes.c_int
     lib.oracle_diffuse.argtypes = [p, p, i64, i32, p, p, i32, ctypes.c_double, p, i32]
+    lib.oracle_attn_backward.restype = ctypes.c_int
+    lib.oracle_attn_backward.argtypes = [p, p, p, p, i64, i32, p, p, i32, ctypes.c_double, p, p,
+                                         p]
     lib.oracle_diffuse_theta.restype = ctypes.c_int
     lib.oracle_diffuse_theta.argtypes = [p, p, i64, i32, p, p, i32, p, p, i32]
     return lib
@@ -179,6 +182,18 @@ class Oracle:
         """Whole path with general diffusion coefficients for one (batch, head)."""
         A = self.scores_softmax(Q, K, row_ptr, col_idx, threads)
         return self.diffuse_theta(A, V, row_ptr, col_idx, theta, threads)
+
+    def attn_backward(self, Q, K, V, dZ, row_ptr, col_idx, K_steps, alpha):
+        """(dQ, dK, dV): gradients of sum(dZ * attn(Q, K, V)) for one (batch, head)."""
+        Q, K, V, dZ = (np.ascontiguousarray(x, dtype=np.float64) for x in (Q, K, V, dZ))
+        rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+        ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+        n, d = Q.shape
+        dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+        _check(self.lib.oracle_attn_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dZ), n, d, _ptr(rp),
+                                             _ptr(ci), K_steps, float(alpha), _ptr(dQ), _ptr(dK),
+                                             _ptr(dV)), "oracle_attn_backward")
+        return dQ, dK, dV
 
     def attn(self, Q, K, V, row_ptr, col_idx, K_steps, alpha, threads=1):
         """Whole path for one (batch, head): scores, softmax, K diffusion steps."""

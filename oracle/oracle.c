@@ -454,3 +454,83 @@ int oracle_diffuse_theta(const double* A, const double* V, int64_t n, int32_t d,
     free(next);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward of the whole path for one (batch, head): the chain rule through  */
+/* the recurrence (eq. S.7), the edge softmax (eqs. S.1-S.5) and the scores. */
+/* With G_K = dZ, for k = K-1 .. 0:                                          */
+/*   dA_ij += (1 - alpha) G_{k+1}[i] . Z_k[j]   (edges),                     */
+/*   dV    += alpha G_{k+1},                                                 */
+/*   G_k    = (1 - alpha) A^T G_{k+1};                                       */
+/* then dV += G_0 (Z_0 = V), dS_ij = A_ij (dA_ij - sum_u A_iu dA_iu),       */
+/* dQ_i = sum_j dS_ij k_j / sqrt(d), dK_j = sum_i dS_ij q_i / sqrt(d).     */
+/* Serial; column sums run over edges in CSR order (ascending rows).        */
+/* ------------------------------------------------------------------------ */
+
+int oracle_attn_backward(const double* Q, const double* K, const double* V, const double* dZ,
+                         int64_t n, int32_t d, const int64_t* row_ptr, const int32_t* col_idx,
+                         int32_t K_steps, double alpha, double* dQ, double* dK, double* dV) {
+    if (check_csr(n, d, row_ptr, col_idx) || !Q || !K || !V || !dZ || !dQ || !dK || !dV ||
+        K_steps < 0 || !(alpha >= 0.0 && alpha <= 1.0))
+        return -1;
+    const int64_t nnz = row_ptr[n];
+    const size_t cnt = (size_t)n * (size_t)d;
+    double* A = (double*)malloc(sizeof(double) * (size_t)(nnz > 0 ? nnz : 1));
+    double* dA = (double*)calloc((size_t)(nnz > 0 ? nnz : 1), sizeof(double));
+    double* Zs = (double*)malloc(sizeof(double) * cnt * (size_t)(K_steps > 0 ? K_steps : 1));
+    double* G = (double*)malloc(sizeof(double) * cnt);
+    double* Gn = (double*)malloc(sizeof(double) * cnt);
+    int st = (A && dA && Zs && G && Gn) ? 0 : -1;
+    if (st == 0) st = oracle_scores_softmax(Q, K, n, d, row_ptr, col_idx, A, 1);
+    if (st == 0) {
+        /* Forward states Z_0 .. Z_{K-1}. */
+        if (K_steps > 0) memcpy(Zs, V, sizeof(double) * cnt);
+        for (int32_t k = 1; k < K_steps; ++k) {
+            diffuse_ctx c = {A, V, Zs + (size_t)(k - 1) * cnt, Zs + (size_t)k * cnt, d, alpha,
+                             row_ptr, col_idx};
+            parallel_rows(diffuse_row, &c, n, 1);
+        }
+        memcpy(G, dZ, sizeof(double) * cnt);
+        for (size_t e = 0; e < cnt; ++e) dV[e] = 0.0;
+        for (int32_t k = K_steps - 1; k >= 0; --k) {
+            const double* Zk = Zs + (size_t)k * cnt;
+            for (size_t e = 0; e < cnt; ++e) Gn[e] = 0.0;
+            for (int64_t i = 0; i < n; ++i) {
+                const double* gi = G + i * d;
+                for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+                    const int64_t j = col_idx[e];
+                    const double* zj = Zk + j * d;
+                    double dot = 0.0;
+                    for (int32_t ch = 0; ch < d; ++ch) dot += gi[ch] * zj[ch];
+                    dA[e] += (1.0 - alpha) * dot;
+                    double* gj = Gn + j * d;
+                    for (int32_t ch = 0; ch < d; ++ch) gj[ch] += (1.0 - alpha) * A[e] * gi[ch];
+                }
+            }
+            for (size_t e = 0; e < cnt; ++e) dV[e] += alpha * G[e];
+            memcpy(G, Gn, sizeof(double) * cnt);
+        }
+        for (size_t e = 0; e < cnt; ++e) dV[e] += G[e];
+        /* Softmax and score backward. */
+        const double scale = 1.0 / sqrt((double)d);
+        for (size_t e = 0; e < cnt; ++e) dQ[e] = dK[e] = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            double s = 0.0;
+            for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) s += A[e] * dA[e];
+            for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+                const double ds = A[e] * (dA[e] - s) * scale;
+                const int64_t j = col_idx[e];
+                for (int32_t ch = 0; ch < d; ++ch) {
+                    dQ[i * d + ch] += ds * K[j * d + ch];
+                    dK[j * d + ch] += ds * Q[i * d + ch];
+                }
+            }
+        }
+    }
+    free(A);
+    free(dA);
+    free(Zs);
+    free(G);
+    free(Gn);
+    return st;
+}

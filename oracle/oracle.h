@@ -91,6 +91,12 @@ int oracle_diffuse_theta(const double* A, const double* V, int64_t n, int32_t d,
                          int32_t K_steps, const double* theta, double* Z_out,
                          int32_t threads);
 
+/* Gradients of sum(dZ * Z) for the whole path of one (batch, head) (scores,
+ * edge softmax, K_steps PPR steps): dQ, dK [n][d], dV [n][d]. */
+int oracle_attn_backward(const double* Q, const double* K, const double* V, const double* dZ,
+                         int64_t n, int32_t d, const int64_t* row_ptr, const int32_t* col_idx,
+                         int32_t K_steps, double alpha, double* dQ, double* dK, double* dV);
+
 #ifdef __cplusplus
 }
 #endif

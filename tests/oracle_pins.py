@@ -475,6 +475,42 @@ def pin_even_extras(o):
             assert [int(c) for c in colsc[0][rpc[0][i]:rpc[0][i + 1]]] == want, (n, i)
 
 
+def pin_backward_finite_differences(o):
+    """The gradients of sum(dZ * Z) match central differences of the oracle's
+    own forward pass in every coordinate of Q, K and V (bidirectional graph
+    with a global row; causal graph)."""
+    rng = np.random.default_rng(21)
+    for n, r, G, R, causal, K, alpha in [(24, 2, [5], 3, False, 3, 0.2),
+                                         (20, 1, [0, 13], 4, True, 2, 0.1)]:
+        rp, cols = o.graph(n, r, G, R, 1, causal, 31)
+        rp, cols = rp[0], cols[0]
+        Q, Kx, V, dZ = (rng.standard_normal((n, 3)) for _ in range(4))
+        dQ, dK, dV = o.attn_backward(Q, Kx, V, dZ, rp, cols, K, alpha)
+
+        def loss(q, k, v):
+            return float((dZ * o.attn(q, k, v, rp, cols, K, alpha)).sum())
+
+        h = 1e-6
+        for which, grad in ((0, dQ), (1, dK), (2, dV)):
+            for idx in np.ndindex(n, 3):
+                args_p = [Q.copy(), Kx.copy(), V.copy()]
+                args_m = [Q.copy(), Kx.copy(), V.copy()]
+                args_p[which][idx] += h
+                args_m[which][idx] -= h
+                fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+                assert abs(fd - grad[idx]) < 1e-7 * max(1.0, abs(fd)), (which, idx, fd, grad[idx])
+
+
+def pin_backward_special_cases(o):
+    """alpha = 1 or K = 0 make Z = V: then dV = dZ and dQ = dK = 0 exactly."""
+    rng = np.random.default_rng(22)
+    rp, cols = o.graph(16, 1, [3], 2, 1, False, 4)
+    Q, Kx, V, dZ = (rng.standard_normal((16, 4)) for _ in range(4))
+    for K, alpha in ((3, 1.0), (0, 0.3)):
+        dQ, dK, dV = o.attn_backward(Q, Kx, V, dZ, rp[0], cols[0], K, alpha)
+        assert np.array_equal(dV, dZ) and not dQ.any() and not dK.any(), (K, alpha)
+
+
 ALL_PINS = [
     pin_splitmix64, pin_edge_counts_8pos, pin_window_closed_form, pin_degrees,
     pin_row_structure, pin_random_uniform, pin_softmax_8pos, pin_row_sums,
@@ -482,5 +518,5 @@ ALL_PINS = [
     pin_dense_brute_force, pin_softmax_attention_reduction, pin_infinite_limit,
     pin_causality, pin_reach, pin_two_hop_global, pin_constant_fixed_point,
     pin_theta_printed_coefficients, pin_theta_three_token, pin_theta_powers,
-    pin_even_extras,
+    pin_even_extras, pin_backward_finite_differences, pin_backward_special_cases,
 ]

@@ -56,6 +56,13 @@ MUTANTS = [
      "if (rank == (q * pool + s->num_random - 1) / s->num_random) {"),
     ("even_skip_first", "if (rank == q * pool / s->num_random) {",
      "if (rank == (q + 1) * pool / s->num_random - 1) {"),
+    ("backward_no_softmax_centering", "const double ds = A[e] * (dA[e] - s) * scale;",
+     "const double ds = A[e] * dA[e] * scale;"),
+    ("backward_untransposed", "double* gj = Gn + j * d;", "double* gj = Gn + i * d;"),
+    ("backward_no_input_term", "for (size_t e = 0; e < cnt; ++e) dV[e] += G[e];",
+     "(void)0;"),
+    ("backward_stale_state", "const double* Zk = Zs + (size_t)k * cnt;",
+     "const double* Zk = Zs;"),
     ("mix_shift", "z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;",
      "z = (z ^ (z >> 26)) * 0x94D049BB133111EBull;"),
 ]
