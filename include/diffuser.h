@@ -221,6 +221,30 @@ DIFFUSER_API diffuser_status diffuser_diffuse_theta(const void* A, const void* V
                                        const float* theta, void* Z, void* workspace,
                                        size_t ws_bytes, void* stream);
 
+/*
+ * Backward of diffuser_attn (the chain rule through the recurrence of
+ * "Diffuser" notes section 2.4, eq. S.7, the edge softmax of section 2.1,
+ * eqs. S.1-S.5, and the scores): given dZ = dL/dZ, writes dQ, dK, dV (the
+ * gradients of L through Z). Q, K, V, dZ, dQ, dK, dV: [B][H][n][d] of
+ * `dtype` (d_h = d_v = d); accumulation and every intermediate are fp32.
+ * The workspace (size from diffuser_attn_backward_workspace_size, about
+ * (2 slots + (K_steps + 3) n d) * 4 bytes per (b, h)) holds A, dA, the
+ * states Z_0 .. Z_{K-1}, the backward states and dV. The first call on a
+ * graph builds its column index (device memory owned by the graph, freed
+ * with it; built once, under a lock, synchronising `stream`). Outputs must
+ * not overlap inputs, each other or the workspace. Errors as for
+ * diffuser_attn.
+ */
+DIFFUSER_API diffuser_status diffuser_attn_backward_workspace_size(const diffuser_graph* g, int32_t B,
+                                                      int32_t H, int32_t d, int32_t K_steps,
+                                                      diffuser_dtype dtype, size_t* bytes);
+DIFFUSER_API diffuser_status diffuser_attn_backward(const void* Q, const void* K, const void* V,
+                                        const void* dZ, diffuser_dtype dtype, int32_t B,
+                                        int32_t H, int32_t d, const diffuser_graph* g,
+                                        int32_t K_steps, float alpha, void* dQ, void* dK,
+                                        void* dV, void* workspace, size_t ws_bytes,
+                                        void* stream);
+
 /* Static string for a status code. */
 DIFFUSER_API const char* diffuser_status_string(diffuser_status s);
 

@@ -12,6 +12,7 @@ Functions mirror the C ABI names:
   attn            -> diffuser_attn
   scores_softmax  -> diffuser_scores_softmax
   diffuse         -> diffuser_diffuse
+  attn_backward   -> diffuser_attn_backward (+ _workspace_size)
   attn_theta      -> diffuser_attn_theta
   diffuse_theta   -> diffuser_diffuse_theta
 """
@@ -41,6 +42,7 @@ ABI_SYMBOLS = (
     "diffuser_attn_workspace_size",
     "diffuser_attn", "diffuser_scores_softmax", "diffuser_diffuse",
     "diffuser_attn_theta", "diffuser_diffuse_theta",
+    "diffuser_attn_backward_workspace_size", "diffuser_attn_backward",
     "diffuser_status_string", "diffuser_last_error",
 )
 
@@ -104,6 +106,12 @@ def load_library(path: str = LIB_PATH):
     lib.diffuser_scores_softmax.restype = st
     lib.diffuser_diffuse.argtypes = [p, p, st, i32, i32, i32, p, i32, ctypes.c_float, p, p, sz, p]
     lib.diffuser_diffuse.restype = st
+    lib.diffuser_attn_backward_workspace_size.argtypes = [p, i32, i32, i32, i32, st,
+                                                          ctypes.POINTER(sz)]
+    lib.diffuser_attn_backward_workspace_size.restype = st
+    lib.diffuser_attn_backward.argtypes = [p, p, p, p, st, i32, i32, i32, p, i32, ctypes.c_float,
+                                           p, p, p, p, sz, p]
+    lib.diffuser_attn_backward.restype = st
     lib.diffuser_attn_theta.argtypes = [p, p, p, st, i32, i32, i32, i32, p, i32, p, p, p, sz, p]
     lib.diffuser_attn_theta.restype = st
     lib.diffuser_diffuse_theta.argtypes = [p, p, st, i32, i32, i32, p, i32, p, p, p, sz, p]
@@ -381,3 +389,28 @@ def diffuse_theta(A, v, graph: Graph, theta, out=None, workspace=None):
                                       graph.handle, K, th, out.data_ptr(), workspace.data_ptr(),
                                       workspace.numel(), ctypes.c_void_p(_stream_handle(v.device))))
     return out
+
+
+def attn_backward(q, k, v, dz, graph: Graph, K: int, alpha: float, workspace=None):
+    """(dq, dk, dv): gradients through attn(q, k, v, graph, K, alpha) of a loss
+    whose gradient with respect to its output is dz."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dz, "dz")):
+        _check_bhnd(t, nm, graph.n)
+    if not (q.shape == k.shape == v.shape == dz.shape) or \
+            not (q.dtype == k.dtype == v.dtype == dz.dtype):
+        raise DiffuserError(1, "q, k, v, dz shapes/dtypes disagree")
+    B, H, _, d = q.shape
+    lib = load_library()
+    need = ctypes.c_size_t()
+    _check(lib.diffuser_attn_backward_workspace_size(graph.handle, B, H, d, K,
+                                                     _dtype_code(q.dtype), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib.diffuser_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dz.data_ptr(),
+                                      _dtype_code(q.dtype), B, H, d, graph.handle, K,
+                                      float(alpha), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel(),
+                                      ctypes.c_void_p(_stream_handle(q.device))))
+    return dq, dk, dv

@@ -67,6 +67,9 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_sched_row);
     hipFree(g->d_sched_j);
     hipFree(g->d_sched_k);
+    hipFree(g->d_col_ptr);
+    hipFree(g->d_col_off_slots);
+    hipFree(g->d_col_slot);
     g->d_row_ptr = nullptr;
     g->d_col_idx = nullptr;
     g->d_col_off = nullptr;
@@ -86,6 +89,9 @@ void free_graph_memory(diffuser_graph* g) {
     g->d_sched_row = nullptr;
     g->d_sched_j = nullptr;
     g->d_sched_k = nullptr;
+    g->d_col_ptr = nullptr;
+    g->d_col_off_slots = nullptr;
+    g->d_col_slot = nullptr;
 }
 
 diffuser_status alloc_status(hipError_t e, const char* what) {
@@ -233,6 +239,98 @@ diffuser_status check_theta(int32_t K_steps, const float* theta) {
     }
     if (std::fabs(sum - 1.0) > 1e-5)
         return fail(DIFFUSER_ERR_INVALID_ARG, "theta must sum to 1");
+    return DIFFUSER_OK;
+}
+
+// Workspace of diffuser_attn_backward (fp32 intermediates): A, dA in the A
+// layout, the states Z_0 .. Z_{K-1}, two G buffers and dV.
+struct bw_layout {
+    size_t a, zs, v, total;
+};
+
+bw_layout backward_layout(const diffuser_graph* g, int32_t B, int32_t H, int32_t d,
+                          int32_t K_steps) {
+    bw_layout w;
+    const size_t cnt = (size_t)B * H * (size_t)g->n * d;
+    w.a = align_up((size_t)total_a_elems(g, B, H) * sizeof(float));
+    w.zs = align_up(cnt * sizeof(float) * (size_t)K_steps);
+    w.v = align_up(cnt * sizeof(float));
+    w.total = 2 * w.a + w.zs + 3 * w.v;
+    return w;
+}
+
+// Builds the graph's column index (once, under bw_mutex): the valid slots
+// of each graph ordered by column, then by row (two stable counting sorts
+// on the host), uploaded with per-graph column offsets.
+diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
+    std::lock_guard<std::mutex> lock(g->bw_mutex);
+    if (g->d_col_ptr != nullptr) return DIFFUSER_OK;
+    const int64_t n = g->n;
+    std::vector<int64_t> col_ptr((size_t)g->num_graphs * (n + 1));
+    std::vector<int64_t> col_off(g->num_graphs + 1, 0);
+    std::vector<int32_t> col_slot;
+    std::vector<int32_t> srow, scol, by_row;
+    std::vector<int64_t> cnt;
+    hipError_t e;
+    for (int32_t gr = 0; gr < g->num_graphs; ++gr) {
+        const int64_t slots = g->slots[gr];
+        srow.resize(slots);
+        scol.resize(slots);
+        if ((e = hipMemcpyAsync(srow.data(), g->d_slot_row + g->slot_off[gr],
+                                sizeof(int32_t) * slots, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+            (e = hipMemcpyAsync(scol.data(), g->d_slot_col + g->slot_off[gr],
+                                sizeof(int32_t) * slots, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+            (e = hipStreamSynchronize(st)) != hipSuccess)
+            return hip_fail(e, "copy of the slot layout for the column index");
+        // Stable counting sort of the valid slots by row ...
+        cnt.assign(n + 1, 0);
+        for (int64_t s = 0; s < slots; ++s)
+            if (scol[s] >= 0) ++cnt[srow[s] + 1];
+        for (int64_t i = 0; i < n; ++i) cnt[i + 1] += cnt[i];
+        const int64_t valid = cnt[n];
+        by_row.resize(valid);
+        for (int64_t s = 0; s < slots; ++s)
+            if (scol[s] >= 0) by_row[cnt[srow[s]]++] = (int32_t)s;
+        // ... then by column, which keeps rows ascending within a column.
+        int64_t* cp = col_ptr.data() + (size_t)gr * (n + 1);
+        for (int64_t j = 0; j <= n; ++j) cp[j] = 0;
+        for (int64_t k = 0; k < valid; ++k) ++cp[scol[by_row[k]] + 1];
+        for (int64_t j = 0; j < n; ++j) cp[j + 1] += cp[j];
+        cnt.assign(cp, cp + n + 1);
+        const size_t base = col_slot.size();
+        col_slot.resize(base + valid);
+        for (int64_t k = 0; k < valid; ++k) {
+            const int32_t s = by_row[k];
+            col_slot[base + cnt[scol[s]]++] = s;
+        }
+        col_off[gr + 1] = (int64_t)col_slot.size();
+    }
+    int64_t *d_ptr = nullptr, *d_off = nullptr;
+    int32_t* d_slot = nullptr;
+    if ((e = dev_alloc(&d_ptr, col_ptr.size())) != hipSuccess ||
+        (e = dev_alloc(&d_off, col_off.size())) != hipSuccess ||
+        (e = dev_alloc(&d_slot, col_slot.size())) != hipSuccess) {
+        hipFree(d_ptr);
+        hipFree(d_off);
+        hipFree(d_slot);
+        return alloc_status(e, "device allocation of the column index");
+    }
+    if ((e = hipMemcpyAsync(d_ptr, col_ptr.data(), sizeof(int64_t) * col_ptr.size(),
+                            hipMemcpyHostToDevice, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(d_off, col_off.data(), sizeof(int64_t) * col_off.size(),
+                            hipMemcpyHostToDevice, st)) != hipSuccess ||
+        (col_slot.size() > 0 &&
+         (e = hipMemcpyAsync(d_slot, col_slot.data(), sizeof(int32_t) * col_slot.size(),
+                             hipMemcpyHostToDevice, st)) != hipSuccess) ||
+        (e = hipStreamSynchronize(st)) != hipSuccess) {
+        hipFree(d_ptr);
+        hipFree(d_off);
+        hipFree(d_slot);
+        return hip_fail(e, "upload of the column index");
+    }
+    g->d_col_ptr = d_ptr;
+    g->d_col_off_slots = d_off;
+    g->d_col_slot = d_slot;
     return DIFFUSER_OK;
 }
 
@@ -751,5 +849,80 @@ diffuser_status diffuser_diffuse_theta(const void* A, const void* V, diffuser_dt
                         stream);
 }
 
+
+diffuser_status diffuser_attn_backward_workspace_size(const diffuser_graph* g, int32_t B,
+                                                     int32_t H, int32_t d, int32_t K_steps,
+                                                     diffuser_dtype dtype, size_t* bytes) {
+    g_last_error.clear();
+    if (!bytes) return fail(DIFFUSER_ERR_INVALID_ARG, "bytes is NULL");
+    if (auto s = check_shape(g, B, H, d, dtype, "d")) return s;
+    if (K_steps < 0) return fail(DIFFUSER_ERR_INVALID_ARG, "K_steps must be >= 0");
+    *bytes = backward_layout(g, B, H, d, K_steps).total;
+    return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_attn_backward(const void* Q, const void* K, const void* V,
+                                       const void* dZ, diffuser_dtype dtype, int32_t B, int32_t H,
+                                       int32_t d, const diffuser_graph* g, int32_t K_steps,
+                                       float alpha, void* dQ, void* dK, void* dV, void* workspace,
+                                       size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (auto s = check_shape(g, B, H, d, dtype, "d")) return s;
+    if (auto s = check_alpha_k(K_steps, alpha)) return s;
+    const size_t bytes = (size_t)B * H * g->n * d * elem_size(dtype);
+    const void* ins[4] = {Q, K, V, dZ};
+    const void* outs[3] = {dQ, dK, dV};
+    const char* in_names[4] = {"Q", "K", "V", "dZ"};
+    const char* out_names[3] = {"dQ", "dK", "dV"};
+    for (int k = 0; k < 4; ++k)
+        if (auto s = check_ptr(ins[k], in_names[k])) return s;
+    for (int k = 0; k < 3; ++k)
+        if (auto s = check_ptr(outs[k], out_names[k])) return s;
+    if (auto s = check_ptr(workspace, "workspace")) return s;
+    const bw_layout w = backward_layout(g, B, H, d, K_steps);
+    if (ws_bytes < w.total) return fail(DIFFUSER_ERR_INVALID_ARG, "workspace too small");
+    for (int k = 0; k < 3; ++k) {
+        for (int l = 0; l < 4; ++l)
+            if (overlaps(outs[k], bytes, ins[l], bytes))
+                return fail(DIFFUSER_ERR_INVALID_ARG, "an output overlaps an input");
+        for (int l = k + 1; l < 3; ++l)
+            if (overlaps(outs[k], bytes, outs[l], bytes))
+                return fail(DIFFUSER_ERR_INVALID_ARG, "outputs overlap");
+        if (overlaps(outs[k], bytes, workspace, ws_bytes))
+            return fail(DIFFUSER_ERR_INVALID_ARG, "an output overlaps the workspace");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (auto s = ensure_col_index(const_cast<diffuser_graph*>(g), st)) return s;
+    char* ws = static_cast<char*>(workspace);
+    BackwardArgs p;
+    p.B = B;
+    p.H = H;
+    p.d = d;
+    p.dtype = dtype;
+    p.K_steps = K_steps;
+    p.alpha = alpha;
+    p.scale = (float)(1.0 / std::sqrt((double)d));
+    p.Q = Q;
+    p.K = K;
+    p.V = V;
+    p.dZ = dZ;
+    p.dQ = dQ;
+    p.dK = dK;
+    p.dVout = dV;
+    p.a_count = total_a_elems(g, B, H);
+    p.A = reinterpret_cast<float*>(ws);
+    p.dA = reinterpret_cast<float*>(ws + w.a);
+    p.Zs = reinterpret_cast<float*>(ws + 2 * w.a);
+    p.G0 = reinterpret_cast<float*>(ws + 2 * w.a + w.zs);
+    p.G1 = reinterpret_cast<float*>(ws + 2 * w.a + w.zs + w.v);
+    p.dV = reinterpret_cast<float*>(ws + 2 * w.a + w.zs + 2 * w.v);
+    const float scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
+    hipError_t e = launch_scores_softmax_f32(*g, attn_shape{B, H, d, dtype}, Q, K, p.A,
+                                             scale_log2, st);
+    if (e != hipSuccess) return hip_fail(e, "score/softmax launch");
+    e = launch_backward(*g, p, st);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return DIFFUSER_OK;
+}
 
 }  // extern "C"

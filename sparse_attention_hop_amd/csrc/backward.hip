@@ -1,0 +1,299 @@
+// Backward of the whole path: the chain rule through the PPR recurrence
+// ("Diffuser" reading notes, section 2.4, eq. S.7), the edge softmax
+// (section 2.1, eqs. S.1-S.5) and the edge scores. For one (b, h), with
+// G_K = dZ and k = K-1 .. 0:
+//   dA_ij += (1 - alpha) G_{k+1}[i] . Z_k[j]      (edges of the graph)
+//   dV    += alpha G_{k+1}
+//   G_k    = (1 - alpha) A^T G_{k+1}
+// then dV += G_0 (Z_0 = V), dS_ij = A_ij (dA_ij - sum_u A_iu dA_iu),
+// dQ_i = sum_j dS_ij k_j / sqrt(d_h), dK_j = sum_i dS_ij q_i / sqrt(d_h).
+//
+// Generic kernels over the weight slots (any built graph, fp32 or bf16
+// storage, d in {16, 32, 64, 128}); every intermediate (A, dA, the states
+// Z_k, G_k, dV) is fp32. Row-wise products walk a row's slots; the
+// transposed ones walk the graph's column index (the slots of each column
+// by ascending row), so every sum has a fixed order.
+#include "internal.h"
+#include "vec.h"
+
+namespace diffuser {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kThreads = kWave * kWavesPerBlock;
+
+__device__ __forceinline__ float ld(const float* p) { return *p; }
+__device__ __forceinline__ float ld(const bf16_t* p) { return bf16_to_f32(p->bits); }
+__device__ __forceinline__ void st(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st(bf16_t* p, float v) { p->bits = (uint16_t)f32_to_bf16(v); }
+
+// Y[i] = a * sum_{slots s of row i} W[s] X[col(s)] + b * U[i], one wave per
+// row, lane = channel (and channel + 64 when D = 128).
+template <typename TX, typename TU, typename TY, int D>
+__global__ __launch_bounds__(kThreads)
+void k_rows(GenericGraph gg, int32_t H, const float* __restrict__ W, const TX* __restrict__ X,
+            const TU* __restrict__ U, TY* __restrict__ Y, float a, float b) {
+    constexpr int CPL = D > kWave ? D / kWave : 1;
+    const int wave = threadIdx.x / kWave, lane = __lane_id();
+    const int64_t n = gg.n;
+    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (i >= n) return;
+    const int32_t bh = blockIdx.y, bb = bh / H, hh = bh - bb * H;
+    const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
+    const RowSlots rs = gg.row(gr, i);
+    const float* Wb = W + a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
+    const TX* Xb = X + (int64_t)bh * n * D;
+    float acc[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) acc[k] = 0.0f;
+    const int64_t cnt = rs.count();
+    for (int64_t e = 0; e < cnt; ++e) {
+        int32_t j;
+        const int64_t s = rs.slot(e, j);
+        if (j < 0) continue;
+        const float w = Wb[s];
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            const int c = lane + kWave * k;
+            if (c < D) acc[k] = fmaf(w, ld(Xb + (int64_t)j * D + c), acc[k]);
+        }
+    }
+    const int64_t o = ((int64_t)bh * n + i) * D;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const int c = lane + kWave * k;
+        if (c < D) {
+            float y = a * acc[k];
+            if (U != nullptr) y += b * ld(U + o + c);
+            st(Y + o + c, y);
+        }
+    }
+}
+
+// Column index of one graph family: col_ptr [graphs][n + 1], col_slot (slot
+// numbers within the graph, ascending row within a column), slot_row.
+struct ColIndex {
+    int64_t n;
+    int32_t num_graphs;
+    const int64_t* col_ptr;
+    const int64_t* col_off;    // [graphs + 1] start of each graph's col_slot run
+    const int32_t* col_slot;
+    const int32_t* slot_row;   // [slots of all graphs]
+    const int64_t* slot_off;   // [graphs + 1]
+};
+
+// Y[j] = a * sum_{slots s of column j} W[s] X[row(s)], one wave per column.
+template <typename TX, typename TY, int D>
+__global__ __launch_bounds__(kThreads)
+void k_cols(ColIndex ci, int32_t H, const float* __restrict__ W, const TX* __restrict__ X,
+            TY* __restrict__ Y, float a) {
+    constexpr int CPL = D > kWave ? D / kWave : 1;
+    const int wave = threadIdx.x / kWave, lane = __lane_id();
+    const int64_t n = ci.n;
+    const int64_t j = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (j >= n) return;
+    const int32_t bh = blockIdx.y, bb = bh / H, hh = bh - bb * H;
+    const int32_t gr = ci.num_graphs == 1 ? 0 : bb;
+    const int64_t* cp = ci.col_ptr + (int64_t)gr * (n + 1);
+    const int32_t* cs = ci.col_slot + ci.col_off[gr];
+    const int32_t* srow = ci.slot_row + ci.slot_off[gr];
+    const float* Wb = W + a_block_offset(ci.slot_off, ci.num_graphs, H, bb, hh);
+    const TX* Xb = X + (int64_t)bh * n * D;
+    float acc[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) acc[k] = 0.0f;
+    for (int64_t e = cp[j]; e < cp[j + 1]; ++e) {
+        const int32_t s = cs[e];
+        const int64_t i = srow[s];
+        const float w = Wb[s];
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            const int c = lane + kWave * k;
+            if (c < D) acc[k] = fmaf(w, ld(Xb + i * D + c), acc[k]);
+        }
+    }
+    const int64_t o = ((int64_t)bh * n + j) * D;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const int c = lane + kWave * k;
+        if (c < D) st(Y + o + c, a * acc[k]);
+    }
+}
+
+// dA[s] += a * G[i] . Z[col(s)] for the slots of row i: groups of L lanes
+// take one slot each (L = D / 4 lanes of 4 channels).
+template <int D>
+__global__ __launch_bounds__(kThreads)
+void k_edge_dots(GenericGraph gg, int32_t H, const float* __restrict__ G,
+                 const float* __restrict__ Z, float* __restrict__ dA, float a) {
+    constexpr int L = D / 4, EPI = kWave / L;
+    const int wave = threadIdx.x / kWave, lane = __lane_id();
+    const int64_t n = gg.n;
+    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (i >= n) return;
+    const int32_t bh = blockIdx.y, bb = bh / H, hh = bh - bb * H;
+    const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
+    const RowSlots rs = gg.row(gr, i);
+    float* dAb = dA + a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
+    const int sub = lane % L, grp = lane / L;
+    const float4 g = *reinterpret_cast<const float4*>(G + ((int64_t)bh * n + i) * D + 4 * sub);
+    const float* Zb = Z + (int64_t)bh * n * D + 4 * sub;
+    const int64_t cnt = rs.count();
+    for (int64_t base = 0; base < cnt; base += EPI) {
+        const int64_t e = base + grp;
+        int32_t j = -1;
+        int64_t s = 0;
+        if (e < cnt) s = rs.slot(e, j);
+        float dot = 0.0f;
+        if (j >= 0) {
+            const float4 z = *reinterpret_cast<const float4*>(Zb + (int64_t)j * D);
+            dot = g.x * z.x + g.y * z.y + g.z * z.z + g.w * z.w;
+        }
+#pragma unroll
+        for (int off = 1; off < L; off <<= 1) dot += __shfl_xor(dot, off);
+        if (j >= 0 && sub == 0) dAb[s] += a * dot;
+    }
+}
+
+// dS = A (dA - sum_row A dA) * scale, in place of dA; one wave per row.
+__global__ __launch_bounds__(kThreads)
+void k_softmax_grad(GenericGraph gg, int32_t H, const float* __restrict__ A,
+                    float* __restrict__ dA, float scale) {
+    const int wave = threadIdx.x / kWave, lane = __lane_id();
+    const int64_t n = gg.n;
+    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (i >= n) return;
+    const int32_t bh = blockIdx.y, bb = bh / H, hh = bh - bb * H;
+    const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
+    const RowSlots rs = gg.row(gr, i);
+    const int64_t off = a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
+    const float* Ab = A + off;
+    float* dAb = dA + off;
+    const int64_t cnt = rs.count();
+    float sum = 0.0f;
+    for (int64_t e = lane; e < cnt; e += kWave) {
+        int32_t j;
+        const int64_t s = rs.slot(e, j);
+        if (j >= 0) sum += Ab[s] * dAb[s];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    for (int64_t e = lane; e < cnt; e += kWave) {
+        int32_t j;
+        const int64_t s = rs.slot(e, j);
+        if (j >= 0) dAb[s] = Ab[s] * (dAb[s] - sum) * scale;
+    }
+}
+
+// y = a * x + b * y elementwise over count values (x of type TX).
+template <typename TX>
+__global__ __launch_bounds__(kThreads)
+void k_axpby(int64_t count, const TX* __restrict__ x, float* __restrict__ y, float a, float b) {
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < count;
+         e += (int64_t)gridDim.x * kThreads)
+        y[e] = a * ld(x + e) + (b == 0.0f ? 0.0f : b * y[e]);
+}
+
+// out = x + y, converted to TY.
+template <typename TY>
+__global__ __launch_bounds__(kThreads)
+void k_sum_to(int64_t count, const float* __restrict__ x, const float* __restrict__ y,
+              TY* __restrict__ out) {
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < count;
+         e += (int64_t)gridDim.x * kThreads)
+        st(out + e, x[e] + y[e]);
+}
+
+// x[e] = 0 for e < count.
+__global__ __launch_bounds__(kThreads)
+void k_zero(int64_t count, float* __restrict__ x) {
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < count;
+         e += (int64_t)gridDim.x * kThreads)
+        x[e] = 0.0f;
+}
+
+dim3 grid_elems(int64_t count) {
+    int64_t blocks = (count + kThreads - 1) / kThreads;
+    if (blocks > 65536) blocks = 65536;
+    return dim3((unsigned)(blocks < 1 ? 1 : blocks));
+}
+
+template <typename T, int D>
+hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_t stream) {
+    const GenericGraph gg = generic_graph(g);
+    ColIndex ci;
+    ci.n = g.n;
+    ci.num_graphs = g.num_graphs;
+    ci.col_ptr = g.d_col_ptr;
+    ci.col_off = g.d_col_off_slots;
+    ci.col_slot = g.d_col_slot;
+    ci.slot_row = g.d_slot_row;
+    ci.slot_off = g.d_slot_off;
+    const int32_t BH = p.B * p.H;
+    const dim3 rows((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)BH);
+    const dim3 blk(kThreads);
+    const int64_t cnt = (int64_t)BH * g.n * D;
+    const T* V = static_cast<const T*>(p.V);
+    const float keep = 1.0f - p.alpha;
+
+    hipLaunchKernelGGL(k_zero, grid_elems(p.a_count), blk, 0, stream, p.a_count, p.dA);
+    // Forward states Z_0 = V, Z_{k+1} = (1 - alpha) A Z_k + alpha V (fp32).
+    if (p.K_steps > 0)
+        hipLaunchKernelGGL((k_axpby<T>), grid_elems(cnt), blk, 0, stream, cnt, V, p.Zs, 1.0f,
+                           0.0f);
+    for (int32_t k = 1; k < p.K_steps; ++k)
+        hipLaunchKernelGGL((k_rows<float, T, float, D>), rows, blk, 0, stream, gg, p.H, p.A,
+                           p.Zs + (size_t)(k - 1) * cnt, V, p.Zs + (size_t)k * cnt, keep,
+                           p.alpha);
+    // G_K = dZ; dV = 0.
+    hipLaunchKernelGGL((k_axpby<T>), grid_elems(cnt), blk, 0, stream, cnt,
+                       static_cast<const T*>(p.dZ), p.G0, 1.0f, 0.0f);
+    float* G = p.G0;
+    float* Gn = p.G1;
+    for (int32_t k = p.K_steps - 1; k >= 0; --k) {
+        hipLaunchKernelGGL((k_edge_dots<D>), rows, blk, 0, stream, gg, p.H, G,
+                           p.Zs + (size_t)k * cnt, p.dA, keep);
+        hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, G, p.dV,
+                           p.alpha, k == p.K_steps - 1 ? 0.0f : 1.0f);
+        hipLaunchKernelGGL((k_cols<float, float, D>), rows, blk, 0, stream, ci, p.H, p.A, G, Gn,
+                           keep);
+        float* t = G;
+        G = Gn;
+        Gn = t;
+    }
+    // dV = (sum of alpha G_{k+1}) + G_0.
+    if (p.K_steps == 0)
+        hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, G, p.dV,
+                           0.0f, 0.0f);
+    hipLaunchKernelGGL((k_sum_to<T>), grid_elems(cnt), blk, 0, stream, cnt, p.dV, G,
+                       static_cast<T*>(p.dVout));
+    // dS, then dQ = dS K and dK = dS^T Q (the 1 / sqrt(d_h) inside dS).
+    hipLaunchKernelGGL(k_softmax_grad, rows, blk, 0, stream, gg, p.H, p.A, p.dA, p.scale);
+    hipLaunchKernelGGL((k_rows<T, T, T, D>), rows, blk, 0, stream, gg, p.H, p.dA,
+                       static_cast<const T*>(p.K), static_cast<const T*>(nullptr),
+                       static_cast<T*>(p.dQ), 1.0f, 0.0f);
+    hipLaunchKernelGGL((k_cols<T, T, D>), rows, blk, 0, stream, ci, p.H, p.dA,
+                       static_cast<const T*>(p.Q), static_cast<T*>(p.dK), 1.0f);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t backward_d(const diffuser_graph& g, const BackwardArgs& p, hipStream_t st) {
+    switch (p.d) {
+        case 16: return backward_t<T, 16>(g, p, st);
+        case 32: return backward_t<T, 32>(g, p, st);
+        case 64: return backward_t<T, 64>(g, p, st);
+        case 128: return backward_t<T, 128>(g, p, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_backward(const diffuser_graph& g, const BackwardArgs& p, hipStream_t st) {
+    if (p.dtype == DIFFUSER_F32) return backward_d<float>(g, p, st);
+    return backward_d<bf16_t>(g, p, st);
+}
+
+}  // namespace diffuser

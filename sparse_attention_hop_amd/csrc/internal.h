@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -105,6 +106,15 @@ struct diffuser_graph {
                                     //   kZeroRow's code for a dummy
     uint16_t* d_sched_k = nullptr;  // [groups][32]: score_row_code of the key row of
                                     //   each slot, in slot order
+
+    // Column index of the weight slots (built on first use by the backward
+    // pass, under bw_mutex): for each graph, col_ptr [n + 1] and, from
+    // col_off_slots[gr], the slot numbers (within the graph) of each column
+    // by ascending row.
+    std::mutex bw_mutex;
+    int64_t* d_col_ptr = nullptr;        // [num_graphs][n + 1]
+    int64_t* d_col_off_slots = nullptr;  // [num_graphs + 1]
+    int32_t* d_col_slot = nullptr;       // [valid slots of all graphs]
 };
 
 namespace diffuser {
@@ -171,5 +181,24 @@ bool fast_diffuse_supported(const diffuser_graph& g, const attn_shape& s);
 hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
                                step_coefs k, hipStream_t st);
+
+// Backward of the whole path (backward.hip). Workspace pointers are fp32:
+// A and dA [a_count] in the A layout, Zs [K_steps][B*H*n*d], G0, G1, dV
+// [B*H*n*d]. d_h == d_v == d.
+struct BackwardArgs {
+    int32_t B, H, d;
+    diffuser_dtype dtype;
+    int32_t K_steps;
+    float alpha, scale;                    // scale = 1 / sqrt(d)
+    const void *Q, *K, *V, *dZ;
+    void *dQ, *dK, *dVout;
+    int64_t a_count;
+    float *A, *dA, *Zs, *G0, *G1, *dV;
+};
+hipError_t launch_backward(const diffuser_graph& g, const BackwardArgs& p, hipStream_t st);
+
+// Normalised edge softmax into fp32 A (generic kernel, any graph).
+hipError_t launch_scores_softmax_f32(const diffuser_graph& g, const attn_shape& s, const void* Q,
+                                     const void* K, float* A, float scale_log2, hipStream_t st);
 
 }  // namespace diffuser

@@ -21,10 +21,10 @@ constexpr int kWavesPerBlock = 4;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <typename T, int D>
+template <typename T, typename TA, int D>
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_scores_softmax(GenericGraph gg, int32_t H, const T* __restrict__ Q,
-                      const T* __restrict__ K, T* __restrict__ A, float* __restrict__ row_scale,
+                      const T* __restrict__ K, TA* __restrict__ A, float* __restrict__ row_scale,
                       float scale_log2) {
     constexpr int E = chunk<T>::kElems;
     constexpr int L = D / E;          // lanes per edge
@@ -40,7 +40,7 @@ void k_scores_softmax(GenericGraph gg, int32_t H, const T* __restrict__ Q,
     const int32_t b = bh / H, h = bh - b * H;
     const int32_t gr = gg.num_graphs == 1 ? 0 : b;
     const RowSlots rs = gg.row(gr, i);
-    T* Ab = A + a_block_offset(gg.slot_off, gg.num_graphs, H, b, h);
+    TA* Ab = A + a_block_offset(gg.slot_off, gg.num_graphs, H, b, h);
     const int64_t e1 = rs.count();
     const int sub = lane % L, grp = lane / L;
 
@@ -100,8 +100,8 @@ void k_scores_softmax(GenericGraph gg, int32_t H, const T* __restrict__ Q,
         for (int off = 1; off < L; off <<= 1) dot += __shfl_xor(dot, off);
         if (e < e1 && sub == 0) {
             const float a = valid ? fast_exp2(dot * scale_log2 - m) * inv : 0.0f;
-            chunk<T>::store1(Ab + slot, a);
-            stored_sum += chunk<T>::round(a);
+            chunk<TA>::store1(Ab + slot, a);
+            stored_sum += chunk<TA>::round(a);
         }
     }
     if (row_scale != nullptr) {
@@ -137,7 +137,7 @@ template <typename T, int D>
 hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
                     void* A, float* row_scale, float scale_log2, hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
-    hipLaunchKernelGGL((k_scores_softmax<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
+    hipLaunchKernelGGL((k_scores_softmax<T, T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
                        generic_graph(g), s.H, static_cast<const T*>(Q),
                        static_cast<const T*>(K), static_cast<T*>(A), row_scale, scale_log2);
     if (g.scheduled)
@@ -159,7 +159,35 @@ hipError_t launch_d(const diffuser_graph& g, const attn_shape& s, const void* Q,
     }
 }
 
+template <typename T, int D>
+hipError_t launch_f32_t(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
+                        float* A, float scale_log2, hipStream_t st) {
+    dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
+    hipLaunchKernelGGL((k_scores_softmax<T, float, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
+                       generic_graph(g), s.H, static_cast<const T*>(Q),
+                       static_cast<const T*>(K), A, nullptr, scale_log2);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_f32_d(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
+                        float* A, float scale_log2, hipStream_t st) {
+    switch (s.d) {
+        case 16: return launch_f32_t<T, 16>(g, s, Q, K, A, scale_log2, st);
+        case 32: return launch_f32_t<T, 32>(g, s, Q, K, A, scale_log2, st);
+        case 64: return launch_f32_t<T, 64>(g, s, Q, K, A, scale_log2, st);
+        case 128: return launch_f32_t<T, 128>(g, s, Q, K, A, scale_log2, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_scores_softmax_f32(const diffuser_graph& g, const attn_shape& s, const void* Q,
+                                     const void* K, float* A, float scale_log2, hipStream_t st) {
+    if (s.dtype == DIFFUSER_F32) return launch_f32_d<float>(g, s, Q, K, A, scale_log2, st);
+    return launch_f32_d<bf16_t>(g, s, Q, K, A, scale_log2, st);
+}
 
 hipError_t launch_scores_softmax(const diffuser_graph& g, const attn_shape& s, const void* Q,
                                  const void* K, void* A, float* row_scale, float scale_log2,

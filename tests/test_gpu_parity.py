@@ -637,3 +637,98 @@ def test_build_layout_invalid():
     with pytest.raises(sah.DiffuserError) as ei:
         sah.build_graph(64, 2, [0], 3, 1, False, 5, layout=2)
     assert ei.value.status_name == "DIFFUSER_ERR_INVALID_ARG"
+
+
+# ---------------------------------------------------------------------------
+# Backward of the whole path
+# ---------------------------------------------------------------------------
+
+def _assert_grad_close(got, ref, dtype, what):
+    """f32: max error <= 1e-4 max|ref|; bf16: the output rounding (relative
+    2^-9) plus fp32 accumulation: |err| <= 2^-8 |ref| + 1e-4 max|ref|."""
+    scale = float(np.abs(ref).max(initial=0.0))
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        assert err.max(initial=0.0) <= 1e-4 * scale + 1e-7, (what, err.max(), scale)
+    else:
+        bound = 2.0 ** -8 * np.abs(ref) + 1e-4 * scale + 1e-7
+        assert np.all(err <= bound), (what, float((err / bound).max()))
+
+
+BACKWARD_CASES = [
+    # n, r, G, R, ng, causal, B, H, d, dtype
+    (300, 6, [0, 150], 9, 1, False, 2, 2, 64, "f32"),
+    (513, 16, [3, 200], 20, 2, False, 2, 1, 64, "bf16"),
+    (700, 20, list(range(0, 700, 7))[:70], 12, 1, True, 1, 2, 32, "bf16"),
+    (257, 3, [], 5, 1, False, 1, 1, 128, "f32"),
+    (129, 2, [64], 4, 1, True, 1, 1, 16, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", BACKWARD_CASES, ids=lambda c: f"n{c[0]}d{c[8]}{c[9]}c{int(c[5])}")
+@pytest.mark.parametrize("K,alpha", [(0, 0.1), (1, 0.3), (3, 0.1), (5, 0.0)])
+def test_backward_small(orc, case, K, alpha):
+    n, r, G, R, ngr, causal, B, H, d, dt = case
+    ng = ngr if ngr in (1, B) else B
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    g = _gpu_graph(n, r, G, R, ng, causal, 43)
+    rp, cols = orc.graph(n, r, G, R, ng, causal, 43)
+    shape = (B, H, n, d)
+    q, k, v, dz = (make_tensor(shape, 81 + i, tdt) for i in range(4))
+    dq, dk, dv = (_as64(x) for x in sah.attn_backward(q.to(DEV), k.to(DEV), v.to(DEV), dz.to(DEV),
+                                                      g, K, alpha))
+    for b in range(B):
+        gr = 0 if ng == 1 else b
+        for h in range(H):
+            rq, rk, rv = orc.attn_backward(_as64(q[b, h]), _as64(k[b, h]), _as64(v[b, h]),
+                                           _as64(dz[b, h]), rp[gr], cols[gr], K, alpha)
+            _assert_grad_close(dq[b, h], rq, dt, f"dQ b={b} h={h}")
+            _assert_grad_close(dk[b, h], rk, dt, f"dK b={b} h={h}")
+            _assert_grad_close(dv[b, h], rv, dt, f"dV b={b} h={h}")
+
+
+def test_backward_imported_csr(orc):
+    """An imported graph (any layout, here a dilated window)."""
+    n, d = 200, 32
+    rows = [sorted({i} | {j for j in range(i - 12, i + 13, 4) if 0 <= j < n}) for i in range(n)]
+    rp = np.zeros(n + 1, dtype=np.int64)
+    rp[1:] = np.cumsum([len(x) for x in rows])
+    cols = np.concatenate([np.array(x, dtype=np.int32) for x in rows])
+    g = sah.graph_from_csr(n, rp[None, :], cols)
+    shape = (1, 2, n, d)
+    q, k, v, dz = (make_tensor(shape, 91 + i, torch.float32) for i in range(4))
+    dq, dk, dv = (_as64(x) for x in sah.attn_backward(q.to(DEV), k.to(DEV), v.to(DEV), dz.to(DEV),
+                                                      g, 4, 0.2))
+    for h in range(2):
+        rq, rk, rv = orc.attn_backward(_as64(q[0, h]), _as64(k[0, h]), _as64(v[0, h]),
+                                       _as64(dz[0, h]), rp, cols, 4, 0.2)
+        _assert_grad_close(dq[0, h], rq, "f32", "dQ")
+        _assert_grad_close(dk[0, h], rk, "f32", "dK")
+        _assert_grad_close(dv[0, h], rv, "f32", "dV")
+
+
+def test_backward_headline_shape(orc):
+    """Headline graph and shape, two sampled (b, h) pairs; repeated calls are
+    bitwise equal."""
+    w = WORKLOADS["mlm4096_bf16"]
+    print(f"\n[parity] backward {w.describe()}", flush=True)
+    g = _gpu_graph(w.n, w.radius, w.global_idx, w.num_random, w.num_graphs, w.causal,
+                   w.graph_seed)
+    rp, cols = orc.graph(w.n, w.radius, w.global_idx, w.num_random, w.num_graphs, w.causal,
+                         w.graph_seed)
+    q, k, v = make_qkv(w)
+    dz = make_tensor(q.shape, 7, torch.bfloat16)
+    args = (q.to(DEV), k.to(DEV), v.to(DEV), dz.to(DEV), g, w.K, w.alpha)
+    out = sah.attn_backward(*args)
+    again = sah.attn_backward(*args)
+    for x, y in zip(out, again):
+        assert torch.equal(x, y)
+    dq, dk, dv = (_as64(x) for x in out)
+    for b, h in [(0, 0), (w.B - 1, w.H - 1)]:
+        gr = 0 if w.num_graphs == 1 else b
+        rq, rk, rv = orc.attn_backward(_as64(q[b, h]), _as64(k[b, h]), _as64(v[b, h]),
+                                       _as64(dz[b, h]), rp[gr], cols[gr], w.K, w.alpha)
+        _assert_grad_close(dq[b, h], rq, "bf16", f"dQ b={b} h={h}")
+        _assert_grad_close(dk[b, h], rk, "bf16", f"dK b={b} h={h}")
+        _assert_grad_close(dv[b, h], rv, "bf16", f"dV b={b} h={h}")
+        print(f"[parity] backward b={b} h={h} ok", flush=True)
