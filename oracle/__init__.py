@@ -67,6 +67,15 @@ def _bind(lib):
     return lib
 
 
+def round_bf16_rne(x):
+    """Nearest bf16 value (ties to even) of each element, via its float32
+    value, as float64."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def load(path: str = LIB_PATH):
     """Loads (building first if absent) the oracle library."""
     global _lib
@@ -194,6 +203,31 @@ class Oracle:
                                              _ptr(ci), K_steps, float(alpha), _ptr(dQ), _ptr(dK),
                                              _ptr(dV)), "oracle_attn_backward")
         return dQ, dK, dV
+
+    def layer_forward(self, X, W_qkv, W_o, H, row_ptr, cols, K_steps, alpha, round_bf16=False,
+                      threads=1):
+        """One layer around the path ("Diffuser" notes sections 2.1 and 2.4):
+        [Q | K | V] = X W_qkv per head, Z per (b, h) by the whole path, Y =
+        concat_h(Z) W_o. X: [B, n, d_model]; row_ptr: [graphs, n+1]; cols: per
+        graph. round_bf16: Q, K, V and Z are held in bf16 (round to nearest
+        even), as a bf16 implementation stores them."""
+        X = np.asarray(X, dtype=np.float64)
+        B, n, _ = X.shape
+        d = W_qkv.shape[1] // (3 * H)
+        T = X @ np.asarray(W_qkv, dtype=np.float64)            # [B, n, 3 H d]
+        if round_bf16:
+            T = round_bf16_rne(T)
+        T = T.reshape(B, n, 3, H, d)
+        Z = np.zeros((B, H, n, d))
+        for b in range(B):
+            gr = 0 if len(cols) == 1 else b
+            for h in range(H):
+                Z[b, h] = self.attn(T[b, :, 0, h], T[b, :, 1, h], T[b, :, 2, h], row_ptr[gr],
+                                    cols[gr], K_steps, alpha, threads)
+        if round_bf16:
+            Z = round_bf16_rne(Z)
+        Zc = Z.transpose(0, 2, 1, 3).reshape(B, n, H * d)
+        return Zc @ np.asarray(W_o, dtype=np.float64)
 
     def attn(self, Q, K, V, row_ptr, col_idx, K_steps, alpha, threads=1):
         """Whole path for one (batch, head): scores, softmax, K diffusion steps."""

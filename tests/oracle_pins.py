@@ -511,6 +511,45 @@ def pin_backward_special_cases(o):
         assert np.array_equal(dV, dZ) and not dQ.any() and not dK.any(), (K, alpha)
 
 
+def pin_bf16_rounding(o):
+    """Round to nearest even on bf16 (8 significant bits): ties go to the
+    even significand."""
+    import oracle as _oracle
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -7, -(1 + 2.0 ** -8 + 2.0 ** -12),
+                  3.0e38, 2.0 ** -130])
+    want = np.array([1.0, 1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -(1 + 2.0 ** -7), 226 * 2.0 ** 120,
+                     2.0 ** -130])
+    got = _oracle.round_bf16_rne(x)
+    assert np.allclose(got, want, rtol=1e-7, atol=0), got
+
+
+def pin_layer_identity(o):
+    """With identity projections (d_model = H d, W_qkv = [I I I], W_o = I)
+    the layer returns each head's attention on its own slice of X, placed
+    back in its slice; consistent permutations of heads leave Y unchanged."""
+    rng = np.random.default_rng(31)
+    B, n, H, d = 2, 20, 3, 4
+    D = H * d
+    rp, cols = o.graph(n, 2, [4], 3, 1, False, 9)
+    X = rng.standard_normal((B, n, D))
+    W_qkv = np.concatenate([np.eye(D)] * 3, axis=1)
+    Y = o.layer_forward(X, W_qkv, np.eye(D), H, rp, cols, 3, 0.2)
+    for b in range(B):
+        for h in range(H):
+            xs = X[b, :, h * d:(h + 1) * d]
+            want = o.attn(xs, xs, xs, rp[0], cols[0], 3, 0.2)
+            assert np.max(np.abs(Y[b, :, h * d:(h + 1) * d] - want)) < 1e-13, (b, h)
+    Wq = rng.standard_normal((D, 3 * H * d))
+    Wo = rng.standard_normal((H * d, D))
+    perm = [2, 0, 1]
+    cols_perm = np.concatenate([np.arange(p * H * d + h * d, p * H * d + (h + 1) * d)
+                                for p in range(3) for h in perm])
+    rows_perm = np.concatenate([np.arange(h * d, (h + 1) * d) for h in perm])
+    Y1 = o.layer_forward(X, Wq, Wo, H, rp, cols, 3, 0.2)
+    Y2 = o.layer_forward(X, Wq[:, cols_perm], Wo[rows_perm], H, rp, cols, 3, 0.2)
+    assert np.max(np.abs(Y1 - Y2)) < 1e-10
+
+
 ALL_PINS = [
     pin_splitmix64, pin_edge_counts_8pos, pin_window_closed_form, pin_degrees,
     pin_row_structure, pin_random_uniform, pin_softmax_8pos, pin_row_sums,
@@ -519,4 +558,5 @@ ALL_PINS = [
     pin_causality, pin_reach, pin_two_hop_global, pin_constant_fixed_point,
     pin_theta_printed_coefficients, pin_theta_three_token, pin_theta_powers,
     pin_even_extras, pin_backward_finite_differences, pin_backward_special_cases,
+    pin_bf16_rounding, pin_layer_identity,
 ]
