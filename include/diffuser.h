@@ -245,6 +245,32 @@ DIFFUSER_API diffuser_status diffuser_attn_backward(const void* Q, const void* K
                                         void* dV, void* workspace, size_t ws_bytes,
                                         void* stream);
 
+/*
+ * One attention layer around the path ("Diffuser" notes section 2.1: the
+ * per-head Q, K, V of the input; section 2.4: head concatenation and the
+ * output projection outside the diffusion module):
+ *   [Q | K | V] = X W_qkv, Z = diffuser_attn(Q, K, V), Y = concat_h(Z) W_o.
+ * X: [B][n][d_model]; W_qkv: [d_model][3 H d], columns p H d + h d + c give
+ * channel c of head h of Q (p = 0), K (1), V (2); W_o: [H d][d_model];
+ * Y: [B][n][d_model]; all of `dtype`, row-major, 16-byte aligned. The two
+ * products are dense GEMMs with fp32 accumulation (rocBLAS, on a handle the
+ * library creates once per device; calls sharing a device are serialised
+ * through it). The workspace (size from diffuser_layer_workspace_size)
+ * holds the projections, Q, K, V, Z, the path's own workspace and the GEMM
+ * library's workspace; no other memory is allocated by the call after the
+ * handle exists. Y must not overlap the inputs or the workspace. Errors as
+ * for diffuser_attn; a GEMM failure gives DIFFUSER_ERR_INTERNAL.
+ */
+DIFFUSER_API diffuser_status diffuser_layer_workspace_size(const diffuser_graph* g, int32_t B,
+                                              int32_t H, int32_t d, int32_t d_model,
+                                              diffuser_dtype dtype, size_t* bytes);
+DIFFUSER_API diffuser_status diffuser_layer_forward(const void* X, const void* W_qkv,
+                                       const void* W_o, diffuser_dtype dtype, int32_t B,
+                                       int32_t H, int32_t d, int32_t d_model,
+                                       const diffuser_graph* g, int32_t K_steps, float alpha,
+                                       void* Y, void* workspace, size_t ws_bytes,
+                                       void* stream);
+
 /* Static string for a status code. */
 DIFFUSER_API const char* diffuser_status_string(diffuser_status s);
 

@@ -13,6 +13,7 @@ Functions mirror the C ABI names:
   scores_softmax  -> diffuser_scores_softmax
   diffuse         -> diffuser_diffuse
   attn_backward   -> diffuser_attn_backward (+ _workspace_size)
+  layer_forward   -> diffuser_layer_forward (+ _workspace_size)
   attn_theta      -> diffuser_attn_theta
   diffuse_theta   -> diffuser_diffuse_theta
 """
@@ -43,6 +44,7 @@ ABI_SYMBOLS = (
     "diffuser_attn", "diffuser_scores_softmax", "diffuser_diffuse",
     "diffuser_attn_theta", "diffuser_diffuse_theta",
     "diffuser_attn_backward_workspace_size", "diffuser_attn_backward",
+    "diffuser_layer_workspace_size", "diffuser_layer_forward",
     "diffuser_status_string", "diffuser_last_error",
 )
 
@@ -112,6 +114,11 @@ def load_library(path: str = LIB_PATH):
     lib.diffuser_attn_backward.argtypes = [p, p, p, p, st, i32, i32, i32, p, i32, ctypes.c_float,
                                            p, p, p, p, sz, p]
     lib.diffuser_attn_backward.restype = st
+    lib.diffuser_layer_workspace_size.argtypes = [p, i32, i32, i32, i32, st, ctypes.POINTER(sz)]
+    lib.diffuser_layer_workspace_size.restype = st
+    lib.diffuser_layer_forward.argtypes = [p, p, p, st, i32, i32, i32, i32, p, i32,
+                                           ctypes.c_float, p, p, sz, p]
+    lib.diffuser_layer_forward.restype = st
     lib.diffuser_attn_theta.argtypes = [p, p, p, st, i32, i32, i32, i32, p, i32, p, p, p, sz, p]
     lib.diffuser_attn_theta.restype = st
     lib.diffuser_diffuse_theta.argtypes = [p, p, st, i32, i32, i32, p, i32, p, p, p, sz, p]
@@ -414,3 +421,32 @@ def attn_backward(q, k, v, dz, graph: Graph, K: int, alpha: float, workspace=Non
                                       workspace.data_ptr(), workspace.numel(),
                                       ctypes.c_void_p(_stream_handle(q.device))))
     return dq, dk, dv
+
+
+def layer_forward(x, w_qkv, w_o, graph: Graph, H: int, K: int, alpha: float, workspace=None):
+    """Y = concat_h(attn(Q, K, V)) w_o with [Q | K | V] = x w_qkv per head.
+    x: [B, n, d_model]; w_qkv: [d_model, 3 H d]; w_o: [H d, d_model]."""
+    torch = _torch()
+    if x.dim() != 3 or x.shape[1] != graph.n or not x.is_cuda or not x.is_contiguous():
+        raise DiffuserError(1, "x must be a contiguous CUDA tensor [B, n, d_model]")
+    B, _, d_model = x.shape
+    if w_qkv.dim() != 2 or w_qkv.shape[0] != d_model or w_qkv.shape[1] % (3 * H):
+        raise DiffuserError(1, "w_qkv must be [d_model, 3 H d]")
+    d = w_qkv.shape[1] // (3 * H)
+    if tuple(w_o.shape) != (H * d, d_model):
+        raise DiffuserError(1, "w_o must be [H d, d_model]")
+    for t in (w_qkv, w_o):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype:
+            raise DiffuserError(1, "weights must be contiguous CUDA tensors of x's dtype")
+    lib = load_library()
+    need = ctypes.c_size_t()
+    _check(lib.diffuser_layer_workspace_size(graph.handle, B, H, d, d_model, _dtype_code(x.dtype),
+                                             ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=x.device)
+    y = torch.empty_like(x)
+    _check(lib.diffuser_layer_forward(x.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(),
+                                      _dtype_code(x.dtype), B, H, d, d_model, graph.handle, K,
+                                      float(alpha), y.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel(), ctypes.c_void_p(_stream_handle(x.device))))
+    return y

@@ -334,6 +334,26 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
     return DIFFUSER_OK;
 }
 
+// Workspace of diffuser_layer_forward: the [B*n][3 H d] projection (reused
+// for the merged heads), Q, K, V, Z, the whole path's own workspace and
+// the GEMM library's workspace.
+constexpr size_t kBlasWorkspace = (size_t)32 << 20;
+
+struct layer_layout {
+    size_t t, h, attn, total;
+};
+
+layer_layout make_layer_layout(const diffuser_graph* g, int32_t B, int32_t H, int32_t d,
+                               diffuser_dtype dtype) {
+    layer_layout w;
+    const size_t es = elem_size(dtype);
+    w.t = align_up((size_t)B * g->n * 3 * H * d * es);
+    w.h = align_up((size_t)B * H * g->n * d * es);
+    w.attn = layout(g, B, H, d, dtype).total;
+    w.total = w.t + 4 * w.h + w.attn + kBlasWorkspace;
+    return w;
+}
+
 }  // namespace
 
 diffuser_status fail(diffuser_status s, const std::string& msg) {
@@ -923,6 +943,62 @@ diffuser_status diffuser_attn_backward(const void* Q, const void* K, const void*
     e = launch_backward(*g, p, st);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_layer_workspace_size(const diffuser_graph* g, int32_t B, int32_t H,
+                                             int32_t d, int32_t d_model, diffuser_dtype dtype,
+                                             size_t* bytes) {
+    g_last_error.clear();
+    if (!bytes) return fail(DIFFUSER_ERR_INVALID_ARG, "bytes is NULL");
+    if (auto s = check_shape(g, B, H, d, dtype, "d")) return s;
+    if (d_model < 1) return fail(DIFFUSER_ERR_INVALID_ARG, "d_model must be >= 1");
+    *bytes = make_layer_layout(g, B, H, d, dtype).total;
+    return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_layer_forward(const void* X, const void* W_qkv, const void* W_o,
+                                       diffuser_dtype dtype, int32_t B, int32_t H, int32_t d,
+                                       int32_t d_model, const diffuser_graph* g, int32_t K_steps,
+                                       float alpha, void* Y, void* workspace, size_t ws_bytes,
+                                       void* stream) {
+    g_last_error.clear();
+    if (auto s = check_shape(g, B, H, d, dtype, "d")) return s;
+    if (d_model < 1) return fail(DIFFUSER_ERR_INVALID_ARG, "d_model must be >= 1");
+    if (auto s = check_alpha_k(K_steps, alpha)) return s;
+    for (auto pr : {std::make_pair(X, "X"), std::make_pair(W_qkv, "W_qkv"),
+                    std::make_pair(W_o, "W_o"), std::make_pair((const void*)Y, "Y"),
+                    std::make_pair((const void*)workspace, "workspace")})
+        if (auto s = check_ptr(pr.first, pr.second)) return s;
+    const layer_layout w = make_layer_layout(g, B, H, d, dtype);
+    if (ws_bytes < w.total) return fail(DIFFUSER_ERR_INVALID_ARG, "workspace too small");
+    const size_t es = elem_size(dtype);
+    const size_t y_bytes = (size_t)B * g->n * d_model * es;
+    if (overlaps(Y, y_bytes, X, y_bytes) || overlaps(Y, y_bytes, workspace, ws_bytes) ||
+        overlaps(Y, y_bytes, W_qkv, (size_t)d_model * 3 * H * d * es) ||
+        overlaps(Y, y_bytes, W_o, (size_t)H * d * d_model * es))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "Y overlaps an input or the workspace");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    void* t = ws;
+    void* q = ws + w.t;
+    void* k = ws + w.t + w.h;
+    void* v = ws + w.t + 2 * w.h;
+    void* z = ws + w.t + 3 * w.h;
+    void* attn_ws = ws + w.t + 4 * w.h;
+    void* blas_ws = ws + w.t + 4 * w.h + w.attn;
+    const int64_t rows = (int64_t)B * g->n;
+    if (auto s = blas_gemm(g->device, dtype, rows, 3 * (int64_t)H * d, d_model, X, W_qkv, t,
+                           blas_ws, kBlasWorkspace, st))
+        return s;
+    hipError_t e = launch_split_heads(dtype, B, (int32_t)g->n, H, d, t, q, k, v, st);
+    if (e != hipSuccess) return hip_fail(e, "head split launch");
+    if (auto s = diffuser_attn(q, k, v, dtype, B, H, d, d, g, K_steps, alpha, z, attn_ws, w.attn,
+                               stream))
+        return s;
+    e = launch_merge_heads(dtype, B, (int32_t)g->n, H, d, z, t, st);
+    if (e != hipSuccess) return hip_fail(e, "head merge launch");
+    return blas_gemm(g->device, dtype, rows, d_model, (int64_t)H * d, t, W_o, Y, blas_ws,
+                     kBlasWorkspace, st);
 }
 
 }  // extern "C"

@@ -197,6 +197,17 @@ struct BackwardArgs {
 };
 hipError_t launch_backward(const diffuser_graph& g, const BackwardArgs& p, hipStream_t st);
 
+// Projections around the path (layer.hip): head split of [B*n][3 H d] into
+// Q, K, V [B][H][n][d]; head merge of Z into [B*n][H d]; a row-major GEMM
+// C[M][N] = A[M][K] B[K][N] on the device's library-owned rocBLAS handle.
+hipError_t launch_split_heads(diffuser_dtype t, int64_t B, int32_t n, int32_t H, int32_t d,
+                              const void* in, void* q, void* k, void* v, hipStream_t st);
+hipError_t launch_merge_heads(diffuser_dtype t, int64_t B, int32_t n, int32_t H, int32_t d,
+                              const void* z, void* out, hipStream_t st);
+diffuser_status blas_gemm(int device, diffuser_dtype t, int64_t M, int64_t N, int64_t K,
+                          const void* A, const void* B, void* C, void* blas_ws,
+                          size_t blas_ws_bytes, hipStream_t st);
+
 // Normalised edge softmax into fp32 A (generic kernel, any graph).
 hipError_t launch_scores_softmax_f32(const diffuser_graph& g, const attn_shape& s, const void* Q,
                                      const void* K, float* A, float scale_log2, hipStream_t st);

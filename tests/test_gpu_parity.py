@@ -732,3 +732,41 @@ def test_backward_headline_shape(orc):
         _assert_grad_close(dk[b, h], rk, "bf16", f"dK b={b} h={h}")
         _assert_grad_close(dv[b, h], rv, "bf16", f"dV b={b} h={h}")
         print(f"[parity] backward b={b} h={h} ok", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# One layer around the path (projections in, head concatenation and
+# output projection out)
+# ---------------------------------------------------------------------------
+
+LAYER_CASES = [
+    # n, r, G, R, ng, B, H, d, d_model, dtype
+    (300, 6, [0, 150], 9, 1, 2, 2, 64, 96, "f32"),
+    (513, 16, [3, 200], 20, 2, 2, 3, 64, 128, "bf16"),
+    (700, 20, list(range(0, 700, 7))[:70], 12, 1, 1, 4, 32, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", LAYER_CASES, ids=lambda c: f"n{c[0]}H{c[6]}d{c[7]}{c[9]}")
+def test_layer_forward(orc, case):
+    n, r, G, R, ngr, B, H, d, dm, dt = case
+    ng = ngr if ngr in (1, B) else B
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    g = _gpu_graph(n, r, G, R, ng, False, 47)
+    rp, cols = orc.graph(n, r, G, R, ng, False, 47)
+    x = make_tensor((B, n, dm), 101, tdt)
+    wq = make_tensor((dm, 3 * H * d), 102, tdt, scale=dm ** -0.5)
+    wo = make_tensor((H * d, dm), 103, tdt, scale=(H * d) ** -0.5)
+    y = _as64(sah.layer_forward(x.to(DEV), wq.to(DEV), wo.to(DEV), g, H, 5, 0.1))
+    ref = orc.layer_forward(_as64(x), _as64(wq), _as64(wo), H, rp, cols, 5, 0.1,
+                            round_bf16=(dt == "bf16"))
+    # Y = Zc W_o: a per-element bound from the bound on Z, carried through
+    # |W_o| column sums, plus one output rounding.
+    colsum = np.abs(_as64(wo)).sum(axis=0)
+    if dt == "f32":
+        zc_mag = np.abs(ref).max()
+        bound = 1e-4 * max(zc_mag, 1.0) * np.ones_like(ref) + 1e-6
+    else:
+        bound = pu.bf16_tolerance(5, 0.1) * colsum[None, None, :] + 2.0 ** -8 * np.abs(ref) + 1e-6
+    err = np.abs(y - ref)
+    assert np.all(err <= bound), float((err / bound).max())
