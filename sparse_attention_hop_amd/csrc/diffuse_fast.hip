@@ -80,7 +80,7 @@ struct FastArgs {
     uint16_t* Zn;
     const float* row_scale;     // [B*H][n] or null
     float keep, restart;
-    int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items;
+    int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items, bh_per_xcd;
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const char LDS_AS* p) {
@@ -375,11 +375,11 @@ void k_diffuse_sched(FastArgs a) {
     const int s16 = lane & 15;         // row (W^T) / channel (Z^T) index
     const uint32_t a8 = 8u * (lane & 3), q4 = (lane >> 2) & 3;   // transposed-read source
 
-    const int32_t item = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
-    if (item >= a.total_items) return;
-    const int32_t per_bh = a.grow_per_bh + a.tiles_per_bh;
-    const int32_t bh = item / per_bh;
-    const int32_t sub = item - bh * per_bh;
+    const WorkItem wi = work_item(blockIdx.x, a.per_xcd, a.total_items, a.grow_per_bh,
+                                  a.tiles_per_bh, a.bh_per_xcd);
+    if (!wi.valid) return;
+    const int32_t bh = wi.bh;
+    const int32_t sub = wi.sub;
     const int32_t b = bh / a.H, h = bh - b * a.H;
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
     const int64_t n = a.n;
@@ -577,7 +577,9 @@ hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, con
     a.tiles_per_bh = (int32_t)((g.n + kTileRows - 1) / kTileRows);
     a.grow_per_bh = (g.num_global + kGrowRows - 1) / kGrowRows;
     a.total_items = BH * (a.tiles_per_bh + a.grow_per_bh);
-    a.per_xcd = (a.total_items + 7) / 8;
+    a.bh_per_xcd = 0;   // (b, h)-ordered runs (measured slightly faster here than tiles-first)
+    a.per_xcd = a.bh_per_xcd > 0 ? a.bh_per_xcd * (a.tiles_per_bh + a.grow_per_bh)
+                                 : (a.total_items + 7) / 8;
     static int attr_device = -1;   // dynamic LDS above 64 KB is enabled per device
     if (attr_device != g.device) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_diffuse_sched),

@@ -60,6 +60,42 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Work item (batch-head pair, sub-item) of workgroup `blk`: XCD blk % 8
+// runs position blk / 8 of its own list. When the pairs split evenly over
+// the 8 XCDs (bh_per_xcd > 0), an XCD's list is its pairs' row tiles
+// (sub >= grow) followed by their global-row items (sub < grow), so the
+// last, partly filled round of workgroups holds the short items; otherwise
+// the lists are consecutive runs of (bh, sub) order.
+struct WorkItem {
+    int32_t bh, sub;
+    bool valid;
+};
+
+__device__ __forceinline__ WorkItem work_item(uint32_t blk, int32_t per_xcd, int32_t total,
+                                              int32_t grow, int32_t tiles, int32_t bh_per_xcd) {
+    const int32_t x = (int32_t)(blk & 7u), pos = (int32_t)(blk >> 3);
+    WorkItem w{0, 0, false};
+    if (bh_per_xcd > 0) {
+        const int32_t nt = bh_per_xcd * tiles;
+        if (pos < nt) {
+            w.bh = x * bh_per_xcd + pos / tiles;
+            w.sub = grow + pos % tiles;
+            w.valid = true;
+        } else if (pos - nt < bh_per_xcd * grow) {
+            w.bh = x * bh_per_xcd + (pos - nt) / grow;
+            w.sub = (pos - nt) % grow;
+            w.valid = true;
+        }
+        return w;
+    }
+    const int32_t item = x * per_xcd + pos;
+    if (item >= total) return w;
+    w.bh = item / (grow + tiles);
+    w.sub = item - w.bh * (grow + tiles);
+    w.valid = true;
+    return w;
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 

@@ -83,7 +83,7 @@ struct ScoreArgs {
     float scale_log2;           // log2(e) / sqrt(d_h)
     int32_t normalized;
     int32_t band_prepass;       // the band window of a row tile fits one buffer
-    int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items;
+    int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items, bh_per_xcd;
 };
 
 // The K operands (channels 8 kg .. + 7 and 32 + 8 kg .. + 7) of the key row
@@ -493,11 +493,11 @@ void k_scores_sched(ScoreArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int kg = lane >> 4, s16 = lane & 15;
 
-    const int32_t item = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
-    if (item >= a.total_items) return;
-    const int32_t per_bh = a.grow_per_bh + a.tiles_per_bh;
-    const int32_t bh = item / per_bh;
-    const int32_t sub = item - bh * per_bh;
+    const WorkItem wi = work_item(blockIdx.x, a.per_xcd, a.total_items, a.grow_per_bh,
+                                  a.tiles_per_bh, a.bh_per_xcd);
+    if (!wi.valid) return;
+    const int32_t bh = wi.bh;
+    const int32_t sub = wi.sub;
     const int32_t b = bh / a.H, h = bh - b * a.H;
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
     const int32_t n = a.n;
@@ -712,7 +712,9 @@ hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, cons
     a.tiles_per_bh = (int32_t)((g.n + kTileRows - 1) / kTileRows);
     a.grow_per_bh = (g.num_global + kGrowRows - 1) / kGrowRows;
     a.total_items = BH * (a.tiles_per_bh + a.grow_per_bh);
-    a.per_xcd = (a.total_items + 7) / 8;
+    a.bh_per_xcd = BH % 8 == 0 ? BH / 8 : 0;
+    a.per_xcd = a.bh_per_xcd > 0 ? a.bh_per_xcd * (a.tiles_per_bh + a.grow_per_bh)
+                                 : (a.total_items + 7) / 8;
     static int attr_device = -1;   // dynamic LDS above 64 KB is enabled per device
     if (attr_device != g.device) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_scores_sched),
