@@ -182,6 +182,33 @@ def read_traffic(workload):
     return float(fields["traffic_bytes_per_launch"])
 
 
+def extras(sah, torch, w, g, q, k, v, ws, reps=5):
+    """Mean milliseconds of the other entry points on the same inputs (not
+    part of `value`): general coefficients (uniform over A^0 .. A^K), the
+    backward pass, and one layer with d_model = H d (QKV and output
+    projections around the path)."""
+    out = {}
+    theta = [1.0 / (w.K + 1)] * (w.K + 1)
+    z = torch.empty_like(v)
+    out["attn_theta_ms"] = time_events(lambda: sah.attn_theta(q, k, v, g, theta, out=z,
+                                                             workspace=ws), reps, torch)
+    dz = torch.randn(q.shape, generator=torch.Generator(device="cpu").manual_seed(5)).to(
+        dtype=q.dtype, device=q.device)
+    sah.attn_backward(q, k, v, dz, g, w.K, w.alpha)
+    out["backward_ms"] = time_events(lambda: sah.attn_backward(q, k, v, dz, g, w.K, w.alpha),
+                                     reps, torch)
+    dm = w.H * w.d
+    gen = torch.Generator(device="cpu").manual_seed(6)
+    x = (torch.randn(w.B, w.n, dm, generator=gen)).to(dtype=q.dtype, device=q.device)
+    wq = (torch.randn(dm, 3 * dm, generator=gen) * dm ** -0.5).to(dtype=q.dtype, device=q.device)
+    wo = (torch.randn(dm, dm, generator=gen) * dm ** -0.5).to(dtype=q.dtype, device=q.device)
+    sah.layer_forward(x, wq, wo, g, w.H, w.K, w.alpha)
+    out["layer_ms"] = time_events(lambda: sah.layer_forward(x, wq, wo, g, w.H, w.K, w.alpha),
+                                  reps, torch)
+    out["layer_d_model"] = dm
+    return out
+
+
 def cpu_baseline(w, q, k, v, budget_s=15.0, max_pairs=None):
     """The oracle, as it stands, on (b, h) pairs of the same workload until
     the time budget is spent; returns diffused edges/s over the sample."""
@@ -221,6 +248,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip timing the other entry points on the same workload")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
 
@@ -331,6 +360,8 @@ def main():
             "diffusion_GBs": diff_b / (t_diff * 1e-3) / 1e9,
         },
     }
+    if not args.no_extras:
+        line["extras"] = extras(sah, torch, w, g, q, k, v, ws)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, q_h, k_h, v_h, budget_s=args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -12,7 +12,9 @@
 // storage, d in {16, 32, 64, 128}); every intermediate (A, dA, the states
 // Z_k, G_k, dV) is fp32. Row-wise products walk a row's slots; the
 // transposed ones walk the graph's column index (the slots of each column
-// by ascending row), so every sum has a fixed order.
+// by ascending row). Each wave splits its row or column over groups of
+// lanes and adds the groups' partial sums in a fixed order, so every sum
+// has a fixed order.
 #include "internal.h"
 #include "vec.h"
 
@@ -28,13 +30,22 @@ __device__ __forceinline__ float ld(const bf16_t* p) { return bf16_to_f32(p->bit
 __device__ __forceinline__ void st(float* p, float v) { *p = v; }
 __device__ __forceinline__ void st(bf16_t* p, float v) { p->bits = (uint16_t)f32_to_bf16(v); }
 
+// Four channels of row r of X as floats.
+template <typename TX>
+__device__ __forceinline__ void ld4(const TX* p, float (&x)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = ld(p + e);
+}
+
 // Y[i] = a * sum_{slots s of row i} W[s] X[col(s)] + b * U[i], one wave per
-// row, lane = channel (and channel + 64 when D = 128).
+// row: groups of L = D / 4 lanes take one slot each (lane = 4 channels),
+// so 64 / L slots are in flight per step; the groups' partial sums are
+// added in a fixed order at the end.
 template <typename TX, typename TU, typename TY, int D>
 __global__ __launch_bounds__(kThreads)
 void k_rows(GenericGraph gg, int32_t H, const float* __restrict__ W, const TX* __restrict__ X,
             const TU* __restrict__ U, TY* __restrict__ Y, float a, float b) {
-    constexpr int CPL = D > kWave ? D / kWave : 1;
+    constexpr int L = D / 4, EPI = kWave / L;
     const int wave = threadIdx.x / kWave, lane = __lane_id();
     const int64_t n = gg.n;
     const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -43,28 +54,32 @@ void k_rows(GenericGraph gg, int32_t H, const float* __restrict__ W, const TX* _
     const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
     const RowSlots rs = gg.row(gr, i);
     const float* Wb = W + a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
-    const TX* Xb = X + (int64_t)bh * n * D;
-    float acc[CPL];
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) acc[k] = 0.0f;
+    const int sub = lane % L, grp = lane / L;
+    const TX* Xb = X + (int64_t)bh * n * D + 4 * sub;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const int64_t cnt = rs.count();
-    for (int64_t e = 0; e < cnt; ++e) {
-        int32_t j;
-        const int64_t s = rs.slot(e, j);
-        if (j < 0) continue;
-        const float w = Wb[s];
+    for (int64_t base = 0; base < cnt; base += EPI) {
+        const int64_t e = base + grp;
+        int32_t j = -1;
+        int64_t s = 0;
+        if (e < cnt) s = rs.slot(e, j);
+        if (j >= 0) {
+            const float w = Wb[s];
+            float x[4];
+            ld4(Xb + (int64_t)j * D, x);
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-            const int c = lane + kWave * k;
-            if (c < D) acc[k] = fmaf(w, ld(Xb + (int64_t)j * D + c), acc[k]);
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(w, x[c], acc[c]);
         }
     }
-    const int64_t o = ((int64_t)bh * n + i) * D;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        const int c = lane + kWave * k;
-        if (c < D) {
-            float y = a * acc[k];
+    for (int off = L; off < kWave; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
+    if (grp == 0) {
+        const int64_t o = ((int64_t)bh * n + i) * D + 4 * sub;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float y = a * acc[c];
             if (U != nullptr) y += b * ld(U + o + c);
             st(Y + o + c, y);
         }
@@ -83,12 +98,13 @@ struct ColIndex {
     const int64_t* slot_off;   // [graphs + 1]
 };
 
-// Y[j] = a * sum_{slots s of column j} W[s] X[row(s)], one wave per column.
+// Y[j] = a * sum_{slots s of column j} W[s] X[row(s)], one wave per
+// column, lanes grouped as in k_rows.
 template <typename TX, typename TY, int D>
 __global__ __launch_bounds__(kThreads)
 void k_cols(ColIndex ci, int32_t H, const float* __restrict__ W, const TX* __restrict__ X,
             TY* __restrict__ Y, float a) {
-    constexpr int CPL = D > kWave ? D / kWave : 1;
+    constexpr int L = D / 4, EPI = kWave / L;
     const int wave = threadIdx.x / kWave, lane = __lane_id();
     const int64_t n = ci.n;
     const int64_t j = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -99,25 +115,27 @@ void k_cols(ColIndex ci, int32_t H, const float* __restrict__ W, const TX* __res
     const int32_t* cs = ci.col_slot + ci.col_off[gr];
     const int32_t* srow = ci.slot_row + ci.slot_off[gr];
     const float* Wb = W + a_block_offset(ci.slot_off, ci.num_graphs, H, bb, hh);
-    const TX* Xb = X + (int64_t)bh * n * D;
-    float acc[CPL];
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) acc[k] = 0.0f;
-    for (int64_t e = cp[j]; e < cp[j + 1]; ++e) {
+    const int sub = lane % L, grp = lane / L;
+    const TX* Xb = X + (int64_t)bh * n * D + 4 * sub;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const int64_t e0 = cp[j], e1 = cp[j + 1];
+    for (int64_t e = e0 + grp; e < e1; e += EPI) {
         const int32_t s = cs[e];
         const int64_t i = srow[s];
         const float w = Wb[s];
+        float x[4];
+        ld4(Xb + i * D, x);
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-            const int c = lane + kWave * k;
-            if (c < D) acc[k] = fmaf(w, ld(Xb + i * D + c), acc[k]);
-        }
+        for (int c = 0; c < 4; ++c) acc[c] = fmaf(w, x[c], acc[c]);
     }
-    const int64_t o = ((int64_t)bh * n + j) * D;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        const int c = lane + kWave * k;
-        if (c < D) st(Y + o + c, a * acc[k]);
+    for (int off = L; off < kWave; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
+    if (grp == 0) {
+        const int64_t o = ((int64_t)bh * n + j) * D + 4 * sub;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) st(Y + o + c, a * acc[c]);
     }
 }
 
