@@ -30,8 +30,12 @@
 // (kChunkRows keys) with random edges, the block's edges into that chunk by
 // row, then column, two edges of one row per pair (an odd one out paired
 // with a dummy), 16 pairs = kGroupSlots slots per group, the last group of
-// a (block, chunk) padded with dummy pairs. Padding and dummy slots carry
-// row and column -1 and weight 0.
+// a (block, chunk) padded with dummy pairs. Within a group the k-th pair in
+// that order takes position 2k (k < 8) or 2 (k - 8) + 1, so the two pairs
+// at positions 2m, 2m + 1 (read by one lane of the score kernel) are 8 apart
+// in row order and, unless a row has more than 8 pairs in the group, belong
+// to different rows. Padding and dummy slots carry row and column -1 and
+// weight 0.
 #include "internal.h"
 
 namespace diffuser {
@@ -381,6 +385,12 @@ __device__ __forceinline__ int32_t sched_j_index(int32_t s) {
     return 2 * (4 * k + (a & 3)) + (a >> 2);
 }
 
+// Position within its group of the q-th pair (0..15) of the group in row
+// order.
+__device__ __forceinline__ int32_t pair_position(int32_t q) {
+    return q < 8 ? 2 * q : 2 * (q - 8) + 1;
+}
+
 template <bool kFill>
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_sched(SchedArgs a) {
@@ -428,7 +438,7 @@ void k_sched(SchedArgs a) {
             for (int32_t t = 0; t < pairs; ++t) {
                 const int32_t pidx = pre + t;
                 const int64_t gg = gbase + g0 + pidx / 16;
-                const int32_t pig = pidx % 16;
+                const int32_t pig = pair_position(pidx % 16);
                 const bool lone = p + 2 * t + 1 >= k;   // second slot is a dummy
                 a.sched_row[gg * 16 + pig] = (uint8_t)(lane | (lone ? 0x80 : 0));
                 for (int h = 0; h < 2; ++h) {
@@ -447,7 +457,7 @@ void k_sched(SchedArgs a) {
             // Dummy pairs that pad the chunk's last group.
             for (int32_t pidx = total + lane; pidx < 16 * ng; pidx += kWave) {
                 const int64_t gg = gbase + g0 + pidx / 16;
-                const int32_t pig = pidx % 16;
+                const int32_t pig = pair_position(pidx % 16);
                 a.sched_row[gg * 16 + pig] = (uint8_t)0xFF;
                 for (int h = 0; h < 2; ++h) {
                     const int32_t s = 2 * pig + h;

@@ -87,7 +87,8 @@ struct diffuser_graph {
     // padded to a multiple of 8). Rows form blocks of kRowBlock, key rows
     // chunks of kChunkRows. For each (row block, chunk) the block's random
     // edges with keys in the chunk are listed by row, two edges of one row
-    // per pair (a lone edge is paired with a dummy), 16 pairs per group; a
+    // per pair (a lone edge is paired with a dummy), 16 pairs per group (the
+    // k-th pair in row order at position 2k, k < 8, or 2 (k - 8) + 1); a
     // group's 32 weights occupy 32 consecutive slots of the random area.
     bool scheduled = false;
     std::vector<int64_t> groups;    // [num_graphs]

@@ -224,12 +224,24 @@ __device__ __forceinline__ void random_tile(SLane& t, const f32x4& x, uint32_t r
         return;
     }
     float w[4];
+    if (!__any(ma && mb)) {
+        // The schedule interleaves rows, so a lane almost never owns both
+        // of its pairs: two exponentials, of the pair it owns (if any).
+        const float y0 = ma ? x[0] : x[2], y1 = ma ? x[1] : x[3];
+        const float e0 = exp2f_fast(__builtin_fmaf(y0, scale_log2, -t.ms));
+        const float e1 = exp2f_fast(__builtin_fmaf(y1, scale_log2, -t.ms));
+        w[0] = ma ? e0 : 0.0f;
+        w[1] = ma && !sa ? e1 : 0.0f;
+        w[2] = mb ? e0 : 0.0f;
+        w[3] = mb && !sb ? e1 : 0.0f;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = exp2f_fast(__builtin_fmaf(x[e], scale_log2, -t.ms));
-    w[0] = ma ? w[0] : 0.0f;
-    w[1] = ma && !sa ? w[1] : 0.0f;
-    w[2] = mb ? w[2] : 0.0f;
-    w[3] = mb && !sb ? w[3] : 0.0f;
+        for (int e = 0; e < 4; ++e) w[e] = exp2f_fast(__builtin_fmaf(x[e], scale_log2, -t.ms));
+        w[0] = ma ? w[0] : 0.0f;
+        w[1] = ma && !sa ? w[1] : 0.0f;
+        w[2] = mb ? w[2] : 0.0f;
+        w[3] = mb && !sb ? w[3] : 0.0f;
+    }
     if (P == kPassSum) {
         t.sum += (w[0] + w[1]) + (w[2] + w[3]);
         return;
