@@ -8,8 +8,9 @@ Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this module. It shares no code with the HIP library.
 
 Sources: "Diffuser" reading notes sections 2.1 (eqs. S.1-S.5), 2.2, 2.4
-(eq. S.7), 2.5; "1.2.1 Static sparsity" sections 1, 1.1 (eq. 5), 1.2 (eq. 12);
-"038 BigBird" section 2 (union neighbourhood).
+(eq. S.7), 2.5; "1.2.1 Static sparsity" sections 1, 1.1 (eq. 5), 1.2 (eqs. 11
+and 12), 2 (eq. 13, the block graph); "038 BigBird" section 2 (union
+neighbourhood).
 """
 from __future__ import annotations
 
@@ -134,6 +135,84 @@ class Oracle:
             out.append(cols[base:base + int(nnz[gr])].copy())
             base += int(nnz[gr])
         return row_ptr, out
+
+    def block_graph(self, n, block, local_blocks, num_random_blocks, num_global_blocks,
+                    num_graphs=1, seed=0):
+        """BigBird block graph ("1.2.1 Static sparsity", section 2, eq. 13 and
+        the twelve-block example). The sequence splits into N = n / block
+        blocks. Query block I < g_b (a global block) reads every key block;
+        any other reads the local blocks I - h .. I + h (h = (c - 1) / 2,
+        clipped to the sequence), the global blocks 0 .. g_b - 1, and s random
+        blocks drawn from the rest: draw t of block I of graph b is
+        SplitMix64's counter-based output at (b N + I, t) (the same generator
+        as the token graph), mapped to a block by (u >> 32) N >> 32, kept if
+        new; when at most s blocks remain, all of them are taken. Every token
+        of a query block reads every token of its key blocks.
+
+        Returns (row_ptr int64[graphs, n + 1], cols per graph, key blocks:
+        per graph a list over query blocks of ascending block lists)."""
+        if block < 1 or n % block != 0:
+            raise OracleError("block graph: block must divide n")
+        if local_blocks < 1 or local_blocks % 2 == 0:
+            raise OracleError("block graph: local_blocks must be odd")
+        N = n // block
+        h = (local_blocks - 1) // 2
+        gb, s = int(num_global_blocks), int(num_random_blocks)
+        if gb < 0 or s < 0 or gb > N:
+            raise OracleError("block graph: bad global or random block count")
+        row_ptr = np.zeros((num_graphs, n + 1), dtype=np.int64)
+        cols, blocks = [], []
+        for gr in range(num_graphs):
+            keys = []
+            for I in range(N):
+                if I < gb:
+                    keys.append(list(range(N)))
+                    continue
+                base = set(range(max(0, I - h), min(N - 1, I + h) + 1)) | set(range(gb))
+                pool = [J for J in range(N) if J not in base]
+                if len(pool) <= s:
+                    chosen = set(pool)
+                else:
+                    chosen, t = set(), 0
+                    while len(chosen) < s:
+                        if t >= (1 << 20):
+                            raise OracleError("block graph: draw budget exhausted")
+                        u = self.draw(seed, gr, N, I, t)
+                        t += 1
+                        J = ((u >> 32) * N) >> 32
+                        if J not in base:
+                            chosen.add(J)
+                keys.append(sorted(base | chosen))
+            row_cols = [np.concatenate([np.arange(J * block, (J + 1) * block, dtype=np.int32)
+                                        for J in ks]) for ks in keys]
+            deg = np.repeat([len(ks) * block for ks in keys], block)
+            row_ptr[gr, 1:] = np.cumsum(deg)
+            cols.append(np.concatenate([row_cols[i // block] for i in range(n)]).astype(np.int32))
+            blocks.append(keys)
+        return row_ptr, cols, blocks
+
+    def dilated_graph(self, n, radius, dilation, global_idx):
+        """Longformer's dilated window with global positions ("1.2.1 Static
+        sparsity", section 1.2, eqs. 11 and 12): row i not in G reads
+        {i + k delta : -r <= k <= r} within the sequence, plus G; a row in G
+        reads every position. Returns (row_ptr int64[1, n + 1], [cols])."""
+        if n < 1 or radius < 0 or dilation < 1:
+            raise OracleError("dilated graph: bad arguments")
+        G = sorted(set(int(x) for x in global_idx))
+        if any(x < 0 or x >= n for x in G):
+            raise OracleError("dilated graph: global position out of range")
+        Gs = set(G)
+        rows = []
+        for i in range(n):
+            if i in Gs:
+                rows.append(np.arange(n, dtype=np.int32))
+                continue
+            s = {i + k * dilation for k in range(-radius, radius + 1)}
+            s = {j for j in s if 0 <= j < n} | Gs
+            rows.append(np.array(sorted(s), dtype=np.int32))
+        row_ptr = np.zeros((1, n + 1), dtype=np.int64)
+        row_ptr[0, 1:] = np.cumsum([len(r) for r in rows])
+        return row_ptr, [np.concatenate(rows).astype(np.int32)]
 
     # -- per (batch, head) arithmetic ----------------------------------------
     def scores_softmax(self, Q, K, row_ptr, col_idx, threads=1):

@@ -550,6 +550,138 @@ def pin_layer_identity(o):
     assert np.max(np.abs(Y1 - Y2)) < 1e-10
 
 
+# --------------------------------------------------------------------------
+# Block graph (BigBird, eq. 13) and dilated window (Longformer, eq. 11)
+# --------------------------------------------------------------------------
+
+def _key_block_count(N, h, gb, s, I):
+    """Key blocks of query block I from set sizes: N for a global block,
+    else |L u G| + min(s, N - |L u G|)."""
+    if I < gb:
+        return N
+    base = set(range(max(0, I - h), min(N - 1, I + h) + 1)) | set(range(gb))
+    return len(base) + min(s, N - len(base))
+
+
+def pin_block_graph_example(o):
+    g = golden_dict("bigbird_12blocks.txt")
+    N, b, c, s, gb = (int(g[k][0]) for k in ("blocks", "block", "local", "random", "global"))
+    n = N * b
+    rp, cols, blocks = o.block_graph(n, b, c, s, gb, 1, 0)
+    keys = blocks[0]
+    I = int(g["example_query_block"][0])
+    local = {int(x) for x in g["example_local"][0].split(",")}
+    glob = {int(x) for x in g["example_global"][0].split(",")}
+    assert local | glob <= set(keys[I]), keys[I]
+    assert len(keys[I]) == 6
+    deg = np.diff(rp[0])
+    assert int(deg[I * b:(I + 1) * b].sum()) == int(g["pairs_ordinary_block"][0])
+    assert int(deg[0:b].sum()) == int(g["pairs_global_block"][0])
+    nnz = int(rp[0, -1])
+    assert (N - gb) * int(g["pairs_ordinary_block"][0]) + gb * int(g["pairs_global_block"][0]) \
+        == int(g["upper_bound"][0])
+    assert nnz <= int(g["upper_bound"][0]) < int(g["full"][0]) == n * n
+    want = sum(_key_block_count(N, (c - 1) // 2, gb, s, J) for J in range(N)) * b * b
+    assert nnz == want, (nnz, want)
+
+
+def pin_block_graph_structure(o):
+    """Rows of one block are identical and ascending; each is a union of
+    whole key blocks: the local blocks, the global blocks and exactly
+    min(s, pool) distinct others; global query blocks read everything;
+    seeds and graphs vary the draws."""
+    cases = [(96, 8, 3, 2, 1), (128, 16, 1, 3, 0), (64, 8, 5, 9, 2), (64, 16, 9, 2, 1),
+             (256, 16, 3, 4, 2)]
+    for n, b, c, s, gb in cases:
+        N, h = n // b, (c - 1) // 2
+        rp, cols, blocks = o.block_graph(n, b, c, s, gb, 2, 5)
+        for gr in range(2):
+            rows = csr_rows(rp[gr], cols[gr])
+            for I in range(N):
+                ks = blocks[gr][I]
+                want = np.concatenate([np.arange(J * b, (J + 1) * b) for J in ks])
+                for i in range(I * b, (I + 1) * b):
+                    assert np.array_equal(rows[i], want), (n, b, c, s, gb, i)
+                assert np.all(np.diff(ks) > 0)
+                assert len(ks) == _key_block_count(N, h, gb, s, I)
+                if I < gb:
+                    assert ks == list(range(N))
+                else:
+                    base = set(range(max(0, I - h), min(N - 1, I + h) + 1)) | set(range(gb))
+                    assert base <= set(ks)
+    n, b, c, s, gb = 256, 8, 3, 4, 1
+    _, c1, _ = o.block_graph(n, b, c, s, gb, 2, 5)
+    _, c2, _ = o.block_graph(n, b, c, s, gb, 2, 5)
+    _, c3, _ = o.block_graph(n, b, c, s, gb, 1, 6)
+    assert all(np.array_equal(x, y) for x, y in zip(c1, c2))
+    assert not np.array_equal(c1[0], c1[1]) and not np.array_equal(c1[0], c3[0])
+
+
+def pin_block_random_uniform(o):
+    """Random key blocks are spread evenly over the pool: over many query
+    blocks each pool block is picked about equally often."""
+    n, b, c, s, gb = 4096, 4, 3, 8, 2
+    N = n // b
+    _, _, blocks = o.block_graph(n, b, c, s, gb, 1, 3)
+    hits = np.zeros(N)
+    for I in range(gb, N):
+        base = set(range(max(0, I - 1), min(N - 1, I + 1) + 1)) | set(range(gb))
+        for J in blocks[0][I]:
+            if J not in base:
+                hits[J] += 1
+    inner = hits[gb + 8:N - 8]
+    mean = (N - gb) * s / (N - gb - 3)
+    assert abs(inner.mean() - mean) < 0.05 * mean, inner.mean()
+    assert inner.std() < 3.5 * math.sqrt(mean), inner.std()
+
+
+def pin_block_draws_golden(o):
+    """Query block 0 of graph 0 (no global blocks, c = 1, seed 0) takes its
+    random blocks from SplitMix64(seed 0)'s first outputs (the golden file),
+    each mapped to a block by (u >> 32) N >> 32."""
+    u = [int(r[0], 16) for r in read_golden("splitmix64_seed0.txt")]
+    N, b = 1000, 4
+    want = []
+    for x in u:
+        J = ((x >> 32) * N) >> 32
+        if J != 0 and J not in want:
+            want.append(J)
+    want = sorted(want[:2])
+    assert len(want) == 2
+    _, _, blocks = o.block_graph(N * b, b, 1, 2, 0, 1, 0)
+    assert blocks[0][0] == sorted([0] + want), (blocks[0][0], want)
+
+
+def pin_dilated_example(o):
+    for r, dl, pos, nb in read_golden("dilated_window.txt"):
+        r, dl, i = int(r), int(dl), int(pos) - 1
+        want = [int(x) - 1 for x in nb.split(",")]
+        rp, cols = o.dilated_graph(40, r, dl, [])
+        row = csr_rows(rp[0], cols[0])[i].tolist()
+        assert row == want, (row, want)
+        assert i - 1 not in row and i + 1 not in row
+
+
+def pin_dilated_structure(o):
+    """Step 1 is the contiguous window with globals (the token graph
+    without random extras); with step delta and no globals every neighbour
+    is congruent to the row mod delta and rows have at most 2r + 1 of them;
+    global rows are full."""
+    for n, r, G in ((50, 3, [0, 17]), (33, 0, []), (64, 5, [63])):
+        rp1, c1 = o.dilated_graph(n, r, 1, G)
+        rp2, c2 = o.graph(n, r, G, 0)
+        assert np.array_equal(rp1[0], rp2[0]) and np.array_equal(c1[0], c2[0]), (n, r, G)
+    n, r, dl = 100, 4, 7
+    rp, cols = o.dilated_graph(n, r, dl, [])
+    for i, row in enumerate(csr_rows(rp[0], cols[0])):
+        assert len(row) <= 2 * r + 1 and i in row
+        assert all((j - i) % dl == 0 and abs(j - i) <= r * dl for j in row), i
+    rp, cols = o.dilated_graph(n, r, dl, [5, 60])
+    rows = csr_rows(rp[0], cols[0])
+    assert rows[5].tolist() == list(range(n)) and rows[60].tolist() == list(range(n))
+    assert {5, 60} <= set(rows[30].tolist())
+
+
 ALL_PINS = [
     pin_splitmix64, pin_edge_counts_8pos, pin_window_closed_form, pin_degrees,
     pin_row_structure, pin_random_uniform, pin_softmax_8pos, pin_row_sums,
@@ -558,5 +690,6 @@ ALL_PINS = [
     pin_causality, pin_reach, pin_two_hop_global, pin_constant_fixed_point,
     pin_theta_printed_coefficients, pin_theta_three_token, pin_theta_powers,
     pin_even_extras, pin_backward_finite_differences, pin_backward_special_cases,
-    pin_bf16_rounding, pin_layer_identity,
+    pin_bf16_rounding, pin_layer_identity, pin_block_graph_example, pin_block_graph_structure,
+    pin_block_random_uniform, pin_block_draws_golden, pin_dilated_example, pin_dilated_structure,
 ]

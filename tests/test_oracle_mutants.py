@@ -89,3 +89,39 @@ def test_mutant_is_caught(tmp_path, name, orig, planted):
     oracle.build(out_path=str(lib), src_path=str(mut_src))
     o = oracle.Oracle(oracle.load(str(lib)))
     assert _caught(o), f"planted mistake {name} passed every pin"
+
+
+# Mistakes planted in the Python graph builders of oracle/__init__.py (the
+# block graph and the dilated window); the mutated module is loaded next to
+# the real C library.
+PY_MUTANTS = [
+    ("block_local_one_sided", "base = set(range(max(0, I - h), min(N - 1, I + h) + 1)) | set(range(gb))",
+     "base = set(range(I, min(N - 1, I + h) + 1)) | set(range(gb))"),
+    ("block_no_globals", "base = set(range(max(0, I - h), min(N - 1, I + h) + 1)) | set(range(gb))",
+     "base = set(range(max(0, I - h), min(N - 1, I + h) + 1))"),
+    ("block_random_may_repeat_local", "if J not in base:\n                            chosen.add(J)",
+     "chosen.add(J)"),
+    ("block_global_query_local_only", "if I < gb:\n                    keys.append(list(range(N)))",
+     "if I < 0:\n                    keys.append(list(range(N)))"),
+    ("block_draw_wrong_counter", "u = self.draw(seed, gr, N, I, t)", "u = self.draw(seed, gr, N, I + 1, t)"),
+    ("block_short_tokens", "np.arange(J * block, (J + 1) * block, dtype=np.int32)",
+     "np.arange(J * block, (J + 1) * block - 1, dtype=np.int32)"),
+    ("dilated_step_off_by_one", "s = {i + k * dilation for k in range(-radius, radius + 1)}",
+     "s = {i + k * (dilation + 1) for k in range(-radius, radius + 1)}"),
+    ("dilated_one_sided", "s = {i + k * dilation for k in range(-radius, radius + 1)}",
+     "s = {i + k * dilation for k in range(0, radius + 1)}"),
+    ("dilated_no_globals", "s = {j for j in s if 0 <= j < n} | Gs", "s = {j for j in s if 0 <= j < n}"),
+]
+
+
+@pytest.mark.parametrize("name,orig,planted", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_python_mutant_is_caught(name, orig, planted):
+    import types
+    path = os.path.join(ORACLE_DIR, "__init__.py")
+    src = open(path).read()
+    assert src.count(orig) >= 1, f"mutation site for {name} not found"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    mod.__file__ = path
+    exec(compile(src.replace(orig, planted), path, "exec"), mod.__dict__)
+    o = mod.Oracle(oracle.load())
+    assert _caught(o), f"planted mistake {name} passed every pin"
