@@ -122,6 +122,45 @@ DIFFUSER_API diffuser_status diffuser_graph_from_csr(int64_t n, int32_t num_grap
                                         const int32_t* col_idx_host, void* stream,
                                         diffuser_graph** out);
 
+/* BigBird block graph ("1.2.1 Static sparsity", section 2, eq. 13): the
+ * sequence splits into N = n / block blocks. Query block I < num_global_blocks
+ * reads every key block; any other reads the local blocks I - h .. I + h
+ * (h = (local_blocks - 1) / 2, clipped to [0, N)), the global blocks
+ * 0 .. num_global_blocks - 1, and num_random_blocks random blocks drawn
+ * from the others (draw t of block I of graph b: SplitMix64 at counter
+ * ((b N + I) << 20 | t), block (u >> 32) N >> 32, kept if new; all others
+ * when at most num_random_blocks remain). Every token of a query block reads
+ * every token of its key blocks; rows are ascending, so each row's weight
+ * slots are its key blocks' columns in order. Constraints: block >= 1
+ * divides n, local_blocks odd >= 1, 0 <= num_global_blocks <= N,
+ * num_random_blocks >= 0, num_graphs >= 1 (graph of batch element b as in
+ * diffuser_graph_desc). Built on the host, then imported as by
+ * diffuser_graph_from_csr (synchronous). With block == 64 the bf16, d = 64
+ * score and diffusion entry points run block-tile kernels on it. */
+typedef struct {
+    int64_t n;
+    int32_t block;
+    int32_t local_blocks;
+    int32_t num_random_blocks;
+    int32_t num_global_blocks;
+    int32_t num_graphs;
+    uint64_t seed;
+} diffuser_block_graph_desc;
+
+DIFFUSER_API diffuser_status diffuser_build_block_graph(const diffuser_block_graph_desc* desc,
+                                                        void* stream, diffuser_graph** out);
+
+/* Longformer dilated window with global positions ("1.2.1 Static sparsity",
+ * section 1.2, eqs. 11 and 12): row i not in G reads {i + k dilation :
+ * -radius <= k <= radius} within [0, n) plus G; a row in G reads every
+ * position. global_idx is a HOST array of num_global strictly increasing
+ * positions in [0, n); radius >= 0, dilation >= 1. One graph; built on the
+ * host and imported as by diffuser_graph_from_csr (synchronous). */
+DIFFUSER_API diffuser_status diffuser_build_dilated_graph(int64_t n, int32_t radius,
+                                                          int32_t dilation, int32_t num_global,
+                                                          const int32_t* global_idx, void* stream,
+                                                          diffuser_graph** out);
+
 /* n, num_graphs, nnz[num_graphs] edges per graph and slots[num_graphs]
  * weight slots per graph (see diffuser_graph_copy_slots). Any output
  * pointer may be NULL. */

@@ -38,6 +38,7 @@ STATUS_NAMES = {
 # Every symbol the header declares.
 ABI_SYMBOLS = (
     "diffuser_build_graph", "diffuser_build_graph_layout", "diffuser_graph_from_csr",
+    "diffuser_build_block_graph", "diffuser_build_dilated_graph",
     "diffuser_graph_info",
     "diffuser_graph_copy_csr", "diffuser_graph_copy_slots", "diffuser_graph_destroy",
     "diffuser_attn_workspace_size",
@@ -54,6 +55,18 @@ class DiffuserError(RuntimeError):
         self.status = status
         self.status_name = STATUS_NAMES.get(status, str(status))
         super().__init__(f"{self.status_name}: {message}")
+
+
+class _BlockGraphDesc(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int64),
+        ("block", ctypes.c_int32),
+        ("local_blocks", ctypes.c_int32),
+        ("num_random_blocks", ctypes.c_int32),
+        ("num_global_blocks", ctypes.c_int32),
+        ("num_graphs", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
+    ]
 
 
 class _GraphDesc(ctypes.Structure):
@@ -90,6 +103,11 @@ def load_library(path: str = LIB_PATH):
                                                 ctypes.POINTER(p)]
     lib.diffuser_build_graph_layout.restype = st
     lib.diffuser_graph_from_csr.argtypes = [i64, i32, p, p, p, ctypes.POINTER(p)]
+    lib.diffuser_build_block_graph.argtypes = [ctypes.POINTER(_BlockGraphDesc), p,
+                                               ctypes.POINTER(p)]
+    lib.diffuser_build_block_graph.restype = st
+    lib.diffuser_build_dilated_graph.argtypes = [i64, i32, i32, i32, p, p, ctypes.POINTER(p)]
+    lib.diffuser_build_dilated_graph.restype = st
     lib.diffuser_graph_from_csr.restype = st
     lib.diffuser_graph_info.argtypes = [p, p, p, p, p]
     lib.diffuser_graph_info.restype = st
@@ -268,6 +286,34 @@ def graph_from_csr(n: int, row_ptr, col_idx) -> Graph:
                                        ci.ctypes.data_as(ctypes.c_void_p) if ci.size else None,
                                        ctypes.c_void_p(_stream_handle()), ctypes.byref(out)))
     return Graph(out.value)
+
+
+def build_block_graph(n: int, block: int, local_blocks: int, num_random_blocks: int,
+                      num_global_blocks: int, num_graphs: int = 1, seed: int = 0) -> Graph:
+    """diffuser_build_block_graph: the BigBird block layout."""
+    lib = load_library()
+    desc = _BlockGraphDesc(n, block, local_blocks, num_random_blocks, num_global_blocks,
+                           num_graphs, seed)
+    out = ctypes.c_void_p()
+    _check(lib.diffuser_build_block_graph(ctypes.byref(desc), ctypes.c_void_p(_stream_handle()),
+                                          ctypes.byref(out)))
+    return Graph(out.value, dict(n=n, block=block, local_blocks=local_blocks,
+                                 num_random_blocks=num_random_blocks,
+                                 num_global_blocks=num_global_blocks, num_graphs=num_graphs,
+                                 seed=seed))
+
+
+def build_dilated_graph(n: int, radius: int, dilation: int, global_idx: Sequence[int]) -> Graph:
+    """diffuser_build_dilated_graph: Longformer's dilated window with globals."""
+    lib = load_library()
+    g = np.ascontiguousarray(np.asarray(list(global_idx), dtype=np.int32))
+    out = ctypes.c_void_p()
+    _check(lib.diffuser_build_dilated_graph(n, radius, dilation, g.size,
+                                            g.ctypes.data_as(ctypes.c_void_p) if g.size else None,
+                                            ctypes.c_void_p(_stream_handle()),
+                                            ctypes.byref(out)))
+    return Graph(out.value, dict(n=n, radius=radius, dilation=dilation,
+                                 global_idx=tuple(g.tolist())))
 
 
 def workspace_size(graph: Graph, B: int, H: int, d_h: int, d_v: int, dtype) -> int:

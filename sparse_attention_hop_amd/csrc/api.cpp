@@ -70,6 +70,10 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_col_ptr);
     hipFree(g->d_col_off_slots);
     hipFree(g->d_col_slot);
+    hipFree(g->d_bptr);
+    hipFree(g->d_bcol);
+    g->d_bptr = nullptr;
+    g->d_bcol = nullptr;
     g->d_row_ptr = nullptr;
     g->d_col_idx = nullptr;
     g->d_col_off = nullptr;
@@ -189,13 +193,15 @@ diffuser_status run_diffusion(const diffuser_graph* g, const attn_shape& s, cons
         return DIFFUSER_OK;
     }
     const bool fast = fast_diffuse_supported(*g, s) && aligned16(A);
+    const bool blockwise = fast_block_supported(*g, s) && aligned16(A);
     const void* cur = V;
     for (int32_t k = 0; k < K_steps; ++k) {
         // Steps K-1, K-3, ... write Z; the others write tmp.
         void* dst = ((K_steps - 1 - k) % 2 == 0) ? Z : tmp;
         const step_coefs kc{1.0f - alpha, alpha};
-        hipError_t e = fast ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st)
-                            : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
+        hipError_t e = blockwise ? launch_block_diffuse(*g, s, A, cur, V, dst, row_scale, kc, st)
+                       : fast    ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st)
+                                 : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
         if (e != hipSuccess) return hip_fail(e, "diffusion step launch");
         cur = dst;
     }
@@ -211,6 +217,7 @@ diffuser_status run_diffusion_theta(const diffuser_graph* g, const attn_shape& s
                                     const float* row_scale, const void* V, void* Z, void* tmp,
                                     int32_t K_steps, const float* theta, hipStream_t st) {
     const bool fast = fast_diffuse_supported(*g, s) && aligned16(A);
+    const bool blockwise = fast_block_supported(*g, s) && aligned16(A);
     const int32_t launches = K_steps == 0 ? 1 : K_steps;
     const void* cur = V;
     for (int32_t j = 0; j < launches; ++j) {
@@ -219,8 +226,9 @@ diffuser_status run_diffusion_theta(const diffuser_graph* g, const attn_shape& s
         const step_coefs kc = K_steps == 0 ? step_coefs{0.0f, theta[0]}
                               : j == 0     ? step_coefs{theta[K_steps], theta[k]}
                                            : step_coefs{1.0f, theta[k]};
-        hipError_t e = fast ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st)
-                            : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
+        hipError_t e = blockwise ? launch_block_diffuse(*g, s, A, cur, V, dst, row_scale, kc, st)
+                       : fast    ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st)
+                                 : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
         if (e != hipSuccess) return hip_fail(e, "diffusion step launch");
         cur = dst;
     }
@@ -657,6 +665,93 @@ diffuser_status diffuser_graph_from_csr(int64_t n, int32_t num_graphs, const int
     guard.g = nullptr;
     *out = g;
     return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_build_block_graph(const diffuser_block_graph_desc* desc, void* stream,
+                                          diffuser_graph** out) {
+    g_last_error.clear();
+    if (!desc || !out) return fail(DIFFUSER_ERR_INVALID_ARG, "NULL argument");
+    const int64_t n = desc->n;
+    if (n < 1 || n > kMaxN) return fail(DIFFUSER_ERR_INVALID_ARG, "n must lie in [1, 2^24]");
+    if (desc->block < 1 || n % desc->block != 0)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "block must be >= 1 and divide n");
+    const int64_t N = n / desc->block;
+    if (desc->local_blocks < 1 || desc->local_blocks % 2 == 0)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "local_blocks must be odd and >= 1");
+    if (desc->num_global_blocks < 0 || desc->num_global_blocks > N)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "num_global_blocks must lie in [0, n / block]");
+    if (desc->num_random_blocks < 0)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "num_random_blocks must be >= 0");
+    if (desc->num_graphs < 1 || desc->num_graphs > 65535)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "num_graphs must lie in [1, 65535]");
+    if (N > (1 << 20)) return fail(DIFFUSER_ERR_INVALID_ARG, "too many blocks");
+    std::vector<std::vector<int32_t>> keys;
+    if (!build_block_lists(N, desc->local_blocks, desc->num_random_blocks,
+                           desc->num_global_blocks, desc->num_graphs, desc->seed, keys))
+        return fail(DIFFUSER_ERR_INTERNAL, "random block draws exceeded their budget");
+    int64_t total = 0;
+    for (const auto& ks : keys) total += (int64_t)ks.size() * desc->block * desc->block;
+    if (total >= (1ll << 40)) return fail(DIFFUSER_ERR_INVALID_ARG, "too many edges");
+    std::vector<int64_t> row_ptr;
+    std::vector<int32_t> cols;
+    block_lists_to_csr(n, desc->block, desc->num_graphs, keys, row_ptr, cols);
+    diffuser_graph* g = nullptr;
+    if (auto s = diffuser_graph_from_csr(n, desc->num_graphs, row_ptr.data(), cols.data(), stream,
+                                         &g))
+        return s;
+    graph_guard guard{g};
+    // Block lists: d_bptr per graph with absolute indices into d_bcol.
+    std::vector<int32_t> bptr((size_t)desc->num_graphs * (N + 1)), bcol;
+    int32_t longest = 0;
+    for (int64_t gr = 0; gr < desc->num_graphs; ++gr)
+        for (int64_t I = 0; I < N; ++I) {
+            const auto& ks = keys[(size_t)(gr * N + I)];
+            bptr[(size_t)(gr * (N + 1) + I)] = (int32_t)bcol.size();
+            bcol.insert(bcol.end(), ks.begin(), ks.end());
+            longest = std::max(longest, (int32_t)ks.size());
+            if (I + 1 == N) bptr[(size_t)(gr * (N + 1) + N)] = (int32_t)bcol.size();
+        }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if ((e = dev_alloc(&g->d_bptr, bptr.size())) != hipSuccess ||
+        (e = dev_alloc(&g->d_bcol, bcol.size())) != hipSuccess)
+        return alloc_status(e, "device allocation of the block lists");
+    if ((e = hipMemcpyAsync(g->d_bptr, bptr.data(), sizeof(int32_t) * bptr.size(),
+                            hipMemcpyHostToDevice, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(g->d_bcol, bcol.data(), sizeof(int32_t) * bcol.size(),
+                            hipMemcpyHostToDevice, st)) != hipSuccess)
+        return hip_fail(e, "copy of the block lists");
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "block graph build");
+    g->blocked = true;
+    g->block = desc->block;
+    g->nblocks = N;
+    g->max_key_blocks = longest;
+    guard.g = nullptr;
+    *out = g;
+    return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_build_dilated_graph(int64_t n, int32_t radius, int32_t dilation,
+                                            int32_t num_global, const int32_t* global_idx,
+                                            void* stream, diffuser_graph** out) {
+    g_last_error.clear();
+    if (!out) return fail(DIFFUSER_ERR_INVALID_ARG, "NULL argument");
+    if (n < 1 || n > kMaxN) return fail(DIFFUSER_ERR_INVALID_ARG, "n must lie in [1, 2^24]");
+    if (radius < 0 || dilation < 1)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "radius must be >= 0 and dilation >= 1");
+    if (num_global < 0 || num_global > n)
+        return fail(DIFFUSER_ERR_INVALID_ARG, "num_global must lie in [0, n]");
+    if (num_global > 0 && !global_idx) return fail(DIFFUSER_ERR_INVALID_ARG, "global_idx is NULL");
+    for (int32_t q = 0; q < num_global; ++q)
+        if (global_idx[q] < 0 || global_idx[q] >= n || (q > 0 && global_idx[q] <= global_idx[q - 1]))
+            return fail(DIFFUSER_ERR_INVALID_ARG,
+                        "global_idx must be strictly increasing in [0, n)");
+    if ((int64_t)num_global * n + n * (2 * (int64_t)radius + 1) >= (1ll << 40))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "too many edges");
+    std::vector<int64_t> row_ptr;
+    std::vector<int32_t> cols;
+    dilated_csr(n, radius, dilation, global_idx, num_global, row_ptr, cols);
+    return diffuser_graph_from_csr(n, 1, row_ptr.data(), cols.data(), stream, out);
 }
 
 diffuser_status diffuser_graph_info(const diffuser_graph* g, int64_t* n, int32_t* num_graphs,

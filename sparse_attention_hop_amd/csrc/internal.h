@@ -113,6 +113,16 @@ struct diffuser_graph {
     // col_off_slots[gr], the slot numbers (within the graph) of each column
     // by ascending row.
     std::mutex bw_mutex;
+
+    // Block layout (graphs from diffuser_build_block_graph): every row of
+    // query block I reads whole key blocks, listed (ascending, absolute
+    // indices into d_bcol) at d_bptr[gr][I] .. d_bptr[gr][I + 1].
+    bool blocked = false;
+    int32_t block = 0;              // tokens per block
+    int64_t nblocks = 0;            // n / block
+    int32_t max_key_blocks = 0;     // longest key-block list
+    int32_t* d_bptr = nullptr;      // [num_graphs][nblocks + 1]
+    int32_t* d_bcol = nullptr;      // [key blocks of all graphs]
     int64_t* d_col_ptr = nullptr;        // [num_graphs][n + 1]
     int64_t* d_col_off_slots = nullptr;  // [num_graphs + 1]
     int32_t* d_col_slot = nullptr;       // [valid slots of all graphs]
@@ -182,6 +192,29 @@ bool fast_diffuse_supported(const diffuser_graph& g, const attn_shape& s);
 hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
                                step_coefs k, hipStream_t st);
+
+// Block-tile kernels for block graphs (block_fast.hip; block == 64, bf16,
+// d = 64): the score pass (as launch_scores_fast: normalised, or exp(s - m)
+// with row_scale) and one diffusion step.
+bool fast_block_supported(const diffuser_graph& g, const attn_shape& s);
+hipError_t launch_block_scores(const diffuser_graph& g, const attn_shape& s, const void* Q,
+                               const void* K, void* A, float* row_scale, float scale_log2,
+                               bool normalized, hipStream_t st);
+hipError_t launch_block_diffuse(const diffuser_graph& g, const attn_shape& s, const void* A,
+                                const void* Zk, const void* V, void* Zn, const float* row_scale,
+                                step_coefs k, hipStream_t st);
+
+// Host construction of the block and dilated layouts (block_graph.cpp).
+// build_block_lists: keys[gr * nblocks + I] = ascending key blocks of query
+// block I; false when a row's draws exceed their budget.
+bool build_block_lists(int64_t nblocks, int32_t local_blocks, int32_t num_random,
+                       int32_t num_global, int32_t num_graphs, uint64_t seed,
+                       std::vector<std::vector<int32_t>>& keys);
+void block_lists_to_csr(int64_t n, int32_t block, int32_t num_graphs,
+                        const std::vector<std::vector<int32_t>>& keys,
+                        std::vector<int64_t>& row_ptr, std::vector<int32_t>& cols);
+void dilated_csr(int64_t n, int32_t radius, int32_t dilation, const int32_t* G, int32_t g,
+                 std::vector<int64_t>& row_ptr, std::vector<int32_t>& cols);
 
 // Backward of the whole path (backward.hip). Workspace pointers are fp32:
 // A and dA [a_count] in the A layout, Zs [K_steps][B*H*n*d], G0, G1, dV
