@@ -155,15 +155,22 @@ int64_t total_a_elems(const diffuser_graph* g, int32_t B, int32_t H) {
 
 // Workspace of diffuser_attn: [A][Z ping-pong buffer][row scales (fp32)].
 struct ws_layout {
-    size_t a_bytes, z_bytes, s_bytes, total;
+    size_t a_bytes, z_bytes, s_bytes, p_bytes, total;
 };
+
+// Scratch of the block-tile diffusion step (0 unless it runs on g).
+size_t part_bytes(const diffuser_graph* g, int32_t B, int32_t H, int32_t d_v, diffuser_dtype t) {
+    const attn_shape s{B, H, d_v, t};
+    return fast_block_supported(*g, s) ? align_up(block_part_bytes(*g, s)) : 0;
+}
 
 ws_layout layout(const diffuser_graph* g, int32_t B, int32_t H, int32_t d_v, diffuser_dtype t) {
     ws_layout w;
     w.a_bytes = align_up((size_t)total_a_elems(g, B, H) * elem_size(t));
     w.z_bytes = align_up((size_t)B * H * (size_t)g->n * d_v * elem_size(t));
     w.s_bytes = align_up((size_t)B * H * (size_t)g->n * sizeof(float));
-    w.total = w.a_bytes + w.z_bytes + w.s_bytes;
+    w.p_bytes = part_bytes(g, B, H, d_v, t);
+    w.total = w.a_bytes + w.z_bytes + w.s_bytes + w.p_bytes;
     return w;
 }
 
@@ -185,7 +192,7 @@ diffuser_status check_ptr(const void* p, const char* name, bool need16 = true) {
 // step writes Z.
 diffuser_status run_diffusion(const diffuser_graph* g, const attn_shape& s, const void* A,
                               const float* row_scale, const void* V, void* Z, void* tmp,
-                              int32_t K_steps, float alpha, hipStream_t st) {
+                              float* part, int32_t K_steps, float alpha, hipStream_t st) {
     const size_t zbytes = (size_t)s.B * s.H * (size_t)g->n * s.d * elem_size(s.dtype);
     if (K_steps == 0) {
         hipError_t e = hipMemcpyAsync(Z, V, zbytes, hipMemcpyDeviceToDevice, st);
@@ -199,7 +206,7 @@ diffuser_status run_diffusion(const diffuser_graph* g, const attn_shape& s, cons
         // Steps K-1, K-3, ... write Z; the others write tmp.
         void* dst = ((K_steps - 1 - k) % 2 == 0) ? Z : tmp;
         const step_coefs kc{1.0f - alpha, alpha};
-        hipError_t e = blockwise ? launch_block_diffuse(*g, s, A, cur, V, dst, row_scale, kc, st)
+        hipError_t e = blockwise ? launch_block_diffuse(*g, s, A, cur, V, dst, row_scale, kc, part, st)
                        : fast    ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st)
                                  : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
         if (e != hipSuccess) return hip_fail(e, "diffusion step launch");
@@ -215,7 +222,8 @@ diffuser_status run_diffusion(const diffuser_graph* g, const attn_shape& s, cons
 // coefficients (keep, restart). K = 0 is one launch with keep = 0.
 diffuser_status run_diffusion_theta(const diffuser_graph* g, const attn_shape& s, const void* A,
                                     const float* row_scale, const void* V, void* Z, void* tmp,
-                                    int32_t K_steps, const float* theta, hipStream_t st) {
+                                    float* part, int32_t K_steps, const float* theta,
+                                    hipStream_t st) {
     const bool fast = fast_diffuse_supported(*g, s) && aligned16(A);
     const bool blockwise = fast_block_supported(*g, s) && aligned16(A);
     const int32_t launches = K_steps == 0 ? 1 : K_steps;
@@ -226,7 +234,7 @@ diffuser_status run_diffusion_theta(const diffuser_graph* g, const attn_shape& s
         const step_coefs kc = K_steps == 0 ? step_coefs{0.0f, theta[0]}
                               : j == 0     ? step_coefs{theta[K_steps], theta[k]}
                                            : step_coefs{1.0f, theta[k]};
-        hipError_t e = blockwise ? launch_block_diffuse(*g, s, A, cur, V, dst, row_scale, kc, st)
+        hipError_t e = blockwise ? launch_block_diffuse(*g, s, A, cur, V, dst, row_scale, kc, part, st)
                        : fast    ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st)
                                  : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
         if (e != hipSuccess) return hip_fail(e, "diffusion step launch");
@@ -726,6 +734,7 @@ diffuser_status diffuser_build_block_graph(const diffuser_block_graph_desc* desc
     g->block = desc->block;
     g->nblocks = N;
     g->max_key_blocks = longest;
+    g->global_blocks = desc->num_global_blocks;
     guard.g = nullptr;
     *out = g;
     return DIFFUSER_OK;
@@ -857,14 +866,15 @@ diffuser_status attn_impl(const void* Q, const void* K, const void* V, diffuser_
     void* A = ws;
     void* tmp = ws + w.a_bytes;
     float* row_scale = reinterpret_cast<float*>(ws + w.a_bytes + w.z_bytes);
+    float* part = reinterpret_cast<float*>(ws + w.a_bytes + w.z_bytes + w.s_bytes);
     const float scale_log2 = (float)(1.0 / std::sqrt((double)d_h) * 1.4426950408889634);
     hipError_t e = launch_scores_softmax(*g, attn_shape{B, H, d_h, dtype}, Q, K, A, row_scale,
                                          scale_log2, st);
     if (e != hipSuccess) return hip_fail(e, "score/softmax launch");
     if (theta)
-        return run_diffusion_theta(g, attn_shape{B, H, d_v, dtype}, A, row_scale, V, Z, tmp,
+        return run_diffusion_theta(g, attn_shape{B, H, d_v, dtype}, A, row_scale, V, Z, tmp, part,
                                    K_steps, theta, st);
-    return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, row_scale, V, Z, tmp, K_steps,
+    return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, row_scale, V, Z, tmp, part, K_steps,
                          alpha, st);
 }
 
@@ -930,19 +940,25 @@ diffuser_status diffuse_impl(const void* A, const void* V, diffuser_dtype dtype,
     const size_t vz_bytes = (size_t)B * H * g->n * d_v * es;
     const size_t a_bytes = (size_t)total_a_elems(g, B, H) * es;
     const size_t z_need = align_up(vz_bytes);
-    if (K_steps >= 2) {
+    const size_t p_need = part_bytes(g, B, H, d_v, dtype);
+    const size_t ws_need = (K_steps >= 2 ? z_need : 0) + (K_steps >= 1 ? p_need : 0);
+    if (ws_need > 0) {
         if (auto s = check_ptr(workspace, "workspace")) return s;
-        if (ws_bytes < z_need) return fail(DIFFUSER_ERR_INVALID_ARG, "workspace too small");
+        if (ws_bytes < ws_need) return fail(DIFFUSER_ERR_INVALID_ARG, "workspace too small");
     }
     if (overlaps(Z, vz_bytes, A, a_bytes) || overlaps(Z, vz_bytes, V, vz_bytes) ||
-        (K_steps >= 2 && overlaps(Z, vz_bytes, workspace, z_need)))
+        (ws_need > 0 && overlaps(Z, vz_bytes, workspace, ws_need)))
         return fail(DIFFUSER_ERR_INVALID_ARG, "Z overlaps an input or the workspace");
-    // The Z ping-pong buffer sits at the start of the caller's workspace.
+    // The caller's workspace holds the Z ping-pong buffer, then the
+    // block-tile step's partial sums.
+    float* part = p_need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                    (K_steps >= 2 ? z_need : 0))
+                         : nullptr;
     if (theta)
         return run_diffusion_theta(g, attn_shape{B, H, d_v, dtype}, A, nullptr, V, Z, workspace,
-                                   K_steps, theta, static_cast<hipStream_t>(stream));
-    return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, nullptr, V, Z, workspace, K_steps,
-                         alpha, static_cast<hipStream_t>(stream));
+                                   part, K_steps, theta, static_cast<hipStream_t>(stream));
+    return run_diffusion(g, attn_shape{B, H, d_v, dtype}, A, nullptr, V, Z, workspace, part,
+                         K_steps, alpha, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace

@@ -36,6 +36,7 @@ constexpr int kNB = 4;                        // 16-channel blocks
 constexpr int kRowBytes = kD * 2;
 constexpr int kBufBytes = kBlk * kRowBytes;   // one key block of K or Z_k
 static_assert(kWaves * 16 == kBlk, "a wave per 16 rows of the query block");
+constexpr int kSplit = 8;                     // key blocks per part of a global query block
 
 struct BlockArgs {
     int64_t n;
@@ -50,6 +51,8 @@ struct BlockArgs {
     float* row_scale;
     float scale_log2, keep, restart;
     int32_t normalized, per_xcd, total;
+    int32_t gblocks, gparts;   // global query blocks and the parts each is split into (0: none)
+    float* part;               // [B*H][gblocks][gparts][64][64] fp32 partial sums
 };
 
 // Query block of workgroup blk: XCD blk % 8 runs position blk / 8 of its
@@ -211,6 +214,31 @@ void k_block_scores(BlockArgs a) {
 // ---------------------------------------------------------------------------
 // Diffusion step.
 
+// Diffusion work item of workgroup blk: within a (batch, head) pair the
+// parts of its global query blocks come first (gq = I, keys of part p are
+// list entries kSplit p ..), then the other query blocks whole (p = -1).
+struct DiffItem {
+    int32_t bh, I, p;
+    bool valid;
+};
+
+__device__ __forceinline__ DiffItem diff_item(uint32_t blk, const BlockArgs& a) {
+    const int32_t per_bh = a.gblocks * a.gparts + (a.nblocks - a.gblocks);
+    const int32_t item = (int32_t)(blk & 7u) * a.per_xcd + (int32_t)(blk >> 3);
+    DiffItem it{0, 0, -1, false};
+    if (item >= a.total) return it;
+    it.bh = item / per_bh;
+    const int32_t r = item - it.bh * per_bh;
+    if (r < a.gblocks * a.gparts) {
+        it.I = r / a.gparts;
+        it.p = r - it.I * a.gparts;
+    } else {
+        it.I = a.gblocks + (r - a.gblocks * a.gparts);
+    }
+    it.valid = true;
+    return it;
+}
+
 __device__ __forceinline__ i16x4 tr_read(uint32_t addr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(uintptr_t)addr);
 }
@@ -234,7 +262,7 @@ __global__ __launch_bounds__(kThreads)
 void k_block_diffuse(BlockArgs a) {
     __shared__ __align__(128) char lds_raw[2 * kBufBytes];
     char LDS_AS* lds = (char LDS_AS*)lds_raw;
-    const BlockItem it = block_item(blockIdx.x, a);
+    const DiffItem it = diff_item(blockIdx.x, a);
     if (!it.valid) return;
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -246,8 +274,12 @@ void k_block_diffuse(BlockArgs a) {
     const BlockRows br = block_rows(a, gr, it.I);
     const int64_t row = (int64_t)it.I * kBlk + 16 * wave + s16;   // W^T column of this lane
     const uint16_t* Zbh = a.Y + (int64_t)it.bh * n * kD;
+    // List entries [kb0, kb1) of the query block's key blocks.
+    const int32_t kb0 = it.p < 0 ? 0 : kSplit * it.p;
+    const int32_t kb1 = it.p < 0 ? br.nk : min(br.nk, kb0 + kSplit);
     const uint16_t* Arow = a.X + a_block_offset(a.slot_off, a.num_graphs, a.H, b, h) + br.row0 +
-                           (int64_t)(row - (int64_t)it.I * kBlk) * br.nk * kBlk;
+                           (int64_t)(row - (int64_t)it.I * kBlk) * br.nk * kBlk +
+                           (int64_t)kb0 * kBlk;
     // Transposed-read source rows of the two 32-key steps.
     uint32_t r1[2], r2[2];
 #pragma unroll
@@ -261,13 +293,14 @@ void k_block_diffuse(BlockArgs a) {
     u32x4 w[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) w[ks] = load16(Arow + 32 * ks + 8 * kg);
-    dma_z(lds, Zbh, a.bcol[br.k0], wave, lane);
-    for (int32_t kb = 0; kb < br.nk; ++kb) {
+    const int32_t nk = kb1 - kb0;
+    dma_z(lds, Zbh, a.bcol[br.k0 + kb0], wave, lane);
+    for (int32_t kb = 0; kb < nk; ++kb) {
         full_barrier();   // key block kb and its weights in, kb - 1 done by every wave
         const uint32_t base = lds_addr(lds + (kb & 1) * kBufBytes);
         u32x4 wn[2] = {w[0], w[1]};
-        if (kb + 1 < br.nk) {
-            dma_z(lds + ((kb + 1) & 1) * kBufBytes, Zbh, a.bcol[br.k0 + kb + 1], wave, lane);
+        if (kb + 1 < nk) {
+            dma_z(lds + ((kb + 1) & 1) * kBufBytes, Zbh, a.bcol[br.k0 + kb0 + kb + 1], wave, lane);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) wn[ks] = load16(Arow + (int64_t)(kb + 1) * kBlk + 32 * ks + 8 * kg);
         }
@@ -284,6 +317,14 @@ void k_block_diffuse(BlockArgs a) {
         w[0] = wn[0];
         w[1] = wn[1];
     }
+    if (it.p >= 0) {
+        // A part of a global query block: fp32 partial sums, added later.
+        float* dst = a.part + (((int64_t)it.bh * a.gblocks + it.I) * a.gparts + it.p) * kBlk * kD +
+                     (int64_t)(16 * wave + s16) * kD + 4 * kg;
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) *reinterpret_cast<f32x4*>(dst + 16 * nb) = acc[nb];
+        return;
+    }
     // Restart and store: lane holds channels 16 nb + 4 kg .. + 3 of its row.
     const float keep = a.row_scale != nullptr ? a.keep * a.row_scale[(int64_t)it.bh * n + row] : a.keep;
     const int64_t o = ((int64_t)it.bh * n + row) * kD + 4 * kg;
@@ -296,6 +337,23 @@ void k_block_diffuse(BlockArgs a) {
         z[1] = to_bf16_pair(keep * acc[nb][2] + a.restart * bf16_lo(v[1]),
                             keep * acc[nb][3] + a.restart * bf16_hi(v[1]));
         *reinterpret_cast<u32x2*>(a.out + o + 16 * nb) = z;
+    }
+}
+
+// Sum of the parts of each global query block (in part order), restart and
+// store: one workgroup per (batch, head, global query block).
+__global__ __launch_bounds__(kThreads)
+void k_block_combine(BlockArgs a) {
+    const int32_t bh = (int32_t)blockIdx.x / a.gblocks, I = (int32_t)blockIdx.x % a.gblocks;
+    const int64_t n = a.n;
+    const float* src = a.part + ((int64_t)bh * a.gblocks + I) * a.gparts * kBlk * kD;
+    for (int idx = threadIdx.x; idx < kBlk * kD; idx += kThreads) {
+        float sum = 0.0f;
+        for (int p = 0; p < a.gparts; ++p) sum += src[(int64_t)p * kBlk * kD + idx];
+        const int64_t row = (int64_t)I * kBlk + idx / kD;
+        const int64_t o = ((int64_t)bh * n + row) * kD + idx % kD;
+        const float keep = a.row_scale != nullptr ? a.keep * a.row_scale[(int64_t)bh * n + row] : a.keep;
+        a.out[o] = (uint16_t)f32_to_bf16(keep * sum + a.restart * bf16_to_f32(a.V[o]));
     }
 }
 
@@ -337,10 +395,26 @@ hipError_t launch_block_scores(const diffuser_graph& g, const attn_shape& s, con
     return hipGetLastError();
 }
 
+// Global query blocks read every block: more than kSplit key blocks are
+// split into parts.
+int32_t global_parts(const diffuser_graph& g) {
+    return g.global_blocks > 0 && g.nblocks > kSplit ? (int32_t)((g.nblocks + kSplit - 1) / kSplit)
+                                                    : 0;
+}
+
+size_t block_part_bytes(const diffuser_graph& g, const attn_shape& s) {
+    return (size_t)s.B * s.H * g.global_blocks * global_parts(g) * kBlk * kD * sizeof(float);
+}
+
 hipError_t launch_block_diffuse(const diffuser_graph& g, const attn_shape& s, const void* A,
                                 const void* Zk, const void* V, void* Zn, const float* row_scale,
-                                step_coefs k, hipStream_t st) {
+                                step_coefs k, float* part, hipStream_t st) {
     BlockArgs a = block_args(g, s);
+    a.gparts = global_parts(g);
+    a.gblocks = a.gparts > 0 ? g.global_blocks : 0;
+    a.part = part;
+    a.total = s.B * s.H * (a.gblocks * a.gparts + (a.nblocks - a.gblocks));
+    a.per_xcd = (a.total + 7) / 8;
     a.X = static_cast<const uint16_t*>(A);
     a.Y = static_cast<const uint16_t*>(Zk);
     a.V = static_cast<const uint16_t*>(V);
@@ -349,6 +423,9 @@ hipError_t launch_block_diffuse(const diffuser_graph& g, const attn_shape& s, co
     a.keep = k.keep;
     a.restart = k.restart;
     hipLaunchKernelGGL(k_block_diffuse, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), 0, st, a);
+    if (a.gparts > 0)
+        hipLaunchKernelGGL(k_block_combine, dim3((unsigned)(s.B * s.H * a.gblocks)), dim3(kThreads), 0,
+                           st, a);
     return hipGetLastError();
 }
 

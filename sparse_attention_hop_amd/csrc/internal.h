@@ -121,6 +121,7 @@ struct diffuser_graph {
     int32_t block = 0;              // tokens per block
     int64_t nblocks = 0;            // n / block
     int32_t max_key_blocks = 0;     // longest key-block list
+    int32_t global_blocks = 0;      // query blocks 0 .. global_blocks - 1 read every block
     int32_t* d_bptr = nullptr;      // [num_graphs][nblocks + 1]
     int32_t* d_bcol = nullptr;      // [key blocks of all graphs]
     int64_t* d_col_ptr = nullptr;        // [num_graphs][n + 1]
@@ -200,9 +201,13 @@ bool fast_block_supported(const diffuser_graph& g, const attn_shape& s);
 hipError_t launch_block_scores(const diffuser_graph& g, const attn_shape& s, const void* Q,
                                const void* K, void* A, float* row_scale, float scale_log2,
                                bool normalized, hipStream_t st);
+// The diffusion step splits each global query block's key blocks over
+// several workgroups, whose fp32 partial sums (block_part_bytes of scratch
+// at `part`) a second kernel adds in a fixed order.
+size_t block_part_bytes(const diffuser_graph& g, const attn_shape& s);
 hipError_t launch_block_diffuse(const diffuser_graph& g, const attn_shape& s, const void* A,
                                 const void* Zk, const void* V, void* Zn, const float* row_scale,
-                                step_coefs k, hipStream_t st);
+                                step_coefs k, float* part, hipStream_t st);
 
 // Host construction of the block and dilated layouts (block_graph.cpp).
 // build_block_lists: keys[gr * nblocks + I] = ascending key blocks of query
