@@ -869,7 +869,7 @@ diffuser_status attn_impl(const void* Q, const void* K, const void* V, diffuser_
     float* part = reinterpret_cast<float*>(ws + w.a_bytes + w.z_bytes + w.s_bytes);
     const float scale_log2 = (float)(1.0 / std::sqrt((double)d_h) * 1.4426950408889634);
     hipError_t e = launch_scores_softmax(*g, attn_shape{B, H, d_h, dtype}, Q, K, A, row_scale,
-                                         scale_log2, st);
+                                         scale_log2, st, w.p_bytes ? part : nullptr);
     if (e != hipSuccess) return hip_fail(e, "score/softmax launch");
     if (theta)
         return run_diffusion_theta(g, attn_shape{B, H, d_v, dtype}, A, row_scale, V, Z, tmp, part,

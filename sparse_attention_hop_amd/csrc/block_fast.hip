@@ -52,7 +52,9 @@ struct BlockArgs {
     float scale_log2, keep, restart;
     int32_t normalized, per_xcd, total;
     int32_t gblocks, gparts;   // global query blocks and the parts each is split into (0: none)
-    float* part;               // [B*H][gblocks][gparts][64][64] fp32 partial sums
+    int32_t total_parts;       // B*H*gblocks*gparts
+    float* part;               // diffusion: [B*H][gblocks][gparts][64][64] fp32 partial sums;
+                               // scores: pmax then psum, each [B*H][gblocks][gparts][64]
 };
 
 // Query block of workgroup blk: XCD blk % 8 runs position blk / 8 of its
@@ -91,6 +93,31 @@ __device__ __forceinline__ uint32_t lds_addr(const char LDS_AS* p) {
     return (uint32_t)(uintptr_t)p;
 }
 
+// Work item of workgroup blk (score and diffusion kernels): within a
+// (batch, head) pair the parts of its global query blocks come first (gq = I, keys of part p are
+// list entries kSplit p ..), then the other query blocks whole (p = -1).
+struct DiffItem {
+    int32_t bh, I, p;
+    bool valid;
+};
+
+__device__ __forceinline__ DiffItem diff_item(uint32_t blk, const BlockArgs& a) {
+    const int32_t per_bh = a.gblocks * a.gparts + (a.nblocks - a.gblocks);
+    const int32_t item = (int32_t)(blk & 7u) * a.per_xcd + (int32_t)(blk >> 3);
+    DiffItem it{0, 0, -1, false};
+    if (item >= a.total) return it;
+    it.bh = item / per_bh;
+    const int32_t r = item - it.bh * per_bh;
+    if (r < a.gblocks * a.gparts) {
+        it.I = r / a.gparts;
+        it.p = r - it.I * a.gparts;
+    } else {
+        it.I = a.gblocks + (r - a.gblocks * a.gparts);
+    }
+    it.valid = true;
+    return it;
+}
+
 // ---------------------------------------------------------------------------
 // Scores.
 
@@ -125,18 +152,22 @@ enum BlockPass { kBMax = 0, kBSum = 1, kBWrite = 2, kBWriteNorm = 3 };
 // of the dot products; kBSum: sum of the weights exp(s - m); kBWrite:
 // writes them (bf16) and sums them as stored; kBWriteNorm: writes them
 // times inv.
+// Key blocks are list entries [kb0, kb1) of the query block; Arow points at
+// the slots of entry kb0.
 template <int P>
-__device__ __forceinline__ void score_pass(const BlockArgs& a, const BlockRows& br,
-                                           const uint16_t* Kbh, uint16_t* Arow, char LDS_AS* lds,
-                                           int wave, int lane, const u32x4& q0, const u32x4& q1,
-                                           float& m, float ms, float& sum, float inv) {
+__device__ __forceinline__ void score_pass(const BlockArgs& a, const BlockRows& br, int32_t kb0,
+                                           int32_t kb1, const uint16_t* Kbh, uint16_t* Arow,
+                                           char LDS_AS* lds, int wave, int lane, const u32x4& q0,
+                                           const u32x4& q1, float& m, float ms, float& sum,
+                                           float inv) {
     const uint32_t kg = (uint32_t)(lane >> 4);
     const int s16 = lane & 15;
-    dma_k(lds, Kbh, a.bcol[br.k0], wave, lane);
-    for (int32_t kb = 0; kb < br.nk; ++kb) {
+    const int32_t nk = kb1 - kb0;
+    dma_k(lds, Kbh, a.bcol[br.k0 + kb0], wave, lane);
+    for (int32_t kb = 0; kb < nk; ++kb) {
         full_barrier();   // key block kb in LDS, kb - 1 done by every wave
         const char LDS_AS* cur = lds + (kb & 1) * kBufBytes;
-        if (kb + 1 < br.nk) dma_k(lds + ((kb + 1) & 1) * kBufBytes, Kbh, a.bcol[br.k0 + kb + 1], wave, lane);
+        if (kb + 1 < nk) dma_k(lds + ((kb + 1) & 1) * kBufBytes, Kbh, a.bcol[br.k0 + kb0 + kb + 1], wave, lane);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const f32x4 x = key_tile(cur, t, kg, s16, q0, q1);
@@ -176,11 +207,39 @@ __device__ __forceinline__ float quad_sum(float x) {
     return x + __shfl_xor(x, 32);
 }
 
+// Partial row maxima of the parts of the global query blocks (fused mode):
+// pmax[(bh, gq, part)][row].
+__global__ __launch_bounds__(kThreads)
+void k_block_gmax(BlockArgs a) {
+    __shared__ __align__(16) char lds_raw[2 * kBufBytes];
+    char LDS_AS* lds = (char LDS_AS*)lds_raw;
+    const int32_t per_bh = a.gblocks * a.gparts;
+    const int32_t bh = (int32_t)blockIdx.x / per_bh, r = (int32_t)blockIdx.x % per_bh;
+    const int32_t I = r / a.gparts, p = r % a.gparts;
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int kg = lane >> 4, s16 = lane & 15;
+    const int32_t b = bh / a.H;
+    const int32_t gr = a.num_graphs == 1 ? 0 : b;
+    const int64_t n = a.n;
+    const BlockRows br = block_rows(a, gr, I);
+    const int32_t kb0 = kSplit * p, kb1 = min(br.nk, kb0 + kSplit);
+    const int64_t row = (int64_t)I * kBlk + 16 * wave + s16;
+    const uint16_t* Qbh = a.X + (int64_t)bh * n * kD;
+    const uint16_t* Kbh = a.Y + (int64_t)bh * n * kD;
+    const u32x4 q0 = load16(Qbh + row * kD + 8 * kg);
+    const u32x4 q1 = load16(Qbh + row * kD + 32 + 8 * kg);
+    float m = -INFINITY, sum = 0.0f;
+    score_pass<kBMax>(a, br, kb0, kb1, Kbh, nullptr, lds, wave, lane, q0, q1, m, 0.0f, sum, 0.0f);
+    m = quad_max(m);
+    if (kg == 0) a.part[((int64_t)bh * a.gblocks + I) * a.gparts * kBlk + p * kBlk + 16 * wave + s16] = m;
+}
+
 __global__ __launch_bounds__(kThreads)
 void k_block_scores(BlockArgs a) {
     __shared__ __align__(16) char lds_raw[2 * kBufBytes];
     char LDS_AS* lds = (char LDS_AS*)lds_raw;
-    const BlockItem it = block_item(blockIdx.x, a);
+    const DiffItem it = diff_item(blockIdx.x, a);
     if (!it.valid) return;
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -197,47 +256,52 @@ void k_block_scores(BlockArgs a) {
     const u32x4 q0 = load16(Qbh + row * kD + 8 * kg);
     const u32x4 q1 = load16(Qbh + row * kD + 32 + 8 * kg);
     float m = -INFINITY, sum = 0.0f;
-    score_pass<kBMax>(a, br, Kbh, Arow, lds, wave, lane, q0, q1, m, 0.0f, sum, 0.0f);
+    if (it.p >= 0) {
+        // A part of a global query block (fused mode): the row maximum from
+        // the parts' maxima, one writing pass over the part's key blocks,
+        // its sum of stored weights into psum (after the maxima).
+        const int32_t kb0 = kSplit * it.p, kb1 = min(br.nk, kb0 + kSplit);
+        const float* pm = a.part + ((int64_t)it.bh * a.gblocks + it.I) * a.gparts * kBlk +
+                          16 * wave + s16;
+        for (int32_t p = 0; p < a.gparts; ++p) m = fmaxf(m, pm[p * kBlk]);
+        score_pass<kBWrite>(a, br, kb0, kb1, Kbh, Arow + (int64_t)kb0 * kBlk, lds, wave, lane, q0,
+                            q1, m, m * a.scale_log2, sum, 0.0f);
+        sum = quad_sum(sum);
+        float* ps = a.part + ((int64_t)a.total_parts + ((int64_t)it.bh * a.gblocks + it.I) * a.gparts +
+                              it.p) * kBlk;
+        if (kg == 0) ps[16 * wave + s16] = sum;
+        return;
+    }
+    score_pass<kBMax>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, 0.0f, sum, 0.0f);
     m = quad_max(m);
     const float ms = m * a.scale_log2;
     if (a.normalized) {
-        score_pass<kBSum>(a, br, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum, 0.0f);
+        score_pass<kBSum>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum, 0.0f);
         sum = quad_sum(sum);
-        score_pass<kBWriteNorm>(a, br, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum, 1.0f / sum);
+        score_pass<kBWriteNorm>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum,
+                                1.0f / sum);
     } else {
-        score_pass<kBWrite>(a, br, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum, 0.0f);
+        score_pass<kBWrite>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum, 0.0f);
         sum = quad_sum(sum);
         if (a.row_scale != nullptr && kg == 0) a.row_scale[(int64_t)it.bh * n + row] = 1.0f / sum;
     }
 }
 
+// c_i of the global query blocks' rows from their parts' sums (in part
+// order): one workgroup per (batch, head, global query block).
+__global__ __launch_bounds__(kThreads)
+void k_block_gsum(BlockArgs a) {
+    const int32_t bh = (int32_t)blockIdx.x / a.gblocks, I = (int32_t)blockIdx.x % a.gblocks;
+    const float* ps = a.part + ((int64_t)a.total_parts + ((int64_t)bh * a.gblocks + I) * a.gparts) * kBlk;
+    for (int r = threadIdx.x; r < kBlk; r += kThreads) {
+        float sum = 0.0f;
+        for (int32_t p = 0; p < a.gparts; ++p) sum += ps[p * kBlk + r];
+        a.row_scale[(int64_t)bh * a.n + (int64_t)I * kBlk + r] = 1.0f / sum;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Diffusion step.
-
-// Diffusion work item of workgroup blk: within a (batch, head) pair the
-// parts of its global query blocks come first (gq = I, keys of part p are
-// list entries kSplit p ..), then the other query blocks whole (p = -1).
-struct DiffItem {
-    int32_t bh, I, p;
-    bool valid;
-};
-
-__device__ __forceinline__ DiffItem diff_item(uint32_t blk, const BlockArgs& a) {
-    const int32_t per_bh = a.gblocks * a.gparts + (a.nblocks - a.gblocks);
-    const int32_t item = (int32_t)(blk & 7u) * a.per_xcd + (int32_t)(blk >> 3);
-    DiffItem it{0, 0, -1, false};
-    if (item >= a.total) return it;
-    it.bh = item / per_bh;
-    const int32_t r = item - it.bh * per_bh;
-    if (r < a.gblocks * a.gparts) {
-        it.I = r / a.gparts;
-        it.p = r - it.I * a.gparts;
-    } else {
-        it.I = a.gblocks + (r - a.gblocks * a.gparts);
-    }
-    it.valid = true;
-    return it;
-}
 
 __device__ __forceinline__ i16x4 tr_read(uint32_t addr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(uintptr_t)addr);
@@ -341,58 +405,23 @@ void k_block_diffuse(BlockArgs a) {
 }
 
 // Sum of the parts of each global query block (in part order), restart and
-// store: one workgroup per (batch, head, global query block).
+// store: one thread per output element, kBlk * kD / kThreads workgroups per
+// (batch, head, global query block).
+constexpr int kCombineGroups = kBlk * kD / kThreads;
+
 __global__ __launch_bounds__(kThreads)
 void k_block_combine(BlockArgs a) {
-    const int32_t bh = (int32_t)blockIdx.x / a.gblocks, I = (int32_t)blockIdx.x % a.gblocks;
+    const int32_t q = (int32_t)blockIdx.x / kCombineGroups;
+    const int32_t bh = q / a.gblocks, I = q % a.gblocks;
+    const int idx = ((int)blockIdx.x % kCombineGroups) * kThreads + (int)threadIdx.x;
     const int64_t n = a.n;
-    const float* src = a.part + ((int64_t)bh * a.gblocks + I) * a.gparts * kBlk * kD;
-    for (int idx = threadIdx.x; idx < kBlk * kD; idx += kThreads) {
-        float sum = 0.0f;
-        for (int p = 0; p < a.gparts; ++p) sum += src[(int64_t)p * kBlk * kD + idx];
-        const int64_t row = (int64_t)I * kBlk + idx / kD;
-        const int64_t o = ((int64_t)bh * n + row) * kD + idx % kD;
-        const float keep = a.row_scale != nullptr ? a.keep * a.row_scale[(int64_t)bh * n + row] : a.keep;
-        a.out[o] = (uint16_t)f32_to_bf16(keep * sum + a.restart * bf16_to_f32(a.V[o]));
-    }
-}
-
-BlockArgs block_args(const diffuser_graph& g, const attn_shape& s) {
-    BlockArgs a{};
-    a.n = g.n;
-    a.H = s.H;
-    a.num_graphs = g.num_graphs;
-    a.nblocks = (int32_t)g.nblocks;
-    a.slot_off = g.d_slot_off;
-    a.bptr = g.d_bptr;
-    a.bcol = g.d_bcol;
-    a.total = s.B * s.H * a.nblocks;
-    a.per_xcd = (a.total + 7) / 8;
-    return a;
-}
-
-}  // namespace
-
-bool fast_block_supported(const diffuser_graph& g, const attn_shape& s) {
-    if (!g.blocked || g.block != kBlk || s.dtype != DIFFUSER_BF16 || s.d != kD) return false;
-    if ((int64_t)s.B * s.H * g.nblocks >= (1ll << 31)) return false;
-    for (int64_t x : g.slots)
-        if (x >= (1ll << 31)) return false;
-    return true;
-}
-
-hipError_t launch_block_scores(const diffuser_graph& g, const attn_shape& s, const void* Q,
-                               const void* K, void* A, float* row_scale, float scale_log2,
-                               bool normalized, hipStream_t st) {
-    BlockArgs a = block_args(g, s);
-    a.X = static_cast<const uint16_t*>(Q);
-    a.Y = static_cast<const uint16_t*>(K);
-    a.out = static_cast<uint16_t*>(A);
-    a.row_scale = row_scale;
-    a.scale_log2 = scale_log2;
-    a.normalized = normalized ? 1 : 0;
-    hipLaunchKernelGGL(k_block_scores, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), 0, st, a);
-    return hipGetLastError();
+    const float* src = a.part + ((int64_t)bh * a.gblocks + I) * a.gparts * kBlk * kD + idx;
+    float sum = 0.0f;
+    for (int p = 0; p < a.gparts; ++p) sum += src[(int64_t)p * kBlk * kD];
+    const int64_t row = (int64_t)I * kBlk + idx / kD;
+    const int64_t o = ((int64_t)bh * n + row) * kD + idx % kD;
+    const float keep = a.row_scale != nullptr ? a.keep * a.row_scale[(int64_t)bh * n + row] : a.keep;
+    a.out[o] = (uint16_t)f32_to_bf16(keep * sum + a.restart * bf16_to_f32(a.V[o]));
 }
 
 // Global query blocks read every block: more than kSplit key blocks are
@@ -404,6 +433,42 @@ int32_t global_parts(const diffuser_graph& g) {
 
 size_t block_part_bytes(const diffuser_graph& g, const attn_shape& s) {
     return (size_t)s.B * s.H * g.global_blocks * global_parts(g) * kBlk * kD * sizeof(float);
+}
+
+bool fast_block_supported(const diffuser_graph& g, const attn_shape& s) {
+    if (!g.blocked || g.block != kBlk || s.dtype != DIFFUSER_BF16 || s.d != kD) return false;
+    if ((int64_t)s.B * s.H * g.nblocks >= (1ll << 31)) return false;
+    for (int64_t x : g.slots)
+        if (x >= (1ll << 31)) return false;
+    return true;
+}
+
+hipError_t launch_block_scores(const diffuser_graph& g, const attn_shape& s, const void* Q,
+                               const void* K, void* A, float* row_scale, float scale_log2,
+                               bool normalized, float* part, hipStream_t st) {
+    BlockArgs a = block_args(g, s);
+    a.X = static_cast<const uint16_t*>(Q);
+    a.Y = static_cast<const uint16_t*>(K);
+    a.out = static_cast<uint16_t*>(A);
+    a.row_scale = row_scale;
+    a.scale_log2 = scale_log2;
+    a.normalized = normalized ? 1 : 0;
+    // The fused mode splits the global query blocks (as the diffusion step);
+    // the normalised one keeps them whole.
+    const bool split = !normalized && row_scale != nullptr && part != nullptr;
+    a.gparts = split ? global_parts(g) : 0;
+    a.gblocks = a.gparts > 0 ? g.global_blocks : 0;
+    a.part = part;
+    a.total_parts = s.B * s.H * a.gblocks * a.gparts;
+    a.total = s.B * s.H * (a.gblocks * a.gparts + (a.nblocks - a.gblocks));
+    a.per_xcd = (a.total + 7) / 8;
+    if (a.gparts > 0)
+        hipLaunchKernelGGL(k_block_gmax, dim3((unsigned)a.total_parts), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(k_block_scores, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), 0, st, a);
+    if (a.gparts > 0)
+        hipLaunchKernelGGL(k_block_gsum, dim3((unsigned)(s.B * s.H * a.gblocks)), dim3(kThreads), 0,
+                           st, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_block_diffuse(const diffuser_graph& g, const attn_shape& s, const void* A,
@@ -424,8 +489,8 @@ hipError_t launch_block_diffuse(const diffuser_graph& g, const attn_shape& s, co
     a.restart = k.restart;
     hipLaunchKernelGGL(k_block_diffuse, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), 0, st, a);
     if (a.gparts > 0)
-        hipLaunchKernelGGL(k_block_combine, dim3((unsigned)(s.B * s.H * a.gblocks)), dim3(kThreads), 0,
-                           st, a);
+        hipLaunchKernelGGL(k_block_combine, dim3((unsigned)(s.B * s.H * a.gblocks * kCombineGroups)),
+                           dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 

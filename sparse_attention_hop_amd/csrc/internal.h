@@ -163,9 +163,10 @@ struct attn_shape {
 
 // Writes A; when row_scale != nullptr also 1 / (sum of each row's stored
 // weights) per (b, h, row).
+// `part`: the block-tile kernels' scratch (block_part_bytes), or null.
 hipError_t launch_scores_softmax(const diffuser_graph& g, const attn_shape& s, const void* Q,
                                  const void* K, void* A, float* row_scale, float scale_log2,
-                                 hipStream_t st);
+                                 hipStream_t st, float* part = nullptr);
 
 // The same on scheduled graphs (bf16, d_h = 64), LDS-streamed with MFMA.
 // normalized: A holds the softmax weights; otherwise A holds exp(s - m)
@@ -200,7 +201,7 @@ hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, con
 bool fast_block_supported(const diffuser_graph& g, const attn_shape& s);
 hipError_t launch_block_scores(const diffuser_graph& g, const attn_shape& s, const void* Q,
                                const void* K, void* A, float* row_scale, float scale_log2,
-                               bool normalized, hipStream_t st);
+                               bool normalized, float* part, hipStream_t st);
 // The diffusion step splits each global query block's key blocks over
 // several workgroups, whose fp32 partial sums (block_part_bytes of scratch
 // at `part`) a second kernel adds in a fixed order.

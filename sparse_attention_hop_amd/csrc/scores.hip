@@ -191,10 +191,11 @@ hipError_t launch_scores_softmax_f32(const diffuser_graph& g, const attn_shape& 
 
 hipError_t launch_scores_softmax(const diffuser_graph& g, const attn_shape& s, const void* Q,
                                  const void* K, void* A, float* row_scale, float scale_log2,
-                                 hipStream_t st) {
+                                 hipStream_t st, float* part) {
     const bool aligned = (reinterpret_cast<uintptr_t>(A) & 15u) == 0;
     if (aligned && fast_block_supported(g, s))
-        return launch_block_scores(g, s, Q, K, A, row_scale, scale_log2, row_scale == nullptr, st);
+        return launch_block_scores(g, s, Q, K, A, row_scale, scale_log2, row_scale == nullptr, part,
+                                   st);
     if (aligned && fast_scores_supported(g, s))
         return launch_scores_fast(g, s, Q, K, A, row_scale, scale_log2, row_scale == nullptr, st);
     if (s.dtype == DIFFUSER_F32) return launch_d<float>(g, s, Q, K, A, row_scale, scale_log2, st);
