@@ -57,23 +57,6 @@ struct BlockArgs {
                                // scores: pmax then psum, each [B*H][gblocks][gparts][64]
 };
 
-// Query block of workgroup blk: XCD blk % 8 runs position blk / 8 of its
-// own contiguous range of (bh, block) items.
-struct BlockItem {
-    int32_t bh, I;
-    bool valid;
-};
-
-__device__ __forceinline__ BlockItem block_item(uint32_t blk, const BlockArgs& a) {
-    const int32_t item = (int32_t)(blk & 7u) * a.per_xcd + (int32_t)(blk >> 3);
-    BlockItem it{0, 0, false};
-    if (item >= a.total) return it;
-    it.bh = item / a.nblocks;
-    it.I = item - it.bh * a.nblocks;
-    it.valid = true;
-    return it;
-}
-
 // The query block's key-block list and where its rows' weight slots start.
 struct BlockRows {
     int32_t k0, nk;      // key blocks bcol[k0 .. k0 + nk)
@@ -430,6 +413,20 @@ int32_t global_parts(const diffuser_graph& g) {
     return g.global_blocks > 0 && g.nblocks > kSplit ? (int32_t)((g.nblocks + kSplit - 1) / kSplit)
                                                     : 0;
 }
+
+BlockArgs block_args(const diffuser_graph& g, const attn_shape& s) {
+    BlockArgs a{};
+    a.n = g.n;
+    a.H = s.H;
+    a.num_graphs = g.num_graphs;
+    a.nblocks = (int32_t)g.nblocks;
+    a.slot_off = g.d_slot_off;
+    a.bptr = g.d_bptr;
+    a.bcol = g.d_bcol;
+    return a;
+}
+
+}  // namespace
 
 size_t block_part_bytes(const diffuser_graph& g, const attn_shape& s) {
     return (size_t)s.B * s.H * g.global_blocks * global_parts(g) * kBlk * kD * sizeof(float);
