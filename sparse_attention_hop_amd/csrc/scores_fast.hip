@@ -288,20 +288,30 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
 
     if (more) dma_chunk(nxt, Kbh, a.n, c0 + kChunkRows, wave, lane);
 
-    // Random groups: two tiles of 16 slots each (staged ones from LDS, any
-    // others straight from memory).
-    for (int32_t k = 0; k < gcnt; ++k) {
-        const bool staged = k < kStageGroups;
-        const char LDS_AS* o = stg + (staged ? k : 0) * kSGroupBytes;
+    // Random groups: two tiles of 16 slots each. The staged ones read their
+    // codes from LDS, any others straight from memory; the two loops are
+    // kept apart so that no register is loaded from both places, which would
+    // make every LDS read wait for all outstanding memory operations (the
+    // next chunk's loads and the weight stores among them).
+    const int32_t nstaged = min(gcnt, kStageGroups);
+    for (int32_t k = 0; k < nstaged; ++k) {
+        const char LDS_AS* o = stg + k * kSGroupBytes;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t code = *reinterpret_cast<const uint16_t LDS_AS*>(o + 2 * (16 * h + t.s16));
+            const uint32_t rows2 = *reinterpret_cast<const uint16_t LDS_AS*>(o + 64 + 8 * h + 2 * t.kg);
+            u32x4 k0, k1;
+            k_operands(cur, code, (uint32_t)t.kg, k0, k1);
+            random_tile<P>(t, dots(k0, k1, t.q0, t.q1), rows2, a.scale_log2,
+                           Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 16 * h + 4 * t.kg);
+        }
+    }
+    for (int32_t k = nstaged; k < gcnt; ++k) {
         const int64_t gi = t.goff + g0 + k;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint32_t code =
-                staged ? *reinterpret_cast<const uint16_t LDS_AS*>(o + 2 * (16 * h + t.s16))
-                       : a.sched_k[gi * kGroupSlots + 16 * h + t.s16];
-            const uint32_t rows2 =
-                staged ? *reinterpret_cast<const uint16_t LDS_AS*>(o + 64 + 8 * h + 2 * t.kg)
-                       : reinterpret_cast<const uint16_t*>(a.sched_row + gi * 4)[4 * h + t.kg];
+            const uint32_t code = a.sched_k[gi * kGroupSlots + 16 * h + t.s16];
+            const uint32_t rows2 = reinterpret_cast<const uint16_t*>(a.sched_row + gi * 4)[4 * h + t.kg];
             u32x4 k0, k1;
             k_operands(cur, code, (uint32_t)t.kg, k0, k1);
             random_tile<P>(t, dots(k0, k1, t.q0, t.q1), rows2, a.scale_log2,
