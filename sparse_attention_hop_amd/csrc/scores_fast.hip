@@ -293,18 +293,24 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
     // kept apart so that no register is loaded from both places, which would
     // make every LDS read wait for all outstanding memory operations (the
     // next chunk's loads and the weight stores among them).
+    // Both tiles' operands are read and multiplied before either is used.
     const int32_t nstaged = min(gcnt, kStageGroups);
     for (int32_t k = 0; k < nstaged; ++k) {
         const char LDS_AS* o = stg + k * kSGroupBytes;
+        uint32_t rows2[2];
+        f32x4 x[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t code = *reinterpret_cast<const uint16_t LDS_AS*>(o + 2 * (16 * h + t.s16));
-            const uint32_t rows2 = *reinterpret_cast<const uint16_t LDS_AS*>(o + 64 + 8 * h + 2 * t.kg);
+            rows2[h] = *reinterpret_cast<const uint16_t LDS_AS*>(o + 64 + 8 * h + 2 * t.kg);
             u32x4 k0, k1;
             k_operands(cur, code, (uint32_t)t.kg, k0, k1);
-            random_tile<P>(t, dots(k0, k1, t.q0, t.q1), rows2, a.scale_log2,
-                           Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 16 * h + 4 * t.kg);
+            x[h] = dots(k0, k1, t.q0, t.q1);
         }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            random_tile<P>(t, x[h], rows2[h], a.scale_log2,
+                           Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 16 * h + 4 * t.kg);
     }
     for (int32_t k = nstaged; k < gcnt; ++k) {
         const int64_t gi = t.goff + g0 + k;
