@@ -30,11 +30,8 @@
 // (kChunkRows keys) with random edges, the block's edges into that chunk by
 // row, then column, two edges of one row per pair (an odd one out paired
 // with a dummy), 16 pairs = kGroupSlots slots per group, the last group of
-// a (block, chunk) padded with dummy pairs. Within a group the k-th pair in
-// that order takes position 2k (k < 8) or 2 (k - 8) + 1, so the two pairs
-// at positions 2m, 2m + 1 (read by one lane of the score kernel) are 8 apart
-// in row order and, unless a row has more than 8 pairs in the group, belong
-// to different rows. Padding and dummy slots carry row and column -1 and
+// a (block, chunk) padded with dummy pairs; pair p of a group owns slots
+// 2p and 2p + 1. Padding and dummy slots carry row and column -1 and
 // weight 0.
 #include "internal.h"
 
@@ -363,7 +360,7 @@ struct SchedArgs {
     int32_t* grp_cptr;             // [graphs][nrb][nchunks + 1]
     uint8_t* sched_row;            // [groups][16] pair rows
     uint16_t* sched_j;             // [groups][32] slot key rows (diffusion layout)
-    uint16_t* sched_k;             // [groups][32] slot key rows (score layout)
+    uint16_t* sched_k;             // [groups][32] key rows, slot h of pair p at 16 h + p
     int32_t* slot_col;
     int32_t* slot_row;
     int32_t* rslot;
@@ -383,12 +380,6 @@ __device__ __forceinline__ int32_t wave_min(int32_t v) {
 __device__ __forceinline__ int32_t sched_j_index(int32_t s) {
     const int32_t k = s >> 3, a = s & 7;
     return 2 * (4 * k + (a & 3)) + (a >> 2);
-}
-
-// Position within its group of the q-th pair (0..15) of the group in row
-// order.
-__device__ __forceinline__ int32_t pair_position(int32_t q) {
-    return q < 8 ? 2 * q : 2 * (q - 8) + 1;
 }
 
 template <bool kFill>
@@ -438,7 +429,7 @@ void k_sched(SchedArgs a) {
             for (int32_t t = 0; t < pairs; ++t) {
                 const int32_t pidx = pre + t;
                 const int64_t gg = gbase + g0 + pidx / 16;
-                const int32_t pig = pair_position(pidx % 16);
+                const int32_t pig = pidx % 16;
                 const bool lone = p + 2 * t + 1 >= k;   // second slot is a dummy
                 a.sched_row[gg * 16 + pig] = (uint8_t)(lane | (lone ? 0x80 : 0));
                 for (int h = 0; h < 2; ++h) {
@@ -448,7 +439,7 @@ void k_sched(SchedArgs a) {
                     const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
                     const uint32_t jr = real ? (uint32_t)(rr[kk] - c * kChunkRows) : kZeroRow;
                     a.sched_j[gg * kGroupSlots + sched_j_index(s)] = (uint16_t)key_row_code(jr);
-                    a.sched_k[gg * kGroupSlots + s] = (uint16_t)score_row_code(jr);
+                    a.sched_k[gg * kGroupSlots + 16 * h + pig] = (uint16_t)score_row_code(jr);
                     a.slot_col[soff + slot] = real ? rr[kk] : -1;
                     a.slot_row[soff + slot] = real ? (int32_t)i : -1;
                     if (real) a.rslot[row * (int64_t)a.rnd_width + kk] = (int32_t)slot;
@@ -457,13 +448,13 @@ void k_sched(SchedArgs a) {
             // Dummy pairs that pad the chunk's last group.
             for (int32_t pidx = total + lane; pidx < 16 * ng; pidx += kWave) {
                 const int64_t gg = gbase + g0 + pidx / 16;
-                const int32_t pig = pair_position(pidx % 16);
+                const int32_t pig = pidx % 16;
                 a.sched_row[gg * 16 + pig] = (uint8_t)0xFF;
                 for (int h = 0; h < 2; ++h) {
                     const int32_t s = 2 * pig + h;
                     const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
                     a.sched_j[gg * kGroupSlots + sched_j_index(s)] = (uint16_t)key_row_code(kZeroRow);
-                    a.sched_k[gg * kGroupSlots + s] = (uint16_t)score_row_code(kZeroRow);
+                    a.sched_k[gg * kGroupSlots + 16 * h + pig] = (uint16_t)score_row_code(kZeroRow);
                     a.slot_col[soff + slot] = -1;
                     a.slot_row[soff + slot] = -1;
                 }

@@ -87,9 +87,9 @@ struct diffuser_graph {
     // padded to a multiple of 8). Rows form blocks of kRowBlock, key rows
     // chunks of kChunkRows. For each (row block, chunk) the block's random
     // edges with keys in the chunk are listed by row, two edges of one row
-    // per pair (a lone edge is paired with a dummy), 16 pairs per group (the
-    // k-th pair in row order at position 2k, k < 8, or 2 (k - 8) + 1); a
-    // group's 32 weights occupy 32 consecutive slots of the random area.
+    // per pair (a lone edge is paired with a dummy), 16 pairs per group in
+    // that order, pair p owning slots 2p and 2p + 1; a group's 32 weights
+    // occupy 32 consecutive slots of the random area.
     bool scheduled = false;
     std::vector<int64_t> groups;    // [num_graphs]
     std::vector<int64_t> grp_off;   // [num_graphs + 1] prefix sums of groups
@@ -106,7 +106,7 @@ struct diffuser_graph {
                                     //   half) and of slot 8k + 4 + a (high half);
                                     //   kZeroRow's code for a dummy
     uint16_t* d_sched_k = nullptr;  // [groups][32]: score_row_code of the key row of
-                                    //   each slot, in slot order
+                                    //   slot h of pair p (slot 2 p + h) at 16 h + p
 
     // Column index of the weight slots (built on first use by the backward
     // pass, under bw_mutex): for each graph, col_ptr [n + 1] and, from

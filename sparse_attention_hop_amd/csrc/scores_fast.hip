@@ -95,10 +95,14 @@ __device__ __forceinline__ void k_operands(const char LDS_AS* buf, uint32_t code
     k1 = *reinterpret_cast<const u32x4 LDS_AS*>(buf + (o ^ 64u));   // unit kg + 4
 }
 
-// Unscaled dot products D[key][row] of one 16 x 16 tile.
-__device__ __forceinline__ f32x4 dots(const u32x4& k0, const u32x4& k1, const u32x4& q0,
-                                      const u32x4& q1) {
-    return mfma_bf16(k1, q1, mfma_bf16(k0, q0, f32x4{0.f, 0.f, 0.f, 0.f}));
+// Unscaled dot products of one 16 x 16 tile, D[i][j] = a_i . b_j over the
+// 64 channels, where lane (kg, s16) supplies channels 8 kg .. + 7 and
+// 32 + 8 kg .. + 7 of a_{s16} (a0, a1) and of b_{s16} (b0, b1) and receives
+// D[4 kg + e][s16] in element e. Band and global tiles take keys as a
+// (D[key][row]), random groups take query rows as a (D[row][key]).
+__device__ __forceinline__ f32x4 dots(const u32x4& a0, const u32x4& a1, const u32x4& b0,
+                                      const u32x4& b1) {
+    return mfma_bf16(a1, b1, mfma_bf16(a0, b0, f32x4{0.f, 0.f, 0.f, 0.f}));
 }
 
 // Direct loads of chunk rows [c0, c0 + kChunkRows) of K into `buf` (wave w
@@ -142,6 +146,10 @@ struct SLane {
     int64_t goff, rbase;
     u32x4 pk;                  // next chunk's score codes, compact
     uint32_t pr;               // next chunk's pair rows, compact
+    // Random groups put row 4 kg + e in element e of a lane's products:
+    float ms4[4];              // shift of rows 4 kg + e
+    float inv4[4];             // inverse sums of rows 4 kg + e (normalised write)
+    float racc[4];             // their random weights' max (max pass) or sum
 };
 
 // Pass-specific treatment of 4 dot products of consecutive slots of the
@@ -207,54 +215,93 @@ __device__ __forceinline__ void band_tile(SLane& t, const ScoreArgs& a, uint16_t
     consume4<P, true>(t, x, valid, a.scale_log2, dst);
 }
 
-// One random tile: slots 16 h .. 16 h + 15 of a group. The lane's slots
-// 16 h + 4 kg + e are pairs 8 h + 2 kg + e / 2, whose bytes (row, + 0x80
-// when the second slot is a dummy, 0xFF for a dummy pair) are `rows2`;
-// gdst is the weight slot of the lane's first slot.
+// Element e = 2 b1 + b0 of x, for a lane-dependent e.
+__device__ __forceinline__ float pick4(float x0, float x1, float x2, float x3, bool b0, bool b1) {
+    const float lo = b0 ? x1 : x0, hi = b0 ? x3 : x2;
+    return b1 ? hi : lo;
+}
+
+// One random group. The products are taken with the query rows as the
+// first operand: lane (kg, s16) holds, in element e of x0 (x1), the product
+// of row 4 kg + e with the key of slot 0 (1) of pair s16, whose row byte
+// (row, + 0x80 when the second slot is a dummy, 0xFF for a dummy pair) is
+// rb. The lane of kg = row / 4 owns the pair: two exponentials, one 4-byte
+// store of both weights at gdst (slot 2 s16 of the group), and the pair's
+// share of row 4 kg + e in racc[e]. A dummy pair is written by the lane of
+// kg = 0.
 template <int P>
-__device__ __forceinline__ void random_tile(SLane& t, const f32x4& x, uint32_t rows2,
-                                            float scale_log2, uint16_t* gdst) {
-    const uint32_t ra = rows2 & 0xffu, rb = (rows2 >> 8) & 0xffu;
-    const uint32_t me = (uint32_t)t.s16;
-    const bool ma = (ra & 0x7fu) == me, mb = (rb & 0x7fu) == me;
-    const bool sa = (ra & 0x80u) != 0, sb = (rb & 0x80u) != 0;   // lone slots
+__device__ __forceinline__ void random_group(SLane& t, const f32x4& x0, const f32x4& x1,
+                                             uint32_t rb, float scale_log2, uint16_t* gdst) {
+    const uint32_t r = rb & 0x7fu;
+    const bool mine = (r >> 2) == (uint32_t)t.kg;
+    const bool two = mine && (rb & 0x80u) == 0;
+    const bool b0 = (r & 1u) != 0, b1 = (r & 2u) != 0;
+    const float y0 = pick4(x0[0], x0[1], x0[2], x0[3], b0, b1);
+    const float y1 = pick4(x1[0], x1[1], x1[2], x1[3], b0, b1);
+    float v;
     if (P == kPassMax) {
-        if (ma) t.m = fmaxf(t.m, fmaxf(x[0], sa ? x[0] : x[1]));
-        if (mb) t.m = fmaxf(t.m, fmaxf(x[2], sb ? x[2] : x[3]));
-        return;
-    }
-    float w[4];
-    if (!__any(ma && mb)) {
-        // The schedule interleaves rows, so a lane almost never owns both
-        // of its pairs: two exponentials, of the pair it owns (if any).
-        const float y0 = ma ? x[0] : x[2], y1 = ma ? x[1] : x[3];
-        const float e0 = exp2f_fast(__builtin_fmaf(y0, scale_log2, -t.ms));
-        const float e1 = exp2f_fast(__builtin_fmaf(y1, scale_log2, -t.ms));
-        w[0] = ma ? e0 : 0.0f;
-        w[1] = ma && !sa ? e1 : 0.0f;
-        w[2] = mb ? e0 : 0.0f;
-        w[3] = mb && !sb ? e1 : 0.0f;
+        v = mine ? (two ? fmaxf(y0, y1) : y0) : -INFINITY;
     } else {
+        const float ms = pick4(t.ms4[0], t.ms4[1], t.ms4[2], t.ms4[3], b0, b1);
+        float w0 = exp2f_fast(__builtin_fmaf(y0, scale_log2, -ms));
+        float w1 = exp2f_fast(__builtin_fmaf(y1, scale_log2, -ms));
+        w0 = mine ? w0 : 0.0f;
+        w1 = two ? w1 : 0.0f;
+        if (P == kPassSum) {
+            v = w0 + w1;
+        } else {
+            if (P == kPassWriteNorm) {
+                const float inv = pick4(t.inv4[0], t.inv4[1], t.inv4[2], t.inv4[3], b0, b1);
+                w0 *= inv;
+                w1 *= inv;
+            }
+            const uint32_t pw = to_bf16_pair(w0, w1);
+            if (mine || (rb == 0xffu && t.kg == 0)) *reinterpret_cast<uint32_t*>(gdst) = pw;
+            if (P == kPassWriteNorm) return;
+            v = add_pair(pw, 0.0f);   // fused mode: c_i is over the weights as stored
+        }
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = exp2f_fast(__builtin_fmaf(x[e], scale_log2, -t.ms));
-        w[0] = ma ? w[0] : 0.0f;
-        w[1] = ma && !sa ? w[1] : 0.0f;
-        w[2] = mb ? w[2] : 0.0f;
-        w[3] = mb && !sb ? w[3] : 0.0f;
+    for (int e = 0; e < 4; ++e) {
+        const bool here = b0 == ((e & 1) != 0) && b1 == ((e & 2) != 0);
+        if (P == kPassMax) t.racc[e] = here ? fmaxf(t.racc[e], v) : t.racc[e];
+        else t.racc[e] = here ? t.racc[e] + v : t.racc[e];
     }
-    if (P == kPassSum) {
-        t.sum += (w[0] + w[1]) + (w[2] + w[3]);
-        return;
-    }
-    if (P == kPassWriteNorm) {
+}
+
+// Start of a pass: random accumulators cleared, the shift (and inverse sum)
+// of rows 4 kg + e fetched from the lanes of those rows.
+template <int P>
+__device__ __forceinline__ void random_begin(SLane& t) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] *= t.inv;
+    for (int e = 0; e < 4; ++e) {
+        t.racc[e] = P == kPassMax ? -INFINITY : 0.0f;
+        if (P != kPassMax) t.ms4[e] = __shfl(t.ms, 4 * t.kg + e);
+        if (P == kPassWriteNorm) t.inv4[e] = __shfl(t.inv, 4 * t.kg + e);
     }
-    const uint32_t pa = to_bf16_pair(w[0], w[1]), pb = to_bf16_pair(w[2], w[3]);
-    // A pair is written by the lane of its row; a dummy pair by row 0's lane.
-    if (ma || (ra == 0xffu && me == 0)) *reinterpret_cast<uint32_t*>(gdst) = pa;
-    if (mb || (rb == 0xffu && me == 0)) *reinterpret_cast<uint32_t*>(gdst + 2) = pb;
-    if (P == kPassWriteFused) t.sum = add_pair(pb, add_pair(pa, t.sum));
+}
+
+// End of a pass: racc[e] over the 16 lanes of kg (row 4 kg + e), then
+// into the row's lanes: into m (max pass) or, once per row, into sum.
+template <int P>
+__device__ __forceinline__ void random_end(SLane& t) {
+    if (P == kPassWriteNorm) return;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const float o = __shfl_xor(t.racc[e], off);
+            t.racc[e] = P == kPassMax ? fmaxf(t.racc[e], o) : t.racc[e] + o;
+        }
+    }
+    float row = P == kPassMax ? -INFINITY : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float o = __shfl(t.racc[e], 16 * (t.s16 >> 2));
+        if ((t.s16 & 3) == e) row = o;
+    }
+    if (P == kPassMax) t.m = fmaxf(t.m, row);
+    else if (t.kg == 0) t.sum += row;
 }
 
 // One key chunk of a row-tile wave in pass P: band tiles of chunk c, then
@@ -293,36 +340,34 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
     // kept apart so that no register is loaded from both places, which would
     // make every LDS read wait for all outstanding memory operations (the
     // next chunk's loads and the weight stores among them).
-    // Both tiles' operands are read and multiplied before either is used.
     const int32_t nstaged = min(gcnt, kStageGroups);
     for (int32_t k = 0; k < nstaged; ++k) {
         const char LDS_AS* o = stg + k * kSGroupBytes;
-        uint32_t rows2[2];
         f32x4 x[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t code = *reinterpret_cast<const uint16_t LDS_AS*>(o + 2 * (16 * h + t.s16));
-            rows2[h] = *reinterpret_cast<const uint16_t LDS_AS*>(o + 64 + 8 * h + 2 * t.kg);
             u32x4 k0, k1;
             k_operands(cur, code, (uint32_t)t.kg, k0, k1);
-            x[h] = dots(k0, k1, t.q0, t.q1);
+            x[h] = dots(t.q0, t.q1, k0, k1);
         }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            random_tile<P>(t, x[h], rows2[h], a.scale_log2,
-                           Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 16 * h + 4 * t.kg);
+        const uint32_t rb = *reinterpret_cast<const uint8_t LDS_AS*>(o + 64 + t.s16);
+        random_group<P>(t, x[0], x[1], rb, a.scale_log2,
+                        Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 2 * t.s16);
     }
     for (int32_t k = nstaged; k < gcnt; ++k) {
         const int64_t gi = t.goff + g0 + k;
+        f32x4 x[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t code = a.sched_k[gi * kGroupSlots + 16 * h + t.s16];
-            const uint32_t rows2 = reinterpret_cast<const uint16_t*>(a.sched_row + gi * 4)[4 * h + t.kg];
             u32x4 k0, k1;
             k_operands(cur, code, (uint32_t)t.kg, k0, k1);
-            random_tile<P>(t, dots(k0, k1, t.q0, t.q1), rows2, a.scale_log2,
-                           Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 16 * h + 4 * t.kg);
+            x[h] = dots(t.q0, t.q1, k0, k1);
         }
+        const uint32_t rb = reinterpret_cast<const uint8_t*>(a.sched_row + gi * 4)[t.s16];
+        random_group<P>(t, x[0], x[1], rb, a.scale_log2,
+                        Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 2 * t.s16);
     }
     if (more && lane < 4 * ncnt) {
         char LDS_AS* d = stg + (lane >> 2) * kSGroupBytes;
@@ -387,6 +432,7 @@ __device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uin
     const int32_t LDS_AS* gidx = (const int32_t LDS_AS*)(zg + gpad * kRowBytes);
     char LDS_AS* stg = zg + gpad * (kRowBytes + 4) + wave * kStageBytes;
 
+    random_begin<P>(t);
     if (!prestaged) {
         stage_first(t, a, Kbh, lds, stg, active, wave, lane);
         full_barrier();
@@ -401,6 +447,7 @@ __device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uin
             dma_chunk((c & 1) ? buf0 : buf1, Kbh, a.n, (c + 1) * kChunkRows, wave, lane);
         }
     }
+    random_end<P>(t);
     full_barrier();   // every wave is done with the buffers
 }
 
