@@ -360,7 +360,7 @@ struct SchedArgs {
     int32_t* grp_cptr;             // [graphs][nrb][nchunks + 1]
     uint8_t* sched_row;            // [groups][16] pair rows
     uint16_t* sched_j;             // [groups][32] slot key rows (diffusion layout)
-    uint16_t* sched_k;             // [groups][32] key rows, slot h of pair p at 16 h + p
+    uint16_t* sched_k;             // [groups][32] slot key rows (score layout)
     int32_t* slot_col;
     int32_t* slot_row;
     int32_t* rslot;
@@ -439,7 +439,7 @@ void k_sched(SchedArgs a) {
                     const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
                     const uint32_t jr = real ? (uint32_t)(rr[kk] - c * kChunkRows) : kZeroRow;
                     a.sched_j[gg * kGroupSlots + sched_j_index(s)] = (uint16_t)key_row_code(jr);
-                    a.sched_k[gg * kGroupSlots + 16 * h + pig] = (uint16_t)score_row_code(jr);
+                    a.sched_k[gg * kGroupSlots + s] = (uint16_t)score_row_code(jr);
                     a.slot_col[soff + slot] = real ? rr[kk] : -1;
                     a.slot_row[soff + slot] = real ? (int32_t)i : -1;
                     if (real) a.rslot[row * (int64_t)a.rnd_width + kk] = (int32_t)slot;
@@ -454,7 +454,7 @@ void k_sched(SchedArgs a) {
                     const int32_t s = 2 * pig + h;
                     const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
                     a.sched_j[gg * kGroupSlots + sched_j_index(s)] = (uint16_t)key_row_code(kZeroRow);
-                    a.sched_k[gg * kGroupSlots + 16 * h + pig] = (uint16_t)score_row_code(kZeroRow);
+                    a.sched_k[gg * kGroupSlots + s] = (uint16_t)score_row_code(kZeroRow);
                     a.slot_col[soff + slot] = -1;
                     a.slot_row[soff + slot] = -1;
                 }

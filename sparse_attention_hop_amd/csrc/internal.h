@@ -106,7 +106,7 @@ struct diffuser_graph {
                                     //   half) and of slot 8k + 4 + a (high half);
                                     //   kZeroRow's code for a dummy
     uint16_t* d_sched_k = nullptr;  // [groups][32]: score_row_code of the key row of
-                                    //   slot h of pair p (slot 2 p + h) at 16 h + p
+                                    //   each slot, in slot order
 
     // Column index of the weight slots (built on first use by the backward
     // pass, under bw_mutex): for each graph, col_ptr [n + 1] and, from

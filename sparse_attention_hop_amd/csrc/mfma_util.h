@@ -62,10 +62,10 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Work item (batch-head pair, sub-item) of workgroup `blk`: XCD blk % 8
 // runs position blk / 8 of its own list. When the pairs split evenly over
-// the 8 XCDs (bh_per_xcd > 0), an XCD's list is its pairs' row tiles
-// (sub >= grow) followed by their global-row items (sub < grow), so the
-// last, partly filled round of workgroups holds the short items; otherwise
-// the lists are consecutive runs of (bh, sub) order.
+// the 8 XCDs (bh_per_xcd > 0), an XCD's list is its pairs' global-row
+// items (sub < grow), which read every key and take longest, followed by
+// their row tiles (sub >= grow); otherwise the lists are consecutive runs
+// of (bh, sub) order.
 struct WorkItem {
     int32_t bh, sub;
     bool valid;
@@ -76,14 +76,14 @@ __device__ __forceinline__ WorkItem work_item(uint32_t blk, int32_t per_xcd, int
     const int32_t x = (int32_t)(blk & 7u), pos = (int32_t)(blk >> 3);
     WorkItem w{0, 0, false};
     if (bh_per_xcd > 0) {
-        const int32_t nt = bh_per_xcd * tiles;
-        if (pos < nt) {
-            w.bh = x * bh_per_xcd + pos / tiles;
-            w.sub = grow + pos % tiles;
+        const int32_t ng = bh_per_xcd * grow;
+        if (pos < ng) {
+            w.bh = x * bh_per_xcd + pos / grow;
+            w.sub = pos % grow;
             w.valid = true;
-        } else if (pos - nt < bh_per_xcd * grow) {
-            w.bh = x * bh_per_xcd + (pos - nt) / grow;
-            w.sub = (pos - nt) % grow;
+        } else if (pos - ng < bh_per_xcd * tiles) {
+            w.bh = x * bh_per_xcd + (pos - ng) / tiles;
+            w.sub = grow + (pos - ng) % tiles;
             w.valid = true;
         }
         return w;

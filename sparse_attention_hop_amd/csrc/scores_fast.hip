@@ -343,10 +343,11 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
     const int32_t nstaged = min(gcnt, kStageGroups);
     for (int32_t k = 0; k < nstaged; ++k) {
         const char LDS_AS* o = stg + k * kSGroupBytes;
+        const uint32_t codes = *reinterpret_cast<const uint32_t LDS_AS*>(o + 4 * t.s16);
         f32x4 x[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint32_t code = *reinterpret_cast<const uint16_t LDS_AS*>(o + 2 * (16 * h + t.s16));
+            const uint32_t code = (codes >> (16 * h)) & 0xffffu;
             u32x4 k0, k1;
             k_operands(cur, code, (uint32_t)t.kg, k0, k1);
             x[h] = dots(t.q0, t.q1, k0, k1);
@@ -357,10 +358,11 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
     }
     for (int32_t k = nstaged; k < gcnt; ++k) {
         const int64_t gi = t.goff + g0 + k;
+        const uint32_t codes = reinterpret_cast<const uint32_t*>(a.sched_k + gi * kGroupSlots)[t.s16];
         f32x4 x[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint32_t code = a.sched_k[gi * kGroupSlots + 16 * h + t.s16];
+            const uint32_t code = (codes >> (16 * h)) & 0xffffu;
             u32x4 k0, k1;
             k_operands(cur, code, (uint32_t)t.kg, k0, k1);
             x[h] = dots(t.q0, t.q1, k0, k1);
