@@ -24,6 +24,9 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = kWave * kWavesPerBlock;
+// Slot steps whose index and row loads a wave issues before it uses any of
+// them: the products are bound by the latency of those dependent loads.
+constexpr int kUnroll = 4;
 
 __device__ __forceinline__ float ld(const float* p) { return *p; }
 __device__ __forceinline__ float ld(const bf16_t* p) { return bf16_to_f32(p->bits); }
@@ -58,18 +61,28 @@ void k_rows(GenericGraph gg, int32_t H, const float* __restrict__ W, const TX* _
     const TX* Xb = X + (int64_t)bh * n * D + 4 * sub;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const int64_t cnt = rs.count();
-    for (int64_t base = 0; base < cnt; base += EPI) {
-        const int64_t e = base + grp;
-        int32_t j = -1;
-        int64_t s = 0;
-        if (e < cnt) s = rs.slot(e, j);
-        if (j >= 0) {
-            const float w = Wb[s];
-            float x[4];
-            ld4(Xb + (int64_t)j * D, x);
+    for (int64_t base = 0; base < cnt; base += EPI * kUnroll) {
+        // Slots base + u EPI + grp; padding and slots past the row read
+        // column 0 with weight 0.
+        int32_t j[kUnroll];
+        int64_t s[kUnroll];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = fmaf(w, x[c], acc[c]);
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t e = base + u * EPI + grp;
+            j[u] = -1;
+            s[u] = 0;
+            if (e < cnt) s[u] = rs.slot(e, j[u]);
         }
+        float w[kUnroll], x[kUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            w[u] = j[u] >= 0 ? Wb[s[u]] : 0.0f;
+            ld4(Xb + (int64_t)(j[u] >= 0 ? j[u] : 0) * D, x[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(w[u], x[u][c], acc[c]);
     }
 #pragma unroll
     for (int off = L; off < kWave; off <<= 1)
@@ -119,14 +132,30 @@ void k_cols(ColIndex ci, int32_t H, const float* __restrict__ W, const TX* __res
     const TX* Xb = X + (int64_t)bh * n * D + 4 * sub;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const int64_t e0 = cp[j], e1 = cp[j + 1];
-    for (int64_t e = e0 + grp; e < e1; e += EPI) {
-        const int32_t s = cs[e];
-        const int64_t i = srow[s];
-        const float w = Wb[s];
-        float x[4];
-        ld4(Xb + i * D, x);
+    for (int64_t base = e0; base < e1; base += EPI * kUnroll) {
+        // Entries base + u EPI + grp; those past the column read slot
+        // cs[e0] with weight 0.
+        int32_t s[kUnroll];
+        bool ok[kUnroll];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = fmaf(w, x[c], acc[c]);
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t e = base + u * EPI + grp;
+            ok[u] = e < e1;
+            s[u] = cs[ok[u] ? e : e0];
+        }
+        int64_t i[kUnroll];
+        float w[kUnroll], x[kUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            i[u] = srow[s[u]];
+            w[u] = ok[u] ? Wb[s[u]] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) ld4(Xb + i[u] * D, x[u]);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(w[u], x[u][c], acc[c]);
     }
 #pragma unroll
     for (int off = L; off < kWave; off <<= 1)
@@ -158,19 +187,31 @@ void k_edge_dots(GenericGraph gg, int32_t H, const float* __restrict__ G,
     const float4 g = *reinterpret_cast<const float4*>(G + ((int64_t)bh * n + i) * D + 4 * sub);
     const float* Zb = Z + (int64_t)bh * n * D + 4 * sub;
     const int64_t cnt = rs.count();
-    for (int64_t base = 0; base < cnt; base += EPI) {
-        const int64_t e = base + grp;
-        int32_t j = -1;
-        int64_t s = 0;
-        if (e < cnt) s = rs.slot(e, j);
-        float dot = 0.0f;
-        if (j >= 0) {
-            const float4 z = *reinterpret_cast<const float4*>(Zb + (int64_t)j * D);
-            dot = g.x * z.x + g.y * z.y + g.z * z.z + g.w * z.w;
+    for (int64_t base = 0; base < cnt; base += EPI * kUnroll) {
+        int32_t j[kUnroll];
+        int64_t s[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t e = base + u * EPI + grp;
+            j[u] = -1;
+            s[u] = 0;
+            if (e < cnt) s[u] = rs.slot(e, j[u]);
+        }
+        float dot[kUnroll], old[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const float4 z =
+                *reinterpret_cast<const float4*>(Zb + (int64_t)(j[u] >= 0 ? j[u] : 0) * D);
+            dot[u] = g.x * z.x + g.y * z.y + g.z * z.z + g.w * z.w;
+            old[u] = (j[u] >= 0 && sub == 0) ? dAb[s[u]] : 0.0f;
         }
 #pragma unroll
-        for (int off = 1; off < L; off <<= 1) dot += __shfl_xor(dot, off);
-        if (j >= 0 && sub == 0) dAb[s] += a * dot;
+        for (int off = 1; off < L; off <<= 1)
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) dot[u] += __shfl_xor(dot[u], off);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (j[u] >= 0 && sub == 0) dAb[s[u]] = old[u] + a * dot[u];
     }
 }
 
