@@ -267,8 +267,9 @@ DIFFUSER_API diffuser_status diffuser_diffuse_theta(const void* A, const void* V
  * gradients of L through Z). Q, K, V, dZ, dQ, dK, dV: [B][H][n][d] of
  * `dtype` (d_h = d_v = d); accumulation and every intermediate are fp32.
  * The workspace (size from diffuser_attn_backward_workspace_size, about
- * (2 slots + (K_steps + 3) n d) * 4 bytes per (b, h)) holds A, dA, the
- * states Z_0 .. Z_{K-1}, the backward states and dV. The first call on a
+ * (3 slots + (2 K_steps + 2) n d) * 4 bytes per (b, h)) holds A, dA, the
+ * weights in column order, the states Z_0 .. Z_{K-1}, the backward states
+ * G_0 .. G_K and dV. The first call on a
  * graph builds its column index (device memory owned by the graph, freed
  * with it; built once, under a lock, synchronising `stream`). Outputs must
  * not overlap inputs, each other or the workspace. Errors as for

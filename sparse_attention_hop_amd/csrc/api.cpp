@@ -70,6 +70,7 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_col_ptr);
     hipFree(g->d_col_off_slots);
     hipFree(g->d_col_slot);
+    hipFree(g->d_col_row);
     hipFree(g->d_bptr);
     hipFree(g->d_bcol);
     g->d_bptr = nullptr;
@@ -96,6 +97,7 @@ void free_graph_memory(diffuser_graph* g) {
     g->d_col_ptr = nullptr;
     g->d_col_off_slots = nullptr;
     g->d_col_slot = nullptr;
+    g->d_col_row = nullptr;
 }
 
 diffuser_status alloc_status(hipError_t e, const char* what) {
@@ -261,7 +263,7 @@ diffuser_status check_theta(int32_t K_steps, const float* theta) {
 // Workspace of diffuser_attn_backward (fp32 intermediates): A, dA in the A
 // layout, the states Z_0 .. Z_{K-1}, two G buffers and dV.
 struct bw_layout {
-    size_t a, zs, v, total;
+    size_t a, zs, gs, v, total;
 };
 
 bw_layout backward_layout(const diffuser_graph* g, int32_t B, int32_t H, int32_t d,
@@ -270,21 +272,23 @@ bw_layout backward_layout(const diffuser_graph* g, int32_t B, int32_t H, int32_t
     const size_t cnt = (size_t)B * H * (size_t)g->n * d;
     w.a = align_up((size_t)total_a_elems(g, B, H) * sizeof(float));
     w.zs = align_up(cnt * sizeof(float) * (size_t)K_steps);
+    w.gs = align_up(cnt * sizeof(float) * ((size_t)K_steps + 1));
     w.v = align_up(cnt * sizeof(float));
-    w.total = 2 * w.a + w.zs + 3 * w.v;
+    w.total = 3 * w.a + w.zs + w.gs + w.v;
     return w;
 }
 
 // Builds the graph's column index (once, under bw_mutex): the valid slots
 // of each graph ordered by column, then by row (two stable counting sorts
-// on the host), uploaded with per-graph column offsets.
+// on the host), with the row of each entry, uploaded with per-graph column
+// offsets.
 diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
     std::lock_guard<std::mutex> lock(g->bw_mutex);
     if (g->d_col_ptr != nullptr) return DIFFUSER_OK;
     const int64_t n = g->n;
     std::vector<int64_t> col_ptr((size_t)g->num_graphs * (n + 1));
     std::vector<int64_t> col_off(g->num_graphs + 1, 0);
-    std::vector<int32_t> col_slot;
+    std::vector<int32_t> col_slot, col_row;
     std::vector<int32_t> srow, scol, by_row;
     std::vector<int64_t> cnt;
     hipError_t e;
@@ -315,20 +319,25 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
         cnt.assign(cp, cp + n + 1);
         const size_t base = col_slot.size();
         col_slot.resize(base + valid);
+        col_row.resize(base + valid);
         for (int64_t k = 0; k < valid; ++k) {
             const int32_t s = by_row[k];
-            col_slot[base + cnt[scol[s]]++] = s;
+            const int64_t at = cnt[scol[s]]++;
+            col_slot[base + at] = s;
+            col_row[base + at] = srow[s];
         }
         col_off[gr + 1] = (int64_t)col_slot.size();
     }
     int64_t *d_ptr = nullptr, *d_off = nullptr;
-    int32_t* d_slot = nullptr;
+    int32_t *d_slot = nullptr, *d_row = nullptr;
     if ((e = dev_alloc(&d_ptr, col_ptr.size())) != hipSuccess ||
         (e = dev_alloc(&d_off, col_off.size())) != hipSuccess ||
-        (e = dev_alloc(&d_slot, col_slot.size())) != hipSuccess) {
+        (e = dev_alloc(&d_slot, col_slot.size())) != hipSuccess ||
+        (e = dev_alloc(&d_row, col_row.size())) != hipSuccess) {
         hipFree(d_ptr);
         hipFree(d_off);
         hipFree(d_slot);
+        hipFree(d_row);
         return alloc_status(e, "device allocation of the column index");
     }
     if ((e = hipMemcpyAsync(d_ptr, col_ptr.data(), sizeof(int64_t) * col_ptr.size(),
@@ -338,15 +347,20 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
         (col_slot.size() > 0 &&
          (e = hipMemcpyAsync(d_slot, col_slot.data(), sizeof(int32_t) * col_slot.size(),
                              hipMemcpyHostToDevice, st)) != hipSuccess) ||
+        (col_row.size() > 0 &&
+         (e = hipMemcpyAsync(d_row, col_row.data(), sizeof(int32_t) * col_row.size(),
+                             hipMemcpyHostToDevice, st)) != hipSuccess) ||
         (e = hipStreamSynchronize(st)) != hipSuccess) {
         hipFree(d_ptr);
         hipFree(d_off);
         hipFree(d_slot);
+        hipFree(d_row);
         return hip_fail(e, "upload of the column index");
     }
     g->d_col_ptr = d_ptr;
     g->d_col_off_slots = d_off;
     g->d_col_slot = d_slot;
+    g->d_col_row = d_row;
     return DIFFUSER_OK;
 }
 
@@ -1043,10 +1057,10 @@ diffuser_status diffuser_attn_backward(const void* Q, const void* K, const void*
     p.a_count = total_a_elems(g, B, H);
     p.A = reinterpret_cast<float*>(ws);
     p.dA = reinterpret_cast<float*>(ws + w.a);
-    p.Zs = reinterpret_cast<float*>(ws + 2 * w.a);
-    p.G0 = reinterpret_cast<float*>(ws + 2 * w.a + w.zs);
-    p.G1 = reinterpret_cast<float*>(ws + 2 * w.a + w.zs + w.v);
-    p.dV = reinterpret_cast<float*>(ws + 2 * w.a + w.zs + 2 * w.v);
+    p.At = reinterpret_cast<float*>(ws + 2 * w.a);
+    p.Zs = reinterpret_cast<float*>(ws + 3 * w.a);
+    p.Gs = reinterpret_cast<float*>(ws + 3 * w.a + w.zs);
+    p.dV = reinterpret_cast<float*>(ws + 3 * w.a + w.zs + w.gs);
     const float scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
     hipError_t e = launch_scores_softmax_f32(*g, attn_shape{B, H, d, dtype}, Q, K, p.A,
                                              scale_log2, st);

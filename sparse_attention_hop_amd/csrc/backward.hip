@@ -12,9 +12,13 @@
 // storage, d in {16, 32, 64, 128}); every intermediate (A, dA, the states
 // Z_k, G_k, dV) is fp32. Row-wise products walk a row's slots; the
 // transposed ones walk the graph's column index (the slots of each column
-// by ascending row). Each wave splits its row or column over groups of
-// lanes and adds the groups' partial sums in a fixed order, so every sum
-// has a fixed order.
+// by ascending row), with the weights first copied into that order so that
+// only the rows of X are gathered. dA takes all K terms in one pass over
+// the slots, from the stored states G_1 .. G_K. Each wave splits its row or
+// column over groups of lanes and adds the groups' partial sums in a fixed
+// order, so every sum has a fixed order.
+#include <algorithm>
+
 #include "internal.h"
 #include "vec.h"
 
@@ -107,15 +111,30 @@ struct ColIndex {
     const int64_t* col_ptr;
     const int64_t* col_off;    // [graphs + 1] start of each graph's col_slot run
     const int32_t* col_slot;
-    const int32_t* slot_row;   // [slots of all graphs]
+    const int32_t* col_row;    // row of each col_slot entry
     const int64_t* slot_off;   // [graphs + 1]
 };
 
-// Y[j] = a * sum_{slots s of column j} W[s] X[row(s)], one wave per
-// column, lanes grouped as in k_rows.
+// Wt[e] = W[col_slot[e]] for every column-index entry e of each (b, h)
+// (both at the (b, h) block's slot offset): the weights in column order.
+__global__ __launch_bounds__(kThreads)
+void k_to_columns(ColIndex ci, int32_t H, const float* __restrict__ W, float* __restrict__ Wt) {
+    const int32_t bh = blockIdx.y, bb = bh / H, hh = bh - bb * H;
+    const int32_t gr = ci.num_graphs == 1 ? 0 : bb;
+    const int32_t* cs = ci.col_slot + ci.col_off[gr];
+    const int64_t count = ci.col_off[gr + 1] - ci.col_off[gr];
+    const int64_t off = a_block_offset(ci.slot_off, ci.num_graphs, H, bb, hh);
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < count;
+         e += (int64_t)gridDim.x * kThreads)
+        Wt[off + e] = W[off + cs[e]];
+}
+
+// Y[j] = a * sum_{entries e of column j} Wt[e] X[col_row[e]], one wave per
+// column, lanes grouped as in k_rows; Wt holds the weights in column order
+// (k_to_columns).
 template <typename TX, typename TY, int D>
 __global__ __launch_bounds__(kThreads)
-void k_cols(ColIndex ci, int32_t H, const float* __restrict__ W, const TX* __restrict__ X,
+void k_cols(ColIndex ci, int32_t H, const float* __restrict__ Wt, const TX* __restrict__ X,
             TY* __restrict__ Y, float a) {
     constexpr int L = D / 4, EPI = kWave / L;
     const int wave = threadIdx.x / kWave, lane = __lane_id();
@@ -125,30 +144,23 @@ void k_cols(ColIndex ci, int32_t H, const float* __restrict__ W, const TX* __res
     const int32_t bh = blockIdx.y, bb = bh / H, hh = bh - bb * H;
     const int32_t gr = ci.num_graphs == 1 ? 0 : bb;
     const int64_t* cp = ci.col_ptr + (int64_t)gr * (n + 1);
-    const int32_t* cs = ci.col_slot + ci.col_off[gr];
-    const int32_t* srow = ci.slot_row + ci.slot_off[gr];
-    const float* Wb = W + a_block_offset(ci.slot_off, ci.num_graphs, H, bb, hh);
+    const int32_t* crow = ci.col_row + ci.col_off[gr];
+    const float* Wb = Wt + a_block_offset(ci.slot_off, ci.num_graphs, H, bb, hh);
     const int sub = lane % L, grp = lane / L;
     const TX* Xb = X + (int64_t)bh * n * D + 4 * sub;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const int64_t e0 = cp[j], e1 = cp[j + 1];
     for (int64_t base = e0; base < e1; base += EPI * kUnroll) {
-        // Entries base + u EPI + grp; those past the column read slot
-        // cs[e0] with weight 0.
-        int32_t s[kUnroll];
-        bool ok[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t e = base + u * EPI + grp;
-            ok[u] = e < e1;
-            s[u] = cs[ok[u] ? e : e0];
-        }
+        // Entries base + u EPI + grp; those past the column read entry e0
+        // with weight 0.
         int64_t i[kUnroll];
         float w[kUnroll], x[kUnroll][4];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            i[u] = srow[s[u]];
-            w[u] = ok[u] ? Wb[s[u]] : 0.0f;
+            const int64_t e = base + u * EPI + grp;
+            const bool ok = e < e1;
+            i[u] = crow[ok ? e : e0];
+            w[u] = ok ? Wb[e] : 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) ld4(Xb + i[u] * D, x[u]);
@@ -168,12 +180,14 @@ void k_cols(ColIndex ci, int32_t H, const float* __restrict__ W, const TX* __res
     }
 }
 
-// dA[s] += a * G[i] . Z[col(s)] for the slots of row i: groups of L lanes
-// take one slot each (L = D / 4 lanes of 4 channels).
+// dA[s] = a * sum_{k < K} G_{k+1}[i] . Z_k[col(s)] for the slots of row i
+// (padding slots get 0): groups of L lanes take one slot each (L = D / 4
+// lanes of 4 channels); state k of G or Z starts at k * stride.
 template <int D>
 __global__ __launch_bounds__(kThreads)
-void k_edge_dots(GenericGraph gg, int32_t H, const float* __restrict__ G,
-                 const float* __restrict__ Z, float* __restrict__ dA, float a) {
+void k_edge_dots(GenericGraph gg, int32_t H, const float* __restrict__ Gs,
+                 const float* __restrict__ Zs, int64_t stride, int32_t K, float* __restrict__ dA,
+                 float a) {
     constexpr int L = D / 4, EPI = kWave / L;
     const int wave = threadIdx.x / kWave, lane = __lane_id();
     const int64_t n = gg.n;
@@ -184,8 +198,8 @@ void k_edge_dots(GenericGraph gg, int32_t H, const float* __restrict__ G,
     const RowSlots rs = gg.row(gr, i);
     float* dAb = dA + a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
     const int sub = lane % L, grp = lane / L;
-    const float4 g = *reinterpret_cast<const float4*>(G + ((int64_t)bh * n + i) * D + 4 * sub);
-    const float* Zb = Z + (int64_t)bh * n * D + 4 * sub;
+    const float* Gi = Gs + stride + ((int64_t)bh * n + i) * D + 4 * sub;
+    const float* Zb = Zs + (int64_t)bh * n * D + 4 * sub;
     const int64_t cnt = rs.count();
     for (int64_t base = 0; base < cnt; base += EPI * kUnroll) {
         int32_t j[kUnroll];
@@ -194,16 +208,18 @@ void k_edge_dots(GenericGraph gg, int32_t H, const float* __restrict__ G,
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t e = base + u * EPI + grp;
             j[u] = -1;
-            s[u] = 0;
+            s[u] = -1;
             if (e < cnt) s[u] = rs.slot(e, j[u]);
         }
-        float dot[kUnroll], old[kUnroll];
+        float dot[kUnroll] = {};
+        for (int32_t k = 0; k < K; ++k) {
+            const float4 g = *reinterpret_cast<const float4*>(Gi + k * stride);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const float4 z =
-                *reinterpret_cast<const float4*>(Zb + (int64_t)(j[u] >= 0 ? j[u] : 0) * D);
-            dot[u] = g.x * z.x + g.y * z.y + g.z * z.z + g.w * z.w;
-            old[u] = (j[u] >= 0 && sub == 0) ? dAb[s[u]] : 0.0f;
+            for (int u = 0; u < kUnroll; ++u) {
+                const float4 z = *reinterpret_cast<const float4*>(
+                    Zb + k * stride + (int64_t)(j[u] >= 0 ? j[u] : 0) * D);
+                dot[u] += g.x * z.x + g.y * z.y + g.z * z.z + g.w * z.w;
+            }
         }
 #pragma unroll
         for (int off = 1; off < L; off <<= 1)
@@ -211,7 +227,7 @@ void k_edge_dots(GenericGraph gg, int32_t H, const float* __restrict__ G,
             for (int u = 0; u < kUnroll; ++u) dot[u] += __shfl_xor(dot[u], off);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            if (j[u] >= 0 && sub == 0) dAb[s[u]] = old[u] + a * dot[u];
+            if (s[u] >= 0 && sub == 0) dAb[s[u]] = j[u] >= 0 ? a * dot[u] : 0.0f;
     }
 }
 
@@ -264,14 +280,6 @@ void k_sum_to(int64_t count, const float* __restrict__ x, const float* __restric
         st(out + e, x[e] + y[e]);
 }
 
-// x[e] = 0 for e < count.
-__global__ __launch_bounds__(kThreads)
-void k_zero(int64_t count, float* __restrict__ x) {
-    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < count;
-         e += (int64_t)gridDim.x * kThreads)
-        x[e] = 0.0f;
-}
-
 dim3 grid_elems(int64_t count) {
     int64_t blocks = (count + kThreads - 1) / kThreads;
     if (blocks > 65536) blocks = 65536;
@@ -287,52 +295,55 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     ci.col_ptr = g.d_col_ptr;
     ci.col_off = g.d_col_off_slots;
     ci.col_slot = g.d_col_slot;
-    ci.slot_row = g.d_slot_row;
+    ci.col_row = g.d_col_row;
     ci.slot_off = g.d_slot_off;
     const int32_t BH = p.B * p.H;
     const dim3 rows((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)BH);
     const dim3 blk(kThreads);
     const int64_t cnt = (int64_t)BH * g.n * D;
+    int64_t max_entries = 0;
+    for (int32_t gr = 0; gr < g.num_graphs; ++gr)
+        max_entries = std::max(max_entries, g.slots[gr]);
+    const dim3 entries(grid_elems(max_entries).x, (unsigned)BH);
     const T* V = static_cast<const T*>(p.V);
     const float keep = 1.0f - p.alpha;
+    const int32_t K = p.K_steps;
 
-    hipLaunchKernelGGL(k_zero, grid_elems(p.a_count), blk, 0, stream, p.a_count, p.dA);
     // Forward states Z_0 = V, Z_{k+1} = (1 - alpha) A Z_k + alpha V (fp32).
-    if (p.K_steps > 0)
+    if (K > 0)
         hipLaunchKernelGGL((k_axpby<T>), grid_elems(cnt), blk, 0, stream, cnt, V, p.Zs, 1.0f,
                            0.0f);
-    for (int32_t k = 1; k < p.K_steps; ++k)
+    for (int32_t k = 1; k < K; ++k)
         hipLaunchKernelGGL((k_rows<float, T, float, D>), rows, blk, 0, stream, gg, p.H, p.A,
                            p.Zs + (size_t)(k - 1) * cnt, V, p.Zs + (size_t)k * cnt, keep,
                            p.alpha);
-    // G_K = dZ; dV = 0.
+    // G_K = dZ, G_k = (1 - alpha) A^T G_{k+1}; dV = alpha (G_K + .. + G_1).
     hipLaunchKernelGGL((k_axpby<T>), grid_elems(cnt), blk, 0, stream, cnt,
-                       static_cast<const T*>(p.dZ), p.G0, 1.0f, 0.0f);
-    float* G = p.G0;
-    float* Gn = p.G1;
-    for (int32_t k = p.K_steps - 1; k >= 0; --k) {
-        hipLaunchKernelGGL((k_edge_dots<D>), rows, blk, 0, stream, gg, p.H, G,
-                           p.Zs + (size_t)k * cnt, p.dA, keep);
-        hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, G, p.dV,
-                           p.alpha, k == p.K_steps - 1 ? 0.0f : 1.0f);
-        hipLaunchKernelGGL((k_cols<float, float, D>), rows, blk, 0, stream, ci, p.H, p.A, G, Gn,
-                           keep);
-        float* t = G;
-        G = Gn;
-        Gn = t;
+                       static_cast<const T*>(p.dZ), p.Gs + (size_t)K * cnt, 1.0f, 0.0f);
+    if (K > 0) hipLaunchKernelGGL(k_to_columns, entries, blk, 0, stream, ci, p.H, p.A, p.At);
+    for (int32_t k = K - 1; k >= 0; --k) {
+        const float* Gk1 = p.Gs + (size_t)(k + 1) * cnt;
+        hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, Gk1, p.dV,
+                           p.alpha, k == K - 1 ? 0.0f : 1.0f);
+        hipLaunchKernelGGL((k_cols<float, float, D>), rows, blk, 0, stream, ci, p.H, p.At, Gk1,
+                           p.Gs + (size_t)k * cnt, keep);
     }
+    // dA = (1 - alpha) sum_k G_{k+1} Z_k^T on the edges.
+    hipLaunchKernelGGL((k_edge_dots<D>), rows, blk, 0, stream, gg, p.H, p.Gs, p.Zs, cnt, K,
+                       p.dA, keep);
     // dV = (sum of alpha G_{k+1}) + G_0.
-    if (p.K_steps == 0)
-        hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, G, p.dV,
+    if (K == 0)
+        hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, p.Gs, p.dV,
                            0.0f, 0.0f);
-    hipLaunchKernelGGL((k_sum_to<T>), grid_elems(cnt), blk, 0, stream, cnt, p.dV, G,
+    hipLaunchKernelGGL((k_sum_to<T>), grid_elems(cnt), blk, 0, stream, cnt, p.dV, p.Gs,
                        static_cast<T*>(p.dVout));
     // dS, then dQ = dS K and dK = dS^T Q (the 1 / sqrt(d_h) inside dS).
     hipLaunchKernelGGL(k_softmax_grad, rows, blk, 0, stream, gg, p.H, p.A, p.dA, p.scale);
     hipLaunchKernelGGL((k_rows<T, T, T, D>), rows, blk, 0, stream, gg, p.H, p.dA,
                        static_cast<const T*>(p.K), static_cast<const T*>(nullptr),
                        static_cast<T*>(p.dQ), 1.0f, 0.0f);
-    hipLaunchKernelGGL((k_cols<T, T, D>), rows, blk, 0, stream, ci, p.H, p.dA,
+    hipLaunchKernelGGL(k_to_columns, entries, blk, 0, stream, ci, p.H, p.dA, p.At);
+    hipLaunchKernelGGL((k_cols<T, T, D>), rows, blk, 0, stream, ci, p.H, p.At,
                        static_cast<const T*>(p.Q), static_cast<T*>(p.dK), 1.0f);
     return hipGetLastError();
 }

@@ -127,6 +127,7 @@ struct diffuser_graph {
     int64_t* d_col_ptr = nullptr;        // [num_graphs][n + 1]
     int64_t* d_col_off_slots = nullptr;  // [num_graphs + 1]
     int32_t* d_col_slot = nullptr;       // [valid slots of all graphs]
+    int32_t* d_col_row = nullptr;        // row of each d_col_slot entry
 };
 
 namespace diffuser {
@@ -233,7 +234,9 @@ struct BackwardArgs {
     const void *Q, *K, *V, *dZ;
     void *dQ, *dK, *dVout;
     int64_t a_count;
-    float *A, *dA, *Zs, *G0, *G1, *dV;
+    // A, dA and At (the weights in column order) are [a_count]; Zs holds
+    // Z_0 .. Z_{K-1}, Gs G_0 .. G_K, each [B][H][n][d].
+    float *A, *dA, *At, *Zs, *Gs, *dV;
 };
 hipError_t launch_backward(const diffuser_graph& g, const BackwardArgs& p, hipStream_t st);
 
