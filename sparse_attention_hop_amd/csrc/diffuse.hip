@@ -8,8 +8,10 @@
 // slots; padding slots are skipped). One wavefront
 // per row. A group of L lanes gathers one neighbour row of Z_k
 // with 16-byte loads (L = d * elem_size / 16), so a wave consumes 64 / L
-// edges per iteration; the groups' partial sums are reduced at the end and
-// the restart term is fused into the store.
+// edges per step, and issues the loads of kUnroll steps before it uses any
+// of them (the step is bound by these dependent index and row loads); the
+// groups' partial sums are reduced at the end and the restart term is fused
+// into the store.
 #include "internal.h"
 #include "vec.h"
 
@@ -18,6 +20,7 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
+constexpr int kUnroll = 4;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
@@ -46,17 +49,27 @@ void k_diffuse_step(GenericGraph gg, int32_t H, const T* __restrict__ A, const T
     float acc[E];
 #pragma unroll
     for (int c = 0; c < E; ++c) acc[c] = 0.0f;
-    for (int64_t base = 0; base < e1; base += EPI) {
-        const int64_t e = base + grp;
-        int32_t j = -1;
-        const int64_t slot = e < e1 ? rs.slot(e, j) : 0;
-        if (j >= 0) {
-            const float a = chunk<T>::load1(Ab + slot);
-            float z[E];
-            chunk<T>::load(Zb + (int64_t)j * D, z);
+    for (int64_t base = 0; base < e1; base += EPI * kUnroll) {
+        // Edges base + u EPI + grp, in order; padding and edges past the row
+        // read row 0 with weight 0.
+        int32_t j[kUnroll];
+        int64_t slot[kUnroll];
 #pragma unroll
-            for (int c = 0; c < E; ++c) acc[c] = fmaf(a, z[c], acc[c]);
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t e = base + u * EPI + grp;
+            j[u] = -1;
+            slot[u] = e < e1 ? rs.slot(e, j[u]) : 0;
         }
+        float a[kUnroll], z[kUnroll][E];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            a[u] = j[u] >= 0 ? chunk<T>::load1(Ab + slot[u]) : 0.0f;
+            chunk<T>::load(Zb + (int64_t)(j[u] >= 0 ? j[u] : 0) * D, z[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < E; ++c) acc[c] = fmaf(a[u], z[u][c], acc[c]);
     }
 #pragma unroll
     for (int off = L; off < kWave; off <<= 1) {

@@ -5,9 +5,11 @@
 // The normalisation runs over exactly the row's neighbour set.
 //
 // Generic path (any slot layout: the row segment, then any scheduled random
-// slots). One wavefront per row; padding slots (column -1) get weight 0. A group of L lanes covers one key row with
-// 16-byte loads (L = d * elem_size / 16), so a wave scores 64 / L edges per
-// iteration. The scale folds log2(e) so the exponentials are exp2.
+// slots). One wavefront per row; padding slots (column -1) get weight 0. A
+// group of L lanes covers one key row with 16-byte loads (L = d * elem_size
+// / 16), so a wave scores 64 / L edges per step, and issues the loads of
+// kUnroll steps before it uses any of them. The scale folds log2(e) so the
+// exponentials are exp2.
 // Pass 1 keeps an online (max, sum) per lane group; pass 2 recomputes the
 // scores and writes A in the storage type.
 #include "internal.h"
@@ -18,6 +20,7 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
+constexpr int kUnroll = 4;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -48,26 +51,46 @@ void k_scores_softmax(GenericGraph gg, int32_t H, const T* __restrict__ Q,
     chunk<T>::load(Q + ((int64_t)bh * n + i) * D + sub * E, q);
     const T* Kb = K + (int64_t)bh * n * D + sub * E;
 
-    float m = -INFINITY, l = 0.0f;
-    for (int64_t base = 0; base < e1; base += EPI) {
-        const int64_t e = base + grp;
-        int32_t j = -1;
-        if (e < e1) rs.slot(e, j);
-        const bool valid = j >= 0;
-        float dot = 0.0f;
-        if (valid) {
-            float k[E];
-            chunk<T>::load(Kb + (int64_t)j * D, k);
+    // Dot products of edges base + u EPI + grp (row 0 for padding and edges
+    // past the row), reduced over the group's lanes.
+    auto dots = [&](int64_t base, int32_t (&j)[kUnroll], int64_t (&slot)[kUnroll],
+                    float (&dot)[kUnroll]) {
 #pragma unroll
-            for (int c = 0; c < E; ++c) dot = fmaf(q[c], k[c], dot);
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t e = base + u * EPI + grp;
+            j[u] = -1;
+            slot[u] = e < e1 ? rs.slot(e, j[u]) : -1;
+        }
+        float k[kUnroll][E];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            chunk<T>::load(Kb + (int64_t)(j[u] >= 0 ? j[u] : 0) * D, k[u]);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            dot[u] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < E; ++c) dot[u] = fmaf(q[c], k[u][c], dot[u]);
         }
 #pragma unroll
-        for (int off = 1; off < L; off <<= 1) dot += __shfl_xor(dot, off);
-        if (valid) {
-            const float t = dot * scale_log2;
-            const float mn = fmaxf(m, t);
-            l = l * fast_exp2(m - mn) + fast_exp2(t - mn);
-            m = mn;
+        for (int off = 1; off < L; off <<= 1)
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) dot[u] += __shfl_xor(dot[u], off);
+    };
+
+    float m = -INFINITY, l = 0.0f;
+    for (int64_t base = 0; base < e1; base += EPI * kUnroll) {
+        int32_t j[kUnroll];
+        int64_t slot[kUnroll];
+        float dot[kUnroll];
+        dots(base, j, slot, dot);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (j[u] >= 0) {
+                const float t = dot[u] * scale_log2;
+                const float mn = fmaxf(m, t);
+                l = l * fast_exp2(m - mn) + fast_exp2(t - mn);
+                m = mn;
+            }
         }
     }
     // Merge the per-group (max, sum) pairs.
@@ -84,24 +107,18 @@ void k_scores_softmax(GenericGraph gg, int32_t H, const T* __restrict__ Q,
     const float inv = 1.0f / l;
 
     float stored_sum = 0.0f;  // sum of the weights as stored (after rounding)
-    for (int64_t base = 0; base < e1; base += EPI) {
-        const int64_t e = base + grp;
-        int32_t j = -1;
-        const int64_t slot = e < e1 ? rs.slot(e, j) : 0;
-        const bool valid = j >= 0;
-        float dot = 0.0f;
-        if (valid) {
-            float k[E];
-            chunk<T>::load(Kb + (int64_t)j * D, k);
+    for (int64_t base = 0; base < e1; base += EPI * kUnroll) {
+        int32_t j[kUnroll];
+        int64_t slot[kUnroll];
+        float dot[kUnroll];
+        dots(base, j, slot, dot);
 #pragma unroll
-            for (int c = 0; c < E; ++c) dot = fmaf(q[c], k[c], dot);
-        }
-#pragma unroll
-        for (int off = 1; off < L; off <<= 1) dot += __shfl_xor(dot, off);
-        if (e < e1 && sub == 0) {
-            const float a = valid ? fast_exp2(dot * scale_log2 - m) * inv : 0.0f;
-            chunk<TA>::store1(Ab + slot, a);
-            stored_sum += chunk<TA>::round(a);
+        for (int u = 0; u < kUnroll; ++u) {
+            if (slot[u] >= 0 && sub == 0) {
+                const float a = j[u] >= 0 ? fast_exp2(dot[u] * scale_log2 - m) * inv : 0.0f;
+                chunk<TA>::store1(Ab + slot[u], a);
+                stored_sum += chunk<TA>::round(a);
+            }
         }
     }
     if (row_scale != nullptr) {
