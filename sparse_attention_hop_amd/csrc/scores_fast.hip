@@ -13,24 +13,22 @@
 //  * window edges: keys are consecutive columns of the band (tiles that lie
 //    inside every row's window skip the masking);
 //  * global columns: the g global rows of K, staged once per workgroup;
-//  * random edges: keys are the 16 slots of half a schedule group; a slot's
-//    score is kept by the lane of its pair's row.
+//  * random edges: per schedule group two products with the query rows as
+//    the first operand (D[row][key]) against the first and the second
+//    slots of the group's 16 pairs; the lane of a pair's row keeps both.
 // A workgroup (16 waves, 16 rows each) streams K of its (batch, head)
 // through LDS in chunks of kChunkRows rows with direct global-to-LDS loads,
 // double-buffered, once per pass. The shift m_i of the exponentials can be
 // any value: exp(s - m) / sum exp(s - m) does not depend on it, and any m_i
 // at most the row maximum keeps every weight at least as large as with the
-// maximum itself (no extra underflow). The kernel takes m_i = the maximum
-// over the row's window and global columns, scored in a prologue from a
-// band window of K staged next to the first chunk; a random score above it
-// only makes a weight exceed one. A row whose stored weights sum to 2^64 or
-// more (a random score far above the window) is redone with the exact
-// maximum from a full pass, so the weights never overflow.
+// maximum itself (no extra underflow). The kernel takes m_i = the row's own
+// score s_ii (the self-loop is an edge of every row); scores above it only
+// make weights exceed one. A row whose stored weights sum to 2^64 or more
+// (a score far above s_ii) is redone with the exact maximum from a full
+// pass, so the weights never overflow.
 //   fused mode: one pass writes w_ij = exp(s_ij - m_i) unnormalised and c_i
 //     = 1 / (sum of the stored w_ij), which the diffusion step applies;
 //   normalised mode: one pass sums w_ij, a second writes w_ij / sum.
-// Without room for the band window (a large radius), m_i is the exact row
-// maximum from a first full pass.
 // exp(s - m) is evaluated as exp2(x * log2(e) / sqrt(d_h) - m'), x the dot
 // product and m' the scaled maximum. Global rows (full rows of length n)
 // get workgroups of their own: 32 rows, the 16 waves split each chunk's
@@ -82,7 +80,6 @@ struct ScoreArgs {
     float* row_scale;           // [B*H][n] (fused mode)
     float scale_log2;           // log2(e) / sqrt(d_h)
     int32_t normalized;
-    int32_t band_prepass;       // the band window of a row tile fits one buffer
     int32_t tiles_per_bh, grow_per_bh, per_xcd, total_items, bh_per_xcd;
 };
 
@@ -127,6 +124,13 @@ __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
                                            __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+}
+
+// acc + a.lo b.lo + a.hi b.hi for two packed bf16 pairs (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
 }
 
 // Per-lane state of a row-tile wave (the lane's row is r0w + l % 16).
@@ -422,12 +426,10 @@ __device__ __forceinline__ void stage_first(const SLane& t, const ScoreArgs& a,
     }
 }
 
-// One pass of a row-tile wave; `prestaged`: chunk 0 and its groups are
-// already in LDS (and the barrier after their loads has passed).
+// One pass of a row-tile wave.
 template <int P>
 __device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uint16_t* Abh,
-                          char LDS_AS* lds, int gpad, bool active, int wave, int lane,
-                          bool prestaged) {
+                          char LDS_AS* lds, int gpad, bool active, int wave, int lane) {
     char LDS_AS* buf0 = lds;
     char LDS_AS* buf1 = lds + kBufBytes;
     char LDS_AS* zg = lds + 2 * kBufBytes;
@@ -435,10 +437,8 @@ __device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uin
     char LDS_AS* stg = zg + gpad * (kRowBytes + 4) + wave * kStageBytes;
 
     random_begin<P>(t);
-    if (!prestaged) {
-        stage_first(t, a, Kbh, lds, stg, active, wave, lane);
-        full_barrier();
-    }
+    stage_first(t, a, Kbh, lds, stg, active, wave, lane);
+    full_barrier();
     if (active) tile_globals<P>(t, a, Abh, zg, gidx, gpad);
     for (int c = 0; c < a.nchunks; ++c) {
         if (c > 0) full_barrier();
@@ -696,50 +696,38 @@ void k_scores_sched(ScoreArgs a) {
     for (int q = threadIdx.x; q < gpad; q += kThreads)
         ((int32_t LDS_AS*)gidx)[q] = q < a.g ? a.G[q] : 0;
 
-    char LDS_AS* stg = zg + gpad * (kRowBytes + 4) + wave * kStageBytes;
-    bool prestaged = false;
-    if (a.band_prepass) {
-        // Shift: the maximum over the window and global columns, from the
-        // band window of the tile's rows staged in buffer 1.
-        const int32_t tile_r0 = (sub - a.grow_per_bh) * kTileRows;
-        const int32_t bw0 = max(tile_r0 - a.radius, 0) & ~15;
-        stage_first(t, a, Kbh, lds, stg, active, wave, lane);
-        dma_chunk(lds + kBufBytes, Kbh, n, bw0, wave, lane);
-        full_barrier();
-        if (active) {
-            for (int32_t kb = t.band_lo; kb <= t.band_hi; kb += 16)
-                band_tile<kPassMax>(t, a, Abh, lds + kBufBytes, kb, bw0);
-            tile_globals<kPassMax>(t, a, Abh, zg, gidx, gpad);
-        }
-        lds_barrier();   // buffer 1 is free again
-        prestaged = true;
-    } else {
-        tile_pass<kPassMax>(t, a, Kbh, Abh, lds, gpad, active, wave, lane, false);
+    // Shift: the row's own score q_i . k_i. The self-loop is an edge of
+    // every row, so this is at most the row maximum (the 4 lanes of a row
+    // hold 16 channels each).
+    {
+        const u32x4 k0 = load16(Kbh + (int64_t)qi * kD + 8 * kg);
+        const u32x4 k1 = load16(Kbh + (int64_t)qi * kD + 32 + 8 * kg);
+        float d = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) d = dot2_bf16(t.q1[u], k1[u], dot2_bf16(t.q0[u], k0[u], d));
+        t.m = row_sum(d);
     }
-    t.m = row_max(t.m);
     t.ms = t.m * a.scale_log2;
     for (int attempt = 0; attempt < 2; ++attempt) {
         if (attempt == 1) {
             // Some row's weights reached 2^64: the exact maxima instead.
             t.m = -INFINITY;
-            tile_pass<kPassMax>(t, a, Kbh, Abh, lds, gpad, active, wave, lane, false);
+            tile_pass<kPassMax>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
             t.m = row_max(t.m);
             t.ms = t.m * a.scale_log2;
             t.sum = 0.0f;
         }
         if (a.normalized) {
-            tile_pass<kPassSum>(t, a, Kbh, Abh, lds, gpad, active, wave, lane, prestaged);
+            tile_pass<kPassSum>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
         } else {
-            tile_pass<kPassWriteFused>(t, a, Kbh, Abh, lds, gpad, active, wave, lane, prestaged);
+            tile_pass<kPassWriteFused>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
         }
-        prestaged = false;
         t.sum = row_sum(t.sum);
-        if (attempt == 1 || !a.band_prepass || !__syncthreads_or(t.rok && !(t.sum < kSumLimit)))
-            break;
+        if (attempt == 1 || !__syncthreads_or(t.rok && !(t.sum < kSumLimit))) break;
     }
     if (a.normalized) {
         t.inv = t.rok ? 1.0f / t.sum : 0.0f;   // rows without edges here write zeros only
-        tile_pass<kPassWriteNorm>(t, a, Kbh, Abh, lds, gpad, active, wave, lane, false);
+        tile_pass<kPassWriteNorm>(t, a, Kbh, Abh, lds, gpad, active, wave, lane);
     } else if (a.row_scale != nullptr && t.rok && kg == 0) {
         a.row_scale[(int64_t)bh * n + t.i] = 1.0f / t.sum;
     }
@@ -781,10 +769,6 @@ hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, cons
     a.row_scale = row_scale;
     a.scale_log2 = scale_log2;
     a.normalized = normalized ? 1 : 0;
-    // The band window of a tile's rows (keys from (r0 - r) rounded down to 16
-    // through r0 + kTileRows - 1 + r) must fit one buffer.
-    const int64_t span = kTileRows - 1 + 2 * (int64_t)a.radius + (a.radius % 16 ? 15 : 0);
-    a.band_prepass = span < kChunkRows ? 1 : 0;
     const int32_t BH = s.B * s.H;
     a.tiles_per_bh = (int32_t)((g.n + kTileRows - 1) / kTileRows);
     a.grow_per_bh = (g.num_global + kGrowRows - 1) / kGrowRows;
