@@ -32,8 +32,8 @@
 // exp(s - m) is evaluated as exp2(x * log2(e) / sqrt(d_h) - m'), x the dot
 // product and m' the scaled maximum. Global rows (full rows of length n)
 // get workgroups of their own: 32 rows, the 16 waves split each chunk's
-// keys and merge their partial maxima and sums in a fixed order; their
-// shift is the maximum over the first chunk's keys. K rows sit
+// keys and merge their partial sums (and, when redone, maxima) in a fixed
+// order; their shift is also the row's own score. K rows sit
 // in LDS at 128 bytes, 16-byte units permuted by score_row_code, which
 // spreads the 16 rows of one operand read over the banks.
 #include "internal.h"
@@ -608,14 +608,19 @@ void k_scores_sched(ScoreArgs a) {
             t.sum[mb] = 0.0f;
             t.inv[mb] = 0.0f;
         }
-        // Shift: the maximum over the keys of chunk 0.
-        dma_chunk(lds, Kbh, a.n, 0, wave, lane);
-        full_barrier();
-        grow_chunk<kPassMax>(t, a, Kbh, Abh, lds + kBufBytes, lds, 0, wave, lane, false);
-        full_barrier();
-        grow_merge<true>(t.m, lds, wave, lane);
+        // Shift: the row's own score (a global row reads its own column).
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) t.ms[mb] = t.m[mb] * a.scale_log2;
+        for (int mb = 0; mb < 2; ++mb) {
+            const int32_t qi = t.i[mb] >= 0 ? t.i[mb] : 0;
+            const u32x4 k0 = load16(Kbh + (int64_t)qi * kD + 8 * kg);
+            const u32x4 k1 = load16(Kbh + (int64_t)qi * kD + 32 + 8 * kg);
+            float d = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                d = dot2_bf16(t.q1[mb][u], k1[u], dot2_bf16(t.q0[mb][u], k0[u], d));
+            t.m[mb] = row_sum(d);
+            t.ms[mb] = t.m[mb] * a.scale_log2;
+        }
         for (int attempt = 0; attempt < 2; ++attempt) {
             if (attempt == 1) {
                 // Some row's weights reached 2^64: the exact maxima instead.
