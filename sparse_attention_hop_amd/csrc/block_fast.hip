@@ -7,10 +7,13 @@
 //    (v_mfma_f32_16x16x32_bf16, two per tile for the 64 channels); the K
 //    operand is 8 channels of one key row, read from LDS with
 //    ds_read_b128, the Q^T operand 8 channels of the lane's row, held in
-//    registers. A first pass takes each row's exact maximum m_i over its
-//    key blocks; the next writes exp(s - m_i) (fused: unnormalised, with
-//    c_i = 1 / (sum of the stored weights); normalised: a third pass
-//    writes the weights over their sum).
+//    registers. The shift m_i is the row's own score (the diagonal block is
+//    among its key blocks, so m_i is at most the row maximum; a row whose
+//    weights reach 2^64 is redone with the exact maximum). One pass writes
+//    exp(s - m_i) (fused: unnormalised, with c_i = 1 / (sum of the stored
+//    weights); normalised: a sum pass, then a pass that writes the weights
+//    over their sum). The parts of a split global query block take the
+//    exact maximum from a pass of their own.
 //  * one diffusion step (section 2.4, eq. S.7, as the scheduled kernel):
 //      D[channel][row] += Z^T[channel][key] W^T[key][row]
 //    over 32-key steps: the Z^T operand from LDS with ds_read_b64_tr_b16,
@@ -37,6 +40,9 @@ constexpr int kRowBytes = kD * 2;
 constexpr int kBufBytes = kBlk * kRowBytes;   // one key block of K or Z_k
 static_assert(kWaves * 16 == kBlk, "a wave per 16 rows of the query block");
 constexpr int kSplit = 8;                     // key blocks per part of a global query block
+// A row whose weights (shifted by less than its maximum) sum to this or
+// more is redone with its exact maximum, far from the overflow threshold.
+constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
 
 struct BlockArgs {
     int64_t n;
@@ -180,6 +186,13 @@ __device__ __forceinline__ void score_pass(const BlockArgs& a, const BlockRows& 
     __syncthreads();   // every wave is done with the buffers
 }
 
+// acc + a.lo b.lo + a.hi b.hi for two packed bf16 pairs (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
 __device__ __forceinline__ float quad_max(float x) {
     x = fmaxf(x, __shfl_xor(x, 16));
     return fmaxf(x, __shfl_xor(x, 32));
@@ -255,19 +268,40 @@ void k_block_scores(BlockArgs a) {
         if (kg == 0) ps[16 * wave + s16] = sum;
         return;
     }
-    score_pass<kBMax>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, 0.0f, sum, 0.0f);
-    m = quad_max(m);
-    const float ms = m * a.scale_log2;
-    if (a.normalized) {
-        score_pass<kBSum>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum, 0.0f);
+    // Shift: the row's own score (the diagonal block is among its key
+    // blocks), at most the row maximum; rows whose weights reach 2^64 are
+    // redone with the exact maximum.
+    {
+        const u32x4 k0 = load16(Kbh + row * kD + 8 * kg);
+        const u32x4 k1 = load16(Kbh + row * kD + 32 + 8 * kg);
+        float d = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) d = dot2_bf16(q1[u], k1[u], dot2_bf16(q0[u], k0[u], d));
+        m = quad_sum(d);
+    }
+    float ms = m * a.scale_log2;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        if (attempt == 1) {
+            m = -INFINITY;
+            score_pass<kBMax>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, 0.0f, sum,
+                              0.0f);
+            m = quad_max(m);
+            ms = m * a.scale_log2;
+        }
+        sum = 0.0f;
+        if (a.normalized)
+            score_pass<kBSum>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum, 0.0f);
+        else
+            score_pass<kBWrite>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum,
+                                0.0f);
         sum = quad_sum(sum);
+        if (attempt == 1 || !__syncthreads_or(!(sum < kSumLimit))) break;
+    }
+    if (a.normalized)
         score_pass<kBWriteNorm>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum,
                                 1.0f / sum);
-    } else {
-        score_pass<kBWrite>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum, 0.0f);
-        sum = quad_sum(sum);
-        if (a.row_scale != nullptr && kg == 0) a.row_scale[(int64_t)it.bh * n + row] = 1.0f / sum;
-    }
+    else if (a.row_scale != nullptr && kg == 0)
+        a.row_scale[(int64_t)it.bh * n + row] = 1.0f / sum;
 }
 
 // c_i of the global query blocks' rows from their parts' sums (in part
