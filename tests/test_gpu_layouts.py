@@ -176,6 +176,34 @@ def test_block_attn_full_size(orc):
         pu.assert_z_close(z[bb, h], ref, "bf16", f"b={bb} h={h}")
 
 
+@pytest.mark.parametrize("n", [512, 1024])
+def test_block_far_maximum(orc, n):
+    """Rows with a key scoring far above their own score: their shifted
+    weights would pass 2^64, so the block-tile score kernel redoes them with
+    the exact maximum (head 0); head 1 has ordinary inputs. At n = 1024 the
+    global query block is split into parts."""
+    b, c, s, gb = 64, 3, 2, 1
+    g = sah.build_block_graph(n, b, c, s, gb, 1, 29)
+    rp, cols = g.copy_csr(0)
+    q, k, v = _qkv((1, 2, n, 64), 71, torch.bfloat16)
+    far_key = n - 100
+    q[0, 0] = 0
+    q[0, 0, :, 0] = 16.0
+    k[0, 0] = 0
+    k[0, 0, far_key, 0] = 32.0        # score 64 for one key, 0 for every other one
+    rows = np.repeat(np.arange(n), np.diff(rp))[cols == far_key]
+    assert any(abs(int(i) - far_key) >= 2 * b for i in rows), "a non-local row must read it"
+    A = _as64(sah.scores_softmax(q.to(DEV), k.to(DEV), g))
+    z = _as64(sah.attn(q.to(DEV), k.to(DEV), v.to(DEV), g, 5, 0.1))
+    for h in range(2):
+        off = g.a_offset(0, h, 2)
+        got = A[off:off + g.slots[0]]
+        ref = orc.scores_softmax(_as64(q[0, h]), _as64(k[0, h]), rp, cols)
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * ref + 1e-6), h
+        zref = orc.attn(_as64(q[0, h]), _as64(k[0, h]), _as64(v[0, h]), rp, cols, 5, 0.1)
+        pu.assert_z_close(z[0, h], zref, "bf16", f"h={h}")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_dilated_attn(orc, dt):
     n, r, dl, G, B, H, d = 300, 3, 4, [0, 150], 2, 2, 32
