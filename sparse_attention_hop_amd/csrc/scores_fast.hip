@@ -344,10 +344,17 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
     // kept apart so that no register is loaded from both places, which would
     // make every LDS read wait for all outstanding memory operations (the
     // next chunk's loads and the weight stores among them).
+    // A group's codes and row byte are read one group ahead.
     const int32_t nstaged = min(gcnt, kStageGroups);
+    uint32_t codes_n = *reinterpret_cast<const uint32_t LDS_AS*>(stg + 4 * t.s16);
+    uint32_t rb_n = *reinterpret_cast<const uint8_t LDS_AS*>(stg + 64 + t.s16);
     for (int32_t k = 0; k < nstaged; ++k) {
-        const char LDS_AS* o = stg + k * kSGroupBytes;
-        const uint32_t codes = *reinterpret_cast<const uint32_t LDS_AS*>(o + 4 * t.s16);
+        const uint32_t codes = codes_n, rb = rb_n;
+        if (k + 1 < nstaged) {
+            const char LDS_AS* o = stg + (k + 1) * kSGroupBytes;
+            codes_n = *reinterpret_cast<const uint32_t LDS_AS*>(o + 4 * t.s16);
+            rb_n = *reinterpret_cast<const uint8_t LDS_AS*>(o + 64 + t.s16);
+        }
         f32x4 x[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -356,7 +363,6 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
             k_operands(cur, code, (uint32_t)t.kg, k0, k1);
             x[h] = dots(t.q0, t.q1, k0, k1);
         }
-        const uint32_t rb = *reinterpret_cast<const uint8_t LDS_AS*>(o + 64 + t.s16);
         random_group<P>(t, x[0], x[1], rb, a.scale_log2,
                         Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 2 * t.s16);
     }
