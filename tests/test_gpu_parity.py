@@ -403,6 +403,29 @@ def test_fast_diffusion_shapes(orc, case, K, alpha):
             pu.assert_z_close(zs_h[b, h], ref_s, "bf16", f"diffuse b={b} h={h}", K, alpha)
 
 
+@pytest.mark.parametrize("n", [1 << 16, (1 << 16) + 1])
+def test_longest_scheduled_sequence(orc, n):
+    """The longest sequence that gets the random schedule (2^16 tokens, the
+    LDS-streamed kernels) and one token more (row-segment random slots, the
+    generic kernels): graph bit-exact, weights and Z against the oracle."""
+    r, G, R = 32, [0, n // 2, n - 1], 16
+    print(f"\n[parity] n={n} r={r} g={len(G)} R={R}", flush=True)
+    g = _gpu_graph(n, r, G, R, 1, False, 57)
+    rp, cols = _check_csr(orc, g, n, r, G, R, 1, False, 57)
+    shape = (1, 1, n, 64)
+    q = make_tensor(shape, 81, torch.bfloat16)
+    k = make_tensor(shape, 82, torch.bfloat16)
+    v = make_tensor(shape, 83, torch.bfloat16)
+    z = _as64(sah.attn(q.to(DEV), k.to(DEV), v.to(DEV), g, 3, 0.1))
+    A = _as64(sah.scores_softmax(q.to(DEV), k.to(DEV), g))
+    A_csr = _a_csr(g, A, 0, 0, 1, 0, rp, cols)
+    A_ref = orc.scores_softmax(_as64(q[0, 0]), _as64(k[0, 0]), rp[0], cols[0])
+    assert np.all(np.abs(A_csr - A_ref) <= 2.0 ** -8 * A_ref + 1e-6)
+    ref = orc.attn(_as64(q[0, 0]), _as64(k[0, 0]), _as64(v[0, 0]), rp[0], cols[0], 3, 0.1,
+                   pu.oracle_threads())
+    pu.assert_z_close(z[0, 0], ref, "bf16", f"n={n}", 3, 0.1)
+
+
 @pytest.mark.parametrize("case", [FAST_CASES[1], FAST_CASES[6]],
                          ids=lambda c: f"n{c[0]}r{c[1]}g{len(c[2])}R{c[3]}c{int(c[5])}")
 def test_fast_paths_deterministic(case):
