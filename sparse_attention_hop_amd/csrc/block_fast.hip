@@ -441,11 +441,15 @@ void k_block_combine(BlockArgs a) {
     a.out[o] = (uint16_t)f32_to_bf16(keep * sum + a.restart * bf16_to_f32(a.V[o]));
 }
 
-// Global query blocks read every block: more than kSplit key blocks are
-// split into parts.
-int32_t global_parts(const diffuser_graph& g) {
-    return g.global_blocks > 0 && g.nblocks > kSplit ? (int32_t)((g.nblocks + kSplit - 1) / kSplit)
-                                                    : 0;
+// Global query blocks read every block: with more than kSplit key blocks
+// they are split into parts of kSplit, unless the item and thread counts
+// of the launches would then pass the int32 range (they run whole).
+int32_t global_parts(const diffuser_graph& g, const attn_shape& s) {
+    if (g.global_blocks == 0 || g.nblocks <= kSplit) return 0;
+    const int64_t parts = (g.nblocks + kSplit - 1) / kSplit;
+    const int64_t items = (int64_t)s.B * s.H * (g.global_blocks * parts + g.nblocks);
+    if (items * kCombineGroups >= (1ll << 31)) return 0;
+    return (int32_t)parts;
 }
 
 BlockArgs block_args(const diffuser_graph& g, const attn_shape& s) {
@@ -463,7 +467,7 @@ BlockArgs block_args(const diffuser_graph& g, const attn_shape& s) {
 }  // namespace
 
 size_t block_part_bytes(const diffuser_graph& g, const attn_shape& s) {
-    return (size_t)s.B * s.H * g.global_blocks * global_parts(g) * kBlk * kD * sizeof(float);
+    return (size_t)s.B * s.H * g.global_blocks * global_parts(g, s) * kBlk * kD * sizeof(float);
 }
 
 bool fast_block_supported(const diffuser_graph& g, const attn_shape& s) {
@@ -487,7 +491,7 @@ hipError_t launch_block_scores(const diffuser_graph& g, const attn_shape& s, con
     // The fused mode splits the global query blocks (as the diffusion step);
     // the normalised one keeps them whole.
     const bool split = !normalized && row_scale != nullptr && part != nullptr;
-    a.gparts = split ? global_parts(g) : 0;
+    a.gparts = split ? global_parts(g, s) : 0;
     a.gblocks = a.gparts > 0 ? g.global_blocks : 0;
     a.part = part;
     a.total_parts = s.B * s.H * a.gblocks * a.gparts;
@@ -506,7 +510,7 @@ hipError_t launch_block_diffuse(const diffuser_graph& g, const attn_shape& s, co
                                 const void* Zk, const void* V, void* Zn, const float* row_scale,
                                 step_coefs k, float* part, hipStream_t st) {
     BlockArgs a = block_args(g, s);
-    a.gparts = global_parts(g);
+    a.gparts = global_parts(g, s);
     a.gblocks = a.gparts > 0 ? g.global_blocks : 0;
     a.part = part;
     a.total = s.B * s.H * (a.gblocks * a.gparts + (a.nblocks - a.gblocks));
