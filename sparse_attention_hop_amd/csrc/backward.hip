@@ -32,6 +32,21 @@ constexpr int kThreads = kWave * kWavesPerBlock;
 // them: the products are bound by the latency of those dependent loads.
 constexpr int kUnroll = 4;
 
+// Row (or column) i and pair bh of a wave. The 1-D grid holds 8 per_xcd
+// workgroups; XCD blk % 8 takes items [x per_xcd, (x + 1) per_xcd) of the
+// (bh, block of kWavesPerBlock rows) order, so each XCD's L2 serves the
+// rows of few (b, h) pairs. False past the last item or row.
+__device__ __forceinline__ bool row_item(int64_t n, int32_t BH, int wave, int64_t& i,
+                                         int32_t& bh) {
+    const int64_t per_xcd = gridDim.x >> 3;
+    const int64_t item = (int64_t)(blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+    const int64_t nrb = (n + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (item >= (int64_t)BH * nrb) return false;
+    bh = (int32_t)(item / nrb);
+    i = (item - (int64_t)bh * nrb) * kWavesPerBlock + wave;
+    return i < n;
+}
+
 __device__ __forceinline__ float ld(const float* p) { return *p; }
 __device__ __forceinline__ float ld(const bf16_t* p) { return bf16_to_f32(p->bits); }
 __device__ __forceinline__ void st(float* p, float v) { *p = v; }
@@ -50,14 +65,16 @@ __device__ __forceinline__ void ld4(const TX* p, float (&x)[4]) {
 // added in a fixed order at the end.
 template <typename TX, typename TU, typename TY, int D>
 __global__ __launch_bounds__(kThreads)
-void k_rows(GenericGraph gg, int32_t H, const float* __restrict__ W, const TX* __restrict__ X,
-            const TU* __restrict__ U, TY* __restrict__ Y, float a, float b) {
+void k_rows(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict__ W,
+            const TX* __restrict__ X, const TU* __restrict__ U, TY* __restrict__ Y, float a,
+            float b) {
     constexpr int L = D / 4, EPI = kWave / L;
     const int wave = threadIdx.x / kWave, lane = __lane_id();
     const int64_t n = gg.n;
-    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    if (i >= n) return;
-    const int32_t bh = blockIdx.y, bb = bh / H, hh = bh - bb * H;
+    int64_t i;
+    int32_t bh;
+    if (!row_item(n, BH, wave, i, bh)) return;
+    const int32_t bb = bh / H, hh = bh - bb * H;
     const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
     const RowSlots rs = gg.row(gr, i);
     const float* Wb = W + a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
@@ -134,14 +151,15 @@ void k_to_columns(ColIndex ci, int32_t H, const float* __restrict__ W, float* __
 // (k_to_columns).
 template <typename TX, typename TY, int D>
 __global__ __launch_bounds__(kThreads)
-void k_cols(ColIndex ci, int32_t H, const float* __restrict__ Wt, const TX* __restrict__ X,
-            TY* __restrict__ Y, float a) {
+void k_cols(ColIndex ci, int32_t H, int32_t BH, const float* __restrict__ Wt,
+            const TX* __restrict__ X, TY* __restrict__ Y, float a) {
     constexpr int L = D / 4, EPI = kWave / L;
     const int wave = threadIdx.x / kWave, lane = __lane_id();
     const int64_t n = ci.n;
-    const int64_t j = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    if (j >= n) return;
-    const int32_t bh = blockIdx.y, bb = bh / H, hh = bh - bb * H;
+    int64_t j;
+    int32_t bh;
+    if (!row_item(n, BH, wave, j, bh)) return;
+    const int32_t bb = bh / H, hh = bh - bb * H;
     const int32_t gr = ci.num_graphs == 1 ? 0 : bb;
     const int64_t* cp = ci.col_ptr + (int64_t)gr * (n + 1);
     const int32_t* crow = ci.col_row + ci.col_off[gr];
@@ -185,15 +203,16 @@ void k_cols(ColIndex ci, int32_t H, const float* __restrict__ Wt, const TX* __re
 // lanes of 4 channels); state k of G or Z starts at k * stride.
 template <int D>
 __global__ __launch_bounds__(kThreads)
-void k_edge_dots(GenericGraph gg, int32_t H, const float* __restrict__ Gs,
+void k_edge_dots(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict__ Gs,
                  const float* __restrict__ Zs, int64_t stride, int32_t K, float* __restrict__ dA,
                  float a) {
     constexpr int L = D / 4, EPI = kWave / L;
     const int wave = threadIdx.x / kWave, lane = __lane_id();
     const int64_t n = gg.n;
-    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    if (i >= n) return;
-    const int32_t bh = blockIdx.y, bb = bh / H, hh = bh - bb * H;
+    int64_t i;
+    int32_t bh;
+    if (!row_item(n, BH, wave, i, bh)) return;
+    const int32_t bb = bh / H, hh = bh - bb * H;
     const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
     const RowSlots rs = gg.row(gr, i);
     float* dAb = dA + a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
@@ -233,13 +252,14 @@ void k_edge_dots(GenericGraph gg, int32_t H, const float* __restrict__ Gs,
 
 // dS = A (dA - sum_row A dA) * scale, in place of dA; one wave per row.
 __global__ __launch_bounds__(kThreads)
-void k_softmax_grad(GenericGraph gg, int32_t H, const float* __restrict__ A,
+void k_softmax_grad(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict__ A,
                     float* __restrict__ dA, float scale) {
     const int wave = threadIdx.x / kWave, lane = __lane_id();
     const int64_t n = gg.n;
-    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    if (i >= n) return;
-    const int32_t bh = blockIdx.y, bb = bh / H, hh = bh - bb * H;
+    int64_t i;
+    int32_t bh;
+    if (!row_item(n, BH, wave, i, bh)) return;
+    const int32_t bb = bh / H, hh = bh - bb * H;
     const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
     const RowSlots rs = gg.row(gr, i);
     const int64_t off = a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
@@ -298,7 +318,8 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     ci.col_row = g.d_col_row;
     ci.slot_off = g.d_slot_off;
     const int32_t BH = p.B * p.H;
-    const dim3 rows((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)BH);
+    const int64_t items = (int64_t)BH * ((g.n + kWavesPerBlock - 1) / kWavesPerBlock);
+    const dim3 rows((unsigned)(8 * ((items + 7) / 8)));
     const dim3 blk(kThreads);
     const int64_t cnt = (int64_t)BH * g.n * D;
     int64_t max_entries = 0;
@@ -314,7 +335,7 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
         hipLaunchKernelGGL((k_axpby<T>), grid_elems(cnt), blk, 0, stream, cnt, V, p.Zs, 1.0f,
                            0.0f);
     for (int32_t k = 1; k < K; ++k)
-        hipLaunchKernelGGL((k_rows<float, T, float, D>), rows, blk, 0, stream, gg, p.H, p.A,
+        hipLaunchKernelGGL((k_rows<float, T, float, D>), rows, blk, 0, stream, gg, p.H, BH, p.A,
                            p.Zs + (size_t)(k - 1) * cnt, V, p.Zs + (size_t)k * cnt, keep,
                            p.alpha);
     // G_K = dZ, G_k = (1 - alpha) A^T G_{k+1}; dV = alpha (G_K + .. + G_1).
@@ -325,11 +346,11 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
         const float* Gk1 = p.Gs + (size_t)(k + 1) * cnt;
         hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, Gk1, p.dV,
                            p.alpha, k == K - 1 ? 0.0f : 1.0f);
-        hipLaunchKernelGGL((k_cols<float, float, D>), rows, blk, 0, stream, ci, p.H, p.At, Gk1,
+        hipLaunchKernelGGL((k_cols<float, float, D>), rows, blk, 0, stream, ci, p.H, BH, p.At, Gk1,
                            p.Gs + (size_t)k * cnt, keep);
     }
     // dA = (1 - alpha) sum_k G_{k+1} Z_k^T on the edges.
-    hipLaunchKernelGGL((k_edge_dots<D>), rows, blk, 0, stream, gg, p.H, p.Gs, p.Zs, cnt, K,
+    hipLaunchKernelGGL((k_edge_dots<D>), rows, blk, 0, stream, gg, p.H, BH, p.Gs, p.Zs, cnt, K,
                        p.dA, keep);
     // dV = (sum of alpha G_{k+1}) + G_0.
     if (K == 0)
@@ -338,12 +359,12 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     hipLaunchKernelGGL((k_sum_to<T>), grid_elems(cnt), blk, 0, stream, cnt, p.dV, p.Gs,
                        static_cast<T*>(p.dVout));
     // dS, then dQ = dS K and dK = dS^T Q (the 1 / sqrt(d_h) inside dS).
-    hipLaunchKernelGGL(k_softmax_grad, rows, blk, 0, stream, gg, p.H, p.A, p.dA, p.scale);
-    hipLaunchKernelGGL((k_rows<T, T, T, D>), rows, blk, 0, stream, gg, p.H, p.dA,
+    hipLaunchKernelGGL(k_softmax_grad, rows, blk, 0, stream, gg, p.H, BH, p.A, p.dA, p.scale);
+    hipLaunchKernelGGL((k_rows<T, T, T, D>), rows, blk, 0, stream, gg, p.H, BH, p.dA,
                        static_cast<const T*>(p.K), static_cast<const T*>(nullptr),
                        static_cast<T*>(p.dQ), 1.0f, 0.0f);
     hipLaunchKernelGGL(k_to_columns, entries, blk, 0, stream, ci, p.H, p.dA, p.At);
-    hipLaunchKernelGGL((k_cols<T, T, D>), rows, blk, 0, stream, ci, p.H, p.At,
+    hipLaunchKernelGGL((k_cols<T, T, D>), rows, blk, 0, stream, ci, p.H, BH, p.At,
                        static_cast<const T*>(p.Q), static_cast<T*>(p.dK), 1.0f);
     return hipGetLastError();
 }
