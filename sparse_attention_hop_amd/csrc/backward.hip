@@ -32,20 +32,6 @@ constexpr int kThreads = kWave * kWavesPerBlock;
 // them: the products are bound by the latency of those dependent loads.
 constexpr int kUnroll = 4;
 
-// Row (or column) i and pair bh of a wave. The 1-D grid holds 8 per_xcd
-// workgroups; XCD blk % 8 takes items [x per_xcd, (x + 1) per_xcd) of the
-// (bh, block of kWavesPerBlock rows) order, so each XCD's L2 serves the
-// rows of few (b, h) pairs. False past the last item or row.
-__device__ __forceinline__ bool row_item(int64_t n, int32_t BH, int wave, int64_t& i,
-                                         int32_t& bh) {
-    const int64_t per_xcd = gridDim.x >> 3;
-    const int64_t item = (int64_t)(blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
-    const int64_t nrb = (n + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (item >= (int64_t)BH * nrb) return false;
-    bh = (int32_t)(item / nrb);
-    i = (item - (int64_t)bh * nrb) * kWavesPerBlock + wave;
-    return i < n;
-}
 
 __device__ __forceinline__ float ld(const float* p) { return *p; }
 __device__ __forceinline__ float ld(const bf16_t* p) { return bf16_to_f32(p->bits); }
@@ -73,7 +59,7 @@ void k_rows(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict__ W,
     const int64_t n = gg.n;
     int64_t i;
     int32_t bh;
-    if (!row_item(n, BH, wave, i, bh)) return;
+    if (!xcd_row_item<kWavesPerBlock>(n, BH, wave, i, bh)) return;
     const int32_t bb = bh / H, hh = bh - bb * H;
     const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
     const RowSlots rs = gg.row(gr, i);
@@ -158,7 +144,7 @@ void k_cols(ColIndex ci, int32_t H, int32_t BH, const float* __restrict__ Wt,
     const int64_t n = ci.n;
     int64_t j;
     int32_t bh;
-    if (!row_item(n, BH, wave, j, bh)) return;
+    if (!xcd_row_item<kWavesPerBlock>(n, BH, wave, j, bh)) return;
     const int32_t bb = bh / H, hh = bh - bb * H;
     const int32_t gr = ci.num_graphs == 1 ? 0 : bb;
     const int64_t* cp = ci.col_ptr + (int64_t)gr * (n + 1);
@@ -211,7 +197,7 @@ void k_edge_dots(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict
     const int64_t n = gg.n;
     int64_t i;
     int32_t bh;
-    if (!row_item(n, BH, wave, i, bh)) return;
+    if (!xcd_row_item<kWavesPerBlock>(n, BH, wave, i, bh)) return;
     const int32_t bb = bh / H, hh = bh - bb * H;
     const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
     const RowSlots rs = gg.row(gr, i);
@@ -258,7 +244,7 @@ void k_softmax_grad(GenericGraph gg, int32_t H, int32_t BH, const float* __restr
     const int64_t n = gg.n;
     int64_t i;
     int32_t bh;
-    if (!row_item(n, BH, wave, i, bh)) return;
+    if (!xcd_row_item<kWavesPerBlock>(n, BH, wave, i, bh)) return;
     const int32_t bb = bh / H, hh = bh - bb * H;
     const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
     const RowSlots rs = gg.row(gr, i);
@@ -318,8 +304,7 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     ci.col_row = g.d_col_row;
     ci.slot_off = g.d_slot_off;
     const int32_t BH = p.B * p.H;
-    const int64_t items = (int64_t)BH * ((g.n + kWavesPerBlock - 1) / kWavesPerBlock);
-    const dim3 rows((unsigned)(8 * ((items + 7) / 8)));
+    const dim3 rows = xcd_row_grid(g.n, BH, kWavesPerBlock);
     const dim3 blk(kThreads);
     const int64_t cnt = (int64_t)BH * g.n * D;
     int64_t max_entries = 0;

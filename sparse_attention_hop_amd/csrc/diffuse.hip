@@ -24,7 +24,8 @@ constexpr int kUnroll = 4;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
-void k_diffuse_step(GenericGraph gg, int32_t H, const T* __restrict__ A, const T* __restrict__ Zk,
+void k_diffuse_step(GenericGraph gg, int32_t H, int32_t BH, const T* __restrict__ A,
+                    const T* __restrict__ Zk,
                     const T* __restrict__ V, T* __restrict__ Zn,
                     const float* __restrict__ row_scale, step_coefs kc) {
     constexpr int E = chunk<T>::kElems;
@@ -35,9 +36,9 @@ void k_diffuse_step(GenericGraph gg, int32_t H, const T* __restrict__ A, const T
     const int wave = threadIdx.x / kWave;
     const int lane = __lane_id();
     const int64_t n = gg.n;
-    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    if (i >= n) return;
-    const int32_t bh = blockIdx.y;
+    int64_t i;
+    int32_t bh;
+    if (!xcd_row_item<kWavesPerBlock>(n, BH, wave, i, bh)) return;
     const int32_t b = bh / H, h = bh - b * H;
     const int32_t gr = gg.num_graphs == 1 ? 0 : b;
     const RowSlots rs = gg.row(gr, i);
@@ -92,9 +93,9 @@ template <typename T, int D>
 hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
                     const void* V, void* Zn, const float* row_scale, step_coefs kc,
                     hipStream_t st) {
-    dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
+    const dim3 grid = xcd_row_grid(g.n, s.B * s.H, kWavesPerBlock);
     hipLaunchKernelGGL((k_diffuse_step<T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
-                       generic_graph(g), s.H, static_cast<const T*>(A),
+                       generic_graph(g), s.H, s.B * s.H, static_cast<const T*>(A),
                        static_cast<const T*>(Zk), static_cast<const T*>(V),
                        static_cast<T*>(Zn), row_scale, kc);
     return hipGetLastError();

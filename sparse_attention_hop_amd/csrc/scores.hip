@@ -26,7 +26,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 template <typename T, typename TA, int D>
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
-void k_scores_softmax(GenericGraph gg, int32_t H, const T* __restrict__ Q,
+void k_scores_softmax(GenericGraph gg, int32_t H, int32_t BH, const T* __restrict__ Q,
                       const T* __restrict__ K, TA* __restrict__ A, float* __restrict__ row_scale,
                       float scale_log2) {
     constexpr int E = chunk<T>::kElems;
@@ -37,9 +37,9 @@ void k_scores_softmax(GenericGraph gg, int32_t H, const T* __restrict__ Q,
     const int wave = threadIdx.x / kWave;
     const int lane = __lane_id();
     const int64_t n = gg.n;
-    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    if (i >= n) return;
-    const int32_t bh = blockIdx.y;
+    int64_t i;
+    int32_t bh;
+    if (!xcd_row_item<kWavesPerBlock>(n, BH, wave, i, bh)) return;
     const int32_t b = bh / H, h = bh - b * H;
     const int32_t gr = gg.num_graphs == 1 ? 0 : b;
     const RowSlots rs = gg.row(gr, i);
@@ -153,9 +153,9 @@ void k_zero_dummies(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __r
 template <typename T, int D>
 hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
                     void* A, float* row_scale, float scale_log2, hipStream_t st) {
-    dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
+    const dim3 grid = xcd_row_grid(g.n, s.B * s.H, kWavesPerBlock);
     hipLaunchKernelGGL((k_scores_softmax<T, T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
-                       generic_graph(g), s.H, static_cast<const T*>(Q),
+                       generic_graph(g), s.H, s.B * s.H, static_cast<const T*>(Q),
                        static_cast<const T*>(K), static_cast<T*>(A), row_scale, scale_log2);
     if (g.scheduled)
         hipLaunchKernelGGL((k_zero_dummies<T>), dim3(64, (unsigned)(s.B * s.H)), dim3(256), 0, st,
@@ -179,9 +179,9 @@ hipError_t launch_d(const diffuser_graph& g, const attn_shape& s, const void* Q,
 template <typename T, int D>
 hipError_t launch_f32_t(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
                         float* A, float scale_log2, hipStream_t st) {
-    dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(s.B * s.H));
+    const dim3 grid = xcd_row_grid(g.n, s.B * s.H, kWavesPerBlock);
     hipLaunchKernelGGL((k_scores_softmax<T, float, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
-                       generic_graph(g), s.H, static_cast<const T*>(Q),
+                       generic_graph(g), s.H, s.B * s.H, static_cast<const T*>(Q),
                        static_cast<const T*>(K), A, nullptr, scale_log2);
     return hipGetLastError();
 }

@@ -100,6 +100,28 @@ struct RowSlots {
     }
 };
 
+// Row i and pair bh of wave `wave` in a 1-D grid of 8 per_xcd workgroups
+// of kW waves (xcd_row_grid): XCD blk % 8 takes items [x per_xcd,
+// (x + 1) per_xcd) of the (bh, block of kW rows) order, so each XCD's L2
+// serves the rows of few (b, h) pairs. False past the last item or row.
+template <int kW>
+__device__ __forceinline__ bool xcd_row_item(int64_t n, int32_t BH, int wave, int64_t& i,
+                                             int32_t& bh) {
+    const int64_t per_xcd = gridDim.x >> 3;
+    const int64_t item = (int64_t)(blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+    const int64_t nrb = (n + kW - 1) / kW;
+    if (item >= (int64_t)BH * nrb) return false;
+    bh = (int32_t)(item / nrb);
+    i = (item - (int64_t)bh * nrb) * kW + wave;
+    return i < n;
+}
+
+// Workgroups of that grid.
+inline dim3 xcd_row_grid(int64_t n, int32_t BH, int kW) {
+    const int64_t items = (int64_t)BH * ((n + kW - 1) / kW);
+    return dim3((unsigned)(8 * ((items + 7) / 8)));
+}
+
 // Graph arrays the generic kernels read.
 struct GenericGraph {
     int64_t n;
