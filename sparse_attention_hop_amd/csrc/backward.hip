@@ -120,16 +120,21 @@ struct ColIndex {
 
 // Wt[e] = W[col_slot[e]] for every column-index entry e of each (b, h)
 // (both at the (b, h) block's slot offset): the weights in column order.
+// Workgroup items are (b, h, block of kThreads entries) on an XCD-aware grid
+// over `blocks` entry blocks per (b, h).
 __global__ __launch_bounds__(kThreads)
-void k_to_columns(ColIndex ci, int32_t H, const float* __restrict__ W, float* __restrict__ Wt) {
-    const int32_t bh = blockIdx.y, bb = bh / H, hh = bh - bb * H;
+void k_to_columns(ColIndex ci, int32_t H, int32_t BH, int64_t blocks, const float* __restrict__ W,
+                  float* __restrict__ Wt) {
+    int64_t eb;
+    int32_t bh;
+    if (!xcd_row_item<1>(blocks, BH, 0, eb, bh)) return;
+    const int32_t bb = bh / H, hh = bh - bb * H;
     const int32_t gr = ci.num_graphs == 1 ? 0 : bb;
-    const int32_t* cs = ci.col_slot + ci.col_off[gr];
     const int64_t count = ci.col_off[gr + 1] - ci.col_off[gr];
+    const int64_t e = eb * kThreads + threadIdx.x;
+    if (e >= count) return;
     const int64_t off = a_block_offset(ci.slot_off, ci.num_graphs, H, bb, hh);
-    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < count;
-         e += (int64_t)gridDim.x * kThreads)
-        Wt[off + e] = W[off + cs[e]];
+    Wt[off + e] = W[off + ci.col_slot[ci.col_off[gr] + e]];
 }
 
 // Y[j] = a * sum_{entries e of column j} Wt[e] X[col_row[e]], one wave per
@@ -310,7 +315,8 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     int64_t max_entries = 0;
     for (int32_t gr = 0; gr < g.num_graphs; ++gr)
         max_entries = std::max(max_entries, g.slots[gr]);
-    const dim3 entries(grid_elems(max_entries).x, (unsigned)BH);
+    const int64_t entry_blocks = (max_entries + kThreads - 1) / kThreads;
+    const dim3 entries = xcd_row_grid(entry_blocks, BH, 1);
     const T* V = static_cast<const T*>(p.V);
     const float keep = 1.0f - p.alpha;
     const int32_t K = p.K_steps;
@@ -326,7 +332,9 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     // G_K = dZ, G_k = (1 - alpha) A^T G_{k+1}; dV = alpha (G_K + .. + G_1).
     hipLaunchKernelGGL((k_axpby<T>), grid_elems(cnt), blk, 0, stream, cnt,
                        static_cast<const T*>(p.dZ), p.Gs + (size_t)K * cnt, 1.0f, 0.0f);
-    if (K > 0) hipLaunchKernelGGL(k_to_columns, entries, blk, 0, stream, ci, p.H, p.A, p.At);
+    if (K > 0)
+        hipLaunchKernelGGL(k_to_columns, entries, blk, 0, stream, ci, p.H, BH, entry_blocks, p.A,
+                           p.At);
     for (int32_t k = K - 1; k >= 0; --k) {
         const float* Gk1 = p.Gs + (size_t)(k + 1) * cnt;
         hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, Gk1, p.dV,
@@ -348,7 +356,8 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     hipLaunchKernelGGL((k_rows<T, T, T, D>), rows, blk, 0, stream, gg, p.H, BH, p.dA,
                        static_cast<const T*>(p.K), static_cast<const T*>(nullptr),
                        static_cast<T*>(p.dQ), 1.0f, 0.0f);
-    hipLaunchKernelGGL(k_to_columns, entries, blk, 0, stream, ci, p.H, p.dA, p.At);
+    hipLaunchKernelGGL(k_to_columns, entries, blk, 0, stream, ci, p.H, BH, entry_blocks, p.dA,
+                       p.At);
     hipLaunchKernelGGL((k_cols<T, T, D>), rows, blk, 0, stream, ci, p.H, BH, p.At,
                        static_cast<const T*>(p.Q), static_cast<T*>(p.dK), 1.0f);
     return hipGetLastError();
