@@ -156,7 +156,8 @@ __device__ __forceinline__ void score_pass(const BlockArgs& a, const BlockRows& 
     for (int32_t kb = 0; kb < nk; ++kb) {
         full_barrier();   // key block kb in LDS, kb - 1 done by every wave
         const char LDS_AS* cur = lds + (kb & 1) * kBufBytes;
-        if (kb + 1 < nk) dma_k(lds + ((kb + 1) & 1) * kBufBytes, Kbh, a.bcol[br.k0 + kb0 + kb + 1], wave, lane);
+        if (kb + 1 < nk)
+            dma_k(lds + ((kb + 1) & 1) * kBufBytes, Kbh, a.bcol[br.k0 + kb0 + kb + 1], wave, lane);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const f32x4 x = key_tile(cur, t, kg, s16, q0, q1);
@@ -166,7 +167,8 @@ __device__ __forceinline__ void score_pass(const BlockArgs& a, const BlockRows& 
             }
             float w[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], a.scale_log2, -ms));
+            for (int e = 0; e < 4; ++e)
+                w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], a.scale_log2, -ms));
             if (P == kBWriteNorm) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) w[e] *= inv;
@@ -180,7 +182,8 @@ __device__ __forceinline__ void score_pass(const BlockArgs& a, const BlockRows& 
             // Fused mode: c_i is over the weights as stored.
             if (P == kBWrite) sum += (bf16_lo(lo) + bf16_hi(lo)) + (bf16_lo(hi) + bf16_hi(hi));
             if (P == kBWrite || P == kBWriteNorm)
-                *reinterpret_cast<u32x2*>(Arow + (int64_t)kb * kBlk + 16 * t + 4 * kg) = u32x2{lo, hi};
+                *reinterpret_cast<u32x2*>(Arow + (int64_t)kb * kBlk + 16 * t + 4 * kg) =
+                    u32x2{lo, hi};
         }
     }
     __syncthreads();   // every wave is done with the buffers
@@ -228,7 +231,8 @@ void k_block_gmax(BlockArgs a) {
     float m = -INFINITY, sum = 0.0f;
     score_pass<kBMax>(a, br, kb0, kb1, Kbh, nullptr, lds, wave, lane, q0, q1, m, 0.0f, sum, 0.0f);
     m = quad_max(m);
-    if (kg == 0) a.part[((int64_t)bh * a.gblocks + I) * a.gparts * kBlk + p * kBlk + 16 * wave + s16] = m;
+    if (kg == 0)
+        a.part[((int64_t)bh * a.gblocks + I) * a.gparts * kBlk + p * kBlk + 16 * wave + s16] = m;
 }
 
 __global__ __launch_bounds__(kThreads)
@@ -263,7 +267,8 @@ void k_block_scores(BlockArgs a) {
         score_pass<kBWrite>(a, br, kb0, kb1, Kbh, Arow + (int64_t)kb0 * kBlk, lds, wave, lane, q0,
                             q1, m, m * a.scale_log2, sum, 0.0f);
         sum = quad_sum(sum);
-        float* ps = a.part + ((int64_t)a.total_parts + ((int64_t)it.bh * a.gblocks + it.I) * a.gparts +
+        float* ps = a.part + ((int64_t)a.total_parts +
+                              ((int64_t)it.bh * a.gblocks + it.I) * a.gparts +
                               it.p) * kBlk;
         if (kg == 0) ps[16 * wave + s16] = sum;
         return;
@@ -290,7 +295,8 @@ void k_block_scores(BlockArgs a) {
         }
         sum = 0.0f;
         if (a.normalized)
-            score_pass<kBSum>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum, 0.0f);
+            score_pass<kBSum>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum,
+                              0.0f);
         else
             score_pass<kBWrite>(a, br, 0, br.nk, Kbh, Arow, lds, wave, lane, q0, q1, m, ms, sum,
                                 0.0f);
@@ -309,7 +315,8 @@ void k_block_scores(BlockArgs a) {
 __global__ __launch_bounds__(kThreads)
 void k_block_gsum(BlockArgs a) {
     const int32_t bh = (int32_t)blockIdx.x / a.gblocks, I = (int32_t)blockIdx.x % a.gblocks;
-    const float* ps = a.part + ((int64_t)a.total_parts + ((int64_t)bh * a.gblocks + I) * a.gparts) * kBlk;
+    const float* ps =
+        a.part + ((int64_t)a.total_parts + ((int64_t)bh * a.gblocks + I) * a.gparts) * kBlk;
     for (int r = threadIdx.x; r < kBlk; r += kThreads) {
         float sum = 0.0f;
         for (int32_t p = 0; p < a.gparts; ++p) sum += ps[p * kBlk + r];
@@ -383,7 +390,8 @@ void k_block_diffuse(BlockArgs a) {
         if (kb + 1 < nk) {
             dma_z(lds + ((kb + 1) & 1) * kBufBytes, Zbh, a.bcol[br.k0 + kb0 + kb + 1], wave, lane);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) wn[ks] = load16(Arow + (int64_t)(kb + 1) * kBlk + 32 * ks + 8 * kg);
+            for (int ks = 0; ks < 2; ++ks)
+                wn[ks] = load16(Arow + (int64_t)(kb + 1) * kBlk + 32 * ks + 8 * kg);
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -407,7 +415,8 @@ void k_block_diffuse(BlockArgs a) {
         return;
     }
     // Restart and store: lane holds channels 16 nb + 4 kg .. + 3 of its row.
-    const float keep = a.row_scale != nullptr ? a.keep * a.row_scale[(int64_t)it.bh * n + row] : a.keep;
+    const float keep =
+        a.row_scale != nullptr ? a.keep * a.row_scale[(int64_t)it.bh * n + row] : a.keep;
     const int64_t o = ((int64_t)it.bh * n + row) * kD + 4 * kg;
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
@@ -437,7 +446,8 @@ void k_block_combine(BlockArgs a) {
     for (int p = 0; p < a.gparts; ++p) sum += src[(int64_t)p * kBlk * kD];
     const int64_t row = (int64_t)I * kBlk + idx / kD;
     const int64_t o = ((int64_t)bh * n + row) * kD + idx % kD;
-    const float keep = a.row_scale != nullptr ? a.keep * a.row_scale[(int64_t)bh * n + row] : a.keep;
+    const float keep =
+        a.row_scale != nullptr ? a.keep * a.row_scale[(int64_t)bh * n + row] : a.keep;
     a.out[o] = (uint16_t)f32_to_bf16(keep * sum + a.restart * bf16_to_f32(a.V[o]));
 }
 
@@ -524,7 +534,8 @@ hipError_t launch_block_diffuse(const diffuser_graph& g, const attn_shape& s, co
     a.restart = k.restart;
     hipLaunchKernelGGL(k_block_diffuse, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), 0, st, a);
     if (a.gparts > 0)
-        hipLaunchKernelGGL(k_block_combine, dim3((unsigned)(s.B * s.H * a.gblocks * kCombineGroups)),
+        hipLaunchKernelGGL(k_block_combine,
+                           dim3((unsigned)(s.B * s.H * a.gblocks * kCombineGroups)),
                            dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
