@@ -42,9 +42,9 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = 16;
 constexpr int kThreads = kWave * kWaves;
-constexpr int kD = 64;                                // head width
-constexpr int kNB = 4;                                // 16-channel blocks
-constexpr int kRowBytes = kD * 2;                     // a Z row in LDS
+// Head width KD (a template parameter) is 64 or 32: KD / 16 channel blocks;
+// a Z row sits in a 128-byte LDS slot either way.
+constexpr int kRowBytes = 128;                        // LDS slot of one Z row
 constexpr int kBufBytes = (kChunkRows + 1) * kRowBytes;  // chunk + zero row
 constexpr int kTileRows = kWaves * kRowBlock;         // rows per row-tile workgroup
 constexpr int kGrowRows = 32;                         // global rows per workgroup
@@ -59,7 +59,7 @@ constexpr int kMaxGlob = 2;                           // global steps per chunk 
 constexpr int kLdsBytes = 2 * kBufBytes + kWaves * 2 * kStageBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
-static_assert(kWaves * 2 * kNB * 4 * kWave * 4 <= 2 * kBufBytes, "grow partial sums fit");
+static_assert(kWaves * 2 * 4 * 4 * kWave * 4 <= 2 * kBufBytes, "grow partial sums fit");
 
 struct FastArgs {
     int64_t n;
@@ -113,71 +113,88 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const u32x4& b, const f32
 }
 
 // acc[nb] += Z^T(r1, r2) W^T for the four channel blocks.
-__device__ __forceinline__ void mfma4(f32x4 (&acc)[kNB], uint32_t r1, uint32_t r2,
+template <int NB>
+__device__ __forceinline__ void mfma4(f32x4 (&acc)[NB], uint32_t r1, uint32_t r2,
                                       const u32x4& w) {
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma(z_operand(r1, r2, nb), w, acc[nb]);
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma(z_operand(r1, r2, nb), w, acc[nb]);
 }
 
-// Per-lane byte offsets, within a chunk of Z_k rows, of the 16 bytes each of
-// this lane's four direct loads fetches: in LDS block 4 w + j (8 rows, 1 KB)
-// lane l writes 16-byte unit l % 8 of row l / 8, which holds the row's
-// logical unit (l % 8) ^ (2 sw), sw the row's quarter swizzle.
+// Per-lane byte offsets, within a chunk of Z_k rows (2 KD bytes each), of
+// the 16 bytes each of this lane's four direct loads fetches: in LDS block
+// 4 w + j (8 row slots, 1 KB) lane l writes 16-byte unit l % 8 of slot l / 8,
+// which holds the row's logical unit (l % 8) ^ (2 sw), sw the row's quarter
+// swizzle; units past the row (KD = 32: logical units 4..7) are not loaded
+// (bit j of `live` clear).
 struct ChunkLanes {
     uint32_t off[4];
+    uint32_t live;
 };
 
+template <int KD>
 __device__ __forceinline__ ChunkLanes chunk_lanes(int wave, int lane) {
     ChunkLanes cl;
+    cl.live = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t pr = (uint32_t)((4 * wave + j) * 8 + (lane >> 3));
         const uint32_t lu = (uint32_t)(lane & 7) ^ ((key_row_code(pr) & 3u) << 1);
-        cl.off[j] = pr * kRowBytes + lu * 16;
+        const bool live = lu < (uint32_t)(KD / 8);
+        cl.off[j] = live ? pr * (2 * KD) + lu * 16 : 0u;
+        cl.live |= (live ? 1u : 0u) << j;
     }
     return cl;
 }
 
 // Direct loads of chunk rows [c0, c0 + kChunkRows) of Z_k into `buf`. Rows
 // at or beyond n repeat row n - 1 (their weights are zero).
+template <int KD>
 __device__ __forceinline__ void dma_chunk(char LDS_AS* buf, const uint16_t* Zbh, int64_t n,
                                           int64_t c0, const ChunkLanes& cl, int wave) {
-    const char* src = reinterpret_cast<const char*>(Zbh + c0 * kD);
+    constexpr uint32_t kRB = 2 * KD;   // bytes of a Z row in memory
+    const char* src = reinterpret_cast<const char*>(Zbh + c0 * KD);
     if (c0 + kChunkRows <= n) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(src + cl.off[j], buf + (4 * wave + j) * 1024);
+        for (int j = 0; j < 4; ++j)
+            if (KD == 64 || ((cl.live >> j) & 1u)) dma16(src + cl.off[j], buf + (4 * wave + j) * 1024);
     } else {
-        const uint32_t last = (uint32_t)(n - 1 - c0) * kRowBytes;
+        const uint32_t last = (uint32_t)(n - 1 - c0) * kRB;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t o = cl.off[j] < last + kRowBytes ? cl.off[j] : last | (cl.off[j] & 127u);
-            dma16(src + o, buf + (4 * wave + j) * 1024);
+            const uint32_t o = cl.off[j] < last + kRB ? cl.off[j] : last | (cl.off[j] & (kRB - 1));
+            if (KD == 64 || ((cl.live >> j) & 1u)) dma16(src + o, buf + (4 * wave + j) * 1024);
         }
     }
 }
 
 // Direct loads of the rows r0 .. r0 + 15 of V (a wave's restart inputs)
-// into `vbuf`, row j at vbuf + 128 j in order; rows at or beyond n repeat
+// into `vbuf`, row j at vbuf + 2 KD j in order; rows at or beyond n repeat
 // row n - 1.
+template <int KD>
 __device__ __forceinline__ void dma_restart(const FastArgs& a, int32_t bh, int64_t r0,
                                             char LDS_AS* vbuf, int lane) {
+    constexpr int kUnits = KD / 8;             // 16-byte units of a row
+    constexpr int kRowsPer = kWave / kUnits;   // rows per load instruction
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int64_t row = min(r0 + 8 * u + (lane >> 3), a.n - 1);
-        dma16(a.V + ((int64_t)bh * a.n + row) * kD + 8 * (lane & 7), vbuf + 1024 * u);
+    for (int u = 0; u < 16 / kRowsPer; ++u) {
+        const int64_t row = min(r0 + kRowsPer * u + lane / kUnits, a.n - 1);
+        dma16(a.V + ((int64_t)bh * a.n + row) * KD + 8 * (lane % kUnits), vbuf + 1024 * u);
     }
 }
 
 // Restart and store of one lane's accumulators: row `i` (row j of the
-// wave's staged restart inputs), channels 16 nb + 4 kg .. + 3 for nb = 0..3.
+// wave's staged restart inputs), channels 16 nb + 4 kg .. + 3 for
+// nb < KD / 16.
+template <int KD>
 __device__ __forceinline__ void store_row(const FastArgs& a, int32_t bh, int64_t i, int j, int kg,
-                                          const f32x4 (&acc)[kNB], const char LDS_AS* vbuf,
+                                          const f32x4 (&acc)[KD / 16], const char LDS_AS* vbuf,
                                           float scale) {
     const float keep = a.keep * scale;
-    const int64_t base = ((int64_t)bh * a.n + i) * kD + 4 * kg;
+    const int64_t base = ((int64_t)bh * a.n + i) * KD + 4 * kg;
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-        const u32x2 v = *reinterpret_cast<const u32x2 LDS_AS*>(vbuf + 128 * j + 2 * (16 * nb + 4 * kg));
+    for (int nb = 0; nb < KD / 16; ++nb) {
+        const u32x2 v = *reinterpret_cast<const u32x2 LDS_AS*>(vbuf + 2 * KD * j +
+                                                             2 * (16 * nb + 4 * kg));
         u32x2 o;
         o[0] = to_bf16_pair(keep * acc[nb][0] + a.restart * bf16_lo(v[0]),
                             keep * acc[nb][1] + a.restart * bf16_hi(v[0]));
@@ -272,7 +289,8 @@ __device__ __forceinline__ GroupLane group_lane(const TileLane& t, const FastArg
 // `nstg`), multiplies the random groups, then the dense steps. The LDS
 // regions are disjoint, which lets the reads of `cur` and `stg` run while
 // the loads into `nxt` and `nstg` are in flight.
-__device__ __forceinline__ void tile_chunk(const TileLane& t, f32x4 (&acc)[kNB], const FastArgs& a,
+template <int KD>
+__device__ __forceinline__ void tile_chunk(const TileLane& t, f32x4 (&acc)[KD / 16], const FastArgs& a,
                                            const uint16_t* Abh, const uint16_t* Zbh,
                                            const ChunkLanes& cl, char LDS_AS* __restrict__ nxt,
                                            const char LDS_AS* __restrict__ cur,
@@ -293,7 +311,7 @@ __device__ __forceinline__ void tile_chunk(const TileLane& t, f32x4 (&acc)[kNB],
     const int ib1 = kb0 <= kb1 ? (int)((kb1 - t.band_lo) >> 5) : ib0 - 1;
 
     if (more) {
-        dma_chunk(nxt, Zbh, a.n, c0 + kChunkRows, cl, wave);
+        dma_chunk<KD>(nxt, Zbh, a.n, c0 + kChunkRows, cl, wave);
         dma_groups(t, a, Abh, nstg, c + 1, lane);
     }
 
@@ -347,17 +365,18 @@ __device__ __forceinline__ void tile_chunk(const TileLane& t, f32x4 (&acc)[kNB],
 
 // One key chunk of a global-row wave: starts the direct loads of chunk
 // c + 1 into `nxt` and multiplies keys c0 + 32 w .. + 31 of `cur`.
-__device__ __forceinline__ void grow_chunk(f32x4 (&acc)[2][kNB], const u32x4 (&w)[2],
+template <int KD>
+__device__ __forceinline__ void grow_chunk(f32x4 (&acc)[2][KD / 16], const u32x4 (&w)[2],
                                            const uint16_t* Zbh, int64_t n, int nchunks,
                                            const ChunkLanes& cl, char LDS_AS* __restrict__ nxt,
                                            const char LDS_AS* __restrict__ cur, int c, int wave,
                                            uint32_t b1, uint32_t b2) {
     const int64_t c0 = (int64_t)c * kChunkRows;
-    if (c + 1 < nchunks) dma_chunk(nxt, Zbh, n, c0 + kChunkRows, cl, wave);
+    if (c + 1 < nchunks) dma_chunk<KD>(nxt, Zbh, n, c0 + kChunkRows, cl, wave);
     if (c0 + 32 * wave < n) {
         const uint32_t base = lds_addr(cur);
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
+        for (int nb = 0; nb < KD / 16; ++nb) {
             const bf16x8 zop = z_operand(base + b1, base + b2, nb);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma(zop, w[mb], acc[mb][nb]);
@@ -365,8 +384,10 @@ __device__ __forceinline__ void grow_chunk(f32x4 (&acc)[2][kNB], const u32x4 (&w
     }
 }
 
+template <int KD>
 __global__ __launch_bounds__(kThreads)
 void k_diffuse_sched(FastArgs a) {
+    constexpr int NB = KD / 16;   // 16-channel blocks
     extern __shared__ __align__(128) char lds_raw[];
     char LDS_AS* lds = (char LDS_AS*)lds_raw;
     const int lane = __lane_id();
@@ -384,10 +405,10 @@ void k_diffuse_sched(FastArgs a) {
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
     const int64_t n = a.n;
     const uint16_t* Abh = a.A + a_block_offset(a.slot_off, a.num_graphs, a.H, b, h);
-    const uint16_t* Zbh = a.Z + (int64_t)bh * n * kD;
+    const uint16_t* Zbh = a.Z + (int64_t)bh * n * KD;
     const int4* info = a.row_info + (int64_t)gr * n;
     char LDS_AS* buf[2] = {lds, lds + kBufBytes};
-    const ChunkLanes cl = chunk_lanes(wave, lane);
+    const ChunkLanes cl = chunk_lanes<KD>(wave, lane);
 
     // Zero row kChunkRows of both buffers (the key row of dummy slots).
     if (threadIdx.x < 16) {
@@ -419,21 +440,22 @@ void k_diffuse_sched(FastArgs a) {
                 if (kc + 8 * kg < wlen[mb]) w[mb] = load16(Abh + wbase[mb] + kc + 8 * kg);
             }
         };
-        f32x4 acc[2][kNB];
+        f32x4 acc[2][NB];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         u32x4 w[2], wn[2];
         fetch_w(w, 32 * wave);
-        dma_chunk(buf[0], Zbh, n, 0, cl, wave);
+        dma_chunk<KD>(buf[0], Zbh, n, 0, cl, wave);
         const uint32_t b1 = code_addr(a8, key_row_code(32u * wave + 8u * kg + q4));
         const uint32_t b2 = code_addr(a8, key_row_code(32u * wave + 8u * kg + 4u + q4));
         for (int c = 0; c < a.nchunks; ++c) {
             const int64_t c0 = (int64_t)c * kChunkRows;
             full_barrier();   // chunk c in LDS
             if (c + 1 < a.nchunks) fetch_w(wn, c0 + kChunkRows + 32 * wave);
-            grow_chunk(acc, w, Zbh, n, a.nchunks, cl, buf[(c + 1) & 1], buf[c & 1], c, wave, b1, b2);
+            grow_chunk<KD>(acc, w, Zbh, n, a.nchunks, cl, buf[(c + 1) & 1], buf[c & 1], c, wave, b1,
+                           b2);
             w[0] = wn[0];
             w[1] = wn[1];
         }
@@ -443,21 +465,21 @@ void k_diffuse_sched(FastArgs a) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    part[(((wave * 2 + mb) * kNB + nb) * 4 + e) * kWave + lane] = acc[mb][nb][e];
+                    part[(((wave * 2 + mb) * NB + nb) * 4 + e) * kWave + lane] = acc[mb][nb][e];
         lds_barrier();
-        constexpr int kPer = 2 * kNB * 4 * kWave;   // partial sums per wave
+        constexpr int kPer = 2 * NB * 4 * kWave;   // partial sums per wave
         for (int idx = threadIdx.x; idx < kPer; idx += kThreads) {
             float sum = 0.0f;
             for (int w2 = 0; w2 < kWaves; ++w2) sum += part[w2 * kPer + idx];
-            const int l = idx & 63, e = (idx >> 6) & 3, nb = (idx >> 8) & 3, mb = idx >> 10;
+            const int l = idx & 63, e = (idx >> 6) & 3, nb = (idx >> 8) % NB, mb = (idx >> 8) / NB;
             const int q = q0 + 16 * mb + (l & 15);
             if (q >= a.g) continue;
             const int64_t i = a.G[q];
             const int ch = 16 * nb + 4 * (l >> 4) + e;
-            const int64_t o = ((int64_t)bh * n + i) * kD + ch;
+            const int64_t o = ((int64_t)bh * n + i) * KD + ch;
             const float keep = a.row_scale ? a.keep * a.row_scale[(int64_t)bh * n + i] : a.keep;
             a.Zn[o] = (uint16_t)f32_to_bf16(keep * sum + a.restart * bf16_to_f32(a.V[o]));
         }
@@ -490,7 +512,7 @@ void k_diffuse_sched(FastArgs a) {
     t.goff = a.grp_off[gr];
     t.rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];   // random area of the graph
 
-    dma_chunk(buf[0], Zbh, n, 0, cl, wave);
+    dma_chunk<KD>(buf[0], Zbh, n, 0, cl, wave);
     t.nbs = active ? (int)((t.band_hi - t.band_lo) >> 5) + 1 : 0;
     t.ngs = (a.g + 31) >> 5;
 #pragma unroll
@@ -508,37 +530,38 @@ void k_diffuse_sched(FastArgs a) {
         }
     }
     if (active) dma_groups(t, a, Abh, stg[0], 0, lane);
-    f32x4 acc[kNB];
+    f32x4 acc[NB];
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     float scale = 1.0f;   // c_i of this lane's row
     for (int c = 0; c < a.nchunks; ++c) {
         full_barrier();   // chunk c in LDS, chunk c - 1 done by every wave
         if (c + 1 == a.nchunks && active) {
             // The idle buffer takes the restart inputs of the wave's rows.
-            dma_restart(a, bh, t.r0w, buf[(c + 1) & 1] + wave * 2048, lane);
+            dma_restart<KD>(a, bh, t.r0w, buf[(c + 1) & 1] + wave * 2048, lane);
             if (a.row_scale != nullptr && t.rok) scale = a.row_scale[(int64_t)bh * n + my_row];
         }
         if (active) {
-            tile_chunk(t, acc, a, Abh, Zbh, cl, buf[(c + 1) & 1], buf[c & 1], stg[(c + 1) & 1],
-                       stg[c & 1], c, wave, lane);
+            tile_chunk<KD>(t, acc, a, Abh, Zbh, cl, buf[(c + 1) & 1], buf[c & 1],
+                           stg[(c + 1) & 1], stg[c & 1], c, wave, lane);
         } else if (c + 1 < a.nchunks) {
-            dma_chunk(buf[(c + 1) & 1], Zbh, n, (int64_t)(c + 1) * kChunkRows, cl, wave);
+            dma_chunk<KD>(buf[(c + 1) & 1], Zbh, n, (int64_t)(c + 1) * kChunkRows, cl, wave);
         }
     }
 
     if (active) {
         __builtin_amdgcn_s_waitcnt(0x0070);   // this wave's restart inputs have landed
         if (t.rok)
-            store_row(a, bh, my_row, s16, kg, acc, buf[a.nchunks & 1] + wave * 2048, scale);
+            store_row<KD>(a, bh, my_row, s16, kg, acc, buf[a.nchunks & 1] + wave * 2048, scale);
     }
 }
 
 }  // namespace
 
 bool fast_diffuse_supported(const diffuser_graph& g, const attn_shape& s) {
-    if (!g.structured || !g.scheduled || s.dtype != DIFFUSER_BF16 || s.d != kD) return false;
+    if (!g.structured || !g.scheduled || s.dtype != DIFFUSER_BF16 || (s.d != 64 && s.d != 32))
+        return false;
     for (int64_t x : g.slots)
         if (x >= (1ll << 31)) return false;
     return true;
@@ -580,16 +603,24 @@ hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, con
     a.bh_per_xcd = 0;   // (b, h)-ordered runs (measured slightly faster here than tiles-first)
     a.per_xcd = a.bh_per_xcd > 0 ? a.bh_per_xcd * (a.tiles_per_bh + a.grow_per_bh)
                                  : (a.total_items + 7) / 8;
-    static int attr_device = -1;   // dynamic LDS above 64 KB is enabled per device
-    if (attr_device != g.device) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_diffuse_sched),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    // Dynamic LDS above 64 KB is enabled once per device and instantiation.
+    static int attr_device[2] = {-1, -1};
+    const int which = s.d == 64 ? 0 : 1;
+    const void* kern = s.d == 64 ? reinterpret_cast<const void*>(&k_diffuse_sched<64>)
+                                 : reinterpret_cast<const void*>(&k_diffuse_sched<32>);
+    if (attr_device[which] != g.device) {
+        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           kLdsBytes);
         if (e != hipSuccess) return e;
-        attr_device = g.device;
+        attr_device[which] = g.device;
     }
     const size_t lds = kLdsBytes;
-    hipLaunchKernelGGL(k_diffuse_sched, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), lds, st,
-                       a);
+    if (s.d == 64)
+        hipLaunchKernelGGL(k_diffuse_sched<64>, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
+                           lds, st, a);
+    else
+        hipLaunchKernelGGL(k_diffuse_sched<32>, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
+                           lds, st, a);
     return hipGetLastError();
 }
 

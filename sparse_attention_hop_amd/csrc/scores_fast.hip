@@ -45,8 +45,10 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = 16;
 constexpr int kThreads = kWave * kWaves;
-constexpr int kD = 64;
-constexpr int kRowBytes = kD * 2;
+// A key row sits in a 128-byte LDS slot (64 channels of bf16); a head width
+// of 32 fills half of it and leaves channels 32..63 zero, so the second
+// product of each tile adds nothing.
+constexpr int kRowBytes = 128;
 constexpr int kBufBytes = (kChunkRows + 1) * kRowBytes;   // chunk + zero row
 constexpr int kTileRows = kWaves * kRowBlock;
 constexpr int kGrowRows = 32;
@@ -66,6 +68,7 @@ constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
 
 struct ScoreArgs {
     int32_t n, H, num_graphs, radius, g, causal, nchunks, nrb;
+    int32_t kd;                 // head width: 64 or 32
     const int64_t* slot_off;    // [graphs + 1]
     const int64_t* seg_ptr;     // [graphs][n + 1]
     const int4* row_info;       // [graphs][n]
@@ -103,17 +106,19 @@ __device__ __forceinline__ f32x4 dots(const u32x4& a0, const u32x4& a1, const u3
 }
 
 // Direct loads of chunk rows [c0, c0 + kChunkRows) of K into `buf` (wave w
-// fills 1 KB blocks 4w .. 4w+3); rows at or beyond n repeat row n - 1.
-__device__ __forceinline__ void dma_chunk(char LDS_AS* buf, const uint16_t* Kbh, int32_t n,
-                                          int32_t c0, int wave, int lane) {
+// fills 1 KB blocks 4w .. 4w+3); rows at or beyond n repeat row n - 1. A
+// row's logical units past its a.kd channels are not loaded.
+__device__ __forceinline__ void dma_chunk(char LDS_AS* buf, const uint16_t* Kbh,
+                                          const ScoreArgs& a, int32_t c0, int wave, int lane) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int blk = 4 * wave + t;
         const uint32_t pr = (uint32_t)(blk * 8 + (lane >> 3));
         const uint32_t lu = (uint32_t)(lane & 7) ^ (score_row_code(pr) & 7u);
-        const int32_t src = min(c0 + (int32_t)pr, n - 1);
-        __builtin_amdgcn_global_load_lds(Kbh + (int64_t)src * kD + lu * 8,
-                                         (void LDS_AS*)(buf + blk * 1024), 16, 0, 0);
+        const int32_t src = min(c0 + (int32_t)pr, a.n - 1);
+        if (lu * 8 < (uint32_t)a.kd)
+            __builtin_amdgcn_global_load_lds(Kbh + (int64_t)src * a.kd + lu * 8,
+                                             (void LDS_AS*)(buf + blk * 1024), 16, 0, 0);
     }
 }
 
@@ -337,7 +342,7 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
     const int32_t k_hi = min(t.band_hi, c0 + kChunkRows - 1);
     for (int32_t kb = k_lo; kb <= k_hi; kb += 16) band_tile<P>(t, a, Abh, cur, kb, c0);
 
-    if (more) dma_chunk(nxt, Kbh, a.n, c0 + kChunkRows, wave, lane);
+    if (more) dma_chunk(nxt, Kbh, a, c0 + kChunkRows, wave, lane);
 
     // Random groups: two tiles of 16 slots each. The staged ones read their
     // codes from LDS, any others straight from memory; the two loops are
@@ -417,7 +422,7 @@ __device__ __forceinline__ void tile_globals(SLane& t, const ScoreArgs& a, uint1
 __device__ __forceinline__ void stage_first(const SLane& t, const ScoreArgs& a,
                                             const uint16_t* Kbh, char LDS_AS* lds,
                                             char LDS_AS* stg, bool active, int wave, int lane) {
-    dma_chunk(lds, Kbh, a.n, 0, wave, lane);
+    dma_chunk(lds, Kbh, a, 0, wave, lane);
     if (active) {
         const int32_t g0 = uniform_load(t.cptr);
         const int32_t cnt = min(uniform_load(t.cptr + 1) - g0, kStageGroups);
@@ -452,7 +457,7 @@ __device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uin
             tile_chunk<P>(t, a, Kbh, Abh, (c & 1) ? buf0 : buf1, (c & 1) ? buf1 : buf0, stg, c,
                           wave, lane);
         } else if (c + 1 < a.nchunks) {
-            dma_chunk((c & 1) ? buf0 : buf1, Kbh, a.n, (c + 1) * kChunkRows, wave, lane);
+            dma_chunk((c & 1) ? buf0 : buf1, Kbh, a, (c + 1) * kChunkRows, wave, lane);
         }
     }
     random_end<P>(t);
@@ -489,7 +494,7 @@ __device__ __forceinline__ void grow_chunk(GLane& t, const ScoreArgs& a, const u
                                            const char LDS_AS* __restrict__ cur, int c, int wave,
                                            int lane, bool prefetch = true) {
     const int32_t c0 = c * kChunkRows;
-    if (prefetch && c + 1 < a.nchunks) dma_chunk(nxt, Kbh, a.n, c0 + kChunkRows, wave, lane);
+    if (prefetch && c + 1 < a.nchunks) dma_chunk(nxt, Kbh, a, c0 + kChunkRows, wave, lane);
     if (c0 + 32 * wave >= a.n) return;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -536,7 +541,7 @@ __device__ void grow_pass(GLane& t, const ScoreArgs& a, const uint16_t* Kbh, uin
                           char LDS_AS* lds, int wave, int lane) {
     char LDS_AS* buf0 = lds;
     char LDS_AS* buf1 = lds + kBufBytes;
-    dma_chunk(buf0, Kbh, a.n, 0, wave, lane);
+    dma_chunk(buf0, Kbh, a, 0, wave, lane);
     for (int c = 0; c < a.nchunks; ++c) {
         full_barrier();
         grow_chunk<P>(t, a, Kbh, Abh, (c & 1) ? buf0 : buf1, (c & 1) ? buf1 : buf0, c, wave, lane);
@@ -548,7 +553,9 @@ __device__ void grow_pass(GLane& t, const ScoreArgs& a, const uint16_t* Kbh, uin
 // every lane gets the workgroup value of its rows.
 template <bool kMax>
 __device__ __forceinline__ void grow_merge(float (&v)[2], char LDS_AS* lds, int wave, int lane) {
-    float LDS_AS* part = (float LDS_AS*)lds;   // [wave][32 rows]
+    // [wave][32 rows], past the chunk buffers (whose units beyond a head
+    // width of 32 must stay zero)
+    float LDS_AS* part = (float LDS_AS*)(lds + 2 * kBufBytes);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
         const float x = kMax ? row_max(v[mb]) : row_sum(v[mb]);
@@ -585,15 +592,22 @@ void k_scores_sched(ScoreArgs a) {
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
     const int32_t n = a.n;
     uint16_t* Abh = a.A + a_block_offset(a.slot_off, a.num_graphs, a.H, b, h);
-    const uint16_t* Kbh = a.K + (int64_t)bh * n * kD;
-    const uint16_t* Qbh = a.Q + (int64_t)bh * n * kD;
+    const uint16_t* Kbh = a.K + (int64_t)bh * n * a.kd;
+    const uint16_t* Qbh = a.Q + (int64_t)bh * n * a.kd;
     const int4* info = a.row_info + (int64_t)gr * n;
 
-    // Zero row kChunkRows of both buffers (the key row of dummy slots).
-    if (threadIdx.x < 16)
-        *reinterpret_cast<u32x4 LDS_AS*>(lds + (threadIdx.x >> 3) * kBufBytes +
-                                        kChunkRows * kRowBytes + (threadIdx.x & 7) * 16) =
-            u32x4{0u, 0u, 0u, 0u};
+    // Zero row kChunkRows of both buffers (the key row of dummy slots); at
+    // head width 32 both buffers whole, whose unloaded units stay zero.
+    if (a.kd == 64) {
+        if (threadIdx.x < 16)
+            *reinterpret_cast<u32x4 LDS_AS*>(lds + (threadIdx.x >> 3) * kBufBytes +
+                                            kChunkRows * kRowBytes + (threadIdx.x & 7) * 16) =
+                u32x4{0u, 0u, 0u, 0u};
+    } else {
+        for (int u = threadIdx.x; u < 2 * kBufBytes / 16; u += kThreads)
+            *reinterpret_cast<u32x4 LDS_AS*>(lds + 16 * u) = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+    }
 
     if (sub < a.grow_per_bh) {
         GLane t;
@@ -608,8 +622,9 @@ void k_scores_sched(ScoreArgs a) {
             t.sbase[mb] = t.i[mb] >= 0 ? sp[t.i[mb]] : 0;
             t.slen[mb] = t.i[mb] >= 0 ? (int32_t)(sp[t.i[mb] + 1] - sp[t.i[mb]]) : 0;
             const int32_t qi = t.i[mb] >= 0 ? t.i[mb] : 0;
-            t.q0[mb] = load16(Qbh + (int64_t)qi * kD + 8 * kg);
-            t.q1[mb] = load16(Qbh + (int64_t)qi * kD + 32 + 8 * kg);
+            t.q0[mb] = load16(Qbh + (int64_t)qi * a.kd + 8 * kg);
+            t.q1[mb] = a.kd == 64 ? load16(Qbh + (int64_t)qi * a.kd + 32 + 8 * kg)
+                                  : u32x4{0u, 0u, 0u, 0u};
             t.m[mb] = -INFINITY;
             t.sum[mb] = 0.0f;
             t.inv[mb] = 0.0f;
@@ -618,8 +633,9 @@ void k_scores_sched(ScoreArgs a) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             const int32_t qi = t.i[mb] >= 0 ? t.i[mb] : 0;
-            const u32x4 k0 = load16(Kbh + (int64_t)qi * kD + 8 * kg);
-            const u32x4 k1 = load16(Kbh + (int64_t)qi * kD + 32 + 8 * kg);
+            const u32x4 k0 = load16(Kbh + (int64_t)qi * a.kd + 8 * kg);
+            const u32x4 k1 = a.kd == 64 ? load16(Kbh + (int64_t)qi * a.kd + 32 + 8 * kg)
+                                        : u32x4{0u, 0u, 0u, 0u};
             float d = 0.0f;
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -677,8 +693,8 @@ void k_scores_sched(ScoreArgs a) {
     const int32_t whi = a.causal ? t.i : min(t.i + a.radius, n - 1);
     t.span = (uint32_t)(whi - t.lo);
     const int32_t qi = min(t.i, n - 1);
-    t.q0 = load16(Qbh + (int64_t)qi * kD + 8 * kg);
-    t.q1 = load16(Qbh + (int64_t)qi * kD + 32 + 8 * kg);
+    t.q0 = load16(Qbh + (int64_t)qi * a.kd + 8 * kg);
+    t.q1 = a.kd == 64 ? load16(Qbh + (int64_t)qi * a.kd + 32 + 8 * kg) : u32x4{0u, 0u, 0u, 0u};
     t.m = -INFINITY;
     t.ms = 0.0f;
     t.sum = 0.0f;
@@ -700,7 +716,7 @@ void k_scores_sched(ScoreArgs a) {
     for (int idx = threadIdx.x; idx < gpad * 8; idx += kThreads) {
         const int q = idx >> 3, lu = idx & 7;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (q < a.g) v = load16(Kbh + (int64_t)a.G[q] * kD + lu * 8);
+        if (q < a.g && lu * 8 < a.kd) v = load16(Kbh + (int64_t)a.G[q] * a.kd + lu * 8);
         *reinterpret_cast<u32x4 LDS_AS*>(zg + ((score_row_code((uint32_t)q) ^ (uint32_t)lu) << 4)) =
             v;
     }
@@ -711,8 +727,9 @@ void k_scores_sched(ScoreArgs a) {
     // every row, so this is at most the row maximum (the 4 lanes of a row
     // hold 16 channels each).
     {
-        const u32x4 k0 = load16(Kbh + (int64_t)qi * kD + 8 * kg);
-        const u32x4 k1 = load16(Kbh + (int64_t)qi * kD + 32 + 8 * kg);
+        const u32x4 k0 = load16(Kbh + (int64_t)qi * a.kd + 8 * kg);
+        const u32x4 k1 = a.kd == 64 ? load16(Kbh + (int64_t)qi * a.kd + 32 + 8 * kg)
+                                    : u32x4{0u, 0u, 0u, 0u};
         float d = 0.0f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) d = dot2_bf16(t.q1[u], k1[u], dot2_bf16(t.q0[u], k0[u], d));
@@ -747,7 +764,8 @@ void k_scores_sched(ScoreArgs a) {
 }  // namespace
 
 bool fast_scores_supported(const diffuser_graph& g, const attn_shape& s) {
-    if (!g.structured || !g.scheduled || s.dtype != DIFFUSER_BF16 || s.d != kD) return false;
+    if (!g.structured || !g.scheduled || s.dtype != DIFFUSER_BF16 || (s.d != 64 && s.d != 32))
+        return false;
     if (g.num_global > kMaxGlobal) return false;
     for (int64_t x : g.slots)
         if (x >= (1ll << 31)) return false;
@@ -780,6 +798,7 @@ hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, cons
     a.row_scale = row_scale;
     a.scale_log2 = scale_log2;
     a.normalized = normalized ? 1 : 0;
+    a.kd = s.d;
     const int32_t BH = s.B * s.H;
     a.tiles_per_bh = (int32_t)((g.n + kTileRows - 1) / kTileRows);
     a.grow_per_bh = (g.num_global + kGrowRows - 1) / kGrowRows;

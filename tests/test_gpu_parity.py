@@ -355,7 +355,7 @@ def test_invalid_arguments_gpu():
 
 
 # ---------------------------------------------------------------------------
-# LDS-streamed MFMA diffusion (built graphs, bf16, d = 64): shapes that cross
+# LDS-streamed MFMA kernels (built graphs, bf16, d = 64 or 32): shapes that cross
 # chunk and tile boundaries, several global-row workgroups, causal rows,
 # empty random sets, windows wider than the sequence.
 # ---------------------------------------------------------------------------
@@ -375,12 +375,13 @@ FAST_CASES = [
 
 @pytest.mark.parametrize("case", FAST_CASES, ids=lambda c: f"n{c[0]}r{c[1]}g{len(c[2])}R{c[3]}c{int(c[5])}")
 @pytest.mark.parametrize("K,alpha", [(5, 0.1), (2, 0.0), (1, 0.3)])
-def test_fast_diffusion_shapes(orc, case, K, alpha):
+@pytest.mark.parametrize("d", [64, 32])
+def test_fast_diffusion_shapes(orc, case, K, alpha, d):
     n, r, G, R, ngr, causal, B, H = case
     ng = ngr if ngr in (1, B) else B
     g = _gpu_graph(n, r, G, R, ng, causal, 31)
     rp, cols = _check_csr(orc, g, n, r, G, R, ng, causal, 31)
-    shape = (B, H, n, 64)
+    shape = (B, H, n, d)
     q = make_tensor(shape, 71, torch.bfloat16)
     k = make_tensor(shape, 72, torch.bfloat16)
     v = make_tensor(shape, 73, torch.bfloat16)
