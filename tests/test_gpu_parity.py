@@ -445,7 +445,8 @@ def test_fast_paths_deterministic(case):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_fast_scores_far_random_maximum(orc, causal):
+@pytest.mark.parametrize("d", [64, 32])
+def test_fast_scores_far_random_maximum(orc, causal, d):
     """Rows whose maximum score is a random (or, for a global row, a
     late-chunk) edge far above the window: the shifted weights would pass
     2^64, so the kernel redoes those rows with their exact maximum. Head 0
@@ -453,7 +454,7 @@ def test_fast_scores_far_random_maximum(orc, causal):
     n, r, G, R = 1100, 20, [0, 1, 700], 40
     g = _gpu_graph(n, r, G, R, 1, causal, 41)
     rp, cols = _check_csr(orc, g, n, r, G, R, 1, causal, 41)
-    shape = (1, 2, n, 64)
+    shape = (1, 2, n, d)
     q = make_tensor(shape, 91, torch.bfloat16)
     k = make_tensor(shape, 92, torch.bfloat16)
     v = make_tensor(shape, 93, torch.bfloat16)
