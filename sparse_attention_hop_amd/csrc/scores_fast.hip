@@ -575,8 +575,13 @@ __device__ __forceinline__ void grow_merge(float (&v)[2], char LDS_AS* lds, int 
     lds_barrier();
 }
 
+// One instantiation per head width: the local copy's kd is a constant that
+// every (inlined) helper folds.
+template <int KD>
 __global__ __launch_bounds__(kThreads)
-void k_scores_sched(ScoreArgs a) {
+void k_scores_sched(ScoreArgs args) {
+    ScoreArgs a = args;
+    a.kd = KD;
     extern __shared__ __align__(16) char lds_raw[];
     char LDS_AS* lds = (char LDS_AS*)lds_raw;
     const int lane = __lane_id();
@@ -806,17 +811,26 @@ hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, cons
     a.bh_per_xcd = BH % 8 == 0 ? BH / 8 : 0;
     a.per_xcd = a.bh_per_xcd > 0 ? a.bh_per_xcd * (a.tiles_per_bh + a.grow_per_bh)
                                  : (a.total_items + 7) / 8;
-    static int attr_device = -1;   // dynamic LDS above 64 KB is enabled per device
-    if (attr_device != g.device) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_scores_sched),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    // Dynamic LDS above 64 KB is enabled once per device and instantiation.
+    static int attr_device[2] = {-1, -1};
+    const int which = s.d == 64 ? 0 : 1;
+    const void* kern = s.d == 64 ? reinterpret_cast<const void*>(&k_scores_sched<64>)
+                                 : reinterpret_cast<const void*>(&k_scores_sched<32>);
+    if (attr_device[which] != g.device) {
+        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           kLdsBytes);
         if (e != hipSuccess) return e;
-        attr_device = g.device;
+        attr_device[which] = g.device;
     }
     const int gpad = (g.num_global + 31) & ~31;
     const size_t lds = (size_t)2 * kBufBytes + (size_t)gpad * (kRowBytes + 4) +
                        (size_t)kWaves * kStageBytes;
-    hipLaunchKernelGGL(k_scores_sched, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), lds, st, a);
+    if (s.d == 64)
+        hipLaunchKernelGGL(k_scores_sched<64>, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
+                           lds, st, a);
+    else
+        hipLaunchKernelGGL(k_scores_sched<32>, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
+                           lds, st, a);
     return hipGetLastError();
 }
 
