@@ -12,6 +12,8 @@
 // exponentials are exp2.
 // Pass 1 keeps an online (max, sum) per lane group; pass 2 recomputes the
 // scores and writes A in the storage type.
+#include <type_traits>
+
 #include "internal.h"
 #include "vec.h"
 
@@ -23,6 +25,10 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kUnroll = 4;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A row whose weights, shifted by less than the row maximum, sum to this or
+// more is redone with its exact maximum.
+constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
 
 template <typename T, typename TA, int D>
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
@@ -76,6 +82,43 @@ void k_scores_softmax(GenericGraph gg, int32_t H, int32_t BH, const T* __restric
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) dot[u] += __shfl_xor(dot[u], off);
     };
+
+    if (std::is_same<TA, float>::value && row_scale != nullptr) {
+        // fp32 weights for the diffusion step (fused mode): one pass with the
+        // row's own score as the shift (the self-loop is an edge of every
+        // row, so it is at most the row maximum), unnormalised weights and
+        // c_i = 1 / (their sum). A row whose weights sum to 2^64 or more
+        // falls through to the exact two passes below.
+        float ks[E];
+        chunk<T>::load(Kb + i * D, ks);
+        float sii = 0.0f;
+#pragma unroll
+        for (int c = 0; c < E; ++c) sii = fmaf(q[c], ks[c], sii);
+#pragma unroll
+        for (int off = 1; off < L; off <<= 1) sii += __shfl_xor(sii, off);
+        const float ms = sii * scale_log2;
+        float total = 0.0f;
+        for (int64_t base = 0; base < e1; base += EPI * kUnroll) {
+            int32_t j[kUnroll];
+            int64_t slot[kUnroll];
+            float dot[kUnroll];
+            dots(base, j, slot, dot);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (slot[u] >= 0 && sub == 0) {
+                    const float a = j[u] >= 0 ? fast_exp2(dot[u] * scale_log2 - ms) : 0.0f;
+                    chunk<TA>::store1(Ab + slot[u], a);
+                    total += a;
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) total += __shfl_xor(total, off);
+        if (total < kSumLimit) {
+            if (lane == 0) row_scale[(int64_t)bh * n + i] = 1.0f / total;
+            return;
+        }
+    }
 
     float m = -INFINITY, l = 0.0f;
     for (int64_t base = 0; base < e1; base += EPI * kUnroll) {
