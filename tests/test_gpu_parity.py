@@ -477,6 +477,27 @@ def test_fast_scores_far_random_maximum(orc, causal, d):
         pu.assert_z_close(z_h[0, h], ref, "bf16", f"attn h={h}", 5, 0.1)
 
 
+def test_generic_scores_far_maximum_f32(orc):
+    """fp32 (generic kernels): the whole path's single score pass, shifted by
+    each row's own score, is redone with the exact maximum for rows whose
+    weights would pass 2^64 (head 0); head 1 has ordinary inputs."""
+    n, r, G, R = 600, 10, [0, 300], 24
+    g = _gpu_graph(n, r, G, R, 1, False, 43)
+    rp, cols = _check_csr(orc, g, n, r, G, R, 1, False, 43)
+    shape = (1, 2, n, 32)
+    q = make_tensor(shape, 94, torch.float32)
+    k = make_tensor(shape, 95, torch.float32)
+    v = make_tensor(shape, 96, torch.float32)
+    q[0, 0] = 0
+    q[0, 0, :, 0] = 16.0
+    k[0, 0] = 0
+    k[0, 0, 450, 0] = 45.0            # score 127 for key 450, 0 for every other key
+    z = _as64(sah.attn(q.to(DEV), k.to(DEV), v.to(DEV), g, 5, 0.1))
+    for h in range(2):
+        ref = orc.attn(_as64(q[0, h]), _as64(k[0, h]), _as64(v[0, h]), rp[0], cols[0], 5, 0.1)
+        pu.assert_z_close(z[0, h], ref, "f32", f"attn h={h}", 5, 0.1)
+
+
 def _slot_classes(g, gr, n, r, G, causal):
     """Class of every weight slot of graph gr: 0 window, 1 global column,
     2 random, 3 global row, -1 padding."""
