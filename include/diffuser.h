@@ -216,7 +216,10 @@ DIFFUSER_API diffuser_status diffuser_attn_workspace_size(const diffuser_graph* 
 
 /* Whole path: scores and edge softmax into A (in the workspace), then
  * K_steps diffusion steps; writes Z = Z_K. K_steps >= 0 (0 copies V),
- * 0 <= alpha <= 1. No allocation is made. */
+ * 0 <= alpha <= 1. No allocation is made. The call enqueues only kernel
+ * launches (and, at K_steps = 0, one device-to-device copy) on `stream`,
+ * with no memset and no host synchronisation, so it may be captured into
+ * a HIP graph and replayed; diffuser_attn_theta is the same. */
 DIFFUSER_API diffuser_status diffuser_attn(const void* Q, const void* K, const void* V, diffuser_dtype dtype,
                               int32_t B, int32_t H, int32_t d_h, int32_t d_v,
                               const diffuser_graph* g, int32_t K_steps, float alpha, void* Z,
