@@ -250,6 +250,28 @@ def block_layout(sah, torch, w, q, k, v, reps=10):
     }
 
 
+def graph_replay_ms(torch, step, steps):
+    """Mean wall time of one whole-path call replayed from a captured HIP
+    graph (the same kernels and arguments as the eager call)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
 def cpu_baseline(w, q, k, v, budget_s=15.0, max_pairs=None):
     """The oracle, as it stands, on (b, h) pairs of the same workload until
     the time budget is spent; returns diffused edges/s over the sample."""
@@ -404,6 +426,9 @@ def main():
     if not args.no_extras:
         line["extras"] = extras(sah, torch, w, g, q, k, v, ws)
         line["extras"]["block_layout"] = block_layout(sah, torch, w, q, k, v)
+        t_graph = graph_replay_ms(torch, step, args.steps)
+        line["extras"]["graph_replay"] = {"ms_per_step": t_graph,
+                                          "edges_per_s": diffused / (t_graph * 1e-3)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, q_h, k_h, v_h, budget_s=args.cpu_budget)
     print(json.dumps(line), flush=True)
