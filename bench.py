@@ -145,12 +145,12 @@ def write_traffic(fetch_dir, write_dir, workload):
         f"# HBM traffic of {DIFFUSION_KERNEL} (one diffusion step), workload {workload}",
         "#",
         "# Made by (repository root, one MI355X, TMPDIR=/tmp):",
-        "#   timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch "
+        f"#   timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} "
         f"-o p -- python -u bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline",
-        "#   timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write "
+        f"#   timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} "
         f"-o p -- python -u bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline",
         "#   python bench.py --workload "
-        f"{workload} --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        f"{workload} --write-traffic {fetch_dir} {write_dir}",
         "#",
         f"# Each counter is the mean over the kernel's dispatches, in KiB, scaled by factor =",
         f"# {COPY_BYTES} B / (what the same counter reads for a {COPY_BYTES} B device copy,",
