@@ -274,9 +274,10 @@ DIFFUSER_API diffuser_status diffuser_diffuse_theta(const void* A, const void* V
  * weights in column order, the states Z_0 .. Z_{K-1}, the backward states
  * G_0 .. G_K and dV. The first call on a
  * graph builds its column index (device memory owned by the graph, freed
- * with it; built once, under a lock, synchronising `stream`). Outputs must
- * not overlap inputs, each other or the workspace. Errors as for
- * diffuser_attn.
+ * with it; built once, under a lock, synchronising `stream`). Later calls
+ * enqueue only kernel launches, with no memset and no host synchronisation,
+ * so they may be captured into a HIP graph. Outputs must not overlap
+ * inputs, each other or the workspace. Errors as for diffuser_attn.
  */
 DIFFUSER_API diffuser_status diffuser_attn_backward_workspace_size(const diffuser_graph* g, int32_t B,
                                                       int32_t H, int32_t d, int32_t K_steps,

@@ -97,3 +97,36 @@ def test_attn_theta_graph_replay(case):
     graph = _capture(lambda: sah.attn_theta(q, k, v, g, theta, out=out, workspace=ws))
     _replay_matches_eager(graph, (q, k, v), out, shape, dtype,
                           lambda q2, k2, v2: sah.attn_theta(q2, k2, v2, g, theta))
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[3]], ids=lambda c: c[0])
+def test_attn_backward_graph_replay(case):
+    """The backward, once its first call has built the graph's column index
+    (a one-time host step), also enqueues only kernel launches; its outputs
+    are allocated inside the capture and rewritten by every replay."""
+    _, make_graph, B, H, d, dtype = case
+    g = make_graph()
+    shape = (B, H, g.n, d)
+    q, k, v = _inputs(shape, dtype, 700)
+    dz = make_tensor(shape, 710, dtype).to(DEV)
+    sah.attn_backward(q, k, v, dz, g, 3, 0.1)   # builds the column index
+    torch.cuda.synchronize()
+    got = {}
+
+    def call():
+        got["grads"] = sah.attn_backward(q, k, v, dz, g, 3, 0.1)
+
+    graph = _capture(call)
+    for rep in range(REPLAYS):
+        new = _inputs(shape, dtype, 2000 + 10 * rep)
+        for dst, src in zip((q, k, v), new):
+            dst.copy_(src)
+        for t in got["grads"]:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        expect = sah.attn_backward(*new, dz, g, 3, 0.1)
+        torch.cuda.synchronize()
+        for name, a, e in zip(("dq", "dk", "dv"), got["grads"], expect):
+            assert torch.equal(a, e), f"replay {rep}: {name} differs from the eager call"
