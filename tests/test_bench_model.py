@@ -51,3 +51,16 @@ def test_byte_model_fp32_shared_graph():
     csr = 1000 * 4 + 4097 * 8
     assert score == 2 * tensor + weights + csr
     assert diffusion == weights + csr + 2 * tensor
+
+
+def test_multi_gpu_request_exits_with_message():
+    """The path runs on one GPU; asking bench.py for more exits (status 2)
+    with a message, before anything touches a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "8"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
