@@ -195,9 +195,11 @@ DIFFUSER_API diffuser_status diffuser_graph_copy_slots(const diffuser_graph* g, 
 /* Frees the graph (waits for the device first). Accepts NULL. */
 DIFFUSER_API void diffuser_graph_destroy(diffuser_graph* g);
 
-/* Size in bytes of the workspace diffuser_attn needs (A plus one Z buffer,
- * each 256-byte aligned). diffuser_diffuse needs only the Z buffer part and
- * diffuser_scores_softmax none; the same size is accepted by all three. */
+/* Size in bytes of the workspace diffuser_attn needs (A, one Z buffer, the
+ * row scales and, on block graphs, the block step's partial sums, each
+ * 256-byte aligned). diffuser_scores_softmax needs none and
+ * diffuser_diffuse(_theta) what diffuser_diffuse_workspace_size returns;
+ * this size is accepted by all of them. */
 DIFFUSER_API diffuser_status diffuser_attn_workspace_size(const diffuser_graph* g, int32_t B, int32_t H,
                                              int32_t d_h, int32_t d_v, diffuser_dtype dtype,
                                              size_t* bytes);
@@ -239,6 +241,18 @@ DIFFUSER_API diffuser_status diffuser_diffuse(const void* A, const void* V, diff
                                  int32_t H, int32_t d_v, const diffuser_graph* g,
                                  int32_t K_steps, float alpha, void* Z, void* workspace,
                                  size_t ws_bytes, void* stream);
+
+/* Size in bytes of the workspace diffuser_diffuse and diffuser_diffuse_theta
+ * need for K_steps steps on g: one Z buffer when K_steps >= 2, plus, on
+ * block graphs ("1.2.1 Static sparsity", section 2, eq. 13) whose global
+ * query blocks are split over workgroups, the fp32 partial sums of the block
+ * step. 0 means workspace may be NULL. The figure covers both entry points
+ * (diffuser_diffuse_theta launches one step even at K_steps = 0); a smaller
+ * ws_bytes gives DIFFUSER_ERR_INVALID_ARG before any launch. */
+DIFFUSER_API diffuser_status diffuser_diffuse_workspace_size(const diffuser_graph* g, int32_t B,
+                                                             int32_t H, int32_t d_v,
+                                                             int32_t K_steps,
+                                                             diffuser_dtype dtype, size_t* bytes);
 
 /*
  * General diffusion coefficients ("Diffuser" notes, section 2.3, eq. S.6,

@@ -12,6 +12,7 @@ Functions mirror the C ABI names:
   attn            -> diffuser_attn
   scores_softmax  -> diffuser_scores_softmax
   diffuse         -> diffuser_diffuse
+  diffuse_workspace_size -> diffuser_diffuse_workspace_size
   attn_backward   -> diffuser_attn_backward (+ _workspace_size)
   layer_forward   -> diffuser_layer_forward (+ _workspace_size)
   attn_theta      -> diffuser_attn_theta
@@ -43,6 +44,7 @@ ABI_SYMBOLS = (
     "diffuser_graph_copy_csr", "diffuser_graph_copy_slots", "diffuser_graph_destroy",
     "diffuser_attn_workspace_size",
     "diffuser_attn", "diffuser_scores_softmax", "diffuser_diffuse",
+    "diffuser_diffuse_workspace_size",
     "diffuser_attn_theta", "diffuser_diffuse_theta",
     "diffuser_attn_backward_workspace_size", "diffuser_attn_backward",
     "diffuser_layer_workspace_size", "diffuser_layer_forward",
@@ -119,6 +121,9 @@ def load_library(path: str = LIB_PATH):
     lib.diffuser_graph_destroy.restype = None
     lib.diffuser_attn_workspace_size.argtypes = [p, i32, i32, i32, i32, st, ctypes.POINTER(sz)]
     lib.diffuser_attn_workspace_size.restype = st
+    lib.diffuser_diffuse_workspace_size.argtypes = [p, i32, i32, i32, i32, st,
+                                                    ctypes.POINTER(sz)]
+    lib.diffuser_diffuse_workspace_size.restype = st
     lib.diffuser_attn.argtypes = [p, p, p, st, i32, i32, i32, i32, p, i32, ctypes.c_float, p, p,
                                   sz, p]
     lib.diffuser_attn.restype = st
@@ -324,6 +329,23 @@ def workspace_size(graph: Graph, B: int, H: int, d_h: int, d_v: int, dtype) -> i
     return int(out.value)
 
 
+def diffuse_workspace_size(graph: Graph, B: int, H: int, d_v: int, K: int, dtype) -> int:
+    """Workspace bytes of diffuse / diffuse_theta with K steps (0: none)."""
+    lib = load_library()
+    out = ctypes.c_size_t()
+    _check(lib.diffuser_diffuse_workspace_size(graph.handle, B, H, d_v, K, _dtype_code(dtype),
+                                               ctypes.byref(out)))
+    return int(out.value)
+
+
+def _diffuse_workspace(graph, v, K, workspace):
+    if workspace is None:
+        B, H, _, d_v = v.shape
+        need = diffuse_workspace_size(graph, B, H, d_v, K, v.dtype)
+        workspace = _torch().empty(max(need, 1), dtype=_torch().uint8, device=v.device)
+    return workspace
+
+
 def _check_bhnd(t, name, n):
     if not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.shape[2] != n:
         raise DiffuserError(1, f"{name} must be a contiguous CUDA tensor [B, H, n={n}, d]")
@@ -384,9 +406,7 @@ def diffuse(A, v, graph: Graph, K: int, alpha: float, out=None, workspace=None):
         raise DiffuserError(1, "A must be a contiguous CUDA tensor in the A layout")
     if out is None:
         out = torch.empty_like(v)
-    if workspace is None:
-        workspace = torch.empty(max(v.numel() * v.element_size() + 256, 1), dtype=torch.uint8,
-                                device=v.device)
+    workspace = _diffuse_workspace(graph, v, K, workspace)
     lib = load_library()
     _check(lib.diffuser_diffuse(A.data_ptr(), v.data_ptr(), _dtype_code(v.dtype), B, H, d_v,
                                 graph.handle, K, float(alpha), out.data_ptr(),
@@ -433,10 +453,8 @@ def diffuse_theta(A, v, graph: Graph, theta, out=None, workspace=None):
         raise DiffuserError(1, "A must be a contiguous CUDA tensor in the A layout")
     if out is None:
         out = torch.empty_like(v)
-    if workspace is None:
-        workspace = torch.empty(max(v.numel() * v.element_size() + 256, 1), dtype=torch.uint8,
-                                device=v.device)
     th, K = _theta_array(theta)
+    workspace = _diffuse_workspace(graph, v, K, workspace)
     lib = load_library()
     _check(lib.diffuser_diffuse_theta(A.data_ptr(), v.data_ptr(), _dtype_code(v.dtype), B, H, d_v,
                                       graph.handle, K, th, out.data_ptr(), workspace.data_ptr(),

@@ -938,6 +938,17 @@ diffuser_status diffuser_scores_softmax(const void* Q, const void* K, diffuser_d
 
 namespace {
 
+// Workspace of diffuser_diffuse(_theta): the Z ping-pong buffer when there
+// are two or more steps, then the block-tile step's partial sums whenever a
+// diffusion step is launched (theta's nested form launches one even at
+// K_steps = 0).
+size_t diffuse_ws_need(const diffuser_graph* g, int32_t B, int32_t H, int32_t d_v,
+                       diffuser_dtype dtype, int32_t K_steps, bool theta) {
+    const size_t z_need = align_up((size_t)B * H * g->n * d_v * elem_size(dtype));
+    const bool launches = theta || K_steps >= 1;
+    return (K_steps >= 2 ? z_need : 0) + (launches ? part_bytes(g, B, H, d_v, dtype) : 0);
+}
+
 diffuser_status diffuse_impl(const void* A, const void* V, diffuser_dtype dtype, int32_t B,
                              int32_t H, int32_t d_v, const diffuser_graph* g, int32_t K_steps,
                              float alpha, const float* theta, void* Z, void* workspace,
@@ -954,8 +965,8 @@ diffuser_status diffuse_impl(const void* A, const void* V, diffuser_dtype dtype,
     const size_t vz_bytes = (size_t)B * H * g->n * d_v * es;
     const size_t a_bytes = (size_t)total_a_elems(g, B, H) * es;
     const size_t z_need = align_up(vz_bytes);
-    const size_t p_need = part_bytes(g, B, H, d_v, dtype);
-    const size_t ws_need = (K_steps >= 2 ? z_need : 0) + (K_steps >= 1 ? p_need : 0);
+    const size_t ws_need = diffuse_ws_need(g, B, H, d_v, dtype, K_steps, theta != nullptr);
+    const size_t p_need = ws_need - (K_steps >= 2 ? z_need : 0);
     if (ws_need > 0) {
         if (auto s = check_ptr(workspace, "workspace")) return s;
         if (ws_bytes < ws_need) return fail(DIFFUSER_ERR_INVALID_ARG, "workspace too small");
@@ -976,6 +987,17 @@ diffuser_status diffuse_impl(const void* A, const void* V, diffuser_dtype dtype,
 }
 
 }  // namespace
+
+diffuser_status diffuser_diffuse_workspace_size(const diffuser_graph* g, int32_t B, int32_t H,
+                                                int32_t d_v, int32_t K_steps, diffuser_dtype dtype,
+                                                size_t* bytes) {
+    g_last_error.clear();
+    if (!bytes) return fail(DIFFUSER_ERR_INVALID_ARG, "bytes is NULL");
+    if (auto s = check_shape(g, B, H, d_v, dtype, "d_v")) return s;
+    if (K_steps < 0) return fail(DIFFUSER_ERR_INVALID_ARG, "K_steps must be >= 0");
+    *bytes = diffuse_ws_need(g, B, H, d_v, dtype, K_steps, true);
+    return DIFFUSER_OK;
+}
 
 diffuser_status diffuser_diffuse(const void* A, const void* V, diffuser_dtype dtype, int32_t B,
                                  int32_t H, int32_t d_v, const diffuser_graph* g,

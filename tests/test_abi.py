@@ -69,6 +69,7 @@ def test_null_handles_rejected_on_host():
     lib = sah.load_library()
     size = ctypes.c_size_t()
     assert lib.diffuser_attn_workspace_size(None, 1, 1, 64, 64, 0, ctypes.byref(size)) == 1
+    assert lib.diffuser_diffuse_workspace_size(None, 1, 1, 64, 3, 0, ctypes.byref(size)) == 1
     assert lib.diffuser_graph_info(None, None, None, None, None) == 1
     lib.diffuser_graph_destroy(None)
     assert lib.diffuser_attn(None, None, None, 0, 1, 1, 64, 64, None, 1, 0.1, None, None, 0,

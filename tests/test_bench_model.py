@@ -64,3 +64,21 @@ def test_multi_gpu_request_exits_with_message():
                        capture_output=True, text=True, timeout=120, cwd=root)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr and r.stdout == ""
+
+
+def test_cpu_baseline_legs(monkeypatch):
+    """The CPU baseline times the oracle on one thread and on every core the
+    process may use, stages apart, and reports that core count."""
+    from workloads import WORKLOADS, make_qkv
+    monkeypatch.setenv("OMP_NUM_THREADS", "2")
+    assert bench.host_cores() <= 2
+    w = WORKLOADS["small_f32"]
+    q, k, v = make_qkv(w)
+    out = bench.cpu_baseline(w, q, k, v, budget_s=0.01, max_pairs=1)
+    cores = bench.host_cores()
+    assert out["kind"] == "oracle" and out["unit"] == "edges/s" and out["cores"] == cores
+    assert out["one_thread"]["threads"] == 1 and out["one_thread"]["pairs"] == 1
+    assert out["all_cores"]["threads"] == cores and out["value"] == out["all_cores"]["value"]
+    for leg in (out["one_thread"], out["all_cores"]):
+        assert leg["value"] > 0
+        assert leg["score_softmax_s_per_pair"] > 0 and leg["diffusion_s_per_pair"] > 0

@@ -144,6 +144,51 @@ def test_block_scores_and_diffuse(orc, dt):
             pu.assert_z_close(z[bb, h], ref, dt, f"b={bb} h={h}")
 
 
+def test_block_diffuse_default_workspace(orc):
+    """Block graph with its global query blocks split over workgroups
+    (n = 1024, 5 global blocks): diffuse and diffuse_theta with the
+    workspace the query sizes, theta at K = 0 among them (one launch of the
+    block step, whose partial sums need the workspace), and the C ABI's
+    refusal of a NULL or short workspace for that launch."""
+    import ctypes
+    n, b, c, s, gb, B, H, d = 1024, 64, 3, 2, 5, 1, 2, 64
+    g = sah.build_block_graph(n, b, c, s, gb, 1, 37)
+    rp, cols = g.copy_csr(0)
+    q, k, v = _qkv((B, H, n, d), 41, torch.bfloat16)
+    A = sah.scores_softmax(q.to(DEV), k.to(DEV), g)
+    vd = v.to(DEV)
+    need0 = sah.diffuse_workspace_size(g, B, H, d, 0, torch.bfloat16)
+    assert need0 > 0, "the split global blocks need partial sums"
+    assert sah.diffuse_workspace_size(g, B, H, d, 5, torch.bfloat16) >= \
+        need0 + v.numel() * v.element_size()
+    A_h = A.double().cpu().numpy()
+    z5 = _as64(sah.diffuse(A, vd, g, 5, 0.1))
+    z0 = _as64(sah.diffuse_theta(A, vd, g, [1.0]))
+    z2 = _as64(sah.diffuse_theta(A, vd, g, [0.5, 0.3, 0.2]))
+    torch.cuda.synchronize()
+    for h in range(H):
+        off = g.a_offset(0, h, H)
+        Ah = A_h[off:off + g.slots[0]]
+        ref = orc.diffuse(Ah, _as64(v[0, h]), rp, cols, 5, 0.1)
+        pu.assert_z_close(z5[0, h], ref, "bf16", f"K=5 h={h}")
+        assert np.array_equal(z0[0, h], _as64(v[0, h])), f"theta [1] must give V, h={h}"
+        ref2 = orc.diffuse_theta(Ah, _as64(v[0, h]), rp, cols, [0.5, 0.3, 0.2])
+        pu.assert_z_close(z2[0, h], ref2, "bf16", f"theta K=2 h={h}", 2, 0.5)
+    lib = sah.load_library()
+    th = (ctypes.c_float * 1)(1.0)
+    out = torch.empty_like(vd)
+    ws = torch.empty(need0, dtype=torch.uint8, device=DEV)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for ptr, size in ((None, 0), (ws.data_ptr(), need0 - 256)):
+        st = lib.diffuser_diffuse_theta(A.data_ptr(), vd.data_ptr(), 1, B, H, d, g.handle, 0, th,
+                                        out.data_ptr(), ptr, size, stream)
+        assert st == 1, f"workspace {size} bytes: status {st}"
+    assert lib.diffuser_diffuse_theta(A.data_ptr(), vd.data_ptr(), 1, B, H, d, g.handle, 0, th,
+                                      out.data_ptr(), ws.data_ptr(), need0, stream) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out, vd)
+
+
 def test_block_theta(orc):
     """General coefficients (eq. S.6) through the block-tile diffusion."""
     n, b, c, s, gb, B, H, d = 256, 64, 3, 1, 1, 1, 2, 64

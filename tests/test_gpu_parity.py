@@ -370,6 +370,10 @@ FAST_CASES = [
     (64, 1, [], 3, 1, True, 2, 1),
     (1100, 50, [0, 1, 2, 700, 1099], 40, 3, True, 3, 1),
     (33, 2, [32], 40, 1, False, 1, 1),
+    # B * H a multiple of 8: the score kernel numbers its work items per XCD
+    # by (b, h); every pair is compared
+    (600, 16, [0, 300], 12, 1, False, 2, 4),
+    (520, 24, [0, 1, 519], 10, 4, False, 4, 4),
 ]
 
 
