@@ -652,6 +652,31 @@ def pin_block_draws_golden(o):
     assert blocks[0][0] == sorted([0] + want), (blocks[0][0], want)
 
 
+def pin_token_draws_golden(o):
+    """Random extras of the token graph straight from SplitMix64(seed 0)'s
+    first outputs (the golden file): draw t of row i of graph b uses the
+    counter ((b n + i) << 20) | t, so with seed = -(c << 20) gamma (mod 2^64)
+    the row whose packed index is c replays outputs 1, 2, 3 of seed 0. Each
+    output maps to column (u >> 32) n >> 32 and is kept unless it is in the
+    row's window, a global position or already taken, in draw order.
+    n = 1000, radius 20, global {431}, 2 extras: the outputs map to 883, 431
+    (global, skipped) and 26, so the row is its window, 26, 431 and 883.
+    Checked for row 0 of graph 0 (seed 0), row 1 of graph 0 and row 0 of
+    graph 1 (the two packings of a nonzero index)."""
+    u = [int(r[0], 16) for r in read_golden("splitmix64_seed0.txt")]
+    n, r, G = 1000, 20, [431]
+    cols = [((x >> 32) * n) >> 32 for x in u]
+    assert cols == [883, 431, 26], cols
+    gamma = 0x9E3779B97F4A7C15
+    for b, i in ((0, 0), (0, 1), (1, 0)):
+        c = b * n + i
+        seed = (-(c << 20) * gamma) % (1 << 64)
+        rp, cl = o.graph(n, r, G, 2, 2, False, seed)
+        row = csr_rows(rp[b], cl[b])[i].tolist()
+        want = sorted(set(range(0, i + r + 1)) | {26, 431, 883})
+        assert row == want, (b, i, row, want)
+
+
 def pin_dilated_example(o):
     for r, dl, pos, nb in read_golden("dilated_window.txt"):
         r, dl, i = int(r), int(dl), int(pos) - 1
@@ -691,5 +716,6 @@ ALL_PINS = [
     pin_theta_printed_coefficients, pin_theta_three_token, pin_theta_powers,
     pin_even_extras, pin_backward_finite_differences, pin_backward_special_cases,
     pin_bf16_rounding, pin_layer_identity, pin_block_graph_example, pin_block_graph_structure,
-    pin_block_random_uniform, pin_block_draws_golden, pin_dilated_example, pin_dilated_structure,
+    pin_block_random_uniform, pin_block_draws_golden, pin_token_draws_golden, pin_dilated_example,
+    pin_dilated_structure,
 ]

@@ -65,6 +65,12 @@ MUTANTS = [
      "const double* Zk = Zs;"),
     ("mix_shift", "z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;",
      "z = (z ^ (z >> 26)) * 0x94D049BB133111EBull;"),
+    ("draw_modulo_map", "uint64_t j = ((u >> 32) * (uint64_t)n) >> 32;",
+     "uint64_t j = u % (uint64_t)n;"),
+    ("draw_counter_shift", "uint64_t ctr = (((uint64_t)(b * n + i)) << 20) | (uint64_t)t;",
+     "uint64_t ctr = (((uint64_t)(b * n + i)) << 21) | (uint64_t)t;"),
+    ("draw_counter_row_major", "uint64_t ctr = (((uint64_t)(b * n + i)) << 20) | (uint64_t)t;",
+     "uint64_t ctr = (((uint64_t)(i * 8 + b)) << 20) | (uint64_t)t;"),
 ]
 
 
