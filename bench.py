@@ -46,8 +46,8 @@ COPY_BYTES = 1 << 29
 COPY_REPS = 10
 
 # Sources whose change invalidates the diffusion kernel's counter figures.
-DIFFUSION_SOURCES = ("diffuse_fast.hip", "mfma_util.h", "internal.h", "graph_build.hip")
-DIFFUSION_KERNEL = "k_diffuse_sched"
+DIFFUSION_SOURCES = ("diffuse_res.hip", "mfma_util.h", "internal.h", "graph_build.hip")
+DIFFUSION_KERNEL = "k_diffuse_res"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 TRAFFIC_FILE = "traffic_diffuse_step_{workload}.txt"
 

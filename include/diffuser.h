@@ -183,11 +183,16 @@ DIFFUSER_API diffuser_status diffuser_graph_copy_csr(const diffuser_graph* g, in
  * global row's columns in order; for any other row the window as 8-column
  * blocks from (lo & ~7), then the g globals in order (padding where a
  * global lies in the window or, when causal, above the row), then, for
- * n > 65536 only, its random columns in ascending order. For n <= 65536 the
- * random edges follow all row segments in schedule order: for each block of
- * 16 rows and each 512-key chunk, the block's random edges into the chunk,
- * by row and then column, two of one row per pair, 16 pairs per 32-slot
- * group. Synchronous on return. */
+ * n > 65536 only, its random columns in ascending order. The random edges
+ * of shorter sequences follow all row segments:
+ *  - n <= 4576: one area per block of 16 rows, in block order, of
+ *    8 * 16 * noct slots, noct = ceil(most random edges of the block's
+ *    rows / 8): random edge e (ascending column) of row m of the block at
+ *    ((e / 8) * 16 + m) * 8 + e % 8; the rest is padding;
+ *  - 4576 < n <= 65536: in schedule order: for each block of 16 rows and
+ *    each 512-key chunk, the block's random edges into the chunk, by row and
+ *    then column, two of one row per pair, 16 pairs per 32-slot group.
+ * Synchronous on return. */
 DIFFUSER_API diffuser_status diffuser_graph_copy_slots(const diffuser_graph* g, int32_t graph,
                                                        int32_t* slot_row_host,
                                                        int32_t* slot_col_host, void* stream);

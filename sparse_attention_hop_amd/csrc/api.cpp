@@ -67,6 +67,12 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_sched_row);
     hipFree(g->d_sched_j);
     hipFree(g->d_sched_k);
+    hipFree(g->d_sched_off);
+    hipFree(g->d_rkey);
+    hipFree(g->d_rb_oct);
+    hipFree(g->d_rb_roff);
+    hipFree(g->d_rb_cost);
+    hipFree(g->d_rb_cost_max);
     hipFree(g->d_col_ptr);
     hipFree(g->d_col_off_slots);
     hipFree(g->d_col_slot);
@@ -94,6 +100,12 @@ void free_graph_memory(diffuser_graph* g) {
     g->d_sched_row = nullptr;
     g->d_sched_j = nullptr;
     g->d_sched_k = nullptr;
+    g->d_sched_off = nullptr;
+    g->d_rkey = nullptr;
+    g->d_rb_oct = nullptr;
+    g->d_rb_roff = nullptr;
+    g->d_rb_cost = nullptr;
+    g->d_rb_cost_max = nullptr;
     g->d_col_ptr = nullptr;
     g->d_col_off_slots = nullptr;
     g->d_col_slot = nullptr;
@@ -190,6 +202,39 @@ diffuser_status check_ptr(const void* p, const char* name, bool need16 = true) {
     return DIFFUSER_OK;
 }
 
+// One diffusion step Zn = keep * c_i * (A Zk)_i + restart * V_i on the
+// fastest kernel that takes the graph and shape: block tiles (block graphs),
+// the resident channel slice, the LDS-streamed tiles (scheduled graphs up
+// to 2^16 keys), else the generic kernel.
+struct step_launcher {
+    enum kind_t { kBlock, kResident, kStreamed, kGeneric } kind;
+    const diffuser_graph* g;
+    attn_shape s;
+    const void* A;
+    const void* V;
+    float* part;
+    hipError_t operator()(const void* cur, void* dst, const float* row_scale, step_coefs kc,
+                          hipStream_t st) const {
+        switch (kind) {
+            case kBlock: return launch_block_diffuse(*g, s, A, cur, V, dst, row_scale, kc, part, st);
+            case kResident: return launch_diffuse_res(*g, s, A, cur, V, dst, row_scale, kc, st);
+            case kStreamed: return launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st);
+            default: return launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
+        }
+    }
+};
+
+step_launcher pick_step(const diffuser_graph* g, const attn_shape& s, const void* A, const void* V,
+                        float* part) {
+    step_launcher l{step_launcher::kGeneric, g, s, A, V, part};
+    if (aligned16(A)) {
+        if (fast_block_supported(*g, s)) l.kind = step_launcher::kBlock;
+        else if (res_diffuse_supported(*g, s)) l.kind = step_launcher::kResident;
+        else if (fast_diffuse_supported(*g, s)) l.kind = step_launcher::kStreamed;
+    }
+    return l;
+}
+
 // K diffusion steps from V into Z, ping-ponging with `tmp` so that the last
 // step writes Z.
 diffuser_status run_diffusion(const diffuser_graph* g, const attn_shape& s, const void* A,
@@ -201,16 +246,13 @@ diffuser_status run_diffusion(const diffuser_graph* g, const attn_shape& s, cons
         if (e != hipSuccess) return hip_fail(e, "copy of V into Z");
         return DIFFUSER_OK;
     }
-    const bool fast = fast_diffuse_supported(*g, s) && aligned16(A);
-    const bool blockwise = fast_block_supported(*g, s) && aligned16(A);
+    const step_launcher step = pick_step(g, s, A, V, part);
     const void* cur = V;
     for (int32_t k = 0; k < K_steps; ++k) {
         // Steps K-1, K-3, ... write Z; the others write tmp.
         void* dst = ((K_steps - 1 - k) % 2 == 0) ? Z : tmp;
         const step_coefs kc{1.0f - alpha, alpha};
-        hipError_t e = blockwise ? launch_block_diffuse(*g, s, A, cur, V, dst, row_scale, kc, part, st)
-                       : fast    ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st)
-                                 : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
+        hipError_t e = step(cur, dst, row_scale, kc, st);
         if (e != hipSuccess) return hip_fail(e, "diffusion step launch");
         cur = dst;
     }
@@ -226,8 +268,7 @@ diffuser_status run_diffusion_theta(const diffuser_graph* g, const attn_shape& s
                                     const float* row_scale, const void* V, void* Z, void* tmp,
                                     float* part, int32_t K_steps, const float* theta,
                                     hipStream_t st) {
-    const bool fast = fast_diffuse_supported(*g, s) && aligned16(A);
-    const bool blockwise = fast_block_supported(*g, s) && aligned16(A);
+    const step_launcher step = pick_step(g, s, A, V, part);
     const int32_t launches = K_steps == 0 ? 1 : K_steps;
     const void* cur = V;
     for (int32_t j = 0; j < launches; ++j) {
@@ -236,9 +277,7 @@ diffuser_status run_diffusion_theta(const diffuser_graph* g, const attn_shape& s
         const step_coefs kc = K_steps == 0 ? step_coefs{0.0f, theta[0]}
                               : j == 0     ? step_coefs{theta[K_steps], theta[k]}
                                            : step_coefs{1.0f, theta[k]};
-        hipError_t e = blockwise ? launch_block_diffuse(*g, s, A, cur, V, dst, row_scale, kc, part, st)
-                       : fast    ? launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st)
-                                 : launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
+        hipError_t e = step(cur, dst, row_scale, kc, st);
         if (e != hipSuccess) return hip_fail(e, "diffusion step launch");
         cur = dst;
     }
@@ -462,6 +501,10 @@ diffuser_status diffuser_build_graph_layout(const diffuser_graph_desc* desc, int
     g->seed = desc->seed;
     g->random_layout = layout;
     g->scheduled = n <= kMaxScheduledN;
+    g->rand_layout = !g->scheduled        ? diffuser_graph::RandLayout::kRow
+                     : n <= kMaxResidentN ? diffuser_graph::RandLayout::kOctet
+                                          : diffuser_graph::RandLayout::kGroup;
+    g->key_batches = ((g->rnd_width + 7) / 8 + kOctBatch - 1) / kOctBatch;
     hipGetDevice(&g->device);
 
     const int64_t rows = (int64_t)g->num_graphs * n;
@@ -493,8 +536,11 @@ diffuser_status diffuser_build_graph_layout(const diffuser_graph_desc* desc, int
         (e = dev_alloc(&d_deg, rows)) != hipSuccess ||
         (e = dev_alloc(&d_slots, rows)) != hipSuccess ||
         (e = dev_alloc(&d_status, 1)) != hipSuccess ||
-        (e = dev_alloc(&d_max, 3 * (size_t)g->num_graphs)) != hipSuccess ||
-        (e = dev_alloc(&d_gcount, (size_t)g->num_graphs * nrb)) != hipSuccess) {
+        (e = dev_alloc(&d_max, 4 * (size_t)g->num_graphs)) != hipSuccess ||
+        (e = dev_alloc(&d_gcount, (size_t)g->num_graphs * nrb)) != hipSuccess ||
+        (g->octet() &&
+         ((e = dev_alloc(&g->d_rb_oct, (size_t)g->num_graphs * nrb)) != hipSuccess ||
+          (e = dev_alloc(&g->d_rb_roff, (size_t)g->num_graphs * (nrb + 1))) != hipSuccess))) {
         hipFree(d_deg);
         hipFree(d_slots);
         hipFree(d_status);
@@ -529,9 +575,12 @@ diffuser_status diffuser_build_graph_layout(const diffuser_graph_desc* desc, int
          (e = launch_scan(nrb, g->num_graphs, d_gcount, g->d_grp_ptr, d_max + 2 * g->num_graphs,
                           st)) != hipSuccess))
         return hip_fail(e, "schedule count launch");
+    if (g->octet() && (e = launch_rb_octets(*g, d_max + 3 * g->num_graphs, st)) != hipSuccess)
+        return hip_fail(e, "random octet count launch");
     int32_t status = 0;
     std::vector<int64_t> maxes(3 * (size_t)g->num_graphs);
     std::vector<int64_t> last_e(g->num_graphs), last_s(g->num_graphs), last_g(g->num_graphs, 0);
+    g->octets.assign(g->num_graphs, 0);
     if ((e = hipMemcpyAsync(&status, d_status, sizeof(int32_t), hipMemcpyDeviceToHost, st)) !=
             hipSuccess ||
         (e = hipMemcpyAsync(maxes.data(), d_max, sizeof(int64_t) * 2 * g->num_graphs,
@@ -544,6 +593,9 @@ diffuser_status diffuser_build_graph_layout(const diffuser_graph_desc* desc, int
                                 sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess ||
             (g->scheduled &&
              (e = hipMemcpyAsync(&last_g[gr], g->d_grp_ptr + (int64_t)gr * (nrb + 1) + nrb,
+                                 sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess) ||
+            (g->octet() &&
+             (e = hipMemcpyAsync(&g->octets[gr], g->d_rb_roff + (int64_t)gr * (nrb + 1) + nrb,
                                  sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess))
             return hip_fail(e, "copy of edge counts");
     }
@@ -557,7 +609,9 @@ diffuser_status diffuser_build_graph_layout(const diffuser_graph_desc* desc, int
     g->slot_off.assign(g->num_graphs + 1, 0);
     g->grp_off.assign(g->num_graphs + 1, 0);
     for (int32_t gr = 0; gr < g->num_graphs; ++gr) {
-        g->slots[gr] = last_s[gr] + (int64_t)kGroupSlots * last_g[gr];
+        g->slots[gr] = last_s[gr] + (g->grouped() ? (int64_t)kGroupSlots * last_g[gr]
+                                     : g->octet() ? 8 * kRowBlock * g->octets[gr]
+                                                  : 0);
         g->col_off[gr + 1] = g->col_off[gr] + last_e[gr];
         g->slot_off[gr + 1] = g->slot_off[gr] + g->slots[gr];
         g->grp_off[gr + 1] = g->grp_off[gr] + last_g[gr];
@@ -574,7 +628,8 @@ diffuser_status diffuser_build_graph_layout(const diffuser_graph_desc* desc, int
                                                     : 1)) != hipSuccess ||
         (e = dev_alloc(&g->d_sched_row, (size_t)ngroups * 4)) != hipSuccess ||
         (e = dev_alloc(&g->d_sched_j, (size_t)ngroups * 16)) != hipSuccess ||
-        (e = dev_alloc(&g->d_sched_k, (size_t)ngroups * kGroupSlots)) != hipSuccess)
+        (e = dev_alloc(&g->d_sched_k, (size_t)ngroups * kGroupSlots)) != hipSuccess ||
+        (e = dev_alloc(&g->d_sched_off, (size_t)ngroups * 16)) != hipSuccess)
         return alloc_status(e, "device allocation of the columns");
     if ((e = hipMemcpyAsync(g->d_col_off, g->col_off.data(), sizeof(int64_t) * (g->num_graphs + 1),
                             hipMemcpyHostToDevice, st)) != hipSuccess ||
@@ -588,6 +643,18 @@ diffuser_status diffuser_build_graph_layout(const diffuser_graph_desc* desc, int
     if ((e = launch_fill(*g, st)) != hipSuccess) return hip_fail(e, "fill launch");
     if (g->scheduled && (e = launch_sched_fill(*g, st)) != hipSuccess)
         return hip_fail(e, "schedule fill launch");
+    if (g->octet()) {
+        // Tables of the resident-slice diffusion step; d_gcount (graphs x nrb
+        // int32) is free again and holds the row-block costs.
+        // 64 lanes x 8 uint32 entries per (row block, batch).
+        if ((e = dev_alloc(&g->d_rkey, (size_t)g->num_graphs * nrb * g->key_batches * 512)) !=
+                hipSuccess ||
+            (e = dev_alloc(&g->d_rb_cost, (size_t)g->num_graphs * (nrb + 1))) != hipSuccess ||
+            (e = dev_alloc(&g->d_rb_cost_max, (size_t)g->num_graphs)) != hipSuccess)
+            return alloc_status(e, "device allocation of the resident tables");
+        if ((e = launch_res_tables(*g, d_gcount, st)) != hipSuccess)
+            return hip_fail(e, "resident tables launch");
+    }
     if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "graph fill");
     guard.g = nullptr;
     *out = g;

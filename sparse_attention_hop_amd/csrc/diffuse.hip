@@ -124,9 +124,9 @@ GenericGraph generic_graph(const diffuser_graph& g) {
     gg.seg_ptr = g.d_seg_ptr;
     gg.slot_col = g.d_slot_col;
     gg.slot_off = g.d_slot_off;
-    gg.rnd = g.scheduled ? g.d_rnd : nullptr;
-    gg.rnd_cnt = g.scheduled ? g.d_rnd_cnt : nullptr;
-    gg.rslot = g.scheduled ? g.d_rslot : nullptr;
+    gg.rnd = g.rand_apart() ? g.d_rnd : nullptr;
+    gg.rnd_cnt = g.rand_apart() ? g.d_rnd_cnt : nullptr;
+    gg.rslot = g.rand_apart() ? g.d_rslot : nullptr;
     return gg;
 }
 

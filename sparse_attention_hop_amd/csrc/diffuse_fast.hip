@@ -560,7 +560,7 @@ void k_diffuse_sched(FastArgs a) {
 }  // namespace
 
 bool fast_diffuse_supported(const diffuser_graph& g, const attn_shape& s) {
-    if (!g.structured || !g.scheduled || s.dtype != DIFFUSER_BF16 || (s.d != 64 && s.d != 32))
+    if (!g.structured || !g.grouped() || s.dtype != DIFFUSER_BF16 || (s.d != 64 && s.d != 32))
         return false;
     for (int64_t x : g.slots)
         if (x >= (1ll << 31)) return false;

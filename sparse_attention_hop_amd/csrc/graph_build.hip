@@ -87,7 +87,7 @@ __host__ __device__ __forceinline__ int64_t round8(int64_t x) { return (x + 7) &
 
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int32_t R,
-            int32_t rnd_width, int32_t causal, int32_t scheduled, uint64_t seed, int32_t even,
+            int32_t rnd_width, int32_t causal, int32_t apart, uint64_t seed, int32_t even,
             int32_t* __restrict__ deg,
             int32_t* __restrict__ slots, int32_t* __restrict__ rnd,
             int32_t* __restrict__ rnd_cnt, int32_t* __restrict__ status) {
@@ -182,7 +182,7 @@ void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
         if (lane == 0) {
             rnd_cnt[row] = m;
             deg[row] = (int32_t)(wlen + (g - g_in) + m);
-            slots[row] = (int32_t)((hi - wb0) / 8 * 8 + 8 + round8(g) + (scheduled ? 0 : round8(m)));
+            slots[row] = (int32_t)((hi - wb0) / 8 * 8 + 8 + round8(g) + (apart ? 0 : round8(m)));
         }
         return;
     }
@@ -202,7 +202,7 @@ void k_draw(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
         rnd_cnt[row] = below;
         deg[row] = (int32_t)((i - lo + 1) + g_before + below);
         slots[row] = (int32_t)((i - wb0) / 8 * 8 + 8 + round8(g_before) +
-                               (scheduled ? 0 : round8(below)));
+                               (apart ? 0 : round8(below)));
     }
 }
 
@@ -248,9 +248,31 @@ void k_scan(int64_t n, const int32_t* __restrict__ deg, int64_t* __restrict__ ro
     }
 }
 
+// kOctet layout: slot_col / slot_row (and rslot, when given) of row i's
+// positions in its row block's octet area; positions past its cnt random
+// edges rr[0 .. cnt) are padding. A row i >= n (the last block's tail) has
+// only padding.
+__device__ void fill_octets(int64_t n, int64_t i, int32_t cnt, const int32_t* __restrict__ rr,
+                            int64_t rand_base, const int64_t* __restrict__ roff,
+                            const int32_t* __restrict__ oct, int32_t* __restrict__ scol,
+                            int32_t* __restrict__ srow, int32_t* __restrict__ rs, int lane) {
+    const int64_t rb = i / kRowBlock;
+    const int32_t m = (int32_t)(i % kRowBlock);
+    const int64_t base = rand_base + 128 * roff[rb];
+    const int32_t noct = oct[rb];
+    for (int32_t e = lane; e < 8 * noct; e += kWave) {
+        const int64_t slot = base + ((int64_t)(e >> 3) * 16 + m) * 8 + (e & 7);
+        const bool real = i < n && e < cnt;
+        scol[slot] = real ? rr[e] : -1;
+        srow[slot] = real ? (int32_t)i : -1;
+        if (real) rs[e] = (int32_t)slot;
+    }
+}
+
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
 void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int32_t rnd_width,
-            int32_t causal, int32_t scheduled, const int64_t* __restrict__ row_ptr,
+            int32_t causal, int32_t layout, int32_t nrb, const int64_t* __restrict__ rb_roff,
+            const int32_t* __restrict__ rb_oct, const int64_t* __restrict__ row_ptr,
             const int64_t* __restrict__ col_off, const int64_t* __restrict__ seg_ptr,
             const int64_t* __restrict__ slot_off, const int32_t* __restrict__ rnd,
             const int32_t* __restrict__ rnd_cnt, int32_t* __restrict__ col_idx,
@@ -271,6 +293,18 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
     const int64_t deg = rp[i + 1] - rp[i];
     const int64_t nslot = sp[i + 1] - sp[i];
     const int64_t last = causal ? i : n - 1;
+    const bool octet = layout == 2;
+    int32_t* gcol = slot_col + slot_off[gr];
+    int32_t* grow = slot_row + slot_off[gr];
+    const int64_t* roff = rb_roff + gr * (nrb + 1);
+    const int32_t* oct = rb_oct + gr * nrb;
+    int32_t* rs = rslot + row * (int64_t)rnd_width;
+    const int32_t* rr = rnd + row * (int64_t)rnd_width;
+    // The last row's wave also writes the padding of the rows past n in
+    // its block's octet area.
+    if (octet && i == n - 1)
+        for (int64_t v = n; v < (n + kRowBlock - 1) / kRowBlock * kRowBlock; ++v)
+            fill_octets(n, v, 0, rr, sp[n], roff, oct, gcol, grow, rs, lane);
 
     if (is_global(G, g, i)) {
         for (int64_t j = lane; j < nslot; j += kWave) {
@@ -279,6 +313,7 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
             rout[j] = j <= last ? (int32_t)i : -1;
         }
         if (lane == 0) row_info[row] = make_int4((int32_t)sp[i], 0, -1, 0);
+        if (octet) fill_octets(n, i, 0, rr, sp[n], roff, oct, gcol, grow, rs, lane);
         return;
     }
     const int64_t lo = i - r < 0 ? 0 : i - r;
@@ -291,7 +326,6 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
     const int32_t g_in = count_less(G, g, hi + 1) - g_before;
     const int64_t gseg = round8(causal ? g_before : g);
     const int32_t m = rnd_cnt[row];  // random columns kept in this row
-    const int32_t* rr = rnd + row * (int64_t)rnd_width;
     const int32_t r_before = count_less(rr, m, lo);
     const int64_t woff = g_before + r_before;
     if (lane == 0) row_info[row] = make_int4((int32_t)sp[i], (int32_t)wb0, (int32_t)wseg, (int32_t)gseg);
@@ -315,7 +349,7 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
         const int64_t pos = q + gx_less + (right ? wlen : 0);
         if (v <= last && pos < deg) out[pos] = (int32_t)v;
     }
-    // Row segment: window blocks, globals, then (unscheduled) randoms.
+    // Row segment: window blocks, globals, then (kRow layout) randoms.
     for (int64_t t = lane; t < wseg && t < nslot; t += kWave) {
         const int64_t j = wb0 + t;
         const bool in = j >= lo && j <= wend;
@@ -331,8 +365,8 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
         sout[wseg + t] = c;
         rout[wseg + t] = c >= 0 ? (int32_t)i : -1;
     }
-    if (scheduled) return;
-    int32_t* rs = rslot + row * (int64_t)rnd_width;
+    if (octet) fill_octets(n, i, m, rr, sp[n], roff, oct, gcol, grow, rs, lane);
+    if (layout != 0) return;   // random weights outside the row segment
     for (int64_t t = lane; wseg + gseg + t < nslot; t += kWave) {
         sout[wseg + gseg + t] = t < m ? rr[t] : -1;
         rout[wseg + gseg + t] = t < m ? (int32_t)i : -1;
@@ -349,6 +383,7 @@ void k_fill(int64_t n, int32_t r, const int32_t* __restrict__ G, int32_t g, int3
 struct SchedArgs {
     int64_t n;
     int32_t rnd_width, nrb;
+    int32_t octet;                 // kOctet layout (else kGroup)
     const int32_t* rnd;
     const int32_t* rnd_cnt;
     int32_t* counts;               // [graphs][nrb] (count pass)
@@ -361,6 +396,8 @@ struct SchedArgs {
     uint8_t* sched_row;            // [groups][16] pair rows
     uint16_t* sched_j;             // [groups][32] slot key rows (diffusion layout)
     uint16_t* sched_k;             // [groups][32] slot key rows (score layout)
+    uint16_t* sched_off;           // [groups][16] (kOctet) first slot of each pair in its
+                                   //   row block's octet area
     int32_t* slot_col;
     int32_t* slot_row;
     int32_t* rslot;
@@ -407,13 +444,20 @@ void k_sched(SchedArgs a) {
     int32_t p = 0;
     int32_t filled = -1;   // chunk table entries 0..filled are written
     int32_t* cptr = kFill ? a.grp_cptr + (gr * a.nrb + rb) * (int64_t)(a.nchunks + 1) : nullptr;
+    // kOctet: position e of this lane's row sits at slot 8 lane + (e / 8) *
+    // 128 + e % 8 of the block's octet area.
     while (true) {
         const int32_t cur = p < cnt ? rr[p] / kChunkRows : INT32_MAX;
         const int32_t c = wave_min(cur);
         if (c == INT32_MAX) break;
         int32_t k = p;
         while (k < cnt && rr[k] / kChunkRows == c) ++k;
-        const int32_t pairs = (k - p + 1) >> 1;
+        // Pairs cover edge positions [p - lead, k): in the octet layout a
+        // pair starts at an even position, so its two slots are one aligned
+        // 4-byte word of the row's octet, and the odd edge that opens a
+        // chunk is paired with a dummy before it.
+        const int32_t lead = a.octet ? (p & 1) : 0;
+        const int32_t pairs = k > p ? (k - p + lead + 1) >> 1 : 0;
         // Exclusive prefix of the pair counts over the lanes.
         int32_t incl = pairs;
 #pragma unroll
@@ -430,19 +474,28 @@ void k_sched(SchedArgs a) {
                 const int32_t pidx = pre + t;
                 const int64_t gg = gbase + g0 + pidx / 16;
                 const int32_t pig = pidx % 16;
-                const bool lone = p + 2 * t + 1 >= k;   // second slot is a dummy
-                a.sched_row[gg * 16 + pig] = (uint8_t)(lane | (lone ? 0x80 : 0));
+                const int32_t e0 = p - lead + 2 * t;        // the pair's first position
+                const bool first_dummy = e0 < p;
+                const bool second_dummy = e0 + 1 >= k;
+                a.sched_row[gg * 16 + pig] =
+                    (uint8_t)(lane | (first_dummy ? 0x40 : 0) | (second_dummy ? 0x80 : 0));
+                const int64_t gslot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16);
+                if (a.octet)
+                    a.sched_off[gg * 16 + pig] =
+                        (uint16_t)(8 * lane + (e0 >> 3) * 128 + (e0 & 7));
                 for (int h = 0; h < 2; ++h) {
-                    const int32_t kk = p + 2 * t + h;
-                    const bool real = kk < k;
+                    const int32_t kk = e0 + h;
+                    const bool real = kk >= p && kk < k;
                     const int32_t s = 2 * pig + h;
-                    const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
                     const uint32_t jr = real ? (uint32_t)(rr[kk] - c * kChunkRows) : kZeroRow;
                     a.sched_j[gg * kGroupSlots + sched_j_index(s)] = (uint16_t)key_row_code(jr);
                     a.sched_k[gg * kGroupSlots + s] = (uint16_t)score_row_code(jr);
-                    a.slot_col[soff + slot] = real ? rr[kk] : -1;
-                    a.slot_row[soff + slot] = real ? (int32_t)i : -1;
-                    if (real) a.rslot[row * (int64_t)a.rnd_width + kk] = (int32_t)slot;
+                    if (!a.octet) {
+                        const int64_t slot = gslot + s;
+                        a.slot_col[soff + slot] = real ? rr[kk] : -1;
+                        a.slot_row[soff + slot] = real ? (int32_t)i : -1;
+                        if (real) a.rslot[row * (int64_t)a.rnd_width + kk] = (int32_t)slot;
+                    }
                 }
             }
             // Dummy pairs that pad the chunk's last group.
@@ -450,13 +503,17 @@ void k_sched(SchedArgs a) {
                 const int64_t gg = gbase + g0 + pidx / 16;
                 const int32_t pig = pidx % 16;
                 a.sched_row[gg * 16 + pig] = (uint8_t)0xFF;
+                const int64_t gslot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16);
+                // Group layout: the dummy pair's slots are padding, written 0.
+                if (a.octet) a.sched_off[gg * 16 + pig] = 0;
                 for (int h = 0; h < 2; ++h) {
                     const int32_t s = 2 * pig + h;
-                    const int64_t slot = rand_base + (int64_t)kGroupSlots * (g0 + pidx / 16) + s;
                     a.sched_j[gg * kGroupSlots + sched_j_index(s)] = (uint16_t)key_row_code(kZeroRow);
                     a.sched_k[gg * kGroupSlots + s] = (uint16_t)score_row_code(kZeroRow);
-                    a.slot_col[soff + slot] = -1;
-                    a.slot_row[soff + slot] = -1;
+                    if (!a.octet) {
+                        a.slot_col[soff + gslot + s] = -1;
+                        a.slot_row[soff + gslot + s] = -1;
+                    }
                 }
             }
             // Chunks filled + 1 .. c start at this chunk's first group.
@@ -472,6 +529,81 @@ void k_sched(SchedArgs a) {
     if (!kFill && lane == 0) a.counts[gr * a.nrb + rb] = (int32_t)groups;
 }
 
+
+// Slot of key row k in the resident-slice layout of the diffusion step:
+// bit 2 of the row is flipped when bit 3 is set (an involution on every
+// aligned run of 16 rows), which puts the two 4-row halves of one
+// transposed read on different LDS bank groups.
+__host__ __device__ __forceinline__ uint32_t res_unit(uint32_t k) { return k ^ ((k >> 1) & 4u); }
+
+// Random octets of every row block of a kOctet graph: ceil(most random
+// edges of any of its rows / 8) (0 when every row is a global row).
+__global__ void k_rb_oct(int64_t n, int32_t nrb, const int32_t* __restrict__ rnd_cnt,
+                         int32_t* __restrict__ oct) {
+    const int32_t rb = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+    const int64_t gr = blockIdx.y;
+    if (rb >= nrb) return;
+    const int64_t r0 = (int64_t)rb * kRowBlock;
+    const int64_t r1 = r0 + kRowBlock < n ? r0 + kRowBlock : n;
+    int32_t mx = 0;
+    for (int64_t i = r0; i < r1; ++i) mx = max(mx, rnd_cnt[gr * n + i]);
+    oct[gr * nrb + rb] = (mx + 7) / 8;
+}
+
+// Key table of the resident-slice diffusion step, one thread per (row
+// block, batch, lane): the lane's 8 entries (see diffuser_graph::d_rkey) in
+// two 16-byte stores.
+__global__ void k_rkey(int64_t n, int32_t nrb, int32_t batches, int32_t rnd_width,
+                       uint32_t n_pad, const int32_t* __restrict__ rnd,
+                       const int32_t* __restrict__ rnd_cnt, uint32_t* __restrict__ rkey) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gr = blockIdx.y;
+    if (idx >= (int64_t)nrb * batches * kWave) return;
+    const int32_t l = (int32_t)(idx % kWave);
+    const int32_t b = (int32_t)((idx / kWave) % batches);
+    const int64_t rb = idx / ((int64_t)kWave * batches);
+    const int32_t kg = l >> 4, q = (l >> 2) & 3, j = l & 3;
+    const int32_t o = kOctBatch * b + j;
+    uint32_t w[8];
+    for (int32_t t = 0; t < 4; ++t) {
+        const int64_t i = rb * kRowBlock + 4 * t + ((kg + o) & 3);
+        for (int32_t h = 0; h < 2; ++h) {
+            const int32_t e = 8 * o + 4 * h + q;
+            uint32_t k = n_pad;
+            if (i < n) {
+                const int64_t row = gr * n + i;
+                if (e < rnd_cnt[row]) k = res_unit((uint32_t)rnd[row * rnd_width + e]);
+            }
+            w[2 * t + h] = 32u * k;
+        }
+    }
+    uint4* out = reinterpret_cast<uint4*>(rkey) + 2 * (gr * nrb * batches * kWave + idx);
+    out[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    out[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+// Per row block of every graph, for the resident-slice diffusion step's
+// work split: its cost (band steps, global-column steps and 4 products per
+// random octet, plus 2 for the restart and store; 0 when every row of the
+// block is a global row) into cost.
+__global__ void k_rb_cost(int64_t n, int32_t r, int32_t causal, int32_t g, int32_t nrb,
+                          const int32_t* __restrict__ G, const int32_t* __restrict__ oct,
+                          int32_t* __restrict__ cost) {
+    const int32_t rb = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+    const int64_t gr = blockIdx.y;
+    if (rb >= nrb) return;
+    const int64_t r0 = (int64_t)rb * kRowBlock;
+    const int64_t r1 = r0 + kRowBlock < n ? r0 + kRowBlock : n;
+    const int32_t gin = count_less(G, g, r1) - count_less(G, g, r0);
+    int32_t c = 0;
+    if (gin < r1 - r0) {
+        const int64_t lo = (r0 - r < 0 ? 0 : r0 - r) & ~31ll;
+        const int64_t hi = causal ? r1 - 1 : (r1 - 1 + r < n - 1 ? r1 - 1 + r : n - 1);
+        c = (int32_t)(((hi - lo) >> 5) + 1 + ((g + 31) >> 5) + 4 * oct[gr * nrb + rb] + 2);
+    }
+    cost[gr * nrb + rb] = c;
+}
+
 }  // namespace
 
 hipError_t launch_draw(const diffuser_graph& g, int32_t* deg, int32_t* slots, int32_t* status,
@@ -479,7 +611,7 @@ hipError_t launch_draw(const diffuser_graph& g, int32_t* deg, int32_t* slots, in
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
     hipLaunchKernelGGL(k_draw, grid, dim3(kWave * kWavesPerBlock), 0, st, g.n, g.radius,
                        g.d_global, g.num_global, g.num_random, g.rnd_width, g.causal,
-                       (int32_t)g.scheduled, g.seed, g.random_layout, deg, slots, g.d_rnd,
+                       (int32_t)g.rand_apart(), g.seed, g.random_layout, deg, slots, g.d_rnd,
                        g.d_rnd_cnt, status);
     return hipGetLastError();
 }
@@ -494,7 +626,9 @@ hipError_t launch_scan(int64_t n, int32_t num_graphs, const int32_t* counts, int
 hipError_t launch_fill(const diffuser_graph& g, hipStream_t st) {
     dim3 grid((unsigned)((g.n + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
     hipLaunchKernelGGL(k_fill, grid, dim3(kWave * kWavesPerBlock), 0, st, g.n, g.radius,
-                       g.d_global, g.num_global, g.rnd_width, g.causal, (int32_t)g.scheduled,
+                       g.d_global, g.num_global, g.rnd_width, g.causal,
+                       g.octet() ? 2 : g.grouped() ? 1 : 0,
+                       (int32_t)((g.n + kRowBlock - 1) / kRowBlock), g.d_rb_roff, g.d_rb_oct,
                        g.d_row_ptr, g.d_col_off, g.d_seg_ptr, g.d_slot_off, g.d_rnd,
                        g.d_rnd_cnt, g.d_col_idx, g.d_slot_col, g.d_slot_row, g.d_rslot,
                        reinterpret_cast<int4*>(g.d_row_info));
@@ -506,6 +640,7 @@ static SchedArgs sched_args(const diffuser_graph& g) {
     a.n = g.n;
     a.rnd_width = g.rnd_width;
     a.nrb = (int32_t)((g.n + kRowBlock - 1) / kRowBlock);
+    a.octet = g.octet() ? 1 : 0;
     a.rnd = g.d_rnd;
     a.rnd_cnt = g.d_rnd_cnt;
     a.grp_ptr = g.d_grp_ptr;
@@ -517,6 +652,7 @@ static SchedArgs sched_args(const diffuser_graph& g) {
     a.sched_row = reinterpret_cast<uint8_t*>(g.d_sched_row);
     a.sched_j = reinterpret_cast<uint16_t*>(g.d_sched_j);
     a.sched_k = g.d_sched_k;
+    a.sched_off = g.d_sched_off;
     a.slot_col = g.d_slot_col;
     a.slot_row = g.d_slot_row;
     a.rslot = g.d_rslot;
@@ -536,6 +672,32 @@ hipError_t launch_sched_fill(const diffuser_graph& g, hipStream_t st) {
     dim3 grid((unsigned)((a.nrb + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)g.num_graphs);
     hipLaunchKernelGGL(k_sched<true>, grid, dim3(kWave * kWavesPerBlock), 0, st, a);
     return hipGetLastError();
+}
+
+hipError_t launch_rb_octets(const diffuser_graph& g, int64_t* max_count, hipStream_t st) {
+    const int32_t nrb = (int32_t)((g.n + kRowBlock - 1) / kRowBlock);
+    dim3 grid((unsigned)((nrb + 255) / 256), (unsigned)g.num_graphs);
+    hipLaunchKernelGGL(k_rb_oct, grid, dim3(256), 0, st, g.n, nrb, g.d_rnd_cnt, g.d_rb_oct);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_scan(nrb, g.num_graphs, g.d_rb_oct, g.d_rb_roff, max_count, st);
+}
+
+hipError_t launch_res_tables(const diffuser_graph& g, int32_t* cost_tmp, hipStream_t st) {
+    const int32_t nrb = (int32_t)((g.n + kRowBlock - 1) / kRowBlock);
+    hipError_t e;
+    if (g.key_batches > 0) {
+        const int64_t items = (int64_t)nrb * g.key_batches * kWave;
+        dim3 grid((unsigned)((items + 255) / 256), (unsigned)g.num_graphs);
+        hipLaunchKernelGGL(k_rkey, grid, dim3(256), 0, st, g.n, nrb, g.key_batches, g.rnd_width,
+                           (uint32_t)res_npad(g.n), g.d_rnd, g.d_rnd_cnt, g.d_rkey);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    dim3 cgrid((unsigned)((nrb + 255) / 256), (unsigned)g.num_graphs);
+    hipLaunchKernelGGL(k_rb_cost, cgrid, dim3(256), 0, st, g.n, g.radius, g.causal, g.num_global,
+                       nrb, g.d_global, g.d_rb_oct, cost_tmp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_scan(nrb, g.num_graphs, cost_tmp, g.d_rb_cost, g.d_rb_cost_max, st);
 }
 
 }  // namespace diffuser

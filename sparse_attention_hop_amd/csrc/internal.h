@@ -16,6 +16,18 @@ constexpr int32_t kChunkRows = 512;   // key rows per chunk of the random schedu
 constexpr int32_t kGroupSlots = 32;   // weight slots per schedule group
 constexpr uint32_t kZeroRow = kChunkRows;  // key row index of a dummy slot
 constexpr int64_t kMaxScheduledN = 1 << 16;
+// Largest n whose built graphs keep their random weights in per-row-block
+// octet areas (the resident-slice diffusion step's layout): a 16-channel
+// slice of every key row (32 bytes each, a zero row after the last) then
+// fits in LDS beside the 16 KB of global-row partial sums.
+constexpr int64_t kMaxResidentN = 4576;
+// Random octets per batch of the resident-slice step's key table (one
+// 16-byte load per lane covers a batch).
+constexpr int32_t kOctBatch = 4;
+
+// n rounded up to a multiple of 32: the slot of the zero row of the
+// resident-slice layout (every 32-key step of a row block stays below it).
+__host__ __device__ constexpr int64_t res_npad(int64_t n) { return (n + 31) & ~31ll; }
 
 // LDS placement of key row `row` (0..kChunkRows) in the score kernel's
 // layout, in 16-byte units: unit u of the row sits at unit (code ^ u) with
@@ -59,9 +71,10 @@ struct diffuser_graph {
 
     // Weight-slot layout (where the edge weights live in A), per graph:
     //  * row segments: seg_ptr [n + 1] row offsets (a global row: its
-    //    columns; any other row: window blocks then global columns);
-    //  * random area (built graphs): from seg_ptr[n], groups of kGroupSlots
-    //    slots in random-schedule order (below).
+    //    columns; any other row: window blocks then global columns, then,
+    //    for n > kMaxScheduledN, its random columns);
+    //  * random area (built graphs with n <= kMaxScheduledN): from
+    //    seg_ptr[n], laid out as the random layout below says.
     // slot_col / slot_row [slots] give each slot's edge, or -1 for padding
     // (weight 0). Imported graphs use their CSR as is (no random area).
     std::vector<int64_t> slots;     // [num_graphs]
@@ -82,15 +95,31 @@ struct diffuser_graph {
     // column (lo & ~7), window slots (-1 for a global row), global slots}.
     int32_t* d_row_info = nullptr;  // [num_graphs][n][4]
 
-    // Random schedule (built graphs with n <= kMaxScheduledN; larger graphs
-    // keep each row's random columns as a third row segment, ascending,
-    // padded to a multiple of 8). Rows form blocks of kRowBlock, key rows
-    // chunks of kChunkRows. For each (row block, chunk) the block's random
-    // edges with keys in the chunk are listed by row, two edges of one row
-    // per pair (a lone edge is paired with a dummy), 16 pairs per group in
-    // that order, pair p owning slots 2p and 2p + 1; a group's 32 weights
-    // occupy 32 consecutive slots of the random area.
+    // Random schedule (built graphs with n <= kMaxScheduledN). Rows form
+    // blocks of kRowBlock, key rows chunks of kChunkRows. For each (row
+    // block, chunk) the block's random edges with keys in the chunk are
+    // listed by row, two edges of one row per pair (a lone edge is paired
+    // with a dummy), 16 pairs per group in that order.
+    // Where the random weights live (rand_layout):
+    //  * kRow (graphs with n > kMaxScheduledN): in each row's segment, after
+    //    its global slots, ascending, padded to a multiple of 8;
+    //  * kGroup (kMaxResidentN < n <= kMaxScheduledN): after all row
+    //    segments, a group's 32 weights in 32 consecutive slots, pair p
+    //    owning slots 2p and 2p + 1;
+    //  * kOctet (n <= kMaxResidentN): after all row segments, one area per
+    //    row block of noct = ceil(max random edges of its rows / 8) octets,
+    //    starting at slot seg_ptr[n] + 128 * rb_roff[rb]: random edge e of
+    //    row m of the block at ((e / 8) * 16 + m) * 8 + e % 8, positions
+    //    past a row's edges (and rows past n) padding. A pair of the
+    //    schedule covers an even position e and e + 1 of one row (a dummy
+    //    slot is another edge's, or padding); sched_off gives its first slot.
+    enum class RandLayout { kRow, kGroup, kOctet };
     bool scheduled = false;
+    RandLayout rand_layout = RandLayout::kRow;
+    bool grouped() const { return rand_layout == RandLayout::kGroup; }
+    bool octet() const { return rand_layout == RandLayout::kOctet; }
+    // Random weights outside the row segments (found through d_rslot).
+    bool rand_apart() const { return rand_layout != RandLayout::kRow; }
     std::vector<int64_t> groups;    // [num_graphs]
     std::vector<int64_t> grp_off;   // [num_graphs + 1] prefix sums of groups
     int64_t* d_grp_off = nullptr;   // [num_graphs + 1]
@@ -98,15 +127,31 @@ struct diffuser_graph {
     int32_t* d_grp_cptr = nullptr;  // [num_graphs][nrb][nchunks + 1] first group (in the
                                     //   graph) of each key chunk of each row block
     uint32_t* d_sched_row = nullptr;// [groups][4]: byte p of word k = row (within the
-                                    //   block) of pair 4k + p, plus 0x80 when the
-                                    //   pair's second slot is a dummy; 0xFF for a
-                                    //   dummy pair
+                                    //   block) of pair 4k + p, plus 0x40 when the
+                                    //   pair's first slot is a dummy and 0x80 when
+                                    //   its second is; 0xFF for a dummy pair
+    uint16_t* d_sched_off = nullptr;// [groups][16] (kOctet): slot of pair p's first slot
+                                    //   within its row block's octet area
     uint32_t* d_sched_j = nullptr;  // [groups][16]: word 4k + a = key_row_code of the
                                     //   key row (within the chunk) of slot 8k + a (low
                                     //   half) and of slot 8k + 4 + a (high half);
                                     //   kZeroRow's code for a dummy
     uint16_t* d_sched_k = nullptr;  // [groups][32]: score_row_code of the key row of
                                     //   each slot, in slot order
+    // kOctet graphs (n <= kMaxResidentN):
+    int32_t* d_rb_oct = nullptr;    // [graphs][nrb]: random octets of each row block
+    int64_t* d_rb_roff = nullptr;   // [graphs][nrb + 1]: prefix sums of d_rb_oct
+    std::vector<int64_t> octets;    // [num_graphs]: random octets of each graph
+    // Resident-slice diffusion step's key table: for row block rb, batch
+    // b of kOctBatch octets, lane l = 16 kg + 4 q + j (64 lanes), 8 uint32
+    // entries t * 2 + h: 32 times the res_unit slot of the key of random
+    // edge 8 o + 4 h + q of row 4 t + ((kg + o) & 3) of the block, o =
+    // 4 b + j, or of the zero row res_npad(n) where there is none (the
+    // key row's byte offset in an LDS plane).
+    int32_t key_batches = 0;        // batches per row block: ceil(ceil(rnd_width / 8) / 4)
+    uint32_t* d_rkey = nullptr;     // [graphs][nrb][key_batches][64][8]
+    int64_t* d_rb_cost = nullptr;   // [graphs][nrb + 1]: prefix sums of row-block costs
+    int64_t* d_rb_cost_max = nullptr;  // [graphs]: largest row-block cost
 
     // Column index of the weight slots (built on first use by the backward
     // pass, under bw_mutex): for each graph, col_ptr [n + 1] and, from
@@ -151,6 +196,12 @@ hipError_t launch_sched_count(const diffuser_graph& g, int32_t* counts, hipStrea
 // Writes the random schedule, the random area's slot_col / slot_row and
 // d_rslot (needs d_grp_ptr, d_grp_off and the allocated schedule arrays).
 hipError_t launch_sched_fill(const diffuser_graph& g, hipStream_t st);
+// kOctet graphs: the random octets of every row block into d_rb_oct and
+// their prefix sums into d_rb_roff (max_count: [graphs] int64 scratch).
+hipError_t launch_rb_octets(const diffuser_graph& g, int64_t* max_count, hipStream_t st);
+// kOctet graphs: writes d_rkey and d_rb_cost (cost_tmp: [graphs][nrb]
+// int32 scratch).
+hipError_t launch_res_tables(const diffuser_graph& g, int32_t* cost_tmp, hipStream_t st);
 
 // --- compute (scores.hip, diffuse.hip) --------------------------------------
 // Graph arrays of the generic kernels (defined in vec.h).
@@ -190,6 +241,12 @@ struct step_coefs {
 hipError_t launch_diffuse_step(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
                                step_coefs k, hipStream_t st);
+// The same step on built graphs with a whole channel slice of Z_k resident
+// in LDS (bf16, d = 32 or 64, n up to about 4.5 K keys).
+bool res_diffuse_supported(const diffuser_graph& g, const attn_shape& s);
+hipError_t launch_diffuse_res(const diffuser_graph& g, const attn_shape& s, const void* A,
+                              const void* Zk, const void* V, void* Zn, const float* row_scale,
+                              step_coefs k, hipStream_t st);
 // The same step on built graphs (bf16, d = 64), LDS-streamed with MFMA.
 bool fast_diffuse_supported(const diffuser_graph& g, const attn_shape& s);
 hipError_t launch_diffuse_fast(const diffuser_graph& g, const attn_shape& s, const void* A,

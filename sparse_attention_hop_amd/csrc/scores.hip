@@ -180,12 +180,12 @@ template <typename T>
 __global__ __launch_bounds__(256)
 void k_zero_dummies(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ slot_off,
                     const int32_t* __restrict__ slot_col, const int64_t* __restrict__ seg_ptr,
-                    const int64_t* __restrict__ grp_off, T* __restrict__ A) {
+                    T* __restrict__ A) {
     const int32_t bh = blockIdx.y;
     const int32_t b = bh / H, h = bh - b * H;
     const int32_t gr = num_graphs == 1 ? 0 : b;
-    const int64_t base = seg_ptr[(int64_t)gr * (n + 1) + n];           // random area start
-    const int64_t len = kGroupSlots * (grp_off[gr + 1] - grp_off[gr]);  // its length
+    const int64_t base = seg_ptr[(int64_t)gr * (n + 1) + n];              // random area start
+    const int64_t len = slot_off[gr + 1] - slot_off[gr] - base;           // to the graph's end
     const int32_t* cols = slot_col + slot_off[gr] + base;
     T* Ab = A + a_block_offset(slot_off, num_graphs, H, b, h) + base;
     for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < len;
@@ -200,10 +200,10 @@ hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* Q,
     hipLaunchKernelGGL((k_scores_softmax<T, T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
                        generic_graph(g), s.H, s.B * s.H, static_cast<const T*>(Q),
                        static_cast<const T*>(K), static_cast<T*>(A), row_scale, scale_log2);
-    if (g.scheduled)
+    if (g.rand_apart())
         hipLaunchKernelGGL((k_zero_dummies<T>), dim3(64, (unsigned)(s.B * s.H)), dim3(256), 0, st,
                            g.n, s.H, g.num_graphs, g.d_slot_off, g.d_slot_col, g.d_seg_ptr,
-                           g.d_grp_off, static_cast<T*>(A));
+                           static_cast<T*>(A));
     return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@ constexpr int kBufBytes = (kChunkRows + 1) * kRowBytes;   // chunk + zero row
 constexpr int kTileRows = kWaves * kRowBlock;
 constexpr int kGrowRows = 32;
 constexpr int kMaxGlobal = 128;
-constexpr int kSGroupBytes = 80;                          // staged group: codes, pair rows
+constexpr int kSGroupBytes = 112;   // staged group: codes, pair rows, pair slot offsets
 constexpr int kStageGroups = 8;
 constexpr int kStageBytes = kStageGroups * kSGroupBytes;
 constexpr int kLdsBytes = 2 * kBufBytes + kMaxGlobal * (kRowBytes + 4) + kWaves * kStageBytes;
@@ -77,6 +77,11 @@ struct ScoreArgs {
     const int32_t* grp_cptr;    // [graphs][nrb][nchunks + 1]
     const uint32_t* sched_row;  // [groups][4]
     const uint16_t* sched_k;    // [groups][32]
+    const uint16_t* sched_off;  // [groups][16] pair's first slot in its block's octet area
+    const int32_t* rnd_cnt;     // [graphs][n] random edges of each row
+    const int32_t* rb_oct;      // [graphs][nrb] random octets of each row block (octet layout)
+    const int64_t* rb_roff;     // [graphs][nrb + 1] their prefix sums (octet layout)
+    int32_t octet;              // random weights in per-row-block octet areas (else groups)
     const uint16_t* Q;
     const uint16_t* K;
     uint16_t* A;
@@ -151,8 +156,12 @@ struct SLane {
     float ms;                  // m * scale_log2
     float sum, inv;            // sum of the weights, its inverse (normalised mode)
     int32_t band_lo, band_hi;
+    int32_t gr;                // graph of the (b, h) pair
+    uint32_t abase;            // first slot of the row block's octet area (octet layout)
+    uint32_t rbase;            // first slot of the random area
     const int32_t* cptr;
-    int64_t goff, rbase;
+    int64_t goff;
+    u32x2 po;                  // next chunk's pair slot offsets (octet layout)
     u32x4 pk;                  // next chunk's score codes, compact
     uint32_t pr;               // next chunk's pair rows, compact
     // Random groups put row 4 kg + e in element e of a lane's products:
@@ -233,29 +242,33 @@ __device__ __forceinline__ float pick4(float x0, float x1, float x2, float x3, b
 // One random group. The products are taken with the query rows as the
 // first operand: lane (kg, s16) holds, in element e of x0 (x1), the product
 // of row 4 kg + e with the key of slot 0 (1) of pair s16, whose row byte
-// (row, + 0x80 when the second slot is a dummy, 0xFF for a dummy pair) is
-// rb. The lane of kg = row / 4 owns the pair: two exponentials, one 4-byte
-// store of both weights at gdst (slot 2 s16 of the group), and the pair's
-// share of row 4 kg + e in racc[e]. A dummy pair is written by the lane of
-// kg = 0.
+// (row, + 0x40 / 0x80 when the first / second slot is a dummy, 0xFF for a
+// dummy pair) is rb. The lane of kg = row / 4 owns the pair: two
+// exponentials, the store of its weights at slot `dst` of the (b, h) block
+// of A, and the pair's share of row 4 kg + e in racc[e]. In the group layout
+// both slots are the group's own (a dummy slot, or a dummy pair, written
+// 0 by the lane of kg = 0): one 4-byte store. In the octet layout a dummy
+// slot is another edge's or padding, so only the real slots are stored.
 template <int P>
 __device__ __forceinline__ void random_group(SLane& t, const f32x4& x0, const f32x4& x1,
-                                             uint32_t rb, float scale_log2, uint16_t* gdst) {
-    const uint32_t r = rb & 0x7fu;
+                                             uint32_t rb, float scale_log2, uint16_t* Abh,
+                                             uint32_t dst, bool octet) {
+    const uint32_t r = rb & 0x3fu;
     const bool mine = (r >> 2) == (uint32_t)t.kg;
-    const bool two = mine && (rb & 0x80u) == 0;
+    const bool v0 = mine && (rb & 0x40u) == 0;
+    const bool v1 = mine && (rb & 0x80u) == 0;
     const bool b0 = (r & 1u) != 0, b1 = (r & 2u) != 0;
     const float y0 = pick4(x0[0], x0[1], x0[2], x0[3], b0, b1);
     const float y1 = pick4(x1[0], x1[1], x1[2], x1[3], b0, b1);
     float v;
     if (P == kPassMax) {
-        v = mine ? (two ? fmaxf(y0, y1) : y0) : -INFINITY;
+        v = fmaxf(v0 ? y0 : -INFINITY, v1 ? y1 : -INFINITY);
     } else {
         const float ms = pick4(t.ms4[0], t.ms4[1], t.ms4[2], t.ms4[3], b0, b1);
         float w0 = exp2f_fast(__builtin_fmaf(y0, scale_log2, -ms));
         float w1 = exp2f_fast(__builtin_fmaf(y1, scale_log2, -ms));
-        w0 = mine ? w0 : 0.0f;
-        w1 = two ? w1 : 0.0f;
+        w0 = v0 ? w0 : 0.0f;
+        w1 = v1 ? w1 : 0.0f;
         if (P == kPassSum) {
             v = w0 + w1;
         } else {
@@ -265,7 +278,14 @@ __device__ __forceinline__ void random_group(SLane& t, const f32x4& x0, const f3
                 w1 *= inv;
             }
             const uint32_t pw = to_bf16_pair(w0, w1);
-            if (mine || (rb == 0xffu && t.kg == 0)) *reinterpret_cast<uint32_t*>(gdst) = pw;
+            if (!octet) {
+                if (mine || (rb == 0xffu && t.kg == 0))
+                    *reinterpret_cast<uint32_t*>(Abh + dst) = pw;
+            } else if (v0 && v1) {
+                *reinterpret_cast<uint32_t*>(Abh + dst) = pw;
+            } else if (v0 || v1) {
+                Abh[dst + (v0 ? 0u : 1u)] = (uint16_t)(v0 ? pw : pw >> 16);
+            }
             if (P == kPassWriteNorm) return;
             v = add_pair(pw, 0.0f);   // fused mode: c_i is over the weights as stored
         }
@@ -334,6 +354,8 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
             t.pk = *reinterpret_cast<const u32x4*>(a.sched_k + (t.goff + n0) * kGroupSlots +
                                                    8 * lane);
             t.pr = a.sched_row[(t.goff + n0) * 4 + lane];
+            if (a.octet)
+                t.po = *reinterpret_cast<const u32x2*>(a.sched_off + (t.goff + n0) * 16 + 4 * lane);
         }
     }
 
@@ -351,14 +373,19 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
     // next chunk's loads and the weight stores among them).
     // A group's codes and row byte are read one group ahead.
     const int32_t nstaged = min(gcnt, kStageGroups);
+    // A pair's first slot: in the octet layout its row block's area base
+    // plus the staged offset, in the group layout slot 2 s16 of the group.
+    const bool octet = a.octet != 0;
     uint32_t codes_n = *reinterpret_cast<const uint32_t LDS_AS*>(stg + 4 * t.s16);
     uint32_t rb_n = *reinterpret_cast<const uint8_t LDS_AS*>(stg + 64 + t.s16);
+    uint32_t off_n = *reinterpret_cast<const uint16_t LDS_AS*>(stg + 80 + 2 * t.s16);
     for (int32_t k = 0; k < nstaged; ++k) {
-        const uint32_t codes = codes_n, rb = rb_n;
+        const uint32_t codes = codes_n, rb = rb_n, off = off_n;
         if (k + 1 < nstaged) {
             const char LDS_AS* o = stg + (k + 1) * kSGroupBytes;
             codes_n = *reinterpret_cast<const uint32_t LDS_AS*>(o + 4 * t.s16);
             rb_n = *reinterpret_cast<const uint8_t LDS_AS*>(o + 64 + t.s16);
+            off_n = *reinterpret_cast<const uint16_t LDS_AS*>(o + 80 + 2 * t.s16);
         }
         f32x4 x[2];
 #pragma unroll
@@ -368,8 +395,9 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
             k_operands(cur, code, (uint32_t)t.kg, k0, k1);
             x[h] = dots(t.q0, t.q1, k0, k1);
         }
-        random_group<P>(t, x[0], x[1], rb, a.scale_log2,
-                        Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 2 * t.s16);
+        const uint32_t dst = octet ? t.abase + off
+                                   : t.rbase + (uint32_t)(kGroupSlots * (g0 + k) + 2 * t.s16);
+        random_group<P>(t, x[0], x[1], rb, a.scale_log2, Abh, dst, octet);
     }
     for (int32_t k = nstaged; k < gcnt; ++k) {
         const int64_t gi = t.goff + g0 + k;
@@ -383,13 +411,15 @@ __device__ __forceinline__ void tile_chunk(SLane& t, const ScoreArgs& a, const u
             x[h] = dots(t.q0, t.q1, k0, k1);
         }
         const uint32_t rb = reinterpret_cast<const uint8_t*>(a.sched_row + gi * 4)[t.s16];
-        random_group<P>(t, x[0], x[1], rb, a.scale_log2,
-                        Abh + t.rbase + (int64_t)kGroupSlots * (g0 + k) + 2 * t.s16);
+        const uint32_t dst = octet ? t.abase + a.sched_off[gi * 16 + t.s16]
+                                   : t.rbase + (uint32_t)(kGroupSlots * (g0 + k) + 2 * t.s16);
+        random_group<P>(t, x[0], x[1], rb, a.scale_log2, Abh, dst, octet);
     }
     if (more && lane < 4 * ncnt) {
         char LDS_AS* d = stg + (lane >> 2) * kSGroupBytes;
         *reinterpret_cast<u32x4 LDS_AS*>(d + (lane & 3) * 16) = t.pk;
         *reinterpret_cast<uint32_t LDS_AS*>(d + 64 + (lane & 3) * 4) = t.pr;
+        if (octet) *reinterpret_cast<u32x2 LDS_AS*>(d + 80 + (lane & 3) * 8) = t.po;
     }
 }
 
@@ -433,6 +463,9 @@ __device__ __forceinline__ void stage_first(const SLane& t, const ScoreArgs& a,
                                                 8 * lane);
             *reinterpret_cast<uint32_t LDS_AS*>(d + 64 + (lane & 3) * 4) =
                 a.sched_row[(t.goff + g0) * 4 + lane];
+            if (a.octet)
+                *reinterpret_cast<u32x2 LDS_AS*>(d + 80 + (lane & 3) * 8) =
+                    *reinterpret_cast<const u32x2*>(a.sched_off + (t.goff + g0) * 16 + 4 * lane);
         }
     }
 }
@@ -448,6 +481,15 @@ __device__ void tile_pass(SLane& t, const ScoreArgs& a, const uint16_t* Kbh, uin
     char LDS_AS* stg = zg + gpad * (kRowBytes + 4) + wave * kStageBytes;
 
     random_begin<P>(t);
+    if ((P == kPassWriteFused || P == kPassWriteNorm) && a.octet && active && t.kg == 0) {
+        // Octet layout: the positions of the block's octet area past a row's
+        // random edges (every position of a global row or a row past n)
+        // belong to no pair of the schedule; they hold 0.
+        const int32_t noct = uniform_load(a.rb_oct + (int64_t)t.gr * a.nrb + t.r0w / kRowBlock);
+        const int32_t cnt = t.rok ? a.rnd_cnt[(int64_t)t.gr * a.n + t.i] : 0;
+        const uint32_t base = t.abase + 8u * (uint32_t)t.s16;
+        for (int32_t e = cnt; e < 8 * noct; ++e) Abh[base + (uint32_t)((e >> 3) * 128 + (e & 7))] = 0;
+    }
     stage_first(t, a, Kbh, lds, stg, active, wave, lane);
     full_barrier();
     if (active) tile_globals<P>(t, a, Abh, zg, gidx, gpad);
@@ -575,13 +617,14 @@ __device__ __forceinline__ void grow_merge(float (&v)[2], char LDS_AS* lds, int 
     lds_barrier();
 }
 
-// One instantiation per head width: the local copy's kd is a constant that
-// every (inlined) helper folds.
-template <int KD>
+// One instantiation per head width and random layout: the local copy's kd
+// and octet are constants that every (inlined) helper folds.
+template <int KD, bool kOctet>
 __global__ __launch_bounds__(kThreads)
 void k_scores_sched(ScoreArgs args) {
     ScoreArgs a = args;
     a.kd = KD;
+    a.octet = kOctet ? 1 : 0;
     extern __shared__ __align__(16) char lds_raw[];
     char LDS_AS* lds = (char LDS_AS*)lds_raw;
     const int lane = __lane_id();
@@ -710,7 +753,10 @@ void k_scores_sched(ScoreArgs args) {
     const int64_t rb = active ? t.r0w / kRowBlock : 0;
     t.cptr = a.grp_cptr + ((int64_t)gr * a.nrb + rb) * (a.nchunks + 1);
     t.goff = a.grp_off[gr];
-    t.rbase = a.seg_ptr[(int64_t)gr * (n + 1) + n];
+    t.rbase = (uint32_t)a.seg_ptr[(int64_t)gr * (n + 1) + n];
+    t.gr = gr;
+    t.abase = a.octet ? t.rbase + (uint32_t)(128 * a.rb_roff[(int64_t)gr * (a.nrb + 1) + rb]) : 0u;
+    t.po = u32x2{0u, 0u};
     t.pk = u32x4{0u, 0u, 0u, 0u};
     t.pr = 0u;
 
@@ -796,6 +842,11 @@ hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, cons
     a.grp_off = g.d_grp_off;
     a.grp_cptr = g.d_grp_cptr;
     a.sched_row = g.d_sched_row;
+    a.sched_off = g.d_sched_off;
+    a.rnd_cnt = g.d_rnd_cnt;
+    a.rb_oct = g.d_rb_oct;
+    a.rb_roff = g.d_rb_roff;
+    a.octet = g.octet() ? 1 : 0;
     a.sched_k = g.d_sched_k;
     a.Q = static_cast<const uint16_t*>(Q);
     a.K = static_cast<const uint16_t*>(K);
@@ -812,12 +863,14 @@ hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, cons
     a.per_xcd = a.bh_per_xcd > 0 ? a.bh_per_xcd * (a.tiles_per_bh + a.grow_per_bh)
                                  : (a.total_items + 7) / 8;
     // Dynamic LDS above 64 KB is enabled once per device and instantiation.
-    static int attr_device[2] = {-1, -1};
-    const int which = s.d == 64 ? 0 : 1;
-    const void* kern = s.d == 64 ? reinterpret_cast<const void*>(&k_scores_sched<64>)
-                                 : reinterpret_cast<const void*>(&k_scores_sched<32>);
+    static int attr_device[4] = {-1, -1, -1, -1};
+    const int which = (s.d == 64 ? 0 : 1) + (g.octet() ? 2 : 0);
+    const void* kerns[4] = {reinterpret_cast<const void*>(&k_scores_sched<64, false>),
+                            reinterpret_cast<const void*>(&k_scores_sched<32, false>),
+                            reinterpret_cast<const void*>(&k_scores_sched<64, true>),
+                            reinterpret_cast<const void*>(&k_scores_sched<32, true>)};
     if (attr_device[which] != g.device) {
-        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+        hipError_t e = hipFuncSetAttribute(kerns[which], hipFuncAttributeMaxDynamicSharedMemorySize,
                                            kLdsBytes);
         if (e != hipSuccess) return e;
         attr_device[which] = g.device;
@@ -825,12 +878,13 @@ hipError_t launch_scores_fast(const diffuser_graph& g, const attn_shape& s, cons
     const int gpad = (g.num_global + 31) & ~31;
     const size_t lds = (size_t)2 * kBufBytes + (size_t)gpad * (kRowBytes + 4) +
                        (size_t)kWaves * kStageBytes;
-    if (s.d == 64)
-        hipLaunchKernelGGL(k_scores_sched<64>, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
-                           lds, st, a);
-    else
-        hipLaunchKernelGGL(k_scores_sched<32>, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
-                           lds, st, a);
+    const dim3 grid((unsigned)(8 * a.per_xcd));
+    switch (which) {
+        case 0: hipLaunchKernelGGL((k_scores_sched<64, false>), grid, dim3(kThreads), lds, st, a); break;
+        case 1: hipLaunchKernelGGL((k_scores_sched<32, false>), grid, dim3(kThreads), lds, st, a); break;
+        case 2: hipLaunchKernelGGL((k_scores_sched<64, true>), grid, dim3(kThreads), lds, st, a); break;
+        default: hipLaunchKernelGGL((k_scores_sched<32, true>), grid, dim3(kThreads), lds, st, a); break;
+    }
     return hipGetLastError();
 }
 
