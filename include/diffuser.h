@@ -259,6 +259,23 @@ DIFFUSER_API diffuser_status diffuser_diffuse_workspace_size(const diffuser_grap
                                                              int32_t K_steps,
                                                              diffuser_dtype dtype, size_t* bytes);
 
+/* diffuser_diffuse without a workspace argument, for callers that cannot
+ * allocate device memory or pass one in (code under HIP graph capture,
+ * tight serving loops). Arguments, layouts and results as for
+ * diffuser_diffuse. The Z ping-pong buffer and the block step's partial
+ * sums live in a 64 MiB device array inside the library, one per GPU,
+ * held until the process ends; none of it needs to start at zero. A call
+ * whose diffuser_diffuse_workspace_size exceeds 64 MiB (K_steps >= 2 with
+ * B * H * n * d_v * element size above it) gets DIFFUSER_ERR_INVALID_ARG
+ * before any launch. The call allocates nothing. Calls that overlap on one
+ * GPU (on different streams, or from several threads) share that array
+ * and race; serialise them. */
+DIFFUSER_API diffuser_status diffuser_diffuse_noalloc(const void* A, const void* V,
+                                                      diffuser_dtype dtype, int32_t B, int32_t H,
+                                                      int32_t d_v, const diffuser_graph* g,
+                                                      int32_t K_steps, float alpha, void* Z,
+                                                      void* stream);
+
 /*
  * General diffusion coefficients ("Diffuser" notes, section 2.3, eq. S.6,
  * the series taken through A^K): Z = sum_{k=0..K_steps} theta[k] A^k V.

@@ -13,6 +13,7 @@ Functions mirror the C ABI names:
   scores_softmax  -> diffuser_scores_softmax
   diffuse         -> diffuser_diffuse
   diffuse_workspace_size -> diffuser_diffuse_workspace_size
+  diffuse_noalloc -> diffuser_diffuse_noalloc
   attn_backward   -> diffuser_attn_backward (+ _workspace_size)
   layer_forward   -> diffuser_layer_forward (+ _workspace_size)
   attn_theta      -> diffuser_attn_theta
@@ -44,7 +45,7 @@ ABI_SYMBOLS = (
     "diffuser_graph_copy_csr", "diffuser_graph_copy_slots", "diffuser_graph_destroy",
     "diffuser_attn_workspace_size",
     "diffuser_attn", "diffuser_scores_softmax", "diffuser_diffuse",
-    "diffuser_diffuse_workspace_size",
+    "diffuser_diffuse_workspace_size", "diffuser_diffuse_noalloc",
     "diffuser_attn_theta", "diffuser_diffuse_theta",
     "diffuser_attn_backward_workspace_size", "diffuser_attn_backward",
     "diffuser_layer_workspace_size", "diffuser_layer_forward",
@@ -124,6 +125,8 @@ def load_library(path: str = LIB_PATH):
     lib.diffuser_diffuse_workspace_size.argtypes = [p, i32, i32, i32, i32, st,
                                                     ctypes.POINTER(sz)]
     lib.diffuser_diffuse_workspace_size.restype = st
+    lib.diffuser_diffuse_noalloc.argtypes = [p, p, st, i32, i32, i32, p, i32, ctypes.c_float, p, p]
+    lib.diffuser_diffuse_noalloc.restype = st
     lib.diffuser_attn.argtypes = [p, p, p, st, i32, i32, i32, i32, p, i32, ctypes.c_float, p, p,
                                   sz, p]
     lib.diffuser_attn.restype = st
@@ -412,6 +415,23 @@ def diffuse(A, v, graph: Graph, K: int, alpha: float, out=None, workspace=None):
                                 graph.handle, K, float(alpha), out.data_ptr(),
                                 workspace.data_ptr(), workspace.numel(),
                                 ctypes.c_void_p(_stream_handle(v.device))))
+    return out
+
+
+def diffuse_noalloc(A, v, graph: Graph, K: int, alpha: float, out):
+    """diffuse() through the entry point that allocates nothing: its scratch
+    is a fixed device array inside the library (64 MiB per GPU); out must be
+    given."""
+    _check_bhnd(v, "v", graph.n)
+    _check_bhnd(out, "out", graph.n)
+    B, H, _, d_v = v.shape
+    if not A.is_cuda or not A.is_contiguous() or A.dtype != v.dtype or \
+            A.numel() != graph.a_numel(B, H) or out.shape != v.shape or out.dtype != v.dtype:
+        raise DiffuserError(1, "A, v and out must match the A layout and each other")
+    lib = load_library()
+    _check(lib.diffuser_diffuse_noalloc(A.data_ptr(), v.data_ptr(), _dtype_code(v.dtype), B, H,
+                                        d_v, graph.handle, K, float(alpha), out.data_ptr(),
+                                        ctypes.c_void_p(_stream_handle(v.device))))
     return out
 
 

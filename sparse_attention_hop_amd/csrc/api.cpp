@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1064,6 +1065,55 @@ diffuser_status diffuser_diffuse_workspace_size(const diffuser_graph* g, int32_t
     if (K_steps < 0) return fail(DIFFUSER_ERR_INVALID_ARG, "K_steps must be >= 0");
     *bytes = diffuse_ws_need(g, B, H, d_v, dtype, K_steps, true);
     return DIFFUSER_OK;
+}
+
+// Scratch of diffuser_diffuse_noalloc: a file-scope device array, one copy
+// per GPU that the library runs on, kept until the process ends. Host code
+// uses only the address hipGetSymbolAddress returns for it on each device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up once per device).
+diffuser_status scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(DIFFUSER_ERR_INTERNAL, "device index out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "address of the scratch array");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DIFFUSER_OK;
+}
+
+}  // namespace
+
+diffuser_status diffuser_diffuse_noalloc(const void* A, const void* V, diffuser_dtype dtype,
+                                         int32_t B, int32_t H, int32_t d_v,
+                                         const diffuser_graph* g, int32_t K_steps, float alpha,
+                                         void* Z, void* stream) {
+    g_last_error.clear();
+    if (auto s = check_shape(g, B, H, d_v, dtype, "d_v")) return s;
+    if (K_steps < 0) return fail(DIFFUSER_ERR_INVALID_ARG, "K_steps must be >= 0");
+    const size_t need = diffuse_ws_need(g, B, H, d_v, dtype, K_steps, false);
+    if (need > kNoAllocScratchBytes)
+        return fail(DIFFUSER_ERR_INVALID_ARG,
+                    "needs " + std::to_string(need) + " bytes of scratch; the allocation-free "
+                    "entry point holds " + std::to_string(kNoAllocScratchBytes));
+    void* ws = nullptr;
+    if (need > 0)
+        if (auto s = scratch_address(&ws)) return s;
+    return diffuse_impl(A, V, dtype, B, H, d_v, g, K_steps, alpha, nullptr, Z, ws,
+                        need > 0 ? kNoAllocScratchBytes : 0, stream);
 }
 
 diffuser_status diffuser_diffuse(const void* A, const void* V, diffuser_dtype dtype, int32_t B,

@@ -24,6 +24,8 @@ constexpr int64_t kMaxResidentN = 4576;
 // Random octets per batch of the resident-slice step's key table (one
 // 16-byte load per lane covers a batch).
 constexpr int32_t kOctBatch = 4;
+// Bytes of device scratch that diffuser_diffuse_noalloc holds per GPU.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
 
 // n rounded up to a multiple of 32: the slot of the zero row of the
 // resident-slice layout (every 32-key step of a row block stays below it).
