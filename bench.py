@@ -182,6 +182,84 @@ def read_traffic(workload):
     return float(fields["traffic_bytes_per_launch"])
 
 
+def write_kernel_summary(stats_dir, workload, command):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run (the
+    kernel_stats.csv under stats_dir) into profiles/kernels_<workload>.md."""
+    paths = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_stats.csv under {stats_dir}")
+    rows = []
+    with open(paths[0]) as f:
+        for r in csv.DictReader(f):
+            name = re.sub(r"\(.*$", "", r["Name"])
+            name = re.sub(r"^(void )?diffuser::\(anonymous namespace\)::", "", name)
+            if name.startswith("Cijk_"):
+                name = name.split("_MT")[0][:4] + "... (rocBLAS GEMM)"
+            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    from workloads import WORKLOADS
+    w = WORKLOADS[workload]
+    lines = [
+        f"# Kernel-time summary: {w.describe()}",
+        "",
+        "Command (repository root, one MI355X, `TMPDIR=/tmp`):",
+        "",
+        f"    {command}",
+        f"    python bench.py --workload {workload} --write-kernel-summary {stats_dir}",
+        "",
+        "| kernel | calls | mean (us) | min (us) | max (us) | share |",
+        "|---|---|---|---|---|---|",
+    ]
+    for name, calls, mean, lo, hi, pct in rows:
+        lines.append(f"| {name} | {calls} | {mean:.1f} | {lo:.1f} | {hi:.1f} | {pct:.2f}% |")
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def length_sweep(sah, torch, reps):
+    """The headline shape (batch 8, 12 heads, d 64, bf16, radius 64, the
+    first 64 positions global, 64 random per token, one graph per batch
+    element, K 5, alpha 0.1) at n = 1K .. 16K: one JSON line per n with the
+    diffusion step and the fused score pass (HIP events) and their rates
+    against 8 TB/s."""
+    from dataclasses import replace
+    from workloads import HEADLINE, WORKLOADS, make_qkv
+    base = WORKLOADS[HEADLINE]
+    dev = torch.device("cuda:0")
+    for n in (1024, 2048, 4096, 8192, 16384):
+        w = replace(base, name=f"mlm{n}_bf16", n=n)
+        g = sah.build_graph(w.n, w.radius, w.global_idx, w.num_random, w.num_graphs, w.causal,
+                            w.graph_seed)
+        q_h, k_h, v_h = make_qkv(w)
+        q, k, v = q_h.to(dev), k_h.to(dev), v_h.to(dev)
+        z = torch.empty_like(v)
+        ws = torch.empty(sah.workspace_size(g, w.B, w.H, w.d, w.d, q.dtype), dtype=torch.uint8,
+                         device=dev)
+        A = sah.scores_softmax(q, k, g)
+        t_diff = time_events(lambda: sah.diffuse(A, v, g, w.K, w.alpha, out=z, workspace=ws),
+                             reps, torch) / w.K
+        t_all = time_events(lambda: sah.attn(q, k, v, g, w.K, w.alpha, out=z, workspace=ws),
+                            reps, torch)
+        # The fused score pass: the whole path at K = 0, less its copy of V.
+        t_k0 = time_events(lambda: sah.attn(q, k, v, g, 0, w.alpha, out=z, workspace=ws),
+                           reps, torch)
+        t_copy = time_events(lambda: z.copy_(v), reps, torch)
+        score_b, diff_b = algorithmic_bytes(w, g, w.K)
+        t_score = t_k0 - t_copy
+        print(json.dumps({
+            "workload": w.name, "n": n, "diffusion_step_ms": t_diff,
+            "diffusion_frac_hbm": diff_b / w.K / (t_diff * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "score_softmax_fused_ms": t_score,
+            "score_frac_hbm": score_b / (t_score * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "attn_ms": t_all, "edges_per_s": g.edges(w.B, w.H) * w.K / (t_all * 1e-3),
+        }), flush=True)
+        del A, ws, q, k, v, z
+        g.close()
+        torch.cuda.empty_cache()
+
+
 def extras(sah, torch, w, g, q, k, v, ws, reps=5):
     """Mean milliseconds of the other entry points on the same inputs (not
     part of `value`): general coefficients (uniform over A^0 .. A^K), the
@@ -349,8 +427,18 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip timing the other entry points on the same workload")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--write-kernel-summary", metavar="STATS_DIR")
+    ap.add_argument("--summary-command", default="",
+                    help="the rocprofv3 command the stats came from (for the summary's header)")
+    ap.add_argument("--length-sweep", action="store_true",
+                    help="time the headline shape at n = 1K .. 16K (one JSON line per n)")
     args = ap.parse_args()
 
+    if args.write_kernel_summary:
+        from workloads import HEADLINE
+        write_kernel_summary(args.write_kernel_summary, args.workload or HEADLINE,
+                             args.summary_command)
+        return
     if args.write_traffic:
         from workloads import HEADLINE
         write_traffic(*args.write_traffic, args.workload or HEADLINE)
@@ -366,6 +454,11 @@ def main():
 
     import sparse_attention_hop_amd as sah
     from workloads import HEADLINE, WORKLOADS, make_qkv
+
+    if args.length_sweep:
+        torch.cuda.set_device(torch.device("cuda:0"))
+        length_sweep(sah, torch, max(3, args.steps // 4))
+        return
 
     w = WORKLOADS[args.workload or HEADLINE]
     dev = torch.device("cuda:0")

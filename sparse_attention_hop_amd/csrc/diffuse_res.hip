@@ -58,7 +58,7 @@ constexpr int kWave = 64;
 constexpr int kWaves = 16;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kLdsLimit = 160 * 1024;
-constexpr int kGlobItems = 16;     // global-row work items of a first row piece
+constexpr int kGlobItems = 16;     // most partial-sum slots of the global rows (key-part items)
 constexpr int kMaxGcolRegs = 2;    // global-column steps whose key rows stay in registers
 
 struct ResArgs {
@@ -540,24 +540,31 @@ void k_diffuse_res(ResArgs a) {
 // flight) whose planes fit beside the global rows' partial sums, or 0 when
 // none does.
 struct ResPlan {
-    int cb, ngb, lds, plane, red_off;
+    int cb, ngb, gslots, lds, plane, red_off;
 };
 
 ResPlan res_plan(const diffuser_graph& g, int d) {
-    ResPlan p{0, 0, 0, 0, 0};
+    ResPlan p{0, 0, 0, 0, 0, 0};
     const int64_t npad = res_npad(g.n);
     const int ngb = (g.num_global + 15) / 16;
     if (ngb > kGlobItems) return p;
     const int64_t plane = (npad + 1) * 32;   // the loader packs the planes back to back
     for (int cb = d / 16 > 2 ? 2 : d / 16; cb >= 1; cb >>= 1) {
-        const int64_t red = g.num_global > 0 ? (int64_t)kGlobItems * cb * 4 * kWave * 4 : 0;
-        if (plane * cb + red <= kLdsLimit) {
-            p.cb = cb;
-            p.ngb = ngb;
-            p.plane = (int)plane;
-            p.red_off = (int)(plane * cb);
-            p.lds = (int)(plane * cb + red);
-            return p;
+        // Partial-sum slots for the global rows' key parts: kGlobItems, or
+        // half as many (down to one per global row block) when that lets
+        // the planes fit.
+        for (int slots = kGlobItems; slots >= ngb && slots >= 1; slots >>= 1) {
+            const int64_t red = g.num_global > 0 ? (int64_t)slots * cb * 4 * kWave * 4 : 0;
+            if (plane * cb + red <= kLdsLimit) {
+                p.cb = cb;
+                p.ngb = ngb;
+                p.gslots = g.num_global > 0 ? slots : 0;
+                p.plane = (int)plane;
+                p.red_off = (int)(plane * cb);
+                p.lds = (int)(plane * cb + red);
+                return p;
+            }
+            if (g.num_global == 0) break;
         }
     }
     return p;
@@ -622,29 +629,30 @@ hipError_t launch_diffuse_res(const diffuser_graph& g, const attn_shape& s, cons
     a.plane = p.plane;
     a.red_off = p.red_off;
     a.batches = g.key_batches;
-    // Row pieces per (pair, slice): the fewest that keep the last round of
-    // workgroups (one per CU) at least 90 % full, else the best of 1..8.
+    // Row pieces per (pair, slice): the S in 1..8 that minimises the
+    // estimated time, rounds of workgroups (one per CU) times each
+    // workgroup's time, a fixed part (the slice load and its barrier, worth
+    // about kFixedBlocks row blocks of one wave) plus the row blocks of its
+    // busiest wave.
+    constexpr int64_t kFixedBlocks = 4;
     const int64_t units = (int64_t)s.B * s.H * a.nsl;
-    const int cus = device_cus(g.device);
+    const int64_t cus = device_cus(g.device);
     int best = 1;
-    double best_eff = 0.0;
+    int64_t best_cost = -1;
     for (int S = 1; S <= 8; ++S) {
         if (S > 1 && (int64_t)a.nrb < 16ll * S) break;
-        const double wgs = (double)(units * S);
-        const double eff = (wgs / cus) / std::ceil(wgs / cus);
-        if (eff >= 0.9) {
-            best = S;
-            break;
-        }
-        if (eff > best_eff + 1e-9) {
-            best_eff = eff;
+        const int64_t rounds = (units * S + cus - 1) / cus;
+        const int64_t per_wave = ((a.nrb + S - 1) / S + kWaves - 1) / kWaves;
+        const int64_t cost = rounds * (kFixedBlocks + per_wave);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
             best = S;
         }
     }
     a.S = best;
     // Key parts per global row block: a piece holds at most ceil(ngb / S)
-    // blocks, all of whose parts fit in the kGlobItems partial-sum slots.
-    a.ks = p.ngb > 0 ? kGlobItems / ((p.ngb + a.S - 1) / a.S) : 0;
+    // blocks, all of whose parts fit in the plan's partial-sum slots.
+    a.ks = p.ngb > 0 ? p.gslots / ((p.ngb + a.S - 1) / a.S) : 0;
     a.items = (int32_t)(units * a.S);
     a.per_xcd = (a.items + 7) / 8;
     a.slot_off = g.d_slot_off;
