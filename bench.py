@@ -191,8 +191,9 @@ def write_kernel_summary(stats_dir, workload, command):
     rows = []
     with open(paths[0]) as f:
         for r in csv.DictReader(f):
-            name = re.sub(r"\(.*$", "", r["Name"])
-            name = re.sub(r"^(void )?diffuser::\(anonymous namespace\)::", "", name)
+            name = r["Name"].replace("(anonymous namespace)::", "").replace("diffuser::", "")
+            name = re.sub(r"^void ", "", name)
+            name = re.sub(r"\(.*$", "", name)
             if name.startswith("Cijk_"):
                 name = name.split("_MT")[0][:4] + "... (rocBLAS GEMM)"
             rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3,

@@ -3,12 +3,13 @@
 Tolerances (on Z, against the double-precision oracle):
   fp32 storage: |z - z_ref| <= 1e-4 * max(|z_ref|, 1e-2)  (max relative error
                 1e-4 with a 1e-2 floor on the denominator);
-  bf16 storage: |z - z_ref| <= 2e-2 absolute at K = 5, alpha = 0.1 (the
-                workloads' setting). A and every Z_k are stored in bf16, so
-                rounding errors of up to 2^-8 relative enter at each of the
-                steps and decay by (1 - alpha) per later step: the error grows
-                with min(K, 1/alpha). For other (K, alpha) the bound scales by
-                max(1, min(K, 1/alpha) / 5).
+  bf16 storage: |z - z_ref| <= 2e-2 absolute for every (K, alpha). A and
+                every Z_k are stored in bf16, so rounding errors of up to
+                2^-8 relative enter at each step; with the row rescale c_i
+                each step's matrix is row-stochastic, so those errors average
+                out instead of compounding: at K = 10, alpha = 0 the worst
+                case measured is 0.6 of the bound
+                (test_bf16_long_diffusion_plain_bound).
 Edge-softmax rows: |sum_j A_ij - 1| <= 1e-5 (fp32), <= 2^-8 + 1e-6 (bf16,
 whose round-to-nearest-even step is at most 2^-8 relative per weight).
 """
@@ -30,8 +31,8 @@ def oracle_threads() -> int:
 
 
 def bf16_tolerance(K: int = 5, alpha: float = 0.1) -> float:
-    steps = min(K, 1.0 / alpha) if alpha > 0 else K
-    return BF16_ABS * max(1.0, steps / 5.0)
+    """The bf16 bound; the same for every (K, alpha)."""
+    return BF16_ABS
 
 
 def z_error(got: np.ndarray, ref: np.ndarray, dtype: str, K: int = 5, alpha: float = 0.1) -> float:
