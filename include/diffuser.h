@@ -300,6 +300,52 @@ DIFFUSER_API diffuser_status diffuser_diffuse_theta(const void* A, const void* V
                                        size_t ws_bytes, void* stream);
 
 /*
+ * Edge weights in CSR order. A_csr holds, for each (b, h) in row-major
+ * order, the weights of graph(b)'s edges in the order of its CSR
+ * (diffuser_graph_copy_csr: rows ascending, each row's columns ascending),
+ * nnz(graph(b)) values, the block of (b, h) starting at
+ * sum_{b' < b} H * nnz(graph(b')) + h * nnz(graph(b)); `dtype` elements,
+ * element aligned. This is the order in which the "Diffuser" notes write
+ * each row's neighbourhood: the softmax over N(i) (section 2.1,
+ * eqs. S.1-S.5) and the sum over N(i) of one diffusion step (section 2.4,
+ * eq. S.7). The entry points below compute exactly what
+ * diffuser_scores_softmax and diffuser_diffuse compute, with A moved
+ * between CSR order and the weight-slot layout by a permutation kernel
+ * (bits moved, no arithmetic).
+ *
+ * The first call on a graph builds its slot -> CSR map (4 bytes per slot,
+ * device memory owned by the graph, freed with it; built once, under a
+ * lock, synchronising `stream`); later calls enqueue only kernel launches.
+ * Graphs must have fewer than 2^31 edges each.
+ *
+ * diffuser_csr_workspace_size: bytes of workspace that both entry points
+ * accept for K_steps steps at width d: the weights in the slot layout
+ * (256-byte aligned), then what diffuser_diffuse needs.
+ * diffuser_scores_softmax_csr: scores and edge softmax into A_csr; the
+ * workspace (at least the slot-layout weights) receives the slot layout.
+ * A_csr must not overlap Q, K or the workspace.
+ * diffuser_diffuse_csr: K_steps diffusion steps with caller-given weights
+ * A_csr (rows need not sum to one); writes Z as diffuser_diffuse does.
+ * A_csr, V and Z must not overlap the workspace; Z not A_csr or V.
+ * Errors as for diffuser_diffuse; a smaller ws_bytes gives
+ * DIFFUSER_ERR_INVALID_ARG before any launch.
+ */
+DIFFUSER_API diffuser_status diffuser_csr_workspace_size(const diffuser_graph* g, int32_t B,
+                                                         int32_t H, int32_t d, int32_t K_steps,
+                                                         diffuser_dtype dtype, size_t* bytes);
+DIFFUSER_API diffuser_status diffuser_scores_softmax_csr(const void* Q, const void* K,
+                                                         diffuser_dtype dtype, int32_t B,
+                                                         int32_t H, int32_t d_h,
+                                                         const diffuser_graph* g, void* A_csr,
+                                                         void* workspace, size_t ws_bytes,
+                                                         void* stream);
+DIFFUSER_API diffuser_status diffuser_diffuse_csr(const void* A_csr, const void* V,
+                                                  diffuser_dtype dtype, int32_t B, int32_t H,
+                                                  int32_t d_v, const diffuser_graph* g,
+                                                  int32_t K_steps, float alpha, void* Z,
+                                                  void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Backward of diffuser_attn (the chain rule through the recurrence of
  * "Diffuser" notes section 2.4, eq. S.7, the edge softmax of section 2.1,
  * eqs. S.1-S.5, and the scores): given dZ = dL/dZ, writes dQ, dK, dV (the

@@ -47,6 +47,7 @@ ABI_SYMBOLS = (
     "diffuser_attn", "diffuser_scores_softmax", "diffuser_diffuse",
     "diffuser_diffuse_workspace_size", "diffuser_diffuse_noalloc",
     "diffuser_attn_theta", "diffuser_diffuse_theta",
+    "diffuser_csr_workspace_size", "diffuser_scores_softmax_csr", "diffuser_diffuse_csr",
     "diffuser_attn_backward_workspace_size", "diffuser_attn_backward",
     "diffuser_layer_workspace_size", "diffuser_layer_forward",
     "diffuser_status_string", "diffuser_last_error",
@@ -134,6 +135,13 @@ def load_library(path: str = LIB_PATH):
     lib.diffuser_scores_softmax.restype = st
     lib.diffuser_diffuse.argtypes = [p, p, st, i32, i32, i32, p, i32, ctypes.c_float, p, p, sz, p]
     lib.diffuser_diffuse.restype = st
+    lib.diffuser_csr_workspace_size.argtypes = [p, i32, i32, i32, i32, st, ctypes.POINTER(sz)]
+    lib.diffuser_csr_workspace_size.restype = st
+    lib.diffuser_scores_softmax_csr.argtypes = [p, p, st, i32, i32, i32, p, p, p, sz, p]
+    lib.diffuser_scores_softmax_csr.restype = st
+    lib.diffuser_diffuse_csr.argtypes = [p, p, st, i32, i32, i32, p, i32, ctypes.c_float, p, p,
+                                         sz, p]
+    lib.diffuser_diffuse_csr.restype = st
     lib.diffuser_attn_backward_workspace_size.argtypes = [p, i32, i32, i32, i32, st,
                                                           ctypes.POINTER(sz)]
     lib.diffuser_attn_backward_workspace_size.restype = st
@@ -432,6 +440,63 @@ def diffuse_noalloc(A, v, graph: Graph, K: int, alpha: float, out):
     _check(lib.diffuser_diffuse_noalloc(A.data_ptr(), v.data_ptr(), _dtype_code(v.dtype), B, H,
                                         d_v, graph.handle, K, float(alpha), out.data_ptr(),
                                         ctypes.c_void_p(_stream_handle(v.device))))
+    return out
+
+
+def csr_workspace_size(graph: Graph, B: int, H: int, d: int, K: int, dtype) -> int:
+    """Workspace bytes accepted by scores_softmax_csr and diffuse_csr."""
+    lib = load_library()
+    out = ctypes.c_size_t()
+    _check(lib.diffuser_csr_workspace_size(graph.handle, B, H, d, K, _dtype_code(dtype),
+                                           ctypes.byref(out)))
+    return int(out.value)
+
+
+def _csr_workspace(graph, B, H, d, K, dtype, device, workspace):
+    if workspace is None:
+        need = csr_workspace_size(graph, B, H, d, K, dtype)
+        workspace = _torch().empty(max(need, 1), dtype=_torch().uint8, device=device)
+    return workspace
+
+
+def scores_softmax_csr(q, k, graph: Graph, out=None, workspace=None):
+    """Edge-softmax weights in CSR order (1-D, (b, h) blocks of nnz each)."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k")):
+        _check_bhnd(t, nm, graph.n)
+    B, H, _, d_h = q.shape
+    if k.shape != q.shape or q.dtype != k.dtype:
+        raise DiffuserError(1, "q, k shapes/dtypes disagree")
+    if out is None:
+        out = torch.empty(graph.edges(B, H), dtype=q.dtype, device=q.device)
+    elif not out.is_cuda or not out.is_contiguous() or out.dtype != q.dtype or \
+            out.numel() != graph.edges(B, H):
+        raise DiffuserError(1, "out must be a contiguous CUDA tensor of the edges in CSR order")
+    workspace = _csr_workspace(graph, B, H, d_h, 0, q.dtype, q.device, workspace)
+    lib = load_library()
+    _check(lib.diffuser_scores_softmax_csr(q.data_ptr(), k.data_ptr(), _dtype_code(q.dtype), B,
+                                           H, d_h, graph.handle, out.data_ptr(),
+                                           workspace.data_ptr(), workspace.numel(),
+                                           ctypes.c_void_p(_stream_handle(q.device))))
+    return out
+
+
+def diffuse_csr(A_csr, v, graph: Graph, K: int, alpha: float, out=None, workspace=None):
+    """diffuse() with the weights given in CSR order."""
+    torch = _torch()
+    _check_bhnd(v, "v", graph.n)
+    B, H, _, d_v = v.shape
+    if not A_csr.is_cuda or not A_csr.is_contiguous() or A_csr.dtype != v.dtype or \
+            A_csr.numel() != graph.edges(B, H):
+        raise DiffuserError(1, "A_csr must be a contiguous CUDA tensor of the edges in CSR order")
+    if out is None:
+        out = torch.empty_like(v)
+    workspace = _csr_workspace(graph, B, H, d_v, K, v.dtype, v.device, workspace)
+    lib = load_library()
+    _check(lib.diffuser_diffuse_csr(A_csr.data_ptr(), v.data_ptr(), _dtype_code(v.dtype), B, H,
+                                    d_v, graph.handle, K, float(alpha), out.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel(),
+                                    ctypes.c_void_p(_stream_handle(v.device))))
     return out
 
 

@@ -78,6 +78,7 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_col_off_slots);
     hipFree(g->d_col_slot);
     hipFree(g->d_col_row);
+    hipFree(g->d_slot_csr);
     hipFree(g->d_bptr);
     hipFree(g->d_bcol);
     g->d_bptr = nullptr;
@@ -111,6 +112,7 @@ void free_graph_memory(diffuser_graph* g) {
     g->d_col_off_slots = nullptr;
     g->d_col_slot = nullptr;
     g->d_col_row = nullptr;
+    g->d_slot_csr = nullptr;
 }
 
 diffuser_status alloc_status(hipError_t e, const char* what) {
@@ -402,6 +404,32 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
     g->d_col_slot = d_slot;
     g->d_col_row = d_row;
     return DIFFUSER_OK;
+}
+
+// Builds the slot -> CSR position map (once, under bw_mutex) with one
+// kernel on `st`, then waits for it.
+diffuser_status ensure_slot_csr(diffuser_graph* g, hipStream_t st) {
+    std::lock_guard<std::mutex> lock(g->bw_mutex);
+    if (g->d_slot_csr != nullptr) return DIFFUSER_OK;
+    for (int64_t e : g->nnz)
+        if (e >= (1ll << 31))
+            return fail(DIFFUSER_ERR_INVALID_ARG, "CSR order needs fewer than 2^31 edges per graph");
+    int32_t* map = nullptr;
+    hipError_t e = dev_alloc(&map, (size_t)g->slot_off[g->num_graphs]);
+    if (e != hipSuccess) return alloc_status(e, "device allocation of the slot -> CSR map");
+    if ((e = launch_slot_csr(*g, map, st)) != hipSuccess ||
+        (e = hipStreamSynchronize(st)) != hipSuccess) {
+        hipFree(map);
+        return hip_fail(e, "slot -> CSR map build");
+    }
+    g->d_slot_csr = map;
+    return DIFFUSER_OK;
+}
+
+// Edges of all (b, h) blocks in CSR order.
+int64_t total_csr_elems(const diffuser_graph* g, int32_t B, int32_t H) {
+    if (g->num_graphs == 1) return (int64_t)B * H * g->nnz[0];
+    return (int64_t)H * g->col_off[g->num_graphs];
 }
 
 // Workspace of diffuser_layer_forward: the [B*n][3 H d] projection (reused
@@ -1131,6 +1159,75 @@ diffuser_status diffuser_diffuse_theta(const void* A, const void* V, diffuser_dt
                                        size_t ws_bytes, void* stream) {
     return diffuse_impl(A, V, dtype, B, H, d_v, g, K_steps, 0.0f, theta, Z, workspace, ws_bytes,
                         stream);
+}
+
+diffuser_status diffuser_csr_workspace_size(const diffuser_graph* g, int32_t B, int32_t H,
+                                            int32_t d, int32_t K_steps, diffuser_dtype dtype,
+                                            size_t* bytes) {
+    g_last_error.clear();
+    if (!bytes) return fail(DIFFUSER_ERR_INVALID_ARG, "bytes is NULL");
+    if (auto s = check_shape(g, B, H, d, dtype, "d")) return s;
+    if (K_steps < 0) return fail(DIFFUSER_ERR_INVALID_ARG, "K_steps must be >= 0");
+    *bytes = align_up((size_t)total_a_elems(g, B, H) * elem_size(dtype)) +
+             diffuse_ws_need(g, B, H, d, dtype, K_steps, false);
+    return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_scores_softmax_csr(const void* Q, const void* K, diffuser_dtype dtype,
+                                            int32_t B, int32_t H, int32_t d_h,
+                                            const diffuser_graph* g, void* A_csr,
+                                            void* workspace, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (auto s = check_shape(g, B, H, d_h, dtype, "d_h")) return s;
+    if (auto s = check_ptr(A_csr, "A_csr", false)) return s;
+    if (reinterpret_cast<uintptr_t>(A_csr) % elem_size(dtype))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "A_csr is not element aligned");
+    if (auto s = check_ptr(workspace, "workspace")) return s;
+    const size_t es = elem_size(dtype);
+    const size_t a_need = align_up((size_t)total_a_elems(g, B, H) * es);
+    if (ws_bytes < a_need) return fail(DIFFUSER_ERR_INVALID_ARG, "workspace too small");
+    const size_t csr_bytes = (size_t)total_csr_elems(g, B, H) * es;
+    const size_t qk_bytes = (size_t)B * H * g->n * d_h * es;
+    if (overlaps(A_csr, csr_bytes, workspace, a_need) || overlaps(A_csr, csr_bytes, Q, qk_bytes) ||
+        overlaps(A_csr, csr_bytes, K, qk_bytes))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "A_csr overlaps Q, K or the workspace");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (auto s = ensure_slot_csr(const_cast<diffuser_graph*>(g), st)) return s;
+    // The weights in the slot layout (in the workspace), then permuted.
+    if (auto s = diffuser_scores_softmax(Q, K, dtype, B, H, d_h, g, workspace, nullptr, 0, stream))
+        return s;
+    hipError_t e = launch_slots_csr_permute(*g, B, H, es, workspace, A_csr, true, st);
+    if (e != hipSuccess) return hip_fail(e, "slot -> CSR permutation launch");
+    return DIFFUSER_OK;
+}
+
+diffuser_status diffuser_diffuse_csr(const void* A_csr, const void* V, diffuser_dtype dtype,
+                                     int32_t B, int32_t H, int32_t d_v, const diffuser_graph* g,
+                                     int32_t K_steps, float alpha, void* Z, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (auto s = check_shape(g, B, H, d_v, dtype, "d_v")) return s;
+    if (auto s = check_alpha_k(K_steps, alpha)) return s;
+    if (auto s = check_ptr(A_csr, "A_csr", false)) return s;
+    if (reinterpret_cast<uintptr_t>(A_csr) % elem_size(dtype))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "A_csr is not element aligned");
+    if (auto s = check_ptr(workspace, "workspace")) return s;
+    const size_t es = elem_size(dtype);
+    const size_t a_need = align_up((size_t)total_a_elems(g, B, H) * es);
+    const size_t need = a_need + diffuse_ws_need(g, B, H, d_v, dtype, K_steps, false);
+    if (ws_bytes < need) return fail(DIFFUSER_ERR_INVALID_ARG, "workspace too small");
+    const size_t csr_bytes = (size_t)total_csr_elems(g, B, H) * es;
+    const size_t v_bytes = (size_t)B * H * g->n * d_v * es;
+    if (overlaps(A_csr, csr_bytes, workspace, need) || overlaps(V, v_bytes, workspace, need))
+        return fail(DIFFUSER_ERR_INVALID_ARG, "A_csr or V overlaps the workspace");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (auto s = ensure_slot_csr(const_cast<diffuser_graph*>(g), st)) return s;
+    // The weights into the slot layout at the workspace's start; the rest
+    // of it serves the diffusion steps.
+    hipError_t e = launch_slots_csr_permute(*g, B, H, es, A_csr, workspace, false, st);
+    if (e != hipSuccess) return hip_fail(e, "CSR -> slot permutation launch");
+    return diffuse_impl(workspace, V, dtype, B, H, d_v, g, K_steps, alpha, nullptr, Z,
+                        static_cast<char*>(workspace) + a_need, ws_bytes - a_need, stream);
 }
 
 

@@ -160,6 +160,9 @@ struct diffuser_graph {
     // col_off_slots[gr], the slot numbers (within the graph) of each column
     // by ascending row.
     std::mutex bw_mutex;
+    // CSR position (within its graph) of each slot's edge, -1 for padding
+    // (built on first use by the CSR-order entry points, under bw_mutex).
+    int32_t* d_slot_csr = nullptr;  // [slot_off[num_graphs]]
 
     // Block layout (graphs from diffuser_build_block_graph): every row of
     // query block I reads whole key blocks, listed (ascending, absolute
@@ -204,6 +207,16 @@ hipError_t launch_rb_octets(const diffuser_graph& g, int64_t* max_count, hipStre
 // kOctet graphs: writes d_rkey and d_rb_cost (cost_tmp: [graphs][nrb]
 // int32 scratch).
 hipError_t launch_res_tables(const diffuser_graph& g, int32_t* cost_tmp, hipStream_t st);
+
+// --- CSR order of A (csr_order.hip) ----------------------------------------
+// Writes map [slot_off[num_graphs]]: each slot's CSR position within its
+// graph, -1 for padding (graph CSR and slot arrays must be on the device).
+hipError_t launch_slot_csr(const diffuser_graph& g, int32_t* map, hipStream_t st);
+// Moves B * H blocks of es-byte weights (es = 2 or 4) between the slot
+// layout and CSR order through g.d_slot_csr: to_csr reads the slot layout
+// (padding ignored), otherwise writes it (padding 0).
+hipError_t launch_slots_csr_permute(const diffuser_graph& g, int32_t B, int32_t H, size_t es,
+                                    const void* src, void* dst, bool to_csr, hipStream_t st);
 
 // --- compute (scores.hip, diffuse.hip) --------------------------------------
 // Graph arrays of the generic kernels (defined in vec.h).

@@ -74,6 +74,11 @@ def test_null_handles_rejected_on_host():
     lib.diffuser_graph_destroy(None)
     assert lib.diffuser_attn(None, None, None, 0, 1, 1, 64, 64, None, 1, 0.1, None, None, 0,
                              None) == 1
+    assert lib.diffuser_csr_workspace_size(None, 1, 1, 64, 3, 0, ctypes.byref(size)) == 1
+    assert lib.diffuser_scores_softmax_csr(None, None, 0, 1, 1, 64, None, None, None, 0,
+                                           None) == 1
+    assert lib.diffuser_diffuse_csr(None, None, 0, 1, 1, 64, None, 3, 0.1, None, None, 0,
+                                    None) == 1
 
 
 def test_missing_library_fails_loudly(tmp_path):
