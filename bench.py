@@ -48,6 +48,18 @@ COPY_REPS = 10
 # Sources whose change invalidates the diffusion kernel's counter figures.
 DIFFUSION_SOURCES = ("diffuse_res.hip", "mfma_util.h", "internal.h", "graph_build.hip")
 DIFFUSION_KERNEL = "k_diffuse_res"
+
+
+def diffusion_kernel(w):
+    """The step kernel the library picks for a built graph of workload w:
+    the resident-slice kernel for bf16, d in {32, 64}, n <= 4576 (at most
+    256 globals); the LDS-streamed one for other bf16, d = 64 graphs up to
+    n = 65536; else the generic gather kernel."""
+    if w.dtype == "bf16" and w.d in (32, 64) and w.n <= 4576 and len(w.global_idx) <= 256:
+        return "k_diffuse_res"
+    if w.dtype == "bf16" and w.d == 64 and w.n <= 65536:
+        return "k_diffuse_sched"
+    return "k_diffuse_step"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 TRAFFIC_FILE = "traffic_diffuse_step_{workload}.txt"
 
@@ -532,7 +544,7 @@ def main():
             "alpha": w.alpha, "nnz_per_graph": g.nnz[0], "edges_per_pass": nnz_pass,
         },
         "roofline": {
-            "kernel": "diffusion step (" + DIFFUSION_KERNEL + ")",
+            "kernel": "diffusion step (" + diffusion_kernel(w) + ")",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

@@ -79,6 +79,8 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_col_slot);
     hipFree(g->d_col_row);
     hipFree(g->d_slot_csr);
+    hipFree(g->d_long_rows);
+    hipFree(g->d_long_off);
     hipFree(g->d_bptr);
     hipFree(g->d_bcol);
     g->d_bptr = nullptr;
@@ -113,6 +115,8 @@ void free_graph_memory(diffuser_graph* g) {
     g->d_col_slot = nullptr;
     g->d_col_row = nullptr;
     g->d_slot_csr = nullptr;
+    g->d_long_rows = nullptr;
+    g->d_long_off = nullptr;
 }
 
 diffuser_status alloc_status(hipError_t e, const char* what) {
@@ -406,6 +410,61 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
     return DIFFUSER_OK;
 }
 
+// Lists the graph's long rows (more than kLongRow slots) for the generic
+// kernels' long-row companions. Enqueued on `st`; synchronises it.
+diffuser_status build_long_rows(diffuser_graph* g, hipStream_t st) {
+    const int32_t G = g->num_graphs;
+    const int64_t n = g->n;
+    g->long_off.assign(G + 1, 0);
+    g->max_long = 0;
+    const int64_t bound = g->max_row_slots + (g->rand_apart() ? g->rnd_width : 0);
+    int32_t* flags = nullptr;
+    int64_t *offsets = nullptr, *dmax = nullptr;
+    hipError_t e;
+    struct tmp_guard {
+        void* p[3];
+        ~tmp_guard() {
+            for (void* q : p) hipFree(q);
+        }
+    };
+    std::vector<int64_t> totals(G, 0);
+    if (bound > kLongRow) {
+        if ((e = dev_alloc(&flags, (size_t)G * n)) != hipSuccess ||
+            (e = dev_alloc(&offsets, (size_t)G * (n + 1))) != hipSuccess ||
+            (e = dev_alloc(&dmax, (size_t)G)) != hipSuccess) {
+            hipFree(flags);
+            hipFree(offsets);
+            hipFree(dmax);
+            return alloc_status(e, "device allocation for the long-row list");
+        }
+    }
+    tmp_guard tmps{{flags, offsets, dmax}};
+    if (bound > kLongRow) {
+        if ((e = launch_long_flags(*g, flags, st)) != hipSuccess ||
+            (e = launch_scan(n, G, flags, offsets, dmax, st)) != hipSuccess)
+            return hip_fail(e, "long-row flag launch");
+        for (int32_t gr = 0; gr < G; ++gr)
+            if ((e = hipMemcpyAsync(&totals[gr], offsets + (int64_t)gr * (n + 1) + n,
+                                    sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess)
+                return hip_fail(e, "copy of long-row counts");
+        if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "long-row count");
+    }
+    for (int32_t gr = 0; gr < G; ++gr) {
+        g->long_off[gr + 1] = g->long_off[gr] + totals[gr];
+        g->max_long = std::max(g->max_long, totals[gr]);
+    }
+    if ((e = dev_alloc(&g->d_long_rows, (size_t)g->long_off[G])) != hipSuccess ||
+        (e = dev_alloc(&g->d_long_off, (size_t)G + 1)) != hipSuccess)
+        return alloc_status(e, "device allocation of the long-row list");
+    if ((e = hipMemcpyAsync(g->d_long_off, g->long_off.data(), sizeof(int64_t) * (G + 1),
+                            hipMemcpyHostToDevice, st)) != hipSuccess)
+        return hip_fail(e, "copy of long-row offsets");
+    if (g->max_long > 0 && (e = launch_long_fill(*g, flags, offsets, st)) != hipSuccess)
+        return hip_fail(e, "long-row fill launch");
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "long-row list");
+    return DIFFUSER_OK;
+}
+
 // Builds the slot -> CSR position map (once, under bw_mutex) with one
 // kernel on `st`, then waits for it.
 diffuser_status ensure_slot_csr(diffuser_graph* g, hipStream_t st) {
@@ -685,6 +744,7 @@ diffuser_status diffuser_build_graph_layout(const diffuser_graph_desc* desc, int
             return hip_fail(e, "resident tables launch");
     }
     if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "graph fill");
+    if (auto s = build_long_rows(g, st)) return s;
     guard.g = nullptr;
     *out = g;
     return DIFFUSER_OK;
@@ -780,6 +840,7 @@ diffuser_status diffuser_graph_from_csr(int64_t n, int32_t num_graphs, const int
                             st)) != hipSuccess)
         return hip_fail(e, "copy of the imported graph");
     if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(e, "graph import");
+    if (auto s = build_long_rows(g, st)) return s;
     guard.g = nullptr;
     *out = g;
     return DIFFUSER_OK;

@@ -12,6 +12,11 @@
 // of them (the step is bound by these dependent index and row loads); the
 // groups' partial sums are reduced at the end and the restart term is fused
 // into the store.
+// Long rows (more than kLongRow slots, a global row's n, say) are left to
+// a companion kernel that gives each one a workgroup of kLongWaves waves:
+// every wave sums a contiguous share of the row's slots as above, and the
+// waves' partial sums are added in wave order, so no wave walks a whole
+// long row and every sum keeps a fixed order.
 #include "internal.h"
 #include "vec.h"
 
@@ -21,38 +26,18 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kUnroll = 4;
+constexpr int kLongWaves = 16;
 
+// acc (lane group grp's share) += sum over slots [e0, e1) of the row,
+// group grp taking slots e0 + u EPI + grp of each step.
 template <typename T, int D>
-__global__ __launch_bounds__(kWave * kWavesPerBlock)
-void k_diffuse_step(GenericGraph gg, int32_t H, int32_t BH, const T* __restrict__ A,
-                    const T* __restrict__ Zk,
-                    const T* __restrict__ V, T* __restrict__ Zn,
-                    const float* __restrict__ row_scale, step_coefs kc) {
+__device__ __forceinline__ void gather_slots(const RowSlots& rs, const T* Ab, const T* Zb,
+                                             int64_t e0, int64_t e1, int grp,
+                                             float (&acc)[chunk<T>::kElems]) {
     constexpr int E = chunk<T>::kElems;
-    constexpr int L = D / E;
-    constexpr int EPI = kWave / L;
-    static_assert(L >= 1 && L <= kWave && (kWave % L) == 0, "unsupported head width");
-
-    const int wave = threadIdx.x / kWave;
-    const int lane = __lane_id();
-    const int64_t n = gg.n;
-    int64_t i;
-    int32_t bh;
-    if (!xcd_row_item<kWavesPerBlock>(n, BH, wave, i, bh)) return;
-    const int32_t b = bh / H, h = bh - b * H;
-    const int32_t gr = gg.num_graphs == 1 ? 0 : b;
-    const RowSlots rs = gg.row(gr, i);
-    const T* Ab = A + a_block_offset(gg.slot_off, gg.num_graphs, H, b, h);
-    const int64_t e1 = rs.count();
-    const int sub = lane % L, grp = lane / L;
-    const T* Zb = Zk + (int64_t)bh * n * D + sub * E;
-
-    float acc[E];
-#pragma unroll
-    for (int c = 0; c < E; ++c) acc[c] = 0.0f;
-    for (int64_t base = 0; base < e1; base += EPI * kUnroll) {
-        // Edges base + u EPI + grp, in order; padding and edges past the row
-        // read row 0 with weight 0.
+    constexpr int EPI = kWave / (D / E);
+    for (int64_t base = e0; base < e1; base += EPI * kUnroll) {
+        // Padding and slots past the range read row 0 with weight 0.
         int32_t j[kUnroll];
         int64_t slot[kUnroll];
 #pragma unroll
@@ -72,6 +57,37 @@ void k_diffuse_step(GenericGraph gg, int32_t H, int32_t BH, const T* __restrict_
 #pragma unroll
             for (int c = 0; c < E; ++c) acc[c] = fmaf(a[u], z[u][c], acc[c]);
     }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWave * kWavesPerBlock)
+void k_diffuse_step(GenericGraph gg, int32_t H, int32_t BH, const T* __restrict__ A,
+                    const T* __restrict__ Zk,
+                    const T* __restrict__ V, T* __restrict__ Zn,
+                    const float* __restrict__ row_scale, step_coefs kc) {
+    constexpr int E = chunk<T>::kElems;
+    constexpr int L = D / E;
+    static_assert(L >= 1 && L <= kWave && (kWave % L) == 0, "unsupported head width");
+
+    const int wave = threadIdx.x / kWave;
+    const int lane = __lane_id();
+    const int64_t n = gg.n;
+    int64_t i;
+    int32_t bh;
+    if (!xcd_row_item<kWavesPerBlock>(n, BH, wave, i, bh)) return;
+    const int32_t b = bh / H, h = bh - b * H;
+    const int32_t gr = gg.num_graphs == 1 ? 0 : b;
+    const RowSlots rs = gg.row(gr, i);
+    const int64_t e1 = rs.count();
+    if (e1 > kLongRow) return;   // k_diffuse_long's
+    const T* Ab = A + a_block_offset(gg.slot_off, gg.num_graphs, H, b, h);
+    const int sub = lane % L, grp = lane / L;
+    const T* Zb = Zk + (int64_t)bh * n * D + sub * E;
+
+    float acc[E];
+#pragma unroll
+    for (int c = 0; c < E; ++c) acc[c] = 0.0f;
+    gather_slots<T, D>(rs, Ab, Zb, 0, e1, grp, acc);
 #pragma unroll
     for (int off = L; off < kWave; off <<= 1) {
 #pragma unroll
@@ -80,6 +96,65 @@ void k_diffuse_step(GenericGraph gg, int32_t H, int32_t BH, const T* __restrict_
     if (grp == 0) {
         const int64_t o = ((int64_t)bh * n + i) * D + sub * E;
         float v[E];
+        chunk<T>::load(V + o, v);
+        const float keep =
+            row_scale == nullptr ? kc.keep : kc.keep * row_scale[(int64_t)bh * n + i];
+#pragma unroll
+        for (int c = 0; c < E; ++c) v[c] = keep * acc[c] + kc.restart * v[c];
+        chunk<T>::store(Zn + o, v);
+    }
+}
+
+// One long row per workgroup: long row blockIdx.x of the graph of pair
+// blockIdx.y.
+template <typename T, int D>
+__global__ __launch_bounds__(kWave * kLongWaves)
+void k_diffuse_long(GenericGraph gg, int32_t H, const T* __restrict__ A,
+                    const T* __restrict__ Zk, const T* __restrict__ V, T* __restrict__ Zn,
+                    const float* __restrict__ row_scale, step_coefs kc) {
+    constexpr int E = chunk<T>::kElems;
+    constexpr int L = D / E;
+    __shared__ float part[kLongWaves][D];
+    const int32_t bh = blockIdx.y;
+    const int32_t b = bh / H, h = bh - b * H;
+    const int32_t gr = gg.num_graphs == 1 ? 0 : b;
+    const int64_t li = gg.long_off[gr] + blockIdx.x;
+    if (li >= gg.long_off[gr + 1]) return;   // the whole workgroup
+    const int64_t n = gg.n;
+    const int64_t i = gg.long_rows[li];
+    const RowSlots rs = gg.row(gr, i);
+    const int wave = threadIdx.x / kWave;
+    const int lane = __lane_id();
+    const int64_t cnt = rs.count();
+    const int64_t e0 = cnt * wave / kLongWaves, e1 = cnt * (wave + 1) / kLongWaves;
+    const T* Ab = A + a_block_offset(gg.slot_off, gg.num_graphs, H, b, h);
+    const int sub = lane % L, grp = lane / L;
+    const T* Zb = Zk + (int64_t)bh * n * D + sub * E;
+
+    float acc[E];
+#pragma unroll
+    for (int c = 0; c < E; ++c) acc[c] = 0.0f;
+    gather_slots<T, D>(rs, Ab, Zb, e0, e1, grp, acc);
+#pragma unroll
+    for (int off = L; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int c = 0; c < E; ++c) acc[c] += __shfl_xor(acc[c], off);
+    }
+    if (grp == 0) {
+#pragma unroll
+        for (int c = 0; c < E; ++c) part[wave][sub * E + c] = acc[c];
+    }
+    __syncthreads();
+    if (threadIdx.x < L) {
+        const int s = threadIdx.x;
+        float v[E];
+#pragma unroll
+        for (int c = 0; c < E; ++c) {
+            float t = 0.0f;
+            for (int w = 0; w < kLongWaves; ++w) t += part[w][s * E + c];
+            acc[c] = t;
+        }
+        const int64_t o = ((int64_t)bh * n + i) * D + s * E;
         chunk<T>::load(V + o, v);
         const float keep =
             row_scale == nullptr ? kc.keep : kc.keep * row_scale[(int64_t)bh * n + i];
@@ -98,6 +173,11 @@ hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A,
                        generic_graph(g), s.H, s.B * s.H, static_cast<const T*>(A),
                        static_cast<const T*>(Zk), static_cast<const T*>(V),
                        static_cast<T*>(Zn), row_scale, kc);
+    if (g.max_long > 0)
+        hipLaunchKernelGGL((k_diffuse_long<T, D>), dim3((unsigned)g.max_long, (unsigned)(s.B * s.H)),
+                           dim3(kWave * kLongWaves), 0, st, generic_graph(g), s.H,
+                           static_cast<const T*>(A), static_cast<const T*>(Zk),
+                           static_cast<const T*>(V), static_cast<T*>(Zn), row_scale, kc);
     return hipGetLastError();
 }
 
@@ -127,6 +207,8 @@ GenericGraph generic_graph(const diffuser_graph& g) {
     gg.rnd = g.rand_apart() ? g.d_rnd : nullptr;
     gg.rnd_cnt = g.rand_apart() ? g.d_rnd_cnt : nullptr;
     gg.rslot = g.rand_apart() ? g.d_rslot : nullptr;
+    gg.long_rows = g.d_long_rows;
+    gg.long_off = g.d_long_off;
     return gg;
 }
 

@@ -27,8 +27,9 @@
 //    of all 16 rows with no lane idle: lane (m, kg) takes octet
 //    (m - kg) mod 4 of row m, which is exactly its operand in the one
 //    product of the batch it serves; in the other 15 it gives zeros. The
-//    keys of a batch come from the graph's key table, 16 bytes per lane,
-//    each quad of lanes holding 4 octets that a DPP broadcast hands round.
+//    keys of a batch come from the graph's key table in two loads of 16
+//    bytes per lane (each a contiguous kilobyte), each quad of lanes
+//    holding 4 octets that a DPP broadcast hands round.
 // Every weight load is a buffer load: a lane whose slots lie outside its
 // row's part is given an offset past the buffer and reads zeros, with no
 // branch; the step's own offset rides in the scalar offset. The next row
@@ -77,7 +78,7 @@ struct ResArgs {
     const int64_t* seg_ptr;        // [graphs][n + 1]
     const int4* row_info;          // [graphs][n]
     const int32_t* G;              // [g]
-    const uint32_t* rkey;          // [graphs][nrb][batches][64][8]
+    const uint32_t* rkey;          // [graphs][nrb][batches][2][64][4]
     const int32_t* rb_oct;         // [graphs][nrb]
     const int64_t* rb_roff;        // [graphs][nrb + 1]
     const int64_t* cost;           // [graphs][nrb + 1]
@@ -323,7 +324,7 @@ void k_diffuse_res(ResArgs a) {
     // every batch b, with octet jstar of its own row m.
     const uint32_t jstar = (uint32_t)(m - kg) & 3u, pstar = 4u * jstar + (uint32_t)(m >> 2);
     const uint32_t wv_lane = (jstar * 16u + (uint32_t)m) * 16u;   // bytes into a batch
-    const uint32_t kv_lane = 32u * (uint32_t)lane;
+    const uint32_t kv_lane = 16u * (uint32_t)lane;
 
     // Regular row blocks, software-pipelined: the loads of block rb + 1
     // are issued as soon as the registers they land in are free (its band
@@ -389,7 +390,7 @@ void k_diffuse_res(ResArgs a) {
         w = bload16(rA, (int32_t)(4 * b + (int32_t)jstar) < G.noct ? wv_lane : kOutside,
                     G.wsoff + 1024u * (uint32_t)b);
         kk = bload16(rK, b < G.nbat ? kv_lane : kOutside, G.ksoff + 2048u * (uint32_t)b);
-        kh = bload16(rK, b < G.nbat ? kv_lane + 16u : kOutside, G.ksoff + 2048u * (uint32_t)b);
+        kh = bload16(rK, b < G.nbat ? kv_lane + 1024u : kOutside, G.ksoff + 2048u * (uint32_t)b);
     };
     auto issue_rand = [&](const Geo& G) {
         rload(G, w0, k0, k0h, 0);

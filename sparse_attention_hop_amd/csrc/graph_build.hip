@@ -551,8 +551,9 @@ __global__ void k_rb_oct(int64_t n, int32_t nrb, const int32_t* __restrict__ rnd
 }
 
 // Key table of the resident-slice diffusion step, one thread per (row
-// block, batch, lane): the lane's 8 entries (see diffuser_graph::d_rkey) in
-// two 16-byte stores.
+// block, batch, lane): the lane's 8 entries (see diffuser_graph::d_rkey),
+// entries 0..3 in the batch's first kilobyte and 4..7 in its second, each
+// at 16 bytes times the lane.
 __global__ void k_rkey(int64_t n, int32_t nrb, int32_t batches, int32_t rnd_width,
                        uint32_t n_pad, const int32_t* __restrict__ rnd,
                        const int32_t* __restrict__ rnd_cnt, uint32_t* __restrict__ rkey) {
@@ -577,9 +578,9 @@ __global__ void k_rkey(int64_t n, int32_t nrb, int32_t batches, int32_t rnd_widt
             w[2 * t + h] = 32u * k;
         }
     }
-    uint4* out = reinterpret_cast<uint4*>(rkey) + 2 * (gr * nrb * batches * kWave + idx);
-    out[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    out[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    uint4* out = reinterpret_cast<uint4*>(rkey) + 2 * (gr * nrb * batches * kWave + idx - l);
+    out[l] = make_uint4(w[0], w[1], w[2], w[3]);
+    out[kWave + l] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
 // Per row block of every graph, for the resident-slice diffusion step's
@@ -620,6 +621,42 @@ hipError_t launch_scan(int64_t n, int32_t num_graphs, const int32_t* counts, int
                        int64_t* max_count, hipStream_t st) {
     hipLaunchKernelGGL(k_scan, dim3((unsigned)num_graphs), dim3(kScanThreads), 0, st, n, counts,
                        offsets, max_count);
+    return hipGetLastError();
+}
+
+// Long-row flags: row i of graph gr has seg_ptr[i + 1] - seg_ptr[i] slots
+// in its segment plus, when the random slots lie apart, rnd_cnt of them.
+__global__ void k_long_flags(int64_t n, const int64_t* __restrict__ seg_ptr,
+                             const int32_t* __restrict__ rnd_cnt, int32_t* __restrict__ flags) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gr = blockIdx.y;
+    if (i >= n) return;
+    const int64_t* sp = seg_ptr + gr * (n + 1);
+    const int64_t len = sp[i + 1] - sp[i] + (rnd_cnt != nullptr ? rnd_cnt[gr * n + i] : 0);
+    flags[gr * n + i] = len > kLongRow ? 1 : 0;
+}
+
+__global__ void k_long_fill(int64_t n, const int32_t* __restrict__ flags,
+                            const int64_t* __restrict__ offsets,
+                            const int64_t* __restrict__ long_off, int32_t* __restrict__ rows) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gr = blockIdx.y;
+    if (i >= n || flags[gr * n + i] == 0) return;
+    rows[long_off[gr] + offsets[gr * (n + 1) + i]] = (int32_t)i;
+}
+
+hipError_t launch_long_flags(const diffuser_graph& g, int32_t* flags, hipStream_t st) {
+    dim3 grid((unsigned)((g.n + 255) / 256), (unsigned)g.num_graphs);
+    hipLaunchKernelGGL(k_long_flags, grid, dim3(256), 0, st, g.n, g.d_seg_ptr,
+                       g.rand_apart() ? g.d_rnd_cnt : nullptr, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_long_fill(const diffuser_graph& g, const int32_t* flags,
+                            const int64_t* offsets, hipStream_t st) {
+    dim3 grid((unsigned)((g.n + 255) / 256), (unsigned)g.num_graphs);
+    hipLaunchKernelGGL(k_long_fill, grid, dim3(256), 0, st, g.n, flags, offsets, g.d_long_off,
+                       g.d_long_rows);
     return hipGetLastError();
 }
 

@@ -21,6 +21,10 @@ constexpr int64_t kMaxScheduledN = 1 << 16;
 // slice of every key row (32 bytes each, a zero row after the last) then
 // fits in LDS beside the 16 KB of global-row partial sums.
 constexpr int64_t kMaxResidentN = 4576;
+// Rows with more weight slots than this (a global row's n, say) are split
+// over the waves of one workgroup by the generic kernels' long-row
+// companions instead of walked by one wave.
+constexpr int64_t kLongRow = 1024;
 // Random octets per batch of the resident-slice step's key table (one
 // 16-byte load per lane covers a batch).
 constexpr int32_t kOctBatch = 4;
@@ -149,9 +153,11 @@ struct diffuser_graph {
     // entries t * 2 + h: 32 times the res_unit slot of the key of random
     // edge 8 o + 4 h + q of row 4 t + ((kg + o) & 3) of the block, o =
     // 4 b + j, or of the zero row res_npad(n) where there is none (the
-    // key row's byte offset in an LDS plane).
+    // key row's byte offset in an LDS plane). A batch's entries 0..3 of
+    // every lane come first (16 bytes per lane, by lane), then its
+    // entries 4..7, so each half is one contiguous kilobyte.
     int32_t key_batches = 0;        // batches per row block: ceil(ceil(rnd_width / 8) / 4)
-    uint32_t* d_rkey = nullptr;     // [graphs][nrb][key_batches][64][8]
+    uint32_t* d_rkey = nullptr;     // [graphs][nrb][key_batches][2][64][4]
     int64_t* d_rb_cost = nullptr;   // [graphs][nrb + 1]: prefix sums of row-block costs
     int64_t* d_rb_cost_max = nullptr;  // [graphs]: largest row-block cost
 
@@ -160,6 +166,13 @@ struct diffuser_graph {
     // col_off_slots[gr], the slot numbers (within the graph) of each column
     // by ascending row.
     std::mutex bw_mutex;
+    // Long rows (more than kLongRow weight slots, random slots included),
+    // ascending, per graph from long_off[gr]; the generic kernels' main
+    // pass skips them and a companion splits each over a workgroup.
+    std::vector<int64_t> long_off;  // [num_graphs + 1]
+    int64_t max_long = 0;           // most long rows in one graph
+    int32_t* d_long_rows = nullptr; // [long_off[num_graphs]]
+    int64_t* d_long_off = nullptr;  // [num_graphs + 1]
     // CSR position (within its graph) of each slot's edge, -1 for padding
     // (built on first use by the CSR-order entry points, under bw_mutex).
     int32_t* d_slot_csr = nullptr;  // [slot_off[num_graphs]]
@@ -207,6 +220,13 @@ hipError_t launch_rb_octets(const diffuser_graph& g, int64_t* max_count, hipStre
 // kOctet graphs: writes d_rkey and d_rb_cost (cost_tmp: [graphs][nrb]
 // int32 scratch).
 hipError_t launch_res_tables(const diffuser_graph& g, int32_t* cost_tmp, hipStream_t st);
+
+// Marks the long rows of every graph (flags [graphs][n] int32, 1 for a row
+// with more than kLongRow slots), then, once long_off and d_long_rows are
+// allocated from the flags' scan (offsets [graphs][n + 1]), lists them.
+hipError_t launch_long_flags(const diffuser_graph& g, int32_t* flags, hipStream_t st);
+hipError_t launch_long_fill(const diffuser_graph& g, const int32_t* flags,
+                            const int64_t* offsets, hipStream_t st);
 
 // --- CSR order of A (csr_order.hip) ----------------------------------------
 // Writes map [slot_off[num_graphs]]: each slot's CSR position within its

@@ -12,6 +12,9 @@
 // exponentials are exp2.
 // Pass 1 keeps an online (max, sum) per lane group; pass 2 recomputes the
 // scores and writes A in the storage type.
+// Long rows (more than kLongRow slots) are left to a companion kernel that
+// gives each one a workgroup of kLongWaves waves, each scoring a contiguous
+// share of the row; the waves' maxima and sums are merged in wave order.
 #include <type_traits>
 
 #include "internal.h"
@@ -23,6 +26,43 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kUnroll = 4;
+constexpr int kLongWaves = 16;
+
+// Dot products q . k_j of the slots base + u EPI + grp (u < kUnroll) of the
+// row that lie below e1, reduced over the group's L lanes; j[u] = -1 and
+// row 0 for padding, slot[u] = -1 past e1.
+template <typename T, int D>
+__device__ __forceinline__ void slot_dots(const RowSlots& rs, const T* Kb,
+                                          const float (&q)[chunk<T>::kElems], int64_t base,
+                                          int64_t e1, int grp, int32_t (&j)[kUnroll],
+                                          int64_t (&slot)[kUnroll], float (&dot)[kUnroll]) {
+    constexpr int E = chunk<T>::kElems;
+    constexpr int L = D / E;
+    constexpr int EPI = kWave / L;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t e = base + u * EPI + grp;
+        j[u] = -1;
+        slot[u] = e < e1 ? rs.slot(e, j[u]) : -1;
+    }
+    float k[kUnroll][E];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+        chunk<T>::load(Kb + (int64_t)(j[u] >= 0 ? j[u] : 0) * D, k[u]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        dot[u] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < E; ++c) dot[u] = fmaf(q[c], k[u][c], dot[u]);
+    }
+#pragma unroll
+    for (int off = 1; off < L; off <<= 1)
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) dot[u] += __shfl_xor(dot[u], off);
+}
+
+// (m, l) <- the online-softmax merge of (m, l) and (m2, l2).
+__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2);
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -49,38 +89,18 @@ void k_scores_softmax(GenericGraph gg, int32_t H, int32_t BH, const T* __restric
     const int32_t b = bh / H, h = bh - b * H;
     const int32_t gr = gg.num_graphs == 1 ? 0 : b;
     const RowSlots rs = gg.row(gr, i);
-    TA* Ab = A + a_block_offset(gg.slot_off, gg.num_graphs, H, b, h);
     const int64_t e1 = rs.count();
+    if (e1 > kLongRow) return;   // k_scores_long's
+    TA* Ab = A + a_block_offset(gg.slot_off, gg.num_graphs, H, b, h);
     const int sub = lane % L, grp = lane / L;
 
     float q[E];
     chunk<T>::load(Q + ((int64_t)bh * n + i) * D + sub * E, q);
     const T* Kb = K + (int64_t)bh * n * D + sub * E;
 
-    // Dot products of edges base + u EPI + grp (row 0 for padding and edges
-    // past the row), reduced over the group's lanes.
     auto dots = [&](int64_t base, int32_t (&j)[kUnroll], int64_t (&slot)[kUnroll],
                     float (&dot)[kUnroll]) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t e = base + u * EPI + grp;
-            j[u] = -1;
-            slot[u] = e < e1 ? rs.slot(e, j[u]) : -1;
-        }
-        float k[kUnroll][E];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            chunk<T>::load(Kb + (int64_t)(j[u] >= 0 ? j[u] : 0) * D, k[u]);
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            dot[u] = 0.0f;
-#pragma unroll
-            for (int c = 0; c < E; ++c) dot[u] = fmaf(q[c], k[u][c], dot[u]);
-        }
-#pragma unroll
-        for (int off = 1; off < L; off <<= 1)
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) dot[u] += __shfl_xor(dot[u], off);
+        slot_dots<T, D>(rs, Kb, q, base, e1, grp, j, slot, dot);
     };
 
     if (std::is_same<TA, float>::value && row_scale != nullptr) {
@@ -141,11 +161,7 @@ void k_scores_softmax(GenericGraph gg, int32_t H, int32_t BH, const T* __restric
     for (int off = L; off < kWave; off <<= 1) {
         const float m2 = __shfl_xor(m, off);
         const float l2 = __shfl_xor(l, off);
-        const float mn = fmaxf(m, m2);
-        const float a = m == -INFINITY ? 0.0f : l * fast_exp2(m - mn);
-        const float c = m2 == -INFINITY ? 0.0f : l2 * fast_exp2(m2 - mn);
-        l = a + c;
-        m = mn;
+        merge_ml(m, l, m2, l2);
     }
     const float inv = 1.0f / l;
 
@@ -171,6 +187,146 @@ void k_scores_softmax(GenericGraph gg, int32_t H, int32_t BH, const T* __restric
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) stored_sum += __shfl_xor(stored_sum, off);
         if (lane == 0) row_scale[(int64_t)bh * n + i] = 1.0f / stored_sum;
+    }
+}
+
+__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
+    const float mn = fmaxf(m, m2);
+    const float a = m == -INFINITY ? 0.0f : l * fast_exp2(m - mn);
+    const float c = m2 == -INFINITY ? 0.0f : l2 * fast_exp2(m2 - mn);
+    l = a + c;
+    m = mn;
+}
+
+// One long row per workgroup (long row blockIdx.x of the graph of pair
+// blockIdx.y): the same passes as k_scores_softmax, each wave over its
+// contiguous share of the row's slots, with the row's shift, maximum and
+// sums merged across the waves in wave order through LDS.
+template <typename T, typename TA, int D>
+__global__ __launch_bounds__(kWave * kLongWaves)
+void k_scores_long(GenericGraph gg, int32_t H, const T* __restrict__ Q, const T* __restrict__ K,
+                   TA* __restrict__ A, float* __restrict__ row_scale, float scale_log2) {
+    constexpr int E = chunk<T>::kElems;
+    constexpr int L = D / E;
+    constexpr int EPI = kWave / L;
+    __shared__ float red[2][kLongWaves];
+    const int32_t bh = blockIdx.y;
+    const int32_t b = bh / H, h = bh - b * H;
+    const int32_t gr = gg.num_graphs == 1 ? 0 : b;
+    const int64_t li = gg.long_off[gr] + blockIdx.x;
+    if (li >= gg.long_off[gr + 1]) return;   // the whole workgroup
+    const int64_t n = gg.n;
+    const int64_t i = gg.long_rows[li];
+    const RowSlots rs = gg.row(gr, i);
+    const int wave = threadIdx.x / kWave;
+    const int lane = __lane_id();
+    const int64_t cnt = rs.count();
+    const int64_t e0 = cnt * wave / kLongWaves, e1 = cnt * (wave + 1) / kLongWaves;
+    TA* Ab = A + a_block_offset(gg.slot_off, gg.num_graphs, H, b, h);
+    const int sub = lane % L, grp = lane / L;
+
+    float q[E];
+    chunk<T>::load(Q + ((int64_t)bh * n + i) * D + sub * E, q);
+    const T* Kb = K + (int64_t)bh * n * D + sub * E;
+    auto dots = [&](int64_t base, int32_t (&j)[kUnroll], int64_t (&slot)[kUnroll],
+                    float (&dot)[kUnroll]) {
+        slot_dots<T, D>(rs, Kb, q, base, e1, grp, j, slot, dot);
+    };
+    // Sum of one value per wave (lane 0's), in wave order, in every thread.
+    auto wave_sum = [&](float v) -> float {
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off);
+        if (lane == 0) red[0][wave] = v;
+        __syncthreads();
+        float t = 0.0f;
+        for (int w = 0; w < kLongWaves; ++w) t += red[0][w];
+        __syncthreads();
+        return t;
+    };
+
+    if (std::is_same<TA, float>::value && row_scale != nullptr) {
+        // The fused single pass, shifted by the row's own score.
+        float ks[E];
+        chunk<T>::load(Kb + i * D, ks);
+        float sii = 0.0f;
+#pragma unroll
+        for (int c = 0; c < E; ++c) sii = fmaf(q[c], ks[c], sii);
+#pragma unroll
+        for (int off = 1; off < L; off <<= 1) sii += __shfl_xor(sii, off);
+        const float ms = sii * scale_log2;
+        float total = 0.0f;
+        for (int64_t base = e0; base < e1; base += EPI * kUnroll) {
+            int32_t j[kUnroll];
+            int64_t slot[kUnroll];
+            float dot[kUnroll];
+            dots(base, j, slot, dot);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (slot[u] >= 0 && sub == 0) {
+                    const float a = j[u] >= 0 ? fast_exp2(dot[u] * scale_log2 - ms) : 0.0f;
+                    chunk<TA>::store1(Ab + slot[u], a);
+                    total += a;
+                }
+            }
+        }
+        total = wave_sum(total);
+        if (total < kSumLimit) {
+            if (threadIdx.x == 0) row_scale[(int64_t)bh * n + i] = 1.0f / total;
+            return;
+        }
+    }
+
+    float m = -INFINITY, l = 0.0f;
+    for (int64_t base = e0; base < e1; base += EPI * kUnroll) {
+        int32_t j[kUnroll];
+        int64_t slot[kUnroll];
+        float dot[kUnroll];
+        dots(base, j, slot, dot);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (j[u] >= 0) {
+                const float t = dot[u] * scale_log2;
+                const float mn = fmaxf(m, t);
+                l = l * fast_exp2(m - mn) + fast_exp2(t - mn);
+                m = mn;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = L; off < kWave; off <<= 1) {
+        const float m2 = __shfl_xor(m, off);
+        const float l2 = __shfl_xor(l, off);
+        merge_ml(m, l, m2, l2);
+    }
+    if (lane == 0) {
+        red[0][wave] = m;
+        red[1][wave] = l;
+    }
+    __syncthreads();
+    m = -INFINITY;
+    l = 0.0f;
+    for (int w = 0; w < kLongWaves; ++w) merge_ml(m, l, red[0][w], red[1][w]);
+    __syncthreads();
+    const float inv = 1.0f / l;
+
+    float stored_sum = 0.0f;
+    for (int64_t base = e0; base < e1; base += EPI * kUnroll) {
+        int32_t j[kUnroll];
+        int64_t slot[kUnroll];
+        float dot[kUnroll];
+        dots(base, j, slot, dot);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (slot[u] >= 0 && sub == 0) {
+                const float a = j[u] >= 0 ? fast_exp2(dot[u] * scale_log2 - m) * inv : 0.0f;
+                chunk<TA>::store1(Ab + slot[u], a);
+                stored_sum += chunk<TA>::round(a);
+            }
+        }
+    }
+    if (row_scale != nullptr) {
+        stored_sum = wave_sum(stored_sum);
+        if (threadIdx.x == 0) row_scale[(int64_t)bh * n + i] = 1.0f / stored_sum;
     }
 }
 
@@ -200,6 +356,11 @@ hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* Q,
     hipLaunchKernelGGL((k_scores_softmax<T, T, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
                        generic_graph(g), s.H, s.B * s.H, static_cast<const T*>(Q),
                        static_cast<const T*>(K), static_cast<T*>(A), row_scale, scale_log2);
+    if (g.max_long > 0)
+        hipLaunchKernelGGL((k_scores_long<T, T, D>), dim3((unsigned)g.max_long, (unsigned)(s.B * s.H)),
+                           dim3(kWave * kLongWaves), 0, st, generic_graph(g), s.H,
+                           static_cast<const T*>(Q), static_cast<const T*>(K),
+                           static_cast<T*>(A), row_scale, scale_log2);
     if (g.rand_apart())
         hipLaunchKernelGGL((k_zero_dummies<T>), dim3(64, (unsigned)(s.B * s.H)), dim3(256), 0, st,
                            g.n, s.H, g.num_graphs, g.d_slot_off, g.d_slot_col, g.d_seg_ptr,
@@ -226,6 +387,11 @@ hipError_t launch_f32_t(const diffuser_graph& g, const attn_shape& s, const void
     hipLaunchKernelGGL((k_scores_softmax<T, float, D>), grid, dim3(kWave * kWavesPerBlock), 0, st,
                        generic_graph(g), s.H, s.B * s.H, static_cast<const T*>(Q),
                        static_cast<const T*>(K), A, nullptr, scale_log2);
+    if (g.max_long > 0)
+        hipLaunchKernelGGL((k_scores_long<T, float, D>), dim3((unsigned)g.max_long, (unsigned)(s.B * s.H)),
+                           dim3(kWave * kLongWaves), 0, st, generic_graph(g), s.H,
+                           static_cast<const T*>(Q), static_cast<const T*>(K), A, nullptr,
+                           scale_log2);
     return hipGetLastError();
 }
 

@@ -132,6 +132,8 @@ struct GenericGraph {
     const int32_t* rnd;        // [graphs][n][rnd_width] (scheduled graphs, else null)
     const int32_t* rnd_cnt;    // [graphs][n]
     const int32_t* rslot;      // [graphs][n][rnd_width]
+    const int32_t* long_rows;  // rows with more than kLongRow slots, per graph from long_off
+    const int64_t* long_off;   // [graphs + 1]
 
     __device__ __forceinline__ RowSlots row(int32_t gr, int64_t i) const {
         RowSlots r;

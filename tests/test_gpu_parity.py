@@ -542,6 +542,59 @@ def test_generic_scores_far_maximum_f32(orc):
         pu.assert_z_close(z[0, h], ref, "f32", f"attn h={h}", 5, 0.1)
 
 
+# Rows longer than 1024 slots go to the generic kernels' long-row companions
+# (one workgroup per row): global rows of long sequences and, in a dense
+# imported graph, every row.
+LONG_ROW_CASES = [
+    # id, graph maker (orc -> (graph, row_ptrs, cols)), B, H, d, dtype, K, alpha
+    ("globals_f32_d64", lambda orc: (sah.build_graph(2500, 8, [0, 1, 1234, 2499], 5, 1, False, 9),
+                                      *orc.graph(2500, 8, [0, 1, 1234, 2499], 5, 1, False, 9)),
+     2, 2, 64, torch.float32, 3, 0.1),
+    ("globals_causal_bf16_d128", lambda orc: (sah.build_graph(2100, 4, [0, 700, 2099], 3, 2, True, 4),
+                                              *orc.graph(2100, 4, [0, 700, 2099], 3, 2, True, 4)),
+     2, 1, 128, torch.bfloat16, 2, 0.3),
+    ("dense_imported_f32_d16", lambda orc: (sah.graph_from_csr(
+        1100, np.arange(1101, dtype=np.int64)[None, :] * 1100, [np.tile(np.arange(1100, dtype=np.int32), 1100)]),
+        np.arange(1101, dtype=np.int64)[None, :] * 1100, [np.tile(np.arange(1100, dtype=np.int32), 1100)]),
+     1, 2, 16, torch.float32, 2, 0.1),
+]
+
+
+@pytest.mark.parametrize("case", LONG_ROW_CASES, ids=lambda c: c[0])
+def test_generic_long_rows(orc, case):
+    name, make, B, H, d, tdt, K, alpha = case
+    print(f"\n[long rows] {name}", flush=True)
+    g, rp, cols = make(orc)
+    ng = g.num_graphs
+    shape = (B, H, g.n, d)
+    q = make_tensor(shape, 81, tdt)
+    k = make_tensor(shape, 82, tdt)
+    v = make_tensor(shape, 83, tdt)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    A = sah.scores_softmax(qd, kd, g)
+    z = sah.attn(qd, kd, vd, g, K, alpha)
+    zs = sah.diffuse(A, vd, g, K, alpha)
+    torch.cuda.synchronize()
+    A_h, z_h, zs_h = _as64(A), _as64(z), _as64(zs)
+    dt = pu.dtype_name(tdt)
+    a_tol = 1e-5 if dt == "f32" else 2.0 ** -8 + 1e-5
+    for b in range(B):
+        gr = 0 if ng == 1 else b
+        lens = np.diff(rp[gr])
+        assert lens.max() > 1024, "the case must have long rows"
+        for h in range(H):
+            A_ref = orc.scores_softmax(_as64(q[b, h]), _as64(k[b, h]), rp[gr], cols[gr],
+                                       pu.oracle_threads())
+            A_got = _a_csr(g, A_h, b, h, H, gr, rp, cols)
+            assert np.all(np.abs(A_got - A_ref) <= a_tol * np.maximum(A_ref, 1e-30) + 1e-12), (b, h)
+            ref = orc.attn(_as64(q[b, h]), _as64(k[b, h]), _as64(v[b, h]), rp[gr], cols[gr], K,
+                           alpha, pu.oracle_threads())
+            pu.assert_z_close(z_h[b, h], ref, dt, f"{name} attn b={b} h={h}", K, alpha)
+            ref_s = orc.diffuse(A_got, _as64(v[b, h]), rp[gr], cols[gr], K, alpha,
+                                pu.oracle_threads())
+            pu.assert_z_close(zs_h[b, h], ref_s, dt, f"{name} diffuse b={b} h={h}", K, alpha)
+
+
 def _slot_classes(g, gr, n, r, G, causal):
     """Class of every weight slot of graph gr: 0 window, 1 global column,
     2 random, 3 global row, -1 padding."""
