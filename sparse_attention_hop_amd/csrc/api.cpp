@@ -734,7 +734,7 @@ diffuser_status diffuser_build_graph_layout(const diffuser_graph_desc* desc, int
     if (g->octet()) {
         // Tables of the resident-slice diffusion step; d_gcount (graphs x nrb
         // int32) is free again and holds the row-block costs.
-        // 64 lanes x 8 uint32 entries per (row block, batch).
+        // 64 lanes x 8 uint16 entries per (row block, batch).
         if ((e = dev_alloc(&g->d_rkey, (size_t)g->num_graphs * nrb * g->key_batches * 512)) !=
                 hipSuccess ||
             (e = dev_alloc(&g->d_rb_cost, (size_t)g->num_graphs * (nrb + 1))) != hipSuccess ||

@@ -27,8 +27,8 @@
 //    of all 16 rows with no lane idle: lane (m, kg) takes octet
 //    (m - kg) mod 4 of row m, which is exactly its operand in the one
 //    product of the batch it serves; in the other 15 it gives zeros. The
-//    keys of a batch come from the graph's key table in two loads of 16
-//    bytes per lane (each a contiguous kilobyte), each quad of lanes
+//    keys of a batch (16-bit key-row slots) come from the graph's key
+//    table, one contiguous kilobyte, 16 bytes per lane, each quad of lanes
 //    holding 4 octets that a DPP broadcast hands round.
 // Every weight load is a buffer load: a lane whose slots lie outside its
 // row's part is given an offset past the buffer and reads zeros, with no
@@ -78,7 +78,7 @@ struct ResArgs {
     const int64_t* seg_ptr;        // [graphs][n + 1]
     const int4* row_info;          // [graphs][n]
     const int32_t* G;              // [g]
-    const uint32_t* rkey;          // [graphs][nrb][batches][2][64][4]
+    const uint16_t* rkey;          // [graphs][nrb][batches][64][8]
     const int32_t* rb_oct;         // [graphs][nrb]
     const int64_t* rb_roff;        // [graphs][nrb + 1]
     const int64_t* cost;           // [graphs][nrb + 1]
@@ -256,8 +256,8 @@ void k_diffuse_res(ResArgs a) {
 
     const int64_t pair_slots = a.num_graphs == 1 ? a.slot_off[1] : a.slot_off[gr + 1] - a.slot_off[gr];
     const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(Abh, (uint32_t)(2 * pair_slots));
-    const uint32_t* rk = a.rkey + (int64_t)gr * a.nrb * a.batches * 512;
-    const __amdgpu_buffer_rsrc_t rK = buffer_rsrc(rk, (uint32_t)(a.nrb * a.batches * 2048));
+    const uint16_t* rk = a.rkey + (int64_t)gr * a.nrb * a.batches * 512;
+    const __amdgpu_buffer_rsrc_t rK = buffer_rsrc(rk, (uint32_t)(a.nrb * a.batches * 1024));
     const int32_t* oct = a.rb_oct + (int64_t)gr * a.nrb;
     const int64_t* roffs = a.rb_roff + (int64_t)gr * (a.nrb + 1);
     const int64_t rand_base = a.seg_ptr[(int64_t)gr * (n + 1) + n];   // random area's first slot
@@ -369,7 +369,7 @@ void k_diffuse_res(ResArgs a) {
         G.noct = live ? uniform_load32i(oct + rbc) : 0;
         G.nbat = (G.noct + kOctBatch - 1) / kOctBatch;
         G.wsoff = (uint32_t)(2 * (rand_base + 8 * kRowBlock * uniform_load64i(roffs + rbc)));
-        G.ksoff = (uint32_t)rbc * (uint32_t)a.batches * 2048u;
+        G.ksoff = (uint32_t)rbc * (uint32_t)a.batches * 1024u;
         return G;
     };
     u32x4 bw[kMaxBand], gw[kMaxGcolRegs];
@@ -385,16 +385,15 @@ void k_diffuse_res(ResArgs a) {
             gw[s] = bload16(rA, ok ? G.vglob : kOutside, (uint32_t)(64 * s));
         }
     };
-    u32x4 w0, w1, k0, k0h, k1, k1h;
-    auto rload = [&](const Geo& G, u32x4& w, u32x4& kk, u32x4& kh, int b) {
+    u32x4 w0, w1, k0, k1;
+    auto rload = [&](const Geo& G, u32x4& w, u32x4& kk, int b) {
         w = bload16(rA, (int32_t)(4 * b + (int32_t)jstar) < G.noct ? wv_lane : kOutside,
                     G.wsoff + 1024u * (uint32_t)b);
-        kk = bload16(rK, b < G.nbat ? kv_lane : kOutside, G.ksoff + 2048u * (uint32_t)b);
-        kh = bload16(rK, b < G.nbat ? kv_lane + 1024u : kOutside, G.ksoff + 2048u * (uint32_t)b);
+        kk = bload16(rK, b < G.nbat ? kv_lane : kOutside, G.ksoff + 1024u * (uint32_t)b);
     };
     auto issue_rand = [&](const Geo& G) {
-        rload(G, w0, k0, k0h, 0);
-        rload(G, w1, k1, k1h, 1);
+        rload(G, w0, k0, 0);
+        rload(G, w1, k1, 1);
     };
     u32x2 vin[CB];
     float cs = 1.0f;
@@ -461,38 +460,36 @@ void k_diffuse_res(ResArgs a) {
 
         // Random batches. Octet ob + J of a batch: quad lane J's keys for
         // every lane of the quad, then its 4 products.
-        auto octet = [&](const u32x4& w, const u32x4& kk, const u32x4& kh, auto jc, int ob) {
+        auto octet = [&](const u32x4& w, const u32x4& kk, auto jc, int ob) {
             constexpr int J = decltype(jc)::value;
             if (ob + J >= G.noct) return;
-            const uint32_t kq[8] = {quad_bcast<J>(kk[0]), quad_bcast<J>(kk[1]),
-                                    quad_bcast<J>(kk[2]), quad_bcast<J>(kk[3]),
-                                    quad_bcast<J>(kh[0]), quad_bcast<J>(kh[1]),
-                                    quad_bcast<J>(kh[2]), quad_bcast<J>(kh[3])};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
+                // Word t of quad lane J: the key-row slots of product t.
+                const uint32_t kw = quad_bcast<J>(kk[t]);
+                const uint32_t o1 = (kw & 0xffffu) << 5, o2 = (kw >> 16) << 5;
                 const bool mine = pstar == (uint32_t)(4 * J + t);
                 const u32x4 wt = u32x4{mine ? w[0] : 0u, mine ? w[1] : 0u, mine ? w[2] : 0u,
                                        mine ? w[3] : 0u};
 #pragma unroll
                 for (int nb = 0; nb < CB; ++nb)
-                    acc[nb] = mfma_bf16(z_op(base[nb] + kq[2 * t], base[nb] + kq[2 * t + 1]), wt,
-                                        acc[nb]);
+                    acc[nb] = mfma_bf16(z_op(base[nb] + o1, base[nb] + o2), wt, acc[nb]);
             }
         };
-        auto rbatch = [&](const u32x4& w, const u32x4& kk, const u32x4& kh, int b) {
+        auto rbatch = [&](const u32x4& w, const u32x4& kk, int b) {
             const int ob = kOctBatch * b;
-            octet(w, kk, kh, std::integral_constant<int, 0>{}, ob);
-            octet(w, kk, kh, std::integral_constant<int, 1>{}, ob);
-            octet(w, kk, kh, std::integral_constant<int, 2>{}, ob);
-            octet(w, kk, kh, std::integral_constant<int, 3>{}, ob);
+            octet(w, kk, std::integral_constant<int, 0>{}, ob);
+            octet(w, kk, std::integral_constant<int, 1>{}, ob);
+            octet(w, kk, std::integral_constant<int, 2>{}, ob);
+            octet(w, kk, std::integral_constant<int, 3>{}, ob);
         };
-        rbatch(w0, k0, k0h, 0);
-        rbatch(w1, k1, k1h, 1);
+        rbatch(w0, k0, 0);
+        rbatch(w1, k1, 1);
         // Blocks with more than 2 batches: the rest, each loaded on the spot.
         for (int b = 2; b < G.nbat; ++b) {
-            u32x4 w, kk, kh;
-            rload(G, w, kk, kh, b);
-            rbatch(w, kk, kh, b);
+            u32x4 w, kk;
+            rload(G, w, kk, b);
+            rbatch(w, kk, b);
         }
         issue_rand(Gn);
 
@@ -606,7 +603,7 @@ bool res_diffuse_supported(const diffuser_graph& g, const attn_shape& s) {
     for (int64_t x : g.slots)
         if (2 * x >= (1ll << 31)) return false;
     const int64_t nrb = (g.n + kRowBlock - 1) / kRowBlock;
-    if (nrb * g.key_batches * 2048 >= (1ll << 31)) return false;
+    if (nrb * g.key_batches * 1024 >= (1ll << 31)) return false;
     return res_plan(g, s.d).cb > 0;
 }
 

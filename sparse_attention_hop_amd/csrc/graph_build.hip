@@ -551,12 +551,11 @@ __global__ void k_rb_oct(int64_t n, int32_t nrb, const int32_t* __restrict__ rnd
 }
 
 // Key table of the resident-slice diffusion step, one thread per (row
-// block, batch, lane): the lane's 8 entries (see diffuser_graph::d_rkey),
-// entries 0..3 in the batch's first kilobyte and 4..7 in its second, each
-// at 16 bytes times the lane.
+// block, batch, lane): the lane's 8 entries (see diffuser_graph::d_rkey) in
+// one 16-byte store.
 __global__ void k_rkey(int64_t n, int32_t nrb, int32_t batches, int32_t rnd_width,
                        uint32_t n_pad, const int32_t* __restrict__ rnd,
-                       const int32_t* __restrict__ rnd_cnt, uint32_t* __restrict__ rkey) {
+                       const int32_t* __restrict__ rnd_cnt, uint16_t* __restrict__ rkey) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t gr = blockIdx.y;
     if (idx >= (int64_t)nrb * batches * kWave) return;
@@ -575,12 +574,12 @@ __global__ void k_rkey(int64_t n, int32_t nrb, int32_t batches, int32_t rnd_widt
                 const int64_t row = gr * n + i;
                 if (e < rnd_cnt[row]) k = res_unit((uint32_t)rnd[row * rnd_width + e]);
             }
-            w[2 * t + h] = 32u * k;
+            w[2 * t + h] = k;
         }
     }
-    uint4* out = reinterpret_cast<uint4*>(rkey) + 2 * (gr * nrb * batches * kWave + idx - l);
-    out[l] = make_uint4(w[0], w[1], w[2], w[3]);
-    out[kWave + l] = make_uint4(w[4], w[5], w[6], w[7]);
+    uint4* out = reinterpret_cast<uint4*>(rkey) + gr * nrb * batches * kWave + idx;
+    *out = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
+                      w[6] | (w[7] << 16));
 }
 
 // Per row block of every graph, for the resident-slice diffusion step's

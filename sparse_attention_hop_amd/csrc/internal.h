@@ -21,6 +21,7 @@ constexpr int64_t kMaxScheduledN = 1 << 16;
 // slice of every key row (32 bytes each, a zero row after the last) then
 // fits in LDS beside the 16 KB of global-row partial sums.
 constexpr int64_t kMaxResidentN = 4576;
+static_assert(kMaxResidentN < 65535, "resident key-row slots fit 16 bits");
 // Rows with more weight slots than this (a global row's n, say) are split
 // over the waves of one workgroup by the generic kernels' long-row
 // companions instead of walked by one wave.
@@ -149,15 +150,14 @@ struct diffuser_graph {
     int64_t* d_rb_roff = nullptr;   // [graphs][nrb + 1]: prefix sums of d_rb_oct
     std::vector<int64_t> octets;    // [num_graphs]: random octets of each graph
     // Resident-slice diffusion step's key table: for row block rb, batch
-    // b of kOctBatch octets, lane l = 16 kg + 4 q + j (64 lanes), 8 uint32
-    // entries t * 2 + h: 32 times the res_unit slot of the key of random
-    // edge 8 o + 4 h + q of row 4 t + ((kg + o) & 3) of the block, o =
-    // 4 b + j, or of the zero row res_npad(n) where there is none (the
-    // key row's byte offset in an LDS plane). A batch's entries 0..3 of
-    // every lane come first (16 bytes per lane, by lane), then its
-    // entries 4..7, so each half is one contiguous kilobyte.
+    // b of kOctBatch octets, lane l = 16 kg + 4 q + j (64 lanes), 8 uint16
+    // entries t * 2 + h: the res_unit slot of the key of random edge
+    // 8 o + 4 h + q of row 4 t + ((kg + o) & 3) of the block, o = 4 b + j,
+    // or the zero row res_npad(n) where there is none (the key row's slot
+    // in an LDS plane of 32-byte slots). A batch is one contiguous
+    // kilobyte, 16 bytes per lane.
     int32_t key_batches = 0;        // batches per row block: ceil(ceil(rnd_width / 8) / 4)
-    uint32_t* d_rkey = nullptr;     // [graphs][nrb][key_batches][2][64][4]
+    uint16_t* d_rkey = nullptr;     // [graphs][nrb][key_batches][64][8]
     int64_t* d_rb_cost = nullptr;   // [graphs][nrb + 1]: prefix sums of row-block costs
     int64_t* d_rb_cost_max = nullptr;  // [graphs]: largest row-block cost
 
