@@ -374,10 +374,11 @@ def host_cores():
     return max(1, min(cpus, int(cap))) if cap.isdigit() and int(cap) > 0 else max(1, cpus)
 
 
-def _oracle_leg(orc, w, q, k, v, rp, cols, pairs, threads, budget_s):
+def _oracle_leg(orc, w, q, k, v, rp, cols, pairs, threads, budget_s, z=None):
     """(b, h) pairs until the budget is spent: edges, score+softmax seconds,
-    diffusion seconds, pairs done."""
-    edges, t_sc, t_df, done = 0, 0.0, 0.0, 0
+    diffusion seconds, pairs done, and, when the GPU output z is given, the
+    largest |z - z_oracle| over those pairs (untimed)."""
+    edges, t_sc, t_df, done, err = 0, 0.0, 0.0, 0, 0.0
     for b, h in pairs:
         gr = 0 if w.num_graphs == 1 else b
         Q = q[b, h].double().numpy()
@@ -386,22 +387,26 @@ def _oracle_leg(orc, w, q, k, v, rp, cols, pairs, threads, budget_s):
         t0 = time.perf_counter()
         A = orc.scores_softmax(Q, Kx, rp[gr], cols[gr], threads)
         t1 = time.perf_counter()
-        orc.diffuse(A, V, rp[gr], cols[gr], w.K, w.alpha, threads)
+        Zr = orc.diffuse(A, V, rp[gr], cols[gr], w.K, w.alpha, threads)
         t2 = time.perf_counter()
         t_sc += t1 - t0
         t_df += t2 - t1
         edges += int(rp[gr][-1]) * w.K
         done += 1
+        if z is not None:
+            err = max(err, float(abs(z[b, h].double().numpy() - Zr).max()))
         if t_sc + t_df >= budget_s:
             break
-    return edges, t_sc, t_df, done
+    return edges, t_sc, t_df, done, err
 
 
-def cpu_baseline(w, q, k, v, budget_s=15.0, max_pairs=None):
+def cpu_baseline(w, q, k, v, budget_s=15.0, max_pairs=None, z=None):
     """The oracle, as it stands, on (b, h) pairs of the same workload: once
     on one thread and once on every host core this process may use (each
     leg until half the budget is spent). `value` is the all-cores rate in
-    diffused edges/s over the sample; the stages are timed apart."""
+    diffused edges/s over the sample; the stages are timed apart. With the
+    GPU output z (host tensor), also the largest |z - z_oracle| over the
+    all-cores leg's pairs."""
     import oracle
     orc = oracle.Oracle()
     cores = host_cores()
@@ -411,15 +416,19 @@ def cpu_baseline(w, q, k, v, budget_s=15.0, max_pairs=None):
     if max_pairs:
         pairs = pairs[:max_pairs]
     legs = {}
+    err = None
     for threads in (1, cores) if cores > 1 else (1,):
-        edges, t_sc, t_df, done = _oracle_leg(orc, w, q, k, v, rp, cols, pairs, threads,
-                                              budget_s / 2)
+        edges, t_sc, t_df, done, e = _oracle_leg(orc, w, q, k, v, rp, cols, pairs, threads,
+                                                 budget_s / 2, z if threads == cores else None)
         legs[threads] = {
             "value": edges / (t_sc + t_df), "threads": threads, "pairs": done,
             "score_softmax_s_per_pair": t_sc / done, "diffusion_s_per_pair": t_df / done,
         }
+        if threads == cores and z is not None:
+            err = e
     top = legs[cores]
     return {
+        "max_abs_err_vs_oracle": err,
         "value": top["value"], "unit": "edges/s", "cores": cores, "kind": "oracle",
         "sample": f"{top['pairs']} of {len(pairs)} (b,h) pairs on {cores} threads "
                   f"({legs[1]['pairs']} on 1), all rows, scores+softmax then {w.K} diffusion "
@@ -571,7 +580,10 @@ def main():
         line["extras"]["graph_replay"] = {"ms_per_step": t_graph,
                                           "edges_per_s": diffused / (t_graph * 1e-3)}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q_h, k_h, v_h, budget_s=args.cpu_budget)
+        step()
+        torch.cuda.synchronize()
+        line["cpu_baseline"] = cpu_baseline(w, q_h, k_h, v_h, budget_s=args.cpu_budget,
+                                            z=z.cpu())
     print(json.dumps(line), flush=True)
 
 
