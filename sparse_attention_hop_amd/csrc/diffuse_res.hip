@@ -460,14 +460,16 @@ void k_diffuse_res(ResArgs a) {
 
         // Random batches. Octet ob + J of a batch: quad lane J's keys for
         // every lane of the quad, then its 4 products.
-        auto octet = [&](const u32x4& w, const u32x4& kk, auto jc, int ob) {
+        // ko: the lane's 8 key-row slots of the batch as byte offsets in a
+        // plane (entry 2t + h of word t's half h); the products of octet J
+        // take quad lane J's, each added to the plane base in one
+        // broadcast add.
+        auto octet = [&](const u32x4& w, const uint32_t (&ko)[8], auto jc, int ob) {
             constexpr int J = decltype(jc)::value;
             if (ob + J >= G.noct) return;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                // Word t of quad lane J: the key-row slots of product t.
-                const uint32_t kw = quad_bcast<J>(kk[t]);
-                const uint32_t o1 = (kw & 0xffffu) << 5, o2 = (kw >> 16) << 5;
+                const uint32_t o1 = quad_bcast<J>(ko[2 * t]), o2 = quad_bcast<J>(ko[2 * t + 1]);
                 const bool mine = pstar == (uint32_t)(4 * J + t);
                 const u32x4 wt = u32x4{mine ? w[0] : 0u, mine ? w[1] : 0u, mine ? w[2] : 0u,
                                        mine ? w[3] : 0u};
@@ -478,10 +480,16 @@ void k_diffuse_res(ResArgs a) {
         };
         auto rbatch = [&](const u32x4& w, const u32x4& kk, int b) {
             const int ob = kOctBatch * b;
-            octet(w, kk, std::integral_constant<int, 0>{}, ob);
-            octet(w, kk, std::integral_constant<int, 1>{}, ob);
-            octet(w, kk, std::integral_constant<int, 2>{}, ob);
-            octet(w, kk, std::integral_constant<int, 3>{}, ob);
+            uint32_t ko[8];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                ko[2 * t] = (kk[t] & 0xffffu) << 5;
+                ko[2 * t + 1] = (kk[t] >> 16) << 5;
+            }
+            octet(w, ko, std::integral_constant<int, 0>{}, ob);
+            octet(w, ko, std::integral_constant<int, 1>{}, ob);
+            octet(w, ko, std::integral_constant<int, 2>{}, ob);
+            octet(w, ko, std::integral_constant<int, 3>{}, ob);
         };
         rbatch(w0, k0, 0);
         rbatch(w1, k1, 1);
