@@ -78,6 +78,8 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_col_off_slots);
     hipFree(g->d_col_slot);
     hipFree(g->d_col_row);
+    hipFree(g->d_long_cols);
+    hipFree(g->d_long_col_off);
     hipFree(g->d_slot_csr);
     hipFree(g->d_long_rows);
     hipFree(g->d_long_off);
@@ -114,6 +116,8 @@ void free_graph_memory(diffuser_graph* g) {
     g->d_col_off_slots = nullptr;
     g->d_col_slot = nullptr;
     g->d_col_row = nullptr;
+    g->d_long_cols = nullptr;
+    g->d_long_col_off = nullptr;
     g->d_slot_csr = nullptr;
     g->d_long_rows = nullptr;
     g->d_long_off = nullptr;
@@ -335,6 +339,9 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
     std::vector<int64_t> col_ptr((size_t)g->num_graphs * (n + 1));
     std::vector<int64_t> col_off(g->num_graphs + 1, 0);
     std::vector<int32_t> col_slot, col_row;
+    std::vector<int32_t> long_cols;
+    std::vector<int64_t> long_col_off(g->num_graphs + 1, 0);
+    int64_t max_long_col = 0;
     std::vector<int32_t> srow, scol, by_row;
     std::vector<int64_t> cnt;
     hipError_t e;
@@ -373,17 +380,27 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
             col_row[base + at] = srow[s];
         }
         col_off[gr + 1] = (int64_t)col_slot.size();
+        // Long columns (more than kLongRow entries), for the transposed
+        // products' long-column companion.
+        for (int64_t j = 0; j < n; ++j)
+            if (cp[j + 1] - cp[j] > kLongRow) long_cols.push_back((int32_t)j);
+        long_col_off[gr + 1] = (int64_t)long_cols.size();
+        max_long_col = std::max(max_long_col, long_col_off[gr + 1] - long_col_off[gr]);
     }
-    int64_t *d_ptr = nullptr, *d_off = nullptr;
-    int32_t *d_slot = nullptr, *d_row = nullptr;
+    int64_t *d_ptr = nullptr, *d_off = nullptr, *d_loff = nullptr;
+    int32_t *d_slot = nullptr, *d_row = nullptr, *d_lcols = nullptr;
     if ((e = dev_alloc(&d_ptr, col_ptr.size())) != hipSuccess ||
         (e = dev_alloc(&d_off, col_off.size())) != hipSuccess ||
         (e = dev_alloc(&d_slot, col_slot.size())) != hipSuccess ||
-        (e = dev_alloc(&d_row, col_row.size())) != hipSuccess) {
+        (e = dev_alloc(&d_row, col_row.size())) != hipSuccess ||
+        (e = dev_alloc(&d_lcols, long_cols.size())) != hipSuccess ||
+        (e = dev_alloc(&d_loff, long_col_off.size())) != hipSuccess) {
         hipFree(d_ptr);
         hipFree(d_off);
         hipFree(d_slot);
         hipFree(d_row);
+        hipFree(d_lcols);
+        hipFree(d_loff);
         return alloc_status(e, "device allocation of the column index");
     }
     if ((e = hipMemcpyAsync(d_ptr, col_ptr.data(), sizeof(int64_t) * col_ptr.size(),
@@ -396,13 +413,23 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
         (col_row.size() > 0 &&
          (e = hipMemcpyAsync(d_row, col_row.data(), sizeof(int32_t) * col_row.size(),
                              hipMemcpyHostToDevice, st)) != hipSuccess) ||
+        (long_cols.size() > 0 &&
+         (e = hipMemcpyAsync(d_lcols, long_cols.data(), sizeof(int32_t) * long_cols.size(),
+                             hipMemcpyHostToDevice, st)) != hipSuccess) ||
+        (e = hipMemcpyAsync(d_loff, long_col_off.data(), sizeof(int64_t) * long_col_off.size(),
+                            hipMemcpyHostToDevice, st)) != hipSuccess ||
         (e = hipStreamSynchronize(st)) != hipSuccess) {
         hipFree(d_ptr);
         hipFree(d_off);
         hipFree(d_slot);
         hipFree(d_row);
+        hipFree(d_lcols);
+        hipFree(d_loff);
         return hip_fail(e, "upload of the column index");
     }
+    g->d_long_cols = d_lcols;
+    g->d_long_col_off = d_loff;
+    g->max_long_col = max_long_col;
     g->d_col_ptr = d_ptr;
     g->d_col_off_slots = d_off;
     g->d_col_slot = d_slot;

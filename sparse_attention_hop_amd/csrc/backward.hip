@@ -10,7 +10,8 @@
 //
 // Generic kernels over the weight slots (any built graph, fp32 or bf16
 // storage, d in {16, 32, 64, 128}); every intermediate (A, dA, the states
-// Z_k, G_k, dV) is fp32. Row-wise products walk a row's slots; the
+// Z_k, G_k, dV) is fp32. Rows and columns with more than kLongRow entries
+// are split over the waves of one workgroup by companion kernels. Row-wise products walk a row's slots; the
 // transposed ones walk the graph's column index (the slots of each column
 // by ascending row), with the weights first copied into that order so that
 // only the rows of X are gathered. dA takes all K terms in one pass over
@@ -68,6 +69,7 @@ void k_rows(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict__ W,
     const TX* Xb = X + (int64_t)bh * n * D + 4 * sub;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const int64_t cnt = rs.count();
+    if (cnt > kLongRow) return;   // k_rows_long's
     for (int64_t base = 0; base < cnt; base += EPI * kUnroll) {
         // Slots base + u EPI + grp; padding and slots past the row read
         // column 0 with weight 0.
@@ -159,6 +161,7 @@ void k_cols(ColIndex ci, int32_t H, int32_t BH, const float* __restrict__ Wt,
     const TX* Xb = X + (int64_t)bh * n * D + 4 * sub;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const int64_t e0 = cp[j], e1 = cp[j + 1];
+    if (e1 - e0 > kLongRow) return;   // k_cols_long's
     for (int64_t base = e0; base < e1; base += EPI * kUnroll) {
         // Entries base + u EPI + grp; those past the column read entry e0
         // with weight 0.
@@ -189,29 +192,16 @@ void k_cols(ColIndex ci, int32_t H, int32_t BH, const float* __restrict__ Wt,
     }
 }
 
-// dA[s] = a * sum_{k < K} G_{k+1}[i] . Z_k[col(s)] for the slots of row i
-// (padding slots get 0): groups of L lanes take one slot each (L = D / 4
-// lanes of 4 channels); state k of G or Z starts at k * stride.
+// The slots [e0, e1) of one row for k_edge_dots (lane group grp, channel
+// quad sub).
 template <int D>
-__global__ __launch_bounds__(kThreads)
-void k_edge_dots(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict__ Gs,
-                 const float* __restrict__ Zs, int64_t stride, int32_t K, float* __restrict__ dA,
-                 float a) {
+__device__ __forceinline__ void edge_dots_range(const RowSlots& rs, const float* Gi,
+                                                const float* Zb, int64_t stride, int32_t K,
+                                                float* dAb, float a, int64_t e0, int64_t e1,
+                                                int grp, int sub) {
     constexpr int L = D / 4, EPI = kWave / L;
-    const int wave = threadIdx.x / kWave, lane = __lane_id();
-    const int64_t n = gg.n;
-    int64_t i;
-    int32_t bh;
-    if (!xcd_row_item<kWavesPerBlock>(n, BH, wave, i, bh)) return;
-    const int32_t bb = bh / H, hh = bh - bb * H;
-    const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
-    const RowSlots rs = gg.row(gr, i);
-    float* dAb = dA + a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
-    const int sub = lane % L, grp = lane / L;
-    const float* Gi = Gs + stride + ((int64_t)bh * n + i) * D + 4 * sub;
-    const float* Zb = Zs + (int64_t)bh * n * D + 4 * sub;
-    const int64_t cnt = rs.count();
-    for (int64_t base = 0; base < cnt; base += EPI * kUnroll) {
+    const int64_t cnt = e1;
+    for (int64_t base = e0; base < cnt; base += EPI * kUnroll) {
         int32_t j[kUnroll];
         int64_t s[kUnroll];
 #pragma unroll
@@ -239,6 +229,185 @@ void k_edge_dots(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict
         for (int u = 0; u < kUnroll; ++u)
             if (s[u] >= 0 && sub == 0) dAb[s[u]] = j[u] >= 0 ? a * dot[u] : 0.0f;
     }
+}
+
+// dA[s] = a * sum_{k < K} G_{k+1}[i] . Z_k[col(s)] for the slots of row i
+// (padding slots get 0): groups of L lanes take one slot each (L = D / 4
+// lanes of 4 channels); state k of G or Z starts at k * stride.
+template <int D>
+__global__ __launch_bounds__(kThreads)
+void k_edge_dots(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict__ Gs,
+                 const float* __restrict__ Zs, int64_t stride, int32_t K, float* __restrict__ dA,
+                 float a) {
+    constexpr int L = D / 4;
+    const int wave = threadIdx.x / kWave, lane = __lane_id();
+    const int64_t n = gg.n;
+    int64_t i;
+    int32_t bh;
+    if (!xcd_row_item<kWavesPerBlock>(n, BH, wave, i, bh)) return;
+    const int32_t bb = bh / H, hh = bh - bb * H;
+    const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
+    const RowSlots rs = gg.row(gr, i);
+    float* dAb = dA + a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
+    const int sub = lane % L, grp = lane / L;
+    const float* Gi = Gs + stride + ((int64_t)bh * n + i) * D + 4 * sub;
+    const float* Zb = Zs + (int64_t)bh * n * D + 4 * sub;
+    const int64_t cnt = rs.count();
+    if (cnt > kLongRow) return;   // k_edge_dots_long's
+    edge_dots_range<D>(rs, Gi, Zb, stride, K, dAb, a, 0, cnt, grp, sub);
+}
+
+// Long rows and columns (more than kLongRow entries, a global row's or
+// column's n, say): one workgroup of kLongWaves waves per (pair, long row or
+// column), long row (column) blockIdx.x of the pair's graph, each wave a
+// contiguous share of the entries gathered as k_rows / k_cols / k_edge_dots
+// do. The row and column products add the waves' partial sums in wave order
+// through LDS; dA needs no sum across entries.
+constexpr int kLongWaves = 16;
+constexpr int kLongThreads = kWave * kLongWaves;
+
+template <typename TX, typename TU, typename TY, int D>
+__global__ __launch_bounds__(kLongThreads)
+void k_rows_long(GenericGraph gg, int32_t H, const float* __restrict__ W,
+                 const TX* __restrict__ X, const TU* __restrict__ U, TY* __restrict__ Y,
+                 float a, float b) {
+    constexpr int L = D / 4, EPI = kWave / L;
+    __shared__ float part[kLongWaves][D];
+    const int32_t bh = blockIdx.y;
+    const int32_t bb = bh / H, hh = bh - bb * H;
+    const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
+    const int64_t li = gg.long_off[gr] + blockIdx.x;
+    if (li >= gg.long_off[gr + 1]) return;   // the whole workgroup
+    const int64_t n = gg.n;
+    const int64_t i = gg.long_rows[li];
+    const RowSlots rs = gg.row(gr, i);
+    const float* Wb = W + a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
+    const int wave = threadIdx.x / kWave, lane = __lane_id();
+    const int sub = lane % L, grp = lane / L;
+    const TX* Xb = X + (int64_t)bh * n * D + 4 * sub;
+    const int64_t cnt = rs.count();
+    const int64_t e0 = cnt * wave / kLongWaves, e1 = cnt * (wave + 1) / kLongWaves;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t base = e0; base < e1; base += EPI * kUnroll) {
+        int32_t j[kUnroll];
+        int64_t s[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t e = base + u * EPI + grp;
+            j[u] = -1;
+            s[u] = 0;
+            if (e < e1) s[u] = rs.slot(e, j[u]);
+        }
+        float w[kUnroll], x[kUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            w[u] = j[u] >= 0 ? Wb[s[u]] : 0.0f;
+            ld4(Xb + (int64_t)(j[u] >= 0 ? j[u] : 0) * D, x[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(w[u], x[u][c], acc[c]);
+    }
+#pragma unroll
+    for (int off = L; off < kWave; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
+    if (grp == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) part[wave][4 * sub + c] = acc[c];
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+        const int c = threadIdx.x;
+        float t = 0.0f;
+        for (int w = 0; w < kLongWaves; ++w) t += part[w][c];
+        const int64_t o = ((int64_t)bh * n + i) * D + c;
+        float y = a * t;
+        if (U != nullptr) y += b * ld(U + o);
+        st(Y + o, y);
+    }
+}
+
+template <typename TX, typename TY, int D>
+__global__ __launch_bounds__(kLongThreads)
+void k_cols_long(ColIndex ci, int32_t H, const int32_t* __restrict__ long_cols,
+                 const int64_t* __restrict__ long_col_off, const float* __restrict__ Wt,
+                 const TX* __restrict__ X, TY* __restrict__ Y, float a) {
+    constexpr int L = D / 4, EPI = kWave / L;
+    __shared__ float part[kLongWaves][D];
+    const int32_t bh = blockIdx.y;
+    const int32_t bb = bh / H, hh = bh - bb * H;
+    const int32_t gr = ci.num_graphs == 1 ? 0 : bb;
+    const int64_t li = long_col_off[gr] + blockIdx.x;
+    if (li >= long_col_off[gr + 1]) return;   // the whole workgroup
+    const int64_t n = ci.n;
+    const int64_t j = long_cols[li];
+    const int64_t* cp = ci.col_ptr + (int64_t)gr * (n + 1);
+    const int32_t* crow = ci.col_row + ci.col_off[gr];
+    const float* Wb = Wt + a_block_offset(ci.slot_off, ci.num_graphs, H, bb, hh);
+    const int wave = threadIdx.x / kWave, lane = __lane_id();
+    const int sub = lane % L, grp = lane / L;
+    const TX* Xb = X + (int64_t)bh * n * D + 4 * sub;
+    const int64_t c_lo = cp[j], cnt = cp[j + 1] - cp[j];
+    const int64_t e0 = c_lo + cnt * wave / kLongWaves, e1 = c_lo + cnt * (wave + 1) / kLongWaves;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t base = e0; base < e1; base += EPI * kUnroll) {
+        int64_t r[kUnroll];
+        float w[kUnroll], x[kUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t e = base + u * EPI + grp;
+            const bool ok = e < e1;
+            r[u] = crow[ok ? e : c_lo];
+            w[u] = ok ? Wb[e] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) ld4(Xb + r[u] * D, x[u]);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(w[u], x[u][c], acc[c]);
+    }
+#pragma unroll
+    for (int off = L; off < kWave; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
+    if (grp == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) part[wave][4 * sub + c] = acc[c];
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+        const int c = threadIdx.x;
+        float t = 0.0f;
+        for (int w = 0; w < kLongWaves; ++w) t += part[w][c];
+        st(Y + ((int64_t)bh * n + j) * D + c, a * t);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kLongThreads)
+void k_edge_dots_long(GenericGraph gg, int32_t H, const float* __restrict__ Gs,
+                      const float* __restrict__ Zs, int64_t stride, int32_t K,
+                      float* __restrict__ dA, float a) {
+    constexpr int L = D / 4;
+    const int32_t bh = blockIdx.y;
+    const int32_t bb = bh / H, hh = bh - bb * H;
+    const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
+    const int64_t li = gg.long_off[gr] + blockIdx.x;
+    if (li >= gg.long_off[gr + 1]) return;   // the whole workgroup
+    const int64_t n = gg.n;
+    const int64_t i = gg.long_rows[li];
+    const RowSlots rs = gg.row(gr, i);
+    float* dAb = dA + a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
+    const int wave = threadIdx.x / kWave, lane = __lane_id();
+    const int sub = lane % L, grp = lane / L;
+    const float* Gi = Gs + stride + ((int64_t)bh * n + i) * D + 4 * sub;
+    const float* Zb = Zs + (int64_t)bh * n * D + 4 * sub;
+    const int64_t cnt = rs.count();
+    edge_dots_range<D>(rs, Gi, Zb, stride, K, dAb, a, cnt * wave / kLongWaves,
+                       cnt * (wave + 1) / kLongWaves, grp, sub);
 }
 
 // dS = A (dA - sum_row A dA) * scale, in place of dA; one wave per row.
@@ -325,10 +494,18 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     if (K > 0)
         hipLaunchKernelGGL((k_axpby<T>), grid_elems(cnt), blk, 0, stream, cnt, V, p.Zs, 1.0f,
                            0.0f);
-    for (int32_t k = 1; k < K; ++k)
+    const dim3 longs((unsigned)std::max<int64_t>(g.max_long, 1), (unsigned)BH);
+    const dim3 long_cols((unsigned)std::max<int64_t>(g.max_long_col, 1), (unsigned)BH);
+    const dim3 lblk(kLongThreads);
+    for (int32_t k = 1; k < K; ++k) {
         hipLaunchKernelGGL((k_rows<float, T, float, D>), rows, blk, 0, stream, gg, p.H, BH, p.A,
                            p.Zs + (size_t)(k - 1) * cnt, V, p.Zs + (size_t)k * cnt, keep,
                            p.alpha);
+        if (g.max_long > 0)
+            hipLaunchKernelGGL((k_rows_long<float, T, float, D>), longs, lblk, 0, stream, gg, p.H,
+                               p.A, p.Zs + (size_t)(k - 1) * cnt, V, p.Zs + (size_t)k * cnt,
+                               keep, p.alpha);
+    }
     // G_K = dZ, G_k = (1 - alpha) A^T G_{k+1}; dV = alpha (G_K + .. + G_1).
     hipLaunchKernelGGL((k_axpby<T>), grid_elems(cnt), blk, 0, stream, cnt,
                        static_cast<const T*>(p.dZ), p.Gs + (size_t)K * cnt, 1.0f, 0.0f);
@@ -341,10 +518,17 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
                            p.alpha, k == K - 1 ? 0.0f : 1.0f);
         hipLaunchKernelGGL((k_cols<float, float, D>), rows, blk, 0, stream, ci, p.H, BH, p.At, Gk1,
                            p.Gs + (size_t)k * cnt, keep);
+        if (g.max_long_col > 0)
+            hipLaunchKernelGGL((k_cols_long<float, float, D>), long_cols, lblk, 0, stream, ci, p.H,
+                               g.d_long_cols, g.d_long_col_off, p.At, Gk1,
+                               p.Gs + (size_t)k * cnt, keep);
     }
     // dA = (1 - alpha) sum_k G_{k+1} Z_k^T on the edges.
     hipLaunchKernelGGL((k_edge_dots<D>), rows, blk, 0, stream, gg, p.H, BH, p.Gs, p.Zs, cnt, K,
                        p.dA, keep);
+    if (g.max_long > 0)
+        hipLaunchKernelGGL((k_edge_dots_long<D>), longs, lblk, 0, stream, gg, p.H, p.Gs, p.Zs, cnt,
+                           K, p.dA, keep);
     // dV = (sum of alpha G_{k+1}) + G_0.
     if (K == 0)
         hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, p.Gs, p.dV,
@@ -356,10 +540,18 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     hipLaunchKernelGGL((k_rows<T, T, T, D>), rows, blk, 0, stream, gg, p.H, BH, p.dA,
                        static_cast<const T*>(p.K), static_cast<const T*>(nullptr),
                        static_cast<T*>(p.dQ), 1.0f, 0.0f);
+    if (g.max_long > 0)
+        hipLaunchKernelGGL((k_rows_long<T, T, T, D>), longs, lblk, 0, stream, gg, p.H, p.dA,
+                           static_cast<const T*>(p.K), static_cast<const T*>(nullptr),
+                           static_cast<T*>(p.dQ), 1.0f, 0.0f);
     hipLaunchKernelGGL(k_to_columns, entries, blk, 0, stream, ci, p.H, BH, entry_blocks, p.dA,
                        p.At);
     hipLaunchKernelGGL((k_cols<T, T, D>), rows, blk, 0, stream, ci, p.H, BH, p.At,
                        static_cast<const T*>(p.Q), static_cast<T*>(p.dK), 1.0f);
+    if (g.max_long_col > 0)
+        hipLaunchKernelGGL((k_cols_long<T, T, D>), long_cols, lblk, 0, stream, ci, p.H,
+                           g.d_long_cols, g.d_long_col_off, p.At, static_cast<const T*>(p.Q),
+                           static_cast<T*>(p.dK), 1.0f);
     return hipGetLastError();
 }
 

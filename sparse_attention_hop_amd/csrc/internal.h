@@ -191,6 +191,11 @@ struct diffuser_graph {
     int64_t* d_col_off_slots = nullptr;  // [num_graphs + 1]
     int32_t* d_col_slot = nullptr;       // [valid slots of all graphs]
     int32_t* d_col_row = nullptr;        // row of each d_col_slot entry
+    // Columns with more than kLongRow entries (built with the column index),
+    // ascending, per graph from d_long_col_off.
+    int64_t max_long_col = 0;
+    int32_t* d_long_cols = nullptr;      // [long columns of all graphs]
+    int64_t* d_long_col_off = nullptr;   // [num_graphs + 1]
 };
 
 namespace diffuser {
