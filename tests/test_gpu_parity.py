@@ -385,6 +385,13 @@ FAST_CASES = [
     # by (b, h); every pair is compared
     (600, 16, [0, 300], 12, 1, False, 2, 4),
     (520, 24, [0, 1, 519], 10, 4, False, 4, 4),
+    # near the whole-sequence resident step's limits: one 32-channel plane
+    # pair only just fits (n = 2300, no globals), a single 16-channel plane
+    # up to the longest octet-layout sequence (4576), causal rows
+    (3000, 40, [0, 1500, 2999], 30, 1, False, 1, 2),
+    (4576, 64, list(range(64)), 64, 2, True, 2, 1),
+    (2300, 8, [], 20, 1, False, 1, 3),
+    (4100, 100, list(range(0, 4100, 85)), 48, 1, False, 1, 2),
 ]
 
 
