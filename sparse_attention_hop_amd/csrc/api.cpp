@@ -218,7 +218,7 @@ diffuser_status check_ptr(const void* p, const char* name, bool need16 = true) {
 // the resident channel slice, the LDS-streamed tiles (scheduled graphs up
 // to 2^16 keys), else the generic kernel.
 struct step_launcher {
-    enum kind_t { kBlock, kResident, kStreamed, kGeneric } kind;
+    enum kind_t { kBlock, kResident, kStreamed, kRows, kGeneric } kind;
     const diffuser_graph* g;
     attn_shape s;
     const void* A;
@@ -230,6 +230,7 @@ struct step_launcher {
             case kBlock: return launch_block_diffuse(*g, s, A, cur, V, dst, row_scale, kc, part, st);
             case kResident: return launch_diffuse_res(*g, s, A, cur, V, dst, row_scale, kc, st);
             case kStreamed: return launch_diffuse_fast(*g, s, A, cur, V, dst, row_scale, kc, st);
+            case kRows: return launch_diffuse_rows(*g, s, A, cur, V, dst, row_scale, kc, st);
             default: return launch_diffuse_step(*g, s, A, cur, V, dst, row_scale, kc, st);
         }
     }
@@ -242,6 +243,7 @@ step_launcher pick_step(const diffuser_graph* g, const attn_shape& s, const void
         if (fast_block_supported(*g, s)) l.kind = step_launcher::kBlock;
         else if (res_diffuse_supported(*g, s)) l.kind = step_launcher::kResident;
         else if (fast_diffuse_supported(*g, s)) l.kind = step_launcher::kStreamed;
+        else if (rows_diffuse_supported(*g, s)) l.kind = step_launcher::kRows;
     }
     return l;
 }

@@ -1,0 +1,394 @@
+// Diffusion step on built graphs with fp32 storage, one wavefront per row
+// as in the generic step, with the key rows of the window band and of the
+// global columns served from LDS:
+//   Z_{k+1}[i] = keep * c_i * sum_j A_ij Z_k[j] + restart * V[i]
+// ("Diffuser" reading notes, section 2.4, eq. S.7, with keep = 1 - alpha and
+// restart = alpha; other coefficients evaluate section 2.3's eq. S.6 in
+// nested form; c_i rescales the stored weights of row i to sum to one, or
+// is 1).
+//
+// A workgroup of 16 waves owns kRowsPerGroup consecutive rows of one
+// (batch, head) pair. It first copies into LDS, by direct global-to-LDS
+// loads, every key row that a window slot of its rows can name (one
+// contiguous run of Z_k around its rows) and the key rows of the g global
+// columns, then each wave sums its rows alone:
+//  * window slots: 16 consecutive columns at a time, lane group q taking
+//    columns 4 q .. 4 q + 3 with one 16-byte weight load and four key rows
+//    read from LDS; slots outside the row's window (block padding) weigh 0;
+//  * global-column slots: the same over the row's global slots, whose key
+//    rows sit in LDS in global order; a slot whose global lies in the
+//    window (or, when causal, above the row) is padding and weighs 0;
+//  * random edges: gathered from Z_k in global memory, as the generic step
+//    does, each lane group one edge at a time with four edges in flight.
+// A lane holds 4 channels of one key row (lane group q, lanes 16 q .. + 15
+// for a head width of 64); the groups' partial sums are added at the end
+// and the restart term is fused into the store. The window and global
+// slots, most of a row's edges, then cost LDS reads instead of gathers of
+// whole key rows from L2. Global rows (whose segment is every column) go to
+// a second kernel that reads each key row once for kGRows of them.
+#include "internal.h"
+#include "mfma_util.h"
+#include "vec.h"
+
+namespace diffuser {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 16;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kRowsPerWave = 4;
+constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
+constexpr int kPadRows = 32;       // zero rows past the window run and past the globals
+constexpr int kLdsLimit = 160 * 1024;
+constexpr int64_t kMinGroups = 1024;   // workgroups below which the generic step is used
+
+struct RowsArgs {
+    int64_t n;
+    int32_t H, num_graphs, radius, causal, g;
+    int32_t win_rows;              // key rows of the window run in LDS (padding included)
+    int32_t items, per_xcd, blocks;   // work items, per XCD, row groups per pair
+    GenericGraph gg;
+    const int4* row_info;          // [graphs][n]
+    const int32_t* G;              // [g]
+    const float* A;
+    const float* Z;
+    const float* V;
+    float* Zn;
+    const float* row_scale;        // [B*H][n] or null
+    float keep, restart;
+};
+
+__device__ __forceinline__ f32x4 lds4(const float LDS_AS* p) {
+    return *reinterpret_cast<const f32x4 LDS_AS*>(p);
+}
+
+__device__ __forceinline__ f32x4 ld4(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+
+__device__ __forceinline__ void fma4(float (&acc)[4], float w, const f32x4& z) {
+    acc[0] = fmaf(w, z[0], acc[0]);
+    acc[1] = fmaf(w, z[1], acc[1]);
+    acc[2] = fmaf(w, z[2], acc[2]);
+    acc[3] = fmaf(w, z[3], acc[3]);
+}
+
+// Eight waves per SIMD (two workgroups per CU, as many waves as the
+// generic step keeps in flight): at most 64 registers per lane.
+template <int D>
+__global__ __launch_bounds__(kThreads, 8)
+void k_diffuse_rows_f32(RowsArgs a) {
+    constexpr int L = D / 4;            // lanes per key row (4 channels each)
+    constexpr int NG = kWave / L;       // lane groups
+    extern __shared__ __align__(16) char lds_raw[];
+    float LDS_AS* lds = (float LDS_AS*)lds_raw;
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int sub = lane % L, grp = lane / L;
+
+    const int32_t item = (int32_t)(blockIdx.x & 7u) * a.per_xcd + (int32_t)(blockIdx.x >> 3);
+    if (item >= a.items) return;
+    const int32_t bh = item / a.blocks;
+    const int64_t r0 = (int64_t)(item - bh * a.blocks) * kRowsPerGroup;
+    const int32_t b = bh / a.H, h = bh - b * a.H;
+    const int32_t gr = a.num_graphs == 1 ? 0 : b;
+    const int64_t n = a.n;
+    const float* Abh = a.A + a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
+    const float* Zbh = a.Z + (int64_t)bh * n * D;
+    const int4* info = a.row_info + (int64_t)gr * n;
+    const int64_t pair_slots = a.num_graphs == 1 ? a.gg.slot_off[1]
+                                                 : a.gg.slot_off[gr + 1] - a.gg.slot_off[gr];
+    const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(Abh, (uint32_t)(4 * pair_slots));
+    const __amdgpu_buffer_rsrc_t rG = buffer_rsrc(a.G, (uint32_t)(4 * a.g));
+
+    // ---- key rows into LDS ------------------------------------------------
+    // Window run: key rows w0 .. w0 + win_rows - 1 (every window slot of the
+    // group's rows names one of them), then the g global rows, then
+    // kPadRows zero rows. Rows outside [0, n) are zero.
+    const int64_t w0 = (r0 - a.radius < 0 ? 0 : r0 - a.radius) & ~7ll;
+    float LDS_AS* win = lds;
+    float LDS_AS* glob = lds + (int64_t)a.win_rows * D;
+    {
+        const int32_t rows = a.win_rows + a.g + kPadRows;
+        const int32_t units = rows * L;   // 16-byte pieces
+        for (int32_t p0 = 64 * wave; p0 < units; p0 += 64 * kWaves) {
+            const int32_t p = p0 + lane;
+            const int32_t r = p / L, u = p - r * L;
+            int64_t k = -1;
+            if (r < a.win_rows) k = w0 + r;
+            else if (r < a.win_rows + a.g) k = a.G[r - a.win_rows];
+            const bool live = p < units && k >= 0 && k < n;
+            if (live)
+                dma16(Zbh + k * D + 4 * u, (void LDS_AS*)(lds + 4 * p0));
+            else if (p < units)
+                *reinterpret_cast<f32x4 LDS_AS*>(lds + 4 * p) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    full_barrier();
+
+#pragma unroll 1
+    for (int u = 0; u < kRowsPerWave; ++u) {
+        const int64_t i = r0 + kWaves * u + wave;
+        if (i >= n) break;
+        const int4 ri = info[i];
+        if (ri.z < 0) continue;   // a global row: k_diffuse_grows_f32's
+        const RowSlots rs = a.gg.row(gr, i);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        {
+            const int64_t lo = i - a.radius < 0 ? 0 : i - a.radius;
+            const int64_t hi = i + a.radius > n - 1 ? n - 1 : i + a.radius;
+            const int64_t wend = a.causal ? i : hi;
+            const int64_t last = a.causal ? i : n - 1;
+            const int64_t wb0 = ri.y;
+            // Window slots: columns cb + 4 grp + v of the block at cb, two
+            // blocks' weights requested before either is used.
+            const uint32_t wl = 4u * (uint32_t)(ri.x + 4 * grp);
+            for (int64_t cb = wb0; cb <= wend; cb += 8 * NG) {
+                u32x4 wv[2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int64_t c0 = cb + 4 * NG * s2 + 4 * grp;
+                    wv[s2] = bload16(rA, c0 <= wend ? wl + 4u * (uint32_t)(cb + 4 * NG * s2 - wb0)
+                                                    : kOutside, 0u);
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int64_t c0 = cb + 4 * NG * s2 + 4 * grp;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int64_t c = c0 + v;
+                        const bool ok = c >= lo && c <= wend;
+                        const float w = ok ? __uint_as_float(wv[s2][v]) : 0.0f;
+                        // columns past the window read a zero or an in-run row
+                        fma4(acc, w, lds4(win + (ok ? c - w0 : 0) * D + 4 * sub));
+                    }
+                }
+            }
+            // Global-column slots t of the row (G[t] outside the window and,
+            // when causal, not above the row).
+            const int32_t gs = min(a.g, ri.w);
+            for (int32_t tb = 0; tb < gs; tb += 4 * NG) {
+                const int32_t t0 = tb + 4 * grp;
+                const bool any = t0 < gs;
+                const u32x4 wv = bload16(rA, any ? 4u * (uint32_t)(ri.x + ri.z + t0) : kOutside, 0u);
+                const u32x4 gk = bload16(rG, any ? 4u * (uint32_t)t0 : kOutside, 0u);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t k = (int32_t)gk[v];
+                    const bool ok = t0 + v < gs && (k < lo || k > hi) && k <= last;
+                    const float w = ok ? __uint_as_float(wv[v]) : 0.0f;
+                    fma4(acc, w, lds4(glob + (int64_t)(t0 + v) * D + 4 * sub));
+                }
+            }
+            // Random edges, gathered: lane group grp takes edges
+            // base + 4 grp + v, their slots and columns in one 16-byte load
+            // each; the next step's slots and columns are requested before
+            // this step's rows are used.
+            const int32_t nr = rs.rcnt;
+            const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(rs.rslot, (uint32_t)(4 * nr));
+            const __amdgpu_buffer_rsrc_t rC = buffer_rsrc(rs.rcol, (uint32_t)(4 * nr));
+            auto idx = [&](int32_t base, u32x4& sl, u32x4& cl) {
+                const int32_t e0 = base + 4 * grp;
+                sl = bload16(rS, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
+                cl = bload16(rC, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
+            };
+            u32x4 sl, cl;
+            idx(0, sl, cl);
+            for (int32_t base = 0; base < nr; base += 4 * NG) {
+                float w[4];
+                f32x4 z[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const bool ok = base + 4 * grp + v < nr;
+                    w[v] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                        rA, ok ? (int)(4u * sl[v]) : (int)kOutside, 0, 0));
+                    z[v] = ld4(Zbh + (int64_t)(ok ? (int32_t)cl[v] : 0) * D + 4 * sub);
+                }
+                idx(base + 4 * NG, sl, cl);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) fma4(acc, w[v], z[v]);
+            }
+        }
+#pragma unroll
+        for (int off = L; off < kWave; off <<= 1) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
+        }
+        if (grp == 0) {
+            const int64_t o = ((int64_t)bh * n + i) * D + 4 * sub;
+            const f32x4 v = ld4(a.V + o);
+            const float keep =
+                a.row_scale == nullptr ? a.keep : a.keep * a.row_scale[(int64_t)bh * n + i];
+            *reinterpret_cast<f32x4*>(a.Zn + o) =
+                f32x4{keep * acc[0] + a.restart * v[0], keep * acc[1] + a.restart * v[1],
+                      keep * acc[2] + a.restart * v[2], keep * acc[3] + a.restart * v[3]};
+        }
+    }
+}
+
+// Global rows, kGRows per workgroup: the 16 waves split the keys into
+// contiguous ranges, each key row of Z_k is read once per workgroup (16
+// bytes per lane, lane group grp taking 4 consecutive keys) and multiplied
+// by the weights of all kGRows rows (a global row's segment holds its
+// columns in order); the waves' partial sums meet in LDS and are added in
+// wave order. Columns above the row are padding when causal.
+constexpr int kGRows = 8;
+
+template <int D>
+__global__ __launch_bounds__(kThreads)
+void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
+    constexpr int L = D / 4;
+    constexpr int NG = kWave / L;
+    __shared__ f32x4 part[kWaves][kGRows][L];
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int sub = lane % L, grp = lane / L;
+    const int32_t bh = blockIdx.x / gblocks;
+    const int32_t q0 = (blockIdx.x - bh * gblocks) * kGRows;
+    const int32_t b = bh / a.H, h = bh - b * a.H;
+    const int32_t gr = a.num_graphs == 1 ? 0 : b;
+    const int64_t n = a.n;
+    const float* Abh = a.A + a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
+    const float* Zbh = a.Z + (int64_t)bh * n * D;
+    const int4* info = a.row_info + (int64_t)gr * n;
+    const int64_t pair_slots = a.num_graphs == 1 ? a.gg.slot_off[1]
+                                                 : a.gg.slot_off[gr + 1] - a.gg.slot_off[gr];
+    const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(Abh, (uint32_t)(4 * pair_slots));
+    const __amdgpu_buffer_rsrc_t rZ = buffer_rsrc(Zbh, (uint32_t)(4 * n * D));
+    // The rows' segment starts and last columns (-1: no row).
+    uint32_t seg[kGRows];
+    int64_t last[kGRows];
+#pragma unroll
+    for (int r = 0; r < kGRows; ++r) {
+        const int32_t q = q0 + r;
+        const int64_t i = q < a.g ? a.G[q] : -1;
+        seg[r] = i >= 0 ? (uint32_t)info[i].x : 0u;
+        last[r] = i < 0 ? -1 : a.causal ? i : n - 1;
+    }
+    f32x4 acc[kGRows];
+#pragma unroll
+    for (int r = 0; r < kGRows; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t k0 = n * wave / kWaves, k1 = n * (wave + 1) / kWaves;
+    for (int64_t kb = k0 & ~3ll; kb < k1; kb += 4 * NG) {
+        const int64_t j0 = kb + 4 * grp;   // keys j0 .. j0 + 3 of this lane group
+        f32x4 z[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t j = j0 + v;
+            const bool ok = j >= k0 && j < k1;
+            z[v] = __builtin_bit_cast(f32x4, bload16(rZ, ok ? (uint32_t)((j * D + 4 * sub) * 4) : kOutside, 0u));
+        }
+#pragma unroll
+        for (int r = 0; r < kGRows; ++r) {
+            const bool any = j0 <= last[r] && j0 < k1;
+            const u32x4 w = bload16(rA, any ? 4u * (seg[r] + (uint32_t)j0) : kOutside, 0u);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t j = j0 + v;
+                const float wj = j >= k0 && j < k1 && j <= last[r] ? __uint_as_float(w[v]) : 0.0f;
+                acc[r] = acc[r] + wj * z[v];
+            }
+        }
+    }
+    // Lane groups, then waves, in a fixed order.
+#pragma unroll
+    for (int r = 0; r < kGRows; ++r)
+#pragma unroll
+        for (int off = L; off < kWave; off <<= 1)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[r][c] += __shfl_xor(acc[r][c], off);
+    if (grp == 0)
+#pragma unroll
+        for (int r = 0; r < kGRows; ++r) part[wave][r][sub] = acc[r];
+    __syncthreads();
+    for (int t = threadIdx.x; t < kGRows * L; t += kThreads) {
+        const int r = t / L, s2 = t - r * L;
+        const int32_t q = q0 + r;
+        if (q >= a.g) continue;
+        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < kWaves; ++w) sum = sum + part[w][r][s2];
+        const int64_t i = a.G[q];
+        const int64_t o = ((int64_t)bh * n + i) * D + 4 * s2;
+        const f32x4 v = ld4(a.V + o);
+        const float keep =
+            a.row_scale == nullptr ? a.keep : a.keep * a.row_scale[(int64_t)bh * n + i];
+        *reinterpret_cast<f32x4*>(a.Zn + o) = keep * sum + a.restart * v;
+    }
+}
+
+// Key rows of the window run: the group's rows, the radius on either side
+// (on the left only when causal), the 8-column alignment of the window
+// blocks and one 16-column block past the last window column.
+int32_t win_rows(const diffuser_graph& g) {
+    return kRowsPerGroup + (g.causal ? 1 : 2) * g.radius + 8 + kPadRows;
+}
+
+template <int D>
+int32_t lds_bytes(const diffuser_graph& g) {
+    return (win_rows(g) + g.num_global + kPadRows) * D * 4;
+}
+
+template <int D>
+hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
+                    const void* V, void* Zn, const float* row_scale, step_coefs kc,
+                    hipStream_t st) {
+    RowsArgs a;
+    a.n = g.n;
+    a.H = s.H;
+    a.num_graphs = g.num_graphs;
+    a.radius = g.radius;
+    a.causal = g.causal;
+    a.g = g.num_global;
+    a.win_rows = win_rows(g);
+    a.blocks = (int32_t)((g.n + kRowsPerGroup - 1) / kRowsPerGroup);
+    a.items = s.B * s.H * a.blocks;
+    a.per_xcd = (a.items + 7) / 8;
+    a.gg = generic_graph(g);
+    a.row_info = reinterpret_cast<const int4*>(g.d_row_info);
+    a.G = g.d_global;
+    a.A = static_cast<const float*>(A);
+    a.Z = static_cast<const float*>(Zk);
+    a.V = static_cast<const float*>(V);
+    a.Zn = static_cast<float*>(Zn);
+    a.row_scale = row_scale;
+    a.keep = kc.keep;
+    a.restart = kc.restart;
+    const int lds = lds_bytes<D>(g);
+    static int attr_device = -1;
+    if (attr_device != g.device) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_diffuse_rows_f32<D>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+        if (e != hipSuccess) return e;
+        attr_device = g.device;
+    }
+    hipLaunchKernelGGL((k_diffuse_rows_f32<D>), dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
+                       (size_t)lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || g.num_global == 0) return e;
+    const int32_t gblocks = (g.num_global + kGRows - 1) / kGRows;
+    hipLaunchKernelGGL((k_diffuse_grows_f32<D>), dim3((unsigned)(s.B * s.H * gblocks)),
+                       dim3(kThreads), 0, st, a, gblocks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool rows_diffuse_supported(const diffuser_graph& g, const attn_shape& s) {
+    if (!g.structured || !g.rand_apart() || g.d_row_info == nullptr || s.dtype != DIFFUSER_F32 ||
+        s.d != 64)
+        return false;
+    for (int64_t x : g.slots)
+        if (4 * x >= (1ll << 31)) return false;   // byte offsets of a pair's weights fit 31 bits
+    // Enough row groups to give every CU two workgroups twice over; fewer
+    // rows run faster one wave per row on the generic step.
+    const int64_t groups = (int64_t)s.B * s.H * ((g.n + kRowsPerGroup - 1) / kRowsPerGroup);
+    return groups >= kMinGroups && 2 * lds_bytes<64>(g) <= kLdsLimit;
+}
+
+hipError_t launch_diffuse_rows(const diffuser_graph& g, const attn_shape& s, const void* A,
+                               const void* Zk, const void* V, void* Zn, const float* row_scale,
+                               step_coefs kc, hipStream_t st) {
+    return launch_t<64>(g, s, A, Zk, V, Zn, row_scale, kc, st);
+}
+
+}  // namespace diffuser

@@ -281,6 +281,13 @@ struct step_coefs {
 hipError_t launch_diffuse_step(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
                                step_coefs k, hipStream_t st);
+// The same step on built graphs with fp32 storage (d = 64), one wave per
+// row, the window and global-column key rows of each 64-row group in LDS;
+// the global rows several at a time, each key row read once.
+bool rows_diffuse_supported(const diffuser_graph& g, const attn_shape& s);
+hipError_t launch_diffuse_rows(const diffuser_graph& g, const attn_shape& s, const void* A,
+                               const void* Zk, const void* V, void* Zn, const float* row_scale,
+                               step_coefs k, hipStream_t st);
 // The same step on built graphs with a whole channel slice of Z_k resident
 // in LDS (bf16, d = 32 or 64, n up to about 4.5 K keys).
 bool res_diffuse_supported(const diffuser_graph& g, const attn_shape& s);

@@ -36,6 +36,34 @@ __device__ __forceinline__ void dma16(const void* src, void LDS_AS* lds) {
     __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
+// Raw buffer resource over `bytes` bytes from `base`: a load at a byte
+// offset at or past the end returns zero, which masks a lane's load without
+// a branch.
+// The base and size are wave-uniform; they are read from the first lane so
+// that the descriptor lives in scalar registers. readfirstlane returns a
+// signed int: each half goes through an unsigned 32-bit variable, since a
+// sign-extended low half would set every bit of the high half.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t u = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    const uint64_t b = ((uint64_t)hi << 32) | lo;
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(b), (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+constexpr uint32_t kOutside = 0x80000000u;   // a byte offset past every buffer used here
+
+// 16 (8) bytes at lane offset voff plus wave-uniform offset soff.
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         r, (int)voff, (int)__builtin_amdgcn_readfirstlane(soff), 0));
+}
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                         r, (int)voff, (int)__builtin_amdgcn_readfirstlane(soff), 0));
+}
+
 // Load of a wave-uniform int32 of read-only graph data through the scalar
 // cache (the constant address space).
 __device__ __forceinline__ int32_t uniform_load(const int32_t* p) {
