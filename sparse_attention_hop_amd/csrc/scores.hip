@@ -409,6 +409,22 @@ hipError_t launch_f32_d(const diffuser_graph& g, const attn_shape& s, const void
 
 }  // namespace
 
+hipError_t launch_scores_long_fused_f32(const diffuser_graph& g, const attn_shape& s, const void* Q,
+                                       const void* K, void* A, float* row_scale,
+                                       float scale_log2, hipStream_t st) {
+    if (g.max_long > 0)
+        hipLaunchKernelGGL((k_scores_long<float, float, 64>),
+                           dim3((unsigned)g.max_long, (unsigned)(s.B * s.H)),
+                           dim3(kWave * kLongWaves), 0, st, generic_graph(g), s.H,
+                           static_cast<const float*>(Q), static_cast<const float*>(K),
+                           static_cast<float*>(A), row_scale, scale_log2);
+    if (g.rand_apart())
+        hipLaunchKernelGGL((k_zero_dummies<float>), dim3(64, (unsigned)(s.B * s.H)), dim3(256), 0,
+                           st, g.n, s.H, g.num_graphs, g.d_slot_off, g.d_slot_col, g.d_seg_ptr,
+                           static_cast<float*>(A));
+    return hipGetLastError();
+}
+
 hipError_t launch_scores_softmax_f32(const diffuser_graph& g, const attn_shape& s, const void* Q,
                                      const void* K, float* A, float scale_log2, hipStream_t st) {
     if (s.dtype == DIFFUSER_F32) return launch_f32_d<float>(g, s, Q, K, A, scale_log2, st);
@@ -424,6 +440,8 @@ hipError_t launch_scores_softmax(const diffuser_graph& g, const attn_shape& s, c
                                    st);
     if (aligned && fast_scores_supported(g, s))
         return launch_scores_fast(g, s, Q, K, A, row_scale, scale_log2, row_scale == nullptr, st);
+    if (aligned && row_scale != nullptr && rows_scores_supported(g, s))
+        return launch_scores_rows(g, s, Q, K, A, row_scale, scale_log2, st);
     if (s.dtype == DIFFUSER_F32) return launch_d<float>(g, s, Q, K, A, row_scale, scale_log2, st);
     return launch_d<bf16_t>(g, s, Q, K, A, row_scale, scale_log2, st);
 }

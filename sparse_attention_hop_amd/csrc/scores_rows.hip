@@ -1,0 +1,334 @@
+// Fused edge scores and edge softmax on built graphs with fp32 storage
+// ("Diffuser" reading notes, section 2.1, eqs. S.1-S.5; "1.2.1 Static
+// sparsity", section 1, eqs. 1-3):
+//   s_ij = q_i . k_j / sqrt(d_h) on the edges of row i,
+//   w_ij = exp(s_ij - m_i) stored, c_i = 1 / sum_j w_ij,
+// so that c_i w_ij is the row's softmax. As in the generic kernel the shift
+// m_i is the row's own score (the self-loop is an edge of every row, so it
+// is at most the maximum and the largest weight is at least 1); a row whose
+// weights sum to 2^64 or more is redone with its exact maximum, and its
+// stored weights are then normalised, with c_i over them as stored.
+//
+// One wavefront per row, as in the generic kernel, with the key rows of the
+// window band and of the global columns served from LDS: a workgroup of 16
+// waves owns 64 consecutive rows of one (batch, head) pair and first copies
+// into LDS every key row a window slot of its rows can name and the g
+// global key rows, by direct global-to-LDS loads. A lane holds 4 channels
+// of q_i and of a key row (lane group q, lanes 16 q .. + 15); each group
+// scores 4 slots at a time, its dot products reduced over the group's 16
+// lanes:
+//  * window slots: 16 consecutive columns per step, lane group q taking
+//    columns 4 q .. 4 q + 3, key rows from LDS, the four weights stored in
+//    one 16-byte store; block padding stores 0;
+//  * global-column slots: the same over the row's global slots (G[t] from
+//    LDS in global order), padding (a global in the window or, when causal,
+//    above the row) stores 0;
+//  * random edges: key rows gathered from K in global memory, four
+//    consecutive edges per lane group, their slots and columns in one
+//    16-byte load each.
+// Rows with more than kLongRow slots (global rows, whose segment is every
+// column, or when causal every column up to the row) are left to the
+// generic long-row companion; the shorter global rows of a causal graph's
+// first rows are scored here from K in global memory. The random area's
+// dummy slots are zeroed as the generic pass does.
+#include "internal.h"
+#include "mfma_util.h"
+#include "vec.h"
+
+namespace diffuser {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 16;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kRowsPerWave = 4;
+constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
+constexpr int kPadRows = 32;
+constexpr int kLdsLimit = 160 * 1024;
+constexpr int64_t kMinGroups = 1024;
+constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
+
+struct SRowsArgs {
+    int64_t n;
+    int32_t H, num_graphs, radius, causal, g;
+    int32_t win_rows;
+    int32_t items, per_xcd, blocks;
+    GenericGraph gg;
+    const int4* row_info;          // [graphs][n]
+    const int32_t* G;              // [g]
+    const float* Q;
+    const float* K;
+    float* A;
+    float* row_scale;              // [B*H][n]
+    float scale_log2;              // log2(e) / sqrt(d_h)
+};
+
+__device__ __forceinline__ f32x4 lds4(const float LDS_AS* p) {
+    return *reinterpret_cast<const f32x4 LDS_AS*>(p);
+}
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+__device__ __forceinline__ float dot4(const f32x4& q, const f32x4& k) {
+    return fmaf(q[3], k[3], fmaf(q[2], k[2], fmaf(q[1], k[1], q[0] * k[0])));
+}
+
+// Sum over the 16 lanes of a lane group (every lane gets it).
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 8)
+void k_scores_rows_f32(SRowsArgs a) {
+    static_assert(D == 64, "one 16-lane group per key row");
+    extern __shared__ __align__(16) char lds_raw[];
+    float LDS_AS* lds = (float LDS_AS*)lds_raw;
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int sub = lane & 15, grp = lane >> 4;
+
+    const int32_t item = (int32_t)(blockIdx.x & 7u) * a.per_xcd + (int32_t)(blockIdx.x >> 3);
+    if (item >= a.items) return;
+    const int32_t bh = item / a.blocks;
+    const int64_t r0 = (int64_t)(item - bh * a.blocks) * kRowsPerGroup;
+    const int32_t b = bh / a.H, h = bh - b * a.H;
+    const int32_t gr = a.num_graphs == 1 ? 0 : b;
+    const int64_t n = a.n;
+    float* Abh = a.A + a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
+    const float* Kbh = a.K + (int64_t)bh * n * D;
+    const int4* info = a.row_info + (int64_t)gr * n;
+    const __amdgpu_buffer_rsrc_t rG = buffer_rsrc(a.G, (uint32_t)(4 * a.g));
+
+    // ---- key rows into LDS (as the fp32 diffusion step's) -----------------
+    const int64_t w0 = (r0 - a.radius < 0 ? 0 : r0 - a.radius) & ~7ll;
+    float LDS_AS* win = lds;
+    float LDS_AS* glob = lds + (int64_t)a.win_rows * D;
+    {
+        const int32_t rows = a.win_rows + a.g + kPadRows;
+        const int32_t units = rows * 16;
+        for (int32_t p0 = 64 * wave; p0 < units; p0 += 64 * kWaves) {
+            const int32_t p = p0 + lane;
+            const int32_t r = p >> 4, u = p & 15;
+            int64_t k = -1;
+            if (r < a.win_rows) k = w0 + r;
+            else if (r < a.win_rows + a.g) k = a.G[r - a.win_rows];
+            const bool live = p < units && k >= 0 && k < n;
+            if (live)
+                dma16(Kbh + k * D + 4 * u, (void LDS_AS*)(lds + 4 * p0));
+            else if (p < units)
+                *reinterpret_cast<f32x4 LDS_AS*>(lds + 4 * p) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    full_barrier();
+
+#pragma unroll 1
+    for (int u = 0; u < kRowsPerWave; ++u) {
+        const int64_t i = r0 + kWaves * u + wave;
+        if (i >= n) break;
+        const int4 ri = info[i];
+        const RowSlots rs = a.gg.row(gr, i);
+        if (rs.count() > kLongRow) continue;   // the long-row companion's
+        // A global row here is one of a causal graph's first rows: its
+        // segment holds its columns 0 .. i in order.
+        const bool grow = ri.z < 0;
+        const f32x4 q = ld4(a.Q + ((int64_t)bh * n + i) * D + 4 * sub);
+        const int64_t lo = i - a.radius < 0 ? 0 : i - a.radius;
+        const int64_t hi = i + a.radius > n - 1 ? n - 1 : i + a.radius;
+        const int64_t wend = a.causal ? i : hi;
+        const int64_t last = a.causal ? i : n - 1;
+        const int64_t wb0 = ri.y;
+        const int32_t wseg = ri.z, gseg = ri.w;
+        const int32_t nr = rs.rcnt;
+        const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(rs.rslot, (uint32_t)(4 * nr));
+        const __amdgpu_buffer_rsrc_t rC = buffer_rsrc(rs.rcol, (uint32_t)(4 * nr));
+
+        // Every slot of the row, four per lane group per step: f(kind, t0 or
+        // the slots, valid[4], scaled scores[4]); kind 0 window (slots
+        // seg + t0 .. + 3), 1 global (seg + wseg + t0 ..), 2 random, 3 a
+        // short global row (seg + t0 ..).
+        auto sweep = [&](auto&& f) {
+            if (grow) {
+                const int32_t len = (int32_t)rs.seg_len;
+                for (int32_t tb = 0; tb < len; tb += 16) {
+                    const int32_t t0 = tb + 4 * grp;
+                    bool ok[4];
+                    f32x4 kz[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        ok[v] = t0 + v < len && t0 + v <= last;
+                        kz[v] = ld4(Kbh + (int64_t)(ok[v] ? t0 + v : 0) * D + 4 * sub);
+                    }
+                    float s[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) s[v] = a.scale_log2 * group_sum(dot4(q, kz[v]));
+                    f(3, t0, u32x4{0u, 0u, 0u, 0u}, ok, s);
+                }
+                return;
+            }
+            for (int32_t tb = 0; tb < wseg; tb += 16) {
+                const int32_t t0 = tb + 4 * grp;
+                bool ok[4];
+                float s[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t c = wb0 + t0 + v;
+                    ok[v] = t0 < wseg && c >= lo && c <= wend;
+                    s[v] = a.scale_log2 * group_sum(dot4(q, lds4(win + (ok[v] ? c - w0 : 0) * D + 4 * sub)));
+                }
+                f(0, t0, u32x4{0u, 0u, 0u, 0u}, ok, s);
+            }
+            for (int32_t tb = 0; tb < gseg; tb += 16) {
+                const int32_t t0 = tb + 4 * grp;
+                const u32x4 gk = bload16(rG, t0 < min(gseg, a.g) ? 4u * (uint32_t)t0 : kOutside, 0u);
+                bool ok[4];
+                float s[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t k = (int32_t)gk[v];
+                    ok[v] = t0 + v < min(gseg, a.g) && (k < lo || k > hi) && k <= last;
+                    s[v] = a.scale_log2 * group_sum(dot4(q, lds4(glob + (ok[v] ? t0 + v : 0) * D + 4 * sub)));
+                }
+                f(1, t0, u32x4{0u, 0u, 0u, 0u}, ok, s);
+            }
+            for (int32_t eb = 0; eb < nr; eb += 16) {
+                const int32_t e0 = eb + 4 * grp;
+                const u32x4 sl = bload16(rS, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
+                const u32x4 cl = bload16(rC, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
+                bool ok[4];
+                f32x4 kz[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    ok[v] = e0 + v < nr;
+                    kz[v] = ld4(Kbh + (int64_t)(ok[v] ? (int32_t)cl[v] : 0) * D + 4 * sub);
+                }
+                float s[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) s[v] = a.scale_log2 * group_sum(dot4(q, kz[v]));
+                f(2, e0, sl, ok, s);
+            }
+        };
+        // The weights w[4] of one step into A (lane sub == 0 of the group).
+        auto store = [&](int kind, int32_t t0, const u32x4& sl, const bool (&ok)[4],
+                         const float (&w)[4]) {
+            if (sub != 0) return;
+            if (kind == 3) {
+                if (t0 < rs.seg_len)
+                    *reinterpret_cast<f32x4*>(Abh + ri.x + t0) = f32x4{w[0], w[1], w[2], w[3]};
+            } else if (kind == 0) {
+                if (t0 < wseg)
+                    *reinterpret_cast<f32x4*>(Abh + ri.x + t0) = f32x4{w[0], w[1], w[2], w[3]};
+            } else if (kind == 1) {
+                if (t0 < gseg)
+                    *reinterpret_cast<f32x4*>(Abh + ri.x + wseg + t0) = f32x4{w[0], w[1], w[2], w[3]};
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (ok[v]) Abh[sl[v]] = w[v];
+            }
+        };
+
+        // The fused single pass, shifted by the row's own score.
+        const float ms = a.scale_log2 * group_sum(dot4(q, lds4(win + (i - w0) * D + 4 * sub)));
+        float total = 0.0f;
+        sweep([&](int kind, int32_t t0, const u32x4& sl, const bool (&ok)[4], const float (&s)[4]) {
+            float w[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) w[v] = ok[v] ? __builtin_amdgcn_exp2f(s[v] - ms) : 0.0f;
+            store(kind, t0, sl, ok, w);
+            if (sub == 0) total += (w[0] + w[1]) + (w[2] + w[3]);
+        });
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) total += __shfl_xor(total, off);
+        if (total < kSumLimit) {
+            if (lane == 0) a.row_scale[(int64_t)bh * n + i] = 1.0f / total;
+            continue;
+        }
+        // Redone with the exact maximum: its (max, sum), then the normalised
+        // weights and c_i over them as stored.
+        float m = -INFINITY;
+        sweep([&](int, int32_t, const u32x4&, const bool (&ok)[4], const float (&s)[4]) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) m = ok[v] ? fmaxf(m, s[v]) : m;
+        });
+#pragma unroll
+        for (int off = 16; off < kWave; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+        float l = 0.0f;
+        sweep([&](int, int32_t, const u32x4&, const bool (&ok)[4], const float (&s)[4]) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) l += ok[v] ? __builtin_amdgcn_exp2f(s[v] - m) : 0.0f;
+        });
+#pragma unroll
+        for (int off = 16; off < kWave; off <<= 1) l += __shfl_xor(l, off);
+        const float inv = 1.0f / l;
+        float stored = 0.0f;
+        sweep([&](int kind, int32_t t0, const u32x4& sl, const bool (&ok)[4], const float (&s)[4]) {
+            float w[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) w[v] = ok[v] ? __builtin_amdgcn_exp2f(s[v] - m) * inv : 0.0f;
+            store(kind, t0, sl, ok, w);
+            if (sub == 0) stored += (w[0] + w[1]) + (w[2] + w[3]);
+        });
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) stored += __shfl_xor(stored, off);
+        if (lane == 0) a.row_scale[(int64_t)bh * n + i] = 1.0f / stored;
+    }
+}
+
+int32_t win_rows(const diffuser_graph& g) {
+    return kRowsPerGroup + (g.causal ? 1 : 2) * g.radius + 8 + kPadRows;
+}
+
+int32_t lds_bytes(const diffuser_graph& g) { return (win_rows(g) + g.num_global + kPadRows) * 64 * 4; }
+
+}  // namespace
+
+bool rows_scores_supported(const diffuser_graph& g, const attn_shape& s) {
+    if (!g.structured || !g.rand_apart() || g.d_row_info == nullptr || s.dtype != DIFFUSER_F32 ||
+        s.d != 64 || g.n <= kLongRow)
+        return false;
+    for (int64_t x : g.slots)
+        if (4 * x >= (1ll << 31)) return false;
+    const int64_t groups = (int64_t)s.B * s.H * ((g.n + kRowsPerGroup - 1) / kRowsPerGroup);
+    return groups >= kMinGroups && 2 * lds_bytes(g) <= kLdsLimit;
+}
+
+hipError_t launch_scores_rows(const diffuser_graph& g, const attn_shape& s, const void* Q,
+                              const void* K, void* A, float* row_scale, float scale_log2,
+                              hipStream_t st) {
+    SRowsArgs a;
+    a.n = g.n;
+    a.H = s.H;
+    a.num_graphs = g.num_graphs;
+    a.radius = g.radius;
+    a.causal = g.causal;
+    a.g = g.num_global;
+    a.win_rows = win_rows(g);
+    a.blocks = (int32_t)((g.n + kRowsPerGroup - 1) / kRowsPerGroup);
+    a.items = s.B * s.H * a.blocks;
+    a.per_xcd = (a.items + 7) / 8;
+    a.gg = generic_graph(g);
+    a.row_info = reinterpret_cast<const int4*>(g.d_row_info);
+    a.G = g.d_global;
+    a.Q = static_cast<const float*>(Q);
+    a.K = static_cast<const float*>(K);
+    a.A = static_cast<float*>(A);
+    a.row_scale = row_scale;
+    a.scale_log2 = scale_log2;
+    static int attr_device = -1;
+    if (attr_device != g.device) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_scores_rows_f32<64>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+        if (e != hipSuccess) return e;
+        attr_device = g.device;
+    }
+    hipLaunchKernelGGL((k_scores_rows_f32<64>), dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
+                       (size_t)lds_bytes(g), st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_scores_long_fused_f32(g, s, Q, K, A, row_scale, scale_log2, st);
+}
+
+}  // namespace diffuser

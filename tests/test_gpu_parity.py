@@ -613,6 +613,60 @@ def test_generic_long_rows(orc, case):
             pu.assert_z_close(zs_h[b, h], ref_s, dt, f"{name} diffuse b={b} h={h}", K, alpha)
 
 
+# fp32 row kernels with the window and global key rows in LDS (built graphs,
+# d = 64, n > 1024, at least 1024 groups of 64 rows): global rows eight at a
+# time in the diffusion step, the long-row companion in the score pass.
+ROWS_F32_CASES = [
+    # n, r, G, R, causal, B, H
+    (2048, 10, [0, 1024, 2047], 24, False, 1, 32),
+    (1100, 40, list(range(0, 1100, 50)), 30, True, 2, 30),
+    (1300, 70, list(range(13)) + [650, 1299], 40, False, 4, 16),
+]
+
+
+@pytest.mark.parametrize("case", ROWS_F32_CASES, ids=lambda c: f"n{c[0]}r{c[1]}g{len(c[2])}c{int(c[4])}")
+def test_rows_f32_kernels(orc, case):
+    n, r, G, R, causal, B, H = case
+    print(f"\n[rows f32] n={n} r={r} g={len(G)} R={R} causal={causal} B={B} H={H}", flush=True)
+    g = _gpu_graph(n, r, G, R, 1, causal, 61)
+    rp, cols = _check_csr(orc, g, n, r, G, R, 1, causal, 61)
+    assert B * H * -(-n // 64) >= 1024
+    shape = (B, H, n, 64)
+    q, k, v = (make_tensor(shape, 71 + t, torch.float32) for t in range(3))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    z = sah.attn(qd, kd, vd, g, 3, 0.1)
+    A = sah.scores_softmax(qd, kd, g)
+    zs = sah.diffuse(A, vd, g, 3, 0.1)
+    torch.cuda.synchronize()
+    z_h, zs_h, A_h = _as64(z), _as64(zs), _as64(A)
+    for b, h in {(0, 0), (0, H - 1), (B - 1, H // 2), (B - 1, 1)}:
+        ref = orc.attn(_as64(q[b, h]), _as64(k[b, h]), _as64(v[b, h]), rp[0], cols[0], 3, 0.1,
+                       pu.oracle_threads())
+        pu.assert_z_close(z_h[b, h], ref, "f32", f"attn b={b} h={h}", 3, 0.1)
+        A_got = _a_csr(g, A_h, b, h, H, 0, rp, cols)
+        ref_s = orc.diffuse(A_got, _as64(v[b, h]), rp[0], cols[0], 3, 0.1, pu.oracle_threads())
+        pu.assert_z_close(zs_h[b, h], ref_s, "f32", f"diffuse b={b} h={h}", 3, 0.1)
+
+
+def test_rows_f32_far_maximum(orc):
+    """The fp32 row score kernel's single pass, shifted by each row's own
+    score, is redone with the exact maximum for rows whose weights would
+    pass 2^64 (head 0); the other heads have ordinary inputs."""
+    n, r, G, R, B, H = 2048, 10, [0, 1024], 24, 1, 32
+    g = _gpu_graph(n, r, G, R, 1, False, 43)
+    rp, cols = _check_csr(orc, g, n, r, G, R, 1, False, 43)
+    shape = (B, H, n, 64)
+    q, k, v = (make_tensor(shape, 94 + t, torch.float32) for t in range(3))
+    q[0, 0] = 0
+    q[0, 0, :, 0] = 16.0
+    k[0, 0] = 0
+    k[0, 0, 450, 0] = 45.0            # score 90 for key 450, 0 for every other key
+    z = _as64(sah.attn(q.to(DEV), k.to(DEV), v.to(DEV), g, 5, 0.1))
+    for h in (0, 1, 31):
+        ref = orc.attn(_as64(q[0, h]), _as64(k[0, h]), _as64(v[0, h]), rp[0], cols[0], 5, 0.1)
+        pu.assert_z_close(z[0, h], ref, "f32", f"attn h={h}", 5, 0.1)
+
+
 def _slot_classes(g, gr, n, r, G, causal):
     """Class of every weight slot of graph gr: 0 window, 1 global column,
     2 random, 3 global row, -1 padding."""
