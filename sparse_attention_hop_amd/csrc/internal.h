@@ -355,17 +355,17 @@ diffuser_status blas_gemm(int device, diffuser_dtype t, int64_t M, int64_t N, in
                           const void* A, const void* B, void* C, void* blas_ws,
                           size_t blas_ws_bytes, hipStream_t st);
 
-// The fused fp32 score pass on built graphs (d = 64, n > kLongRow): one wave
-// per row with the window and global-column key rows of each 64-row group
-// in LDS; then the generic long-row companion and the zeroing of the
-// random area's dummy slots (launch_scores_long_fused_f32, also on its own).
+// The fused fp32 score pass on built graphs (d = 64, n > kLongRow, every
+// long row a global row): one wave per row with the window and global-column
+// key rows of each 64-row group in LDS, the long global rows four at a
+// time; then the zeroing of the random area's dummy slots
+// (launch_zero_dummies_f32).
 bool rows_scores_supported(const diffuser_graph& g, const attn_shape& s);
 hipError_t launch_scores_rows(const diffuser_graph& g, const attn_shape& s, const void* Q,
                               const void* K, void* A, float* row_scale, float scale_log2,
                               hipStream_t st);
-hipError_t launch_scores_long_fused_f32(const diffuser_graph& g, const attn_shape& s, const void* Q,
-                                       const void* K, void* A, float* row_scale,
-                                       float scale_log2, hipStream_t st);
+hipError_t launch_zero_dummies_f32(const diffuser_graph& g, const attn_shape& s, void* A,
+                                  hipStream_t st);
 // Normalised edge softmax into fp32 A (generic kernel, any graph).
 hipError_t launch_scores_softmax_f32(const diffuser_graph& g, const attn_shape& s, const void* Q,
                                      const void* K, float* A, float scale_log2, hipStream_t st);

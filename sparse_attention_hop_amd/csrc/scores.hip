@@ -409,15 +409,8 @@ hipError_t launch_f32_d(const diffuser_graph& g, const attn_shape& s, const void
 
 }  // namespace
 
-hipError_t launch_scores_long_fused_f32(const diffuser_graph& g, const attn_shape& s, const void* Q,
-                                       const void* K, void* A, float* row_scale,
-                                       float scale_log2, hipStream_t st) {
-    if (g.max_long > 0)
-        hipLaunchKernelGGL((k_scores_long<float, float, 64>),
-                           dim3((unsigned)g.max_long, (unsigned)(s.B * s.H)),
-                           dim3(kWave * kLongWaves), 0, st, generic_graph(g), s.H,
-                           static_cast<const float*>(Q), static_cast<const float*>(K),
-                           static_cast<float*>(A), row_scale, scale_log2);
+hipError_t launch_zero_dummies_f32(const diffuser_graph& g, const attn_shape& s, void* A,
+                                  hipStream_t st) {
     if (g.rand_apart())
         hipLaunchKernelGGL((k_zero_dummies<float>), dim3(64, (unsigned)(s.B * s.H)), dim3(256), 0,
                            st, g.n, s.H, g.num_graphs, g.d_slot_off, g.d_slot_col, g.d_seg_ptr,

@@ -26,11 +26,12 @@
 //  * random edges: key rows gathered from K in global memory, four
 //    consecutive edges per lane group, their slots and columns in one
 //    16-byte load each.
-// Rows with more than kLongRow slots (global rows, whose segment is every
-// column, or when causal every column up to the row) are left to the
-// generic long-row companion; the shorter global rows of a causal graph's
-// first rows are scored here from K in global memory. The random area's
-// dummy slots are zeroed as the generic pass does.
+// Global rows with more than kLongRow slots (a global row's segment is every
+// column, or when causal every column up to the row) go to a second kernel
+// that scores each key row, read once, for four of them; the shorter
+// global rows of a causal graph's first rows are scored here from K in
+// global memory. The random area's dummy slots are zeroed as the generic
+// pass does.
 #include "internal.h"
 #include "mfma_util.h"
 #include "vec.h"
@@ -130,7 +131,7 @@ void k_scores_rows_f32(SRowsArgs a) {
         if (i >= n) break;
         const int4 ri = info[i];
         const RowSlots rs = a.gg.row(gr, i);
-        if (rs.count() > kLongRow) continue;   // the long-row companion's
+        if (rs.count() > kLongRow) continue;   // a long global row: k_scores_grows_f32's
         // A global row here is one of a causal graph's first rows: its
         // segment holds its columns 0 .. i in order.
         const bool grow = ri.z < 0;
@@ -277,6 +278,179 @@ void k_scores_rows_f32(SRowsArgs a) {
     }
 }
 
+// Long global rows, kGRows per workgroup: the 16 waves split the keys into
+// contiguous ranges and score every key row, read once per workgroup, for
+// all kGRows rows (lane group q taking 4 consecutive keys, their weights
+// stored with one 16-byte store per row); a row's sums meet in LDS in wave
+// order. A row whose weights reach 2^64 is redone by the whole workgroup
+// with its exact maximum: the maximum, the sum, then the normalised weights
+// and c_i over them as stored. Short global rows (a causal graph's first
+// rows) are the row kernel's.
+constexpr int kGRows = 4;
+
+template <int D>
+__global__ __launch_bounds__(kThreads)
+void k_scores_grows_f32(SRowsArgs a, int32_t gblocks) {
+    __shared__ float red[kWaves][kGRows];
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int sub = lane & 15, grp = lane >> 4;
+    const int32_t bh = blockIdx.x / gblocks;
+    const int32_t q0 = (blockIdx.x - bh * gblocks) * kGRows;
+    const int32_t b = bh / a.H, h = bh - b * a.H;
+    const int32_t gr = a.num_graphs == 1 ? 0 : b;
+    const int64_t n = a.n;
+    float* Abh = a.A + a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
+    const float* Kbh = a.K + (int64_t)bh * n * D;
+    const int4* info = a.row_info + (int64_t)gr * n;
+    const int64_t* sp = a.gg.seg_ptr + (int64_t)gr * (n + 1);
+    // The rows: segment start, last column (-1: not this kernel's), q, shift.
+    uint32_t seg[kGRows];
+    int64_t seglen[kGRows];   // slots of the row's segment (when causal, columns 0 .. i, padded)
+    int64_t last[kGRows];
+    f32x4 q[kGRows];
+    float ms[kGRows];
+#pragma unroll
+    for (int r = 0; r < kGRows; ++r) {
+        const int32_t qi = q0 + r;
+        const int64_t i = qi < a.g ? a.G[qi] : -1;
+        seglen[r] = i >= 0 ? sp[i + 1] - sp[i] : 0;
+        const bool mine = seglen[r] > kLongRow;
+        seg[r] = mine ? (uint32_t)info[i].x : 0u;
+        last[r] = !mine ? -1 : a.causal ? i : n - 1;
+        q[r] = mine ? ld4(a.Q + ((int64_t)bh * n + i) * D + 4 * sub) : f32x4{0.f, 0.f, 0.f, 0.f};
+        ms[r] = mine ? a.scale_log2 * group_sum(dot4(q[r], ld4(Kbh + i * D + 4 * sub))) : 0.0f;
+    }
+    const int64_t k0 = n * wave / kWaves, k1 = n * (wave + 1) / kWaves;
+    // f(r, j0, ok[4], scaled scores[4]) for every row and every 4 keys of the wave.
+    auto sweep = [&](auto&& f) {
+        for (int64_t kb = k0 & ~3ll; kb < k1; kb += 16) {
+            const int64_t j0 = kb + 4 * grp;
+            f32x4 kz[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t j = j0 + v;
+                kz[v] = ld4(Kbh + (j >= k0 && j < k1 ? j : 0) * D + 4 * sub);
+            }
+#pragma unroll
+            for (int r = 0; r < kGRows; ++r) {
+                if (last[r] < 0) continue;
+                bool ok[4];
+                float sc[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t j = j0 + v;
+                    ok[v] = j >= k0 && j < k1 && j <= last[r];
+                    sc[v] = a.scale_log2 * group_sum(dot4(q[r], kz[v]));
+                }
+                f(r, j0, ok, sc);
+            }
+        }
+    };
+    // One value per (wave, row) summed (or maxed) over the waves in wave
+    // order, into every thread.
+    auto merge = [&](float (&v)[kGRows], bool is_max) {
+#pragma unroll
+        for (int r = 0; r < kGRows; ++r) {
+#pragma unroll
+            for (int off = 16; off < kWave; off <<= 1) {
+                const float o = __shfl_xor(v[r], off);
+                v[r] = is_max ? fmaxf(v[r], o) : v[r] + o;
+            }
+            if (lane == 0) red[wave][r] = v[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kGRows; ++r) {
+            float t = is_max ? -INFINITY : 0.0f;
+            for (int w = 0; w < kWaves; ++w) t = is_max ? fmaxf(t, red[w][r]) : t + red[w][r];
+            v[r] = t;
+        }
+        __syncthreads();
+    };
+    // Weights w[4] of row r at keys j0 .. j0 + 3 (all four in the segment).
+    auto store = [&](int r, int64_t j0, const float (&w)[4]) {
+        if (sub == 0 && j0 >= 0)
+            *reinterpret_cast<f32x4*>(Abh + seg[r] + j0) = f32x4{w[0], w[1], w[2], w[3]};
+    };
+
+    // The fused single pass, shifted by each row's own score. Keys of the
+    // 4-key block outside the wave's range are another wave's to store.
+    float total[kGRows];
+#pragma unroll
+    for (int r = 0; r < kGRows; ++r) total[r] = 0.0f;
+    sweep([&](int r, int64_t j0, const bool (&ok)[4], const float (&sc)[4]) {
+        float w[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) w[v] = ok[v] ? __builtin_amdgcn_exp2f(sc[v] - ms[r]) : 0.0f;
+        // (a segment is a multiple of 8 slots: the 4 keys lie in it or past it)
+        if (j0 < seglen[r]) {
+            if (j0 >= k0 && j0 + 3 < k1) store(r, j0, w);
+            else if (sub == 0)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (j0 + v >= k0 && j0 + v < k1) Abh[seg[r] + j0 + v] = w[v];
+        }
+        if (sub == 0) total[r] += (w[0] + w[1]) + (w[2] + w[3]);
+    });
+    // Slots past column n - 1 (a segment is a multiple of 8 slots) weigh 0.
+    if (k1 == n && sub == 0) {
+#pragma unroll
+        for (int r = 0; r < kGRows; ++r) {
+            if (last[r] < 0) continue;
+            for (int64_t j = n + grp; j < seglen[r]; j += 4) Abh[seg[r] + j] = 0.0f;
+        }
+    }
+    merge(total, false);
+    bool redo = false;
+#pragma unroll
+    for (int r = 0; r < kGRows; ++r) {
+        if (last[r] < 0) continue;
+        if (total[r] < kSumLimit) {
+            if (threadIdx.x == 0) a.row_scale[(int64_t)bh * n + a.G[q0 + r]] = 1.0f / total[r];
+        } else {
+            redo = true;
+        }
+    }
+    if (!redo) return;   // the same in every thread
+    // Rows whose weights reached 2^64, redone with the exact maximum.
+    float m[kGRows], l[kGRows], st[kGRows];
+#pragma unroll
+    for (int r = 0; r < kGRows; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.0f;
+        st[r] = 0.0f;
+        if (total[r] < kSumLimit) last[r] = -1;   // done
+    }
+    sweep([&](int r, int64_t, const bool (&ok)[4], const float (&sc)[4]) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) m[r] = ok[v] ? fmaxf(m[r], sc[v]) : m[r];
+    });
+    merge(m, true);
+    sweep([&](int r, int64_t, const bool (&ok)[4], const float (&sc)[4]) {
+        if (sub == 0)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) l[r] += ok[v] ? __builtin_amdgcn_exp2f(sc[v] - m[r]) : 0.0f;
+    });
+    merge(l, false);
+    sweep([&](int r, int64_t j0, const bool (&ok)[4], const float (&sc)[4]) {
+        const float inv = 1.0f / l[r];
+        float w[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) w[v] = ok[v] ? __builtin_amdgcn_exp2f(sc[v] - m[r]) * inv : 0.0f;
+        if (sub == 0 && j0 < seglen[r])
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (j0 + v >= k0 && j0 + v < k1) Abh[seg[r] + j0 + v] = w[v];
+        if (sub == 0) st[r] += (w[0] + w[1]) + (w[2] + w[3]);
+    });
+    merge(st, false);
+#pragma unroll
+    for (int r = 0; r < kGRows; ++r)
+        if (last[r] >= 0 && threadIdx.x == 0)
+            a.row_scale[(int64_t)bh * n + a.G[q0 + r]] = 1.0f / st[r];
+}
+
 int32_t win_rows(const diffuser_graph& g) {
     return kRowsPerGroup + (g.causal ? 1 : 2) * g.radius + 8 + kPadRows;
 }
@@ -292,7 +466,10 @@ bool rows_scores_supported(const diffuser_graph& g, const attn_shape& s) {
     for (int64_t x : g.slots)
         if (4 * x >= (1ll << 31)) return false;
     const int64_t groups = (int64_t)s.B * s.H * ((g.n + kRowsPerGroup - 1) / kRowsPerGroup);
-    return groups >= kMinGroups && 2 * lds_bytes(g) <= kLdsLimit;
+    // Every long row must be a global row: a row's window blocks, global
+    // slots and random edges stay within kLongRow.
+    const int64_t row_max = 2 * (int64_t)g.radius + 16 + ((g.num_global + 7) & ~7) + g.rnd_width;
+    return groups >= kMinGroups && 2 * lds_bytes(g) <= kLdsLimit && row_max <= kLongRow;
 }
 
 hipError_t launch_scores_rows(const diffuser_graph& g, const attn_shape& s, const void* Q,
@@ -328,7 +505,13 @@ hipError_t launch_scores_rows(const diffuser_graph& g, const attn_shape& s, cons
                        (size_t)lds_bytes(g), st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_scores_long_fused_f32(g, s, Q, K, A, row_scale, scale_log2, st);
+    if (g.num_global > 0) {
+        const int32_t gblocks = (g.num_global + kGRows - 1) / kGRows;
+        hipLaunchKernelGGL((k_scores_grows_f32<64>), dim3((unsigned)(s.B * s.H * gblocks)),
+                           dim3(kThreads), 0, st, a, gblocks);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return launch_zero_dummies_f32(g, s, A, st);
 }
 
 }  // namespace diffuser
