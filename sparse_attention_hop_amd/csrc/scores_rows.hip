@@ -74,10 +74,21 @@ __device__ __forceinline__ float dot4(const f32x4& q, const f32x4& k) {
     return fmaf(q[3], k[3], fmaf(q[2], k[2], fmaf(q[1], k[1], q[0] * k[0])));
 }
 
-// Sum over the 16 lanes of a lane group (every lane gets it).
+// v plus the value of the lane that DPP control `ctrl` names.
+template <int ctrl>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, true));
+}
+
+// Sum over the 16 lanes of a lane group (every lane gets it), by DPP within
+// each row of 16 lanes: lane pairs, then quads (quad permutations), then
+// the two halves of 8 (half-row mirror) and of 16 (row mirror); each step
+// pairs lanes that hold sums of disjoint sets.
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+    v = dpp_add<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v = dpp_add<0x141>(v);   // row_half_mirror
+    v = dpp_add<0x140>(v);   // row_mirror
     return v;
 }
 
