@@ -19,6 +19,7 @@
 // column over groups of lanes and adds the groups' partial sums in a fixed
 // order, so every sum has a fixed order.
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 #include "vec.h"
@@ -497,7 +498,16 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     const dim3 longs((unsigned)std::max<int64_t>(g.max_long, 1), (unsigned)BH);
     const dim3 long_cols((unsigned)std::max<int64_t>(g.max_long_col, 1), (unsigned)BH);
     const dim3 lblk(kLongThreads);
-    for (int32_t k = 1; k < K; ++k) {
+    // On built graphs (d = 64) the states come from the LDS-window step kernels.
+    const bool rows_states = D == 64 && rows_states_supported(g, p.B, p.H, D);
+    for (int32_t k = 1; k < K && rows_states; ++k) {
+        const hipError_t e = launch_states_rows(
+            g, p.B, p.H, p.A, p.Zs + (size_t)(k - 1) * cnt, V,
+            std::is_same<T, float>::value ? DIFFUSER_F32 : DIFFUSER_BF16, p.Zs + (size_t)k * cnt,
+            step_coefs{keep, p.alpha}, stream);
+        if (e != hipSuccess) return e;
+    }
+    for (int32_t k = 1; k < K && !rows_states; ++k) {
         hipLaunchKernelGGL((k_rows<float, T, float, D>), rows, blk, 0, stream, gg, p.H, BH, p.A,
                            p.Zs + (size_t)(k - 1) * cnt, V, p.Zs + (size_t)k * cnt, keep,
                            p.alpha);

@@ -38,7 +38,7 @@ constexpr int kWaves = 16;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRowsPerWave = 4;
 constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
-constexpr int kPadRows = 32;       // zero rows past the window run and past the globals
+constexpr int kGlobPad = 16;       // zero rows past the globals (a global step reads up to 15 past gs)
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int64_t kMinGroups = 1024;   // workgroups below which the generic step is used
 
@@ -52,7 +52,7 @@ struct RowsArgs {
     const int32_t* G;              // [g]
     const float* A;
     const float* Z;
-    const float* V;
+    const void* V;                 // restart rows (fp32 or bf16), or null when restart = 0
     float* Zn;
     const float* row_scale;        // [B*H][n] or null
     float keep, restart;
@@ -66,6 +66,21 @@ __device__ __forceinline__ f32x4 ld4(const float* p) {
     return *reinterpret_cast<const f32x4*>(p);
 }
 
+// Four channels of a restart row as floats.
+__device__ __forceinline__ f32x4 ldv4(const float* p) { return ld4(p); }
+__device__ __forceinline__ f32x4 ldv4(const bf16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return f32x4{bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
+                 bf16_to_f32(u.y >> 16)};
+}
+
+// keep * acc + restart * V[o .. o + 3], with no read of V when restart = 0.
+template <typename TV>
+__device__ __forceinline__ f32x4 restart4(const RowsArgs& a, int64_t o, float keep, f32x4 acc) {
+    if (a.restart == 0.0f) return keep * acc;
+    return keep * acc + a.restart * ldv4(static_cast<const TV*>(a.V) + o);
+}
+
 __device__ __forceinline__ void fma4(float (&acc)[4], float w, const f32x4& z) {
     acc[0] = fmaf(w, z[0], acc[0]);
     acc[1] = fmaf(w, z[1], acc[1]);
@@ -75,7 +90,7 @@ __device__ __forceinline__ void fma4(float (&acc)[4], float w, const f32x4& z) {
 
 // Eight waves per SIMD (two workgroups per CU, as many waves as the
 // generic step keeps in flight): at most 64 registers per lane.
-template <int D>
+template <int D, typename TV>
 __global__ __launch_bounds__(kThreads, 8)
 void k_diffuse_rows_f32(RowsArgs a) {
     constexpr int L = D / 4;            // lanes per key row (4 channels each)
@@ -104,12 +119,12 @@ void k_diffuse_rows_f32(RowsArgs a) {
     // ---- key rows into LDS ------------------------------------------------
     // Window run: key rows w0 .. w0 + win_rows - 1 (every window slot of the
     // group's rows names one of them), then the g global rows, then
-    // kPadRows zero rows. Rows outside [0, n) are zero.
+    // kGlobPad zero rows. Rows outside [0, n) are zero.
     const int64_t w0 = (r0 - a.radius < 0 ? 0 : r0 - a.radius) & ~7ll;
     float LDS_AS* win = lds;
     float LDS_AS* glob = lds + (int64_t)a.win_rows * D;
     {
-        const int32_t rows = a.win_rows + a.g + kPadRows;
+        const int32_t rows = a.win_rows + a.g + kGlobPad;
         const int32_t units = rows * L;   // 16-byte pieces
         for (int32_t p0 = 64 * wave; p0 < units; p0 += 64 * kWaves) {
             const int32_t p = p0 + lane;
@@ -216,12 +231,10 @@ void k_diffuse_rows_f32(RowsArgs a) {
         }
         if (grp == 0) {
             const int64_t o = ((int64_t)bh * n + i) * D + 4 * sub;
-            const f32x4 v = ld4(a.V + o);
             const float keep =
                 a.row_scale == nullptr ? a.keep : a.keep * a.row_scale[(int64_t)bh * n + i];
             *reinterpret_cast<f32x4*>(a.Zn + o) =
-                f32x4{keep * acc[0] + a.restart * v[0], keep * acc[1] + a.restart * v[1],
-                      keep * acc[2] + a.restart * v[2], keep * acc[3] + a.restart * v[3]};
+                restart4<TV>(a, o, keep, f32x4{acc[0], acc[1], acc[2], acc[3]});
         }
     }
 }
@@ -234,7 +247,7 @@ void k_diffuse_rows_f32(RowsArgs a) {
 // wave order. Columns above the row are padding when causal.
 constexpr int kGRows = 8;
 
-template <int D>
+template <int D, typename TV>
 __global__ __launch_bounds__(kThreads)
 void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
     constexpr int L = D / 4;
@@ -309,26 +322,26 @@ void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
         for (int w = 0; w < kWaves; ++w) sum = sum + part[w][r][s2];
         const int64_t i = a.G[q];
         const int64_t o = ((int64_t)bh * n + i) * D + 4 * s2;
-        const f32x4 v = ld4(a.V + o);
         const float keep =
             a.row_scale == nullptr ? a.keep : a.keep * a.row_scale[(int64_t)bh * n + i];
-        *reinterpret_cast<f32x4*>(a.Zn + o) = keep * sum + a.restart * v;
+        *reinterpret_cast<f32x4*>(a.Zn + o) = restart4<TV>(a, o, keep, sum);
     }
 }
 
 // Key rows of the window run: the group's rows, the radius on either side
-// (on the left only when causal), the 8-column alignment of the window
-// blocks and one 16-column block past the last window column.
+// (on the left only when causal) and the 8-column alignment of its start.
+// A window slot outside its row's window reads run row 0 with weight 0, so
+// the run needs no rows past the last window column.
 int32_t win_rows(const diffuser_graph& g) {
-    return kRowsPerGroup + (g.causal ? 1 : 2) * g.radius + 8 + kPadRows;
+    return kRowsPerGroup + (g.causal ? 1 : 2) * g.radius + 8;
 }
 
 template <int D>
 int32_t lds_bytes(const diffuser_graph& g) {
-    return (win_rows(g) + g.num_global + kPadRows) * D * 4;
+    return (win_rows(g) + g.num_global + kGlobPad) * D * 4;
 }
 
-template <int D>
+template <int D, typename TV>
 hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
                     const void* V, void* Zn, const float* row_scale, step_coefs kc,
                     hipStream_t st) {
@@ -348,7 +361,7 @@ hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A,
     a.G = g.d_global;
     a.A = static_cast<const float*>(A);
     a.Z = static_cast<const float*>(Zk);
-    a.V = static_cast<const float*>(V);
+    a.V = V;
     a.Zn = static_cast<float*>(Zn);
     a.row_scale = row_scale;
     a.keep = kc.keep;
@@ -356,17 +369,17 @@ hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A,
     const int lds = lds_bytes<D>(g);
     static int attr_device = -1;
     if (attr_device != g.device) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_diffuse_rows_f32<D>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_diffuse_rows_f32<D, TV>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
         if (e != hipSuccess) return e;
         attr_device = g.device;
     }
-    hipLaunchKernelGGL((k_diffuse_rows_f32<D>), dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
+    hipLaunchKernelGGL((k_diffuse_rows_f32<D, TV>), dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
                        (size_t)lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.num_global == 0) return e;
     const int32_t gblocks = (g.num_global + kGRows - 1) / kGRows;
-    hipLaunchKernelGGL((k_diffuse_grows_f32<D>), dim3((unsigned)(s.B * s.H * gblocks)),
+    hipLaunchKernelGGL((k_diffuse_grows_f32<D, TV>), dim3((unsigned)(s.B * s.H * gblocks)),
                        dim3(kThreads), 0, st, a, gblocks);
     return hipGetLastError();
 }
@@ -374,21 +387,35 @@ hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A,
 }  // namespace
 
 bool rows_diffuse_supported(const diffuser_graph& g, const attn_shape& s) {
-    if (!g.structured || !g.rand_apart() || g.d_row_info == nullptr || s.dtype != DIFFUSER_F32 ||
-        s.d != 64)
-        return false;
+    return s.dtype == DIFFUSER_F32 && rows_states_supported(g, s.B, s.H, s.d);
+}
+
+bool rows_states_supported(const diffuser_graph& g, int32_t B, int32_t H, int32_t d) {
+    if (!g.structured || !g.rand_apart() || g.d_row_info == nullptr || d != 64) return false;
     for (int64_t x : g.slots)
         if (4 * x >= (1ll << 31)) return false;   // byte offsets of a pair's weights fit 31 bits
     // Enough row groups to give every CU two workgroups twice over; fewer
     // rows run faster one wave per row on the generic step.
-    const int64_t groups = (int64_t)s.B * s.H * ((g.n + kRowsPerGroup - 1) / kRowsPerGroup);
+    const int64_t groups = (int64_t)B * H * ((g.n + kRowsPerGroup - 1) / kRowsPerGroup);
     return groups >= kMinGroups && 2 * lds_bytes<64>(g) <= kLdsLimit;
 }
 
 hipError_t launch_diffuse_rows(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
                                step_coefs kc, hipStream_t st) {
-    return launch_t<64>(g, s, A, Zk, V, Zn, row_scale, kc, st);
+    return launch_t<64, float>(g, s, A, Zk, V, Zn, row_scale, kc, st);
+}
+
+hipError_t launch_states_rows(const diffuser_graph& g, int32_t B, int32_t H, const float* A,
+                              const float* Zk, const void* V, diffuser_dtype v_dtype, float* Zn,
+                              step_coefs kc, hipStream_t st) {
+    attn_shape s{};
+    s.B = B;
+    s.H = H;
+    s.d = 64;
+    s.dtype = DIFFUSER_F32;
+    if (v_dtype == DIFFUSER_F32) return launch_t<64, float>(g, s, A, Zk, V, Zn, nullptr, kc, st);
+    return launch_t<64, bf16_t>(g, s, A, Zk, V, Zn, nullptr, kc, st);
 }
 
 }  // namespace diffuser

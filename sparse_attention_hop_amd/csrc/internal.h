@@ -288,6 +288,12 @@ bool rows_diffuse_supported(const diffuser_graph& g, const attn_shape& s);
 hipError_t launch_diffuse_rows(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
                                step_coefs k, hipStream_t st);
+// The same kernels for fp32 states of a B x H batch whose restart rows V
+// are fp32 or bf16 (d = 64, no row scale): the backward's recomputed states.
+bool rows_states_supported(const diffuser_graph& g, int32_t B, int32_t H, int32_t d);
+hipError_t launch_states_rows(const diffuser_graph& g, int32_t B, int32_t H, const float* A,
+                              const float* Zk, const void* V, diffuser_dtype v_dtype, float* Zn,
+                              step_coefs k, hipStream_t st);
 // The same step on built graphs with a whole channel slice of Z_k resident
 // in LDS (bf16, d = 32 or 64, n up to about 4.5 K keys).
 bool res_diffuse_supported(const diffuser_graph& g, const attn_shape& s);

@@ -952,6 +952,40 @@ def test_backward_headline_shape(orc):
         print(f"[parity] backward b={b} h={h} ok", flush=True)
 
 
+BACKWARD_ROWS_CASES = [
+    # n, r, G, R, ng, causal, B, H, dtype, K, alpha: enough 64-row groups
+    # (B H n / 64 >= 1024) for the LDS-window state kernels, global rows
+    # first, inside and last
+    (2048, 32, [0, 5, 1000, 2047], 24, 1, False, 1, 32, "f32", 5, 0.1),
+    (2048, 40, list(range(0, 2048, 64)), 16, 2, True, 2, 16, "bf16", 3, 0.2),
+    (2056, 24, [7, 2055], 10, 1, False, 1, 32, "bf16", 4, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", BACKWARD_ROWS_CASES,
+                         ids=lambda c: f"n{c[0]}{c[8]}c{int(c[5])}K{c[9]}")
+def test_backward_rows_states(orc, case):
+    """The recomputed fp32 states on built d = 64 graphs with enough rows
+    come from the LDS-window step kernels; sampled (b, h) pairs against the
+    oracle's chain rule."""
+    n, r, G, R, ng, causal, B, H, dt, K, alpha = case
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    print(f"\n[parity] backward rows n={n} B={B} H={H} {dt} causal={causal} K={K}", flush=True)
+    g = _gpu_graph(n, r, G, R, ng, causal, 61)
+    rp, cols = orc.graph(n, r, G, R, ng, causal, 61)
+    shape = (B, H, n, 64)
+    q, k, v, dz = (make_tensor(shape, 121 + i, tdt) for i in range(4))
+    dq, dk, dv = (_as64(x) for x in sah.attn_backward(q.to(DEV), k.to(DEV), v.to(DEV), dz.to(DEV),
+                                                      g, K, alpha))
+    for b, h in [(0, 0), (B - 1, H // 2), (B - 1, H - 1)]:
+        gr = 0 if ng == 1 else b
+        rq, rk, rv = orc.attn_backward(_as64(q[b, h]), _as64(k[b, h]), _as64(v[b, h]),
+                                       _as64(dz[b, h]), rp[gr], cols[gr], K, alpha)
+        _assert_grad_close(dq[b, h], rq, dt, f"dQ b={b} h={h}")
+        _assert_grad_close(dk[b, h], rk, dt, f"dK b={b} h={h}")
+        _assert_grad_close(dv[b, h], rv, dt, f"dV b={b} h={h}")
+
+
 # ---------------------------------------------------------------------------
 # One layer around the path (projections in, head concatenation and
 # output projection out)
