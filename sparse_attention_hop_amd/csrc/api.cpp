@@ -80,6 +80,9 @@ void free_graph_memory(diffuser_graph* g) {
     hipFree(g->d_col_row);
     hipFree(g->d_long_cols);
     hipFree(g->d_long_col_off);
+    hipFree(g->d_trand_ptr);
+    hipFree(g->d_trand_slot);
+    hipFree(g->d_trand_row);
     hipFree(g->d_slot_csr);
     hipFree(g->d_long_rows);
     hipFree(g->d_long_off);
@@ -118,6 +121,9 @@ void free_graph_memory(diffuser_graph* g) {
     g->d_col_row = nullptr;
     g->d_long_cols = nullptr;
     g->d_long_col_off = nullptr;
+    g->d_trand_ptr = nullptr;
+    g->d_trand_slot = nullptr;
+    g->d_trand_row = nullptr;
     g->d_slot_csr = nullptr;
     g->d_long_rows = nullptr;
     g->d_long_off = nullptr;
@@ -333,7 +339,9 @@ bw_layout backward_layout(const diffuser_graph* g, int32_t B, int32_t H, int32_t
 // Builds the graph's column index (once, under bw_mutex): the valid slots
 // of each graph ordered by column, then by row (two stable counting sorts
 // on the host), with the row of each entry, uploaded with per-graph column
-// offsets.
+// offsets. On bidirectional built graphs whose random weights lie past the
+// row segments it also lists each column's random edges (the entries whose
+// slot lies in that area), for the transposed products' row kernels.
 diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
     std::lock_guard<std::mutex> lock(g->bw_mutex);
     if (g->d_col_ptr != nullptr) return DIFFUSER_OK;
@@ -346,6 +354,9 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
     int64_t max_long_col = 0;
     std::vector<int32_t> srow, scol, by_row;
     std::vector<int64_t> cnt;
+    const bool trand = g->structured && g->rand_apart() && !g->causal;
+    std::vector<int64_t> trand_ptr(trand ? (size_t)g->num_graphs * (n + 1) : 0);
+    std::vector<int32_t> trand_slot, trand_row;
     hipError_t e;
     for (int32_t gr = 0; gr < g->num_graphs; ++gr) {
         const int64_t slots = g->slots[gr];
@@ -382,6 +393,23 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
             col_row[base + at] = srow[s];
         }
         col_off[gr + 1] = (int64_t)col_slot.size();
+        if (trand) {
+            int64_t seg_end = 0;
+            if ((e = hipMemcpyAsync(&seg_end, g->d_seg_ptr + (int64_t)gr * (n + 1) + n,
+                                    sizeof(int64_t), hipMemcpyDeviceToHost, st)) != hipSuccess ||
+                (e = hipStreamSynchronize(st)) != hipSuccess)
+                return hip_fail(e, "copy of the segment end for the random column lists");
+            int64_t* tp = trand_ptr.data() + (size_t)gr * (n + 1);
+            for (int64_t j = 0; j < n; ++j) {
+                tp[j] = (int64_t)trand_slot.size();
+                for (int64_t k = cp[j]; k < cp[j + 1]; ++k)
+                    if (col_slot[base + k] >= seg_end) {
+                        trand_slot.push_back(col_slot[base + k]);
+                        trand_row.push_back(col_row[base + k]);
+                    }
+            }
+            tp[n] = (int64_t)trand_slot.size();
+        }
         // Long columns (more than kLongRow entries), for the transposed
         // products' long-column companion.
         for (int64_t j = 0; j < n; ++j)
@@ -389,20 +417,29 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
         long_col_off[gr + 1] = (int64_t)long_cols.size();
         max_long_col = std::max(max_long_col, long_col_off[gr + 1] - long_col_off[gr]);
     }
-    int64_t *d_ptr = nullptr, *d_off = nullptr, *d_loff = nullptr;
-    int32_t *d_slot = nullptr, *d_row = nullptr, *d_lcols = nullptr;
+    int64_t *d_ptr = nullptr, *d_off = nullptr, *d_loff = nullptr, *d_tptr = nullptr;
+    int32_t *d_slot = nullptr, *d_row = nullptr, *d_lcols = nullptr, *d_tslot = nullptr,
+            *d_trow = nullptr;
     if ((e = dev_alloc(&d_ptr, col_ptr.size())) != hipSuccess ||
         (e = dev_alloc(&d_off, col_off.size())) != hipSuccess ||
         (e = dev_alloc(&d_slot, col_slot.size())) != hipSuccess ||
         (e = dev_alloc(&d_row, col_row.size())) != hipSuccess ||
         (e = dev_alloc(&d_lcols, long_cols.size())) != hipSuccess ||
-        (e = dev_alloc(&d_loff, long_col_off.size())) != hipSuccess) {
+        (e = dev_alloc(&d_loff, long_col_off.size())) != hipSuccess ||
+        (trand && ((e = dev_alloc(&d_tptr, trand_ptr.size())) != hipSuccess ||
+                   (e = dev_alloc(&d_tslot, std::max<size_t>(trand_slot.size(), 1))) !=
+                       hipSuccess ||
+                   (e = dev_alloc(&d_trow, std::max<size_t>(trand_row.size(), 1))) !=
+                       hipSuccess))) {
         hipFree(d_ptr);
         hipFree(d_off);
         hipFree(d_slot);
         hipFree(d_row);
         hipFree(d_lcols);
         hipFree(d_loff);
+        hipFree(d_tptr);
+        hipFree(d_tslot);
+        hipFree(d_trow);
         return alloc_status(e, "device allocation of the column index");
     }
     if ((e = hipMemcpyAsync(d_ptr, col_ptr.data(), sizeof(int64_t) * col_ptr.size(),
@@ -420,6 +457,14 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
                              hipMemcpyHostToDevice, st)) != hipSuccess) ||
         (e = hipMemcpyAsync(d_loff, long_col_off.data(), sizeof(int64_t) * long_col_off.size(),
                             hipMemcpyHostToDevice, st)) != hipSuccess ||
+        (trand &&
+         (e = hipMemcpyAsync(d_tptr, trand_ptr.data(), sizeof(int64_t) * trand_ptr.size(),
+                             hipMemcpyHostToDevice, st)) != hipSuccess) ||
+        (trand_slot.size() > 0 &&
+         ((e = hipMemcpyAsync(d_tslot, trand_slot.data(), sizeof(int32_t) * trand_slot.size(),
+                              hipMemcpyHostToDevice, st)) != hipSuccess ||
+          (e = hipMemcpyAsync(d_trow, trand_row.data(), sizeof(int32_t) * trand_row.size(),
+                              hipMemcpyHostToDevice, st)) != hipSuccess)) ||
         (e = hipStreamSynchronize(st)) != hipSuccess) {
         hipFree(d_ptr);
         hipFree(d_off);
@@ -427,6 +472,9 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
         hipFree(d_row);
         hipFree(d_lcols);
         hipFree(d_loff);
+        hipFree(d_tptr);
+        hipFree(d_tslot);
+        hipFree(d_trow);
         return hip_fail(e, "upload of the column index");
     }
     g->d_long_cols = d_lcols;
@@ -436,6 +484,9 @@ diffuser_status ensure_col_index(diffuser_graph* g, hipStream_t st) {
     g->d_col_off_slots = d_off;
     g->d_col_slot = d_slot;
     g->d_col_row = d_row;
+    g->d_trand_ptr = d_tptr;
+    g->d_trand_slot = d_tslot;
+    g->d_trand_row = d_trow;
     return DIFFUSER_OK;
 }
 

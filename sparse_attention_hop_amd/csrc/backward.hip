@@ -519,13 +519,26 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     // G_K = dZ, G_k = (1 - alpha) A^T G_{k+1}; dV = alpha (G_K + .. + G_1).
     hipLaunchKernelGGL((k_axpby<T>), grid_elems(cnt), blk, 0, stream, cnt,
                        static_cast<const T*>(p.dZ), p.Gs + (size_t)K * cnt, 1.0f, 0.0f);
-    if (K > 0)
+    // On bidirectional built graphs (d = 64) A^T is laid out in the graph's
+    // own slot geometry and the products run on the LDS-window step kernels.
+    const bool rows_cols = D == 64 && K > 0 && rows_transposed_supported(g, p.B, p.H, D);
+    if (rows_cols) {
+        const hipError_t e = launch_transpose_struct(g, p.B, p.H, p.A, p.At, stream);
+        if (e != hipSuccess) return e;
+    } else if (K > 0) {
         hipLaunchKernelGGL(k_to_columns, entries, blk, 0, stream, ci, p.H, BH, entry_blocks, p.A,
                            p.At);
+    }
     for (int32_t k = K - 1; k >= 0; --k) {
         const float* Gk1 = p.Gs + (size_t)(k + 1) * cnt;
         hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, Gk1, p.dV,
                            p.alpha, k == K - 1 ? 0.0f : 1.0f);
+        if (rows_cols) {
+            const hipError_t e = launch_transposed_rows(g, p.B, p.H, p.At, p.A, Gk1,
+                                                        p.Gs + (size_t)k * cnt, keep, stream);
+            if (e != hipSuccess) return e;
+            continue;
+        }
         hipLaunchKernelGGL((k_cols<float, float, D>), rows, blk, 0, stream, ci, p.H, BH, p.At, Gk1,
                            p.Gs + (size_t)k * cnt, keep);
         if (g.max_long_col > 0)

@@ -51,6 +51,11 @@ struct RowsArgs {
     const int4* row_info;          // [graphs][n]
     const int32_t* G;              // [g]
     const float* A;
+    const float* AR;               // weights of the random edges' slots (A unless transposed)
+    // Random edges by column (transposed products), or null: the graph's rows.
+    const int64_t* t_ptr;          // [graphs][n + 1]
+    const int32_t* t_slot;
+    const int32_t* t_row;
     const float* Z;
     const void* V;                 // restart rows (fp32 or bf16), or null when restart = 0
     float* Zn;
@@ -114,6 +119,8 @@ void k_diffuse_rows_f32(RowsArgs a) {
     const int64_t pair_slots = a.num_graphs == 1 ? a.gg.slot_off[1]
                                                  : a.gg.slot_off[gr + 1] - a.gg.slot_off[gr];
     const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(Abh, (uint32_t)(4 * pair_slots));
+    const __amdgpu_buffer_rsrc_t rAR = buffer_rsrc(
+        a.AR + a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h), (uint32_t)(4 * pair_slots));
     const __amdgpu_buffer_rsrc_t rG = buffer_rsrc(a.G, (uint32_t)(4 * a.g));
 
     // ---- key rows into LDS ------------------------------------------------
@@ -147,7 +154,6 @@ void k_diffuse_rows_f32(RowsArgs a) {
         if (i >= n) break;
         const int4 ri = info[i];
         if (ri.z < 0) continue;   // a global row: k_diffuse_grows_f32's
-        const RowSlots rs = a.gg.row(gr, i);
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         {
             const int64_t lo = i - a.radius < 0 ? 0 : i - a.radius;
@@ -199,9 +205,21 @@ void k_diffuse_rows_f32(RowsArgs a) {
             // base + 4 grp + v, their slots and columns in one 16-byte load
             // each; the next step's slots and columns are requested before
             // this step's rows are used.
-            const int32_t nr = rs.rcnt;
-            const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(rs.rslot, (uint32_t)(4 * nr));
-            const __amdgpu_buffer_rsrc_t rC = buffer_rsrc(rs.rcol, (uint32_t)(4 * nr));
+            int32_t nr;
+            const int32_t *rslot, *rcol;
+            if (a.t_ptr == nullptr) {
+                const RowSlots rs = a.gg.row(gr, i);
+                nr = rs.rcnt;
+                rslot = rs.rslot;
+                rcol = rs.rcol;
+            } else {
+                const int64_t t0 = a.t_ptr[(int64_t)gr * (n + 1) + i];
+                nr = (int32_t)(a.t_ptr[(int64_t)gr * (n + 1) + i + 1] - t0);
+                rslot = a.t_slot + t0;
+                rcol = a.t_row + t0;
+            }
+            const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(rslot, (uint32_t)(4 * nr));
+            const __amdgpu_buffer_rsrc_t rC = buffer_rsrc(rcol, (uint32_t)(4 * nr));
             auto idx = [&](int32_t base, u32x4& sl, u32x4& cl) {
                 const int32_t e0 = base + 4 * grp;
                 sl = bload16(rS, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
@@ -216,7 +234,7 @@ void k_diffuse_rows_f32(RowsArgs a) {
                 for (int v = 0; v < 4; ++v) {
                     const bool ok = base + 4 * grp + v < nr;
                     w[v] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-                        rA, ok ? (int)(4u * sl[v]) : (int)kOutside, 0, 0));
+                        rAR, ok ? (int)(4u * sl[v]) : (int)kOutside, 0, 0));
                     z[v] = ld4(Zbh + (int64_t)(ok ? (int32_t)cl[v] : 0) * D + 4 * sub);
                 }
                 idx(base + 4 * NG, sl, cl);
@@ -328,6 +346,73 @@ void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
     }
 }
 
+// Transposed weights of a bidirectional built graph in the graph's own
+// slot geometry, for the transposed product A^T X: the columns of A^T's
+// row j are the rows i with an edge (i, j), which on these graphs are the
+// window rows |i - j| <= r, the global rows and, for a global j, every
+// row; so row j's window slot for column i and its global slot t (for
+// G[t]) hold A_ij and A_{G[t] j}, and a global row j's slot i holds A_ij.
+// The random edges are listed by column apart. One wave per row j, its
+// lanes over the segment's slots; padding slots are 0. For a source row
+// i, A_ij lies in its full segment when i is global, in its window when
+// |i - j| <= r, and otherwise (j is then a global column) in its global
+// slot for j.
+__global__ __launch_bounds__(kThreads)
+void k_transpose_struct(RowsArgs a, float* __restrict__ At) {
+    const int lane = __lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int64_t n = a.n;
+    const int32_t per = (int32_t)((n + kWaves - 1) / kWaves);
+    const int32_t bh = blockIdx.x / per;
+    const int64_t j = (int64_t)(blockIdx.x - bh * per) * kWaves + wave;
+    if (j >= n) return;
+    const int32_t b = bh / a.H, h = bh - b * a.H;
+    const int32_t gr = a.num_graphs == 1 ? 0 : b;
+    const int64_t off = a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
+    const float* Ab = a.A + off;
+    float* Atb = At + off;
+    const int4* info = a.row_info + (int64_t)gr * n;
+    const int4 rj = info[j];
+    const int64_t r = a.radius;
+    // Position of j among the globals (a global row of A^T is a global
+    // column of A), else -1.
+    int32_t tj = -1;
+    if (rj.z < 0) {
+        int32_t lo = 0, hi = a.g;
+        while (lo < hi) {
+            const int32_t mid = (lo + hi) / 2;
+            if (a.G[mid] < j) lo = mid + 1;
+            else hi = mid;
+        }
+        tj = lo < a.g && a.G[lo] == j ? lo : -1;
+    }
+    const int64_t nslot = a.gg.row(gr, j).seg_len;
+    for (int64_t s = lane; s < nslot; s += kWave) {
+        int64_t i = 0;   // the row of A that slot s of row j of A^T names
+        bool valid;
+        if (rj.z < 0) {
+            i = s;
+            valid = s < n;
+        } else if (s < rj.z) {
+            i = rj.y + s;
+            valid = i < n && i >= j - r && i <= j + r;
+        } else {
+            const int64_t t = s - rj.z;
+            valid = t < a.g;
+            if (valid) i = a.G[t];
+            valid = valid && (i < j - r || i > j + r);
+        }
+        float w = 0.0f;
+        if (valid) {
+            const int4 ri = info[i];
+            if (ri.z < 0) w = Ab[(int64_t)ri.x + j];
+            else if (j >= i - r && j <= i + r) w = Ab[(int64_t)ri.x + (j - ri.y)];
+            else if (tj >= 0) w = Ab[(int64_t)ri.x + ri.z + tj];
+        }
+        Atb[(int64_t)rj.x + s] = w;
+    }
+}
+
 // Key rows of the window run: the group's rows, the radius on either side
 // (on the left only when causal) and the 8-column alignment of its start.
 // A window slot outside its row's window reads run row 0 with weight 0, so
@@ -341,10 +426,8 @@ int32_t lds_bytes(const diffuser_graph& g) {
     return (win_rows(g) + g.num_global + kGlobPad) * D * 4;
 }
 
-template <int D, typename TV>
-hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
-                    const void* V, void* Zn, const float* row_scale, step_coefs kc,
-                    hipStream_t st) {
+RowsArgs make_args(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
+                   const void* V, void* Zn, const float* row_scale, step_coefs kc) {
     RowsArgs a;
     a.n = g.n;
     a.H = s.H;
@@ -360,12 +443,22 @@ hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A,
     a.row_info = reinterpret_cast<const int4*>(g.d_row_info);
     a.G = g.d_global;
     a.A = static_cast<const float*>(A);
+    a.AR = a.A;
+    a.t_ptr = nullptr;
+    a.t_slot = nullptr;
+    a.t_row = nullptr;
     a.Z = static_cast<const float*>(Zk);
     a.V = V;
     a.Zn = static_cast<float*>(Zn);
     a.row_scale = row_scale;
     a.keep = kc.keep;
     a.restart = kc.restart;
+    return a;
+}
+
+template <int D, typename TV>
+hipError_t launch_args(const diffuser_graph& g, const attn_shape& s, const RowsArgs& a,
+                       hipStream_t st) {
     const int lds = lds_bytes<D>(g);
     static int attr_device = -1;
     if (attr_device != g.device) {
@@ -382,6 +475,13 @@ hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A,
     hipLaunchKernelGGL((k_diffuse_grows_f32<D, TV>), dim3((unsigned)(s.B * s.H * gblocks)),
                        dim3(kThreads), 0, st, a, gblocks);
     return hipGetLastError();
+}
+
+template <int D, typename TV>
+hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
+                    const void* V, void* Zn, const float* row_scale, step_coefs kc,
+                    hipStream_t st) {
+    return launch_args<D, TV>(g, s, make_args(g, s, A, Zk, V, Zn, row_scale, kc), st);
 }
 
 }  // namespace
@@ -404,6 +504,40 @@ hipError_t launch_diffuse_rows(const diffuser_graph& g, const attn_shape& s, con
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
                                step_coefs kc, hipStream_t st) {
     return launch_t<64, float>(g, s, A, Zk, V, Zn, row_scale, kc, st);
+}
+
+bool rows_transposed_supported(const diffuser_graph& g, int32_t B, int32_t H, int32_t d) {
+    return !g.causal && g.d_trand_ptr != nullptr && rows_states_supported(g, B, H, d);
+}
+
+hipError_t launch_transpose_struct(const diffuser_graph& g, int32_t B, int32_t H, const float* A,
+                                   float* At, hipStream_t st) {
+    attn_shape s{};
+    s.B = B;
+    s.H = H;
+    s.d = 64;
+    s.dtype = DIFFUSER_F32;
+    const RowsArgs a = make_args(g, s, A, nullptr, nullptr, nullptr, nullptr, step_coefs{0.f, 0.f});
+    const int64_t per = (g.n + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(k_transpose_struct, dim3((unsigned)(B * H * per)), dim3(kThreads), 0, st, a,
+                       At);
+    return hipGetLastError();
+}
+
+hipError_t launch_transposed_rows(const diffuser_graph& g, int32_t B, int32_t H, const float* At,
+                                  const float* A, const float* X, float* Y, float scale,
+                                  hipStream_t st) {
+    attn_shape s{};
+    s.B = B;
+    s.H = H;
+    s.d = 64;
+    s.dtype = DIFFUSER_F32;
+    RowsArgs a = make_args(g, s, At, X, nullptr, Y, nullptr, step_coefs{scale, 0.f});
+    a.AR = A;
+    a.t_ptr = g.d_trand_ptr;
+    a.t_slot = g.d_trand_slot;
+    a.t_row = g.d_trand_row;
+    return launch_args<64, float>(g, s, a, st);
 }
 
 hipError_t launch_states_rows(const diffuser_graph& g, int32_t B, int32_t H, const float* A,

@@ -196,6 +196,14 @@ struct diffuser_graph {
     int64_t max_long_col = 0;
     int32_t* d_long_cols = nullptr;      // [long columns of all graphs]
     int64_t* d_long_col_off = nullptr;   // [num_graphs + 1]
+    // Random edges by column (built with the column index on bidirectional
+    // graphs whose random weights lie outside the row segments): for graph
+    // gr and column j, entries d_trand_ptr[gr (n + 1) + j] .. + 1 hold the
+    // weight slot (within the graph) and the row of each random edge (i, j),
+    // rows ascending.
+    int64_t* d_trand_ptr = nullptr;      // [num_graphs][n + 1]
+    int32_t* d_trand_slot = nullptr;
+    int32_t* d_trand_row = nullptr;
 };
 
 namespace diffuser {
@@ -294,6 +302,16 @@ bool rows_states_supported(const diffuser_graph& g, int32_t B, int32_t H, int32_
 hipError_t launch_states_rows(const diffuser_graph& g, int32_t B, int32_t H, const float* A,
                               const float* Zk, const void* V, diffuser_dtype v_dtype, float* Zn,
                               step_coefs k, hipStream_t st);
+// The transposed product Y = scale * A^T X on the same kernels for
+// bidirectional built graphs once the column index (and with it the random
+// edges by column) exists: At = A^T in the graph's slot geometry
+// (launch_transpose_struct), the random weights read from A.
+bool rows_transposed_supported(const diffuser_graph& g, int32_t B, int32_t H, int32_t d);
+hipError_t launch_transpose_struct(const diffuser_graph& g, int32_t B, int32_t H, const float* A,
+                                   float* At, hipStream_t st);
+hipError_t launch_transposed_rows(const diffuser_graph& g, int32_t B, int32_t H, const float* At,
+                                  const float* A, const float* X, float* Y, float scale,
+                                  hipStream_t st);
 // The same step on built graphs with a whole channel slice of Z_k resident
 // in LDS (bf16, d = 32 or 64, n up to about 4.5 K keys).
 bool res_diffuse_supported(const diffuser_graph& g, const attn_shape& s);

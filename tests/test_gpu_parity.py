@@ -959,15 +959,18 @@ BACKWARD_ROWS_CASES = [
     (2048, 32, [0, 5, 1000, 2047], 24, 1, False, 1, 32, "f32", 5, 0.1),
     (2048, 40, list(range(0, 2048, 64)), 16, 2, True, 2, 16, "bf16", 3, 0.2),
     (2056, 24, [7, 2055], 10, 1, False, 1, 32, "bf16", 4, 0.0),
+    # random weights in groups past the row segments (n > 4576)
+    (6000, 16, [0, 2999, 5999], 12, 1, False, 1, 12, "f32", 2, 0.1),
 ]
 
 
 @pytest.mark.parametrize("case", BACKWARD_ROWS_CASES,
                          ids=lambda c: f"n{c[0]}{c[8]}c{int(c[5])}K{c[9]}")
 def test_backward_rows_states(orc, case):
-    """The recomputed fp32 states on built d = 64 graphs with enough rows
-    come from the LDS-window step kernels; sampled (b, h) pairs against the
-    oracle's chain rule."""
+    """On built d = 64 graphs with enough rows the recomputed fp32 states
+    and (bidirectional graphs) the transposed products come from the
+    LDS-window step kernels; sampled (b, h) pairs against the oracle's
+    chain rule."""
     n, r, G, R, ng, causal, B, H, dt, K, alpha = case
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     print(f"\n[parity] backward rows n={n} B={B} H={H} {dt} causal={causal} K={K}", flush=True)
