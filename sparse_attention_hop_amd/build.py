@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libdiffuser.so")
 SOURCES = ["api.cpp", "block_graph.cpp", "graph_build.hip", "scores.hip", "scores_fast.hip", "scores_rows.hip",
-           "diffuse.hip", "diffuse_fast.hip", "diffuse_res.hip", "diffuse_rows.hip", "block_fast.hip", "backward.hip", "layer.hip",
+           "diffuse.hip", "diffuse_fast.hip", "diffuse_res.hip", "diffuse_rows.hip", "block_fast.hip", "backward.hip", "dots_mfma.hip", "layer.hip",
            "csr_order.hip"]
 ARCH = "gfx950"
 

@@ -234,8 +234,10 @@ __device__ __forceinline__ void edge_dots_range(const RowSlots& rs, const float*
 
 // dA[s] = a * sum_{k < K} G_{k+1}[i] . Z_k[col(s)] for the slots of row i
 // (padding slots get 0): groups of L lanes take one slot each (L = D / 4
-// lanes of 4 channels); state k of G or Z starts at k * stride.
-template <int D>
+// lanes of 4 channels); state k of G or Z starts at k * stride. kRandOnly:
+// only the row's random slots (kept apart from its segment), whatever the
+// row's length.
+template <int D, bool kRandOnly>
 __global__ __launch_bounds__(kThreads)
 void k_edge_dots(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict__ Gs,
                  const float* __restrict__ Zs, int64_t stride, int32_t K, float* __restrict__ dA,
@@ -254,6 +256,10 @@ void k_edge_dots(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict
     const float* Gi = Gs + stride + ((int64_t)bh * n + i) * D + 4 * sub;
     const float* Zb = Zs + (int64_t)bh * n * D + 4 * sub;
     const int64_t cnt = rs.count();
+    if (kRandOnly) {
+        if (rs.rcnt > 0) edge_dots_range<D>(rs, Gi, Zb, stride, K, dAb, a, rs.seg_len, cnt, grp, sub);
+        return;
+    }
     if (cnt > kLongRow) return;   // k_edge_dots_long's
     edge_dots_range<D>(rs, Gi, Zb, stride, K, dAb, a, 0, cnt, grp, sub);
 }
@@ -546,12 +552,21 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
                                g.d_long_cols, g.d_long_col_off, p.At, Gk1,
                                p.Gs + (size_t)k * cnt, keep);
     }
-    // dA = (1 - alpha) sum_k G_{k+1} Z_k^T on the edges.
-    hipLaunchKernelGGL((k_edge_dots<D>), rows, blk, 0, stream, gg, p.H, BH, p.Gs, p.Zs, cnt, K,
-                       p.dA, keep);
-    if (g.max_long > 0)
-        hipLaunchKernelGGL((k_edge_dots_long<D>), longs, lblk, 0, stream, gg, p.H, p.Gs, p.Zs, cnt,
-                           K, p.dA, keep);
+    // dA = (1 - alpha) sum_k G_{k+1} Z_k^T on the edges (on built d = 64
+    // graphs the window bands, global columns and global rows on MFMA, the
+    // random edges gathered).
+    if (D == 64 && K > 0 && mfma_dots_supported(g, D)) {
+        const hipError_t e = launch_dots_dense(g, p.B, p.H, p.Gs, p.Zs, cnt, K, keep, p.dA, stream);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_edge_dots<D, true>), rows, blk, 0, stream, gg, p.H, BH, p.Gs, p.Zs,
+                           cnt, K, p.dA, keep);
+    } else {
+        hipLaunchKernelGGL((k_edge_dots<D, false>), rows, blk, 0, stream, gg, p.H, BH, p.Gs, p.Zs, cnt, K,
+                           p.dA, keep);
+        if (g.max_long > 0)
+            hipLaunchKernelGGL((k_edge_dots_long<D>), longs, lblk, 0, stream, gg, p.H, p.Gs, p.Zs,
+                               cnt, K, p.dA, keep);
+    }
     // dV = (sum of alpha G_{k+1}) + G_0.
     if (K == 0)
         hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, p.Gs, p.dV,

@@ -388,6 +388,13 @@ bool rows_scores_supported(const diffuser_graph& g, const attn_shape& s);
 hipError_t launch_scores_rows(const diffuser_graph& g, const attn_shape& s, const void* Q,
                               const void* K, void* A, float* row_scale, float scale_log2,
                               hipStream_t st);
+// dA_ij = f sum_{k < K} Gs_{k+1}[i] . Zs_k[j] on the segment slots of a
+// built graph (window bands, global columns, global rows) on MFMA, d = 64;
+// the random slots are left to the caller. K >= 1.
+bool mfma_dots_supported(const diffuser_graph& g, int32_t d);
+hipError_t launch_dots_dense(const diffuser_graph& g, int32_t B, int32_t H, const float* Gs,
+                             const float* Zs, int64_t stride, int32_t K, float f, float* dA,
+                             hipStream_t st);
 hipError_t launch_zero_dummies_f32(const diffuser_graph& g, const attn_shape& s, void* A,
                                   hipStream_t st);
 // Normalised edge softmax into fp32 A (generic kernel, any graph).

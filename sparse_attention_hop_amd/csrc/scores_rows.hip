@@ -44,7 +44,6 @@ constexpr int kWaves = 16;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRowsPerWave = 4;
 constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
-constexpr int kPadRows = 32;
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int64_t kMinGroups = 1024;
 constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
@@ -110,16 +109,16 @@ void k_scores_rows_f32(SRowsArgs a) {
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
     const int64_t n = a.n;
     float* Abh = a.A + a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
-    const float* Kbh = a.K + (int64_t)bh * n * D;
     const int4* info = a.row_info + (int64_t)gr * n;
     const __amdgpu_buffer_rsrc_t rG = buffer_rsrc(a.G, (uint32_t)(4 * a.g));
-
-    // ---- key rows into LDS (as the fp32 diffusion step's) -----------------
     const int64_t w0 = (r0 - a.radius < 0 ? 0 : r0 - a.radius) & ~7ll;
     float LDS_AS* win = lds;
     float LDS_AS* glob = lds + (int64_t)a.win_rows * D;
+    const float* Kbh = a.K + (int64_t)bh * n * D;
+
+    // ---- key rows into LDS (as the fp32 diffusion step's) -----------------
     {
-        const int32_t rows = a.win_rows + a.g + kPadRows;
+        const int32_t rows = a.win_rows + a.g;
         const int32_t units = rows * 16;
         for (int32_t p0 = 64 * wave; p0 < units; p0 += 64 * kWaves) {
             const int32_t p = p0 + lane;
@@ -462,30 +461,41 @@ void k_scores_grows_f32(SRowsArgs a, int32_t gblocks) {
             a.row_scale[(int64_t)bh * n + a.G[q0 + r]] = 1.0f / st[r];
 }
 
+// Key rows of the window run: the group's rows, the radius on either side
+// (on the left only when causal) and the 8-column alignment of its start.
+// A slot outside its row's window or global set reads LDS row 0 with a
+// zero weight, so no rows are needed past the run or past the globals.
 int32_t win_rows(const diffuser_graph& g) {
-    return kRowsPerGroup + (g.causal ? 1 : 2) * g.radius + 8 + kPadRows;
+    return kRowsPerGroup + (g.causal ? 1 : 2) * g.radius + 8;
 }
 
-int32_t lds_bytes(const diffuser_graph& g) { return (win_rows(g) + g.num_global + kPadRows) * 64 * 4; }
+int32_t lds_bytes(const diffuser_graph& g) { return (win_rows(g) + g.num_global) * 64 * 4; }
 
-}  // namespace
-
-bool rows_scores_supported(const diffuser_graph& g, const attn_shape& s) {
-    if (!g.structured || !g.rand_apart() || g.d_row_info == nullptr || s.dtype != DIFFUSER_F32 ||
-        s.d != 64 || g.n <= kLongRow)
-        return false;
-    for (int64_t x : g.slots)
-        if (4 * x >= (1ll << 31)) return false;
-    const int64_t groups = (int64_t)s.B * s.H * ((g.n + kRowsPerGroup - 1) / kRowsPerGroup);
-    // Every long row must be a global row: a row's window blocks, global
-    // slots and random edges stay within kLongRow.
-    const int64_t row_max = 2 * (int64_t)g.radius + 16 + ((g.num_global + 7) & ~7) + g.rnd_width;
-    return groups >= kMinGroups && 2 * lds_bytes(g) <= kLdsLimit && row_max <= kLongRow;
+hipError_t launch_args(const diffuser_graph& g, const attn_shape& s, const SRowsArgs& a,
+                       hipStream_t st) {
+    static int attr_device = -1;
+    if (attr_device != g.device) {
+        hipError_t e =
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_scores_rows_f32<64>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+        if (e != hipSuccess) return e;
+        attr_device = g.device;
+    }
+    hipLaunchKernelGGL((k_scores_rows_f32<64>), dim3((unsigned)(8 * a.per_xcd)),
+                       dim3(kThreads), (size_t)lds_bytes(g), st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (g.num_global > 0) {
+        const int32_t gblocks = (g.num_global + kGRows - 1) / kGRows;
+        hipLaunchKernelGGL((k_scores_grows_f32<64>), dim3((unsigned)(s.B * s.H * gblocks)),
+                           dim3(kThreads), 0, st, a, gblocks);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
-hipError_t launch_scores_rows(const diffuser_graph& g, const attn_shape& s, const void* Q,
-                              const void* K, void* A, float* row_scale, float scale_log2,
-                              hipStream_t st) {
+SRowsArgs make_sargs(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
+                     void* A, float* row_scale, float scale_log2) {
     SRowsArgs a;
     a.n = g.n;
     a.H = s.H;
@@ -505,23 +515,30 @@ hipError_t launch_scores_rows(const diffuser_graph& g, const attn_shape& s, cons
     a.A = static_cast<float*>(A);
     a.row_scale = row_scale;
     a.scale_log2 = scale_log2;
-    static int attr_device = -1;
-    if (attr_device != g.device) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_scores_rows_f32<64>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
-        if (e != hipSuccess) return e;
-        attr_device = g.device;
-    }
-    hipLaunchKernelGGL((k_scores_rows_f32<64>), dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
-                       (size_t)lds_bytes(g), st, a);
-    hipError_t e = hipGetLastError();
+    return a;
+}
+
+}  // namespace
+
+bool rows_scores_supported(const diffuser_graph& g, const attn_shape& s) {
+    if (!g.structured || !g.rand_apart() || g.d_row_info == nullptr || s.dtype != DIFFUSER_F32 ||
+        s.d != 64 || g.n <= kLongRow)
+        return false;
+    for (int64_t x : g.slots)
+        if (4 * x >= (1ll << 31)) return false;
+    const int64_t groups = (int64_t)s.B * s.H * ((g.n + kRowsPerGroup - 1) / kRowsPerGroup);
+    // Every long row must be a global row: a row's window blocks, global
+    // slots and random edges stay within kLongRow.
+    const int64_t row_max = 2 * (int64_t)g.radius + 16 + ((g.num_global + 7) & ~7) + g.rnd_width;
+    return groups >= kMinGroups && 2 * lds_bytes(g) <= kLdsLimit && row_max <= kLongRow;
+}
+
+hipError_t launch_scores_rows(const diffuser_graph& g, const attn_shape& s, const void* Q,
+                              const void* K, void* A, float* row_scale, float scale_log2,
+                              hipStream_t st) {
+    const hipError_t e =
+        launch_args(g, s, make_sargs(g, s, Q, K, A, row_scale, scale_log2), st);
     if (e != hipSuccess) return e;
-    if (g.num_global > 0) {
-        const int32_t gblocks = (g.num_global + kGRows - 1) / kGRows;
-        hipLaunchKernelGGL((k_scores_grows_f32<64>), dim3((unsigned)(s.B * s.H * gblocks)),
-                           dim3(kThreads), 0, st, a, gblocks);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
     return launch_zero_dummies_f32(g, s, A, st);
 }
 
