@@ -1439,8 +1439,9 @@ diffuser_status diffuser_attn_backward(const void* Q, const void* K, const void*
     p.Gs = reinterpret_cast<float*>(ws + 3 * w.a + w.zs);
     p.dV = reinterpret_cast<float*>(ws + 3 * w.a + w.zs + w.gs);
     const float scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
+    // p.dV (B H n d floats) is free until the G steps: the row scales.
     hipError_t e = launch_scores_softmax_f32(*g, attn_shape{B, H, d, dtype}, Q, K, p.A,
-                                             scale_log2, st);
+                                             scale_log2, st, p.dV);
     if (e != hipSuccess) return hip_fail(e, "score/softmax launch");
     e = launch_backward(*g, p, st);
     if (e != hipSuccess) return hip_fail(e, "backward launch");

@@ -385,6 +385,8 @@ diffuser_status blas_gemm(int device, diffuser_dtype t, int64_t M, int64_t N, in
 // time; then the zeroing of the random area's dummy slots
 // (launch_zero_dummies_f32).
 bool rows_scores_supported(const diffuser_graph& g, const attn_shape& s);
+// The same for fp32 or bf16 queries and keys (the weights are fp32).
+bool rows_scores_any_supported(const diffuser_graph& g, const attn_shape& s);
 hipError_t launch_scores_rows(const diffuser_graph& g, const attn_shape& s, const void* Q,
                               const void* K, void* A, float* row_scale, float scale_log2,
                               hipStream_t st);
@@ -397,8 +399,11 @@ hipError_t launch_dots_dense(const diffuser_graph& g, int32_t B, int32_t H, cons
                              hipStream_t st);
 hipError_t launch_zero_dummies_f32(const diffuser_graph& g, const attn_shape& s, void* A,
                                   hipStream_t st);
-// Normalised edge softmax into fp32 A (generic kernel, any graph).
+// Normalised edge softmax into fp32 A (any graph). With row_scale (B*H*n
+// floats of scratch) built d = 64 graphs take the fused LDS-window pass and
+// a normalisation; otherwise the generic kernel.
 hipError_t launch_scores_softmax_f32(const diffuser_graph& g, const attn_shape& s, const void* Q,
-                                     const void* K, float* A, float scale_log2, hipStream_t st);
+                                     const void* K, float* A, float scale_log2, hipStream_t st,
+                                     float* row_scale);
 
 }  // namespace diffuser

@@ -349,6 +349,33 @@ void k_zero_dummies(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __r
         if (cols[s] < 0) chunk<T>::store1(Ab + s, 0.0f);
 }
 
+// A[s] *= c[row(s)] over the slots of each (b, h) block of fp32 weights
+// (padding, row -1, untouched): stored weights normalised by their rows'
+// scale. Four slots per thread (a graph's slots are a multiple of 8, its
+// blocks 32-byte aligned).
+__global__ __launch_bounds__(256)
+void k_scale_rows(int64_t n, int32_t H, int32_t num_graphs, const int64_t* __restrict__ slot_off,
+                  const int32_t* __restrict__ slot_row, const float* __restrict__ c,
+                  float* __restrict__ A) {
+    const int32_t bh = blockIdx.y;
+    const int32_t b = bh / H, h = bh - b * H;
+    const int32_t gr = num_graphs == 1 ? 0 : b;
+    const int64_t quads = (slot_off[gr + 1] - slot_off[gr]) / 4;
+    const int4* rows = reinterpret_cast<const int4*>(slot_row + slot_off[gr]);
+    const float* cb = c + (int64_t)bh * n;
+    float4* Ab = reinterpret_cast<float4*>(A + a_block_offset(slot_off, num_graphs, H, b, h));
+    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < quads;
+         s += (int64_t)gridDim.x * blockDim.x) {
+        const int4 r = rows[s];
+        float4 w = Ab[s];
+        if (r.x >= 0) w.x *= cb[r.x];
+        if (r.y >= 0) w.y *= cb[r.y];
+        if (r.z >= 0) w.z *= cb[r.z];
+        if (r.w >= 0) w.w *= cb[r.w];
+        Ab[s] = w;
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* Q, const void* K,
                     void* A, float* row_scale, float scale_log2, hipStream_t st) {
@@ -419,7 +446,18 @@ hipError_t launch_zero_dummies_f32(const diffuser_graph& g, const attn_shape& s,
 }
 
 hipError_t launch_scores_softmax_f32(const diffuser_graph& g, const attn_shape& s, const void* Q,
-                                     const void* K, float* A, float scale_log2, hipStream_t st) {
+                                     const void* K, float* A, float scale_log2, hipStream_t st,
+                                     float* row_scale) {
+    // Built d = 64 graphs: the fused LDS-window pass (weights and row
+    // scales), then the weights normalised in place.
+    if (row_scale != nullptr && (reinterpret_cast<uintptr_t>(A) & 15u) == 0 &&
+        rows_scores_any_supported(g, s)) {
+        hipError_t e = launch_scores_rows(g, s, Q, K, A, row_scale, scale_log2, st);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_scale_rows, dim3(256, (unsigned)(s.B * s.H)), dim3(256), 0, st, g.n,
+                           s.H, g.num_graphs, g.d_slot_off, g.d_slot_row, row_scale, A);
+        return hipGetLastError();
+    }
     if (s.dtype == DIFFUSER_F32) return launch_f32_d<float>(g, s, Q, K, A, scale_log2, st);
     return launch_f32_d<bf16_t>(g, s, Q, K, A, scale_log2, st);
 }

@@ -56,18 +56,26 @@ struct SRowsArgs {
     GenericGraph gg;
     const int4* row_info;          // [graphs][n]
     const int32_t* G;              // [g]
-    const float* Q;
-    const float* K;
+    const void* Q;                 // fp32 or bf16 (the kernels' T)
+    const void* K;
     float* A;
     float* row_scale;              // [B*H][n]
     float scale_log2;              // log2(e) / sqrt(d_h)
 };
 
+// Four channels of a query or key row as floats, from global memory or LDS.
+__device__ __forceinline__ f32x4 bf4(u32x2 u) {
+    return f32x4{bf16_to_f32(u[0] & 0xffffu), bf16_to_f32(u[0] >> 16), bf16_to_f32(u[1] & 0xffffu),
+                 bf16_to_f32(u[1] >> 16)};
+}
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4(const bf16_t* p) { return bf4(*reinterpret_cast<const u32x2*>(p)); }
 __device__ __forceinline__ f32x4 lds4(const float LDS_AS* p) {
     return *reinterpret_cast<const f32x4 LDS_AS*>(p);
 }
-
-__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 lds4(const bf16_t LDS_AS* p) {
+    return bf4(*reinterpret_cast<const u32x2 LDS_AS*>(p));
+}
 
 __device__ __forceinline__ float dot4(const f32x4& q, const f32x4& k) {
     return fmaf(q[3], k[3], fmaf(q[2], k[2], fmaf(q[1], k[1], q[0] * k[0])));
@@ -91,12 +99,13 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(kThreads, 8)
 void k_scores_rows_f32(SRowsArgs a) {
     static_assert(D == 64, "one 16-lane group per key row");
+    constexpr int U = D * (int)sizeof(T) / 16;   // 16-byte pieces of a key row
     extern __shared__ __align__(16) char lds_raw[];
-    float LDS_AS* lds = (float LDS_AS*)lds_raw;
+    T LDS_AS* lds = (T LDS_AS*)lds_raw;
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int sub = lane & 15, grp = lane >> 4;
@@ -112,25 +121,28 @@ void k_scores_rows_f32(SRowsArgs a) {
     const int4* info = a.row_info + (int64_t)gr * n;
     const __amdgpu_buffer_rsrc_t rG = buffer_rsrc(a.G, (uint32_t)(4 * a.g));
     const int64_t w0 = (r0 - a.radius < 0 ? 0 : r0 - a.radius) & ~7ll;
-    float LDS_AS* win = lds;
-    float LDS_AS* glob = lds + (int64_t)a.win_rows * D;
-    const float* Kbh = a.K + (int64_t)bh * n * D;
+    T LDS_AS* win = lds;
+    T LDS_AS* glob = lds + (int64_t)a.win_rows * D;
+    const T* Qg = static_cast<const T*>(a.Q);
+    const T* Kbh = static_cast<const T*>(a.K) + (int64_t)bh * n * D;
 
     // ---- key rows into LDS (as the fp32 diffusion step's) -----------------
     {
         const int32_t rows = a.win_rows + a.g;
-        const int32_t units = rows * 16;
+        const int32_t units = rows * U;
+        char LDS_AS* ldsb = (char LDS_AS*)lds_raw;
         for (int32_t p0 = 64 * wave; p0 < units; p0 += 64 * kWaves) {
             const int32_t p = p0 + lane;
-            const int32_t r = p >> 4, u = p & 15;
+            const int32_t r = p / U, u = p - r * U;
             int64_t k = -1;
             if (r < a.win_rows) k = w0 + r;
             else if (r < a.win_rows + a.g) k = a.G[r - a.win_rows];
             const bool live = p < units && k >= 0 && k < n;
             if (live)
-                dma16(Kbh + k * D + 4 * u, (void LDS_AS*)(lds + 4 * p0));
+                dma16(reinterpret_cast<const char*>(Kbh + k * D) + 16 * u,
+                      (void LDS_AS*)(ldsb + 16 * p0));
             else if (p < units)
-                *reinterpret_cast<f32x4 LDS_AS*>(lds + 4 * p) = f32x4{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<f32x4 LDS_AS*>(ldsb + 16 * p) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
     full_barrier();
@@ -145,7 +157,7 @@ void k_scores_rows_f32(SRowsArgs a) {
         // A global row here is one of a causal graph's first rows: its
         // segment holds its columns 0 .. i in order.
         const bool grow = ri.z < 0;
-        const f32x4 q = ld4(a.Q + ((int64_t)bh * n + i) * D + 4 * sub);
+        const f32x4 q = ld4(Qg + ((int64_t)bh * n + i) * D + 4 * sub);
         const int64_t lo = i - a.radius < 0 ? 0 : i - a.radius;
         const int64_t hi = i + a.radius > n - 1 ? n - 1 : i + a.radius;
         const int64_t wend = a.causal ? i : hi;
@@ -298,7 +310,7 @@ void k_scores_rows_f32(SRowsArgs a) {
 // rows) are the row kernel's.
 constexpr int kGRows = 4;
 
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(kThreads)
 void k_scores_grows_f32(SRowsArgs a, int32_t gblocks) {
     __shared__ float red[kWaves][kGRows];
@@ -311,7 +323,8 @@ void k_scores_grows_f32(SRowsArgs a, int32_t gblocks) {
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
     const int64_t n = a.n;
     float* Abh = a.A + a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
-    const float* Kbh = a.K + (int64_t)bh * n * D;
+    const T* Qg = static_cast<const T*>(a.Q);
+    const T* Kbh = static_cast<const T*>(a.K) + (int64_t)bh * n * D;
     const int4* info = a.row_info + (int64_t)gr * n;
     const int64_t* sp = a.gg.seg_ptr + (int64_t)gr * (n + 1);
     // The rows: segment start, last column (-1: not this kernel's), q, shift.
@@ -328,7 +341,7 @@ void k_scores_grows_f32(SRowsArgs a, int32_t gblocks) {
         const bool mine = seglen[r] > kLongRow;
         seg[r] = mine ? (uint32_t)info[i].x : 0u;
         last[r] = !mine ? -1 : a.causal ? i : n - 1;
-        q[r] = mine ? ld4(a.Q + ((int64_t)bh * n + i) * D + 4 * sub) : f32x4{0.f, 0.f, 0.f, 0.f};
+        q[r] = mine ? ld4(Qg + ((int64_t)bh * n + i) * D + 4 * sub) : f32x4{0.f, 0.f, 0.f, 0.f};
         ms[r] = mine ? a.scale_log2 * group_sum(dot4(q[r], ld4(Kbh + i * D + 4 * sub))) : 0.0f;
     }
     const int64_t k0 = n * wave / kWaves, k1 = n * (wave + 1) / kWaves;
@@ -469,25 +482,28 @@ int32_t win_rows(const diffuser_graph& g) {
     return kRowsPerGroup + (g.causal ? 1 : 2) * g.radius + 8;
 }
 
-int32_t lds_bytes(const diffuser_graph& g) { return (win_rows(g) + g.num_global) * 64 * 4; }
+int32_t lds_bytes(const diffuser_graph& g, diffuser_dtype dt) {
+    return (win_rows(g) + g.num_global) * 64 * (dt == DIFFUSER_F32 ? 4 : 2);
+}
 
+template <typename T>
 hipError_t launch_args(const diffuser_graph& g, const attn_shape& s, const SRowsArgs& a,
                        hipStream_t st) {
     static int attr_device = -1;
     if (attr_device != g.device) {
         hipError_t e =
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_scores_rows_f32<64>),
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_scores_rows_f32<64, T>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
         if (e != hipSuccess) return e;
         attr_device = g.device;
     }
-    hipLaunchKernelGGL((k_scores_rows_f32<64>), dim3((unsigned)(8 * a.per_xcd)),
-                       dim3(kThreads), (size_t)lds_bytes(g), st, a);
+    hipLaunchKernelGGL((k_scores_rows_f32<64, T>), dim3((unsigned)(8 * a.per_xcd)),
+                       dim3(kThreads), (size_t)lds_bytes(g, s.dtype), st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (g.num_global > 0) {
         const int32_t gblocks = (g.num_global + kGRows - 1) / kGRows;
-        hipLaunchKernelGGL((k_scores_grows_f32<64>), dim3((unsigned)(s.B * s.H * gblocks)),
+        hipLaunchKernelGGL((k_scores_grows_f32<64, T>), dim3((unsigned)(s.B * s.H * gblocks)),
                            dim3(kThreads), 0, st, a, gblocks);
         e = hipGetLastError();
     }
@@ -510,8 +526,8 @@ SRowsArgs make_sargs(const diffuser_graph& g, const attn_shape& s, const void* Q
     a.gg = generic_graph(g);
     a.row_info = reinterpret_cast<const int4*>(g.d_row_info);
     a.G = g.d_global;
-    a.Q = static_cast<const float*>(Q);
-    a.K = static_cast<const float*>(K);
+    a.Q = Q;
+    a.K = K;
     a.A = static_cast<float*>(A);
     a.row_scale = row_scale;
     a.scale_log2 = scale_log2;
@@ -521,8 +537,12 @@ SRowsArgs make_sargs(const diffuser_graph& g, const attn_shape& s, const void* Q
 }  // namespace
 
 bool rows_scores_supported(const diffuser_graph& g, const attn_shape& s) {
-    if (!g.structured || !g.rand_apart() || g.d_row_info == nullptr || s.dtype != DIFFUSER_F32 ||
-        s.d != 64 || g.n <= kLongRow)
+    return s.dtype == DIFFUSER_F32 && rows_scores_any_supported(g, s);
+}
+
+bool rows_scores_any_supported(const diffuser_graph& g, const attn_shape& s) {
+    if (!g.structured || !g.rand_apart() || g.d_row_info == nullptr || s.d != 64 ||
+        g.n <= kLongRow)
         return false;
     for (int64_t x : g.slots)
         if (4 * x >= (1ll << 31)) return false;
@@ -530,14 +550,15 @@ bool rows_scores_supported(const diffuser_graph& g, const attn_shape& s) {
     // Every long row must be a global row: a row's window blocks, global
     // slots and random edges stay within kLongRow.
     const int64_t row_max = 2 * (int64_t)g.radius + 16 + ((g.num_global + 7) & ~7) + g.rnd_width;
-    return groups >= kMinGroups && 2 * lds_bytes(g) <= kLdsLimit && row_max <= kLongRow;
+    return groups >= kMinGroups && 2 * lds_bytes(g, s.dtype) <= kLdsLimit && row_max <= kLongRow;
 }
 
 hipError_t launch_scores_rows(const diffuser_graph& g, const attn_shape& s, const void* Q,
                               const void* K, void* A, float* row_scale, float scale_log2,
                               hipStream_t st) {
-    const hipError_t e =
-        launch_args(g, s, make_sargs(g, s, Q, K, A, row_scale, scale_log2), st);
+    const SRowsArgs a = make_sargs(g, s, Q, K, A, row_scale, scale_log2);
+    const hipError_t e = s.dtype == DIFFUSER_F32 ? launch_args<float>(g, s, a, st)
+                                                 : launch_args<bf16_t>(g, s, a, st);
     if (e != hipSuccess) return e;
     return launch_zero_dummies_f32(g, s, A, st);
 }
