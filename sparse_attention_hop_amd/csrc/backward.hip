@@ -575,13 +575,27 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
                        static_cast<T*>(p.dVout));
     // dS, then dQ = dS K and dK = dS^T Q (the 1 / sqrt(d_h) inside dS).
     hipLaunchKernelGGL(k_softmax_grad, rows, blk, 0, stream, gg, p.H, BH, p.A, p.dA, p.scale);
-    hipLaunchKernelGGL((k_rows<T, T, T, D>), rows, blk, 0, stream, gg, p.H, BH, p.dA,
-                       static_cast<const T*>(p.K), static_cast<const T*>(nullptr),
-                       static_cast<T*>(p.dQ), 1.0f, 0.0f);
-    if (g.max_long > 0)
-        hipLaunchKernelGGL((k_rows_long<T, T, T, D>), longs, lblk, 0, stream, gg, p.H, p.dA,
+    // On built d = 64 graphs both products run on the LDS-window step kernels
+    // (dK on bidirectional graphs, with dS^T in the graph's slot geometry).
+    if (rows_states) {
+        const hipError_t e = launch_grad_rows(g, p.B, p.H, p.dA, p.dA, false, p.K, p.dQ, p.dtype,
+                                              1.0f, stream);
+        if (e != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL((k_rows<T, T, T, D>), rows, blk, 0, stream, gg, p.H, BH, p.dA,
                            static_cast<const T*>(p.K), static_cast<const T*>(nullptr),
                            static_cast<T*>(p.dQ), 1.0f, 0.0f);
+        if (g.max_long > 0)
+            hipLaunchKernelGGL((k_rows_long<T, T, T, D>), longs, lblk, 0, stream, gg, p.H, p.dA,
+                               static_cast<const T*>(p.K), static_cast<const T*>(nullptr),
+                               static_cast<T*>(p.dQ), 1.0f, 0.0f);
+    }
+    if (rows_states && rows_transposed_supported(g, p.B, p.H, D)) {
+        hipError_t e = launch_transpose_struct(g, p.B, p.H, p.dA, p.At, stream);
+        if (e == hipSuccess)
+            e = launch_grad_rows(g, p.B, p.H, p.At, p.dA, true, p.Q, p.dK, p.dtype, 1.0f, stream);
+        return e;
+    }
     hipLaunchKernelGGL(k_to_columns, entries, blk, 0, stream, ci, p.H, BH, entry_blocks, p.dA,
                        p.At);
     hipLaunchKernelGGL((k_cols<T, T, D>), rows, blk, 0, stream, ci, p.H, BH, p.At,

@@ -56,34 +56,43 @@ struct RowsArgs {
     const int64_t* t_ptr;          // [graphs][n + 1]
     const int32_t* t_slot;
     const int32_t* t_row;
-    const float* Z;
-    const void* V;                 // restart rows (fp32 or bf16), or null when restart = 0
-    float* Zn;
+    const void* Z;                 // key rows (the kernels' TX)
+    const void* V;                 // restart rows (TV), or null when restart = 0
+    void* Zn;                      // output rows (TY)
     const float* row_scale;        // [B*H][n] or null
     float keep, restart;
 };
 
+// Four channels of a row (fp32 or bf16) as floats, from global memory,
+// LDS or a buffer load, and four floats stored as a row's channels.
+__device__ __forceinline__ f32x4 bf4(u32x2 u) {
+    return f32x4{bf16_to_f32(u[0] & 0xffffu), bf16_to_f32(u[0] >> 16), bf16_to_f32(u[1] & 0xffffu),
+                 bf16_to_f32(u[1] >> 16)};
+}
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4(const bf16_t* p) { return bf4(*reinterpret_cast<const u32x2*>(p)); }
 __device__ __forceinline__ f32x4 lds4(const float LDS_AS* p) {
     return *reinterpret_cast<const f32x4 LDS_AS*>(p);
 }
-
-__device__ __forceinline__ f32x4 ld4(const float* p) {
-    return *reinterpret_cast<const f32x4*>(p);
+__device__ __forceinline__ f32x4 lds4(const bf16_t LDS_AS* p) {
+    return bf4(*reinterpret_cast<const u32x2 LDS_AS*>(p));
 }
-
-// Four channels of a restart row as floats.
-__device__ __forceinline__ f32x4 ldv4(const float* p) { return ld4(p); }
-__device__ __forceinline__ f32x4 ldv4(const bf16_t* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    return f32x4{bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
-                 bf16_to_f32(u.y >> 16)};
+template <typename TX>
+__device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    if constexpr (sizeof(TX) == 4) return __builtin_bit_cast(f32x4, bload16(r, voff, 0u));
+    else return bf4(bload8(r, voff, 0u));
+}
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void st4(bf16_t* p, f32x4 v) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
+                                         f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16)};
 }
 
 // keep * acc + restart * V[o .. o + 3], with no read of V when restart = 0.
 template <typename TV>
 __device__ __forceinline__ f32x4 restart4(const RowsArgs& a, int64_t o, float keep, f32x4 acc) {
     if (a.restart == 0.0f) return keep * acc;
-    return keep * acc + a.restart * ldv4(static_cast<const TV*>(a.V) + o);
+    return keep * acc + a.restart * ld4(static_cast<const TV*>(a.V) + o);
 }
 
 __device__ __forceinline__ void fma4(float (&acc)[4], float w, const f32x4& z) {
@@ -95,13 +104,14 @@ __device__ __forceinline__ void fma4(float (&acc)[4], float w, const f32x4& z) {
 
 // Eight waves per SIMD (two workgroups per CU, as many waves as the
 // generic step keeps in flight): at most 64 registers per lane.
-template <int D, typename TV>
+template <int D, typename TX, typename TV, typename TY>
 __global__ __launch_bounds__(kThreads, 8)
 void k_diffuse_rows_f32(RowsArgs a) {
     constexpr int L = D / 4;            // lanes per key row (4 channels each)
     constexpr int NG = kWave / L;       // lane groups
+    constexpr int U = D * (int)sizeof(TX) / 16;   // 16-byte pieces of a key row
     extern __shared__ __align__(16) char lds_raw[];
-    float LDS_AS* lds = (float LDS_AS*)lds_raw;
+    TX LDS_AS* lds = (TX LDS_AS*)lds_raw;
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int sub = lane % L, grp = lane / L;
@@ -114,7 +124,7 @@ void k_diffuse_rows_f32(RowsArgs a) {
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
     const int64_t n = a.n;
     const float* Abh = a.A + a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
-    const float* Zbh = a.Z + (int64_t)bh * n * D;
+    const TX* Zbh = static_cast<const TX*>(a.Z) + (int64_t)bh * n * D;
     const int4* info = a.row_info + (int64_t)gr * n;
     const int64_t pair_slots = a.num_graphs == 1 ? a.gg.slot_off[1]
                                                  : a.gg.slot_off[gr + 1] - a.gg.slot_off[gr];
@@ -128,22 +138,24 @@ void k_diffuse_rows_f32(RowsArgs a) {
     // group's rows names one of them), then the g global rows, then
     // kGlobPad zero rows. Rows outside [0, n) are zero.
     const int64_t w0 = (r0 - a.radius < 0 ? 0 : r0 - a.radius) & ~7ll;
-    float LDS_AS* win = lds;
-    float LDS_AS* glob = lds + (int64_t)a.win_rows * D;
+    TX LDS_AS* win = lds;
+    TX LDS_AS* glob = lds + (int64_t)a.win_rows * D;
     {
         const int32_t rows = a.win_rows + a.g + kGlobPad;
-        const int32_t units = rows * L;   // 16-byte pieces
+        const int32_t units = rows * U;   // 16-byte pieces
+        char LDS_AS* ldsb = (char LDS_AS*)lds_raw;
         for (int32_t p0 = 64 * wave; p0 < units; p0 += 64 * kWaves) {
             const int32_t p = p0 + lane;
-            const int32_t r = p / L, u = p - r * L;
+            const int32_t r = p / U, u = p - r * U;
             int64_t k = -1;
             if (r < a.win_rows) k = w0 + r;
             else if (r < a.win_rows + a.g) k = a.G[r - a.win_rows];
             const bool live = p < units && k >= 0 && k < n;
             if (live)
-                dma16(Zbh + k * D + 4 * u, (void LDS_AS*)(lds + 4 * p0));
+                dma16(reinterpret_cast<const char*>(Zbh + k * D) + 16 * u,
+                      (void LDS_AS*)(ldsb + 16 * p0));
             else if (p < units)
-                *reinterpret_cast<f32x4 LDS_AS*>(lds + 4 * p) = f32x4{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<f32x4 LDS_AS*>(ldsb + 16 * p) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
     full_barrier();
@@ -251,8 +263,8 @@ void k_diffuse_rows_f32(RowsArgs a) {
             const int64_t o = ((int64_t)bh * n + i) * D + 4 * sub;
             const float keep =
                 a.row_scale == nullptr ? a.keep : a.keep * a.row_scale[(int64_t)bh * n + i];
-            *reinterpret_cast<f32x4*>(a.Zn + o) =
-                restart4<TV>(a, o, keep, f32x4{acc[0], acc[1], acc[2], acc[3]});
+            st4(static_cast<TY*>(a.Zn) + o,
+                restart4<TV>(a, o, keep, f32x4{acc[0], acc[1], acc[2], acc[3]}));
         }
     }
 }
@@ -265,7 +277,7 @@ void k_diffuse_rows_f32(RowsArgs a) {
 // wave order. Columns above the row are padding when causal.
 constexpr int kGRows = 8;
 
-template <int D, typename TV>
+template <int D, typename TX, typename TV, typename TY>
 __global__ __launch_bounds__(kThreads)
 void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
     constexpr int L = D / 4;
@@ -280,12 +292,12 @@ void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
     const int64_t n = a.n;
     const float* Abh = a.A + a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
-    const float* Zbh = a.Z + (int64_t)bh * n * D;
+    const TX* Zbh = static_cast<const TX*>(a.Z) + (int64_t)bh * n * D;
     const int4* info = a.row_info + (int64_t)gr * n;
     const int64_t pair_slots = a.num_graphs == 1 ? a.gg.slot_off[1]
                                                  : a.gg.slot_off[gr + 1] - a.gg.slot_off[gr];
     const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(Abh, (uint32_t)(4 * pair_slots));
-    const __amdgpu_buffer_rsrc_t rZ = buffer_rsrc(Zbh, (uint32_t)(4 * n * D));
+    const __amdgpu_buffer_rsrc_t rZ = buffer_rsrc(Zbh, (uint32_t)(sizeof(TX) * n * D));
     // The rows' segment starts and last columns (-1: no row).
     uint32_t seg[kGRows];
     int64_t last[kGRows];
@@ -307,7 +319,7 @@ void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
         for (int v = 0; v < 4; ++v) {
             const int64_t j = j0 + v;
             const bool ok = j >= k0 && j < k1;
-            z[v] = __builtin_bit_cast(f32x4, bload16(rZ, ok ? (uint32_t)((j * D + 4 * sub) * 4) : kOutside, 0u));
+            z[v] = bload4<TX>(rZ, ok ? (uint32_t)((j * D + 4 * sub) * sizeof(TX)) : kOutside);
         }
 #pragma unroll
         for (int r = 0; r < kGRows; ++r) {
@@ -342,7 +354,7 @@ void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
         const int64_t o = ((int64_t)bh * n + i) * D + 4 * s2;
         const float keep =
             a.row_scale == nullptr ? a.keep : a.keep * a.row_scale[(int64_t)bh * n + i];
-        *reinterpret_cast<f32x4*>(a.Zn + o) = restart4<TV>(a, o, keep, sum);
+        st4(static_cast<TY*>(a.Zn) + o, restart4<TV>(a, o, keep, sum));
     }
 }
 
@@ -421,67 +433,69 @@ int32_t win_rows(const diffuser_graph& g) {
     return kRowsPerGroup + (g.causal ? 1 : 2) * g.radius + 8;
 }
 
-template <int D>
-int32_t lds_bytes(const diffuser_graph& g) {
-    return (win_rows(g) + g.num_global + kGlobPad) * D * 4;
+int32_t lds_bytes(const diffuser_graph& g, int elem_bytes) {
+    return (win_rows(g) + g.num_global + kGlobPad) * 64 * elem_bytes;
 }
 
-RowsArgs make_args(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
+RowsArgs make_args(const diffuser_graph& g, int32_t B, int32_t H, const float* A, const void* Zk,
                    const void* V, void* Zn, const float* row_scale, step_coefs kc) {
     RowsArgs a;
     a.n = g.n;
-    a.H = s.H;
+    a.H = H;
     a.num_graphs = g.num_graphs;
     a.radius = g.radius;
     a.causal = g.causal;
     a.g = g.num_global;
     a.win_rows = win_rows(g);
     a.blocks = (int32_t)((g.n + kRowsPerGroup - 1) / kRowsPerGroup);
-    a.items = s.B * s.H * a.blocks;
+    a.items = B * H * a.blocks;
     a.per_xcd = (a.items + 7) / 8;
     a.gg = generic_graph(g);
     a.row_info = reinterpret_cast<const int4*>(g.d_row_info);
     a.G = g.d_global;
-    a.A = static_cast<const float*>(A);
-    a.AR = a.A;
+    a.A = A;
+    a.AR = A;
     a.t_ptr = nullptr;
     a.t_slot = nullptr;
     a.t_row = nullptr;
-    a.Z = static_cast<const float*>(Zk);
+    a.Z = Zk;
     a.V = V;
-    a.Zn = static_cast<float*>(Zn);
+    a.Zn = Zn;
     a.row_scale = row_scale;
     a.keep = kc.keep;
     a.restart = kc.restart;
     return a;
 }
 
-template <int D, typename TV>
-hipError_t launch_args(const diffuser_graph& g, const attn_shape& s, const RowsArgs& a,
+// The transposed product's weights: A^T in the graph's slot geometry for
+// the window and global slots, A's own slots for the random edges by column.
+void set_transposed(RowsArgs& a, const diffuser_graph& g, const float* A) {
+    a.AR = A;
+    a.t_ptr = g.d_trand_ptr;
+    a.t_slot = g.d_trand_slot;
+    a.t_row = g.d_trand_row;
+}
+
+template <typename TX, typename TV, typename TY>
+hipError_t launch_args(const diffuser_graph& g, int32_t B, int32_t H, const RowsArgs& a,
                        hipStream_t st) {
-    const int lds = lds_bytes<D>(g);
+    const int lds = lds_bytes(g, (int)sizeof(TX));
     static int attr_device = -1;
     if (attr_device != g.device) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_diffuse_rows_f32<D, TV>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&k_diffuse_rows_f32<64, TX, TV, TY>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
         if (e != hipSuccess) return e;
         attr_device = g.device;
     }
-    hipLaunchKernelGGL((k_diffuse_rows_f32<D, TV>), dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads),
-                       (size_t)lds, st, a);
+    hipLaunchKernelGGL((k_diffuse_rows_f32<64, TX, TV, TY>), dim3((unsigned)(8 * a.per_xcd)),
+                       dim3(kThreads), (size_t)lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.num_global == 0) return e;
     const int32_t gblocks = (g.num_global + kGRows - 1) / kGRows;
-    hipLaunchKernelGGL((k_diffuse_grows_f32<D, TV>), dim3((unsigned)(s.B * s.H * gblocks)),
+    hipLaunchKernelGGL((k_diffuse_grows_f32<64, TX, TV, TY>), dim3((unsigned)(B * H * gblocks)),
                        dim3(kThreads), 0, st, a, gblocks);
     return hipGetLastError();
-}
-
-template <int D, typename TV>
-hipError_t launch_t(const diffuser_graph& g, const attn_shape& s, const void* A, const void* Zk,
-                    const void* V, void* Zn, const float* row_scale, step_coefs kc,
-                    hipStream_t st) {
-    return launch_args<D, TV>(g, s, make_args(g, s, A, Zk, V, Zn, row_scale, kc), st);
 }
 
 }  // namespace
@@ -497,13 +511,14 @@ bool rows_states_supported(const diffuser_graph& g, int32_t B, int32_t H, int32_
     // Enough row groups to give every CU two workgroups twice over; fewer
     // rows run faster one wave per row on the generic step.
     const int64_t groups = (int64_t)B * H * ((g.n + kRowsPerGroup - 1) / kRowsPerGroup);
-    return groups >= kMinGroups && 2 * lds_bytes<64>(g) <= kLdsLimit;
+    return groups >= kMinGroups && 2 * lds_bytes(g, 4) <= kLdsLimit;
 }
 
 hipError_t launch_diffuse_rows(const diffuser_graph& g, const attn_shape& s, const void* A,
                                const void* Zk, const void* V, void* Zn, const float* row_scale,
                                step_coefs kc, hipStream_t st) {
-    return launch_t<64, float>(g, s, A, Zk, V, Zn, row_scale, kc, st);
+    const RowsArgs a = make_args(g, s.B, s.H, static_cast<const float*>(A), Zk, V, Zn, row_scale, kc);
+    return launch_args<float, float, float>(g, s.B, s.H, a, st);
 }
 
 bool rows_transposed_supported(const diffuser_graph& g, int32_t B, int32_t H, int32_t d) {
@@ -512,12 +527,8 @@ bool rows_transposed_supported(const diffuser_graph& g, int32_t B, int32_t H, in
 
 hipError_t launch_transpose_struct(const diffuser_graph& g, int32_t B, int32_t H, const float* A,
                                    float* At, hipStream_t st) {
-    attn_shape s{};
-    s.B = B;
-    s.H = H;
-    s.d = 64;
-    s.dtype = DIFFUSER_F32;
-    const RowsArgs a = make_args(g, s, A, nullptr, nullptr, nullptr, nullptr, step_coefs{0.f, 0.f});
+    const RowsArgs a =
+        make_args(g, B, H, A, nullptr, nullptr, nullptr, nullptr, step_coefs{0.f, 0.f});
     const int64_t per = (g.n + kWaves - 1) / kWaves;
     hipLaunchKernelGGL(k_transpose_struct, dim3((unsigned)(B * H * per)), dim3(kThreads), 0, st, a,
                        At);
@@ -527,29 +538,26 @@ hipError_t launch_transpose_struct(const diffuser_graph& g, int32_t B, int32_t H
 hipError_t launch_transposed_rows(const diffuser_graph& g, int32_t B, int32_t H, const float* At,
                                   const float* A, const float* X, float* Y, float scale,
                                   hipStream_t st) {
-    attn_shape s{};
-    s.B = B;
-    s.H = H;
-    s.d = 64;
-    s.dtype = DIFFUSER_F32;
-    RowsArgs a = make_args(g, s, At, X, nullptr, Y, nullptr, step_coefs{scale, 0.f});
-    a.AR = A;
-    a.t_ptr = g.d_trand_ptr;
-    a.t_slot = g.d_trand_slot;
-    a.t_row = g.d_trand_row;
-    return launch_args<64, float>(g, s, a, st);
+    RowsArgs a = make_args(g, B, H, At, X, nullptr, Y, nullptr, step_coefs{scale, 0.f});
+    set_transposed(a, g, A);
+    return launch_args<float, float, float>(g, B, H, a, st);
 }
 
 hipError_t launch_states_rows(const diffuser_graph& g, int32_t B, int32_t H, const float* A,
                               const float* Zk, const void* V, diffuser_dtype v_dtype, float* Zn,
                               step_coefs kc, hipStream_t st) {
-    attn_shape s{};
-    s.B = B;
-    s.H = H;
-    s.d = 64;
-    s.dtype = DIFFUSER_F32;
-    if (v_dtype == DIFFUSER_F32) return launch_t<64, float>(g, s, A, Zk, V, Zn, nullptr, kc, st);
-    return launch_t<64, bf16_t>(g, s, A, Zk, V, Zn, nullptr, kc, st);
+    const RowsArgs a = make_args(g, B, H, A, Zk, V, Zn, nullptr, kc);
+    if (v_dtype == DIFFUSER_F32) return launch_args<float, float, float>(g, B, H, a, st);
+    return launch_args<float, bf16_t, float>(g, B, H, a, st);
+}
+
+hipError_t launch_grad_rows(const diffuser_graph& g, int32_t B, int32_t H, const float* W,
+                            const float* WR, bool transposed, const void* X, void* Y,
+                            diffuser_dtype dtype, float scale, hipStream_t st) {
+    RowsArgs a = make_args(g, B, H, W, X, nullptr, Y, nullptr, step_coefs{scale, 0.f});
+    if (transposed) set_transposed(a, g, WR);
+    if (dtype == DIFFUSER_F32) return launch_args<float, float, float>(g, B, H, a, st);
+    return launch_args<bf16_t, float, bf16_t>(g, B, H, a, st);
 }
 
 }  // namespace diffuser

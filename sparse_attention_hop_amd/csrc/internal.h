@@ -312,6 +312,13 @@ hipError_t launch_transpose_struct(const diffuser_graph& g, int32_t B, int32_t H
 hipError_t launch_transposed_rows(const diffuser_graph& g, int32_t B, int32_t H, const float* At,
                                   const float* A, const float* X, float* Y, float scale,
                                   hipStream_t st);
+// Y = scale * W X with X and Y of storage type dtype (the backward's dQ =
+// dS K and, transposed, dK = dS^T Q): W the weights in the graph's slot
+// geometry (A^T's when transposed), WR the weights the random edges' slots
+// name.
+hipError_t launch_grad_rows(const diffuser_graph& g, int32_t B, int32_t H, const float* W,
+                            const float* WR, bool transposed, const void* X, void* Y,
+                            diffuser_dtype dtype, float scale, hipStream_t st);
 // The same step on built graphs with a whole channel slice of Z_k resident
 // in LDS (bf16, d = 32 or 64, n up to about 4.5 K keys).
 bool res_diffuse_supported(const diffuser_graph& g, const attn_shape& s);
