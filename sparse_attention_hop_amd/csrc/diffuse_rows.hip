@@ -26,6 +26,8 @@
 // slots, most of a row's edges, then cost LDS reads instead of gathers of
 // whole key rows from L2. Global rows (whose segment is every column) go to
 // a second kernel that reads each key row once for kGRows of them.
+#include <algorithm>
+
 #include "internal.h"
 #include "mfma_util.h"
 #include "vec.h"
@@ -364,64 +366,120 @@ void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
 // window rows |i - j| <= r, the global rows and, for a global j, every
 // row; so row j's window slot for column i and its global slot t (for
 // G[t]) hold A_ij and A_{G[t] j}, and a global row j's slot i holds A_ij.
-// The random edges are listed by column apart. One wave per row j, its
-// lanes over the segment's slots; padding slots are 0. For a source row
-// i, A_ij lies in its full segment when i is global, in its window when
-// |i - j| <= r, and otherwise (j is then a global column) in its global
-// slot for j.
+// The random edges are listed by column apart. Padding slots are 0. For a
+// source row i, A_ij lies in its full segment when i is global, in its
+// window when |i - j| <= r, and otherwise (j is then a global column) in
+// its global slot for j.
+//
+// k_transpose_band: the rows j of a tile of kTRows that are not global. A
+// workgroup reads, one wave per source row with a lane per column, the
+// tile's columns of every source row that can be a window row of the tile
+// (rows j0 - r .. j0 + kTRows - 1 + r) and of every global row into LDS,
+// then writes each destination row's slots with a lane per slot.
+constexpr int kTRows = 64;
+constexpr int kTStride = kTRows + 1;   // LDS row stride (column reads fall on distinct banks)
+
 __global__ __launch_bounds__(kThreads)
-void k_transpose_struct(RowsArgs a, float* __restrict__ At) {
+void k_transpose_band(RowsArgs a, float* __restrict__ At, int32_t tiles) {
+    extern __shared__ float tl[];
     const int lane = __lane_id();
     const int wave = threadIdx.x / kWave;
+    constexpr int kW = kWaves;
     const int64_t n = a.n;
-    const int32_t per = (int32_t)((n + kWaves - 1) / kWaves);
-    const int32_t bh = blockIdx.x / per;
-    const int64_t j = (int64_t)(blockIdx.x - bh * per) * kWaves + wave;
-    if (j >= n) return;
+    const int32_t bh = blockIdx.x / tiles;
+    const int64_t j0 = (int64_t)(blockIdx.x - bh * tiles) * kTRows;
     const int32_t b = bh / a.H, h = bh - b * a.H;
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
     const int64_t off = a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
     const float* Ab = a.A + off;
     float* Atb = At + off;
     const int4* info = a.row_info + (int64_t)gr * n;
+    const int64_t r = a.radius;
+    const int64_t ib = j0 - r < 0 ? 0 : j0 - r;
+    const int64_t ie = j0 + kTRows - 1 + r > n - 1 ? n - 1 : j0 + kTRows - 1 + r;
+    const int32_t nsrc = (int32_t)(ie - ib + 1);
+    const int32_t rows = nsrc + a.g;
+    float* win = tl;                                  // [nsrc][kTStride], then [g][kTStride]
+    int4* sinfo = reinterpret_cast<int4*>(tl + (((int64_t)rows * kTStride + 3) & ~3ll));   // [rows]
+    int4* dinfo = sinfo + rows;                                              // [kTRows]
+    // The geometry of the source rows (window rows, then the global rows)
+    // and of the destination rows.
+    for (int32_t u = threadIdx.x; u < rows + kTRows; u += kThreads) {
+        if (u < rows) {
+            sinfo[u] = info[u < nsrc ? ib + u : a.G[u - nsrc]];
+        } else {
+            const int64_t jd = j0 + (u - rows);
+            dinfo[u - rows] = jd < n ? info[jd] : make_int4(0, 0, -1, 0);
+        }
+    }
+    __syncthreads();
+    const int64_t j = j0 + lane;   // this lane's column
+#pragma unroll 4
+    for (int32_t u = wave; u < rows; u += kW) {
+        const int4 ri = sinfo[u];
+        float w = 0.0f;
+        if (u < nsrc) {
+            const int64_t i = ib + u;
+            if (j < n && j >= i - r && j <= i + r) w = Ab[(int64_t)ri.x + (ri.z < 0 ? j : j - ri.y)];
+        } else if (j < n) {
+            w = Ab[(int64_t)ri.x + j];   // a global row's column j
+        }
+        win[(int64_t)u * kTStride + lane] = w;
+    }
+    __syncthreads();
+    const float* glob = win + (int64_t)nsrc * kTStride;
+    for (int32_t jj = wave; jj < kTRows; jj += kW) {
+        const int64_t jd = j0 + jj;
+        const int4 rj = dinfo[jj];
+        if (jd >= n || rj.z < 0) continue;   // past n, or a global row: k_transpose_grows's
+        const int64_t nslot = (int64_t)rj.z + rj.w;
+        for (int64_t s = lane; s < nslot; s += kWave) {
+            float w = 0.0f;
+            if (s < rj.z) {
+                const int64_t i = rj.y + s;
+                if (i < n && i >= jd - r && i <= jd + r) w = win[(i - ib) * kTStride + jj];
+            } else {
+                const int64_t t = s - rj.z;
+                if (t < a.g) {
+                    const int64_t i = a.G[t];
+                    if (i < jd - r || i > jd + r) w = glob[t * kTStride + jj];
+                }
+            }
+            Atb[(int64_t)rj.x + s] = w;
+        }
+    }
+}
+
+// Global destination rows j = G[q] (a global column of A: every row has an
+// edge to it): one wave per row, a lane per slot.
+__global__ __launch_bounds__(kThreads)
+void k_transpose_grows(RowsArgs a, float* __restrict__ At) {
+    const int lane = __lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int64_t n = a.n;
+    const int32_t per = (a.g + kWaves - 1) / kWaves;
+    const int32_t bh = blockIdx.x / per;
+    const int32_t q = (blockIdx.x - bh * per) * kWaves + wave;
+    if (q >= a.g) return;
+    const int32_t b = bh / a.H, h = bh - b * a.H;
+    const int32_t gr = a.num_graphs == 1 ? 0 : b;
+    const int64_t off = a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
+    const float* Ab = a.A + off;
+    float* Atb = At + off;
+    const int4* info = a.row_info + (int64_t)gr * n;
+    const int64_t j = a.G[q];
     const int4 rj = info[j];
     const int64_t r = a.radius;
-    // Position of j among the globals (a global row of A^T is a global
-    // column of A), else -1.
-    int32_t tj = -1;
-    if (rj.z < 0) {
-        int32_t lo = 0, hi = a.g;
-        while (lo < hi) {
-            const int32_t mid = (lo + hi) / 2;
-            if (a.G[mid] < j) lo = mid + 1;
-            else hi = mid;
-        }
-        tj = lo < a.g && a.G[lo] == j ? lo : -1;
-    }
     const int64_t nslot = a.gg.row(gr, j).seg_len;
-    for (int64_t s = lane; s < nslot; s += kWave) {
-        int64_t i = 0;   // the row of A that slot s of row j of A^T names
-        bool valid;
-        if (rj.z < 0) {
-            i = s;
-            valid = s < n;
-        } else if (s < rj.z) {
-            i = rj.y + s;
-            valid = i < n && i >= j - r && i <= j + r;
-        } else {
-            const int64_t t = s - rj.z;
-            valid = t < a.g;
-            if (valid) i = a.G[t];
-            valid = valid && (i < j - r || i > j + r);
-        }
+    for (int64_t i = lane; i < nslot; i += kWave) {
         float w = 0.0f;
-        if (valid) {
+        if (i < n) {
             const int4 ri = info[i];
             if (ri.z < 0) w = Ab[(int64_t)ri.x + j];
             else if (j >= i - r && j <= i + r) w = Ab[(int64_t)ri.x + (j - ri.y)];
-            else if (tj >= 0) w = Ab[(int64_t)ri.x + ri.z + tj];
+            else w = Ab[(int64_t)ri.x + ri.z + q];
         }
-        Atb[(int64_t)rj.x + s] = w;
+        Atb[(int64_t)rj.x + i] = w;
     }
 }
 
@@ -435,6 +493,14 @@ int32_t win_rows(const diffuser_graph& g) {
 
 int32_t lds_bytes(const diffuser_graph& g, int elem_bytes) {
     return (win_rows(g) + g.num_global + kGlobPad) * 64 * elem_bytes;
+}
+
+// LDS of k_transpose_band: the source rows of a tile and the global rows,
+// kTStride floats and an int4 of geometry each, and the destination rows'
+// geometry.
+int64_t transpose_lds_bytes(const diffuser_graph& g) {
+    const int64_t src = std::min<int64_t>(kTRows + 2 * (int64_t)g.radius, g.n);
+    return (src + g.num_global) * (kTStride * 4 + 16) + kTRows * 16 + 16;
 }
 
 RowsArgs make_args(const diffuser_graph& g, int32_t B, int32_t H, const float* A, const void* Zk,
@@ -522,15 +588,29 @@ hipError_t launch_diffuse_rows(const diffuser_graph& g, const attn_shape& s, con
 }
 
 bool rows_transposed_supported(const diffuser_graph& g, int32_t B, int32_t H, int32_t d) {
-    return !g.causal && g.d_trand_ptr != nullptr && rows_states_supported(g, B, H, d);
+    return !g.causal && g.d_trand_ptr != nullptr && transpose_lds_bytes(g) <= kLdsLimit &&
+           rows_states_supported(g, B, H, d);
 }
 
 hipError_t launch_transpose_struct(const diffuser_graph& g, int32_t B, int32_t H, const float* A,
                                    float* At, hipStream_t st) {
     const RowsArgs a =
         make_args(g, B, H, A, nullptr, nullptr, nullptr, nullptr, step_coefs{0.f, 0.f});
-    const int64_t per = (g.n + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL(k_transpose_struct, dim3((unsigned)(B * H * per)), dim3(kThreads), 0, st, a,
+    static int attr_device = -1;
+    if (attr_device != g.device) {
+        const hipError_t e =
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_transpose_band),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+        if (e != hipSuccess) return e;
+        attr_device = g.device;
+    }
+    const int32_t tiles = (int32_t)((g.n + kTRows - 1) / kTRows);
+    hipLaunchKernelGGL(k_transpose_band, dim3((unsigned)(B * H * tiles)), dim3(kThreads),
+                       (size_t)transpose_lds_bytes(g), st, a, At, tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || g.num_global == 0) return e;
+    const int32_t per = (g.num_global + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(k_transpose_grows, dim3((unsigned)(B * H * per)), dim3(kThreads), 0, st, a,
                        At);
     return hipGetLastError();
 }
