@@ -55,14 +55,14 @@ def diffusion_kernel(w):
     the resident-slice kernel for bf16, d in {32, 64}, n <= 4576 (at most
     256 globals); the LDS-streamed one for other bf16, d = 64 graphs up to
     n = 65536; for fp32, d = 64 graphs up to n = 65536 with at least 1024
-    groups of 64 rows, the LDS-window row kernel with its global-row kernel;
+    groups of 64 rows, the LDS-window MFMA row kernel with its global-row kernel;
     else the generic gather kernel."""
     if w.dtype == "bf16" and w.d in (32, 64) and w.n <= 4576 and len(w.global_idx) <= 256:
         return "k_diffuse_res"
     if w.dtype == "bf16" and w.d == 64 and w.n <= 65536:
         return "k_diffuse_sched"
     if w.dtype == "f32" and w.d == 64 and w.n <= 65536 and w.B * w.H * -(-w.n // 64) >= 1024:
-        return "k_diffuse_rows_f32 + k_diffuse_grows_f32"
+        return "k_diffuse_rows_mma + k_diffuse_grows_f32"
     return "k_diffuse_step"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 TRAFFIC_FILE = "traffic_diffuse_step_{workload}.txt"

@@ -1,31 +1,24 @@
-// Diffusion step on built graphs with fp32 storage, one wavefront per row
-// as in the generic step, with the key rows of the window band and of the
-// global columns served from LDS:
+// Diffusion step on built graphs with fp32 states (keys fp32 or bf16), the
+// key rows of the window band and of the global columns served from LDS:
 //   Z_{k+1}[i] = keep * c_i * sum_j A_ij Z_k[j] + restart * V[i]
 // ("Diffuser" reading notes, section 2.4, eq. S.7, with keep = 1 - alpha and
 // restart = alpha; other coefficients evaluate section 2.3's eq. S.6 in
 // nested form; c_i rescales the stored weights of row i to sum to one, or
-// is 1).
+// is 1). The same kernels serve the backward's products with fp32 weights:
+// the recomputed states, the transposed products (A^T laid out in the
+// graph's slot geometry, the random edges listed by column) and dQ, dK.
 //
 // A workgroup of 16 waves owns kRowsPerGroup consecutive rows of one
 // (batch, head) pair. It first copies into LDS, by direct global-to-LDS
 // loads, every key row that a window slot of its rows can name (one
 // contiguous run of Z_k around its rows) and the key rows of the g global
-// columns, then each wave sums its rows alone:
-//  * window slots: 16 consecutive columns at a time, lane group q taking
-//    columns 4 q .. 4 q + 3 with one 16-byte weight load and four key rows
-//    read from LDS; slots outside the row's window (block padding) weigh 0;
-//  * global-column slots: the same over the row's global slots, whose key
-//    rows sit in LDS in global order; a slot whose global lies in the
-//    window (or, when causal, above the row) is padding and weighs 0;
-//  * random edges: gathered from Z_k in global memory, as the generic step
-//    does, each lane group one edge at a time with four edges in flight.
-// A lane holds 4 channels of one key row (lane group q, lanes 16 q .. + 15
-// for a head width of 64); the groups' partial sums are added at the end
-// and the restart term is fused into the store. The window and global
-// slots, most of a row's edges, then cost LDS reads instead of gathers of
-// whole key rows from L2. Global rows (whose segment is every column) go to
-// a second kernel that reads each key row once for kGRows of them.
+// columns. The window and global slots, most of a row's edges, are then a
+// dense product per block of 16 rows on MFMA (k_diffuse_rows_mma), which
+// reads each key row from LDS once per block instead of once per row; the
+// random edges are gathered from Z_k in global memory a row at a time, and
+// the restart term is fused into the store. Global rows (whose segment is
+// every column) go to a second kernel that reads each key row once for
+// kGRows of them.
 #include <algorithm>
 
 #include "internal.h"
@@ -65,20 +58,14 @@ struct RowsArgs {
     float keep, restart;
 };
 
-// Four channels of a row (fp32 or bf16) as floats, from global memory,
-// LDS or a buffer load, and four floats stored as a row's channels.
+// Four channels of a row (fp32 or bf16) as floats, from global memory or a
+// buffer load, and four floats stored as a row's channels.
 __device__ __forceinline__ f32x4 bf4(u32x2 u) {
     return f32x4{bf16_to_f32(u[0] & 0xffffu), bf16_to_f32(u[0] >> 16), bf16_to_f32(u[1] & 0xffffu),
                  bf16_to_f32(u[1] >> 16)};
 }
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 ld4(const bf16_t* p) { return bf4(*reinterpret_cast<const u32x2*>(p)); }
-__device__ __forceinline__ f32x4 lds4(const float LDS_AS* p) {
-    return *reinterpret_cast<const f32x4 LDS_AS*>(p);
-}
-__device__ __forceinline__ f32x4 lds4(const bf16_t LDS_AS* p) {
-    return bf4(*reinterpret_cast<const u32x2 LDS_AS*>(p));
-}
 template <typename TX>
 __device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
     if constexpr (sizeof(TX) == 4) return __builtin_bit_cast(f32x4, bload16(r, voff, 0u));
@@ -104,16 +91,51 @@ __device__ __forceinline__ void fma4(float (&acc)[4], float w, const f32x4& z) {
     acc[3] = fmaf(w, z[3], acc[3]);
 }
 
-// Eight waves per SIMD (two workgroups per CU, as many waves as the
-// generic step keeps in flight): at most 64 registers per lane.
+// LDS element position of channel c of run row k: a row's 16-byte pieces
+// are permuted by ((k >> 2) & 3), so that the four rows one MFMA operand
+// read touches (rows 4 apart) fall on distinct banks.
+template <typename TX>
+__device__ __forceinline__ int32_t zpos(int32_t k, int32_t c) {
+    if constexpr (sizeof(TX) == 4)
+        return k * 64 + ((c >> 2) ^ (((k >> 2) & 3) << 2)) * 4 + (c & 3);
+    else
+        return k * 64 + ((c >> 3) ^ (((k >> 2) & 3) << 1)) * 8 + (c & 7);
+}
+// The 16-byte piece a staging lane fetches for position `pos` of run row r.
+template <typename TX>
+__device__ __forceinline__ int32_t zpiece(int32_t r, int32_t pos) {
+    if constexpr (sizeof(TX) == 4) return pos ^ (((r >> 2) & 3) << 2);
+    else return pos ^ (((r >> 2) & 3) << 1);
+}
+__device__ __forceinline__ float zld(const float LDS_AS* base, int32_t p) { return base[p]; }
+__device__ __forceinline__ float zld(const bf16_t LDS_AS* base, int32_t p) {
+    return bf16_to_f32(*reinterpret_cast<const uint16_t LDS_AS*>(base + p));
+}
+
+// The same step with the window band and the global columns of each block
+// of 16 rows on v_mfma_f32_16x16x4_f32: wave w takes the rows of block
+// w / 4 against channels 16 (w mod 4) .. + 15,
+//   D[row][channel] += W[row][key] Z[key][channel]
+// over the block's window keys and the g globals, four keys per product:
+// lane (m, kq) = (lane mod 16, lane / 16) supplies the weights of row m for
+// keys base + 4 kq .. + 3 (one 16-byte load) and channel m of those keys'
+// rows from LDS, product e pairing key base + 4 kq + e in both operands.
+// A weight whose key lies outside its row's window (or, for a global slot,
+// inside it or above a causal row) is 0. The block's sums go to LDS; then
+// each row's random edges are gathered (a wave per row, lane group q
+// taking edges 4 q .. 4 q + 3 of each step of 16, their slots and columns
+// in one 16-byte load each) and added to them. Eight waves per SIMD (two workgroups per CU): at most 64
+// registers per lane.
 template <int D, typename TX, typename TV, typename TY>
 __global__ __launch_bounds__(kThreads, 8)
-void k_diffuse_rows_f32(RowsArgs a) {
-    constexpr int L = D / 4;            // lanes per key row (4 channels each)
-    constexpr int NG = kWave / L;       // lane groups
-    constexpr int U = D * (int)sizeof(TX) / 16;   // 16-byte pieces of a key row
+void k_diffuse_rows_mma(RowsArgs a) {
+    static_assert(D == 64, "four 16-channel tiles per block");
+    constexpr int L = D / 4;
+    constexpr int NG = kWave / L;
+    constexpr int U = D * (int)sizeof(TX) / 16;
     extern __shared__ __align__(16) char lds_raw[];
     TX LDS_AS* lds = (TX LDS_AS*)lds_raw;
+    float LDS_AS* csum = (float LDS_AS*)lds_raw;   // [64][64], after the products
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int sub = lane % L, grp = lane / L;
@@ -124,7 +146,7 @@ void k_diffuse_rows_f32(RowsArgs a) {
     const int64_t r0 = (int64_t)(item - bh * a.blocks) * kRowsPerGroup;
     const int32_t b = bh / a.H, h = bh - b * a.H;
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
-    const int64_t n = a.n;
+    const int64_t n = a.n, r = a.radius;
     const float* Abh = a.A + a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h);
     const TX* Zbh = static_cast<const TX*>(a.Z) + (int64_t)bh * n * D;
     const int4* info = a.row_info + (int64_t)gr * n;
@@ -135,26 +157,21 @@ void k_diffuse_rows_f32(RowsArgs a) {
         a.AR + a_block_offset(a.gg.slot_off, a.num_graphs, a.H, b, h), (uint32_t)(4 * pair_slots));
     const __amdgpu_buffer_rsrc_t rG = buffer_rsrc(a.G, (uint32_t)(4 * a.g));
 
-    // ---- key rows into LDS ------------------------------------------------
-    // Window run: key rows w0 .. w0 + win_rows - 1 (every window slot of the
-    // group's rows names one of them), then the g global rows, then
-    // kGlobPad zero rows. Rows outside [0, n) are zero.
-    const int64_t w0 = (r0 - a.radius < 0 ? 0 : r0 - a.radius) & ~7ll;
-    TX LDS_AS* win = lds;
-    TX LDS_AS* glob = lds + (int64_t)a.win_rows * D;
+    // ---- key rows into LDS (pieces permuted by zpiece) ---------------------
+    const int64_t w0 = (r0 - r < 0 ? 0 : r0 - r) & ~7ll;
     {
         const int32_t rows = a.win_rows + a.g + kGlobPad;
-        const int32_t units = rows * U;   // 16-byte pieces
+        const int32_t units = rows * U;
         char LDS_AS* ldsb = (char LDS_AS*)lds_raw;
         for (int32_t p0 = 64 * wave; p0 < units; p0 += 64 * kWaves) {
             const int32_t p = p0 + lane;
-            const int32_t r = p / U, u = p - r * U;
+            const int32_t rr = p / U, pos = p - rr * U;
             int64_t k = -1;
-            if (r < a.win_rows) k = w0 + r;
-            else if (r < a.win_rows + a.g) k = a.G[r - a.win_rows];
+            if (rr < a.win_rows) k = w0 + rr;
+            else if (rr < a.win_rows + a.g) k = a.G[rr - a.win_rows];
             const bool live = p < units && k >= 0 && k < n;
             if (live)
-                dma16(reinterpret_cast<const char*>(Zbh + k * D) + 16 * u,
+                dma16(reinterpret_cast<const char*>(Zbh + k * D) + 16 * zpiece<TX>(rr, pos),
                       (void LDS_AS*)(ldsb + 16 * p0));
             else if (p < units)
                 *reinterpret_cast<f32x4 LDS_AS*>(ldsb + 16 * p) = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -162,6 +179,63 @@ void k_diffuse_rows_f32(RowsArgs a) {
     }
     full_barrier();
 
+    // ---- window band and global columns, one 16 x 16 tile per wave ---------
+    const int m = lane & 15, kq = lane >> 4;
+    const int64_t ib0 = r0 + 16 * (wave >> 2);
+    const int32_t cch = 16 * (wave & 3) + m;   // this lane's channel of the key rows
+    f32x4 acc16 = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ib0 < n) {
+        const int64_t i = ib0 + m;   // this lane's weight row
+        const int4 ri = i < n ? info[i] : make_int4(0, 0, -1, 0);
+        const bool live = i < n && ri.z >= 0;
+        const int64_t lo = i - r < 0 ? 0 : i - r;
+        const int64_t hi = i + r > n - 1 ? n - 1 : i + r;
+        const int64_t wend = a.causal ? i : hi;
+        const int64_t last = a.causal ? i : n - 1;
+        // The block's window keys: from its first row's block start through
+        // the last slot of its last row's window.
+        const int64_t ibl = ib0 + 15 < n ? ib0 + 15 : n - 1;
+        const int64_t J0 = (ib0 - r < 0 ? 0 : ib0 - r) & ~7ll;
+        const int64_t wend_l = a.causal ? ibl : (ibl + r > n - 1 ? n - 1 : ibl + r);
+        const int32_t nch = (int32_t)(((wend_l | 7) - J0) / 16 + 1);
+        for (int32_t c = 0; c < nch; ++c) {
+            const int64_t key0 = J0 + 16 * c + 4 * kq;
+            const int64_t s0 = key0 - ri.y;
+            const bool in = live && s0 >= 0 && s0 < ri.z;
+            const u32x4 wv = bload16(rA, in ? 4u * (uint32_t)(ri.x + s0) : kOutside, 0u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t key = key0 + e;
+                const bool ok = live && key >= lo && key <= wend;
+                const int32_t kl = (int32_t)min(key - w0, (int64_t)a.win_rows - 1);
+                acc16 = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? __uint_as_float(wv[e]) : 0.0f,
+                                                             zld(lds, zpos<TX>(kl, cch)), acc16,
+                                                             0, 0, 0);
+            }
+        }
+        const int32_t gch = (a.g + 15) / 16;
+        for (int32_t c = 0; c < gch; ++c) {
+            const int32_t t0 = 16 * c + 4 * kq;
+            const bool in = live && t0 < ri.w;
+            const u32x4 wv = bload16(rA, in ? 4u * (uint32_t)(ri.x + ri.z + t0) : kOutside, 0u);
+            const u32x4 gk = bload16(rG, t0 < a.g ? 4u * (uint32_t)t0 : kOutside, 0u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t kc = (int32_t)gk[e];
+                const bool ok = in && t0 + e < a.g && (kc < lo || kc > hi) && kc <= last;
+                acc16 = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                    ok ? __uint_as_float(wv[e]) : 0.0f,
+                    zld(lds, zpos<TX>(a.win_rows + t0 + e, cch)), acc16, 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();   // every wave is done with the key rows
+    // Lane (m, kq) holds rows 4 kq + v of its block at channel cch.
+#pragma unroll
+    for (int v = 0; v < 4; ++v) csum[(16 * (wave >> 2) + 4 * kq + v) * 64 + cch] = acc16[v];
+    __syncthreads();
+
+    // ---- random edges per row, gathered, plus the block sums ----------------
 #pragma unroll 1
     for (int u = 0; u < kRowsPerWave; ++u) {
         const int64_t i = r0 + kWaves * u + wave;
@@ -169,92 +243,41 @@ void k_diffuse_rows_f32(RowsArgs a) {
         const int4 ri = info[i];
         if (ri.z < 0) continue;   // a global row: k_diffuse_grows_f32's
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        {
-            const int64_t lo = i - a.radius < 0 ? 0 : i - a.radius;
-            const int64_t hi = i + a.radius > n - 1 ? n - 1 : i + a.radius;
-            const int64_t wend = a.causal ? i : hi;
-            const int64_t last = a.causal ? i : n - 1;
-            const int64_t wb0 = ri.y;
-            // Window slots: columns cb + 4 grp + v of the block at cb, two
-            // blocks' weights requested before either is used.
-            const uint32_t wl = 4u * (uint32_t)(ri.x + 4 * grp);
-            for (int64_t cb = wb0; cb <= wend; cb += 8 * NG) {
-                u32x4 wv[2];
+        int32_t nr;
+        const int32_t *rslot, *rcol;
+        if (a.t_ptr == nullptr) {
+            const RowSlots rs = a.gg.row(gr, i);
+            nr = rs.rcnt;
+            rslot = rs.rslot;
+            rcol = rs.rcol;
+        } else {
+            const int64_t t0 = a.t_ptr[(int64_t)gr * (n + 1) + i];
+            nr = (int32_t)(a.t_ptr[(int64_t)gr * (n + 1) + i + 1] - t0);
+            rslot = a.t_slot + t0;
+            rcol = a.t_row + t0;
+        }
+        const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(rslot, (uint32_t)(4 * nr));
+        const __amdgpu_buffer_rsrc_t rC = buffer_rsrc(rcol, (uint32_t)(4 * nr));
+        auto idx = [&](int32_t base, u32x4& sl, u32x4& cl) {
+            const int32_t e0 = base + 4 * grp;
+            sl = bload16(rS, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
+            cl = bload16(rC, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
+        };
+        u32x4 sl, cl;
+        idx(0, sl, cl);
+        for (int32_t base = 0; base < nr; base += 4 * NG) {
+            float w[4];
+            f32x4 z[4];
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int64_t c0 = cb + 4 * NG * s2 + 4 * grp;
-                    wv[s2] = bload16(rA, c0 <= wend ? wl + 4u * (uint32_t)(cb + 4 * NG * s2 - wb0)
-                                                    : kOutside, 0u);
-                }
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int64_t c0 = cb + 4 * NG * s2 + 4 * grp;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int64_t c = c0 + v;
-                        const bool ok = c >= lo && c <= wend;
-                        const float w = ok ? __uint_as_float(wv[s2][v]) : 0.0f;
-                        // columns past the window read a zero or an in-run row
-                        fma4(acc, w, lds4(win + (ok ? c - w0 : 0) * D + 4 * sub));
-                    }
-                }
+            for (int v = 0; v < 4; ++v) {
+                const bool ok = base + 4 * grp + v < nr;
+                w[v] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                    rAR, ok ? (int)(4u * sl[v]) : (int)kOutside, 0, 0));
+                z[v] = ld4(Zbh + (int64_t)(ok ? (int32_t)cl[v] : 0) * D + 4 * sub);
             }
-            // Global-column slots t of the row (G[t] outside the window and,
-            // when causal, not above the row).
-            const int32_t gs = min(a.g, ri.w);
-            for (int32_t tb = 0; tb < gs; tb += 4 * NG) {
-                const int32_t t0 = tb + 4 * grp;
-                const bool any = t0 < gs;
-                const u32x4 wv = bload16(rA, any ? 4u * (uint32_t)(ri.x + ri.z + t0) : kOutside, 0u);
-                const u32x4 gk = bload16(rG, any ? 4u * (uint32_t)t0 : kOutside, 0u);
+            idx(base + 4 * NG, sl, cl);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int64_t k = (int32_t)gk[v];
-                    const bool ok = t0 + v < gs && (k < lo || k > hi) && k <= last;
-                    const float w = ok ? __uint_as_float(wv[v]) : 0.0f;
-                    fma4(acc, w, lds4(glob + (int64_t)(t0 + v) * D + 4 * sub));
-                }
-            }
-            // Random edges, gathered: lane group grp takes edges
-            // base + 4 grp + v, their slots and columns in one 16-byte load
-            // each; the next step's slots and columns are requested before
-            // this step's rows are used.
-            int32_t nr;
-            const int32_t *rslot, *rcol;
-            if (a.t_ptr == nullptr) {
-                const RowSlots rs = a.gg.row(gr, i);
-                nr = rs.rcnt;
-                rslot = rs.rslot;
-                rcol = rs.rcol;
-            } else {
-                const int64_t t0 = a.t_ptr[(int64_t)gr * (n + 1) + i];
-                nr = (int32_t)(a.t_ptr[(int64_t)gr * (n + 1) + i + 1] - t0);
-                rslot = a.t_slot + t0;
-                rcol = a.t_row + t0;
-            }
-            const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(rslot, (uint32_t)(4 * nr));
-            const __amdgpu_buffer_rsrc_t rC = buffer_rsrc(rcol, (uint32_t)(4 * nr));
-            auto idx = [&](int32_t base, u32x4& sl, u32x4& cl) {
-                const int32_t e0 = base + 4 * grp;
-                sl = bload16(rS, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
-                cl = bload16(rC, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
-            };
-            u32x4 sl, cl;
-            idx(0, sl, cl);
-            for (int32_t base = 0; base < nr; base += 4 * NG) {
-                float w[4];
-                f32x4 z[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const bool ok = base + 4 * grp + v < nr;
-                    w[v] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-                        rAR, ok ? (int)(4u * sl[v]) : (int)kOutside, 0, 0));
-                    z[v] = ld4(Zbh + (int64_t)(ok ? (int32_t)cl[v] : 0) * D + 4 * sub);
-                }
-                idx(base + 4 * NG, sl, cl);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) fma4(acc, w[v], z[v]);
-            }
+            for (int v = 0; v < 4; ++v) fma4(acc, w[v], z[v]);
         }
 #pragma unroll
         for (int off = L; off < kWave; off <<= 1) {
@@ -262,11 +285,12 @@ void k_diffuse_rows_f32(RowsArgs a) {
             for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
         }
         if (grp == 0) {
+            const f32x4 bs = *reinterpret_cast<const f32x4 LDS_AS*>(csum + (i - r0) * 64 + 4 * sub);
             const int64_t o = ((int64_t)bh * n + i) * D + 4 * sub;
             const float keep =
                 a.row_scale == nullptr ? a.keep : a.keep * a.row_scale[(int64_t)bh * n + i];
             st4(static_cast<TY*>(a.Zn) + o,
-                restart4<TV>(a, o, keep, f32x4{acc[0], acc[1], acc[2], acc[3]}));
+                restart4<TV>(a, o, keep, f32x4{acc[0], acc[1], acc[2], acc[3]} + bs));
         }
     }
 }
@@ -545,17 +569,16 @@ void set_transposed(RowsArgs& a, const diffuser_graph& g, const float* A) {
 template <typename TX, typename TV, typename TY>
 hipError_t launch_args(const diffuser_graph& g, int32_t B, int32_t H, const RowsArgs& a,
                        hipStream_t st) {
-    const int lds = lds_bytes(g, (int)sizeof(TX));
+    const int lds = std::max(lds_bytes(g, (int)sizeof(TX)), kRowsPerGroup * 64 * 4);
+    auto kern = &k_diffuse_rows_mma<64, TX, TV, TY>;
     static int attr_device = -1;
     if (attr_device != g.device) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&k_diffuse_rows_f32<64, TX, TV, TY>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
         if (e != hipSuccess) return e;
         attr_device = g.device;
     }
-    hipLaunchKernelGGL((k_diffuse_rows_f32<64, TX, TV, TY>), dim3((unsigned)(8 * a.per_xcd)),
-                       dim3(kThreads), (size_t)lds, st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), (size_t)lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.num_global == 0) return e;
     const int32_t gblocks = (g.num_global + kGRows - 1) / kGRows;
