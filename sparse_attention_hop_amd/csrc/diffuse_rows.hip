@@ -17,8 +17,8 @@
 // reads each key row from LDS once per block instead of once per row; the
 // random edges are gathered from Z_k in global memory a row at a time, and
 // the restart term is fused into the store. Global rows (whose segment is
-// every column) go to a second kernel that reads each key row once for
-// kGRows of them.
+// every column) go to a second kernel, 16 of them against each key row on
+// MFMA.
 #include <algorithm>
 
 #include "internal.h"
@@ -295,25 +295,26 @@ void k_diffuse_rows_mma(RowsArgs a) {
     }
 }
 
-// Global rows, kGRows per workgroup: the 16 waves split the keys into
-// contiguous ranges, each key row of Z_k is read once per workgroup (16
-// bytes per lane, lane group grp taking 4 consecutive keys) and multiplied
-// by the weights of all kGRows rows (a global row's segment holds its
-// columns in order); the waves' partial sums meet in LDS and are added in
-// wave order. Columns above the row are padding when causal.
-constexpr int kGRows = 8;
+// Global rows, 16 per workgroup, on v_mfma_f32_16x16x4_f32: the 16 waves
+// split the keys into contiguous ranges and each computes, over its range,
+//   D_ct[row][n] += W[row][key] Z[key][4 n + ct]      (ct = 0..3)
+// for the workgroup's 16 rows (a global row's segment holds its columns in
+// order), so lane (n, kq) reads channels 4 n .. 4 n + 3 of a key row with
+// one 16-byte load and ends with four consecutive channels of each of its
+// rows. Keys outside the wave's range, past n or (causal) above the row
+// weigh 0. The waves' partial sums meet in LDS and are added in wave order.
+constexpr int kGTile = 16;
 
 template <int D, typename TX, typename TV, typename TY>
 __global__ __launch_bounds__(kThreads)
 void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
-    constexpr int L = D / 4;
-    constexpr int NG = kWave / L;
-    __shared__ f32x4 part[kWaves][kGRows][L];
+    static_assert(D == 64, "four channel tiles of 16");
+    __shared__ f32x4 part[kWaves][kGTile][16];   // [wave][row][channels 4 n ..]
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int sub = lane % L, grp = lane / L;
+    const int m = lane & 15, kq = lane >> 4;
     const int32_t bh = blockIdx.x / gblocks;
-    const int32_t q0 = (blockIdx.x - bh * gblocks) * kGRows;
+    const int32_t q0 = (blockIdx.x - bh * gblocks) * kGTile;
     const int32_t b = bh / a.H, h = bh - b * a.H;
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
     const int64_t n = a.n;
@@ -324,60 +325,43 @@ void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
                                                  : a.gg.slot_off[gr + 1] - a.gg.slot_off[gr];
     const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(Abh, (uint32_t)(4 * pair_slots));
     const __amdgpu_buffer_rsrc_t rZ = buffer_rsrc(Zbh, (uint32_t)(sizeof(TX) * n * D));
-    // The rows' segment starts and last columns (-1: no row).
-    uint32_t seg[kGRows];
-    int64_t last[kGRows];
+    // This lane's weight row (row m of the tile) and its last column.
+    const int32_t q = q0 + m;
+    const int64_t gi = q < a.g ? a.G[q] : -1;
+    const uint32_t seg = gi >= 0 ? (uint32_t)info[gi].x : 0u;
+    const int64_t last = gi < 0 ? -1 : a.causal ? gi : n - 1;
+    f32x4 acc[4];
 #pragma unroll
-    for (int r = 0; r < kGRows; ++r) {
-        const int32_t q = q0 + r;
-        const int64_t i = q < a.g ? a.G[q] : -1;
-        seg[r] = i >= 0 ? (uint32_t)info[i].x : 0u;
-        last[r] = i < 0 ? -1 : a.causal ? i : n - 1;
-    }
-    f32x4 acc[kGRows];
-#pragma unroll
-    for (int r = 0; r < kGRows; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t k0 = n * wave / kWaves, k1 = n * (wave + 1) / kWaves;
-    for (int64_t kb = k0 & ~3ll; kb < k1; kb += 4 * NG) {
-        const int64_t j0 = kb + 4 * grp;   // keys j0 .. j0 + 3 of this lane group
-        f32x4 z[4];
+    for (int64_t kb = k0 & ~15ll; kb < k1; kb += 16) {
+        const int64_t key0 = kb + 4 * kq;   // this lane's keys key0 .. key0 + 3
+        const bool any = key0 <= last && key0 + 3 >= k0 && key0 < k1;
+        const u32x4 w = bload16(rA, any ? 4u * (seg + (uint32_t)key0) : kOutside, 0u);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t j = j0 + v;
-            const bool ok = j >= k0 && j < k1;
-            z[v] = bload4<TX>(rZ, ok ? (uint32_t)((j * D + 4 * sub) * sizeof(TX)) : kOutside);
-        }
+        for (int e = 0; e < 4; ++e) {
+            const int64_t key = key0 + e;
+            const bool ok = key >= k0 && key < k1 && key <= last;
+            const float we = ok ? __uint_as_float(w[e]) : 0.0f;
+            const bool zk = key >= k0 && key < k1;
+            const f32x4 z = bload4<TX>(rZ, zk ? (uint32_t)((key * D + 4 * m) * sizeof(TX)) : kOutside);
 #pragma unroll
-        for (int r = 0; r < kGRows; ++r) {
-            const bool any = j0 <= last[r] && j0 < k1;
-            const u32x4 w = bload16(rA, any ? 4u * (seg[r] + (uint32_t)j0) : kOutside, 0u);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t j = j0 + v;
-                const float wj = j >= k0 && j < k1 && j <= last[r] ? __uint_as_float(w[v]) : 0.0f;
-                acc[r] = acc[r] + wj * z[v];
-            }
+            for (int ct = 0; ct < 4; ++ct)
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(we, z[ct], acc[ct], 0, 0, 0);
         }
     }
-    // Lane groups, then waves, in a fixed order.
+    // Lane (n, kq) holds rows 4 kq + v at channels 4 n + ct.
 #pragma unroll
-    for (int r = 0; r < kGRows; ++r)
-#pragma unroll
-        for (int off = L; off < kWave; off <<= 1)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[r][c] += __shfl_xor(acc[r][c], off);
-    if (grp == 0)
-#pragma unroll
-        for (int r = 0; r < kGRows; ++r) part[wave][r][sub] = acc[r];
+    for (int v = 0; v < 4; ++v)
+        part[wave][4 * kq + v][m] = f32x4{acc[0][v], acc[1][v], acc[2][v], acc[3][v]};
     __syncthreads();
-    for (int t = threadIdx.x; t < kGRows * L; t += kThreads) {
-        const int r = t / L, s2 = t - r * L;
-        const int32_t q = q0 + r;
-        if (q >= a.g) continue;
+    for (int t = threadIdx.x; t < kGTile * 16; t += kThreads) {
+        const int rr = t / 16, c4 = t - rr * 16;
+        if (q0 + rr >= a.g) continue;
         f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int w = 0; w < kWaves; ++w) sum = sum + part[w][r][s2];
-        const int64_t i = a.G[q];
-        const int64_t o = ((int64_t)bh * n + i) * D + 4 * s2;
+        for (int w = 0; w < kWaves; ++w) sum = sum + part[w][rr][c4];
+        const int64_t i = a.G[q0 + rr];
+        const int64_t o = ((int64_t)bh * n + i) * D + 4 * c4;
         const float keep =
             a.row_scale == nullptr ? a.keep : a.keep * a.row_scale[(int64_t)bh * n + i];
         st4(static_cast<TY*>(a.Zn) + o, restart4<TV>(a, o, keep, sum));
@@ -581,7 +565,7 @@ hipError_t launch_args(const diffuser_graph& g, int32_t B, int32_t H, const Rows
     hipLaunchKernelGGL(kern, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), (size_t)lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.num_global == 0) return e;
-    const int32_t gblocks = (g.num_global + kGRows - 1) / kGRows;
+    const int32_t gblocks = (g.num_global + kGTile - 1) / kGTile;
     hipLaunchKernelGGL((k_diffuse_grows_f32<64, TX, TV, TY>), dim3((unsigned)(B * H * gblocks)),
                        dim3(kThreads), 0, st, a, gblocks);
     return hipGetLastError();
