@@ -448,6 +448,63 @@ void k_softmax_grad(GenericGraph gg, int32_t H, int32_t BH, const float* __restr
     }
 }
 
+// The same on built graphs, whose padding slots hold A = 0 and dA = 0: a
+// row's segment is read as whole 16-byte quads (a segment starts on and
+// spans a multiple of 8 slots) with no column lookups, its random slots
+// through the row's slot list; a lane keeps the values it read for the
+// write when the row fits one pass.
+__global__ __launch_bounds__(kThreads)
+void k_softmax_grad_built(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict__ A,
+                          float* __restrict__ dA, float scale) {
+    const int wave = threadIdx.x / kWave, lane = __lane_id();
+    const int64_t n = gg.n;
+    int64_t i;
+    int32_t bh;
+    if (!xcd_row_item<kWavesPerBlock>(n, BH, wave, i, bh)) return;
+    const int32_t bb = bh / H, hh = bh - bb * H;
+    const int32_t gr = gg.num_graphs == 1 ? 0 : bb;
+    const RowSlots rs = gg.row(gr, i);
+    const int64_t off = a_block_offset(gg.slot_off, gg.num_graphs, H, bb, hh);
+    const float4* A4 = reinterpret_cast<const float4*>(A + off + rs.seg_begin);
+    float4* dA4 = reinterpret_cast<float4*>(dA + off + rs.seg_begin);
+    const float* Ab = A + off;
+    float* dAb = dA + off;
+    const int64_t quads = rs.seg_len / 4;
+    float sum = 0.0f;
+    float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), d0 = a0;
+    float ar = 0.0f, dr = 0.0f;
+    if (lane < quads) {
+        a0 = A4[lane];
+        d0 = dA4[lane];
+        sum = a0.x * d0.x + a0.y * d0.y + a0.z * d0.z + a0.w * d0.w;
+    }
+    for (int64_t qd = lane + kWave; qd < quads; qd += kWave) {
+        const float4 x = A4[qd], y = dA4[qd];
+        sum += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+    }
+    if (lane < rs.rcnt) {
+        ar = Ab[rs.rslot[lane]];
+        dr = dAb[rs.rslot[lane]];
+        sum += ar * dr;
+    }
+    for (int32_t e = lane + kWave; e < rs.rcnt; e += kWave) sum += Ab[rs.rslot[e]] * dAb[rs.rslot[e]];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane < quads)
+        dA4[lane] = make_float4(a0.x * (d0.x - sum) * scale, a0.y * (d0.y - sum) * scale,
+                                a0.z * (d0.z - sum) * scale, a0.w * (d0.w - sum) * scale);
+    for (int64_t qd = lane + kWave; qd < quads; qd += kWave) {
+        const float4 x = A4[qd], y = dA4[qd];
+        dA4[qd] = make_float4(x.x * (y.x - sum) * scale, x.y * (y.y - sum) * scale,
+                              x.z * (y.z - sum) * scale, x.w * (y.w - sum) * scale);
+    }
+    if (lane < rs.rcnt) dAb[rs.rslot[lane]] = ar * (dr - sum) * scale;
+    for (int32_t e = lane + kWave; e < rs.rcnt; e += kWave) {
+        const int32_t s = rs.rslot[e];
+        dAb[s] = Ab[s] * (dAb[s] - sum) * scale;
+    }
+}
+
 // y = a * x + b * y elementwise over count values (x of type TX).
 template <typename TX>
 __global__ __launch_bounds__(kThreads)
@@ -574,7 +631,11 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     hipLaunchKernelGGL((k_sum_to<T>), grid_elems(cnt), blk, 0, stream, cnt, p.dV, p.Gs,
                        static_cast<T*>(p.dVout));
     // dS, then dQ = dS K and dK = dS^T Q (the 1 / sqrt(d_h) inside dS).
-    hipLaunchKernelGGL(k_softmax_grad, rows, blk, 0, stream, gg, p.H, BH, p.A, p.dA, p.scale);
+    if (rows_states)
+        hipLaunchKernelGGL(k_softmax_grad_built, rows, blk, 0, stream, gg, p.H, BH, p.A, p.dA,
+                           p.scale);
+    else
+        hipLaunchKernelGGL(k_softmax_grad, rows, blk, 0, stream, gg, p.H, BH, p.A, p.dA, p.scale);
     // On built d = 64 graphs both products run on the LDS-window step kernels
     // (dK on bidirectional graphs, with dS^T in the graph's slot geometry).
     if (rows_states) {
