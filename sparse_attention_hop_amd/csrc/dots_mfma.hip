@@ -158,6 +158,121 @@ void k_dots_band(DotsArgs a) {
     }
 }
 
+// k_dots_band with the key rows in LDS: a workgroup of 16 waves owns 64
+// consecutive rows (four blocks); for each state k it copies the key rows
+// of Z_k that a window slot of its rows can name (one contiguous run) and
+// the g global rows into LDS by direct global-to-LDS loads, a row's 16-byte
+// pieces permuted by (row mod 16) so that the 16 rows one operand read
+// touches fall on distinct banks; wave w takes the tiles w mod 4,
+// w mod 4 + 4, ... of block w / 4. Every key row is then read from L2 once
+// per 64 rows and state instead of once per block of 16.
+constexpr int kLdsWaves = 16;
+constexpr int kLdsThreads = kWave * kLdsWaves;
+constexpr int kWaveTiles = 4;     // tiles per wave: at most 16 per block
+constexpr int kLdsPad = 16;       // zero rows past the globals (a global tile reads up to 15 past g)
+
+__global__ __launch_bounds__(kLdsThreads, 8)
+void k_dots_band_lds(DotsArgs a, int32_t groups, int32_t per_xcd, int32_t win_rows) {
+    extern __shared__ __align__(16) char lds_raw[];
+    float LDS_AS* lds = (float LDS_AS*)lds_raw;
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int m = lane & 15, kq = lane >> 4;
+    const int32_t item = (int32_t)(blockIdx.x & 7u) * per_xcd + (int32_t)(blockIdx.x >> 3);
+    if (item >= a.BH * groups) return;
+    const int32_t bh = item / groups;
+    const int64_t r0 = (int64_t)(item - bh * groups) * 64;
+    const int32_t b = bh / a.H, h = bh - b * a.H;
+    const int32_t gr = a.num_graphs == 1 ? 0 : b;
+    const int64_t n = a.n, r = a.radius;
+    const int4* info = a.row_info + (int64_t)gr * n;
+    float* dAb = a.dA + a_block_offset(a.slot_off, a.num_graphs, a.H, b, h);
+    const int64_t w0 = (r0 - r < 0 ? 0 : r0 - r) & ~7ll;
+    // This wave's block and tiles.
+    const int64_t i0 = r0 + 16 * (wave >> 2);
+    const int tq = wave & 3;
+    int64_t J0, wl_first, wb_last, Jend;
+    window_span(i0 < n ? i0 : n - 1, n, r, a.causal, J0, wl_first);
+    window_span(i0 + 15 < n ? i0 + 15 : n - 1, n, r, a.causal, wb_last, Jend);
+    const int32_t twin = (int32_t)((Jend - J0) / 16 + 1);
+    const int32_t T = i0 < n ? twin + (a.g + 15) / 16 : 0;
+    const int64_t qi = i0 + m;
+    const float* Gq = a.Gs + a.stride + ((int64_t)bh * n + (qi < n ? qi : 0)) * 64 + 4 * kq;
+    const int32_t rows = win_rows + a.g + kLdsPad;
+    f32x4 acc[kWaveTiles];
+#pragma unroll
+    for (int tt = 0; tt < kWaveTiles; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int32_t k = 0; k < a.K; ++k) {
+        if (k > 0) __syncthreads();   // every wave is done with state k - 1's rows
+        const float* Zk = a.Zs + (int64_t)k * a.stride + (int64_t)bh * n * 64;
+        for (int32_t p0 = 64 * wave; p0 < rows * 16; p0 += 64 * kLdsWaves) {
+            const int32_t p = p0 + lane;
+            const int32_t rr = p >> 4, pos = p & 15;
+            int64_t key = -1;
+            if (rr < win_rows) key = w0 + rr;
+            else if (rr < win_rows + a.g) key = a.G[rr - win_rows];
+            if (p < rows * 16 && key >= 0 && key < n)
+                dma16(Zk + key * 64 + 4 * (pos ^ (rr & 15)), (void LDS_AS*)(lds + 4 * p0));
+            else if (p < rows * 16)
+                *reinterpret_cast<f32x4 LDS_AS*>(lds + 4 * p) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        f32x4 q[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) q[s] = ld4z(Gq + k * a.stride + 16 * s, qi < n);
+        full_barrier();
+#pragma unroll
+        for (int tt = 0; tt < kWaveTiles; ++tt) {
+            const int32_t t = tq + 4 * tt;
+            if (t >= T) continue;   // the same in every lane
+            int32_t kl;
+            if (t < twin) {
+                const int64_t key = J0 + 16 * t + m;
+                kl = (int32_t)min(key - w0, (int64_t)win_rows - 1);
+            } else {
+                kl = win_rows + 16 * (t - twin) + m;
+            }
+            const float LDS_AS* row = lds + (int64_t)kl * 64;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const f32x4 z =
+                    *reinterpret_cast<const f32x4 LDS_AS*>(row + 4 * ((4 * s + kq) ^ (kl & 15)));
+                acc[tt] = mfma_chunk(acc[tt], q[s], z);
+            }
+        }
+    }
+    // Lane holds rows i0 + 4 kq + v against key m of each of its tiles.
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t i = i0 + 4 * kq + v;
+        if (i >= n) continue;
+        const int4 ri = info[i];
+        if (ri.z < 0) continue;   // a global row: k_dots_glob's
+        const int64_t lo = i - r < 0 ? 0 : i - r;
+        const int64_t hi = i + r > n - 1 ? n - 1 : i + r;
+        const int64_t wend = a.causal ? i : hi;
+        const int64_t last = a.causal ? i : n - 1;
+#pragma unroll
+        for (int tt = 0; tt < kWaveTiles; ++tt) {
+            const int32_t t = tq + 4 * tt;
+            if (t >= T) continue;
+            if (t < twin) {
+                const int64_t j = J0 + 16 * t + m;
+                const int64_t s = j - ri.y;
+                if (s >= 0 && s < ri.z)
+                    dAb[(int64_t)ri.x + s] = j >= lo && j <= wend ? a.f * acc[tt][v] : 0.0f;
+            } else {
+                const int32_t gt = 16 * (t - twin) + m;
+                if (gt < ri.w) {
+                    const int64_t c = gt < a.g ? a.G[gt] : -1;
+                    const bool ok = c >= 0 && (c < lo || c > hi) && c <= last;
+                    dAb[(int64_t)ri.x + ri.z + gt] = ok ? a.f * acc[tt][v] : 0.0f;
+                }
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads)
 void k_dots_glob(DotsArgs a) {
     const int lane = __lane_id();
@@ -241,6 +356,21 @@ DotsArgs make_args(const diffuser_graph& g, int32_t B, int32_t H, const float* G
     return a;
 }
 
+// Key rows of a 64-row group's window run (its rows, the radius on either
+// side, or on the left when causal, and the 8-column alignment).
+int32_t lds_win_rows(const diffuser_graph& g) {
+    return 64 + (g.causal ? 1 : 2) * g.radius + 8;
+}
+
+// k_dots_band_lds serves a graph whose blocks have at most 16 tiles and
+// whose window run and globals fit two workgroups per CU.
+bool lds_band_fits(const diffuser_graph& g) {
+    const int64_t twin = (15 + (g.causal ? 1 : 2) * (int64_t)g.radius + 14) / 16 + 1;
+    const int64_t tiles = twin + (g.num_global + 15) / 16;
+    const int64_t bytes = (int64_t)(lds_win_rows(g) + g.num_global + kLdsPad) * 256;
+    return tiles <= 4 * kWaveTiles && 2 * bytes <= 160 * 1024;
+}
+
 }  // namespace
 
 bool mfma_dots_supported(const diffuser_graph& g, int32_t d) {
@@ -254,9 +384,26 @@ hipError_t launch_dots_dense(const diffuser_graph& g, int32_t B, int32_t H, cons
                              const float* Zs, int64_t stride, int32_t K, float f, float* dA,
                              hipStream_t st) {
     const DotsArgs a = make_args(g, B, H, Gs, Zs, stride, K, f, dA);
-    const int64_t band = ((int64_t)a.BH * a.nrb + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(k_dots_band, dim3((unsigned)band), dim3(kThreads), 0, st, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    const int32_t wrows = lds_win_rows(g);
+    if (lds_band_fits(g)) {
+        static int attr_device = -1;
+        if (attr_device != g.device) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dots_band_lds),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            if (e != hipSuccess) return e;
+            attr_device = g.device;
+        }
+        const int32_t groups = (int32_t)((g.n + 63) / 64);
+        const int32_t per_xcd = (a.BH * groups + 7) / 8;
+        hipLaunchKernelGGL(k_dots_band_lds, dim3((unsigned)(8 * per_xcd)), dim3(kLdsThreads),
+                           (size_t)(wrows + g.num_global + kLdsPad) * 256, st, a, groups, per_xcd,
+                           wrows);
+    } else {
+        const int64_t band = ((int64_t)a.BH * a.nrb + kWavesPerBlock - 1) / kWavesPerBlock;
+        hipLaunchKernelGGL(k_dots_band, dim3((unsigned)band), dim3(kThreads), 0, st, a);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess || g.num_global == 0) return e;
     const int64_t glob = ((int64_t)a.BH * a.nkt + kWavesPerBlock - 1) / kWavesPerBlock;
     hipLaunchKernelGGL(k_dots_glob, dim3((unsigned)glob), dim3(kThreads), 0, st, a);
