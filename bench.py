@@ -198,9 +198,10 @@ def read_traffic(workload):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def write_kernel_summary(stats_dir, workload, command):
+def write_kernel_summary(stats_dir, workload, command, backward=False):
     """Markdown table of a rocprofv3 --kernel-trace --stats run (the
-    kernel_stats.csv under stats_dir) into profiles/kernels_<workload>.md."""
+    kernel_stats.csv under stats_dir) into profiles/kernels_<workload>.md
+    (kernels_backward_<workload>.md for a --backward-only run)."""
     paths = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not paths:
         raise SystemExit(f"no kernel_stats.csv under {stats_dir}")
@@ -217,19 +218,21 @@ def write_kernel_summary(stats_dir, workload, command):
     from workloads import WORKLOADS
     w = WORKLOADS[workload]
     lines = [
-        f"# Kernel-time summary: {w.describe()}",
+        f"# Kernel-time summary{' of the backward pass' if backward else ''}: {w.describe()}",
         "",
         "Command (repository root, one MI355X, `TMPDIR=/tmp`):",
         "",
         f"    {command}",
-        f"    python bench.py --workload {workload} --write-kernel-summary {stats_dir}",
+        f"    python bench.py --workload {workload} --write-kernel-summary {stats_dir}"
+        + (" --backward-only" if backward else ""),
         "",
         "| kernel | calls | mean (us) | min (us) | max (us) | share |",
         "|---|---|---|---|---|---|",
     ]
     for name, calls, mean, lo, hi, pct in rows:
         lines.append(f"| {name} | {calls} | {mean:.1f} | {lo:.1f} | {hi:.1f} | {pct:.2f}% |")
-    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    path = os.path.join(ROOT, "profiles",
+                        f"kernels_{'backward_' if backward else ''}{workload}.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -458,12 +461,15 @@ def main():
                     help="the rocprofv3 command the stats came from (for the summary's header)")
     ap.add_argument("--length-sweep", action="store_true",
                     help="time the headline shape at n = 1K .. 16K (one JSON line per n)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward pass at the workload (one JSON line; "
+                         "--warmup untimed calls, then --steps timed ones)")
     args = ap.parse_args()
 
     if args.write_kernel_summary:
         from workloads import HEADLINE
         write_kernel_summary(args.write_kernel_summary, args.workload or HEADLINE,
-                             args.summary_command)
+                             args.summary_command, args.backward_only)
         return
     if args.write_traffic:
         from workloads import HEADLINE
@@ -493,6 +499,16 @@ def main():
                         w.graph_seed)
     q_h, k_h, v_h = make_qkv(w)
     q, k, v = q_h.to(dev), k_h.to(dev), v_h.to(dev)
+    if args.backward_only:
+        dz = torch.randn(q.shape, generator=torch.Generator(device="cpu").manual_seed(5)).to(
+            dtype=q.dtype, device=q.device)
+        for _ in range(max(args.warmup, 1)):
+            sah.attn_backward(q, k, v, dz, g, w.K, w.alpha)
+        ms = time_events(lambda: sah.attn_backward(q, k, v, dz, g, w.K, w.alpha), args.steps,
+                         torch)
+        print(json.dumps({"metric": "backward_ms", "value": ms, "unit": "ms",
+                          "workload": w.name, "steps": args.steps}), flush=True)
+        return
     z = torch.empty_like(v)
     ws = torch.empty(sah.workspace_size(g, w.B, w.H, w.d, w.d, q.dtype), dtype=torch.uint8,
                      device=dev)
