@@ -45,6 +45,7 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kRowsPerWave = 4;
 constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
 constexpr int kLdsLimit = 160 * 1024;
+constexpr int kGlobPad = 16;   // zero key rows past the globals (a global tile reads up to 15 past g)
 constexpr int64_t kMinGroups = 1024;
 constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
 
@@ -70,12 +71,6 @@ __device__ __forceinline__ f32x4 bf4(u32x2 u) {
 }
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 ld4(const bf16_t* p) { return bf4(*reinterpret_cast<const u32x2*>(p)); }
-__device__ __forceinline__ f32x4 lds4(const float LDS_AS* p) {
-    return *reinterpret_cast<const f32x4 LDS_AS*>(p);
-}
-__device__ __forceinline__ f32x4 lds4(const bf16_t LDS_AS* p) {
-    return bf4(*reinterpret_cast<const u32x2 LDS_AS*>(p));
-}
 
 __device__ __forceinline__ float dot4(const f32x4& q, const f32x4& k) {
     return fmaf(q[3], k[3], fmaf(q[2], k[2], fmaf(q[1], k[1], q[0] * k[0])));
@@ -99,6 +94,57 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// LDS layout of the key rows: a row's 16-byte pieces are permuted so that
+// the 16 consecutive rows one MFMA operand read touches (lane m reading row
+// base + m at one channel offset) fall on distinct banks: piece position
+// u ^ (row mod 16) for fp32 rows (16 pieces), u ^ ((row / 2) mod 8) for
+// bf16 rows (8 pieces, two rows per bank cycle).
+template <typename T>
+__device__ __forceinline__ int32_t kpiece(int32_t row, int32_t u) {
+    if constexpr (sizeof(T) == 4) return u ^ (row & 15);
+    else return u ^ ((row >> 1) & 7);
+}
+// Channels ch .. ch + 3 (ch a multiple of 4) of LDS key row `row`.
+__device__ __forceinline__ f32x4 klds4(const float LDS_AS* lds, int32_t row, int32_t ch) {
+    return *reinterpret_cast<const f32x4 LDS_AS*>(lds + row * 64 + 4 * kpiece<float>(row, ch >> 2));
+}
+__device__ __forceinline__ f32x4 klds4(const bf16_t LDS_AS* lds, int32_t row, int32_t ch) {
+    return bf4(*reinterpret_cast<const u32x2 LDS_AS*>(lds + row * 64 + 8 * kpiece<bf16_t>(row, ch >> 3) +
+                                                     (ch & 7)));
+}
+__device__ __forceinline__ i16x4 klds4_bf16(const bf16_t LDS_AS* lds, int32_t row, int32_t ch) {
+    return *reinterpret_cast<const i16x4 LDS_AS*>(lds + row * 64 + 8 * kpiece<bf16_t>(row, ch >> 3) +
+                                                  (ch & 7));
+}
+
+// The band products of one 16 x 16 tile over the 64 channels: D[row m][key
+// n] = Q[m] . K[n], lane (m, kq) supplying channels 16 s + 4 kq .. + 3 of
+// query row m (from qrow, which points at channel 4 kq of it) and of key
+// row `krow` (from LDS) for chunk s.
+__device__ __forceinline__ f32x4 tile_dots(const float* qrow, const float LDS_AS* lds,
+                                           int32_t krow, int kq) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const f32x4 q = ld4(qrow + 16 * s);
+        const f32x4 z = klds4(lds, krow, 16 * s + 4 * kq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(q[e], z[e], acc, 0, 0, 0);
+    }
+    return acc;
+}
+__device__ __forceinline__ f32x4 tile_dots(const bf16_t* qrow, const bf16_t LDS_AS* lds,
+                                           int32_t krow, int kq) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            *reinterpret_cast<const i16x4*>(qrow + 16 * s), klds4_bf16(lds, krow, 16 * s + 4 * kq),
+            acc, 0, 0, 0);
+    return acc;
+}
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 template <int D, typename T>
 __global__ __launch_bounds__(kThreads, 8)
 void k_scores_rows_f32(SRowsArgs a) {
@@ -121,14 +167,12 @@ void k_scores_rows_f32(SRowsArgs a) {
     const int4* info = a.row_info + (int64_t)gr * n;
     const __amdgpu_buffer_rsrc_t rG = buffer_rsrc(a.G, (uint32_t)(4 * a.g));
     const int64_t w0 = (r0 - a.radius < 0 ? 0 : r0 - a.radius) & ~7ll;
-    T LDS_AS* win = lds;
-    T LDS_AS* glob = lds + (int64_t)a.win_rows * D;
     const T* Qg = static_cast<const T*>(a.Q);
     const T* Kbh = static_cast<const T*>(a.K) + (int64_t)bh * n * D;
 
     // ---- key rows into LDS (as the fp32 diffusion step's) -----------------
     {
-        const int32_t rows = a.win_rows + a.g;
+        const int32_t rows = a.win_rows + a.g + kGlobPad;
         const int32_t units = rows * U;
         char LDS_AS* ldsb = (char LDS_AS*)lds_raw;
         for (int32_t p0 = 64 * wave; p0 < units; p0 += 64 * kWaves) {
@@ -139,13 +183,98 @@ void k_scores_rows_f32(SRowsArgs a) {
             else if (r < a.win_rows + a.g) k = a.G[r - a.win_rows];
             const bool live = p < units && k >= 0 && k < n;
             if (live)
-                dma16(reinterpret_cast<const char*>(Kbh + k * D) + 16 * u,
+                dma16(reinterpret_cast<const char*>(Kbh + k * D) + 16 * kpiece<T>(r, u),
                       (void LDS_AS*)(ldsb + 16 * p0));
             else if (p < units)
                 *reinterpret_cast<f32x4 LDS_AS*>(ldsb + 16 * p) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
+    // Shifts: each row's own score (the self-loop is an edge of every row).
+    float LDS_AS* msh = reinterpret_cast<float LDS_AS*>(lds + (int64_t)(a.win_rows + a.g + kGlobPad) * D);
+    float LDS_AS* psum = msh + kRowsPerGroup;   // [4][kRowsPerGroup] band sums per tile quarter
+    i32x4 LDS_AS* rinfo = reinterpret_cast<i32x4 LDS_AS*>(psum + 4 * kRowsPerGroup);   // [kRowsPerGroup]
     full_barrier();
+#pragma unroll 1
+    for (int u = 0; u < kRowsPerWave; ++u) {
+        const int64_t i = r0 + kWaves * u + wave;
+        float ms = 0.0f;
+        if (i < n) {
+            const f32x4 q = ld4(Qg + ((int64_t)bh * n + i) * D + 4 * sub);
+            ms = a.scale_log2 * group_sum(dot4(q, klds4(lds, (int32_t)(i - w0), 4 * sub)));
+        }
+        if (lane == 0) {
+            msh[kWaves * u + wave] = ms;
+            const int4 ri = i < n ? info[i] : make_int4(0, 0, -1, 0);
+            rinfo[kWaves * u + wave] = i32x4{ri.x, ri.y, ri.z, ri.w};
+        }
+    }
+    __syncthreads();
+
+    // ---- window bands and global columns on MFMA ---------------------------
+    // Wave w: block w / 4 (16 rows), tiles w mod 4, + 4, ... of its keys:
+    // the window keys (16 consecutive per tile, from the first row's block
+    // start through the last row's last window slot), then the globals.
+    // Each weight exp(s - m_row) goes to its row's slot (0 for padding and
+    // keys not the row's); the tiles' row sums meet in psum. Row and key
+    // numbers fit 32 bits here (n < 2^31).
+    {
+        const int m = lane & 15, kq = lane >> 4;
+        const int bb = wave >> 2, tq = wave & 3;
+        const int32_t n32 = (int32_t)n, r = a.radius;
+        const int32_t i0 = (int32_t)r0 + 16 * bb;
+        float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+        if (i0 < n32) {
+            const int32_t il = i0 + 15 < n32 ? i0 + 15 : n32 - 1;
+            const int32_t J0 = (i0 - r < 0 ? 0 : i0 - r) & ~7;
+            const int32_t wend_l = a.causal ? il : (il + r > n32 - 1 ? n32 - 1 : il + r);
+            const int32_t twin = ((wend_l | 7) - J0) / 16 + 1;
+            const int32_t ntile = twin + (a.g + 15) / 16;
+            const int32_t qi = i0 + m;
+            const T* qrow = Qg + ((int64_t)bh * n + (qi < n32 ? qi : i0)) * D + 4 * kq;
+#pragma unroll 1
+            for (int32_t t = tq; t < ntile; t += 4) {
+                int32_t krow;
+                if (t < twin) krow = min(J0 + 16 * t + m - (int32_t)w0, a.win_rows - 1);
+                else krow = a.win_rows + 16 * (t - twin) + m;
+                const f32x4 d = tile_dots(qrow, lds, krow, kq);
+                const int32_t gt = 16 * (t - twin) + m;   // a global tile's slot
+                const int32_t gc = t >= twin && gt < a.g ? a.G[gt] : -1;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    // the lane's output row i0 + 4 kq + v
+                    const int32_t i = i0 + 4 * kq + v;
+                    const i32x4 ri = rinfo[16 * bb + 4 * kq + v];
+                    if (i >= n32 || ri[2] < 0) continue;   // past n, or a global row
+                    const int32_t lo = i - r < 0 ? 0 : i - r;
+                    const int32_t hi = i + r > n32 - 1 ? n32 - 1 : i + r;
+                    int32_t slot;
+                    bool ok;
+                    if (t < twin) {
+                        const int32_t j = J0 + 16 * t + m;
+                        const int32_t s2 = j - ri[1];
+                        if (s2 < 0 || s2 >= ri[2]) continue;
+                        slot = ri[0] + s2;
+                        ok = j >= lo && j <= (a.causal ? i : hi);
+                    } else {
+                        if (gt >= ri[3]) continue;
+                        slot = ri[0] + ri[2] + gt;
+                        ok = gc >= 0 && (gc < lo || gc > hi) && (!a.causal || gc <= i);
+                    }
+                    const float w = ok ? __builtin_amdgcn_exp2f(a.scale_log2 * d[v] -
+                                                                msh[16 * bb + 4 * kq + v])
+                                       : 0.0f;
+                    Abh[slot] = w;
+                    rsum[v] += w;
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float t = group_sum(rsum[v]);
+            if (m == 0) psum[tq * kRowsPerGroup + 16 * bb + 4 * kq + v] = t;
+        }
+    }
+    __syncthreads();
 
 #pragma unroll 1
     for (int u = 0; u < kRowsPerWave; ++u) {
@@ -172,7 +301,7 @@ void k_scores_rows_f32(SRowsArgs a) {
         // the slots, valid[4], scaled scores[4]); kind 0 window (slots
         // seg + t0 .. + 3), 1 global (seg + wseg + t0 ..), 2 random, 3 a
         // short global row (seg + t0 ..).
-        auto sweep = [&](auto&& f) {
+        auto sweep = [&](bool band, auto&& f) {
             if (grow) {
                 const int32_t len = (int32_t)rs.seg_len;
                 for (int32_t tb = 0; tb < len; tb += 16) {
@@ -191,7 +320,7 @@ void k_scores_rows_f32(SRowsArgs a) {
                 }
                 return;
             }
-            for (int32_t tb = 0; tb < wseg; tb += 16) {
+            for (int32_t tb = 0; band && tb < wseg; tb += 16) {
                 const int32_t t0 = tb + 4 * grp;
                 bool ok[4];
                 float s[4];
@@ -199,11 +328,11 @@ void k_scores_rows_f32(SRowsArgs a) {
                 for (int v = 0; v < 4; ++v) {
                     const int64_t c = wb0 + t0 + v;
                     ok[v] = t0 < wseg && c >= lo && c <= wend;
-                    s[v] = a.scale_log2 * group_sum(dot4(q, lds4(win + (ok[v] ? c - w0 : 0) * D + 4 * sub)));
+                    s[v] = a.scale_log2 * group_sum(dot4(q, klds4(lds, (int32_t)(ok[v] ? c - w0 : 0), 4 * sub)));
                 }
                 f(0, t0, u32x4{0u, 0u, 0u, 0u}, ok, s);
             }
-            for (int32_t tb = 0; tb < gseg; tb += 16) {
+            for (int32_t tb = 0; band && tb < gseg; tb += 16) {
                 const int32_t t0 = tb + 4 * grp;
                 const u32x4 gk = bload16(rG, t0 < min(gseg, a.g) ? 4u * (uint32_t)t0 : kOutside, 0u);
                 bool ok[4];
@@ -212,7 +341,7 @@ void k_scores_rows_f32(SRowsArgs a) {
                 for (int v = 0; v < 4; ++v) {
                     const int64_t k = (int32_t)gk[v];
                     ok[v] = t0 + v < min(gseg, a.g) && (k < lo || k > hi) && k <= last;
-                    s[v] = a.scale_log2 * group_sum(dot4(q, lds4(glob + (ok[v] ? t0 + v : 0) * D + 4 * sub)));
+                    s[v] = a.scale_log2 * group_sum(dot4(q, klds4(lds, a.win_rows + (ok[v] ? t0 + v : 0), 4 * sub)));
                 }
                 f(1, t0, u32x4{0u, 0u, 0u, 0u}, ok, s);
             }
@@ -253,18 +382,24 @@ void k_scores_rows_f32(SRowsArgs a) {
             }
         };
 
-        // The fused single pass, shifted by the row's own score.
-        const float ms = a.scale_log2 * group_sum(dot4(q, lds4(win + (i - w0) * D + 4 * sub)));
+        // The fused single pass, shifted by the row's own score: the random
+        // edges here (a short global row: every slot), the band's weights and
+        // sums from the MFMA tiles.
+        const float ms = msh[i - r0];
         float total = 0.0f;
-        sweep([&](int kind, int32_t t0, const u32x4& sl, const bool (&ok)[4], const float (&s)[4]) {
+        if (!grow)
+            for (int t = 0; t < 4; ++t) total += psum[t * kRowsPerGroup + (i - r0)];
+        float rtot = 0.0f;
+        sweep(false, [&](int kind, int32_t t0, const u32x4& sl, const bool (&ok)[4], const float (&s)[4]) {
             float w[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) w[v] = ok[v] ? __builtin_amdgcn_exp2f(s[v] - ms) : 0.0f;
             store(kind, t0, sl, ok, w);
-            if (sub == 0) total += (w[0] + w[1]) + (w[2] + w[3]);
+            if (sub == 0) rtot += (w[0] + w[1]) + (w[2] + w[3]);
         });
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) total += __shfl_xor(total, off);
+        for (int off = 1; off < kWave; off <<= 1) rtot += __shfl_xor(rtot, off);
+        total += rtot;
         if (total < kSumLimit) {
             if (lane == 0) a.row_scale[(int64_t)bh * n + i] = 1.0f / total;
             continue;
@@ -272,14 +407,14 @@ void k_scores_rows_f32(SRowsArgs a) {
         // Redone with the exact maximum: its (max, sum), then the normalised
         // weights and c_i over them as stored.
         float m = -INFINITY;
-        sweep([&](int, int32_t, const u32x4&, const bool (&ok)[4], const float (&s)[4]) {
+        sweep(true, [&](int, int32_t, const u32x4&, const bool (&ok)[4], const float (&s)[4]) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) m = ok[v] ? fmaxf(m, s[v]) : m;
         });
 #pragma unroll
         for (int off = 16; off < kWave; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
         float l = 0.0f;
-        sweep([&](int, int32_t, const u32x4&, const bool (&ok)[4], const float (&s)[4]) {
+        sweep(true, [&](int, int32_t, const u32x4&, const bool (&ok)[4], const float (&s)[4]) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) l += ok[v] ? __builtin_amdgcn_exp2f(s[v] - m) : 0.0f;
         });
@@ -287,7 +422,7 @@ void k_scores_rows_f32(SRowsArgs a) {
         for (int off = 16; off < kWave; off <<= 1) l += __shfl_xor(l, off);
         const float inv = 1.0f / l;
         float stored = 0.0f;
-        sweep([&](int kind, int32_t t0, const u32x4& sl, const bool (&ok)[4], const float (&s)[4]) {
+        sweep(true, [&](int kind, int32_t t0, const u32x4& sl, const bool (&ok)[4], const float (&s)[4]) {
             float w[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) w[v] = ok[v] ? __builtin_amdgcn_exp2f(s[v] - m) * inv : 0.0f;
@@ -482,8 +617,11 @@ int32_t win_rows(const diffuser_graph& g) {
     return kRowsPerGroup + (g.causal ? 1 : 2) * g.radius + 8;
 }
 
+// The key rows (window run, globals and kGlobPad zero rows), then the rows'
+// shifts, the band sums of the four tile quarters and the rows' geometry.
 int32_t lds_bytes(const diffuser_graph& g, diffuser_dtype dt) {
-    return (win_rows(g) + g.num_global) * 64 * (dt == DIFFUSER_F32 ? 4 : 2);
+    return (win_rows(g) + g.num_global + kGlobPad) * 64 * (dt == DIFFUSER_F32 ? 4 : 2) +
+           9 * kRowsPerGroup * 4;
 }
 
 template <typename T>
