@@ -621,6 +621,9 @@ ROWS_F32_CASES = [
     (2048, 10, [0, 1024, 2047], 24, False, 1, 32),
     (1100, 40, list(range(0, 1100, 50)), 30, True, 2, 30),
     (1300, 70, list(range(13)) + [650, 1299], 40, False, 4, 16),
+    # no globals, n not a multiple of 16
+    (2051, 20, [], 12, False, 1, 33),
+    (1057, 33, [], 9, True, 1, 64),
 ]
 
 
@@ -961,6 +964,9 @@ BACKWARD_ROWS_CASES = [
     (2056, 24, [7, 2055], 10, 1, False, 1, 32, "bf16", 4, 0.0),
     # random weights in groups past the row segments (n > 4576)
     (6000, 16, [0, 2999, 5999], 12, 1, False, 1, 12, "f32", 2, 0.1),
+    # no globals, n not a multiple of 16
+    (2051, 20, [], 8, 1, False, 1, 33, "f32", 3, 0.1),
+    (2051, 12, [], 6, 1, True, 1, 33, "bf16", 2, 0.3),
 ]
 
 
