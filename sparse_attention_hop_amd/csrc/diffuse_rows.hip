@@ -266,16 +266,27 @@ void k_diffuse_rows_mma(RowsArgs a) {
         u32x4 sl, cl;
         idx(0, sl, cl);
         for (int32_t base = 0; base < nr; base += 4 * NG) {
-            float w[4];
+            // One weight load per lane: lane sub of each group fetches the
+            // weight of edge base + 4 grp + (sub mod 4); the group's four
+            // weights are then broadcast from its lanes 0 .. 3 (DPP
+            // row_newbcast).
+            const int vv = sub & 3;
+            const uint32_t slv = vv == 0 ? sl[0] : vv == 1 ? sl[1] : vv == 2 ? sl[2] : sl[3];
+            const bool okw = base + 4 * grp + vv < nr;
+            const int wl = __builtin_amdgcn_raw_buffer_load_b32(
+                rAR, okw ? (int)(4u * slv) : (int)kOutside, 0, 0);
             f32x4 z[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const bool ok = base + 4 * grp + v < nr;
-                w[v] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-                    rAR, ok ? (int)(4u * sl[v]) : (int)kOutside, 0, 0));
                 z[v] = ld4(Zbh + (int64_t)(ok ? (int32_t)cl[v] : 0) * D + 4 * sub);
             }
             idx(base + 4 * NG, sl, cl);
+            float w[4];
+            w[0] = __int_as_float(__builtin_amdgcn_mov_dpp(wl, 0x150, 0xf, 0xf, false));
+            w[1] = __int_as_float(__builtin_amdgcn_mov_dpp(wl, 0x151, 0xf, 0xf, false));
+            w[2] = __int_as_float(__builtin_amdgcn_mov_dpp(wl, 0x152, 0xf, 0xf, false));
+            w[3] = __int_as_float(__builtin_amdgcn_mov_dpp(wl, 0x153, 0xf, 0xf, false));
 #pragma unroll
             for (int v = 0; v < 4; ++v) fma4(acc, w[v], z[v]);
         }
