@@ -232,6 +232,60 @@ __device__ __forceinline__ void edge_dots_range(const RowSlots& rs, const float*
     }
 }
 
+// v plus the value of the lane of its DPP row that `ctrl` names.
+template <int ctrl>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, true));
+}
+// Sum over a row of 16 lanes (every lane gets it): lane pairs, quads, the
+// halves of 8 and of 16.
+__device__ __forceinline__ float row16_sum(float v) {
+    v = dpp_add<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v = dpp_add<0x141>(v);   // row_half_mirror
+    v = dpp_add<0x140>(v);   // row_mirror
+    return v;
+}
+// Lane u of the caller's row of 16 lanes (DPP row_newbcast).
+template <int u>
+__device__ __forceinline__ int32_t row16_lane(int32_t v) {
+    return __builtin_amdgcn_mov_dpp(v, 0x150 + u, 0xf, 0xf, false);
+}
+
+// The random slots of row i for D = 64 (a lane group is one DPP row of 16
+// lanes): per step of 16 edges, lane u < 4 of group q loads the slot and
+// column of edge base + 4 u + q and hands them round the group, each group
+// sums its four edges' K dot products over its 16 lanes, and lane u stores
+// edge u's value: two index loads and one store per step.
+__device__ __forceinline__ void rand_dots64(const RowSlots& rs, const float* Gi, const float* Zb,
+                                            int64_t stride, int32_t K, float* dAb, float a,
+                                            int grp, int sub) {
+    const int32_t nr = rs.rcnt;
+    for (int32_t base = 0; base < nr; base += 4 * kUnroll) {
+        const int32_t el = base + 4 * (sub & 3) + grp;
+        const int32_t sl = el < nr ? rs.rslot[el] : -1;
+        const int32_t cl = el < nr ? rs.rcol[el] : 0;
+        const int32_t s[kUnroll] = {row16_lane<0>(sl), row16_lane<1>(sl), row16_lane<2>(sl),
+                                    row16_lane<3>(sl)};
+        const int32_t j[kUnroll] = {row16_lane<0>(cl), row16_lane<1>(cl), row16_lane<2>(cl),
+                                    row16_lane<3>(cl)};
+        float dot[kUnroll] = {};
+        for (int32_t k = 0; k < K; ++k) {
+            const float4 g = *reinterpret_cast<const float4*>(Gi + k * stride);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const float4 z = *reinterpret_cast<const float4*>(Zb + k * stride + (int64_t)j[u] * 64);
+                dot[u] += g.x * z.x + g.y * z.y + g.z * z.z + g.w * z.w;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) dot[u] = row16_sum(dot[u]);
+        const int u = sub & 3;
+        const float dv = u == 0 ? dot[0] : u == 1 ? dot[1] : u == 2 ? dot[2] : dot[3];
+        if (sub < 4 && sl >= 0) dAb[sl] = a * dv;
+    }
+}
+
 // dA[s] = a * sum_{k < K} G_{k+1}[i] . Z_k[col(s)] for the slots of row i
 // (padding slots get 0): groups of L lanes take one slot each (L = D / 4
 // lanes of 4 channels); state k of G or Z starts at k * stride. kRandOnly:
@@ -257,7 +311,8 @@ void k_edge_dots(GenericGraph gg, int32_t H, int32_t BH, const float* __restrict
     const float* Zb = Zs + (int64_t)bh * n * D + 4 * sub;
     const int64_t cnt = rs.count();
     if (kRandOnly) {
-        if (rs.rcnt > 0) edge_dots_range<D>(rs, Gi, Zb, stride, K, dAb, a, rs.seg_len, cnt, grp, sub);
+        if constexpr (D == 64) rand_dots64(rs, Gi, Zb, stride, K, dAb, a, grp, sub);
+        else if (rs.rcnt > 0) edge_dots_range<D>(rs, Gi, Zb, stride, K, dAb, a, rs.seg_len, cnt, grp, sub);
         return;
     }
     if (cnt > kLongRow) return;   // k_edge_dots_long's
