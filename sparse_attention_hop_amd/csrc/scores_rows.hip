@@ -611,8 +611,9 @@ void k_scores_grows_f32(SRowsArgs a, int32_t gblocks) {
 
 // Key rows of the window run: the group's rows, the radius on either side
 // (on the left only when causal) and the 8-column alignment of its start.
-// A slot outside its row's window or global set reads LDS row 0 with a
-// zero weight, so no rows are needed past the run or past the globals.
+// A per-row slot outside its row's window or global set reads LDS row 0
+// with a zero weight, and a band tile's keys past the run read its last
+// row, so no rows are needed past the run.
 int32_t win_rows(const diffuser_graph& g) {
     return kRowsPerGroup + (g.causal ? 1 : 2) * g.radius + 8;
 }
