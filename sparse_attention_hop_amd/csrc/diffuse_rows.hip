@@ -84,6 +84,12 @@ __device__ __forceinline__ f32x4 restart4(const RowsArgs& a, int64_t o, float ke
     return keep * acc + a.restart * ld4(static_cast<const TV*>(a.V) + o);
 }
 
+// Lane u of the caller's row of 16 lanes (DPP row_newbcast).
+template <int u>
+__device__ __forceinline__ int32_t row16_lane(int32_t v) {
+    return __builtin_amdgcn_mov_dpp(v, 0x150 + u, 0xf, 0xf, false);
+}
+
 __device__ __forceinline__ void fma4(float (&acc)[4], float w, const f32x4& z) {
     acc[0] = fmaf(w, z[0], acc[0]);
     acc[1] = fmaf(w, z[1], acc[1]);
@@ -256,37 +262,40 @@ void k_diffuse_rows_mma(RowsArgs a) {
             rslot = a.t_slot + t0;
             rcol = a.t_row + t0;
         }
-        const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(rslot, (uint32_t)(4 * nr));
-        const __amdgpu_buffer_rsrc_t rC = buffer_rsrc(rcol, (uint32_t)(4 * nr));
-        auto idx = [&](int32_t base, u32x4& sl, u32x4& cl) {
-            const int32_t e0 = base + 4 * grp;
-            sl = bload16(rS, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
-            cl = bload16(rC, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
+        // Indices, one load per lane: lane sub of group grp fetches the slot
+        // (sub mod 8 < 4) or the column (sub mod 8 >= 4) of edge
+        // base + 4 grp + (sub mod 4); the group's four slots and columns
+        // are then broadcast from its lanes 0 .. 3 and 4 .. 7 (DPP
+        // row_newbcast), as are the four weights from the lanes that load
+        // them.
+        const int vv = sub & 3;
+        const int32_t* ixp = (sub & 4) ? rcol : rslot;
+        auto idx = [&](int32_t base) -> int32_t {
+            const int32_t e = base + 4 * grp + vv;
+            return e < nr ? ixp[e] : 0;
         };
-        u32x4 sl, cl;
-        idx(0, sl, cl);
+        int32_t ix = idx(0);
         for (int32_t base = 0; base < nr; base += 4 * NG) {
-            // One weight load per lane: lane sub of each group fetches the
-            // weight of edge base + 4 grp + (sub mod 4); the group's four
-            // weights are then broadcast from its lanes 0 .. 3 (DPP
-            // row_newbcast).
-            const int vv = sub & 3;
-            const uint32_t slv = vv == 0 ? sl[0] : vv == 1 ? sl[1] : vv == 2 ? sl[2] : sl[3];
+            const int32_t sl[4] = {row16_lane<0>(ix), row16_lane<1>(ix), row16_lane<2>(ix),
+                                   row16_lane<3>(ix)};
+            const int32_t cl[4] = {row16_lane<4>(ix), row16_lane<5>(ix), row16_lane<6>(ix),
+                                   row16_lane<7>(ix)};
+            const int32_t slv = vv == 0 ? sl[0] : vv == 1 ? sl[1] : vv == 2 ? sl[2] : sl[3];
             const bool okw = base + 4 * grp + vv < nr;
             const int wl = __builtin_amdgcn_raw_buffer_load_b32(
-                rAR, okw ? (int)(4u * slv) : (int)kOutside, 0, 0);
+                rAR, okw ? (int)(4u * (uint32_t)slv) : (int)kOutside, 0, 0);
             f32x4 z[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const bool ok = base + 4 * grp + v < nr;
-                z[v] = ld4(Zbh + (int64_t)(ok ? (int32_t)cl[v] : 0) * D + 4 * sub);
+                z[v] = ld4(Zbh + (int64_t)(ok ? cl[v] : 0) * D + 4 * sub);
             }
-            idx(base + 4 * NG, sl, cl);
+            ix = idx(base + 4 * NG);
             float w[4];
-            w[0] = __int_as_float(__builtin_amdgcn_mov_dpp(wl, 0x150, 0xf, 0xf, false));
-            w[1] = __int_as_float(__builtin_amdgcn_mov_dpp(wl, 0x151, 0xf, 0xf, false));
-            w[2] = __int_as_float(__builtin_amdgcn_mov_dpp(wl, 0x152, 0xf, 0xf, false));
-            w[3] = __int_as_float(__builtin_amdgcn_mov_dpp(wl, 0x153, 0xf, 0xf, false));
+            w[0] = __int_as_float(row16_lane<0>(wl));
+            w[1] = __int_as_float(row16_lane<1>(wl));
+            w[2] = __int_as_float(row16_lane<2>(wl));
+            w[3] = __int_as_float(row16_lane<3>(wl));
 #pragma unroll
             for (int v = 0; v < 4; ++v) fma4(acc, w[v], z[v]);
         }
