@@ -254,21 +254,25 @@ __device__ __forceinline__ int32_t row16_lane(int32_t v) {
 
 // The random slots of row i for D = 64 (a lane group is one DPP row of 16
 // lanes): per step of 16 edges, lane u < 4 of group q loads the slot and
-// column of edge base + 4 u + q and hands them round the group, each group
+// lane 4 + u the column of edge base + 4 u + q, handed round the group; each group
 // sums its four edges' K dot products over its 16 lanes, and lane u stores
-// edge u's value: two index loads and one store per step.
+// edge u's value: one index load and one store per step.
 __device__ __forceinline__ void rand_dots64(const RowSlots& rs, const float* Gi, const float* Zb,
                                             int64_t stride, int32_t K, float* dAb, float a,
                                             int grp, int sub) {
     const int32_t nr = rs.rcnt;
+    // Lanes 0-3 of a group load slots, lanes 4-7 columns: one load per step.
+    const int32_t* ixp = (sub & 4) ? rs.rcol : rs.rslot;
     for (int32_t base = 0; base < nr; base += 4 * kUnroll) {
         const int32_t el = base + 4 * (sub & 3) + grp;
-        const int32_t sl = el < nr ? rs.rslot[el] : -1;
-        const int32_t cl = el < nr ? rs.rcol[el] : 0;
-        const int32_t s[kUnroll] = {row16_lane<0>(sl), row16_lane<1>(sl), row16_lane<2>(sl),
-                                    row16_lane<3>(sl)};
-        const int32_t j[kUnroll] = {row16_lane<0>(cl), row16_lane<1>(cl), row16_lane<2>(cl),
-                                    row16_lane<3>(cl)};
+        const int32_t ix = el < nr ? ixp[el] : -1;
+        const int32_t sl = ix;   // this lane's slot (lanes 0-3 store)
+        const int32_t s[kUnroll] = {row16_lane<0>(ix), row16_lane<1>(ix), row16_lane<2>(ix),
+                                    row16_lane<3>(ix)};
+        int32_t j[kUnroll] = {row16_lane<4>(ix), row16_lane<5>(ix), row16_lane<6>(ix),
+                              row16_lane<7>(ix)};
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) j[u] = s[u] >= 0 ? j[u] : 0;
         float dot[kUnroll] = {};
         for (int32_t k = 0; k < K; ++k) {
             const float4 g = *reinterpret_cast<const float4*>(Gi + k * stride);

@@ -82,6 +82,12 @@ __device__ __forceinline__ float dpp_add(float v) {
     return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, true));
 }
 
+// Lane u of the caller's row of 16 lanes (DPP row_newbcast).
+template <int u>
+__device__ __forceinline__ int32_t row16_lane(int32_t v) {
+    return __builtin_amdgcn_mov_dpp(v, 0x150 + u, 0xf, 0xf, false);
+}
+
 // Sum over the 16 lanes of a lane group (every lane gets it), by DPP within
 // each row of 16 lanes: lane pairs, then quads (quad permutations), then
 // the two halves of 8 (half-row mirror) and of 16 (row mirror); each step
@@ -294,8 +300,6 @@ void k_scores_rows_f32(SRowsArgs a) {
         const int64_t wb0 = ri.y;
         const int32_t wseg = ri.z, gseg = ri.w;
         const int32_t nr = rs.rcnt;
-        const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(rs.rslot, (uint32_t)(4 * nr));
-        const __amdgpu_buffer_rsrc_t rC = buffer_rsrc(rs.rcol, (uint32_t)(4 * nr));
 
         // Every slot of the row, four per lane group per step: f(kind, t0 or
         // the slots, valid[4], scaled scores[4]); kind 0 window (slots
@@ -347,8 +351,14 @@ void k_scores_rows_f32(SRowsArgs a) {
             }
             for (int32_t eb = 0; eb < nr; eb += 16) {
                 const int32_t e0 = eb + 4 * grp;
-                const u32x4 sl = bload16(rS, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
-                const u32x4 cl = bload16(rC, e0 < nr ? 4u * (uint32_t)e0 : kOutside, 0u);
+                // one index load per lane: slots from lanes 0-3, columns
+                // from lanes 4-7 of the group (DPP row_newbcast)
+                const int32_t el = e0 + (sub & 3);
+                const int32_t ix = el < nr ? ((sub & 4) ? rs.rcol : rs.rslot)[el] : 0;
+                const u32x4 sl = u32x4{(uint32_t)row16_lane<0>(ix), (uint32_t)row16_lane<1>(ix),
+                                       (uint32_t)row16_lane<2>(ix), (uint32_t)row16_lane<3>(ix)};
+                const u32x4 cl = u32x4{(uint32_t)row16_lane<4>(ix), (uint32_t)row16_lane<5>(ix),
+                                       (uint32_t)row16_lane<6>(ix), (uint32_t)row16_lane<7>(ix)};
                 bool ok[4];
                 f32x4 kz[4];
 #pragma unroll
