@@ -20,6 +20,7 @@
 // every column) go to a second kernel, 16 of them against each key row on
 // MFMA.
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 #include "mfma_util.h"
@@ -262,24 +263,25 @@ void k_diffuse_rows_mma(RowsArgs a) {
             rslot = a.t_slot + t0;
             rcol = a.t_row + t0;
         }
-        // Indices, one load per lane: lane sub of group grp fetches the slot
-        // (sub mod 8 < 4) or the column (sub mod 8 >= 4) of edge
-        // base + 4 grp + (sub mod 4); the group's four slots and columns
-        // are then broadcast from its lanes 0 .. 3 and 4 .. 7 (DPP
-        // row_newbcast), as are the four weights from the lanes that load
-        // them.
+        // Indices, one load per lane per two steps of 16 edges: lane sub of
+        // group grp fetches the slot (sub mod 8 < 4) or the column (sub mod
+        // 8 >= 4) of edge base + 16 (sub / 8) + 4 grp + (sub mod 4); each
+        // step's four slots and columns are then broadcast from the group's
+        // lanes (DPP row_newbcast), as are the four weights from the lanes
+        // that load them.
         const int vv = sub & 3;
         const int32_t* ixp = (sub & 4) ? rcol : rslot;
         auto idx = [&](int32_t base) -> int32_t {
-            const int32_t e = base + 4 * grp + vv;
+            const int32_t e = base + 16 * (sub >> 3) + 4 * grp + vv;
             return e < nr ? ixp[e] : 0;
         };
-        int32_t ix = idx(0);
-        for (int32_t base = 0; base < nr; base += 4 * NG) {
-            const int32_t sl[4] = {row16_lane<0>(ix), row16_lane<1>(ix), row16_lane<2>(ix),
-                                   row16_lane<3>(ix)};
-            const int32_t cl[4] = {row16_lane<4>(ix), row16_lane<5>(ix), row16_lane<6>(ix),
-                                   row16_lane<7>(ix)};
+        // One step of 16 edges from index lanes 8 h .. 8 h + 7.
+        auto step = [&](auto hc, int32_t base, int32_t ix) {
+            constexpr int h = decltype(hc)::value;
+            const int32_t sl[4] = {row16_lane<8 * h + 0>(ix), row16_lane<8 * h + 1>(ix),
+                                   row16_lane<8 * h + 2>(ix), row16_lane<8 * h + 3>(ix)};
+            const int32_t cl[4] = {row16_lane<8 * h + 4>(ix), row16_lane<8 * h + 5>(ix),
+                                   row16_lane<8 * h + 6>(ix), row16_lane<8 * h + 7>(ix)};
             const int32_t slv = vv == 0 ? sl[0] : vv == 1 ? sl[1] : vv == 2 ? sl[2] : sl[3];
             const bool okw = base + 4 * grp + vv < nr;
             const int wl = __builtin_amdgcn_raw_buffer_load_b32(
@@ -290,7 +292,6 @@ void k_diffuse_rows_mma(RowsArgs a) {
                 const bool ok = base + 4 * grp + v < nr;
                 z[v] = ld4(Zbh + (int64_t)(ok ? cl[v] : 0) * D + 4 * sub);
             }
-            ix = idx(base + 4 * NG);
             float w[4];
             w[0] = __int_as_float(row16_lane<0>(wl));
             w[1] = __int_as_float(row16_lane<1>(wl));
@@ -298,6 +299,13 @@ void k_diffuse_rows_mma(RowsArgs a) {
             w[3] = __int_as_float(row16_lane<3>(wl));
 #pragma unroll
             for (int v = 0; v < 4; ++v) fma4(acc, w[v], z[v]);
+        };
+        int32_t ix = idx(0);
+        for (int32_t base = 0; base < nr; base += 8 * NG) {
+            const int32_t ixn = idx(base + 8 * NG);
+            step(std::integral_constant<int, 0>{}, base, ix);
+            if (base + 4 * NG < nr) step(std::integral_constant<int, 1>{}, base + 4 * NG, ix);
+            ix = ixn;
         }
 #pragma unroll
         for (int off = L; off < kWave; off <<= 1) {
