@@ -261,6 +261,13 @@ __device__ __forceinline__ void rand_dots64(const RowSlots& rs, const float* Gi,
                                             int64_t stride, int32_t K, float* dAb, float a,
                                             int grp, int sub) {
     const int32_t nr = rs.rcnt;
+    // The row's first kHeld states of G stay in registers for all its edges.
+    constexpr int kHeld = 6;
+    float4 gh[kHeld];
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k)
+        gh[k] = k < K && nr > 0 ? *reinterpret_cast<const float4*>(Gi + k * stride)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
     // Lanes 0-3 of a group load slots, lanes 4-7 columns: one load per step.
     const int32_t* ixp = (sub & 4) ? rs.rcol : rs.rslot;
     for (int32_t base = 0; base < nr; base += 4 * kUnroll) {
@@ -274,7 +281,17 @@ __device__ __forceinline__ void rand_dots64(const RowSlots& rs, const float* Gi,
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) j[u] = s[u] >= 0 ? j[u] : 0;
         float dot[kUnroll] = {};
-        for (int32_t k = 0; k < K; ++k) {
+#pragma unroll
+        for (int32_t k = 0; k < kHeld; ++k) {
+            if (k >= K) break;
+            const float4 g = gh[k];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const float4 z = *reinterpret_cast<const float4*>(Zb + k * stride + (int64_t)j[u] * 64);
+                dot[u] += g.x * z.x + g.y * z.y + g.z * z.z + g.w * z.w;
+            }
+        }
+        for (int32_t k = kHeld; k < K; ++k) {
             const float4 g = *reinterpret_cast<const float4*>(Gi + k * stride);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
