@@ -142,7 +142,7 @@ void k_diffuse_rows_mma(RowsArgs a) {
     constexpr int U = D * (int)sizeof(TX) / 16;
     extern __shared__ __align__(16) char lds_raw[];
     TX LDS_AS* lds = (TX LDS_AS*)lds_raw;
-    float LDS_AS* csum = (float LDS_AS*)lds_raw;   // [64][64], after the products
+    float LDS_AS* csum = (float LDS_AS*)lds_raw;   // [4][64][64], after the products
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int sub = lane % L, grp = lane / L;
@@ -186,11 +186,17 @@ void k_diffuse_rows_mma(RowsArgs a) {
     }
     full_barrier();
 
-    // ---- window band and global columns, one 16 x 16 tile per wave ---------
+    // ---- window band and global columns, a quarter of the keys per wave ------
+    // Wave w takes the rows of block w / 4 and every fourth 16-key chunk
+    // (from chunk w mod 4) of its window keys and globals, against all 64
+    // channels (four tiles), so each weight is loaded once; the four
+    // quarters' partial sums meet in LDS.
     const int m = lane & 15, kq = lane >> 4;
     const int64_t ib0 = r0 + 16 * (wave >> 2);
-    const int32_t cch = 16 * (wave & 3) + m;   // this lane's channel of the key rows
-    f32x4 acc16 = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int kqt = wave & 3;
+    f32x4 acc16[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc16[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (ib0 < n) {
         const int64_t i = ib0 + m;   // this lane's weight row
         const int4 ri = i < n ? info[i] : make_int4(0, 0, -1, 0);
@@ -205,41 +211,53 @@ void k_diffuse_rows_mma(RowsArgs a) {
         const int64_t J0 = (ib0 - r < 0 ? 0 : ib0 - r) & ~7ll;
         const int64_t wend_l = a.causal ? ibl : (ibl + r > n - 1 ? n - 1 : ibl + r);
         const int32_t nch = (int32_t)(((wend_l | 7) - J0) / 16 + 1);
-        for (int32_t c = 0; c < nch; ++c) {
-            const int64_t key0 = J0 + 16 * c + 4 * kq;
-            const int64_t s0 = key0 - ri.y;
-            const bool in = live && s0 >= 0 && s0 < ri.z;
-            const u32x4 wv = bload16(rA, in ? 4u * (uint32_t)(ri.x + s0) : kOutside, 0u);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t key = key0 + e;
-                const bool ok = live && key >= lo && key <= wend;
-                const int32_t kl = (int32_t)min(key - w0, (int64_t)a.win_rows - 1);
-                acc16 = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? __uint_as_float(wv[e]) : 0.0f,
-                                                             zld(lds, zpos<TX>(kl, cch)), acc16,
-                                                             0, 0, 0);
-            }
-        }
         const int32_t gch = (a.g + 15) / 16;
-        for (int32_t c = 0; c < gch; ++c) {
-            const int32_t t0 = 16 * c + 4 * kq;
-            const bool in = live && t0 < ri.w;
-            const u32x4 wv = bload16(rA, in ? 4u * (uint32_t)(ri.x + ri.z + t0) : kOutside, 0u);
-            const u32x4 gk = bload16(rG, t0 < a.g ? 4u * (uint32_t)t0 : kOutside, 0u);
+        for (int32_t c = kqt; c < nch + gch; c += 4) {
+            u32x4 wv;
+            int32_t kl[4];
+            bool ok[4];
+            if (c < nch) {
+                const int64_t key0 = J0 + 16 * c + 4 * kq;
+                const int64_t s0 = key0 - ri.y;
+                const bool in = live && s0 >= 0 && s0 < ri.z;
+                wv = bload16(rA, in ? 4u * (uint32_t)(ri.x + s0) : kOutside, 0u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t key = key0 + e;
+                    ok[e] = live && key >= lo && key <= wend;
+                    kl[e] = (int32_t)min(key - w0, (int64_t)a.win_rows - 1);
+                }
+            } else {
+                const int32_t t0 = 16 * (c - nch) + 4 * kq;
+                const bool in = live && t0 < ri.w;
+                wv = bload16(rA, in ? 4u * (uint32_t)(ri.x + ri.z + t0) : kOutside, 0u);
+                const u32x4 gk = bload16(rG, t0 < a.g ? 4u * (uint32_t)t0 : kOutside, 0u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t kc = (int32_t)gk[e];
+                    ok[e] = in && t0 + e < a.g && (kc < lo || kc > hi) && kc <= last;
+                    kl[e] = a.win_rows + t0 + e;
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t kc = (int32_t)gk[e];
-                const bool ok = in && t0 + e < a.g && (kc < lo || kc > hi) && kc <= last;
-                acc16 = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                    ok ? __uint_as_float(wv[e]) : 0.0f,
-                    zld(lds, zpos<TX>(a.win_rows + t0 + e, cch)), acc16, 0, 0, 0);
+                const float we = ok[e] ? __uint_as_float(wv[e]) : 0.0f;
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+                    acc16[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        we, zld(lds, zpos<TX>(kl[e], 16 * ct + m)), acc16[ct], 0, 0, 0);
             }
         }
     }
     __syncthreads();   // every wave is done with the key rows
-    // Lane (m, kq) holds rows 4 kq + v of its block at channel cch.
+    // Lane (m, kq) holds rows 4 kq + v of its block at channels 16 ct + m;
+    // quarter kqt's partial sums go to csum[kqt].
 #pragma unroll
-    for (int v = 0; v < 4; ++v) csum[(16 * (wave >> 2) + 4 * kq + v) * 64 + cch] = acc16[v];
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            csum[(kqt * kRowsPerGroup + 16 * (wave >> 2) + 4 * kq + v) * 64 + 16 * ct + m] =
+                acc16[ct][v];
     __syncthreads();
 
     // ---- random edges per row, gathered, plus the block sums ----------------
@@ -313,7 +331,11 @@ void k_diffuse_rows_mma(RowsArgs a) {
             for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
         }
         if (grp == 0) {
-            const f32x4 bs = *reinterpret_cast<const f32x4 LDS_AS*>(csum + (i - r0) * 64 + 4 * sub);
+            f32x4 bs = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                bs = bs + *reinterpret_cast<const f32x4 LDS_AS*>(
+                              csum + (q * kRowsPerGroup + (i - r0)) * 64 + 4 * sub);
             const int64_t o = ((int64_t)bh * n + i) * D + 4 * sub;
             const float keep =
                 a.row_scale == nullptr ? a.keep : a.keep * a.row_scale[(int64_t)bh * n + i];
@@ -581,7 +603,7 @@ void set_transposed(RowsArgs& a, const diffuser_graph& g, const float* A) {
 template <typename TX, typename TV, typename TY>
 hipError_t launch_args(const diffuser_graph& g, int32_t B, int32_t H, const RowsArgs& a,
                        hipStream_t st) {
-    const int lds = std::max(lds_bytes(g, (int)sizeof(TX)), kRowsPerGroup * 64 * 4);
+    const int lds = std::max(lds_bytes(g, (int)sizeof(TX)), 4 * kRowsPerGroup * 64 * 4);
     auto kern = &k_diffuse_rows_mma<64, TX, TV, TY>;
     static int attr_device = -1;
     if (attr_device != g.device) {
