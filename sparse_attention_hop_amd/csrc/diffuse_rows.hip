@@ -353,13 +353,14 @@ void k_diffuse_rows_mma(RowsArgs a) {
 // one 16-byte load and ends with four consecutive channels of each of its
 // rows. Keys outside the wave's range, past n or (causal) above the row
 // weigh 0. The waves' partial sums meet in LDS and are added in wave order.
-constexpr int kGTile = 16;
 
-template <int D, typename TX, typename TV, typename TY>
+// kGTiles tiles of 16 global rows per workgroup share each key row's load.
+template <int D, typename TX, typename TV, typename TY, int kGTiles>
 __global__ __launch_bounds__(kThreads)
 void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
+    constexpr int kGTile = 16 * kGTiles;
     static_assert(D == 64, "four channel tiles of 16");
-    __shared__ f32x4 part[kWaves][kGTile][16];   // [wave][row][channels 4 n ..]
+    __shared__ f32x4 part[kWaves][16][16];   // [wave][row of a tile][channels 4 n ..]
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int m = lane & 15, kq = lane >> 4;
@@ -375,46 +376,66 @@ void k_diffuse_grows_f32(RowsArgs a, int32_t gblocks) {
                                                  : a.gg.slot_off[gr + 1] - a.gg.slot_off[gr];
     const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(Abh, (uint32_t)(4 * pair_slots));
     const __amdgpu_buffer_rsrc_t rZ = buffer_rsrc(Zbh, (uint32_t)(sizeof(TX) * n * D));
-    // This lane's weight row (row m of the tile) and its last column.
-    const int32_t q = q0 + m;
-    const int64_t gi = q < a.g ? a.G[q] : -1;
-    const uint32_t seg = gi >= 0 ? (uint32_t)info[gi].x : 0u;
-    const int64_t last = gi < 0 ? -1 : a.causal ? gi : n - 1;
-    f32x4 acc[4];
+    // This lane's weight rows (row m of each tile) and their last columns.
+    uint32_t seg[kGTiles];
+    int64_t last[kGTiles];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tl = 0; tl < kGTiles; ++tl) {
+        const int32_t q = q0 + 16 * tl + m;
+        const int64_t gi = q < a.g ? a.G[q] : -1;
+        seg[tl] = gi >= 0 ? (uint32_t)info[gi].x : 0u;
+        last[tl] = gi < 0 ? -1 : a.causal ? gi : n - 1;
+    }
+    f32x4 acc[kGTiles][4];
+#pragma unroll
+    for (int tl = 0; tl < kGTiles; ++tl)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[tl][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t k0 = n * wave / kWaves, k1 = n * (wave + 1) / kWaves;
     for (int64_t kb = k0 & ~15ll; kb < k1; kb += 16) {
         const int64_t key0 = kb + 4 * kq;   // this lane's keys key0 .. key0 + 3
-        const bool any = key0 <= last && key0 + 3 >= k0 && key0 < k1;
-        const u32x4 w = bload16(rA, any ? 4u * (seg + (uint32_t)key0) : kOutside, 0u);
+        u32x4 w[kGTiles];
+#pragma unroll
+        for (int tl = 0; tl < kGTiles; ++tl) {
+            const bool any = key0 <= last[tl] && key0 + 3 >= k0 && key0 < k1;
+            w[tl] = bload16(rA, any ? 4u * (seg[tl] + (uint32_t)key0) : kOutside, 0u);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int64_t key = key0 + e;
-            const bool ok = key >= k0 && key < k1 && key <= last;
-            const float we = ok ? __uint_as_float(w[e]) : 0.0f;
             const bool zk = key >= k0 && key < k1;
             const f32x4 z = bload4<TX>(rZ, zk ? (uint32_t)((key * D + 4 * m) * sizeof(TX)) : kOutside);
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(we, z[ct], acc[ct], 0, 0, 0);
+            for (int tl = 0; tl < kGTiles; ++tl) {
+                const float we = zk && key <= last[tl] ? __uint_as_float(w[tl][e]) : 0.0f;
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+                    acc[tl][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(we, z[ct], acc[tl][ct], 0, 0, 0);
+            }
         }
     }
-    // Lane (n, kq) holds rows 4 kq + v at channels 4 n + ct.
+    // Lane (n, kq) holds rows 4 kq + v of each tile at channels 4 n + ct;
+    // the tiles' partial sums meet in LDS one tile at a time.
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-        part[wave][4 * kq + v][m] = f32x4{acc[0][v], acc[1][v], acc[2][v], acc[3][v]};
-    __syncthreads();
-    for (int t = threadIdx.x; t < kGTile * 16; t += kThreads) {
-        const int rr = t / 16, c4 = t - rr * 16;
-        if (q0 + rr >= a.g) continue;
-        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int w = 0; w < kWaves; ++w) sum = sum + part[w][rr][c4];
-        const int64_t i = a.G[q0 + rr];
-        const int64_t o = ((int64_t)bh * n + i) * D + 4 * c4;
-        const float keep =
-            a.row_scale == nullptr ? a.keep : a.keep * a.row_scale[(int64_t)bh * n + i];
-        st4(static_cast<TY*>(a.Zn) + o, restart4<TV>(a, o, keep, sum));
+    for (int tl = 0; tl < kGTiles; ++tl) {
+        if (tl > 0) __syncthreads();   // the previous tile's sums are read
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            part[wave][4 * kq + v][m] =
+                f32x4{acc[tl][0][v], acc[tl][1][v], acc[tl][2][v], acc[tl][3][v]};
+        __syncthreads();
+        for (int t = threadIdx.x; t < 16 * 16; t += kThreads) {
+            const int rr = t / 16, c4 = t - rr * 16;
+            const int32_t q = q0 + 16 * tl + rr;
+            if (q >= a.g) continue;
+            f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ww = 0; ww < kWaves; ++ww) sum = sum + part[ww][rr][c4];
+            const int64_t i = a.G[q];
+            const int64_t o = ((int64_t)bh * n + i) * D + 4 * c4;
+            const float keep =
+                a.row_scale == nullptr ? a.keep : a.keep * a.row_scale[(int64_t)bh * n + i];
+            st4(static_cast<TY*>(a.Zn) + o, restart4<TV>(a, o, keep, sum));
+        }
     }
 }
 
@@ -615,9 +636,17 @@ hipError_t launch_args(const diffuser_graph& g, int32_t B, int32_t H, const Rows
     hipLaunchKernelGGL(kern, dim3((unsigned)(8 * a.per_xcd)), dim3(kThreads), (size_t)lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.num_global == 0) return e;
-    const int32_t gblocks = (g.num_global + kGTile - 1) / kGTile;
-    hipLaunchKernelGGL((k_diffuse_grows_f32<64, TX, TV, TY>), dim3((unsigned)(B * H * gblocks)),
-                       dim3(kThreads), 0, st, a, gblocks);
+    // Two tiles of 16 global rows per workgroup when that leaves at least
+    // half as many workgroups as CUs (measured: 192 workgroups gain, 32
+    // lose), else one.
+    const int32_t g2 = (g.num_global + 31) / 32;
+    if ((int64_t)B * H * g2 >= 128)
+        hipLaunchKernelGGL((k_diffuse_grows_f32<64, TX, TV, TY, 2>), dim3((unsigned)(B * H * g2)),
+                           dim3(kThreads), 0, st, a, g2);
+    else
+        hipLaunchKernelGGL((k_diffuse_grows_f32<64, TX, TV, TY, 1>),
+                           dim3((unsigned)(B * H * ((g.num_global + 15) / 16))), dim3(kThreads), 0,
+                           st, a, (g.num_global + 15) / 16);
     return hipGetLastError();
 }
 
