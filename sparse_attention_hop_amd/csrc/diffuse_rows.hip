@@ -85,6 +85,8 @@ __device__ __forceinline__ f32x4 restart4(const RowsArgs& a, int64_t o, float ke
     return keep * acc + a.restart * ld4(static_cast<const TV*>(a.V) + o);
 }
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 // Lane u of the caller's row of 16 lanes (DPP row_newbcast).
 template <int u>
 __device__ __forceinline__ int32_t row16_lane(int32_t v) {
@@ -184,6 +186,26 @@ void k_diffuse_rows_mma(RowsArgs a) {
                 *reinterpret_cast<f32x4 LDS_AS*>(ldsb + 16 * p) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
+    // The group's row geometry and random-edge counts (or list starts) in
+    // LDS past the key rows and the partial sums, loaded once by the last
+    // wave.
+    const int32_t aux = max((a.win_rows + a.g + kGlobPad) * D * (int)sizeof(TX),
+                            4 * kRowsPerGroup * 64 * 4);
+    i32x4 LDS_AS* rinfo = reinterpret_cast<i32x4 LDS_AS*>((char LDS_AS*)lds_raw + aux);   // [64]
+    int64_t LDS_AS* rlist = reinterpret_cast<int64_t LDS_AS*>(rinfo + kRowsPerGroup);   // [65]
+    if (wave == kWaves - 1) {
+        const int64_t ir = r0 + lane;
+        const int4 t = ir < n ? info[ir] : make_int4(0, 0, -1, 0);
+        rinfo[lane] = i32x4{t.x, t.y, t.z, t.w};
+        if (a.t_ptr != nullptr) {
+            rlist[lane] = a.t_ptr[(int64_t)gr * (n + 1) + (ir < n ? ir : n)];
+            if (lane == 0)
+                rlist[kRowsPerGroup] =
+                    a.t_ptr[(int64_t)gr * (n + 1) + (r0 + kRowsPerGroup < n ? r0 + kRowsPerGroup : n)];
+        } else {
+            rlist[lane] = ir < n && a.gg.rslot != nullptr ? a.gg.rnd_cnt[(int64_t)gr * n + ir] : 0;
+        }
+    }
     full_barrier();
 
     // ---- window band and global columns, a quarter of the keys per wave ------
@@ -199,7 +221,8 @@ void k_diffuse_rows_mma(RowsArgs a) {
     for (int ct = 0; ct < 4; ++ct) acc16[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (ib0 < n) {
         const int64_t i = ib0 + m;   // this lane's weight row
-        const int4 ri = i < n ? info[i] : make_int4(0, 0, -1, 0);
+        const i32x4 rv = rinfo[i - r0];
+        const int4 ri = make_int4(rv[0], rv[1], rv[2], rv[3]);
         const bool live = i < n && ri.z >= 0;
         const int64_t lo = i - r < 0 ? 0 : i - r;
         const int64_t hi = i + r > n - 1 ? n - 1 : i + r;
@@ -265,19 +288,19 @@ void k_diffuse_rows_mma(RowsArgs a) {
     for (int u = 0; u < kRowsPerWave; ++u) {
         const int64_t i = r0 + kWaves * u + wave;
         if (i >= n) break;
-        const int4 ri = info[i];
-        if (ri.z < 0) continue;   // a global row: k_diffuse_grows_f32's
+        const int32_t li = kWaves * u + wave;
+        if (rinfo[li][2] < 0) continue;   // a global row: k_diffuse_grows_f32's
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         int32_t nr;
         const int32_t *rslot, *rcol;
         if (a.t_ptr == nullptr) {
-            const RowSlots rs = a.gg.row(gr, i);
-            nr = rs.rcnt;
-            rslot = rs.rslot;
-            rcol = rs.rcol;
+            const int64_t row = (int64_t)gr * n + i;
+            nr = (int32_t)rlist[li];
+            rslot = a.gg.rslot + row * a.gg.rnd_width;
+            rcol = a.gg.rnd + row * a.gg.rnd_width;
         } else {
-            const int64_t t0 = a.t_ptr[(int64_t)gr * (n + 1) + i];
-            nr = (int32_t)(a.t_ptr[(int64_t)gr * (n + 1) + i + 1] - t0);
+            const int64_t t0 = rlist[li];
+            nr = (int32_t)(rlist[li + 1] - t0);
             rslot = a.t_slot + t0;
             rcol = a.t_row + t0;
         }
@@ -624,7 +647,8 @@ void set_transposed(RowsArgs& a, const diffuser_graph& g, const float* A) {
 template <typename TX, typename TV, typename TY>
 hipError_t launch_args(const diffuser_graph& g, int32_t B, int32_t H, const RowsArgs& a,
                        hipStream_t st) {
-    const int lds = std::max(lds_bytes(g, (int)sizeof(TX)), 4 * kRowsPerGroup * 64 * 4);
+    const int lds = std::max(lds_bytes(g, (int)sizeof(TX)), 4 * kRowsPerGroup * 64 * 4) +
+                    kRowsPerGroup * 16 + (kRowsPerGroup + 1) * 8;
     auto kern = &k_diffuse_rows_mma<64, TX, TV, TY>;
     static int attr_device = -1;
     if (attr_device != g.device) {
