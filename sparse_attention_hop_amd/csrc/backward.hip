@@ -590,14 +590,28 @@ void k_axpby(int64_t count, const TX* __restrict__ x, float* __restrict__ y, flo
         y[e] = a * ld(x + e) + (b == 0.0f ? 0.0f : b * y[e]);
 }
 
-// out = x + y, converted to TY.
+// dV = alpha (G_K + .. + G_1) + G_0, rounded to TY once, summed from G_K
+// down as a running alpha G_k + acc; four values per thread (count is a
+// multiple of 4).
 template <typename TY>
 __global__ __launch_bounds__(kThreads)
-void k_sum_to(int64_t count, const float* __restrict__ x, const float* __restrict__ y,
+void k_dv_sum(int64_t count, const float* __restrict__ Gs, int64_t stride, int32_t K, float alpha,
               TY* __restrict__ out) {
-    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < count;
-         e += (int64_t)gridDim.x * kThreads)
-        st(out + e, x[e] + y[e]);
+    for (int64_t e = 4 * ((int64_t)blockIdx.x * kThreads + threadIdx.x); e < count;
+         e += 4 * (int64_t)gridDim.x * kThreads) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int32_t k = K; k >= 1; --k) {
+            const float4 g = *reinterpret_cast<const float4*>(Gs + k * stride + e);
+            acc = k == K ? make_float4(alpha * g.x, alpha * g.y, alpha * g.z, alpha * g.w)
+                         : make_float4(alpha * g.x + acc.x, alpha * g.y + acc.y,
+                                       alpha * g.z + acc.z, alpha * g.w + acc.w);
+        }
+        const float4 g0 = *reinterpret_cast<const float4*>(Gs + e);
+        st(out + e, acc.x + g0.x);
+        st(out + e + 1, acc.y + g0.y);
+        st(out + e + 2, acc.z + g0.z);
+        st(out + e + 3, acc.w + g0.w);
+    }
 }
 
 dim3 grid_elems(int64_t count) {
@@ -670,8 +684,6 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
     }
     for (int32_t k = K - 1; k >= 0; --k) {
         const float* Gk1 = p.Gs + (size_t)(k + 1) * cnt;
-        hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, Gk1, p.dV,
-                           p.alpha, k == K - 1 ? 0.0f : 1.0f);
         if (rows_cols) {
             const hipError_t e = launch_transposed_rows(g, p.B, p.H, p.At, p.A, Gk1,
                                                         p.Gs + (size_t)k * cnt, keep, stream);
@@ -700,12 +712,9 @@ hipError_t backward_t(const diffuser_graph& g, const BackwardArgs& p, hipStream_
             hipLaunchKernelGGL((k_edge_dots_long<D>), longs, lblk, 0, stream, gg, p.H, p.Gs, p.Zs,
                                cnt, K, p.dA, keep);
     }
-    // dV = (sum of alpha G_{k+1}) + G_0.
-    if (K == 0)
-        hipLaunchKernelGGL((k_axpby<float>), grid_elems(cnt), blk, 0, stream, cnt, p.Gs, p.dV,
-                           0.0f, 0.0f);
-    hipLaunchKernelGGL((k_sum_to<T>), grid_elems(cnt), blk, 0, stream, cnt, p.dV, p.Gs,
-                       static_cast<T*>(p.dVout));
+    // dV = (sum of alpha G_{k+1}) + G_0, in one pass over the states.
+    hipLaunchKernelGGL((k_dv_sum<T>), grid_elems(cnt / 4), blk, 0, stream, cnt, p.Gs, cnt, K,
+                       p.alpha, static_cast<T*>(p.dVout));
     // dS, then dQ = dS K and dK = dS^T Q (the 1 / sqrt(d_h) inside dS).
     if (rows_states)
         hipLaunchKernelGGL(k_softmax_grad_built, rows, blk, 0, stream, gg, p.H, BH, p.A, p.dA,
