@@ -8,16 +8,24 @@
 // then dV += G_0 (Z_0 = V), dS_ij = A_ij (dA_ij - sum_u A_iu dA_iu),
 // dQ_i = sum_j dS_ij k_j / sqrt(d_h), dK_j = sum_i dS_ij q_i / sqrt(d_h).
 //
-// Generic kernels over the weight slots (any built graph, fp32 or bf16
-// storage, d in {16, 32, 64, 128}); every intermediate (A, dA, the states
-// Z_k, G_k, dV) is fp32. Rows and columns with more than kLongRow entries
-// are split over the waves of one workgroup by companion kernels. Row-wise products walk a row's slots; the
-// transposed ones walk the graph's column index (the slots of each column
-// by ascending row), with the weights first copied into that order so that
-// only the rows of X are gathered. dA takes all K terms in one pass over
-// the slots, from the stored states G_1 .. G_K. Each wave splits its row or
-// column over groups of lanes and adds the groups' partial sums in a fixed
-// order, so every sum has a fixed order.
+// Every intermediate (A, dA, the states Z_k, G_k, dV) is fp32; the outputs
+// are rounded to the storage type once, and every sum has a fixed order.
+//
+// On built graphs with d = 64 and enough rows the products run on the fp32
+// LDS-window step kernels (the states and dQ; on bidirectional graphs also
+// G_k and dK, over A^T laid out in the graph's own slot geometry), dA's
+// dense parts on MFMA (dots_mfma.hip) with its random slots here, and the
+// softmax gradient reads each segment as quads. Everything else runs on
+// generic kernels over the weight slots (any graph, fp32 or bf16 storage,
+// d in {16, 32, 64, 128}): rows and columns with more than kLongRow entries
+// are split over the waves of one workgroup by companion kernels;
+// row-wise products walk a row's slots, the transposed ones the graph's
+// column index (the slots of each column by ascending row) with the
+// weights first copied into that order, so only the rows of X are
+// gathered; dA takes all K terms in one pass over the slots, from the
+// stored states G_1 .. G_K; each wave splits its row or column over groups
+// of lanes and adds the groups' partial sums in a fixed order. dV is one
+// pass over the stored states at the end.
 #include <algorithm>
 #include <type_traits>
 
