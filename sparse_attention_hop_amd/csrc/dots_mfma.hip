@@ -273,34 +273,48 @@ void k_dots_band_lds(DotsArgs a, int32_t groups, int32_t per_xcd, int32_t win_ro
     }
 }
 
+// Each wave takes kKTiles tiles of 16 keys, so every global row's operand
+// load serves them all.
+constexpr int kKTiles = 2;
+
 __global__ __launch_bounds__(kThreads)
 void k_dots_glob(DotsArgs a) {
     const int lane = __lane_id();
     const int wave = threadIdx.x / kWave;
     const int m = lane & 15, kq = lane >> 4;
+    const int64_t nkp = (a.nkt + kKTiles - 1) / kKTiles;
     const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    if (item >= (int64_t)a.BH * a.nkt) return;
-    const int32_t bh = (int32_t)(item / a.nkt);
-    const int64_t j0 = (item - (int64_t)bh * a.nkt) * 16;
+    if (item >= (int64_t)a.BH * nkp) return;
+    const int32_t bh = (int32_t)(item / nkp);
+    const int64_t j0 = (item - (int64_t)bh * nkp) * 16 * kKTiles;
     const int32_t b = bh / a.H, h = bh - b * a.H;
     const int32_t gr = a.num_graphs == 1 ? 0 : b;
     const int64_t n = a.n;
     const int4* info = a.row_info + (int64_t)gr * n;
     const int64_t* sp = a.seg_ptr + (int64_t)gr * (n + 1);
     float* dAb = a.dA + a_block_offset(a.slot_off, a.num_graphs, a.H, b, h);
-    const int64_t key = j0 + m;   // this lane's key row
-    const bool kok = key < n;
-    const float* Zk = a.Zs + ((int64_t)bh * n + (kok ? key : 0)) * 64 + 4 * kq;
+    int64_t key[kKTiles];   // this lane's key row of each tile
+    const float* Zk[kKTiles];
+#pragma unroll
+    for (int kt = 0; kt < kKTiles; ++kt) {
+        key[kt] = j0 + 16 * kt + m;
+        Zk[kt] = a.Zs + ((int64_t)bh * n + (key[kt] < n ? key[kt] : 0)) * 64 + 4 * kq;
+    }
     const float* Gb = a.Gs + a.stride + (int64_t)bh * n * 64 + 4 * kq;
 
     for (int32_t qp = 0; qp < a.g; qp += 16 * kQTiles) {
-        f32x4 acc[kQTiles];
+        f32x4 acc[kQTiles][kKTiles];
 #pragma unroll
-        for (int qt = 0; qt < kQTiles; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qt = 0; qt < kQTiles; ++qt)
+#pragma unroll
+            for (int kt = 0; kt < kKTiles; ++kt) acc[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int32_t k = 0; k < a.K; ++k) {
-            f32x4 z[4];
+            f32x4 z[kKTiles][4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) z[s] = ld4z(Zk + k * a.stride + 16 * s, kok);
+            for (int kt = 0; kt < kKTiles; ++kt)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    z[kt][s] = ld4z(Zk[kt] + k * a.stride + 16 * s, key[kt] < n);
 #pragma unroll
             for (int qt = 0; qt < kQTiles; ++qt) {
                 const int32_t q0 = qp + 16 * qt;
@@ -310,10 +324,15 @@ void k_dots_glob(DotsArgs a) {
                 const float* Gq = Gb + k * a.stride + gi * 64;
                 // rows of the product = global rows, columns = keys
 #pragma unroll
-                for (int s = 0; s < 4; ++s) acc[qt] = mfma_chunk(acc[qt], ld4z(Gq + 16 * s, qok), z[s]);
+                for (int s = 0; s < 4; ++s) {
+                    const f32x4 gq = ld4z(Gq + 16 * s, qok);
+#pragma unroll
+                    for (int kt = 0; kt < kKTiles; ++kt)
+                        acc[qt][kt] = mfma_chunk(acc[qt][kt], gq, z[kt][s]);
+                }
             }
         }
-        // Lane holds global rows q0 + 4 kq + v against key j0 + m.
+        // Lane holds global rows q0 + 4 kq + v against key j0 + 16 kt + m.
 #pragma unroll
         for (int qt = 0; qt < kQTiles; ++qt) {
             const int32_t q0 = qp + 16 * qt;
@@ -323,9 +342,12 @@ void k_dots_glob(DotsArgs a) {
                 if (q >= a.g) continue;
                 const int64_t i = a.G[q];
                 const int64_t seglen = sp[i + 1] - sp[i];
-                if (key >= seglen) continue;
                 const int64_t last = a.causal ? i : n - 1;
-                dAb[(int64_t)info[i].x + key] = key <= last ? a.f * acc[qt][v] : 0.0f;
+#pragma unroll
+                for (int kt = 0; kt < kKTiles; ++kt)
+                    if (key[kt] < seglen)
+                        dAb[(int64_t)info[i].x + key[kt]] =
+                            key[kt] <= last ? a.f * acc[qt][kt][v] : 0.0f;
             }
         }
     }
@@ -405,7 +427,8 @@ hipError_t launch_dots_dense(const diffuser_graph& g, int32_t B, int32_t H, cons
     }
     e = hipGetLastError();
     if (e != hipSuccess || g.num_global == 0) return e;
-    const int64_t glob = ((int64_t)a.BH * a.nkt + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t glob =
+        ((int64_t)a.BH * ((a.nkt + kKTiles - 1) / kKTiles) + kWavesPerBlock - 1) / kWavesPerBlock;
     hipLaunchKernelGGL(k_dots_glob, dim3((unsigned)glob), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
